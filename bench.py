@@ -1,0 +1,198 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+One step = the whole path on one batch of the single-layer KV-key workload (Llama-3-8B shape:
+1 x 8 KV heads x 32768 tokens x d = 128, bf16 keys with outlier channels and log-normal
+per-token scale): TurboQuant_mse b = 3 encode of all 262144 keys (norm, dense rotation on MFMA,
+Lloyd-Max bucketize, bit-pack), then the decode-step scores of 32 query heads (GQA 4) over the
+packed keys.  Inputs are resident in HBM before timing; the step rotates through several input
+and output buffer sets whose total exceeds the last-level cache.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this path runs on one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CACHE_DEFEAT_BYTES = 1.5e9
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc"))):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(open(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key, launches_bytes_key):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except Exception:
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get(launches_bytes_key)
+
+
+def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: one KV head slab of
+    keys encoded and scored by the 4 query heads that share it (the full step is 8 such slabs of
+    32768 tokens)."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rot = oracle.dense_rotation(cfg.d, cfg.rot_seed)
+    cb = oracle.codebook(cfg.d, cfg.bits)
+    ratio = cfg.hq // cfg.hkv
+    tokens = 0
+    scores = 0
+    t0 = time.perf_counter()
+    chunk = 4096
+    head = 0
+    while True:
+        x = wl.bf16_bits_to_f32(keys_bits[0, head % cfg.hkv, (tokens % cfg.T):(tokens % cfg.T) + chunk])
+        enc = oracle.encode_mse(x.astype(np.float64), rot, cb)
+        qs = q[0, (head % cfg.hkv) * ratio:((head % cfg.hkv) + 1) * ratio].astype(np.float64)
+        s = oracle.scores_mse(qs, enc.idx, enc.norms, rot, cb)
+        tokens += x.shape[0]
+        scores += s.size
+        if time.perf_counter() - t0 > budget_s:
+            break
+        if tokens % cfg.T == 0:
+            head += 1
+    dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    return {"value": scores / dt, "unit": "scores/s (encode + score of the sampled keys)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens} keys of the workload (4096-key chunks of one KV head slab) encoded "
+                      f"and scored by their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in the design notes, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_turboquant_amd as tq
+    from kv_cache_compression_turboquant_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS["c2"]
+    n = cfg.B * cfg.hkv * cfg.T
+    keys_bits = wl.kv_keys(cfg)
+    q_np = wl.kv_queries(cfg)
+
+    cb = tq.codebook(cfg.d, cfg.bits)
+    rot = tq.make_rotation(cfg.d, cfg.rot_seed, "dense")
+    in_bytes = n * cfg.d * 2
+    words = cfg.d * cfg.bits // 32
+    out_bytes = n * (words * 4 + 4)
+    score_bytes_out = cfg.B * cfg.hq * cfg.T * 4
+    per_set = in_bytes + out_bytes + score_bytes_out
+    nbuf = max(1, int(np.ceil(CACHE_DEFEAT_BYTES / per_set)))
+    base = torch.from_numpy(keys_bits.reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [base] + [base.clone() for _ in range(nbuf - 1)]
+    packs = [tq.alloc_packed(n, cfg.d, cfg.bits, "mse", device=dev) for _ in range(nbuf)]
+    q = torch.from_numpy(q_np).to(dev)
+    outs = [torch.empty((cfg.B, cfg.hq, cfg.T), dtype=torch.float32, device=dev) for _ in range(nbuf)]
+    ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        j = i % nbuf
+        if ev is not None:
+            ev[0].record()
+        tq.encode(xs[j], cfg.bits, "mse", cb, rot, out=packs[j])
+        if ev is not None:
+            ev[1].record()
+        tq.scores(q, packs[j], cfg.hkv, cb, rot, out=outs[j], ws=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, events on the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    scores_per_step = cfg.B * cfg.hq * cfg.T
+    enc_alg_bytes = in_bytes + out_bytes
+    score_alg_bytes = n * (words * 4 + 4) + cfg.B * cfg.hq * cfg.d * 4 + score_bytes_out
+    achieved = enc_alg_bytes / (enc_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile("k_encode_d128:c2", "hbm_bytes_per_launch")
+
+    result = {
+        "metric": "Q·K^T scores/s over packed keys + encode vectors/s; % of HBM roofline",
+        "value": scores_per_step / step_s,
+        "unit": "scores/s (each step encodes all keys, then scores every query head)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.workload, "keys": [cfg.B, cfg.hkv, cfg.T, cfg.d], "bits": cfg.bits,
+                   "mode": cfg.mode, "query_heads": cfg.hq, "rotation": "dense QR (seed 1)",
+                   "encode_vectors_per_s": n / step_s,
+                   "encode_kernel_ms": enc_ms, "score_path_ms": sc_ms,
+                   "score_path_gbs": score_alg_bytes / (sc_ms * 1e-3) / 1e9,
+                   "buffer_sets": nbuf},
+        "roofline": {"bound": "hbm", "kernel": "k_encode_d128 (MSE b=3, dense R, bf16 keys)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": enc_alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, keys_bits, q_np, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

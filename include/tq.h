@@ -1,0 +1,185 @@
+/*
+ * tq.h -- C ABI of the TurboQuant encode / compressed-key score library for MI355X (gfx950).
+ *
+ * The library implements the data-parallel hot path of TurboQuant:
+ *   encode : s = ||x||, y = R (x / s), per-coordinate Lloyd-Max index, b-bit packing, and for
+ *            TurboQuant_prod a 1-bit QJL sign sketch of the residual plus its norm;
+ *   score  : <q, x_hat> from packed keys with the query rotated once, optional QJL term,
+ *            GQA sharing, and fused decode attention softmax(q K_hat^T * scale) V_hat.
+ * Source pages (cited by title and section):
+ *   [TQ]  "TurboQuant 详解" (wnma3mz blog): quantizer definition, TurboQuant_mse official steps,
+ *         TurboQuant_prod section, KV prefill/decode flow.
+ *   [FP]  "TurboQuant first-principles walkthrough" (blog.hotdry.top): rotation, codebook,
+ *         distortion bound, QJL constant, fixed seed.
+ *   [RQ]  "TurboQuant 和 RotorQuant 的真相" (zhichai.net): attention formula, word-wise unpack.
+ *   [SB]  "Sub-byte KV cache quantization with TurboQuant" (blog2.hotdry.top): codebook
+ *         recipe, fused score kernel with a pre-rotated query, GQA mapping, checklist.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev are device pointers (HIP global memory of the current device);
+ *    pointers named *_host are host pointers.  The caller owns every buffer it passes; the
+ *    library never frees or retains caller memory.  Handles (codebook, rotation, qjl) are
+ *    owned by the library until the matching *_free call; they are immutable after creation
+ *    and may be shared across streams and threads.
+ *  - Device work is enqueued on the given stream (NULL = the default stream) and is
+ *    asynchronous; nothing synchronises the stream.  No entry point that takes a stream
+ *    allocates device memory.
+ *  - Return value: TQ_OK, or an error code.  Arguments are validated before any launch; on
+ *    error nothing is enqueued, outputs are untouched, and tq_last_error() returns a
+ *    thread-local message.  Asynchronous device faults surface at the caller's next
+ *    synchronisation.  Non-finite inputs give unspecified (but in-bounds) results.
+ *  - Sizes: 1 <= b <= 4 bits per index stage; d * b must be a multiple of 32; the fused
+ *    kernels cover d = 128; other d in [64, 3072] use the general path where stated.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* null pointer, bits out of range, negative size, bad enum */
+  TQ_ESHAPE = 2,        /* d mismatch between codebook / rotation / tensors ([SB] checklist:
+                           the codebook dimension must equal head_dim); Hq % Hkv != 0;
+                           d * b not a multiple of 32 */
+  TQ_EUNSUPPORTED = 3,  /* Hadamard rotation with d not a power of two; d outside the
+                           supported range for this entry point; unsupported dtype */
+  TQ_ENOMEM = 4,        /* caller workspace too small, or host allocation failed */
+  TQ_EDEVICE = 5        /* a HIP runtime error (text in tq_last_error) */
+} tq_status;
+
+typedef enum tq_density { TQ_DENSITY_BETA = 0, TQ_DENSITY_GAUSS = 1 } tq_density;
+typedef enum tq_rot_kind { TQ_ROT_DENSE = 0, TQ_ROT_WHT = 1 } tq_rot_kind;
+typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+typedef enum tq_mode { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1 } tq_mode;
+
+typedef struct tq_codebook_s* tq_codebook_t;
+typedef struct tq_rotation_s* tq_rotation_t;
+typedef struct tq_qjl_s* tq_qjl_t;
+
+/* A packed set of n encoded vectors, all buffers device memory owned by the caller.
+ * Row r of idx holds the d indices of vector r as one LSB-first bit stream: coordinate i
+ * occupies stream bits [i*bits, i*bits + bits), stream bit p is bit (p % 32) of word p / 32
+ * ([TQ] KV prefill example, step 5: a compact bit stream).  Row r of qjl holds bit i = 1 iff
+ * (S r)_i >= 0 ([TQ] TurboQuant_prod: sign(0) = +1).  norms are fp32 ||x||, rnorms fp32
+ * residual norms gamma = ||x - x_hat_mse||. */
+typedef struct tq_packed {
+  int32_t d;          /* vector length */
+  int32_t bits;       /* bits per index: b for MSE, b - 1 for prod */
+  int32_t mode;       /* tq_mode */
+  int32_t reserved;   /* must be 0 */
+  int64_t n;          /* number of vectors (rows) */
+  uint32_t* idx;      /* [n, d*bits/32] */
+  float* norms;       /* [n] */
+  uint32_t* qjl;      /* [n, d/32] for prod, else NULL */
+  float* rnorms;      /* [n] for prod, else NULL */
+} tq_packed;
+
+/* ---- housekeeping ------------------------------------------------------------------- */
+int tq_abi_version(void);
+/* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
+const char* tq_last_error(void);
+
+/* ---- host-only math (no GPU needed; deterministic; caller-owned host outputs) -------- */
+
+/* Draws offset .. offset+n-1 of the SplitMix64 stream of `seed` (Steele, Lea, Flood 2014):
+ * mix(seed + (i+1) * 0x9E3779B97F4A7C15).  The pages fix only "a fixed seed" ([FP] deployment
+ * parameters); this generator is the library's reading. */
+tq_status tq_host_splitmix64(uint64_t seed, uint64_t offset, int64_t n, uint64_t* out_host);
+/* n standard normals of stream `seed`: Box-Muller cosine branch, draws 2e and 2e+1. */
+tq_status tq_host_gaussian(uint64_t seed, int64_t n, double* out_host);
+/* The (d, b) Lloyd-Max codebook on a 50000-point grid over +-6/sqrt(d) (clipped to [-1, 1]),
+ * 300 iterations ([SB] engineering path, first layer; density [TQ] key insight), made
+ * antisymmetric.  centroids_host: 2^b values; thresholds_host: 2^b - 1 midpoints.
+ * Errors: TQ_EINVAL for b outside 1..4, d < 2 or bad density. */
+tq_status tq_host_codebook(int d, int b, tq_density dens, double* centroids_host,
+                           double* thresholds_host);
+/* Rotation matrix R (d x d, row-major, y = R u): DENSE = Q of the QR of the seeded Gaussian
+ * matrix with a non-negative triangular diagonal ([TQ] official step 1; [FP] rotation);
+ * WHT = (1/sqrt(d)) H_d diag(sigma), Sylvester H, Rademacher sigma ([RQ] chapter 3).
+ * Errors: TQ_EUNSUPPORTED for WHT with d not a power of two; TQ_EINVAL for d < 2. */
+tq_status tq_host_rotation(int d, uint64_t seed, tq_rot_kind kind, double* r_host);
+/* QJL matrix S (d x d, row-major, i.i.d. N(0,1) from stream `seed`). */
+tq_status tq_host_qjl_matrix(int d, uint64_t seed, double* s_host);
+
+/* ---- handles (created on the current device; uploads are synchronous) ---------------- */
+
+/* Codebook handle for (d, b) by the recipe of tq_host_codebook. */
+tq_status tq_codebook(int d, int b, tq_density dens, tq_codebook_t* out);
+/* Codebook handle from caller centroids (2^b strictly increasing values, host). */
+tq_status tq_codebook_from_values(int d, int b, const double* centroids_host, tq_codebook_t* out);
+/* Reads back the fp64 centroids (2^b) and thresholds (2^b - 1) of a handle. */
+tq_status tq_codebook_values(tq_codebook_t cb, double* centroids_host, double* thresholds_host);
+void tq_codebook_free(tq_codebook_t cb);
+
+/* Rotation handle: R generated once from `seed` and kept ([FP]: generated at init, shared by
+ * all vectors).  d must be 128 for the fused encode kernels. */
+tq_status tq_make_rotation(int d, uint64_t seed, tq_rot_kind kind, tq_rotation_t* out);
+/* Rotation handle from a caller matrix (row-major d x d host fp64; treated as DENSE). */
+tq_status tq_rotation_from_matrix(int d, const double* r_host, tq_rotation_t* out);
+/* Copies the fp64 matrix of a rotation handle to r_host (d*d). */
+tq_status tq_rotation_export(tq_rotation_t rot, double* r_host);
+void tq_rotation_free(tq_rotation_t rot);
+
+/* QJL handle for TurboQuant_prod ([TQ] TurboQuant_prod; [FP] QJL paragraph): S from `seed`,
+ * bound to `rot` (the library keeps S' = S R^T so the sketch is taken of the rotated-domain
+ * residual: sign(S r) = sign(S' (y - y_hat))).  rot must outlive nothing: S' is copied. */
+tq_status tq_make_qjl(int d, uint64_t seed, tq_rotation_t rot, tq_qjl_t* out);
+tq_status tq_qjl_from_matrix(int d, const double* s_host, tq_rotation_t rot, tq_qjl_t* out);
+void tq_qjl_free(tq_qjl_t qjl);
+
+/* ---- hot path ------------------------------------------------------------------------ */
+
+/* Words per packed row: d * bits / 32. */
+size_t tq_packed_words(int d, int bits);
+
+/* Encode n vectors x_dev [n, d] (dtype dt, row-major) into *out ([TQ] official steps 1-4 and
+ * KV prefill steps 1-6; prod: [TQ] TurboQuant_prod, (b-1)-bit stage + 1-bit QJL).
+ * b is the total bit budget per coordinate; cb must have b bits (MSE) or b - 1 bits (prod);
+ * qjl must be non-NULL exactly for prod and bound to `rot`.  out->d, out->bits, out->mode,
+ * out->n must describe the call; out->idx/norms (and qjl/rnorms for prod) are written.
+ * A zero vector encodes to norm 0 and the indices of y = 0.  Supported: d = 128 (fused).
+ * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED as above. */
+tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_mode mode,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* out,
+                    void* stream);
+
+/* Rotated unit coordinates y = R x / ||x|| (fp32 [n, d]) and norms (fp32 [n]) exactly as the
+ * encode kernel forms them before quantizing (same kernel, stores instead of packing).
+ * For parity checks of the rotation.  d = 128. */
+tq_status tq_rotate(const void* x_dev, tq_dtype dt, int64_t n, int d, tq_rotation_t rot,
+                    float* y_dev, float* norms_dev, void* stream);
+
+/* Bucketize + pack given fp32 rotated unit coordinates y_dev [n, d] against the fp32
+ * thresholds of cb ([TQ] official step 3, nearest centroid; ties to the upper index);
+ * writes idx_dev [n, d*b/32].  Bit-exact reference entry for the quantizer. */
+tq_status tq_quantize_rotated(const float* y_dev, int64_t n, int d, tq_codebook_t cb,
+                              uint32_t* idx_dev, void* stream);
+
+/* Reconstruct x_hat_dev [n, d] fp32 = s R^T C[idx] ([TQ] official step 5), plus
+ * gamma sqrt(pi/2)/d S^T z when qjl is non-NULL and p->mode is prod. */
+tq_status tq_decode(const tq_packed* p, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl,
+                    float* xhat_dev, void* stream);
+
+/* Workspace bytes tq_scores needs for B*Hq query heads of length d. */
+size_t tq_scores_workspace(int B, int Hq, int d);
+/* Raw scores <q, k_hat> (no 1/sqrt(d)) of q_dev [B, Hq, d] fp32 against packed keys K laid out
+ * [B, Hkv, T] (K->n == B*Hkv*T), into scores_dev [B, Hq, T] fp32.  The query is rotated once
+ * ([SB] third layer); query head h reads kv head h / (Hq / Hkv) ([SB] GQA mapping).
+ * MSE: s <R q, C[idx]>;  prod: plus gamma sqrt(pi/2)/d <S q, z> ([TQ] TurboQuant_prod;
+ * [FP] QJL constant).  Requires Hq / Hkv in {1, 2, 4} when B*Hkv*T > 0; d = 128. */
+tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
+                    void* ws_dev, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

@@ -1,0 +1,235 @@
+"""TurboQuant encode and compressed-key score on MI355X (gfx950).
+
+A thin Python layer over libtq.so (include/tq.h): handles for the codebook, rotation and QJL
+matrix; torch tensors for device memory; torch's current stream for ordering.  Every step of the
+encode / score path runs in the library's HIP kernels; if the library is missing, calls raise.
+"""
+
+import ctypes
+
+import numpy as np
+
+from ._binding import (DENSITY, MODE, ROT_KIND, DTYPE_BF16, DTYPE_F32, TQError, check, lib,
+                       tq_packed, host_splitmix64, host_gaussian, host_codebook, host_rotation,
+                       host_qjl_matrix, SIGNATURES)
+
+__all__ = [
+    "Codebook", "Rotation", "QJL", "Packed", "codebook", "codebook_from_values", "make_rotation",
+    "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
+    "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
+    "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _np(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class _Handle:
+    _free = None
+
+    def __init__(self, ptr):
+        self._ptr = ptr
+
+    @property
+    def ptr(self):
+        return self._ptr
+
+    def close(self):
+        if self._ptr:
+            getattr(lib(), self._free)(self._ptr)
+            self._ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Codebook(_Handle):
+    _free = "tq_codebook_free"
+
+    def __init__(self, ptr, d, b):
+        super().__init__(ptr)
+        self.d, self.b = d, b
+
+    def values(self):
+        c = np.empty(1 << self.b)
+        t = np.empty((1 << self.b) - 1)
+        check(lib().tq_codebook_values(self.ptr, _np(c), _np(t)))
+        return c, t
+
+
+class Rotation(_Handle):
+    _free = "tq_rotation_free"
+
+    def __init__(self, ptr, d, kind):
+        super().__init__(ptr)
+        self.d, self.kind = d, kind
+
+    def matrix(self):
+        r = np.empty((self.d, self.d))
+        check(lib().tq_rotation_export(self.ptr, _np(r)))
+        return r
+
+
+class QJL(_Handle):
+    _free = "tq_qjl_free"
+
+    def __init__(self, ptr, d, rotation):
+        super().__init__(ptr)
+        self.d = d
+        self.rotation = rotation
+
+
+def codebook(d, b, density="beta"):
+    h = ctypes.c_void_p()
+    check(lib().tq_codebook(d, b, DENSITY[density], ctypes.byref(h)))
+    return Codebook(h.value, d, b)
+
+
+def codebook_from_values(d, centroids):
+    c = np.ascontiguousarray(centroids, dtype=np.float64)
+    b = int(round(np.log2(c.size)))
+    h = ctypes.c_void_p()
+    check(lib().tq_codebook_from_values(d, b, _np(c), ctypes.byref(h)))
+    return Codebook(h.value, d, b)
+
+
+def make_rotation(d, seed, kind="dense"):
+    h = ctypes.c_void_p()
+    check(lib().tq_make_rotation(d, seed, ROT_KIND[kind], ctypes.byref(h)))
+    return Rotation(h.value, d, kind)
+
+
+def rotation_from_matrix(m):
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    h = ctypes.c_void_p()
+    check(lib().tq_rotation_from_matrix(m.shape[0], _np(m), ctypes.byref(h)))
+    return Rotation(h.value, m.shape[0], "dense")
+
+
+def make_qjl(d, seed, rotation):
+    h = ctypes.c_void_p()
+    check(lib().tq_make_qjl(d, seed, rotation.ptr, ctypes.byref(h)))
+    return QJL(h.value, d, rotation)
+
+
+def qjl_from_matrix(s, rotation):
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    h = ctypes.c_void_p()
+    check(lib().tq_qjl_from_matrix(s.shape[0], _np(s), rotation.ptr, ctypes.byref(h)))
+    return QJL(h.value, s.shape[0], rotation)
+
+
+def packed_words(d, bits):
+    return int(lib().tq_packed_words(d, bits))
+
+
+class Packed:
+    """Caller-owned packed storage: idx [n, d*bits/32] int32 (uint32 bits), norms [n] fp32,
+    and for prod qjl [n, d/32] int32 and rnorms [n] fp32."""
+
+    def __init__(self, d, bits, mode, n, idx, norms, qjl=None, rnorms=None):
+        self.d, self.bits, self.mode, self.n = d, bits, mode, n
+        self.idx, self.norms, self.qjl, self.rnorms = idx, norms, qjl, rnorms
+
+    def descriptor(self):
+        return tq_packed(self.d, self.bits, MODE[self.mode], 0, self.n, _dptr(self.idx),
+                         _dptr(self.norms), _dptr(self.qjl), _dptr(self.rnorms))
+
+
+def alloc_packed(n, d, bits, mode="mse", device="cuda"):
+    torch = _torch()
+    w = d * bits // 32
+    idx = torch.empty((n, w), dtype=torch.int32, device=device)
+    norms = torch.empty((n,), dtype=torch.float32, device=device)
+    qjl = rn = None
+    if mode == "prod":
+        qjl = torch.empty((n, d // 32), dtype=torch.int32, device=device)
+        rn = torch.empty((n,), dtype=torch.float32, device=device)
+    return Packed(d, bits, mode, n, idx, norms, qjl, rn)
+
+
+def _dtype_code(x):
+    torch = _torch()
+    if x.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if x.dtype == torch.float32:
+        return DTYPE_F32
+    raise TQError(3, f"unsupported dtype {x.dtype}")
+
+
+def encode(x, b, mode, cb, rot, qjl=None, out=None):
+    """Encode rows of x [n, d] (bf16 or fp32, contiguous, on the GPU) with b total bits."""
+    n, d = x.shape
+    stage = b - 1 if mode == "prod" else b
+    if out is None:
+        out = alloc_packed(n, d, stage, mode, device=x.device)
+    desc = out.descriptor()
+    check(lib().tq_encode(_dptr(x), _dtype_code(x), n, d, b, MODE[mode], cb.ptr, rot.ptr,
+                          qjl.ptr if qjl is not None else None, ctypes.byref(desc), _stream()))
+    return out
+
+
+def rotate(x, rot):
+    """(y_unit [n, d] fp32, norms [n] fp32) as formed inside the encode kernel."""
+    torch = _torch()
+    n, d = x.shape
+    y = torch.empty((n, d), dtype=torch.float32, device=x.device)
+    nr = torch.empty((n,), dtype=torch.float32, device=x.device)
+    check(lib().tq_rotate(_dptr(x), _dtype_code(x), n, d, rot.ptr, _dptr(y), _dptr(nr), _stream()))
+    return y, nr
+
+
+def quantize_rotated(y, cb):
+    torch = _torch()
+    n, d = y.shape
+    out = torch.empty((n, d * cb.b // 32), dtype=torch.int32, device=y.device)
+    check(lib().tq_quantize_rotated(_dptr(y), n, d, cb.ptr, _dptr(out), _stream()))
+    return out
+
+
+def decode(p, cb, rot, qjl=None):
+    torch = _torch()
+    out = torch.empty((p.n, p.d), dtype=torch.float32, device=p.norms.device)
+    desc = p.descriptor()
+    check(lib().tq_decode(ctypes.byref(desc), cb.ptr, rot.ptr, qjl.ptr if qjl is not None else None,
+                          _dptr(out), _stream()))
+    return out
+
+
+def scores_workspace(B, Hq, d):
+    return int(lib().tq_scores_workspace(B, Hq, d))
+
+
+def scores(q, K, Hkv, cb, rot, qjl=None, out=None, ws=None):
+    """Raw scores [B, Hq, T] of q [B, Hq, d] fp32 against packed keys K laid out [B, Hkv, T]."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    T = K.n // max(B * Hkv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    nbytes = scores_workspace(B, Hq, d)
+    if ws is None:
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    desc = K.descriptor()
+    check(lib().tq_scores(_dptr(q), B, Hq, Hkv, T, ctypes.byref(desc), cb.ptr, rot.ptr,
+                          qjl.ptr if qjl is not None else None, _dptr(out), _dptr(ws),
+                          ws.numel() * ws.element_size(), _stream()))
+    return out

@@ -1,0 +1,652 @@
+// Host side of the TurboQuant library: seeded generator, Householder QR, Lloyd-Max codebook,
+// handle lifetime, argument validation and the C ABI entry points.
+//
+// Host arithmetic is compiled without floating-point contraction so that every fp64 step
+// rounds once, as written.
+#pragma clang fp contract(off)
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+tq_status ok() { return TQ_OK; }
+
+tq_status hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+std::atomic<uint64_t> g_next_id{1};
+
+// ---- SplitMix64 (Steele, Lea, Flood 2014), counter form --------------------------------
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline uint64_t draw(uint64_t seed, uint64_t i) { return mix64(seed + (i + 1) * kGamma); }
+
+inline double uniform53(uint64_t z) { return (double)(z >> 11) * 0x1.0p-53; }
+
+// Box-Muller, cosine branch, draws 2e and 2e+1.
+void gaussian_fill(uint64_t seed, int64_t n, double* out) {
+  const double two_pi = 6.283185307179586476925;
+  for (int64_t e = 0; e < n; ++e) {
+    double u1 = uniform53(draw(seed, 2 * (uint64_t)e));
+    double u2 = uniform53(draw(seed, 2 * (uint64_t)e + 1));
+    out[e] = std::sqrt(-2.0 * std::log(1.0 - u1)) * std::cos(two_pi * u2);
+  }
+}
+
+// ---- parallel helper ------------------------------------------------------------------
+template <class F>
+void parallel_for(int64_t begin, int64_t end, int64_t grain, F&& f) {
+  int64_t n = end - begin;
+  unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  int64_t nthreads = std::min<int64_t>(std::min<int64_t>(hw, 16), (n + grain - 1) / std::max<int64_t>(grain, 1));
+  if (nthreads <= 1) {
+    for (int64_t i = begin; i < end; ++i) f(i);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nthreads);
+  int64_t chunk = (n + nthreads - 1) / nthreads;
+  for (int64_t t = 0; t < nthreads; ++t) {
+    int64_t lo = begin + t * chunk, hi = std::min(end, lo + chunk);
+    if (lo >= hi) break;
+    th.emplace_back([lo, hi, &f]() {
+      for (int64_t i = lo; i < hi; ++i) f(i);
+    });
+  }
+  for (auto& t : th) t.join();
+}
+
+// ---- Householder QR with the non-negative-diagonal convention ----------------------------
+// g: d x d row-major.  Returns R = Q D (row-major) where G = Q T, T upper triangular, and D
+// flips the columns of Q whose diagonal entry of T is negative (sign(0) = +1), so that the
+// factorisation G = (Q D)(D T) has a non-negative diagonal and is unique.
+void qr_rotation(int d, const double* g, double* r_out) {
+  // column-major working copy: a[j*d + i] = G[i][j]
+  std::vector<double> a((size_t)d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) a[(size_t)j * d + i] = g[(size_t)i * d + j];
+  std::vector<double> vs((size_t)d * d, 0.0);  // Householder vectors, column k from row k
+  std::vector<double> diag(d, 0.0);
+  std::vector<double> beta(d, 0.0);
+  for (int k = 0; k < d; ++k) {
+    double* col = &a[(size_t)k * d];
+    double norm2 = 0.0;
+    for (int i = k; i < d; ++i) norm2 += col[i] * col[i];
+    double norm = std::sqrt(norm2);
+    double* v = &vs[(size_t)k * d];
+    if (norm == 0.0) {
+      diag[k] = 0.0;
+      beta[k] = 0.0;
+      continue;
+    }
+    double alpha = col[k] >= 0.0 ? -norm : norm;
+    for (int i = k; i < d; ++i) v[i] = col[i];
+    v[k] -= alpha;
+    double vnorm2 = 0.0;
+    for (int i = k; i < d; ++i) vnorm2 += v[i] * v[i];
+    beta[k] = vnorm2 > 0.0 ? 2.0 / vnorm2 : 0.0;
+    diag[k] = alpha;
+    const double bk = beta[k];
+    // apply H = I - beta v v^T to the trailing columns
+    parallel_for(k + 1, d, 64, [&](int64_t j) {
+      double* cj = &a[(size_t)j * d];
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * cj[i];
+      double f = bk * dot;
+      for (int i = k; i < d; ++i) cj[i] -= f * v[i];
+    });
+  }
+  // Q = H_0 H_1 ... H_{d-1}: accumulate backwards on the identity (column-major q)
+  std::vector<double> q((size_t)d * d, 0.0);
+  for (int i = 0; i < d; ++i) q[(size_t)i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    if (beta[k] == 0.0) continue;
+    const double* v = &vs[(size_t)k * d];
+    const double bk = beta[k];
+    parallel_for(k, d, 64, [&](int64_t j) {
+      double* cj = &q[(size_t)j * d];
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * cj[i];
+      double f = bk * dot;
+      for (int i = k; i < d; ++i) cj[i] -= f * v[i];
+    });
+  }
+  for (int j = 0; j < d; ++j) {
+    double sgn = diag[j] >= 0.0 ? 1.0 : -1.0;
+    for (int i = 0; i < d; ++i) r_out[(size_t)i * d + j] = sgn * q[(size_t)j * d + i];
+  }
+}
+
+bool is_pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
+
+void hadamard_rotation(int d, uint64_t seed, double* r_out) {
+  const double inv = 1.0 / std::sqrt((double)d);
+  for (int j = 0; j < d; ++j) {
+    double sigma = (draw(seed, (uint64_t)j) >> 63) ? -1.0 : 1.0;
+    for (int i = 0; i < d; ++i) {
+      int par = __builtin_popcount((unsigned)(i & j)) & 1;
+      r_out[(size_t)i * d + j] = (par ? -1.0 : 1.0) * sigma * inv;
+    }
+  }
+}
+
+// ---- Lloyd-Max on the rotated-coordinate density, grid recipe ---------------------------
+constexpr int kGridPoints = 50000;
+constexpr int kIterations = 300;
+
+void lloyd_codebook(int d, int b, int density, double* c_out, double* t_out) {
+  const double sigma = 1.0 / std::sqrt((double)d);
+  const double lo = std::max(-6.0 * sigma, -1.0);
+  const double hi = std::min(6.0 * sigma, 1.0);
+  const int n = kGridPoints;
+  std::vector<double> x(n), w(n), wx(n);
+  const double step = (hi - lo) / (double)(n - 1);
+  for (int j = 0; j < n; ++j) x[j] = (double)j * step + lo;
+  x[n - 1] = hi;
+  const double expo = 0.5 * (double)(d - 3);
+  for (int j = 0; j < n; ++j) {
+    double xx = x[j] * x[j];
+    if (density == TQ_DENSITY_BETA) {
+      double one_minus = 1.0 - xx;
+      w[j] = one_minus > 0.0 ? std::exp(expo * std::log1p(-xx)) : 0.0;
+    } else {
+      w[j] = std::exp(-0.5 * (double)d * x[j] * x[j]);
+    }
+    wx[j] = w[j] * x[j];
+  }
+  const int k = 1 << b;
+  const double m = std::min(3.0 * sigma, 1.0);
+  double c[tq::kMaxCentroids], t[tq::kMaxCentroids];
+  for (int i = 0; i < k; ++i) c[i] = m * (-1.0 + (2.0 * (double)i + 1.0) / (double)k);
+  for (int it = 0; it < kIterations; ++it) {
+    for (int i = 0; i + 1 < k; ++i) t[i] = 0.5 * (c[i] + c[i + 1]);
+    double mass[tq::kMaxCentroids] = {0}, mom[tq::kMaxCentroids] = {0};
+    int cell = 0;  // grid is increasing: the cell index only grows
+    for (int j = 0; j < n; ++j) {
+      while (cell < k - 1 && x[j] >= t[cell]) ++cell;
+      mass[cell] += w[j];
+      mom[cell] += wx[j];
+    }
+    for (int i = 0; i < k; ++i)
+      if (mass[i] > 0.0) c[i] = mom[i] / mass[i];
+  }
+  double cm[tq::kMaxCentroids];
+  for (int i = 0; i < k; ++i) cm[i] = 0.5 * (c[i] - c[k - 1 - i]);
+  for (int i = 0; i < k; ++i) c_out[i] = cm[i];
+  for (int i = 0; i + 1 < k; ++i) t_out[i] = 0.5 * (cm[i] + cm[i + 1]);
+}
+
+void fill_args(tq_codebook_s* cb) {
+  const int k = 1 << cb->b;
+  for (int i = 0; i < tq::kMaxCentroids; ++i) {
+    cb->args.c[i] = i < k ? (float)cb->c[i] : 0.0f;
+    cb->args.t[i] = i + 1 < k ? (float)cb->t[i] : INFINITY;
+  }
+  cb->args.bits = cb->b;
+  bool sym = cb->args.t[k / 2 - 1] == 0.0f;
+  for (int i = 0; i < k && sym; ++i) sym = cb->args.c[k - 1 - i] == -cb->args.c[i];
+  for (int i = 0; i + 1 < k && sym; ++i) sym = cb->args.t[k - 2 - i] == -cb->args.t[i];
+  cb->args.sym = sym ? 1 : 0;
+  for (int p = 0; p < tq::kMaxCentroids / 2; ++p) {
+    cb->args.cpos[p] = p < k / 2 ? cb->args.c[k / 2 + p] : 0.0f;
+    float tp = p < k / 2 - 1 ? cb->args.t[k / 2 + p] : INFINITY;
+    int bitsv;
+    std::memcpy(&bitsv, &tp, 4);
+    cb->args.tpos[p] = bitsv;
+  }
+}
+
+// ---- bf16 split fragments ------------------------------------------------------------
+inline uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+inline float bf16_to_f(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Fragments of the d = 128 matrix m (row-major fp64) scaled by `scale`.
+void build_fragments(const double* m, double scale, std::vector<uint16_t>& out) {
+  out.assign(2 * (size_t)tq::kFragElems, 0);
+  for (int cb = 0; cb < 8; ++cb)
+    for (int s = 0; s < 4; ++s)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          int mm = lane % 16, g = lane / 16;
+          int row = 32 * (mm / 4) + 4 * cb + (mm % 4);
+          int col = 32 * g + 8 * s + e;
+          float v = (float)(m[(size_t)row * 128 + col] * scale);
+          uint16_t hi = bf16_rne(v);
+          float rem = v - bf16_to_f(hi);
+          uint16_t lo = bf16_rne(rem);
+          size_t idx = (((size_t)cb * 4 + s) * 64 + lane) * 8 + e;
+          out[idx] = hi;
+          out[(size_t)tq::kFragElems + idx] = lo;
+        }
+}
+
+template <class T>
+tq_status upload(const std::vector<T>& host, T** dev, const char* what) {
+  hipError_t e = hipMalloc((void**)dev, host.size() * sizeof(T));
+  if (e != hipSuccess) return hip_fail(e, what);
+  e = hipMemcpy(*dev, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    hipFree(*dev);
+    *dev = nullptr;
+    return hip_fail(e, what);
+  }
+  return TQ_OK;
+}
+
+void free_rotation(tq_rotation_s* r) {
+  if (!r) return;
+  if (r->r32_dev) hipFree(r->r32_dev);
+  if (r->frag_dev) hipFree(r->frag_dev);
+  delete r;
+}
+
+void free_qjl(tq_qjl_s* q) {
+  if (!q) return;
+  if (q->s32_dev) hipFree(q->s32_dev);
+  if (q->frag_dev) hipFree(q->frag_dev);
+  delete q;
+}
+
+tq_status finish_rotation(tq_rotation_s* r) {
+  const int d = r->d;
+  std::vector<float> r32((size_t)d * d);
+  for (size_t i = 0; i < r32.size(); ++i) r32[i] = (float)r->r[i];
+  tq_status st = upload(r32, &r->r32_dev, "upload rotation");
+  if (st != TQ_OK) return st;
+  if (d == tq::kFragD) {
+    std::vector<uint16_t> frag;
+    if (r->kind == TQ_ROT_WHT) {
+      // sqrt(d) R = H diag(sigma) has entries +-1: exact in bf16, one pass, scale after.
+      build_fragments(r->r.data(), std::sqrt((double)d), frag);
+      r->passes = 1;
+      r->post_scale = (float)(1.0 / std::sqrt((double)d));
+    } else {
+      build_fragments(r->r.data(), 1.0, frag);
+      r->passes = 2;
+      r->post_scale = 1.0f;
+    }
+    st = upload(frag, &r->frag_dev, "upload rotation fragments");
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
+tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* out) {
+  auto* q = new (std::nothrow) tq_qjl_s();
+  if (!q) return fail(TQ_ENOMEM, "host allocation failed");
+  q->d = d;
+  q->rot_id = rot->id;
+  q->s = std::move(s);
+  hipGetDevice(&q->device);
+  std::vector<float> s32((size_t)d * d);
+  for (size_t i = 0; i < s32.size(); ++i) s32[i] = (float)q->s[i];
+  tq_status st = upload(s32, &q->s32_dev, "upload qjl");
+  if (st == TQ_OK && d == tq::kFragD) {
+    // S' = S R^T in fp64
+    std::vector<double> sp((size_t)d * d, 0.0);
+    const double* sm = q->s.data();
+    const double* rm = rot->r.data();
+    parallel_for(0, d, 8, [&](int64_t i) {
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += sm[(size_t)i * d + k] * rm[(size_t)j * d + k];
+        sp[(size_t)i * d + j] = acc;
+      }
+    });
+    std::vector<uint16_t> frag;
+    build_fragments(sp.data(), 1.0, frag);
+    st = upload(frag, &q->frag_dev, "upload qjl fragments");
+  }
+  if (st != TQ_OK) {
+    free_qjl(q);
+    return st;
+  }
+  *out = q;
+  return ok();
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+tq_status check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_host_splitmix64(uint64_t seed, uint64_t offset, int64_t n, uint64_t* out_host) {
+  if (n < 0 || (n > 0 && !out_host)) return fail(TQ_EINVAL, "tq_host_splitmix64: bad arguments");
+  for (int64_t i = 0; i < n; ++i) out_host[i] = draw(seed, offset + (uint64_t)i);
+  return ok();
+}
+
+tq_status tq_host_gaussian(uint64_t seed, int64_t n, double* out_host) {
+  if (n < 0 || (n > 0 && !out_host)) return fail(TQ_EINVAL, "tq_host_gaussian: bad arguments");
+  gaussian_fill(seed, n, out_host);
+  return ok();
+}
+
+tq_status tq_host_codebook(int d, int b, tq_density dens, double* c_host, double* t_host) {
+  if (d < 2 || b < 1 || b > tq::kMaxBits || !c_host || !t_host ||
+      (dens != TQ_DENSITY_BETA && dens != TQ_DENSITY_GAUSS))
+    return fail(TQ_EINVAL, "tq_host_codebook: need d >= 2, 1 <= b <= 4, valid density, outputs");
+  lloyd_codebook(d, b, dens, c_host, t_host);
+  return ok();
+}
+
+tq_status tq_host_rotation(int d, uint64_t seed, tq_rot_kind kind, double* r_host) {
+  if (d < 2 || !r_host) return fail(TQ_EINVAL, "tq_host_rotation: need d >= 2 and an output");
+  if (kind == TQ_ROT_WHT) {
+    if (!is_pow2(d)) return fail(TQ_EUNSUPPORTED, "tq_host_rotation: Hadamard needs d = 2^k (d=%d)", d);
+    hadamard_rotation(d, seed, r_host);
+    return ok();
+  }
+  if (kind != TQ_ROT_DENSE) return fail(TQ_EINVAL, "tq_host_rotation: bad kind");
+  std::vector<double> g((size_t)d * d);
+  gaussian_fill(seed, (int64_t)d * d, g.data());
+  qr_rotation(d, g.data(), r_host);
+  return ok();
+}
+
+tq_status tq_host_qjl_matrix(int d, uint64_t seed, double* s_host) {
+  if (d < 2 || !s_host) return fail(TQ_EINVAL, "tq_host_qjl_matrix: need d >= 2 and an output");
+  gaussian_fill(seed, (int64_t)d * d, s_host);
+  return ok();
+}
+
+tq_status tq_codebook(int d, int b, tq_density dens, tq_codebook_t* out) {
+  if (!out) return fail(TQ_EINVAL, "tq_codebook: null output");
+  auto* cb = new (std::nothrow) tq_codebook_s();
+  if (!cb) return fail(TQ_ENOMEM, "host allocation failed");
+  tq_status st = tq_host_codebook(d, b, dens, cb->c, cb->t);
+  if (st != TQ_OK) {
+    delete cb;
+    return st;
+  }
+  cb->d = d;
+  cb->b = b;
+  fill_args(cb);
+  *out = cb;
+  return ok();
+}
+
+tq_status tq_codebook_from_values(int d, int b, const double* c_host, tq_codebook_t* out) {
+  if (!out || !c_host || b < 1 || b > tq::kMaxBits || d < 1)
+    return fail(TQ_EINVAL, "tq_codebook_from_values: bad arguments");
+  const int k = 1 << b;
+  for (int i = 0; i + 1 < k; ++i)
+    if (!(c_host[i] < c_host[i + 1])) return fail(TQ_EINVAL, "centroids must be strictly increasing");
+  auto* cb = new (std::nothrow) tq_codebook_s();
+  if (!cb) return fail(TQ_ENOMEM, "host allocation failed");
+  cb->d = d;
+  cb->b = b;
+  for (int i = 0; i < k; ++i) cb->c[i] = c_host[i];
+  for (int i = 0; i + 1 < k; ++i) cb->t[i] = 0.5 * (c_host[i] + c_host[i + 1]);
+  fill_args(cb);
+  *out = cb;
+  return ok();
+}
+
+tq_status tq_codebook_values(tq_codebook_t cb, double* c_host, double* t_host) {
+  if (!cb || !c_host || !t_host) return fail(TQ_EINVAL, "tq_codebook_values: bad arguments");
+  const int k = 1 << cb->b;
+  for (int i = 0; i < k; ++i) c_host[i] = cb->c[i];
+  for (int i = 0; i + 1 < k; ++i) t_host[i] = cb->t[i];
+  return ok();
+}
+
+void tq_codebook_free(tq_codebook_t cb) { delete cb; }
+
+tq_status tq_make_rotation(int d, uint64_t seed, tq_rot_kind kind, tq_rotation_t* out) {
+  if (!out) return fail(TQ_EINVAL, "tq_make_rotation: null output");
+  if (d < 2 || d > 8192) return fail(TQ_EUNSUPPORTED, "tq_make_rotation: d=%d out of range", d);
+  auto* r = new (std::nothrow) tq_rotation_s();
+  if (!r) return fail(TQ_ENOMEM, "host allocation failed");
+  r->d = d;
+  r->kind = kind;
+  r->id = g_next_id++;
+  hipGetDevice(&r->device);
+  r->r.resize((size_t)d * d);
+  tq_status st = tq_host_rotation(d, seed, kind, r->r.data());
+  if (st == TQ_OK) st = finish_rotation(r);
+  if (st != TQ_OK) {
+    free_rotation(r);
+    return st;
+  }
+  *out = r;
+  return ok();
+}
+
+tq_status tq_rotation_from_matrix(int d, const double* r_host, tq_rotation_t* out) {
+  if (!out || !r_host || d < 1) return fail(TQ_EINVAL, "tq_rotation_from_matrix: bad arguments");
+  auto* r = new (std::nothrow) tq_rotation_s();
+  if (!r) return fail(TQ_ENOMEM, "host allocation failed");
+  r->d = d;
+  r->kind = TQ_ROT_DENSE;
+  r->id = g_next_id++;
+  hipGetDevice(&r->device);
+  r->r.assign(r_host, r_host + (size_t)d * d);
+  tq_status st = finish_rotation(r);
+  if (st != TQ_OK) {
+    free_rotation(r);
+    return st;
+  }
+  *out = r;
+  return ok();
+}
+
+tq_status tq_rotation_export(tq_rotation_t rot, double* r_host) {
+  if (!rot || !r_host) return fail(TQ_EINVAL, "tq_rotation_export: bad arguments");
+  std::memcpy(r_host, rot->r.data(), rot->r.size() * sizeof(double));
+  return ok();
+}
+
+void tq_rotation_free(tq_rotation_t rot) { free_rotation(rot); }
+
+tq_status tq_make_qjl(int d, uint64_t seed, tq_rotation_t rot, tq_qjl_t* out) {
+  if (!out || !rot) return fail(TQ_EINVAL, "tq_make_qjl: bad arguments");
+  if (rot->d != d) return fail(TQ_ESHAPE, "tq_make_qjl: d=%d but rotation has d=%d", d, rot->d);
+  std::vector<double> s((size_t)d * d);
+  gaussian_fill(seed, (int64_t)d * d, s.data());
+  return make_qjl(d, std::move(s), rot, out);
+}
+
+tq_status tq_qjl_from_matrix(int d, const double* s_host, tq_rotation_t rot, tq_qjl_t* out) {
+  if (!out || !rot || !s_host) return fail(TQ_EINVAL, "tq_qjl_from_matrix: bad arguments");
+  if (rot->d != d) return fail(TQ_ESHAPE, "tq_qjl_from_matrix: d=%d but rotation has d=%d", d, rot->d);
+  std::vector<double> s(s_host, s_host + (size_t)d * d);
+  return make_qjl(d, std::move(s), rot, out);
+}
+
+void tq_qjl_free(tq_qjl_t qjl) { free_qjl(qjl); }
+
+size_t tq_packed_words(int d, int bits) {
+  if (d <= 0 || bits <= 0 || ((int64_t)d * bits) % 32 != 0) return 0;
+  return (size_t)d * bits / 32;
+}
+
+static tq_status check_packed(const tq_packed* p, int d, int bits, int mode, const char* fn) {
+  if (!p) return fail(TQ_EINVAL, "%s: null packed descriptor", fn);
+  if (p->d != d) return fail(TQ_ESHAPE, "%s: packed d=%d, expected %d", fn, p->d, d);
+  if (p->bits != bits) return fail(TQ_ESHAPE, "%s: packed bits=%d, codebook has %d", fn, p->bits, bits);
+  if (p->mode != mode) return fail(TQ_EINVAL, "%s: packed mode mismatch", fn);
+  if (p->reserved != 0) return fail(TQ_EINVAL, "%s: reserved field must be 0", fn);
+  if (p->n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
+  if (p->n > 0 && (!p->idx || !p->norms)) return fail(TQ_EINVAL, "%s: null idx/norms", fn);
+  if (mode == TQ_MODE_PROD && p->n > 0 && (!p->qjl || !p->rnorms))
+    return fail(TQ_EINVAL, "%s: prod needs qjl and rnorms buffers", fn);
+  return TQ_OK;
+}
+
+tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_mode mode,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* out,
+                    void* stream) {
+  static const char* fn = "tq_encode";
+  if (!cb || !rot || !out) return fail(TQ_EINVAL, "%s: null handle or output", fn);
+  if (n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
+  if (n > 0 && !x_dev) return fail(TQ_EINVAL, "%s: null input", fn);
+  if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_EUNSUPPORTED, "%s: dtype must be f32 or bf16", fn);
+  if (mode != TQ_MODE_MSE && mode != TQ_MODE_PROD) return fail(TQ_EINVAL, "%s: bad mode", fn);
+  const int stage = mode == TQ_MODE_PROD ? b - 1 : b;
+  if (stage < 1 || stage > tq::kMaxBits) return fail(TQ_EINVAL, "%s: bits b=%d invalid for this mode", fn, b);
+  if (cb->b != stage) return fail(TQ_ESHAPE, "%s: codebook has %d bits, mode needs %d", fn, cb->b, stage);
+  if (cb->d != d || rot->d != d) return fail(TQ_ESHAPE, "%s: d=%d, codebook d=%d, rotation d=%d", fn, d, cb->d, rot->d);
+  if (((int64_t)d * stage) % 32 != 0) return fail(TQ_ESHAPE, "%s: d*bits must be a multiple of 32", fn);
+  if (mode == TQ_MODE_PROD) {
+    if (!qjl) return fail(TQ_EINVAL, "%s: prod mode needs a qjl handle", fn);
+    if (qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
+    if (qjl->rot_id != rot->id) return fail(TQ_EINVAL, "%s: qjl handle is bound to another rotation", fn);
+  } else if (qjl) {
+    return fail(TQ_EINVAL, "%s: qjl handle given for MSE mode", fn);
+  }
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (fused path covers d=128)", fn, d);
+  if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the fused encode needs an antisymmetric codebook", fn);
+  tq_status st = check_packed(out, d, stage, mode, fn);
+  if (st != TQ_OK) return st;
+  if (out->n != n) return fail(TQ_ESHAPE, "%s: out->n=%lld, n=%lld", fn, (long long)out->n, (long long)n);
+  if (n == 0) return ok();
+  return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, mode == TQ_MODE_PROD ? qjl : nullptr,
+                                             cb->args, out->idx, out->norms,
+                                             mode == TQ_MODE_PROD ? out->qjl : nullptr,
+                                             mode == TQ_MODE_PROD ? out->rnorms : nullptr, nullptr,
+                                             as_stream(stream)),
+                      fn);
+}
+
+tq_status tq_rotate(const void* x_dev, tq_dtype dt, int64_t n, int d, tq_rotation_t rot,
+                    float* y_dev, float* norms_dev, void* stream) {
+  static const char* fn = "tq_rotate";
+  if (!rot) return fail(TQ_EINVAL, "%s: null rotation", fn);
+  if (n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
+  if (n > 0 && (!x_dev || !y_dev || !norms_dev)) return fail(TQ_EINVAL, "%s: null buffer", fn);
+  if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_EUNSUPPORTED, "%s: dtype must be f32 or bf16", fn);
+  if (rot->d != d) return fail(TQ_ESHAPE, "%s: rotation d=%d, d=%d", fn, rot->d, d);
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported", fn, d);
+  if (n == 0) return ok();
+  tq::CodebookArgs none{};
+  none.bits = 1;
+  return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, nullptr, none, nullptr, norms_dev,
+                                             nullptr, nullptr, y_dev, as_stream(stream)),
+                      fn);
+}
+
+tq_status tq_quantize_rotated(const float* y_dev, int64_t n, int d, tq_codebook_t cb,
+                              uint32_t* idx_dev, void* stream) {
+  static const char* fn = "tq_quantize_rotated";
+  if (!cb) return fail(TQ_EINVAL, "%s: null codebook", fn);
+  if (n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
+  if (n > 0 && (!y_dev || !idx_dev)) return fail(TQ_EINVAL, "%s: null buffer", fn);
+  if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, d=%d", fn, cb->d, d);
+  if (d % 32 != 0) return fail(TQ_ESHAPE, "%s: d must be a multiple of 32", fn);
+  if (n == 0) return ok();
+  return check_launch(tq::launch_quantize_rotated(y_dev, n, d, cb->args, idx_dev, as_stream(stream)), fn);
+}
+
+tq_status tq_decode(const tq_packed* p, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl,
+                    float* xhat_dev, void* stream) {
+  static const char* fn = "tq_decode";
+  if (!p || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
+  tq_status st = check_packed(p, rot->d, cb->b, p->mode, fn);
+  if (st != TQ_OK) return st;
+  if (p->mode != TQ_MODE_MSE && p->mode != TQ_MODE_PROD) return fail(TQ_EINVAL, "%s: bad mode", fn);
+  if (cb->d != p->d) return fail(TQ_ESHAPE, "%s: codebook d=%d, packed d=%d", fn, cb->d, p->d);
+  if (((int64_t)p->d * p->bits) % 32 != 0 || p->d % 32 != 0) return fail(TQ_ESHAPE, "%s: d*bits must be a multiple of 32", fn);
+  if (qjl) {
+    if (p->mode != TQ_MODE_PROD) return fail(TQ_EINVAL, "%s: qjl given for MSE data", fn);
+    if (qjl->d != p->d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
+  }
+  if (p->n > 0 && !xhat_dev) return fail(TQ_EINVAL, "%s: null output", fn);
+  if (p->n == 0) return ok();
+  return check_launch(tq::launch_decode(p, cb->args, rot, qjl, xhat_dev, as_stream(stream)), fn);
+}
+
+size_t tq_scores_workspace(int B, int Hq, int d) {
+  if (B < 0 || Hq < 0 || d <= 0) return 0;
+  return tq::scores_workspace_bytes(B, Hq, d);
+}
+
+tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
+                    void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_scores";
+  if (!K || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  const int ratio = Hq / Hkv;
+  if (ratio > 4 && ratio % 4 != 0) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d must be <= 4 or a multiple of 4", fn, ratio);
+  if (ratio > 64) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d above 64", fn, ratio);
+  if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv=%lld above 65535", fn, (long long)B * Hkv);
+  const int d = rot->d;
+  tq_status st = check_packed(K, d, cb->b, K->mode, fn);
+  if (st != TQ_OK) return st;
+  if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, rotation d=%d", fn, cb->d, d);
+  if (K->n != (int64_t)B * Hkv * T) return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*T=%lld", fn, (long long)K->n, (long long)B * Hkv * T);
+  if (K->mode == TQ_MODE_PROD) {
+    if (!qjl) return fail(TQ_EINVAL, "%s: prod keys need the qjl handle", fn);
+    if (qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
+  } else if (K->mode == TQ_MODE_MSE) {
+    if (qjl) return fail(TQ_EINVAL, "%s: qjl handle given for MSE keys", fn);
+  } else {
+    return fail(TQ_EINVAL, "%s: bad mode", fn);
+  }
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if ((int64_t)B * Hq * T == 0) return ok();
+  if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
+  size_t need = tq::scores_workspace_bytes(B, Hq, d);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_scores(q_dev, B, Hq, Hkv, T, K, cb->args, rot, qjl, scores_dev, ws_dev,
+                                        as_stream(stream)),
+                      fn);
+}
+
+}  // extern "C"

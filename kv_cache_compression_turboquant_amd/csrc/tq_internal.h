@@ -1,0 +1,85 @@
+// Internal definitions shared by the host setup code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxBits = 4;
+constexpr int kMaxCentroids = 1 << kMaxBits;
+constexpr double kQjlConst = 1.2533141373155002512;  // sqrt(pi / 2)
+
+// Codebook values handed to kernels by value (they live in the kernel argument segment).
+struct CodebookArgs {
+  float c[kMaxCentroids];  // centroids, fp32 rounded to nearest from fp64
+  float t[kMaxCentroids];  // thresholds t[0 .. K-2]; t[K-1 ..] = +inf padding
+  int bits;
+  int sym;                 // 1 when exactly antisymmetric in fp32 (c[K-1-k] = -c[k], middle t = 0)
+  // Sign-magnitude form used by the fused encode when sym: the K/2 - 1 positive thresholds as
+  // their fp32 bit patterns and the K/2 non-negative centroids.
+  int tpos[kMaxCentroids / 2];
+  float cpos[kMaxCentroids / 2];
+};
+
+// MFMA A-operand fragments of a d x d matrix for the fused d = 128 kernels, bf16 bits.
+// Element [pass][cb][s][lane][e] = M[32*(m/4) + 4*cb + (m%4)][32*g + 8*s + e],
+// m = lane % 16, g = lane / 16; pass 0 = round-to-nearest bf16 of M, pass 1 = bf16 of the
+// remainder.  Output block cb, lane group G and register r of the product then hold output
+// coordinate 32*G + 4*cb + r (so one lane holds 32 consecutive output coordinates).
+constexpr int kFragD = 128;
+constexpr int kFragElems = 8 * 4 * 64 * 8;  // per pass, = 128 * 128
+
+}  // namespace tq
+
+struct tq_codebook_s {
+  int d;
+  int b;
+  double c[tq::kMaxCentroids];
+  double t[tq::kMaxCentroids];
+  tq::CodebookArgs args;
+};
+
+struct tq_rotation_s {
+  int d;
+  int kind;                 // tq_rot_kind
+  int device;
+  uint64_t id;
+  std::vector<double> r;    // fp64 R, row-major
+  float* r32_dev = nullptr;       // fp32 R, row-major [d, d]
+  uint16_t* frag_dev = nullptr;   // bf16 fragments [2][kFragElems] (d = 128 only)
+  int passes = 2;                 // 1 when R is exactly representable after scaling
+  float post_scale = 1.0f;        // y = post_scale * (fragments . x)
+};
+
+struct tq_qjl_s {
+  int d;
+  int device;
+  uint64_t rot_id;
+  std::vector<double> s;    // fp64 S, row-major
+  float* s32_dev = nullptr;       // fp32 S, row-major [d, d]
+  uint16_t* frag_dev = nullptr;   // bf16 fragments of S' = S R^T [2][kFragElems] (d = 128)
+};
+
+namespace tq {
+
+// Launchers (tq_kernels.hip).  All return the HIP error of the launch.
+hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                              const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx,
+                              float* norms, uint32_t* qjl_bits, float* rnorms, float* y_out,
+                              hipStream_t st);
+hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const CodebookArgs& cb,
+                                   uint32_t* idx, hipStream_t st);
+hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
+                         const tq_qjl_s* qjl, float* xhat, hipStream_t st);
+hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                         float* scores, void* ws, hipStream_t st);
+size_t scores_workspace_bytes(int B, int Hq, int d);
+
+}  // namespace tq

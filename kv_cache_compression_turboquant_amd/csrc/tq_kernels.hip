@@ -1,0 +1,723 @@
+// HIP kernels for gfx950 (MI355X): fused TurboQuant encode at d = 128, the reference
+// quantizer, decode, the query prologue and the compressed-key score kernel.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_{bf16,f16}): lane l = n + 16 g (n = l % 16,
+// g = l / 16) holds A row n, B column n and D column n.  Within one instruction, element e of
+// lane group g covers contraction slot 8 g + e for both A and B, and register r of D holds row
+// 4 g + r.  Every contraction here is over vector coordinates, and the kernels assign
+// coordinate 32 g + 8 s + e to element e of lane group g in instruction s (s = 0..3 for
+// d = 128), identically for both operands, so each lane streams 32 consecutive coordinates.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kQjl = 1.2533141373155002512f;  // sqrt(pi / 2)
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// idx = #{k : y >= t_k} over the 2^BITS - 1 thresholds (ties go to the upper index).
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize(float y, const CodebookArgs& cb) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (int k = 0; k < (1 << BITS) - 1; ++k) idx += (y >= cb.t[k]) ? 1u : 0u;
+  return idx;
+}
+
+// Same, also returning the centroid C[idx].
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize_c(float y, const CodebookArgs& cb, float& c) {
+  uint32_t idx = 0;
+  c = cb.c[0];
+#pragma unroll
+  for (int k = 0; k < (1 << BITS) - 1; ++k) {
+    bool ge = y >= cb.t[k];
+    idx += ge ? 1u : 0u;
+    c = ge ? cb.c[k + 1] : c;
+  }
+  return idx;
+}
+
+// Pack 32 BITS-bit indices (local order) into BITS words, LSB-first stream.
+template <int BITS>
+__device__ __forceinline__ void pack32(const uint32_t (&idx)[32], uint32_t (&w)[BITS]) {
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) w[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int p = BITS * i, wi = p >> 5, sh = p & 31;
+    w[wi] |= idx[i] << sh;
+    if (sh + BITS > 32) w[wi + 1] |= idx[i] >> (32 - sh);
+  }
+}
+
+// Sign-magnitude bucketize for an antisymmetric codebook (cb.sym): with m the number of
+// positive thresholds below |y| (<= for y >= 0, < for y < 0), idx = K/2 + m for y >= 0 and
+// K/2 - 1 - m for y < 0.  This equals #{k : y >= t_k} exactly, including ties and -0.0.
+// Also returns the centroid sign(y) * cpos[m].
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize_sym(float y, const CodebookArgs& cb, float& c) {
+  constexpr int H = 1 << (BITS - 1);
+  const bool neg = y < 0.f;
+  const int a = (int)(__float_as_uint(y) & 0x7fffffffu) - (neg ? 1 : 0);
+  uint32_t m = 0;
+  float mag = cb.cpos[0];
+#pragma unroll
+  for (int p = 0; p < H - 1; ++p) {
+    const bool ge = a >= cb.tpos[p];
+    m += ge ? 1u : 0u;
+    mag = ge ? cb.cpos[p + 1] : mag;
+  }
+  c = neg ? -mag : mag;
+  return neg ? (uint32_t)(H - 1) - m : (uint32_t)H + m;
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused encode, d = 128.  One wave computes y^T = R x^T for NT tiles of 16 vectors:
+// A = rotation fragments (LDS), B = x (registers, straight from HBM), D = y^T.  Lane (n, G)
+// ends with coordinates 32 G .. 32 G + 31 of vector n, bucketizes them and writes BITS packed
+// words (its aligned share of the row).  PROD runs a second product Z^T = S' R_res^T on the
+// rotated-domain residual, whose B operand is exactly the lane's own registers.
+// The fragment loops are software pipelined: block c + 1's fragments are read from LDS while
+// block c's MFMAs run; scheduling barriers keep the compiler from hoisting every read.
+// ---------------------------------------------------------------------------------------
+constexpr int kFragU4 = kFragElems * 2 / 16;  // u32x4 per pass = 2048
+
+// MSE: 4 waves per block, two blocks per CU (<= 64 KB LDS each).  PROD keeps R and S' in LDS
+// (up to 128 KB, one block per CU) and runs 8 waves per block instead.
+template <bool PROD>
+struct EncShape {
+  static constexpr int kWaves = PROD ? 8 : 4;
+  static constexpr int kBlocksPerCU = PROD ? 1 : 2;
+};
+
+template <int P>
+__device__ __forceinline__ void load_frags(const u32x4* lds, int c, int lane, u32x4 (&a)[P][4]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[p][s] = lds[p * kFragU4 + (c * 4 + s) * 64 + lane];
+}
+
+template <int BITS, bool PROD, bool BF16IN, bool STORE_Y, int PASSES, int NT>
+__global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlocksPerCU) void k_encode_d128(
+    const void* __restrict__ x, int64_t n, const u32x4* __restrict__ frag_r,
+    const u32x4* __restrict__ frag_s, float post_scale, CodebookArgs cb,
+    uint32_t* __restrict__ idx_out, float* __restrict__ norms_out, uint32_t* __restrict__ qjl_out,
+    float* __restrict__ rnorm_out, float* __restrict__ y_out) {
+  constexpr int RP = PASSES;              // rotation passes held in LDS
+  constexpr int SP = PROD ? 2 : 0;        // S' passes
+  constexpr int kWaves = EncShape<PROD>::kWaves;
+  __shared__ u32x4 lds[(RP + SP) * kFragU4];
+  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = frag_r[i];
+  if constexpr (PROD) {
+    for (int i = threadIdx.x; i < SP * kFragU4; i += blockDim.x) lds[RP * kFragU4 + i] = frag_s[i];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int64_t ntiles = (n + 15) >> 4;
+  const int64_t stride = (int64_t)gridDim.x * kWaves * NT;
+
+  for (int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * NT; t0 < ntiles; t0 += stride) {
+    u32x4 bx[NT][4];      // bf16 x (or its hi part) for the 4 instructions
+    u32x4 bxl[NT][4];     // bf16 low part of fp32 x
+    float ss[NT];
+    int64_t rows[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = (t0 + t) * 16 + nl;
+      rows[t] = row;
+      const int64_t lrow = row < n ? row : n - 1;
+      float acc2 = 0.f;
+      if constexpr (BF16IN) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(x) + lrow * 128 + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u32x4 v = src[s];
+          bx[t][s] = v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xffff0000u);
+            acc2 += lo * lo + hi * hi;
+          }
+        }
+      } else {
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + lrow * 128 + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          f32x4 a = src[2 * s], b = src[2 * s + 1];
+          float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+          u32x4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t h0 = bf16_bits(v[2 * j]), h1 = bf16_bits(v[2 * j + 1]);
+            uint32_t l0 = bf16_bits(v[2 * j] - bf16_val(h0)), l1 = bf16_bits(v[2 * j + 1] - bf16_val(h1));
+            hi[j] = h0 | (h1 << 16);
+            lo[j] = l0 | (l1 << 16);
+            acc2 += v[2 * j] * v[2 * j] + v[2 * j + 1] * v[2 * j + 1];
+          }
+          bx[t][s] = hi;
+          bxl[t][s] = lo;
+        }
+      }
+      ss[t] = acc2;
+    }
+
+    // y^T blocks: acc[t][c] holds rows 32 G + 4 c + r of tile t
+    f32x4 acc[NT][8];
+    {
+      u32x4 cur[RP][4], nxt[RP][4];
+      load_frags<RP>(lds, 0, lane, cur);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c + 1 < 8) load_frags<RP>(lds, c + 1, lane, nxt);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            a = mfma_bf16(cur[0][s], bx[t][s], a);
+            if constexpr (!BF16IN) a = mfma_bf16(cur[0][s], bxl[t][s], a);
+            if constexpr (RP == 2) a = mfma_bf16(cur[1][s], bx[t][s], a);
+          }
+          acc[t][c] = a;
+        }
+        if (c + 1 < 8) {
+#pragma unroll
+          for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cur[p][s] = nxt[p][s];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float sq = ss[t];
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const float nrm = sqrtf(sq);
+      const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
+      const float scale = post_scale * inv;
+      const int64_t row = rows[t];
+      const bool valid = row < n;
+      if (valid && g == 0 && norms_out) norms_out[row] = nrm;
+      if constexpr (STORE_Y) {
+        if (valid) {
+          f32x4* dst = reinterpret_cast<f32x4*>(y_out + row * 128 + 32 * g);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) dst[c] = acc[t][c] * scale;
+        }
+      } else {
+        // bucketize and pack on the fly; PROD also forms the residual's bf16 hi/lo B operand
+        // (element e of instruction s = local coordinate 8 s + e = 4 c + r with c = 2 s + e / 4).
+        uint32_t w[BITS];
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) w[j] = 0;
+        u32x4 rh[4], rl[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int rp = 0; rp < 2; ++rp) {
+            uint32_t id[2];
+            float res[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float yv = acc[t][c][2 * rp + q] * scale;
+              float cv;
+              id[q] = bucketize_sym<BITS>(yv, cb, cv);
+              if constexpr (PROD) {
+                res[q] = nrm > 0.f ? yv - cv : 0.f;
+                rs += res[q] * res[q];
+              }
+              const int li = 4 * c + 2 * rp + q;
+              const int p = BITS * li, wi = p >> 5, sh = p & 31;
+              w[wi] |= id[q] << sh;
+              if (sh + BITS > 32) w[wi + 1] |= id[q] >> (32 - sh);
+            }
+            if constexpr (PROD) {
+              const uint32_t h0 = bf16_bits(res[0]), h1 = bf16_bits(res[1]);
+              const uint32_t l0 = bf16_bits(res[0] - bf16_val(h0)), l1 = bf16_bits(res[1] - bf16_val(h1));
+              rh[c >> 1][2 * (c & 1) + rp] = h0 | (h1 << 16);
+              rl[c >> 1][2 * (c & 1) + rp] = l0 | (l1 << 16);
+            }
+          }
+        if (valid) {
+          uint32_t* dst = idx_out + row * (4 * BITS) + BITS * g;
+#pragma unroll
+          for (int j = 0; j < BITS; ++j) dst[j] = w[j];
+        }
+        if constexpr (PROD) {
+          uint32_t bits = 0;
+          const u32x4* sl = lds + RP * kFragU4;
+          u32x4 cur[2][4], nxt[2][4];
+          load_frags<2>(sl, 0, lane, cur);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            if (c + 1 < 8) load_frags<2>(sl, c + 1, lane, nxt);
+            f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              z = mfma_bf16(cur[0][s], rh[s], z);
+              z = mfma_bf16(cur[0][s], rl[s], z);
+              z = mfma_bf16(cur[1][s], rh[s], z);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bits |= (z[r] >= 0.f ? 1u : 0u) << (4 * c + r);
+            if (c + 1 < 8) {
+#pragma unroll
+              for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) cur[p][s] = nxt[p][s];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          rs += __shfl_xor(rs, 16);
+          rs += __shfl_xor(rs, 32);
+          if (valid) {
+            qjl_out[row * 4 + g] = bits;
+            if (g == 0) rnorm_out[row] = nrm * sqrtf(rs);
+          }
+        }
+      }
+    }
+  }
+}
+
+int g_num_cus[64] = {0};
+
+int num_cus() {
+  int dev = 0;
+  hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) return 256;
+  if (!g_num_cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_num_cus[dev] = v;
+  }
+  return g_num_cus[dev];
+}
+
+template <int BITS, bool PROD, bool BF16IN, bool STORE_Y, int PASSES>
+hipError_t enc_launch(const void* x, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                      const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits,
+                      float* rnorms, float* y, hipStream_t st) {
+  constexpr int NT = PROD ? 1 : 2;
+  constexpr int kWaves = EncShape<PROD>::kWaves;
+  (void)kWaves;
+  const int64_t ntiles = (n + 15) / 16;
+  const int64_t per_block = (int64_t)kWaves * NT;
+  int64_t blocks = (ntiles + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)num_cus() * EncShape<PROD>::kBlocksPerCU;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((k_encode_d128<BITS, PROD, BF16IN, STORE_Y, PASSES, NT>), dim3((unsigned)blocks),
+                     dim3(kWaves * 64), 0, st, x, n,
+                     reinterpret_cast<const u32x4*>(rot->frag_dev),
+                     reinterpret_cast<const u32x4*>(qjl ? qjl->frag_dev : nullptr), rot->post_scale, cb, idx,
+                     norms, qbits, rnorms, y);
+  return hipGetLastError();
+}
+
+template <int BITS, bool PROD, bool STORE_Y>
+hipError_t enc_dispatch_in(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                           const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                           uint32_t* qbits, float* rnorms, float* y, hipStream_t st) {
+  if (bf16) {
+    if (rot->passes == 1)
+      return enc_launch<BITS, PROD, true, STORE_Y, 1>(x, n, rot, qjl, cb, idx, norms, qbits, rnorms, y, st);
+    return enc_launch<BITS, PROD, true, STORE_Y, 2>(x, n, rot, qjl, cb, idx, norms, qbits, rnorms, y, st);
+  }
+  if (rot->passes == 1)
+    return enc_launch<BITS, PROD, false, STORE_Y, 1>(x, n, rot, qjl, cb, idx, norms, qbits, rnorms, y, st);
+  return enc_launch<BITS, PROD, false, STORE_Y, 2>(x, n, rot, qjl, cb, idx, norms, qbits, rnorms, y, st);
+}
+
+// ---------------------------------------------------------------------------------------
+// Reference quantizer: bucketize + pack fp32 rotated coordinates, one thread per
+// (row, 32-coordinate group).
+// ---------------------------------------------------------------------------------------
+template <int BITS>
+__global__ void k_quantize_rotated(const float* __restrict__ y, int64_t n, int d, CodebookArgs cb,
+                                   uint32_t* __restrict__ out) {
+  const int groups = d / 32;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * groups) return;
+  const int64_t row = i / groups;
+  const int grp = (int)(i % groups);
+  const f32x4* src = reinterpret_cast<const f32x4*>(y + row * d + 32 * grp);
+  uint32_t idx[32];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    f32x4 v = src[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) idx[4 * k + j] = bucketize<BITS>(v[j], cb);
+  }
+  uint32_t w[BITS];
+  pack32<BITS>(idx, w);
+  uint32_t* dst = out + row * ((int64_t)d * BITS / 32) + BITS * grp;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) dst[j] = w[j];
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode: x_hat = s R^T C[idx] (+ gamma sqrt(pi/2)/d S^T z).  One block per row.
+// ---------------------------------------------------------------------------------------
+__global__ void k_decode(const uint32_t* __restrict__ idx, const float* __restrict__ norms,
+                         const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, int d,
+                         int bits, CodebookArgs cb, const float* __restrict__ r32,
+                         const float* __restrict__ s32, float* __restrict__ out) {
+  extern __shared__ float sh[];  // [d] centroid values, [d] signs
+  const int64_t row = blockIdx.x;
+  const int words = d * bits / 32;
+  const uint32_t* w = idx + row * words;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    const int p = j * bits;
+    uint64_t win = w[p >> 5];
+    if ((p & 31) + bits > 32) win |= (uint64_t)w[(p >> 5) + 1] << 32;
+    const uint32_t id = (uint32_t)(win >> (p & 31)) & ((1u << bits) - 1u);
+    sh[j] = cb.c[id];
+    if (s32) sh[d + j] = ((qbits[row * (d / 32) + (j >> 5)] >> (j & 31)) & 1u) ? 1.f : -1.f;
+  }
+  __syncthreads();
+  const float s = norms[row];
+  const float gc = s32 ? rnorms[row] * kQjl / (float)d : 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float a = 0.f, b = 0.f;
+    for (int j = 0; j < d; ++j) a += r32[(int64_t)j * d + i] * sh[j];
+    if (s32)
+      for (int j = 0; j < d; ++j) b += s32[(int64_t)j * d + i] * sh[d + j];
+    out[row * d + i] = s * a + gc * b;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Query prologue: for each (batch, kv head) block, q_rot = R q and q_s = S q for the heads that
+// share the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][d], part = 0 rot hi,
+// 1 rot lo, 2 sketch hi, 3 sketch lo.
+// ---------------------------------------------------------------------------------------
+__global__ void k_qprep(const float* __restrict__ q, int Hq, int ratio, int d,
+                        const float* __restrict__ r32, const float* __restrict__ s32,
+                        uint16_t* __restrict__ ws) {
+  extern __shared__ float qs[];  // [ratio][d]
+  const int bg = blockIdx.x;     // b * Hkv + kvh
+  const int b = bg / (Hq / ratio), kvh = bg % (Hq / ratio);
+  const int h0 = kvh * ratio;
+  for (int i = threadIdx.x; i < ratio * d; i += blockDim.x)
+    qs[i] = q[((int64_t)b * Hq + h0 + i / d) * d + (i % d)];
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    for (int h = 0; h < ratio; ++h) {
+      float a = 0.f, c = 0.f;
+      const float* qh = qs + h * d;
+      for (int k = 0; k < d; ++k) a += r32[(int64_t)j * d + k] * qh[k];
+      if (s32)
+        for (int k = 0; k < d; ++k) c += s32[(int64_t)j * d + k] * qh[k];
+      uint16_t* o = ws + ((int64_t)b * Hq + h0 + h) * 4 * d;
+      const _Float16 ah = (_Float16)a;
+      const _Float16 al = (_Float16)(a - (float)ah);
+      o[j] = __builtin_bit_cast(uint16_t, ah);
+      o[d + j] = __builtin_bit_cast(uint16_t, al);
+      if (s32) {
+        const _Float16 ch = (_Float16)c;
+        const _Float16 cl = (_Float16)(c - (float)ch);
+        o[2 * d + j] = __builtin_bit_cast(uint16_t, ch);
+        o[3 * d + j] = __builtin_bit_cast(uint16_t, cl);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Compressed-key score, d = 128.  Grid (key chunk, b * Hkv).  D = A B with A = query slots
+// (16 rows: rot hi / rot lo / sketch hi / sketch lo for 4 heads), B = decoded keys (columns =
+// 16 keys), so lane (n, G) receives the four partial sums of key n for slot group G.  Keys are
+// decoded from whole packed words through LDS tables that map a field of F bits to F / BITS
+// fp16 centroids (F = 12 for 3 bits, else 8).
+// ---------------------------------------------------------------------------------------
+constexpr int kScoreWaves = 4;
+
+template <int BITS>
+struct DecodeTable {
+  static constexpr int F = BITS == 3 ? 12 : 8;
+  static constexpr int PER = F / BITS;             // coordinates per field
+  static constexpr int ENTRIES = 1 << F;
+  static constexpr int BYTES = ENTRIES * PER * 2;  // fp16 entries
+  static constexpr int FIELDS = 8 / PER;           // fields per instruction (8 coordinates)
+};
+
+template <int BITS>
+__device__ __forceinline__ u32x4 decode_keys(const uint32_t (&w)[BITS], int s, const uint8_t* tab) {
+  using DT = DecodeTable<BITS>;
+  u32x4 out;
+  if constexpr (BITS == 1) {
+    const uint32_t f = (w[0] >> (8 * s)) & 0xffu;
+    out = *reinterpret_cast<const u32x4*>(tab + f * 16);
+  } else if constexpr (BITS == 2) {
+    const uint32_t half = (w[s >> 1] >> (16 * (s & 1))) & 0xffffu;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + (half & 0xffu) * 8);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + (half >> 8) * 8);
+    out = u32x4{a[0], a[1], b[0], b[1]};
+  } else if constexpr (BITS == 3) {
+    const int off = 24 * s;
+    const uint64_t win = ((uint64_t)w[(off + 23) >> 5 < BITS ? (off + 23) >> 5 : BITS - 1] << 32) |
+                         w[off >> 5];
+    const uint32_t bits24 = (uint32_t)(win >> (off & 31)) & 0xffffffu;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + (bits24 & 0xfffu) * 8);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + (bits24 >> 12) * 8);
+    out = u32x4{a[0], a[1], b[0], b[1]};
+  } else {
+    const uint32_t word = w[s];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tab + ((word >> (8 * j)) & 0xffu) * 4);
+  }
+  (void)DT::ENTRIES;
+  return out;
+}
+
+template <int BITS, bool PROD>
+__global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
+    const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int tiles_per_wave,
+    const uint32_t* __restrict__ idx, const float* __restrict__ norms,
+    const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
+    float* __restrict__ scores) {
+  using DT = DecodeTable<BITS>;
+  __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stab[PROD ? 4096 : 16];
+  __shared__ _Float16 cent[16];
+  if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
+  __syncthreads();
+  for (int e = threadIdx.x; e < DT::ENTRIES; e += blockDim.x) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(tab + e * DT::PER * 2);
+#pragma unroll
+    for (int j = 0; j < DT::PER; ++j)
+      dst[j] = __builtin_bit_cast(uint16_t, cent[(e >> (BITS * j)) & ((1 << BITS) - 1)]);
+  }
+  if constexpr (PROD) {
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(stab + e * 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = ((e >> j) & 1) ? 0x3c00u : 0xbc00u;  // +1 / -1
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int ratio = Hq / Hkv;
+  const int groups = (ratio + 3) / 4;
+  const int64_t base_row = (int64_t)bg * T;
+  const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
+  const int64_t ntiles_seq = (T + 15) / 16;
+
+  // A operands for head group 0 (kept in registers).
+  auto load_a = [&](int hg, u32x4 (&am)[4], u32x4 (&aq)[4]) {
+    const int slot = nl;             // A row
+    const int hl = slot & 3;         // head within the group
+    const int part = slot >> 2;      // 0 rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo
+    const int h = 4 * hg + hl;
+    const bool live = h < ratio;
+    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (live ? h : 0)) * 4 + part) * 128 + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
+      if (!live) v = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      am[s] = part < 2 ? v : z;
+      aq[s] = (PROD && part >= 2) ? v : z;
+    }
+  };
+  u32x4 am0[4], aq0[4];
+  load_a(0, am0, aq0);
+
+  for (int64_t ti = 0; ti < tiles_per_wave; ++ti) {
+    const int64_t tile = tile0 + ti;
+    if (tile >= ntiles_seq) break;
+    const int64_t t = tile * 16 + nl;
+    const bool valid = t < T;
+    const int64_t row = base_row + (valid ? t : T - 1);
+    uint32_t w[BITS];
+    const uint32_t* src = idx + row * (4 * BITS) + BITS * g;
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) w[j] = src[j];
+    const float nrm = norms[row];
+    uint32_t zw = 0;
+    float gam = 0.f;
+    if constexpr (PROD) {
+      zw = qbits[row * 4 + g];
+      gam = rnorms[row] * (kQjl / 128.0f);
+    }
+    u32x4 bk[4], bz[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bk[s] = decode_keys<BITS>(w, s, tab);
+      if constexpr (PROD) bz[s] = *reinterpret_cast<const u32x4*>(stab + ((zw >> (8 * s)) & 0xffu) * 16);
+    }
+    for (int hg = 0; hg < groups; ++hg) {
+      u32x4 am[4], aq[4];
+      if (hg == 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { am[s] = am0[s]; aq[s] = aq0[s]; }
+      } else {
+        load_a(hg, am, aq);
+      }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc = mfma_f16(am[s], bk[s], acc);
+        if constexpr (PROD) acc = mfma_f16(aq[s], bz[s], acc);
+      }
+      const float sc = g < 2 ? nrm : gam;
+      const float v0 = acc[0] * sc, v1 = acc[1] * sc, v2 = acc[2] * sc, v3 = acc[3] * sc;
+      const bool lowg = g < 2;
+      float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
+      const float s0 = lowg ? v2 : v0, s1 = lowg ? v3 : v1;
+      k0 += __shfl_xor(s0, 32);
+      k1 += __shfl_xor(s1, 32);
+      const bool odd = g & 1;
+      float mine = odd ? k1 : k0;
+      const float other = odd ? k0 : k1;
+      mine += __shfl_xor(other, 16);
+      const int h = 4 * hg + g;
+      if (valid && h < ratio) scores[((int64_t)b * Hq + kvh * ratio + h) * T + t] = mine;
+    }
+  }
+}
+
+template <int BITS, bool PROD>
+hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                         float* scores, void* ws, hipStream_t st) {
+  const int ratio = Hq / Hkv;
+  const int d = 128;
+  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const int qthreads = 128;
+  hipLaunchKernelGGL(k_qprep, dim3(B * Hkv), dim3(qthreads), ratio * d * sizeof(float), st, q, Hq, ratio, d,
+                     rot->r32_dev, PROD ? qjl->s32_dev : nullptr, qws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (T + 15) / 16;
+  // enough blocks to fill the device about four times over
+  const int64_t target = (int64_t)num_cus() * 4;
+  const int64_t seqs = (int64_t)B * Hkv;
+  int64_t tpw = (tiles * seqs + target * kScoreWaves - 1) / (target * kScoreWaves);
+  if (tpw < 1) tpw = 1;
+  if (tpw > 64) tpw = 64;
+  const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
+  hipLaunchKernelGGL((k_scores_d128<BITS, PROD>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
+                     0, st, qws, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
+                     PROD ? K->rnorms : nullptr, cb, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                              const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx,
+                              float* norms, uint32_t* qjl_bits, float* rnorms, float* y_out,
+                              hipStream_t st) {
+  if (y_out) return enc_dispatch_in<1, false, true>(x, bf16, n, rot, nullptr, cb, nullptr, norms, nullptr, nullptr, y_out, st);
+  const bool prod = qjl != nullptr;
+  switch (cb.bits) {
+    case 1:
+      return prod ? enc_dispatch_in<1, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)
+                  : enc_dispatch_in<1, false, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st);
+    case 2:
+      return prod ? enc_dispatch_in<2, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)
+                  : enc_dispatch_in<2, false, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st);
+    case 3:
+      return prod ? enc_dispatch_in<3, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)
+                  : enc_dispatch_in<3, false, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st);
+    case 4:
+      return prod ? enc_dispatch_in<4, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)
+                  : enc_dispatch_in<4, false, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const CodebookArgs& cb,
+                                   uint32_t* idx, hipStream_t st) {
+  const int64_t work = n * (d / 32);
+  const int threads = 256;
+  const dim3 grid((unsigned)((work + threads - 1) / threads));
+  switch (cb.bits) {
+    case 1: hipLaunchKernelGGL(k_quantize_rotated<1>, grid, dim3(threads), 0, st, y, n, d, cb, idx); break;
+    case 2: hipLaunchKernelGGL(k_quantize_rotated<2>, grid, dim3(threads), 0, st, y, n, d, cb, idx); break;
+    case 3: hipLaunchKernelGGL(k_quantize_rotated<3>, grid, dim3(threads), 0, st, y, n, d, cb, idx); break;
+    case 4: hipLaunchKernelGGL(k_quantize_rotated<4>, grid, dim3(threads), 0, st, y, n, d, cb, idx); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
+                         const tq_qjl_s* qjl, float* xhat, hipStream_t st) {
+  const int d = p->d;
+  const int threads = d < 256 ? d : 256;
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)p->n), dim3(threads), 2 * d * sizeof(float), st, p->idx, p->norms,
+                     qjl ? p->qjl : nullptr, qjl ? p->rnorms : nullptr, d, p->bits, cb, rot->r32_dev,
+                     qjl ? qjl->s32_dev : nullptr, xhat);
+  return hipGetLastError();
+}
+
+size_t scores_workspace_bytes(int B, int Hq, int d) { return (size_t)B * Hq * 4 * d * sizeof(uint16_t); }
+
+hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                         float* scores, void* ws, hipStream_t st) {
+  const bool prod = K->mode == TQ_MODE_PROD;
+  switch (cb.bits) {
+    case 1: return prod ? scores_launch<1, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<1, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 2: return prod ? scores_launch<2, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<2, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 3: return prod ? scores_launch<3, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<3, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 4: return prod ? scores_launch<4, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<4, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

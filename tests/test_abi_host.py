@@ -1,0 +1,126 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol include/tq.h declares, and its
+host-side math (generator, QR rotation, Lloyd-Max codebook, QJL matrix) agrees with the oracle.
+No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import kv_cache_compression_turboquant_amd as tq
+    from kv_cache_compression_turboquant_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        pytest.fail("libtq.so is not built: run `python -m kv_cache_compression_turboquant_amd.build`")
+    return tq
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(tq):
+    from kv_cache_compression_turboquant_amd import _binding
+    raw = ctypes.CDLL(_binding.LIB_PATH)
+    names = _declared_functions()
+    assert len(names) >= 20
+    for name in names:
+        assert hasattr(raw, name), name
+        assert name in _binding.SIGNATURES, f"binding lacks {name}"
+    assert tq.lib().tq_abi_version() == 1
+
+
+def test_splitmix_bit_identical(tq):
+    for seed in (0, 1, 2, 12345, 2 ** 64 - 1):
+        np.testing.assert_array_equal(tq.host_splitmix64(seed, 1000, offset=7),
+                                      oracle.splitmix64(seed, 1000, offset=7))
+
+
+def test_gaussian_stream(tq):
+    g = tq.host_gaussian(1, 200000)
+    np.testing.assert_allclose(g, oracle.gaussian(1, 200000), rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("d", [3, 64, 128, 1536])
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_codebook_matches_oracle(tq, d, b):
+    c, t = tq.host_codebook(d, b)
+    cb = oracle.codebook(d, b)
+    np.testing.assert_allclose(c, cb.centroids, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(t, cb.thresholds, rtol=0, atol=1e-12)
+    # the float32 thresholds the kernels compare against are identical
+    np.testing.assert_array_equal(t.astype(np.float32), cb.thresholds32)
+    g, _ = tq.host_codebook(d, b, "gauss")
+    np.testing.assert_allclose(g, oracle.codebook(d, b, "gauss").centroids, atol=1e-12)
+
+
+def test_codebook_handle_host_only(tq):
+    cb = tq.codebook(128, 3)
+    c, t = cb.values()
+    np.testing.assert_allclose(c, oracle.codebook(128, 3).centroids, atol=1e-12)
+    cb.close()
+
+
+@pytest.mark.parametrize("d", [2, 16, 128, 256])
+def test_dense_rotation_matches_oracle(tq, d):
+    r = tq.host_rotation(d, 1)
+    np.testing.assert_allclose(r, oracle.dense_rotation(d, 1), rtol=0, atol=1e-12)
+
+
+def test_dense_rotation_d1536(tq):
+    r = tq.host_rotation(1536, 1)
+    np.testing.assert_allclose(r, oracle.dense_rotation(1536, 1), rtol=0, atol=1e-12)
+
+
+def test_wht_rotation_matches_oracle(tq):
+    for d in (2, 64, 128):
+        np.testing.assert_array_equal(tq.host_rotation(d, 1, "wht"), oracle.wht_rotation(d, 1))
+
+
+def test_qjl_matrix(tq):
+    np.testing.assert_allclose(tq.host_qjl_matrix(128, 2), oracle.qjl_matrix(128, 2), rtol=1e-14, atol=1e-14)
+
+
+def test_error_paths(tq):
+    lib = tq.lib()
+    c = np.empty(32)
+    t = np.empty(32)
+    P = lambda a: ctypes.c_void_p(a.ctypes.data)
+    assert lib.tq_host_codebook(128, 5, 0, P(c), P(t)) == 1          # b out of range
+    assert lib.tq_host_codebook(128, 0, 0, P(c), P(t)) == 1
+    assert lib.tq_host_codebook(128, 2, 7, P(c), P(t)) == 1          # bad density
+    assert lib.tq_host_codebook(128, 2, 0, None, P(t)) == 1
+    r = np.empty(96 * 96)
+    assert lib.tq_host_rotation(96, 1, 1, P(r)) == 3                 # Hadamard needs 2^k
+    assert "Hadamard" in lib.tq_last_error().decode()
+    assert lib.tq_host_splitmix64(0, 0, -1, None) == 1
+    assert lib.tq_packed_words(128, 3) == 12 and lib.tq_packed_words(100, 3) == 0
+    # hot-path entry points validate before touching the device
+    desc = tq.tq_packed(128, 3, 0, 0, 10, None, None, None, None)
+    assert lib.tq_encode(None, 1, 10, 128, 3, 0, None, None, None, ctypes.byref(desc), None) == 1
+    cbh = tq.codebook(128, 2)
+    assert lib.tq_encode(None, 1, 10, 128, 3, 0, cbh.ptr, None, None, ctypes.byref(desc), None) == 1
+    assert lib.tq_scores(None, 1, 32, 5, 10, ctypes.byref(desc), cbh.ptr, None, None, None, None, 0, None) == 1
+    assert lib.tq_quantize_rotated(None, 10, 64, cbh.ptr, None, None) == 1   # null buffers
+    assert lib.tq_quantize_rotated(None, -1, 128, cbh.ptr, None, None) == 1
+    assert lib.tq_quantize_rotated(None, 0, 64, cbh.ptr, None, None) == 2    # d mismatch
+    assert lib.tq_quantize_rotated(None, 0, 128, cbh.ptr, None, None) == 0   # empty is fine
+
+
+def test_codebook_from_values_checks(tq):
+    with pytest.raises(tq.TQError):
+        tq.codebook_from_values(4, [0.5, -0.5])
+    cb = tq.codebook_from_values(4, [-0.6, 0.6])
+    c, t = cb.values()
+    assert t.tolist() == [0.0]
