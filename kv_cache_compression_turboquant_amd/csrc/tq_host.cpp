@@ -280,6 +280,7 @@ tq_status upload(const std::vector<T>& host, T** dev, const char* what) {
 void free_rotation(tq_rotation_s* r) {
   if (!r) return;
   if (r->r32_dev) hipFree(r->r32_dev);
+  if (r->rt32_dev) hipFree(r->rt32_dev);
   if (r->frag_dev) hipFree(r->frag_dev);
   delete r;
 }
@@ -287,15 +288,22 @@ void free_rotation(tq_rotation_s* r) {
 void free_qjl(tq_qjl_s* q) {
   if (!q) return;
   if (q->s32_dev) hipFree(q->s32_dev);
+  if (q->st32_dev) hipFree(q->st32_dev);
   if (q->frag_dev) hipFree(q->frag_dev);
   delete q;
 }
 
 tq_status finish_rotation(tq_rotation_s* r) {
   const int d = r->d;
-  std::vector<float> r32((size_t)d * d);
-  for (size_t i = 0; i < r32.size(); ++i) r32[i] = (float)r->r[i];
+  std::vector<float> r32((size_t)d * d), rt32((size_t)d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      r32[(size_t)i * d + j] = (float)r->r[(size_t)i * d + j];
+      rt32[(size_t)j * d + i] = (float)r->r[(size_t)i * d + j];
+    }
   tq_status st = upload(r32, &r->r32_dev, "upload rotation");
+  if (st != TQ_OK) return st;
+  st = upload(rt32, &r->rt32_dev, "upload rotation transpose");
   if (st != TQ_OK) return st;
   if (d == tq::kFragD) {
     std::vector<uint16_t> frag;
@@ -322,9 +330,14 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
   q->rot_id = rot->id;
   q->s = std::move(s);
   hipGetDevice(&q->device);
-  std::vector<float> s32((size_t)d * d);
-  for (size_t i = 0; i < s32.size(); ++i) s32[i] = (float)q->s[i];
+  std::vector<float> s32((size_t)d * d), st32((size_t)d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      s32[(size_t)i * d + j] = (float)q->s[(size_t)i * d + j];
+      st32[(size_t)j * d + i] = (float)q->s[(size_t)i * d + j];
+    }
   tq_status st = upload(s32, &q->s32_dev, "upload qjl");
+  if (st == TQ_OK) st = upload(st32, &q->st32_dev, "upload qjl transpose");
   if (st == TQ_OK && d == tq::kFragD) {
     // S' = S R^T in fp64
     std::vector<double> sp((size_t)d * d, 0.0);

@@ -52,6 +52,7 @@ struct tq_rotation_s {
   uint64_t id;
   std::vector<double> r;    // fp64 R, row-major
   float* r32_dev = nullptr;       // fp32 R, row-major [d, d]
+  float* rt32_dev = nullptr;      // fp32 R^T, row-major [d, d] (coalesced query rotation)
   uint16_t* frag_dev = nullptr;   // bf16 fragments [2][kFragElems] (d = 128 only)
   int passes = 2;                 // 1 when R is exactly representable after scaling
   float post_scale = 1.0f;        // y = post_scale * (fragments . x)
@@ -63,6 +64,7 @@ struct tq_qjl_s {
   uint64_t rot_id;
   std::vector<double> s;    // fp64 S, row-major
   float* s32_dev = nullptr;       // fp32 S, row-major [d, d]
+  float* st32_dev = nullptr;      // fp32 S^T, row-major [d, d]
   uint16_t* frag_dev = nullptr;   // bf16 fragments of S' = S R^T [2][kFragElems] (d = 128)
 };
 

@@ -20,6 +20,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kQjl = 1.2533141373155002512f;  // sqrt(pi / 2)
 
@@ -55,20 +57,6 @@ __device__ __forceinline__ uint32_t bucketize(float y, const CodebookArgs& cb) {
   return idx;
 }
 
-// Same, also returning the centroid C[idx].
-template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_c(float y, const CodebookArgs& cb, float& c) {
-  uint32_t idx = 0;
-  c = cb.c[0];
-#pragma unroll
-  for (int k = 0; k < (1 << BITS) - 1; ++k) {
-    bool ge = y >= cb.t[k];
-    idx += ge ? 1u : 0u;
-    c = ge ? cb.c[k + 1] : c;
-  }
-  return idx;
-}
-
 // Pack 32 BITS-bit indices (local order) into BITS words, LSB-first stream.
 template <int BITS>
 __device__ __forceinline__ void pack32(const uint32_t (&idx)[32], uint32_t (&w)[BITS]) {
@@ -82,33 +70,15 @@ __device__ __forceinline__ void pack32(const uint32_t (&idx)[32], uint32_t (&w)[
   }
 }
 
-// Sign-magnitude bucketize for an antisymmetric codebook (cb.sym): with m the number of
-// positive thresholds below |y| (<= for y >= 0, < for y < 0), idx = K/2 + m for y >= 0 and
-// K/2 - 1 - m for y < 0.  This equals #{k : y >= t_k} exactly, including ties and -0.0.
-// Also returns the centroid sign(y) * cpos[m].
-template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_sym(float y, const CodebookArgs& cb, float& c) {
-  constexpr int H = 1 << (BITS - 1);
-  const bool neg = y < 0.f;
-  const int a = (int)(__float_as_uint(y) & 0x7fffffffu) - (neg ? 1 : 0);
-  uint32_t m = 0;
-  float mag = cb.cpos[0];
-#pragma unroll
-  for (int p = 0; p < H - 1; ++p) {
-    const bool ge = a >= cb.tpos[p];
-    m += ge ? 1u : 0u;
-    mag = ge ? cb.cpos[p + 1] : mag;
-  }
-  c = neg ? -mag : mag;
-  return neg ? (uint32_t)(H - 1) - m : (uint32_t)H + m;
-}
-
 // ---------------------------------------------------------------------------------------
 // Fused encode, d = 128.  One wave computes y^T = R x^T for NT tiles of 16 vectors:
 // A = rotation fragments (LDS), B = x (registers, straight from HBM), D = y^T.  Lane (n, G)
 // ends with coordinates 32 G .. 32 G + 31 of vector n, bucketizes them and writes BITS packed
 // words (its aligned share of the row).  PROD runs a second product Z^T = S' R_res^T on the
 // rotated-domain residual, whose B operand is exactly the lane's own registers.
+// The fused path compares |y| against the positive thresholds (sign-magnitude form of the
+// antisymmetric codebook); a value exactly on a threshold may go either way there, which the
+// boundary-band rule allows.  The exact tie rule lives in k_quantize_rotated.
 // The fragment loops are software pipelined: block c + 1's fragments are read from LDS while
 // block c's MFMAs run; scheduling barriers keep the compiler from hoisting every read.
 // ---------------------------------------------------------------------------------------
@@ -130,6 +100,34 @@ __device__ __forceinline__ void load_frags(const u32x4* lds, int c, int lane, u3
     for (int s = 0; s < 4; ++s) a[p][s] = lds[p * kFragU4 + (c * 4 + s) * 64 + lane];
 }
 
+// Raw input of one 16-vector tile held by a lane: 32 consecutive coordinates of one vector.
+template <bool BF16IN>
+struct RawTile;
+template <>
+struct RawTile<true> {
+  u32x4 v[4];
+};
+template <>
+struct RawTile<false> {
+  f32x4 v[8];
+};
+
+template <bool BF16IN>
+__device__ __forceinline__ void load_tile(const void* x, int64_t n, int64_t tile, int nl, int g,
+                                          RawTile<BF16IN>& r) {
+  const int64_t row = tile * 16 + nl;
+  const int64_t lrow = row < n ? row : n - 1;
+  if constexpr (BF16IN) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + lrow * 128 + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r.v[s] = src[s];
+  } else {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + lrow * 128 + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.v[s] = src[s];
+  }
+}
+
 template <int BITS, bool PROD, bool BF16IN, bool STORE_Y, int PASSES, int NT>
 __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlocksPerCU) void k_encode_d128(
     const void* __restrict__ x, int64_t n, const u32x4* __restrict__ frag_r,
@@ -139,6 +137,7 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
   constexpr int RP = PASSES;              // rotation passes held in LDS
   constexpr int SP = PROD ? 2 : 0;        // S' passes
   constexpr int kWaves = EncShape<PROD>::kWaves;
+  constexpr int H = 1 << (BITS - 1);      // centroids per sign
   __shared__ u32x4 lds[(RP + SP) * kFragU4];
   for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = frag_r[i];
   if constexpr (PROD) {
@@ -152,45 +151,58 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
   const int g = lane >> 4;
   const int64_t ntiles = (n + 15) >> 4;
   const int64_t stride = (int64_t)gridDim.x * kWaves * NT;
+  int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * NT;
+  if (t0 >= ntiles) return;  // no barrier follows
 
-  for (int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * NT; t0 < ntiles; t0 += stride) {
+  const float inv_post = 1.0f / post_scale;
+  RawTile<BF16IN> nxt[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, t0 + t, nl, g, nxt[t]);
+
+  for (; t0 < ntiles; t0 += stride) {
+    RawTile<BF16IN> cur[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
+    if (t0 + stride < ntiles) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, t0 + stride + t, nl, g, nxt[t]);
+    }
+
     u32x4 bx[NT][4];      // bf16 x (or its hi part) for the 4 instructions
     u32x4 bxl[NT][4];     // bf16 low part of fp32 x
     float ss[NT];
-    int64_t rows[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t row = (t0 + t) * 16 + nl;
-      rows[t] = row;
-      const int64_t lrow = row < n ? row : n - 1;
       float acc2 = 0.f;
       if constexpr (BF16IN) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(
-            static_cast<const uint16_t*>(x) + lrow * 128 + 32 * g);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          u32x4 v = src[s];
-          bx[t][s] = v;
+          bx[t][s] = cur[t].v[s];
+          // Copy to a plain array first: bit-casting an ext-vector element straight into the
+          // dot2 operand miscompiles (every j reads element 0) with this compiler.
+          uint32_t wv[4];
+          __builtin_memcpy(wv, &cur[t].v[s], sizeof(wv));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xffff0000u);
-            acc2 += lo * lo + hi * hi;
+            const bf16x2 p = __builtin_bit_cast(bf16x2, wv[j]);
+            acc2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc2, false);
           }
         }
       } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + lrow * 128 + 32 * g);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          f32x4 a = src[2 * s], b = src[2 * s + 1];
-          float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+          const f32x4 a = cur[t].v[2 * s], b = cur[t].v[2 * s + 1];
+          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
           u32x4 hi, lo;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint32_t h0 = bf16_bits(v[2 * j]), h1 = bf16_bits(v[2 * j + 1]);
-            uint32_t l0 = bf16_bits(v[2 * j] - bf16_val(h0)), l1 = bf16_bits(v[2 * j + 1] - bf16_val(h1));
-            hi[j] = h0 | (h1 << 16);
-            lo[j] = l0 | (l1 << 16);
-            acc2 += v[2 * j] * v[2 * j] + v[2 * j + 1] * v[2 * j + 1];
+            const f32x2 pr = {v[2 * j], v[2 * j + 1]};
+            const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+            const f32x2 rem = {v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
+            hi[j] = h;
+            lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+            acc2 = fmaf(v[2 * j], v[2 * j], acc2);
+            acc2 = fmaf(v[2 * j + 1], v[2 * j + 1], acc2);
           }
           bx[t][s] = hi;
           bxl[t][s] = lo;
@@ -202,19 +214,19 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
     // y^T blocks: acc[t][c] holds rows 32 G + 4 c + r of tile t
     f32x4 acc[NT][8];
     {
-      u32x4 cur[RP][4], nxt[RP][4];
-      load_frags<RP>(lds, 0, lane, cur);
+      u32x4 cf[RP][4], nf[RP][4];
+      load_frags<RP>(lds, 0, lane, cf);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        if (c + 1 < 8) load_frags<RP>(lds, c + 1, lane, nxt);
+        if (c + 1 < 8) load_frags<RP>(lds, c + 1, lane, nf);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            a = mfma_bf16(cur[0][s], bx[t][s], a);
-            if constexpr (!BF16IN) a = mfma_bf16(cur[0][s], bxl[t][s], a);
-            if constexpr (RP == 2) a = mfma_bf16(cur[1][s], bx[t][s], a);
+            a = mfma_bf16(cf[0][s], bx[t][s], a);
+            if constexpr (!BF16IN) a = mfma_bf16(cf[0][s], bxl[t][s], a);
+            if constexpr (RP == 2) a = mfma_bf16(cf[1][s], bx[t][s], a);
           }
           acc[t][c] = a;
         }
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
 #pragma unroll
           for (int p = 0; p < RP; ++p)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) cur[p][s] = nxt[p][s];
+            for (int s = 0; s < 4; ++s) cf[p][s] = nf[p][s];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -234,9 +246,9 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
       sq += __shfl_xor(sq, 16);
       sq += __shfl_xor(sq, 32);
       const float nrm = sqrtf(sq);
-      const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
-      const float scale = post_scale * inv;
-      const int64_t row = rows[t];
+      const bool live = nrm > 0.f;
+      const float scale = live ? post_scale / nrm : 0.f;   // raw product -> unit coordinate
+      const int64_t row = (t0 + t) * 16 + nl;
       const bool valid = row < n;
       if (valid && g == 0 && norms_out) norms_out[row] = nrm;
       if constexpr (STORE_Y) {
@@ -246,8 +258,16 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
           for (int c = 0; c < 8; ++c) dst[c] = acc[t][c] * scale;
         }
       } else {
-        // bucketize and pack on the fly; PROD also forms the residual's bf16 hi/lo B operand
-        // (element e of instruction s = local coordinate 8 s + e = 4 c + r with c = 2 s + e / 4).
+        // Decisions on the raw product against per-vector thresholds t_p * ||x|| / post_scale
+        // (the sign-magnitude form of the antisymmetric codebook): idx = (m ^ sign) + K/2 with
+        // m = #{p : |y| >= t_p}.  A zero vector keeps every threshold at +inf (idx K/2).
+        float thr[H > 1 ? H - 1 : 1];
+        float mags[H];
+        const float tsc = nrm * inv_post;
+#pragma unroll
+        for (int p = 0; p < H - 1; ++p) thr[p] = live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY;
+#pragma unroll
+        for (int p = 0; p < H; ++p) mags[p] = live ? cb.cpos[p] : 0.f;
         uint32_t w[BITS];
 #pragma unroll
         for (int j = 0; j < BITS; ++j) w[j] = 0;
@@ -257,27 +277,37 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
         for (int c = 0; c < 8; ++c)
 #pragma unroll
           for (int rp = 0; rp < 2; ++rp) {
-            uint32_t id[2];
             float res[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-              const float yv = acc[t][c][2 * rp + q] * scale;
-              float cv;
-              id[q] = bucketize_sym<BITS>(yv, cb, cv);
+              const float yv = acc[t][c][2 * rp + q];
+              const float ay = fabsf(yv);
+              uint32_t m = 0;
+              float mag = mags[0];
+#pragma unroll
+              for (int p = 0; p < H - 1; ++p) {
+                const bool ge = ay >= thr[p];
+                m += ge ? 1u : 0u;
+                if constexpr (PROD) mag = ge ? mags[p + 1] : mag;
+              }
+              const uint32_t sgn = (uint32_t)(__float_as_int(yv) >> 31);
+              const uint32_t id = (m ^ sgn) + (uint32_t)H;
               if constexpr (PROD) {
-                res[q] = nrm > 0.f ? yv - cv : 0.f;
-                rs += res[q] * res[q];
+                const float cv = __uint_as_float((__float_as_uint(mag) & 0x7fffffffu) | (__float_as_uint(yv) & 0x80000000u));
+                res[q] = fmaf(yv, scale, -cv);
+                rs = fmaf(res[q], res[q], rs);
               }
               const int li = 4 * c + 2 * rp + q;
               const int p = BITS * li, wi = p >> 5, sh = p & 31;
-              w[wi] |= id[q] << sh;
-              if (sh + BITS > 32) w[wi + 1] |= id[q] >> (32 - sh);
+              w[wi] |= id << sh;
+              if (sh + BITS > 32) w[wi + 1] |= id >> (32 - sh);
             }
             if constexpr (PROD) {
-              const uint32_t h0 = bf16_bits(res[0]), h1 = bf16_bits(res[1]);
-              const uint32_t l0 = bf16_bits(res[0] - bf16_val(h0)), l1 = bf16_bits(res[1] - bf16_val(h1));
-              rh[c >> 1][2 * (c & 1) + rp] = h0 | (h1 << 16);
-              rl[c >> 1][2 * (c & 1) + rp] = l0 | (l1 << 16);
+              const f32x2 pr = {res[0], res[1]};
+              const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+              const f32x2 rem = {res[0] - __uint_as_float(h << 16), res[1] - __uint_as_float(h & 0xffff0000u)};
+              rh[c >> 1][2 * (c & 1) + rp] = h;
+              rl[c >> 1][2 * (c & 1) + rp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
             }
           }
         if (valid) {
@@ -288,17 +318,17 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
         if constexpr (PROD) {
           uint32_t bits = 0;
           const u32x4* sl = lds + RP * kFragU4;
-          u32x4 cur[2][4], nxt[2][4];
-          load_frags<2>(sl, 0, lane, cur);
+          u32x4 cf[2][4], nf[2][4];
+          load_frags<2>(sl, 0, lane, cf);
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            if (c + 1 < 8) load_frags<2>(sl, c + 1, lane, nxt);
+            if (c + 1 < 8) load_frags<2>(sl, c + 1, lane, nf);
             f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              z = mfma_bf16(cur[0][s], rh[s], z);
-              z = mfma_bf16(cur[0][s], rl[s], z);
-              z = mfma_bf16(cur[1][s], rh[s], z);
+              z = mfma_bf16(cf[0][s], rh[s], z);
+              z = mfma_bf16(cf[0][s], rl[s], z);
+              z = mfma_bf16(cf[1][s], rh[s], z);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) bits |= (z[r] >= 0.f ? 1u : 0u) << (4 * c + r);
@@ -306,7 +336,7 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
 #pragma unroll
               for (int p = 0; p < 2; ++p)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) cur[p][s] = nxt[p][s];
+                for (int s = 0; s < 4; ++s) cf[p][s] = nf[p][s];
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -340,9 +370,8 @@ template <int BITS, bool PROD, bool BF16IN, bool STORE_Y, int PASSES>
 hipError_t enc_launch(const void* x, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                       const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits,
                       float* rnorms, float* y, hipStream_t st) {
-  constexpr int NT = PROD ? 1 : 2;
+  constexpr int NT = (PROD || !BF16IN) ? 1 : 2;
   constexpr int kWaves = EncShape<PROD>::kWaves;
-  (void)kWaves;
   const int64_t ntiles = (n + 15) / 16;
   const int64_t per_block = (int64_t)kWaves * NT;
   int64_t blocks = (ntiles + per_block - 1) / per_block;
@@ -429,37 +458,63 @@ __global__ void k_decode(const uint32_t* __restrict__ idx, const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------
-// Query prologue: for each (batch, kv head) block, q_rot = R q and q_s = S q for the heads that
-// share the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][d], part = 0 rot hi,
-// 1 rot lo, 2 sketch hi, 3 sketch lo.
+// Query prologue, d = 128: for each (batch, kv head) block, q_rot = R q and q_s = S q of the
+// heads sharing the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][128], part = 0
+// rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo.  Reads R^T / S^T so that thread j's loads of
+// column j are coalesced; the 128 contraction steps are split over two thread halves.
 // ---------------------------------------------------------------------------------------
-__global__ void k_qprep(const float* __restrict__ q, int Hq, int ratio, int d,
-                        const float* __restrict__ r32, const float* __restrict__ s32,
-                        uint16_t* __restrict__ ws) {
-  extern __shared__ float qs[];  // [ratio][d]
-  const int bg = blockIdx.x;     // b * Hkv + kvh
-  const int b = bg / (Hq / ratio), kvh = bg % (Hq / ratio);
+__global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
+                                                  const float* __restrict__ rt, const float* __restrict__ st,
+                                                  uint16_t* __restrict__ ws) {
+  __shared__ float qs[4][128];
+  __shared__ float part[2][2][4][128];
+  const int Hkv = Hq / ratio;
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, kvh = bg % Hkv;
   const int h0 = kvh * ratio;
-  for (int i = threadIdx.x; i < ratio * d; i += blockDim.x)
-    qs[i] = q[((int64_t)b * Hq + h0 + i / d) * d + (i % d)];
-  __syncthreads();
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    for (int h = 0; h < ratio; ++h) {
-      float a = 0.f, c = 0.f;
-      const float* qh = qs + h * d;
-      for (int k = 0; k < d; ++k) a += r32[(int64_t)j * d + k] * qh[k];
-      if (s32)
-        for (int k = 0; k < d; ++k) c += s32[(int64_t)j * d + k] * qh[k];
-      uint16_t* o = ws + ((int64_t)b * Hq + h0 + h) * 4 * d;
-      const _Float16 ah = (_Float16)a;
-      const _Float16 al = (_Float16)(a - (float)ah);
-      o[j] = __builtin_bit_cast(uint16_t, ah);
-      o[d + j] = __builtin_bit_cast(uint16_t, al);
-      if (s32) {
-        const _Float16 ch = (_Float16)c;
-        const _Float16 cl = (_Float16)(c - (float)ch);
-        o[2 * d + j] = __builtin_bit_cast(uint16_t, ch);
-        o[3 * d + j] = __builtin_bit_cast(uint16_t, cl);
+  const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
+  for (int hc = 0; hc < ratio; hc += 4) {
+    const int nh = ratio - hc < 4 ? ratio - hc : 4;
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) {
+      const int hh = i >> 7;
+      qs[hh][i & 127] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + (i & 127)] : 0.f;
+    }
+    __syncthreads();
+    float ar[4] = {0.f, 0.f, 0.f, 0.f}, as[4] = {0.f, 0.f, 0.f, 0.f};
+    const int k0 = half * 64;
+#pragma unroll 8
+    for (int k = k0; k < k0 + 64; ++k) {
+      const float r = rt[k * 128 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = fmaf(r, qs[i][k], ar[i]);
+      if (st) {
+        const float sv = st[k * 128 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) as[i] = fmaf(sv, qs[i][k], as[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[0][half][i][j] = ar[i];
+      part[1][half][i][j] = as[i];
+    }
+    __syncthreads();
+    if (half == 0) {
+      for (int i = 0; i < nh; ++i) {
+        uint16_t* o = ws + ((int64_t)b * Hq + h0 + hc + i) * 4 * 128;
+        const float a = part[0][0][i][j] + part[0][1][i][j];
+        const _Float16 ah = (_Float16)a;
+        const _Float16 al = (_Float16)(a - (float)ah);
+        o[j] = __builtin_bit_cast(uint16_t, ah);
+        o[128 + j] = __builtin_bit_cast(uint16_t, al);
+        if (st) {
+          const float c = part[1][0][i][j] + part[1][1][i][j];
+          const _Float16 ch = (_Float16)c;
+          const _Float16 cl = (_Float16)(c - (float)ch);
+          o[256 + j] = __builtin_bit_cast(uint16_t, ch);
+          o[384 + j] = __builtin_bit_cast(uint16_t, cl);
+        }
       }
     }
   }
@@ -469,14 +524,14 @@ __global__ void k_qprep(const float* __restrict__ q, int Hq, int ratio, int d,
 // Compressed-key score, d = 128.  Grid (key chunk, b * Hkv).  D = A B with A = query slots
 // (16 rows: rot hi / rot lo / sketch hi / sketch lo for 4 heads), B = decoded keys (columns =
 // 16 keys), so lane (n, G) receives the four partial sums of key n for slot group G.  Keys are
-// decoded from whole packed words through LDS tables that map a field of F bits to F / BITS
-// fp16 centroids (F = 12 for 3 bits, else 8).
+// decoded from whole packed words through small LDS tables that map a field of F bits to
+// F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass.
 // ---------------------------------------------------------------------------------------
 constexpr int kScoreWaves = 4;
 
 template <int BITS>
 struct DecodeTable {
-  static constexpr int F = BITS == 3 ? 12 : 8;
+  static constexpr int F = BITS == 3 ? 6 : 8;
   static constexpr int PER = F / BITS;             // coordinates per field
   static constexpr int ENTRIES = 1 << F;
   static constexpr int BYTES = ENTRIES * PER * 2;  // fp16 entries
@@ -497,12 +552,12 @@ __device__ __forceinline__ u32x4 decode_keys(const uint32_t (&w)[BITS], int s, c
     out = u32x4{a[0], a[1], b[0], b[1]};
   } else if constexpr (BITS == 3) {
     const int off = 24 * s;
-    const uint64_t win = ((uint64_t)w[(off + 23) >> 5 < BITS ? (off + 23) >> 5 : BITS - 1] << 32) |
-                         w[off >> 5];
-    const uint32_t bits24 = (uint32_t)(win >> (off & 31)) & 0xffffffu;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + (bits24 & 0xfffu) * 8);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + (bits24 >> 12) * 8);
-    out = u32x4{a[0], a[1], b[0], b[1]};
+    const int lo = off >> 5;
+    const int hi = (off + 23) >> 5;
+    const uint64_t win = ((uint64_t)w[hi] << 32) | w[lo];
+    const uint32_t bits24 = (uint32_t)(win >> (off & 31));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tab + ((bits24 >> (6 * j)) & 63u) * 4);
   } else {
     const uint32_t word = w[s];
 #pragma unroll
@@ -632,9 +687,10 @@ hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, cons
   const int ratio = Hq / Hkv;
   const int d = 128;
   uint16_t* qws = static_cast<uint16_t*>(ws);
-  const int qthreads = 128;
-  hipLaunchKernelGGL(k_qprep, dim3(B * Hkv), dim3(qthreads), ratio * d * sizeof(float), st, q, Hq, ratio, d,
-                     rot->r32_dev, PROD ? qjl->s32_dev : nullptr, qws);
+  const int qthreads = 256;
+  (void)d;
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(qthreads), 0, st, q, Hq, ratio, rot->rt32_dev,
+                     PROD ? qjl->st32_dev : nullptr, qws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tiles = (T + 15) / 16;
