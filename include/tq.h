@@ -59,6 +59,14 @@ typedef enum tq_density { TQ_DENSITY_BETA = 0, TQ_DENSITY_GAUSS = 1 } tq_density
 typedef enum tq_rot_kind { TQ_ROT_DENSE = 0, TQ_ROT_WHT = 1 } tq_rot_kind;
 typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 typedef enum tq_mode { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1 } tq_mode;
+/* Storage layout of packed indices.  ROWS: row r is the LSB-first stream of vector r's d
+ * indices (d*bits/32 words per row).  TOKEN_BLOCKED (MSE only; the value-cache layout read by
+ * tq_decode_attn): rows are grouped in blocks of 32 (rows past n hold index 0); inside block B,
+ * chunk (o, c) for octet o = 0..3 and coordinate c = 0..d-1 sits at chunk position o*d + c and
+ * holds the indices of rows 32B + 8o + e, e = 0..7, at coordinate c, LSB-first (row e at chunk
+ * bits [bits*e, bits*e + bits)); the 8*bits-bit chunks are concatenated LSB-first, d*bits words
+ * per block, ceil(n/32) blocks.  The pages fix no layout; both are this library's choice. */
+typedef enum tq_layout { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_TOKEN_BLOCKED = 1 } tq_layout;
 
 typedef struct tq_codebook_s* tq_codebook_t;
 typedef struct tq_rotation_s* tq_rotation_t;
@@ -74,9 +82,9 @@ typedef struct tq_packed {
   int32_t d;          /* vector length */
   int32_t bits;       /* bits per index: b for MSE, b - 1 for prod */
   int32_t mode;       /* tq_mode */
-  int32_t reserved;   /* must be 0 */
+  int32_t layout;     /* tq_layout of idx */
   int64_t n;          /* number of vectors (rows) */
-  uint32_t* idx;      /* [n, d*bits/32] */
+  uint32_t* idx;      /* ROWS: [n, d*bits/32]; TOKEN_BLOCKED: [ceil(n/32), d*bits] */
   float* norms;       /* [n] */
   uint32_t* qjl;      /* [n, d/32] for prod, else NULL */
   float* rnorms;      /* [n] for prod, else NULL */
@@ -139,9 +147,12 @@ void tq_qjl_free(tq_qjl_t qjl);
 
 /* Words per packed row: d * bits / 32. */
 size_t tq_packed_words(int d, int bits);
+/* Words of the idx buffer for n vectors in the given layout (0 on invalid arguments). */
+size_t tq_packed_idx_words(int64_t n, int d, int bits, tq_layout layout);
 
 /* Encode n vectors x_dev [n, d] (dtype dt, row-major) into *out ([TQ] official steps 1-4 and
  * KV prefill steps 1-6; prod: [TQ] TurboQuant_prod, (b-1)-bit stage + 1-bit QJL).
+ * out->layout selects ROWS or TOKEN_BLOCKED (MSE only).
  * b is the total bit budget per coordinate; cb must have b bits (MSE) or b - 1 bits (prod);
  * qjl must be non-NULL exactly for prod and bound to `rot`.  out->d, out->bits, out->mode,
  * out->n must describe the call; out->idx/norms (and qjl/rnorms for prod) are written.
@@ -178,6 +189,21 @@ size_t tq_scores_workspace(int B, int Hq, int d);
 tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
                     void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Workspace bytes tq_decode_attn needs (query prologue plus per-split softmax partials). */
+size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d);
+/* Fused decode attention over compressed K and V ([RQ] chapter 1: softmax(q K^T / sqrt(d)) V;
+ * [TQ] decode section, second route: unpack, look up, scale and accumulate inside the kernel,
+ * never materialising K_hat or V_hat; K and V stored TurboQuant_mse per [SB]).
+ * out[b, h] = sum_t softmax_t(scale * <q[b,h], k_hat[b,g,t]>) v_hat[b,g,t], g = h / (Hq/Hkv),
+ * k_hat = s_k R_K^T C_K[idx], v_hat = s_v R_V^T C_V[idx].  q_dev [B, Hq, d] fp32; K: ROWS
+ * layout, MSE, n = B*Hkv*T; V: TOKEN_BLOCKED layout, MSE, n = B*Hkv*T; out_dev [B, Hq, d] fp32.
+ * The value sum is accumulated in V's rotated domain and R_V^T is applied once per head.
+ * Requires d = 128, T >= 1, Hq/Hkv in {1, 2, 4}.  Errors as for tq_scores; TQ_EINVAL for T < 1. */
+tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                         tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
+                         void* ws_dev, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ import ctypes
 
 import numpy as np
 
-from ._binding import (DENSITY, MODE, ROT_KIND, DTYPE_BF16, DTYPE_F32, TQError, check, lib,
+from ._binding import (DENSITY, LAYOUT, MODE, ROT_KIND, DTYPE_BF16, DTYPE_F32, TQError, check, lib,
                        tq_packed, host_splitmix64, host_gaussian, host_codebook, host_rotation,
                        host_qjl_matrix, SIGNATURES)
 
@@ -17,6 +17,7 @@ __all__ = [
     "Codebook", "Rotation", "QJL", "Packed", "codebook", "codebook_from_values", "make_rotation",
     "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
+    "decode_attn", "decode_attn_workspace",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -142,21 +143,26 @@ def packed_words(d, bits):
 
 
 class Packed:
-    """Caller-owned packed storage: idx [n, d*bits/32] int32 (uint32 bits), norms [n] fp32,
-    and for prod qjl [n, d/32] int32 and rnorms [n] fp32."""
+    """Caller-owned packed storage: idx int32 (uint32 bits) [n, d*bits/32] (rows layout) or
+    [ceil(n/32), d*bits] (token-blocked layout), norms [n] fp32, and for prod qjl [n, d/32]
+    int32 and rnorms [n] fp32."""
 
-    def __init__(self, d, bits, mode, n, idx, norms, qjl=None, rnorms=None):
-        self.d, self.bits, self.mode, self.n = d, bits, mode, n
+    def __init__(self, d, bits, mode, n, idx, norms, qjl=None, rnorms=None, layout="rows"):
+        self.d, self.bits, self.mode, self.n, self.layout = d, bits, mode, n, layout
         self.idx, self.norms, self.qjl, self.rnorms = idx, norms, qjl, rnorms
 
     def descriptor(self):
-        return tq_packed(self.d, self.bits, MODE[self.mode], 0, self.n, _dptr(self.idx),
+        return tq_packed(self.d, self.bits, MODE[self.mode], LAYOUT[self.layout], self.n, _dptr(self.idx),
                          _dptr(self.norms), _dptr(self.qjl), _dptr(self.rnorms))
 
 
-def alloc_packed(n, d, bits, mode="mse", device="cuda"):
+def alloc_packed(n, d, bits, mode="mse", device="cuda", layout="rows"):
     torch = _torch()
     w = d * bits // 32
+    if layout == "blocked":
+        idx = torch.empty(((n + 31) // 32, d * bits), dtype=torch.int32, device=device)
+        norms = torch.empty((n,), dtype=torch.float32, device=device)
+        return Packed(d, bits, mode, n, idx, norms, layout="blocked")
     idx = torch.empty((n, w), dtype=torch.int32, device=device)
     norms = torch.empty((n,), dtype=torch.float32, device=device)
     qjl = rn = None
@@ -175,12 +181,12 @@ def _dtype_code(x):
     raise TQError(3, f"unsupported dtype {x.dtype}")
 
 
-def encode(x, b, mode, cb, rot, qjl=None, out=None):
+def encode(x, b, mode, cb, rot, qjl=None, out=None, layout="rows"):
     """Encode rows of x [n, d] (bf16 or fp32, contiguous, on the GPU) with b total bits."""
     n, d = x.shape
     stage = b - 1 if mode == "prod" else b
     if out is None:
-        out = alloc_packed(n, d, stage, mode, device=x.device)
+        out = alloc_packed(n, d, stage, mode, device=x.device, layout=layout)
     desc = out.descriptor()
     check(lib().tq_encode(_dptr(x), _dtype_code(x), n, d, b, MODE[mode], cb.ptr, rot.ptr,
                           qjl.ptr if qjl is not None else None, ctypes.byref(desc), _stream()))
@@ -232,4 +238,28 @@ def scores(q, K, Hkv, cb, rot, qjl=None, out=None, ws=None):
     check(lib().tq_scores(_dptr(q), B, Hq, Hkv, T, ctypes.byref(desc), cb.ptr, rot.ptr,
                           qjl.ptr if qjl is not None else None, _dptr(out), _dptr(ws),
                           ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def decode_attn_workspace(B, Hq, Hkv, T, d):
+    return int(lib().tq_decode_attn_workspace(B, Hq, Hkv, T, d))
+
+
+def decode_attn(q, K, V, Hkv, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws=None):
+    """softmax(scale <q, k_hat>) v_hat for q [B, Hq, d] fp32; K rows-layout, V blocked-layout,
+    both laid out [B, Hkv, T]."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    T = K.n // max(B * Hkv, 1)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    nbytes = decode_attn_workspace(B, Hq, Hkv, T, d)
+    if ws is None:
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    kd, vd = K.descriptor(), V.descriptor()
+    check(lib().tq_decode_attn(_dptr(q), B, Hq, Hkv, T, ctypes.byref(kd), ctypes.byref(vd), cb_k.ptr, cb_v.ptr,
+                               rot_k.ptr, rot_v.ptr, ctypes.c_float(scale), _dptr(out), _dptr(ws),
+                               ws.numel() * ws.element_size(), _stream()))
     return out

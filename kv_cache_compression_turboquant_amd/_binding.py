@@ -17,6 +17,7 @@ DENSITY = {"beta": 0, "gauss": 1}
 ROT_KIND = {"dense": 0, "wht": 1}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE = {"mse": 0, "prod": 1}
+LAYOUT = {"rows": 0, "blocked": 1}
 
 
 class TQError(RuntimeError):
@@ -27,7 +28,7 @@ class TQError(RuntimeError):
 
 class tq_packed(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("layout", ctypes.c_int32), ("n", ctypes.c_int64),
                 ("idx", ctypes.c_void_p), ("norms", ctypes.c_void_p),
                 ("qjl", ctypes.c_void_p), ("rnorms", ctypes.c_void_p)]
 
@@ -59,6 +60,10 @@ SIGNATURES = {
     "tq_qjl_from_matrix": (_I, [_I, _P, _P, ctypes.POINTER(_P)]),
     "tq_qjl_free": (None, [_P]),
     "tq_packed_words": (_SZ, [_I, _I]),
+    "tq_packed_idx_words": (_SZ, [_I64, _I, _I, _I]),
+    "tq_decode_attn_workspace": (_SZ, [_I, _I, _I, _I64, _I]),
+    "tq_decode_attn": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed), _P, _P,
+                            _P, _P, ctypes.c_float, _P, _P, _SZ, _P]),
     "tq_encode": (_I, [_P, _I, _I64, _I, _I, _I, _P, _P, _P, ctypes.POINTER(tq_packed), _P]),
     "tq_rotate": (_I, [_P, _I, _I64, _I, _P, _P, _P, _P]),
     "tq_quantize_rotated": (_I, [_P, _I64, _I, _P, _P, _P]),

@@ -244,6 +244,26 @@ inline float bf16_to_f(uint16_t h) {
   return f;
 }
 
+// B-operand fragments of M^T for the token-row product (x M^T): lane (n, g), instruction s,
+// element e holds M[8 n + cb][32 g + 8 s + e].
+void build_fragments_t(const double* m, double scale, std::vector<uint16_t>& out) {
+  out.assign(2 * (size_t)tq::kFragElems, 0);
+  for (int cb = 0; cb < 8; ++cb)
+    for (int s = 0; s < 4; ++s)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          int nn = lane % 16, g = lane / 16;
+          int row = 8 * nn + cb;
+          int col = 32 * g + 8 * s + e;
+          float v = (float)(m[(size_t)row * 128 + col] * scale);
+          uint16_t hi = bf16_rne(v);
+          uint16_t lo = bf16_rne(v - bf16_to_f(hi));
+          size_t idx = (((size_t)cb * 4 + s) * 64 + lane) * 8 + e;
+          out[idx] = hi;
+          out[(size_t)tq::kFragElems + idx] = lo;
+        }
+}
+
 // Fragments of the d = 128 matrix m (row-major fp64) scaled by `scale`.
 void build_fragments(const double* m, double scale, std::vector<uint16_t>& out) {
   out.assign(2 * (size_t)tq::kFragElems, 0);
@@ -282,6 +302,7 @@ void free_rotation(tq_rotation_s* r) {
   if (r->r32_dev) hipFree(r->r32_dev);
   if (r->rt32_dev) hipFree(r->rt32_dev);
   if (r->frag_dev) hipFree(r->frag_dev);
+  if (r->fragt_dev) hipFree(r->fragt_dev);
   delete r;
 }
 
@@ -306,18 +327,22 @@ tq_status finish_rotation(tq_rotation_s* r) {
   st = upload(rt32, &r->rt32_dev, "upload rotation transpose");
   if (st != TQ_OK) return st;
   if (d == tq::kFragD) {
-    std::vector<uint16_t> frag;
+    std::vector<uint16_t> frag, fragt;
     if (r->kind == TQ_ROT_WHT) {
       // sqrt(d) R = H diag(sigma) has entries +-1: exact in bf16, one pass, scale after.
       build_fragments(r->r.data(), std::sqrt((double)d), frag);
+      build_fragments_t(r->r.data(), std::sqrt((double)d), fragt);
       r->passes = 1;
       r->post_scale = (float)(1.0 / std::sqrt((double)d));
     } else {
       build_fragments(r->r.data(), 1.0, frag);
+      build_fragments_t(r->r.data(), 1.0, fragt);
       r->passes = 2;
       r->post_scale = 1.0f;
     }
     st = upload(frag, &r->frag_dev, "upload rotation fragments");
+    if (st != TQ_OK) return st;
+    st = upload(fragt, &r->fragt_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
   }
   return TQ_OK;
@@ -528,12 +553,22 @@ size_t tq_packed_words(int d, int bits) {
   return (size_t)d * bits / 32;
 }
 
+size_t tq_packed_idx_words(int64_t n, int d, int bits, tq_layout layout) {
+  if (n < 0 || d <= 0 || bits <= 0 || ((int64_t)d * bits) % 32 != 0) return 0;
+  if (layout == TQ_LAYOUT_ROWS) return (size_t)n * d * bits / 32;
+  if (layout == TQ_LAYOUT_TOKEN_BLOCKED) return (size_t)((n + 31) / 32) * d * bits;
+  return 0;
+}
+
 static tq_status check_packed(const tq_packed* p, int d, int bits, int mode, const char* fn) {
   if (!p) return fail(TQ_EINVAL, "%s: null packed descriptor", fn);
   if (p->d != d) return fail(TQ_ESHAPE, "%s: packed d=%d, expected %d", fn, p->d, d);
   if (p->bits != bits) return fail(TQ_ESHAPE, "%s: packed bits=%d, codebook has %d", fn, p->bits, bits);
   if (p->mode != mode) return fail(TQ_EINVAL, "%s: packed mode mismatch", fn);
-  if (p->reserved != 0) return fail(TQ_EINVAL, "%s: reserved field must be 0", fn);
+  if (p->layout != TQ_LAYOUT_ROWS && p->layout != TQ_LAYOUT_TOKEN_BLOCKED)
+    return fail(TQ_EINVAL, "%s: bad layout", fn);
+  if (p->layout == TQ_LAYOUT_TOKEN_BLOCKED && mode != TQ_MODE_MSE)
+    return fail(TQ_EUNSUPPORTED, "%s: the token-blocked layout holds MSE data only", fn);
   if (p->n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
   if (p->n > 0 && (!p->idx || !p->norms)) return fail(TQ_EINVAL, "%s: null idx/norms", fn);
   if (mode == TQ_MODE_PROD && p->n > 0 && (!p->qjl || !p->rnorms))
@@ -568,6 +603,10 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   if (st != TQ_OK) return st;
   if (out->n != n) return fail(TQ_ESHAPE, "%s: out->n=%lld, n=%lld", fn, (long long)out->n, (long long)n);
   if (n == 0) return ok();
+  if (out->layout == TQ_LAYOUT_TOKEN_BLOCKED)
+    return check_launch(tq::launch_encode_vblock_d128(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx,
+                                                      out->norms, as_stream(stream)),
+                        fn);
   return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, mode == TQ_MODE_PROD ? qjl : nullptr,
                                              cb->args, out->idx, out->norms,
                                              mode == TQ_MODE_PROD ? out->qjl : nullptr,
@@ -642,6 +681,7 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
   const int d = rot->d;
   tq_status st = check_packed(K, d, cb->b, K->mode, fn);
   if (st != TQ_OK) return st;
+  if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: keys must use the ROWS layout", fn);
   if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, rotation d=%d", fn, cb->d, d);
   if (K->n != (int64_t)B * Hkv * T) return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*T=%lld", fn, (long long)K->n, (long long)B * Hkv * T);
   if (K->mode == TQ_MODE_PROD) {
@@ -659,6 +699,43 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
   return check_launch(tq::launch_scores(q_dev, B, Hq, Hkv, T, K, cb->args, rot, qjl, scores_dev, ws_dev,
                                         as_stream(stream)),
+                      fn);
+}
+
+size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || d <= 0) return 0;
+  return tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
+}
+
+tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                         tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
+                         void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_decode_attn";
+  if (!K || !V || !cb_k || !cb_v || !rot_k || !rot_v) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (T < 1) return fail(TQ_EINVAL, "%s: attention over an empty cache (T=%lld)", fn, (long long)T);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  const int ratio = Hq / Hkv;
+  if (ratio != 1 && ratio != 2 && ratio != 4) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not in {1, 2, 4}", fn, ratio);
+  const int d = rot_k->d;
+  if (rot_v->d != d || cb_k->d != d || cb_v->d != d) return fail(TQ_ESHAPE, "%s: d mismatch between handles", fn);
+  tq_status st = check_packed(K, d, cb_k->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  st = check_packed(V, d, cb_v->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: K must use the ROWS layout", fn);
+  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED) return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout", fn);
+  const int64_t n = (int64_t)B * Hkv * T;
+  if (K->n != n || V->n != n) return fail(TQ_ESHAPE, "%s: K->n=%lld, V->n=%lld, B*Hkv*T=%lld", fn, (long long)K->n, (long long)V->n, (long long)n);
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv above 65535", fn);
+  if ((int64_t)B * Hq == 0) return ok();
+  if (!q_dev || !out_dev) return fail(TQ_EINVAL, "%s: null q or out", fn);
+  size_t need = tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_decode_attn(q_dev, B, Hq, Hkv, T, K, V, cb_k->args, cb_v->args, rot_k, rot_v,
+                                             scale, out_dev, ws_dev, as_stream(stream)),
                       fn);
 }
 

@@ -54,6 +54,8 @@ struct tq_rotation_s {
   float* r32_dev = nullptr;       // fp32 R, row-major [d, d]
   float* rt32_dev = nullptr;      // fp32 R^T, row-major [d, d] (coalesced query rotation)
   uint16_t* frag_dev = nullptr;   // bf16 fragments [2][kFragElems] (d = 128 only)
+  uint16_t* fragt_dev = nullptr;  // bf16 B-operand fragments of R^T [2][kFragElems] (d = 128):
+                                  // [pass][cb][s][lane][e] = R[8*(lane%16) + cb][32*(lane/16) + 8s + e]
   int passes = 2;                 // 1 when R is exactly representable after scaling
   float post_scale = 1.0f;        // y = post_scale * (fragments . x)
 };
@@ -79,6 +81,13 @@ hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const Codeb
                                    uint32_t* idx, hipStream_t st);
 hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
                          const tq_qjl_s* qjl, float* xhat, hipStream_t st);
+hipError_t launch_encode_vblock_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                     const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);
+hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                              const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
+                              const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale,
+                              float* out, void* ws, hipStream_t st);
+size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d);
 hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st);

@@ -28,7 +28,8 @@ from .rotation import (dense_rotation, wht_rotation, sylvester_hadamard,
                        rotation_from_matrix)
 from .codebook import (Codebook, lloyd_max_points, coordinate_weights, codebook,
                        codebook_from_values)
-from .quantizer import (nearest_index, pack_bits, unpack_bits, encode_mse, decode_mse,
+from .quantizer import (nearest_index, pack_bits, unpack_bits, pack_token_blocked,
+                        unpack_token_blocked, encode_mse, decode_mse,
                         encode_prod, decode_prod, qjl_matrix, qjl_encode, qjl_correction, scores_mse, scores_prod,
                         quantize_rotated, EncodedMSE, EncodedProd, QJL_CONST)
 from .attention import decode_attention, topk
@@ -37,7 +38,7 @@ __all__ = [
     "splitmix64", "uniform53", "gaussian", "rademacher",
     "dense_rotation", "wht_rotation", "sylvester_hadamard", "rotation_from_matrix",
     "Codebook", "lloyd_max_points", "coordinate_weights", "codebook", "codebook_from_values",
-    "nearest_index", "pack_bits", "unpack_bits", "encode_mse", "decode_mse", "encode_prod",
+    "nearest_index", "pack_bits", "unpack_bits", "pack_token_blocked", "unpack_token_blocked", "encode_mse", "decode_mse", "encode_prod",
     "decode_prod", "qjl_matrix", "qjl_encode", "qjl_correction", "scores_mse", "scores_prod", "quantize_rotated",
     "EncodedMSE", "EncodedProd", "QJL_CONST",
     "decode_attention", "topk",

@@ -68,6 +68,34 @@ def unpack_bits(words, d, b):
     return idx.astype(np.int64)
 
 
+def pack_token_blocked(idx, b):
+    """Token-blocked layout of b-bit indices idx [n, d] (the layout the decode-attention value
+    cache uses; the pages fix no layout, this is the library's documented reading).
+
+    Rows are grouped in blocks of 32 (rows past n are index 0).  Inside block beta, chunk
+    (o, c) for octet o = 0..3 and coordinate c = 0..d-1 sits at chunk position o * d + c and
+    holds the indices of rows 32 beta + 8 o + e, e = 0..7, at coordinate c, LSB-first (row e at
+    chunk bits [b e, b e + b)).  Chunks of 8 b bits are concatenated LSB-first into the block's
+    stream of 32 d b bits = d b words.  Returns uint32 [ceil(n / 32), d * b].
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    nblk = (n + 31) // 32
+    pad = np.zeros((nblk * 32, d), dtype=np.int64)
+    pad[:n] = idx
+    blocks = pad.reshape(nblk, 4, 8, d)                # [beta, o, e, c]
+    chunks = blocks.transpose(0, 1, 3, 2)               # [beta, o, c, e]: chunk (o, c), row e
+    return pack_bits(chunks.reshape(nblk, 4 * d * 8), b)
+
+
+def unpack_token_blocked(words, n, d, b):
+    """Inverse of pack_token_blocked: uint32 [ceil(n / 32), d b] -> indices [n, d]."""
+    words = np.asarray(words, dtype=np.uint32)
+    nblk = (n + 31) // 32
+    chunks = unpack_bits(words.reshape(nblk, d * b), 4 * d * 8, b).reshape(nblk, 4, d, 8)
+    return chunks.transpose(0, 1, 3, 2).reshape(nblk * 32, d)[:n]
+
+
 @dataclass
 class EncodedMSE:
     idx: np.ndarray      # [..., d] int64 centroid indices

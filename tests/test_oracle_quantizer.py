@@ -66,6 +66,41 @@ def test_pack_three_bit_straddle():
         oracle.pack_bits(np.full(32, 8), 3)
 
 
+def _token_blocked_bruteforce(idx, b):
+    n, d = idx.shape
+    nblk = (n + 31) // 32
+    out = []
+    for beta in range(nblk):
+        bits = []
+        for o in range(4):
+            for c in range(d):
+                for e in range(8):
+                    r = 32 * beta + 8 * o + e
+                    v = int(idx[r, c]) if r < n else 0
+                    bits.extend((v >> j) & 1 for j in range(b))
+        out.append([sum(bits[32 * w + i] << i for i in range(32)) for w in range(len(bits) // 32)])
+    return out
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [32, 45, 70])
+def test_token_blocked_layout(b, n):
+    d = 32
+    idx = np.random.default_rng(n * b).integers(0, 1 << b, size=(n, d))
+    w = oracle.pack_token_blocked(idx, b)
+    assert w.shape == ((n + 31) // 32, d * b)
+    assert w.tolist() == _token_blocked_bruteforce(idx, b)
+    np.testing.assert_array_equal(oracle.unpack_token_blocked(w, n, d, b), idx)
+
+
+def test_token_blocked_first_chunk():
+    # rows 0..7 at coordinate 0 form the first chunk: 2-bit indices 0,1,2,3,0,1,2,3 -> 0xE4E4
+    idx = np.zeros((32, 4), dtype=np.int64)
+    idx[:8, 0] = [0, 1, 2, 3, 0, 1, 2, 3]
+    w = oracle.pack_token_blocked(idx, 2)
+    assert int(w[0, 0]) & 0xFFFF == 0xE4E4
+
+
 def test_zero_vector():
     d = 128
     cb = oracle.codebook(d, 3)
