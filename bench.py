@@ -96,6 +96,83 @@ def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
                       f"and scored by their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
 
 
+def _timed(fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_other(name, steps, warmup):
+    """Per-kernel timing of the other workloads (prod scores, decode attention): not the
+    headline line; reports algorithmic GB/s against the HBM peak."""
+    import torch
+    import kv_cache_compression_turboquant_amd as tq
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    res = {"config": name}
+    if name in ("c3", "c3wht"):
+        cfg = wl.CONFIGS["c3"]
+        kind = "wht" if name == "c3wht" else "dense"
+        n = cfg.B * cfg.hkv * cfg.T
+        keys = torch.from_numpy(wl.kv_keys(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        rot = tq.make_rotation(cfg.d, 1, kind)
+        qjl = tq.make_qjl(cfg.d, 2, rot)
+        cb = tq.codebook(cfg.d, cfg.bits - 1)
+        nbuf = 3
+        packs = [tq.alloc_packed(n, cfg.d, cfg.bits - 1, "prod", device=dev) for _ in range(nbuf)]
+        outs = [torch.empty((cfg.B, cfg.hq, cfg.T), device=dev) for _ in range(nbuf)]
+        ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
+        enc_ms = _timed(lambda i: tq.encode(keys, cfg.bits, "prod", cb, rot, qjl, out=packs[i % nbuf]), steps, warmup)
+        sc_ms = _timed(lambda i: tq.scores(q, packs[i % nbuf], cfg.hkv, cb, rot, qjl, out=outs[i % nbuf], ws=ws),
+                       steps, warmup)
+        enc_bytes = n * (cfg.d * 2 + 48 + 16 + 8)
+        sc_bytes = n * 72 + q.numel() * 4 + outs[0].numel() * 4
+        res.update({"rotation": kind, "encode_ms": enc_ms, "encode_gbs": enc_bytes / enc_ms / 1e6,
+                    "encode_vectors_per_s": n / enc_ms * 1e3,
+                    "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
+                    "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
+                    "scores_per_s": outs[0].numel() / sc_ms * 1e3})
+    elif name in ("c4b2", "c4b4"):
+        cfg = wl.CONFIGS["c4"]
+        b = 2 if name == "c4b2" else 4
+        n = cfg.B * cfg.hkv * cfg.T
+        rot = tq.make_rotation(cfg.d, 1)
+        cb = tq.codebook(cfg.d, b)
+        kx = torch.from_numpy(wl.kv_keys(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        nbuf = 2
+        Ks = [tq.encode(kx, b, "mse", cb, rot)]
+        Ks.append(tq.alloc_packed(n, cfg.d, b, "mse", device=dev))
+        Ks[1].idx.copy_(Ks[0].idx); Ks[1].norms.copy_(Ks[0].norms)
+        del kx
+        vx = torch.from_numpy(wl.kv_values(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        enc_v_ms = _timed(lambda i: tq.encode(vx, b, "mse", cb, rot, layout="blocked"), 3, 1)
+        Vs = [tq.encode(vx, b, "mse", cb, rot, layout="blocked")]
+        Vs.append(tq.alloc_packed(n, cfg.d, b, "mse", device=dev, layout="blocked"))
+        Vs[1].idx.copy_(Vs[0].idx); Vs[1].norms.copy_(Vs[0].norms)
+        del vx
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        out = torch.empty((cfg.B, cfg.hq, cfg.d), device=dev)
+        ws = torch.empty(tq.decode_attn_workspace(cfg.B, cfg.hq, cfg.hkv, cfg.T, cfg.d), dtype=torch.uint8, device=dev)
+        at_ms = _timed(lambda i: tq.decode_attn(q, Ks[i % nbuf], Vs[i % nbuf], cfg.hkv, cb, cb, rot, rot, out=out, ws=ws),
+                       steps, warmup)
+        words = cfg.d * b // 32
+        bytes_ = 2 * n * (words * 4 + 4) + q.numel() * 4 + out.numel() * 4
+        res.update({"bits": b, "encode_v_blocked_ms": enc_v_ms, "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6,
+                    "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
+                    "kv_positions_per_s": n / at_ms * 1e3})
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +180,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4"],
+                    help="c2 = the headline step; the others print per-kernel timings only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -116,6 +195,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.config != "c2":
+        bench_other(args.config, args.steps, args.warmup)
+        return
     dev = torch.device("cuda:0")
     cfg = wl.CONFIGS["c2"]
     n = cfg.B * cfg.hkv * cfg.T

@@ -460,6 +460,36 @@ __global__ void k_decode(const uint32_t* __restrict__ idx, const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------
+// QJL sign bits as an fp16 MFMA operand without a table.  A lane's 32 sign bits z (coordinates
+// 32 g + j at bit j) become 16 dwords: dword d holds the bits of coordinates d and 16 + d, taken
+// in place at bit positions m and m + 16 of (d < 8 ? z << 8 : z), m = (d < 8 ? d + 8 : d), and
+// OR-ed into a base pattern so that each half is the fp16 value alpha_m + beta_m * bit.  The
+// query side carries q_s / beta_m in the same slot order, and the per-head constant
+// K = sum_i q_s,i (1 + 2 alpha_i / beta_i) turns the product D into <q_s, 2 z - 1> = 2 D - K.
+// ---------------------------------------------------------------------------------------
+__device__ __constant__ float kSignAlpha[8] = {1.f, 1.f, 0.5f, 0.25f, 0.0625f, 0.00390625f, 0.f, 1.f};
+__device__ __constant__ float kSignBeta[8] = {0.25f, 0.5f, 0.5f, 0.75f, 0.9375f, 0.99609375f, 2.f, -2.f};
+__device__ __constant__ uint32_t kSignBase[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
+                                                 0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
+
+// Slot order of the sign operand: element e of instruction s <-> local coordinate.
+__host__ __device__ __forceinline__ int sign_slot_coord(int s, int e) { return (4 * s + (e >> 1)) + 16 * (e & 1); }
+// Mask position index (m - 8) of dword d.
+__host__ __device__ __forceinline__ int sign_slot_mpos(int d) { return d < 8 ? d : d - 8; }
+
+__device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
+  const uint32_t zl = z << 8;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    const int m = d < 8 ? d + 8 : d;
+    const uint32_t src = d < 8 ? zl : z;
+    const uint32_t bases[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
+                               0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
+    bz[d >> 2][d & 3] = (src & ((1u << m) | (1u << (m + 16)))) | bases[m - 8];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Query prologue, d = 128: for each (batch, kv head) block, q_rot = R q and q_s = S q of the
 // heads sharing the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][128], part = 0
 // rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo.  Reads R^T / S^T so that thread j's loads of
@@ -467,7 +497,7 @@ __global__ void k_decode(const uint32_t* __restrict__ idx, const float* __restri
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
                                                   const float* __restrict__ rt, const float* __restrict__ st,
-                                                  uint16_t* __restrict__ ws) {
+                                                  uint16_t* __restrict__ ws, float* __restrict__ kconst) {
   __shared__ float qs[4][128];
   __shared__ float part[2][2][4][128];
   const int Hkv = Hq / ratio;
@@ -502,6 +532,12 @@ __global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, i
       part[1][half][i][j] = as[i];
     }
     __syncthreads();
+    if (st) {
+      // sketch in sign-slot order: slot (s, e) of lane group G holds coordinate 32 G + c(s, e)
+      if (half == 0)
+        for (int i = 0; i < 4; ++i) part[1][1][i][j] = part[1][0][i][j] + part[1][1][i][j];
+      __syncthreads();
+    }
     if (half == 0) {
       for (int i = 0; i < nh; ++i) {
         uint16_t* o = ws + ((int64_t)b * Hq + h0 + hc + i) * 4 * 128;
@@ -511,11 +547,32 @@ __global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, i
         o[j] = __builtin_bit_cast(uint16_t, ah);
         o[128 + j] = __builtin_bit_cast(uint16_t, al);
         if (st) {
-          const float c = part[1][0][i][j] + part[1][1][i][j];
-          const _Float16 ch = (_Float16)c;
-          const _Float16 cl = (_Float16)(c - (float)ch);
+          // output slot j = 32 G + 8 s + e  <-  coordinate 32 G + c(s, e), scaled by 1 / beta
+          const int G = j >> 5, s8 = (j & 31) >> 3, e = j & 7;
+          const int c = 32 * G + sign_slot_coord(s8, e);
+          const int mp = sign_slot_mpos(4 * s8 + (e >> 1));
+          const float v = part[1][1][i][c] / kSignBeta[mp];
+          const _Float16 ch = (_Float16)v;
+          const _Float16 cl = (_Float16)(v - (float)ch);
           o[256 + j] = __builtin_bit_cast(uint16_t, ch);
           o[384 + j] = __builtin_bit_cast(uint16_t, cl);
+        }
+      }
+    }
+    if (st) {
+      __syncthreads();
+      // per-head constant K = sum_i q_s,i (1 + 2 alpha_i / beta_i), reduced by wave 0
+      if (threadIdx.x < 64) {
+        for (int i = 0; i < nh; ++i) {
+          float acc = 0.f;
+          for (int c = threadIdx.x; c < 128; c += 64) {
+            const int jl = c & 31;                     // local coordinate within its group
+            const int d = jl < 16 ? jl : jl - 16;      // dword holding it
+            const int mp = sign_slot_mpos(d);
+            acc += part[1][1][i][c] * (1.f + 2.f * kSignAlpha[mp] / kSignBeta[mp]);
+          }
+          for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+          if (threadIdx.x == 0) kconst[(int64_t)b * Hq + h0 + hc + i] = acc;
         }
       }
     }
@@ -530,6 +587,7 @@ __global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, i
 // F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass.
 // ---------------------------------------------------------------------------------------
 constexpr int kScoreWaves = 4;
+constexpr int kScoreBatch = 8;
 
 template <int BITS>
 struct DecodeTable {
@@ -634,25 +692,48 @@ __device__ __forceinline__ void build_table(uint8_t* tab, const _Float16* cent) 
 }
 
 template <int BITS, bool PROD>
+struct KeyTile {
+  uint32_t w[BITS];
+  float nrm;
+  uint32_t zw;
+  float gam;
+};
+
+// Lane (n, g) share of key tile `tile` of one sequence: its BITS words (coordinates 32 g ..),
+// norm, and for prod its sign word and scaled residual norm.  Rows past T are clamped.
+template <int BITS, bool PROD>
+__device__ __forceinline__ void load_key_tile(const uint32_t* __restrict__ idx, const float* __restrict__ norms,
+                                              const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms,
+                                              int64_t base_row, int64_t T, int64_t tile, int nl, int g,
+                                              KeyTile<BITS, PROD>& k) {
+  int64_t t = tile * 16 + nl;
+  t = t < T ? t : T - 1;
+  const int64_t row = base_row + t;
+  const uint32_t* src = idx + row * (4 * BITS) + BITS * g;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) k.w[j] = src[j];
+  k.nrm = norms[row];
+  if constexpr (PROD) {
+    k.zw = qbits[row * 4 + g];
+    k.gam = rnorms[row] * (kQjl / 128.0f);
+  } else {
+    k.zw = 0;
+    k.gam = 0.f;
+  }
+}
+
+template <int BITS, bool PROD>
 __global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
-    const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int tiles_per_wave,
+    const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
     const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
     float* __restrict__ scores) {
   using DT = DecodeTable<BITS>;
   __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t stab[PROD ? 4096 : 16];
   __shared__ _Float16 cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
   __syncthreads();
   build_table<BITS>(tab, cent);
-  if constexpr (PROD) {
-    for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(stab + e * 16);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = ((e >> j) & 1) ? 0x3c00u : 0xbc00u;  // +1 / -1
-    }
-  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -686,30 +767,25 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
   };
   u32x4 am0[4], aq0[4];
   load_a(0, am0, aq0);
+  // sketch constant K of the lane's head (4 hg + g) after the reduction
+  auto load_kc = [&](int hg) -> float {
+    const int h = 4 * hg + g;
+    return (PROD && h < ratio) ? kconst[(int64_t)b * Hq + kvh * ratio + h] : 0.f;
+  };
+  const float kc0 = load_kc(0);
 
-  for (int64_t ti = 0; ti < tiles_per_wave; ++ti) {
+  // Ping-pong over two tile buffers (no register copies), so the next tile's loads stay in flight
+  // while the current one is scored and the wait before scoring counts only the older loads.
+  auto score_tile = [&](const KeyTile<BITS, PROD>& cur, int64_t ti) {
     const int64_t tile = tile0 + ti;
-    if (tile >= ntiles_seq) break;
     const int64_t t = tile * 16 + nl;
     const bool valid = t < T;
-    const int64_t row = base_row + (valid ? t : T - 1);
-    uint32_t w[BITS];
-    const uint32_t* src = idx + row * (4 * BITS) + BITS * g;
-#pragma unroll
-    for (int j = 0; j < BITS; ++j) w[j] = src[j];
-    const float nrm = norms[row];
-    uint32_t zw = 0;
-    float gam = 0.f;
-    if constexpr (PROD) {
-      zw = qbits[row * 4 + g];
-      gam = rnorms[row] * (kQjl / 128.0f);
-    }
+    const float nrm = cur.nrm;
+    const float gam = cur.gam;
     u32x4 bk[4], bz[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bk[s] = decode_keys<BITS>(w, s, tab);
-      if constexpr (PROD) bz[s] = *reinterpret_cast<const u32x4*>(stab + ((zw >> (8 * s)) & 0xffu) * 16);
-    }
+    for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS>(cur.w, s, tab);
+    if constexpr (PROD) sign_operand(cur.zw, bz);
     for (int hg = 0; hg < groups; ++hg) {
       u32x4 am[4], aq[4];
       if (hg == 0) {
@@ -724,7 +800,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
         acc = mfma_f16(am[s], bk[s], acc);
         if constexpr (PROD) acc = mfma_f16(aq[s], bz[s], acc);
       }
-      const float sc = g < 2 ? nrm : gam;
+      const float sc = g < 2 ? nrm : 2.f * gam;
       const float v0 = acc[0] * sc, v1 = acc[1] * sc, v2 = acc[2] * sc, v3 = acc[3] * sc;
       const bool lowg = g < 2;
       float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
@@ -736,8 +812,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
       const float other = odd ? k0 : k1;
       mine += __shfl_xor(other, 16);
       const int h = 4 * hg + g;
+      if constexpr (PROD) mine -= gam * (hg == 0 ? kc0 : load_kc(hg));
       if (valid && h < ratio) scores[((int64_t)b * Hq + kvh * ratio + h) * T + t] = mine;
     }
+  };
+  // Batches of kScoreBatch tiles: every load of a batch is issued before any tile of it is
+  // scored (straight-line code, so the waits are exact), and the batch's latency is paid once.
+  int64_t last = tiles_per_wave;
+  if (ntiles_seq - tile0 < last) last = ntiles_seq - tile0;
+  for (int64_t tb = 0; tb < last; tb += kScoreBatch) {
+    KeyTile<BITS, PROD> kt[kScoreBatch];
+#pragma unroll
+    for (int u = 0; u < kScoreBatch; ++u)
+      load_key_tile<BITS, PROD>(idx, norms, qbits, rnorms, base_row, T, tile0 + tb + u, nl, g, kt[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kScoreBatch; ++u)
+      if (tb + u < last) score_tile(kt[u], tb + u);
   }
 }
 
@@ -746,12 +837,12 @@ hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, cons
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st) {
   const int ratio = Hq / Hkv;
-  const int d = 128;
   uint16_t* qws = static_cast<uint16_t*>(ws);
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
   const int qthreads = 256;
-  (void)d;
   hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(qthreads), 0, st, q, Hq, ratio, rot->rt32_dev,
-                     PROD ? qjl->st32_dev : nullptr, qws);
+                     PROD ? qjl->st32_dev : nullptr, qws, kconst);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tiles = (T + 15) / 16;
@@ -759,11 +850,12 @@ hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, cons
   const int64_t target = (int64_t)num_cus() * 4;
   const int64_t seqs = (int64_t)B * Hkv;
   int64_t tpw = (tiles * seqs + target * kScoreWaves - 1) / (target * kScoreWaves);
-  if (tpw < 1) tpw = 1;
+  tpw = (tpw + kScoreBatch - 1) / kScoreBatch * kScoreBatch;
+  if (tpw < kScoreBatch) tpw = kScoreBatch;
   if (tpw > 64) tpw = 64;
   const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
   hipLaunchKernelGGL((k_scores_d128<BITS, PROD>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
-                     0, st, qws, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
+                     0, st, qws, kconst, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
                      PROD ? K->rnorms : nullptr, cb, scores);
   return hipGetLastError();
 }
@@ -951,6 +1043,35 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 constexpr int kAttnStepsPerBlock = 64;
 constexpr int kAttnPart = 130;  // max, sum, 128 accumulators
 
+// One 32-token step of a wave: the lane's key words and norms for both 16-token tiles, the
+// value norms, and the value chunks of octet g at coordinates 8 n .. 8 n + 7.
+template <int KB, int VB>
+struct AttnStep {
+  uint32_t kw[2][KB];
+  float kn[2];
+  float vn[2];
+  uint32_t vw[2 * VB];
+};
+
+template <int KB, int VB>
+__device__ __forceinline__ void load_attn_step(const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
+                                               const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm,
+                                               int64_t nrows, int64_t blk, int nl, int g, AttnStep<KB, VB>& st) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t r = blk * 32 + tt * 16 + nl;
+    const int64_t rl = r < nrows ? r : nrows - 1;
+    const uint32_t* src = kidx + rl * (4 * KB) + KB * g;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) st.kw[tt][j] = src[j];
+    st.kn[tt] = knorm[rl];
+    st.vn[tt] = vnorm[rl];
+  }
+  const uint32_t* vs = vidx + blk * (128 * VB) + 32 * g * VB + 2 * nl * VB;
+#pragma unroll
+  for (int j = 0; j < 2 * VB; ++j) st.vw[j] = vs[j];
+}
+
 template <int KB, int VB>
 __global__ __launch_bounds__(256) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit,
@@ -1013,24 +1134,23 @@ __global__ __launch_bounds__(256) void k_attn_d128(
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Loads of the next 32-token step are issued before the current step is consumed.
+  AttnStep<KB, VB> cur, nxt;
+  if (wb < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, wb, nl, g, cur);
   for (int64_t blk = wb; blk < we; ++blk) {
+    if (blk + 1 < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, blk + 1, nl, g, nxt);
     float lg[2], svv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int64_t r = blk * 32 + tt * 16 + nl;
       const bool valid = r >= row0 && r < rowE;
-      const int64_t rl = r < nrows ? r : nrows - 1;
-      uint32_t w[KB];
-      const uint32_t* src = kidx + rl * (4 * KB) + KB * g;
-#pragma unroll
-      for (int j = 0; j < KB; ++j) w[j] = src[j];
-      const float sk = knorm[rl];
-      svv[tt] = vnorm[rl];
+      const float sk = cur.kn[tt];
+      svv[tt] = cur.vn[tt];
       f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 khi, klo;
-        decode8_2<KB>(w, 8 * KB * s, ktab, khi, klo);
+        decode8_2<KB>(cur.kw[tt], 8 * KB * s, ktab, khi, klo);
         d = mfma_f16(am[s], khi, d);
         d = mfma_f16(am2[s], klo, d);
       }
@@ -1086,16 +1206,11 @@ __global__ __launch_bounds__(256) void k_attn_d128(
       }
     }
     // B operand: the value chunks of octet g at coordinates 8 n .. 8 n + 7
-    uint32_t vw[2 * VB];
-    {
-      const uint32_t* src = vidx + blk * (128 * VB) + 32 * g * VB + 2 * nl * VB;
 #pragma unroll
-      for (int j = 0; j < 2 * VB; ++j) vw[j] = src[j];
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB>(vw, 8 * VB * c, vtab), acc[c]);
+    for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB>(cur.vw, 8 * VB * c, vtab), acc[c]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    cur = nxt;
   }
 
   // wave totals: sum over the 16 keys lanes; hi + lo accumulator rows
@@ -1174,7 +1289,8 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const 
   uint16_t* qws = static_cast<uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(256), 0, st, q, Hq, ratio, rot_k->rt32_dev, nullptr, qws);
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(256), 0, st, q, Hq, ratio, rot_k->rt32_dev, nullptr, qws,
+                     nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t steps = T / 32 + 2;
@@ -1290,7 +1406,11 @@ hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T,
   return hipErrorInvalidValue;
 }
 
-size_t scores_workspace_bytes(int B, int Hq, int d) { return (size_t)B * Hq * 4 * d * sizeof(uint16_t); }
+size_t scores_workspace_bytes(int B, int Hq, int d) {
+  (void)d;
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  return qbytes + (size_t)B * Hq * sizeof(float);
+}
 
 hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
