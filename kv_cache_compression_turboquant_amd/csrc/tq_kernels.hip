@@ -493,88 +493,106 @@ __device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
 // Query prologue, d = 128: for each (batch, kv head) block, q_rot = R q and q_s = S q of the
 // heads sharing the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][128], part = 0
 // rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo.  Reads R^T / S^T so that thread j's loads of
-// column j are coalesced; the 128 contraction steps are split over two thread halves.
+// column j are coalesced.  The 128 contraction steps are split over eight thread groups of 16
+// steps each, fully unrolled, so every load a thread needs is in flight at once (the kernel is
+// latency-bound, not bandwidth-bound); the partial sums meet in LDS.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
-                                                  const float* __restrict__ rt, const float* __restrict__ st,
-                                                  uint16_t* __restrict__ ws, float* __restrict__ kconst) {
+constexpr int kQprepParts = 8;
+constexpr int kQprepThreads = 128 * kQprepParts;
+
+__global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
+                                                            const float* __restrict__ rt,
+                                                            const float* __restrict__ st,
+                                                            uint16_t* __restrict__ ws,
+                                                            float* __restrict__ kconst) {
   __shared__ float qs[4][128];
-  __shared__ float part[2][2][4][128];
+  __shared__ float part[2][kQprepParts][4][128];
+  __shared__ float sum[2][4][128];
   const int Hkv = Hq / ratio;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int h0 = kvh * ratio;
-  const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
+  const int j = threadIdx.x & 127, p = threadIdx.x >> 7;
+  const int nmat = st ? 2 : 1;
   for (int hc = 0; hc < ratio; hc += 4) {
     const int nh = ratio - hc < 4 ? ratio - hc : 4;
     __syncthreads();
-    for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) {
-      const int hh = i >> 7;
-      qs[hh][i & 127] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + (i & 127)] : 0.f;
+    if (threadIdx.x < 512) {
+      const int hh = threadIdx.x >> 7;
+      qs[hh][j] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
     }
     __syncthreads();
+    const int k0 = p * (128 / kQprepParts);
+    float rv[128 / kQprepParts], sv[128 / kQprepParts];
+#pragma unroll
+    for (int k = 0; k < 128 / kQprepParts; ++k) rv[k] = rt[(k0 + k) * 128 + j];
+    if (st) {
+#pragma unroll
+      for (int k = 0; k < 128 / kQprepParts; ++k) sv[k] = st[(k0 + k) * 128 + j];
+    }
     float ar[4] = {0.f, 0.f, 0.f, 0.f}, as[4] = {0.f, 0.f, 0.f, 0.f};
-    const int k0 = half * 64;
-#pragma unroll 8
-    for (int k = k0; k < k0 + 64; ++k) {
-      const float r = rt[k * 128 + j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = fmaf(r, qs[i][k], ar[i]);
-      if (st) {
-        const float sv = st[k * 128 + j];
+    for (int k = 0; k < 128 / kQprepParts; ++k)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) as[i] = fmaf(sv, qs[i][k], as[i]);
-      }
+      for (int i = 0; i < 4; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
+    if (st) {
+#pragma unroll
+      for (int k = 0; k < 128 / kQprepParts; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) as[i] = fmaf(sv[k], qs[i][k0 + k], as[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      part[0][half][i][j] = ar[i];
-      part[1][half][i][j] = as[i];
+      part[0][p][i][j] = ar[i];
+      part[1][p][i][j] = as[i];
     }
     __syncthreads();
-    if (st) {
-      // sketch in sign-slot order: slot (s, e) of lane group G holds coordinate 32 G + c(s, e)
-      if (half == 0)
-        for (int i = 0; i < 4; ++i) part[1][1][i][j] = part[1][0][i][j] + part[1][1][i][j];
-      __syncthreads();
+    // threads (m, j), m < nmat: the full sum of matrix m for the four heads
+    if (threadIdx.x < 128 * nmat) {
+      const int m = threadIdx.x >> 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < kQprepParts; ++pp) a += part[m][pp][i][j];
+        sum[m][i][j] = a;
+      }
     }
-    if (half == 0) {
+    __syncthreads();
+    if (threadIdx.x < 128 * nmat) {
+      const int m = threadIdx.x >> 7;
       for (int i = 0; i < nh; ++i) {
         uint16_t* o = ws + ((int64_t)b * Hq + h0 + hc + i) * 4 * 128;
-        const float a = part[0][0][i][j] + part[0][1][i][j];
-        const _Float16 ah = (_Float16)a;
-        const _Float16 al = (_Float16)(a - (float)ah);
-        o[j] = __builtin_bit_cast(uint16_t, ah);
-        o[128 + j] = __builtin_bit_cast(uint16_t, al);
-        if (st) {
-          // output slot j = 32 G + 8 s + e  <-  coordinate 32 G + c(s, e), scaled by 1 / beta
+        float v;
+        int mp = 0;
+        if (m == 0) {
+          v = sum[0][i][j];
+        } else {
+          // sketch in sign-slot order: output slot j = 32 G + 8 s + e  <-  coordinate
+          // 32 G + c(s, e), scaled by 1 / beta
           const int G = j >> 5, s8 = (j & 31) >> 3, e = j & 7;
           const int c = 32 * G + sign_slot_coord(s8, e);
-          const int mp = sign_slot_mpos(4 * s8 + (e >> 1));
-          const float v = part[1][1][i][c] / kSignBeta[mp];
-          const _Float16 ch = (_Float16)v;
-          const _Float16 cl = (_Float16)(v - (float)ch);
-          o[256 + j] = __builtin_bit_cast(uint16_t, ch);
-          o[384 + j] = __builtin_bit_cast(uint16_t, cl);
+          mp = sign_slot_mpos(4 * s8 + (e >> 1));
+          v = sum[1][i][c] / kSignBeta[mp];
         }
+        const _Float16 vh = (_Float16)v;
+        const _Float16 vl = (_Float16)(v - (float)vh);
+        o[256 * m + j] = __builtin_bit_cast(uint16_t, vh);
+        o[256 * m + 128 + j] = __builtin_bit_cast(uint16_t, vl);
       }
     }
-    if (st) {
-      __syncthreads();
-      // per-head constant K = sum_i q_s,i (1 + 2 alpha_i / beta_i), reduced by wave 0
-      if (threadIdx.x < 64) {
-        for (int i = 0; i < nh; ++i) {
-          float acc = 0.f;
-          for (int c = threadIdx.x; c < 128; c += 64) {
-            const int jl = c & 31;                     // local coordinate within its group
-            const int d = jl < 16 ? jl : jl - 16;      // dword holding it
-            const int mp = sign_slot_mpos(d);
-            acc += part[1][1][i][c] * (1.f + 2.f * kSignAlpha[mp] / kSignBeta[mp]);
-          }
-          for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-          if (threadIdx.x == 0) kconst[(int64_t)b * Hq + h0 + hc + i] = acc;
-        }
+    if (st && threadIdx.x < 64 * nh) {
+      // per-head constant K = sum_i q_s,i (1 + 2 alpha_i / beta_i); wave i reduces head i
+      const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
+      float acc = 0.f;
+      for (int c = l; c < 128; c += 64) {
+        const int jl = c & 31;                     // local coordinate within its group
+        const int d = jl < 16 ? jl : jl - 16;      // dword holding it
+        const int mp = sign_slot_mpos(d);
+        acc += sum[1][i][c] * (1.f + 2.f * kSignAlpha[mp] / kSignBeta[mp]);
       }
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+      if (l == 0) kconst[(int64_t)b * Hq + h0 + hc + i] = acc;
     }
   }
 }
@@ -840,8 +858,7 @@ hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, cons
   uint16_t* qws = static_cast<uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-  const int qthreads = 256;
-  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(qthreads), 0, st, q, Hq, ratio, rot->rt32_dev,
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, ratio, rot->rt32_dev,
                      PROD ? qjl->st32_dev : nullptr, qws, kconst);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1253,31 +1270,58 @@ __global__ __launch_bounds__(256) void k_attn_d128(
 }
 
 // Merges the splits of one query head and maps back from V's rotated domain: out = R_V^T acc / L.
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hq, int Hkv,
-                                                      int nsplit, const float* __restrict__ r32v,
-                                                      float* __restrict__ out) {
+// 512 threads = 4 groups of 128 columns; the groups take every fourth split, then every fourth
+// quarter of the R_V^T product, so each thread's loads are independent and issued together.
+constexpr int kCombineThreads = 512;
+
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part, int Hq, int Hkv,
+                                                                  int nsplit, const float* __restrict__ r32v,
+                                                                  float* __restrict__ out) {
+  __shared__ float red[4][128];
+  __shared__ float lred[4];
+  __shared__ float wmax[kCombineThreads / 64];
   __shared__ float o[128];
   const int hg = blockIdx.x;
   const int b = hg / Hq, h = hg % Hq;
   const int ratio = Hq / Hkv;
   const int bh = b * Hkv + h / ratio, hl = h % ratio;
-  const int c = threadIdx.x;
-  const float* p = part + (int64_t)bh * nsplit * 4 * kAttnPart + hl * kAttnPart;
+  const int t = threadIdx.x, c = t & 127, pp = t >> 7;
+  const int64_t xs = 4 * kAttnPart;  // floats between consecutive splits of one head
+  const float* p = part + (int64_t)bh * nsplit * xs + hl * kAttnPart;
   float M = -INFINITY;
-  for (int x = 0; x < nsplit; ++x) M = fmaxf(M, p[(int64_t)x * 4 * kAttnPart]);
+  for (int x = t; x < nsplit; x += kCombineThreads) M = fmaxf(M, p[x * xs]);
+  for (int s = 32; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  if ((t & 63) == 0) wmax[t >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) M = fmaxf(M, wmax[w]);
   float L = 0.f, A = 0.f;
-  for (int x = 0; x < nsplit; ++x) {
-    const float mx = p[(int64_t)x * 4 * kAttnPart];
-    if (mx == -INFINITY) continue;
-    const float e = __expf(mx - M);
-    L = fmaf(p[(int64_t)x * 4 * kAttnPart + 1], e, L);
-    A = fmaf(p[(int64_t)x * 4 * kAttnPart + 2 + c], e, A);
+#pragma unroll 4
+  for (int x = pp; x < nsplit; x += 4) {
+    const float mx = p[x * xs];
+    const float l = p[x * xs + 1];
+    const float a = p[x * xs + 2 + c];
+    if (mx != -INFINITY) {
+      const float e = __expf(mx - M);
+      L = fmaf(l, e, L);
+      A = fmaf(a, e, A);
+    }
   }
-  o[c] = L > 0.f ? A / L : 0.f;
+  red[pp][c] = A;
+  if (c == 0) lred[pp] = L;
+  __syncthreads();
+  if (t < 128) {
+    const float a = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    const float l = (lred[0] + lred[1]) + (lred[2] + lred[3]);
+    o[t] = l > 0.f ? a / l : 0.f;
+  }
   __syncthreads();
   float y = 0.f;
-  for (int j = 0; j < 128; ++j) y = fmaf(r32v[j * 128 + c], o[j], y);
-  out[(int64_t)hg * 128 + c] = y;
+#pragma unroll
+  for (int j = 32 * pp; j < 32 * pp + 32; ++j) y = fmaf(r32v[j * 128 + c], o[j], y);
+  red[pp][c] = y;
+  __syncthreads();
+  if (t < 128) out[(int64_t)hg * 128 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
 }
 
 template <int KB, int VB>
@@ -1289,7 +1333,7 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const 
   uint16_t* qws = static_cast<uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(256), 0, st, q, Hq, ratio, rot_k->rt32_dev, nullptr, qws,
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, ratio, rot_k->rt32_dev, nullptr, qws,
                      nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1299,7 +1343,7 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const 
                      K->idx, K->norms, V->idx, V->norms, K->n, cbk, cbv, scale, part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(128), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
+  hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(kCombineThreads), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
   return hipGetLastError();
 }
 
