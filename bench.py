@@ -27,11 +27,14 @@ HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 1.5e9
 
 
+# sources that make up the headline encode kernel: its counters stay valid while these are unchanged
+HEADLINE_SOURCES = ("tq_device.h", "tq_internal.h", "tq_encode128.hip")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc"))):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(open(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc", f), "rb").read())
+    for f in HEADLINE_SOURCES:
+        h.update(open(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -49,6 +52,78 @@ def traffic_from_profile(kernel_key, launches_bytes_key):
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get(launches_bytes_key)
+
+
+COPY_PROBE_BYTES = 512 << 20
+HEADLINE_KERNEL = "k_encode_d128<3, false, true, false,"  # MSE b=3, bf16 keys, packed output
+
+
+def copy_probe(torch, dev, reps=3):
+    """Plain device-to-device copies of a known size: what FETCH_SIZE / WRITE_SIZE read for
+    them calibrates the counters against algorithmic bytes."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(db, counter):
+    import sqlite3
+    con = sqlite3.connect(db)
+    q = ("select k.name, p.value from counters_collection p join kernels k "
+         "on p.dispatch_id = k.dispatch_id where p.counter_name = ?")
+    out = {}
+    for name, v in con.execute(q, (counter,)).fetchall():
+        out.setdefault(name, []).append(float(v))
+    return out
+
+
+def _short(name):
+    return name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(")[0]
+
+
+def pmc_summary(fetch_db, write_db):
+    """HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by bytes / counted for the copy probe of the same run."""
+    fetch = _pmc_rows(fetch_db, "FETCH_SIZE")
+    write = _pmc_rows(write_db, "WRITE_SIZE")
+    probe_kib = COPY_PROBE_BYTES / 1024.0
+
+    def probe_factor(rows):
+        vals = [v for name, vs in rows.items() if "copy" in name.lower() for v in vs
+                if 0.5 * probe_kib < v < 2.0 * probe_kib]
+        if not vals:
+            raise SystemExit("pmc-summary: no copy-probe dispatch found (run bench.py with --copy-probe)")
+        return probe_kib / float(np.median(vals)), len(vals)
+
+    ff, nf = probe_factor(fetch)
+    fw, nw = probe_factor(write)
+    lines = [f"copy probe {COPY_PROBE_BYTES} B: FETCH_SIZE scale {ff:.4f} ({nf} dispatches), "
+             f"WRITE_SIZE scale {fw:.4f} ({nw} dispatches)",
+             f"{'kernel':60s} {'dispatches':>10s} {'fetch MB':>10s} {'write MB':>10s} {'HBM MB':>10s}"]
+    table = {}
+    for name in sorted(set(fetch) & set(write)):
+        if "copy" in name.lower() or "elementwise" in name.lower() or "fill" in name.lower():
+            continue
+        fb = float(np.mean(fetch[name])) * 1024.0 * ff
+        wb = float(np.mean(write[name])) * 1024.0 * fw
+        table[_short(name)] = (name, len(fetch[name]), fb, wb)
+        lines.append(f"{_short(name)[:60]:60s} {len(fetch[name]):10d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} "
+                     f"{(fb + wb) / 1e6:10.2f}")
+    head = [v for k, v in table.items() if v[0].startswith("void tq::(anonymous namespace)::" + HEADLINE_KERNEL)]
+    out = {"_note": "HBM bytes per dispatch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) x 1024, each "
+                    "scaled by the copy-probe factor; valid only for the kernel sources of source_hash",
+           "k_encode_d128:c2": None}
+    if head:
+        name, nd, fb, wb = head[0]
+        out["k_encode_d128:c2"] = {"kernel": name[:120], "dispatches": nd, "fetch_bytes": fb, "write_bytes": wb,
+                                   "hbm_bytes_per_launch": fb + wb, "fetch_scale": ff, "write_scale": fw,
+                                   "source_hash": kernel_source_hash()}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print("\n".join(lines))
 
 
 def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
@@ -182,7 +257,16 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4"],
                     help="c2 = the headline step; the others print per-kernel timings only")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "
+                         "(the calibration for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made with "
+                         "--copy-probe into profiles/traffic.json and print the table; no GPU needed")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described in the design notes, not built)", file=sys.stderr)
@@ -271,6 +355,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": enc_alg_bytes},
     }
+    if args.copy_probe:
+        copy_probe(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, keys_bits, q_np, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -1,0 +1,531 @@
+// Value-cache encode in the token-blocked layout and the fused decode attention at d = 128:
+// scores from packed K, online softmax, P V on MFMA in V's rotated domain, split merge and
+// the inverse rotation.
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// Token-blocked encode (the value-cache layout), d = 128, MSE.  The product is formed the
+// other way round, D[token][coordinate] = x R^T (A = x, straight from HBM; B = R^T fragments in
+// LDS), so lane (n, G) holds tokens 4 G .. 4 G + 3 of a 16-token tile at coordinates
+// 8 n .. 8 n + 7.  Two tiles make one 32-token block; a chunk (8 tokens at one coordinate) is
+// the lane's 4-token piece joined with the piece of lane (n, G ^ 1) after one exchange.
+// ---------------------------------------------------------------------------------------
+template <int BITS, bool BF16IN, int PASSES>
+__global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
+    const void* __restrict__ x, int64_t n, const u32x4* __restrict__ fragt, float post_scale,
+    CodebookArgs cb, uint32_t* __restrict__ idx_out, float* __restrict__ norms_out) {
+  constexpr int RP = PASSES;
+  constexpr int H = 1 << (BITS - 1);
+  constexpr int PB = 4 * BITS;              // bits of a 4-token piece
+  __shared__ u32x4 lds[RP * kFragU4];
+  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = fragt[i];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int h = g & 1;
+  const int64_t nblk = (n + 31) >> 5;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  if (blk >= nblk) return;  // no barrier follows
+  const float inv_post = 1.0f / post_scale;
+
+  RawTile<BF16IN> nxt[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) load_tile<BF16IN>(x, n, 2 * blk + t, nl, g, nxt[t]);
+
+  for (; blk < nblk; blk += stride) {
+    RawTile<BF16IN> cur[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) cur[t] = nxt[t];
+    if (blk + stride < nblk) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) load_tile<BF16IN>(x, n, 2 * (blk + stride) + t, nl, g, nxt[t]);
+    }
+    u32x4 ax[2][4], axl[2][4];
+    float srow[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float acc2 = 0.f;
+      if constexpr (BF16IN) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ax[t][s] = cur[t].v[s];
+          uint32_t wv[4];
+          __builtin_memcpy(wv, &cur[t].v[s], sizeof(wv));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 p = __builtin_bit_cast(bf16x2, wv[j]);
+            acc2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc2, false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 a = cur[t].v[2 * s], b = cur[t].v[2 * s + 1];
+          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+          u32x4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x2 pr = {v[2 * j], v[2 * j + 1]};
+            const uint32_t hh = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+            const f32x2 rem = {v[2 * j] - __uint_as_float(hh << 16), v[2 * j + 1] - __uint_as_float(hh & 0xffff0000u)};
+            hi[j] = hh;
+            lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+            acc2 = fmaf(v[2 * j], v[2 * j], acc2);
+            acc2 = fmaf(v[2 * j + 1], v[2 * j + 1], acc2);
+          }
+          ax[t][s] = hi;
+          axl[t][s] = lo;
+        }
+      }
+      acc2 += __shfl_xor(acc2, 16);
+      acc2 += __shfl_xor(acc2, 32);
+      srow[t] = sqrtf(acc2);
+      const int64_t row = (2 * blk + t) * 16 + nl;
+      if (g == 0 && row < n) norms_out[row] = srow[t];
+    }
+
+    f32x4 acc[2][8];
+    {
+      u32x4 cf[RP][4], nf[RP][4];
+      load_frags<RP>(lds, 0, lane, cf);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c + 1 < 8) load_frags<RP>(lds, c + 1, lane, nf);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            a = mfma_bf16(ax[t][s], cf[0][s], a);
+            if constexpr (!BF16IN) a = mfma_bf16(axl[t][s], cf[0][s], a);
+            if constexpr (RP == 2) a = mfma_bf16(ax[t][s], cf[1][s], a);
+          }
+          acc[t][c] = a;
+        }
+        if (c + 1 < 8) {
+#pragma unroll
+          for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cf[p][s] = nf[p][s];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // per-token thresholds for the lane's tokens 4 G + r
+      float thr[4][H > 1 ? H - 1 : 1];
+      bool tok_ok[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sr = __shfl(srow[t], 4 * g + r);
+        const bool live = sr > 0.f;
+        tok_ok[r] = (2 * blk + t) * 16 + 4 * g + r < n;
+#pragma unroll
+        for (int p = 0; p < H - 1; ++p) thr[r][p] = live ? __int_as_float(cb.tpos[p]) * (sr * inv_post) : INFINITY;
+      }
+      uint32_t P[BITS];
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) P[j] = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float yv = acc[t][c][r];
+          const float ay = fabsf(yv);
+          uint32_t m = 0;
+#pragma unroll
+          for (int p = 0; p < H - 1; ++p) m += (ay >= thr[r][p]) ? 1u : 0u;
+          const uint32_t sgn = (uint32_t)(__float_as_int(yv) >> 31);
+          const uint32_t id = tok_ok[r] ? (m ^ sgn) + (uint32_t)H : 0u;
+          const int pos = PB * c + BITS * r, wi = pos >> 5, sh = pos & 31;
+          P[wi] |= id << sh;
+          if (sh + BITS > 32) P[wi + 1] |= id >> (32 - sh);
+        }
+      uint32_t Q[BITS];
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) Q[j] = __shfl_xor(P[j], 16);
+      uint32_t O[BITS];
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) O[j] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // chunk for coordinate 8 n + 4 h + i: even-lane piece (tokens 0..3) | odd-lane piece << PB
+        const uint32_t pe0 = get_bits(P, PB * i, PB), pe1 = get_bits(P, PB * (4 + i), PB);
+        const uint32_t qe0 = get_bits(Q, PB * i, PB), qe1 = get_bits(Q, PB * (4 + i), PB);
+        const uint32_t even = h ? qe1 : pe0;
+        const uint32_t odd = h ? pe1 : qe0;
+        const uint64_t chunk = (uint64_t)even | ((uint64_t)odd << PB);
+        const int pos = 8 * BITS * i, wi = pos >> 5, sh = pos & 31;
+        O[wi] |= (uint32_t)(chunk << sh);
+        if (sh + 8 * BITS > 32) O[wi + 1] |= (uint32_t)(chunk >> (32 - sh));
+      }
+      const int o = 2 * t + (g >> 1);
+      uint32_t* dst = idx_out + blk * (128 * BITS) + 32 * o * BITS + (2 * nl + h) * BITS;
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) dst[j] = O[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused decode attention, d = 128.  Grid (split, b * Hkv), 4 waves per block.  Each wave walks
+// 32-token steps (aligned to the value cache's 32-row blocks): keys are scored like the score
+// kernel (lane (n, G) ends with head G's logit for key n), an online softmax keeps the running
+// max and sum per head, the weights (times the value norms) go through a wave-private LDS strip
+// to become the A operand (head rows, hi/lo fp16), and the value chunks decode straight into B
+// fragments (8 tokens of one coordinate), so P V accumulates on MFMA in V's rotated domain.
+// The block merges its waves and writes (max, sum, acc[128]) per head; k_attn_combine merges the
+// splits and applies R_V^T.
+// ---------------------------------------------------------------------------------------
+constexpr int kAttnStepsPerBlock = 64;
+constexpr int kAttnPart = 130;  // max, sum, 128 accumulators
+
+// One 32-token step of a wave: the lane's key words and norms for both 16-token tiles, the
+// value norms, and the value chunks of octet g at coordinates 8 n .. 8 n + 7.
+template <int KB, int VB>
+struct AttnStep {
+  uint32_t kw[2][KB];
+  float kn[2];
+  float vn[2];
+  uint32_t vw[2 * VB];
+};
+
+template <int KB, int VB>
+__device__ __forceinline__ void load_attn_step(const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
+                                               const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm,
+                                               int64_t nrows, int64_t blk, int nl, int g, AttnStep<KB, VB>& st) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t r = blk * 32 + tt * 16 + nl;
+    const int64_t rl = r < nrows ? r : nrows - 1;
+    const uint32_t* src = kidx + rl * (4 * KB) + KB * g;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) st.kw[tt][j] = src[j];
+    st.kn[tt] = knorm[rl];
+    st.vn[tt] = vnorm[rl];
+  }
+  const uint32_t* vs = vidx + blk * (128 * VB) + 32 * g * VB + 2 * nl * VB;
+#pragma unroll
+  for (int j = 0; j < 2 * VB; ++j) st.vw[j] = vs[j];
+}
+
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void k_attn_d128(
+    const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit,
+    const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
+    const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
+    CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
+  using DK = DecodeTable<KB>;
+  using DV = DecodeTable<VB>;
+  __shared__ __attribute__((aligned(16))) uint8_t ktab[2 * DK::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
+  __shared__ float kcent[16];
+  __shared__ _Float16 vcent[16];
+  __shared__ __attribute__((aligned(16))) float wl[4][4][32];
+  __shared__ float mm[4][4], ll[4][4];
+  __shared__ float accs[4][4][128];
+  if (threadIdx.x < 16) {
+    kcent[threadIdx.x] = cbk.c[threadIdx.x];
+    vcent[threadIdx.x] = (_Float16)cbv.c[threadIdx.x];
+  }
+  __syncthreads();
+  build_table2<KB>(ktab, kcent);
+  build_table<VB>(vtab, vcent);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int bh = blockIdx.y;
+  const int b = bh / Hkv, kvh = bh % Hkv;
+  const int ratio = Hq / Hkv;
+  const int64_t row0 = (int64_t)bh * T, rowE = row0 + T;
+  const int64_t blk_first = row0 >> 5, blk_end = ((rowE - 1) >> 5) + 1;
+  const int64_t bb = blk_first + (int64_t)blockIdx.x * kAttnStepsPerBlock;
+  const int64_t be = bb + kAttnStepsPerBlock < blk_end ? bb + kAttnStepsPerBlock : blk_end;
+  const int64_t cnt = be > bb ? be - bb : 0;
+  const int64_t per = (cnt + 3) / 4;
+  const int64_t wb = bb + wave * per;
+  const int64_t we = wb + per < be ? wb + per : be;
+
+  // query slots against the centroids' fp16 part (am): rows 0-3 rotated-query hi (heads),
+  // 4-7 lo; against the centroid remainders (am2): rows 8-11 hi.  Other rows zero.
+  u32x4 am[4], am2[4];
+  {
+    const int hl = nl & 3, prt = nl >> 2;
+    const bool live = hl < ratio && prt < 3;
+    const int src_part = prt == 1 ? 1 : 0;
+    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (hl < ratio ? hl : 0)) * 4 + src_part) * 128 + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      am[s] = (live && prt < 2) ? v : z;
+      am2[s] = (live && prt == 2) ? v : z;
+    }
+  }
+
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Loads of the next 32-token step are issued before the current step is consumed.
+  AttnStep<KB, VB> cur, nxt;
+  if (wb < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, wb, nl, g, cur);
+  for (int64_t blk = wb; blk < we; ++blk) {
+    if (blk + 1 < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, blk + 1, nl, g, nxt);
+    float lg[2], svv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t r = blk * 32 + tt * 16 + nl;
+      const bool valid = r >= row0 && r < rowE;
+      const float sk = cur.kn[tt];
+      svv[tt] = cur.vn[tt];
+      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 khi, klo;
+        decode8_2<KB>(cur.kw[tt], 8 * KB * s, ktab, khi, klo);
+        d = mfma_f16(am[s], khi, d);
+        d = mfma_f16(am2[s], klo, d);
+      }
+      const float sc = sk;
+      const float v0 = d[0] * sc, v1 = d[1] * sc, v2 = d[2] * sc, v3 = d[3] * sc;
+      const bool lowg = g < 2;
+      float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
+      const float s0 = lowg ? v2 : v0, s1 = lowg ? v3 : v1;
+      k0 += __shfl_xor(s0, 32);
+      k1 += __shfl_xor(s1, 32);
+      const bool odd = g & 1;
+      float mine = odd ? k1 : k0;
+      mine += __shfl_xor(odd ? k0 : k1, 16);
+      lg[tt] = (valid && g < ratio) ? mine * scale : -INFINITY;
+    }
+    // online softmax for head g
+    float mx = fmaxf(lg[0], lg[1]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
+    const float w0 = lg[0] == -INFINITY ? 0.f : __expf(lg[0] - m_new);
+    const float w1 = lg[1] == -INFINITY ? 0.f : __expf(lg[1] - m_new);
+    l_part = fmaf(l_part, alpha, w0 + w1);
+    m_run = m_new;
+    wl[wave][g][nl] = w0 * svv[0];
+    wl[wave][g][16 + nl] = w1 * svv[1];
+    if (__any(alpha < 1.f)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 16 * r);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c][r] *= ar;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // A operand: rows 0-3 weight hi per head, 4-7 weight lo, 8-15 zero; tokens 8 g .. 8 g + 7
+    u32x4 aw;
+    {
+      const int hm = nl & 3, prt = nl >> 2;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&wl[wave][hm][8 * g]);
+      const f32x4 c2 = *reinterpret_cast<const f32x4*>(&wl[wave][hm][8 * g + 4]);
+      const float v[8] = {a[0], a[1], a[2], a[3], c2[0], c2[1], c2[2], c2[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 h0 = (_Float16)v[2 * j], h1 = (_Float16)v[2 * j + 1];
+        const _Float16 l0 = (_Float16)(v[2 * j] - (float)h0), l1 = (_Float16)(v[2 * j + 1] - (float)h1);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        aw[j] = prt == 0 ? hi : (prt == 1 ? lo : 0u);
+      }
+    }
+    // B operand: the value chunks of octet g at coordinates 8 n .. 8 n + 7
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB>(cur.vw, 8 * VB * c, vtab), acc[c]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    cur = nxt;
+  }
+
+  // wave totals: sum over the 16 keys lanes; hi + lo accumulator rows
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) l_part += __shfl_xor(l_part, o);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[c][r] + __shfl_xor(acc[c][r], 16);
+      if (g == 0) accs[wave][r][8 * nl + c] = v;
+    }
+  if (nl == 0) {
+    mm[wave][g] = m_run;
+    ll[wave][g] = l_part;
+  }
+  __syncthreads();
+  float* out = part + ((int64_t)bh * nsplit + blockIdx.x) * 4 * kAttnPart;
+  for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) {
+    const int hh = i >> 7, c = i & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, mm[wv][hh]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        if (mm[wv][hh] == -INFINITY) continue;
+        const float e = __expf(mm[wv][hh] - M);
+        L = fmaf(ll[wv][hh], e, L);
+        A = fmaf(accs[wv][hh][c], e, A);
+      }
+    }
+    out[hh * kAttnPart + 2 + c] = A;
+    if (c == 0) {
+      out[hh * kAttnPart] = M;
+      out[hh * kAttnPart + 1] = L;
+    }
+  }
+}
+
+// Merges the splits of one query head and maps back from V's rotated domain: out = R_V^T acc / L.
+// 512 threads = 4 groups of 128 columns; the groups take every fourth split, then every fourth
+// quarter of the R_V^T product, so each thread's loads are independent and issued together.
+constexpr int kCombineThreads = 512;
+
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part, int Hq, int Hkv,
+                                                                  int nsplit, const float* __restrict__ r32v,
+                                                                  float* __restrict__ out) {
+  __shared__ float red[4][128];
+  __shared__ float lred[4];
+  __shared__ float wmax[kCombineThreads / 64];
+  __shared__ float o[128];
+  const int hg = blockIdx.x;
+  const int b = hg / Hq, h = hg % Hq;
+  const int ratio = Hq / Hkv;
+  const int bh = b * Hkv + h / ratio, hl = h % ratio;
+  const int t = threadIdx.x, c = t & 127, pp = t >> 7;
+  const int64_t xs = 4 * kAttnPart;  // floats between consecutive splits of one head
+  const float* p = part + (int64_t)bh * nsplit * xs + hl * kAttnPart;
+  float M = -INFINITY;
+  for (int x = t; x < nsplit; x += kCombineThreads) M = fmaxf(M, p[x * xs]);
+  for (int s = 32; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  if ((t & 63) == 0) wmax[t >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) M = fmaxf(M, wmax[w]);
+  float L = 0.f, A = 0.f;
+#pragma unroll 4
+  for (int x = pp; x < nsplit; x += 4) {
+    const float mx = p[x * xs];
+    const float l = p[x * xs + 1];
+    const float a = p[x * xs + 2 + c];
+    if (mx != -INFINITY) {
+      const float e = __expf(mx - M);
+      L = fmaf(l, e, L);
+      A = fmaf(a, e, A);
+    }
+  }
+  red[pp][c] = A;
+  if (c == 0) lred[pp] = L;
+  __syncthreads();
+  if (t < 128) {
+    const float a = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    const float l = (lred[0] + lred[1]) + (lred[2] + lred[3]);
+    o[t] = l > 0.f ? a / l : 0.f;
+  }
+  __syncthreads();
+  float y = 0.f;
+#pragma unroll
+  for (int j = 32 * pp; j < 32 * pp + 32; ++j) y = fmaf(r32v[j * 128 + c], o[j], y);
+  red[pp][c] = y;
+  __syncthreads();
+  if (t < 128) out[(int64_t)hg * 128 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+}
+
+template <int KB, int VB>
+hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                       const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
+                       const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale, float* out,
+                       void* ws, hipStream_t st) {
+  const int ratio = Hq / Hkv;
+  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
+  hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st);
+  if (e != hipSuccess) return e;
+  const int64_t steps = T / 32 + 2;
+  const int nsplit = (int)((steps + kAttnStepsPerBlock - 1) / kAttnStepsPerBlock);
+  hipLaunchKernelGGL((k_attn_d128<KB, VB>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit,
+                     K->idx, K->norms, V->idx, V->norms, K->n, cbk, cbv, scale, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(kCombineThreads), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
+  return hipGetLastError();
+}
+
+template <int BITS, bool BF16IN, int PASSES>
+hipError_t vblock_launch(const void* x, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                         uint32_t* idx, float* norms, hipStream_t st) {
+  const int64_t nblk = (n + 31) / 32;
+  int64_t blocks = (nblk + 3) / 4;
+  const int64_t cap = (int64_t)num_cus() * 2;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((k_encode_vblock_d128<BITS, BF16IN, PASSES>), dim3((unsigned)blocks), dim3(256), 0, st, x, n,
+                     reinterpret_cast<const u32x4*>(rot->fragt_dev), rot->post_scale, cb, idx, norms);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t vblock_dispatch(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                           const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st) {
+  if (bf16) return rot->passes == 1 ? vblock_launch<BITS, true, 1>(x, n, rot, cb, idx, norms, st)
+                                    : vblock_launch<BITS, true, 2>(x, n, rot, cb, idx, norms, st);
+  return rot->passes == 1 ? vblock_launch<BITS, false, 1>(x, n, rot, cb, idx, norms, st)
+                          : vblock_launch<BITS, false, 2>(x, n, rot, cb, idx, norms, st);
+}
+
+}  // namespace
+
+hipError_t launch_encode_vblock_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                     const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st) {
+  switch (cb.bits) {
+    case 1: return vblock_dispatch<1>(x, bf16, n, rot, cb, idx, norms, st);
+    case 2: return vblock_dispatch<2>(x, bf16, n, rot, cb, idx, norms, st);
+    case 3: return vblock_dispatch<3>(x, bf16, n, rot, cb, idx, norms, st);
+    case 4: return vblock_dispatch<4>(x, bf16, n, rot, cb, idx, norms, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d) {
+  (void)d;
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  const int64_t steps = T / 32 + 2;
+  const int64_t nsplit = (steps + kAttnStepsPerBlock - 1) / kAttnStepsPerBlock;
+  return qbytes + (size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float);
+}
+
+hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                              const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
+                              const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale,
+                              float* out, void* ws, hipStream_t st) {
+#define TQ_ATTN(KB, VB) \
+  if (cbk.bits == KB && cbv.bits == VB) return attn_launch<KB, VB>(q, B, Hq, Hkv, T, K, V, cbk, cbv, rot_k, rot_v, scale, out, ws, st);
+  TQ_ATTN(2, 2) TQ_ATTN(4, 4) TQ_ATTN(3, 3) TQ_ATTN(4, 2) TQ_ATTN(2, 4) TQ_ATTN(3, 2) TQ_ATTN(4, 3)
+  TQ_ATTN(1, 1) TQ_ATTN(2, 3) TQ_ATTN(3, 4)
+#undef TQ_ATTN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -72,7 +72,11 @@ struct tq_qjl_s {
 
 namespace tq {
 
-// Launchers (tq_kernels.hip).  All return the HIP error of the launch.
+// Compute units of the current device (cached per device).
+int num_cus();
+
+// Launchers (tq_encode128.hip, tq_misc.hip, tq_score128.hip, tq_attn128.hip).  All return the
+// HIP error of the launch.
 hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                               const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx,
                               float* norms, uint32_t* qjl_bits, float* rnorms, float* y_out,
@@ -92,5 +96,9 @@ hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, cons
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st);
 size_t scores_workspace_bytes(int B, int Hq, int d);
+// q_rot (and, with st_mat, the QJL sketch in sign-slot order plus the per-head constant) of
+// every query head, d = 128, into the score workspace layout.
+hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,
+                           uint16_t* qws, float* kconst, hipStream_t st);
 
 }  // namespace tq

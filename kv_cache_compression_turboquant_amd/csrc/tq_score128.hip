@@ -1,0 +1,356 @@
+// Query prologue (q_rot = R q, q_s = S q once per query head) and the compressed-key score
+// kernel at d = 128, MSE and TurboQuant_prod, with GQA sharing.
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// QJL sign bits as an fp16 MFMA operand without a table.  A lane's 32 sign bits z (coordinates
+// 32 g + j at bit j) become 16 dwords: dword d holds the bits of coordinates d and 16 + d, taken
+// in place at bit positions m and m + 16 of (d < 8 ? z << 8 : z), m = (d < 8 ? d + 8 : d), and
+// OR-ed into a base pattern so that each half is the fp16 value alpha_m + beta_m * bit.  The
+// query side carries q_s / beta_m in the same slot order, and the per-head constant
+// K = sum_i q_s,i (1 + 2 alpha_i / beta_i) turns the product D into <q_s, 2 z - 1> = 2 D - K.
+// ---------------------------------------------------------------------------------------
+__device__ __constant__ float kSignAlpha[8] = {1.f, 1.f, 0.5f, 0.25f, 0.0625f, 0.00390625f, 0.f, 1.f};
+__device__ __constant__ float kSignBeta[8] = {0.25f, 0.5f, 0.5f, 0.75f, 0.9375f, 0.99609375f, 2.f, -2.f};
+__device__ __constant__ uint32_t kSignBase[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
+                                                 0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
+
+// Slot order of the sign operand: element e of instruction s <-> local coordinate.
+__host__ __device__ __forceinline__ int sign_slot_coord(int s, int e) { return (4 * s + (e >> 1)) + 16 * (e & 1); }
+// Mask position index (m - 8) of dword d.
+__host__ __device__ __forceinline__ int sign_slot_mpos(int d) { return d < 8 ? d : d - 8; }
+
+__device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
+  const uint32_t zl = z << 8;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    const int m = d < 8 ? d + 8 : d;
+    const uint32_t src = d < 8 ? zl : z;
+    const uint32_t bases[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
+                               0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
+    bz[d >> 2][d & 3] = (src & ((1u << m) | (1u << (m + 16)))) | bases[m - 8];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Query prologue, d = 128: for each (batch, kv head) block, q_rot = R q and q_s = S q of the
+// heads sharing the kv head, written as fp16 hi/lo pairs: ws[(b*Hq + h)][part][128], part = 0
+// rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo.  Reads R^T / S^T so that thread j's loads of
+// column j are coalesced.  The 128 contraction steps are split over eight thread groups of 16
+// steps each, fully unrolled, so every load a thread needs is in flight at once (the kernel is
+// latency-bound, not bandwidth-bound); the partial sums meet in LDS.
+// ---------------------------------------------------------------------------------------
+constexpr int kQprepParts = 8;
+constexpr int kQprepThreads = 128 * kQprepParts;
+
+__global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
+                                                            const float* __restrict__ rt,
+                                                            const float* __restrict__ st,
+                                                            uint16_t* __restrict__ ws,
+                                                            float* __restrict__ kconst) {
+  __shared__ float qs[4][128];
+  __shared__ float part[2][kQprepParts][4][128];
+  __shared__ float sum[2][4][128];
+  const int Hkv = Hq / ratio;
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int h0 = kvh * ratio;
+  const int j = threadIdx.x & 127, p = threadIdx.x >> 7;
+  const int nmat = st ? 2 : 1;
+  for (int hc = 0; hc < ratio; hc += 4) {
+    const int nh = ratio - hc < 4 ? ratio - hc : 4;
+    __syncthreads();
+    if (threadIdx.x < 512) {
+      const int hh = threadIdx.x >> 7;
+      qs[hh][j] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
+    }
+    __syncthreads();
+    const int k0 = p * (128 / kQprepParts);
+    float rv[128 / kQprepParts], sv[128 / kQprepParts];
+#pragma unroll
+    for (int k = 0; k < 128 / kQprepParts; ++k) rv[k] = rt[(k0 + k) * 128 + j];
+    if (st) {
+#pragma unroll
+      for (int k = 0; k < 128 / kQprepParts; ++k) sv[k] = st[(k0 + k) * 128 + j];
+    }
+    float ar[4] = {0.f, 0.f, 0.f, 0.f}, as[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 128 / kQprepParts; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
+    if (st) {
+#pragma unroll
+      for (int k = 0; k < 128 / kQprepParts; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) as[i] = fmaf(sv[k], qs[i][k0 + k], as[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[0][p][i][j] = ar[i];
+      part[1][p][i][j] = as[i];
+    }
+    __syncthreads();
+    // threads (m, j), m < nmat: the full sum of matrix m for the four heads
+    if (threadIdx.x < 128 * nmat) {
+      const int m = threadIdx.x >> 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < kQprepParts; ++pp) a += part[m][pp][i][j];
+        sum[m][i][j] = a;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 128 * nmat) {
+      const int m = threadIdx.x >> 7;
+      for (int i = 0; i < nh; ++i) {
+        uint16_t* o = ws + ((int64_t)b * Hq + h0 + hc + i) * 4 * 128;
+        float v;
+        int mp = 0;
+        if (m == 0) {
+          v = sum[0][i][j];
+        } else {
+          // sketch in sign-slot order: output slot j = 32 G + 8 s + e  <-  coordinate
+          // 32 G + c(s, e), scaled by 1 / beta
+          const int G = j >> 5, s8 = (j & 31) >> 3, e = j & 7;
+          const int c = 32 * G + sign_slot_coord(s8, e);
+          mp = sign_slot_mpos(4 * s8 + (e >> 1));
+          v = sum[1][i][c] / kSignBeta[mp];
+        }
+        const _Float16 vh = (_Float16)v;
+        const _Float16 vl = (_Float16)(v - (float)vh);
+        o[256 * m + j] = __builtin_bit_cast(uint16_t, vh);
+        o[256 * m + 128 + j] = __builtin_bit_cast(uint16_t, vl);
+      }
+    }
+    if (st && threadIdx.x < 64 * nh) {
+      // per-head constant K = sum_i q_s,i (1 + 2 alpha_i / beta_i); wave i reduces head i
+      const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
+      float acc = 0.f;
+      for (int c = l; c < 128; c += 64) {
+        const int jl = c & 31;                     // local coordinate within its group
+        const int d = jl < 16 ? jl : jl - 16;      // dword holding it
+        const int mp = sign_slot_mpos(d);
+        acc += sum[1][i][c] * (1.f + 2.f * kSignAlpha[mp] / kSignBeta[mp]);
+      }
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+      if (l == 0) kconst[(int64_t)b * Hq + h0 + hc + i] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Compressed-key score, d = 128.  Grid (key chunk, b * Hkv).  D = A B with A = query slots
+// (16 rows: rot hi / rot lo / sketch hi / sketch lo for 4 heads), B = decoded keys (columns =
+// 16 keys), so lane (n, G) receives the four partial sums of key n for slot group G.  Keys are
+// decoded from whole packed words through small LDS tables that map a field of F bits to
+// F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass.
+// ---------------------------------------------------------------------------------------
+constexpr int kScoreWaves = 4;
+constexpr int kScoreBatch = 8;
+
+template <int BITS, bool PROD>
+struct KeyTile {
+  uint32_t w[BITS];
+  float nrm;
+  uint32_t zw;
+  float gam;
+};
+
+// Lane (n, g) share of key tile `tile` of one sequence: its BITS words (coordinates 32 g ..),
+// norm, and for prod its sign word and scaled residual norm.  Rows past T are clamped.
+template <int BITS, bool PROD>
+__device__ __forceinline__ void load_key_tile(const uint32_t* __restrict__ idx, const float* __restrict__ norms,
+                                              const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms,
+                                              int64_t base_row, int64_t T, int64_t tile, int nl, int g,
+                                              KeyTile<BITS, PROD>& k) {
+  int64_t t = tile * 16 + nl;
+  t = t < T ? t : T - 1;
+  const int64_t row = base_row + t;
+  const uint32_t* src = idx + row * (4 * BITS) + BITS * g;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) k.w[j] = src[j];
+  k.nrm = norms[row];
+  if constexpr (PROD) {
+    k.zw = qbits[row * 4 + g];
+    k.gam = rnorms[row] * (kQjl / 128.0f);
+  } else {
+    k.zw = 0;
+    k.gam = 0.f;
+  }
+}
+
+template <int BITS, bool PROD>
+__global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
+    const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int tiles_per_wave,
+    const uint32_t* __restrict__ idx, const float* __restrict__ norms,
+    const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
+    float* __restrict__ scores) {
+  using DT = DecodeTable<BITS>;
+  __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
+  __shared__ _Float16 cent[16];
+  if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
+  __syncthreads();
+  build_table<BITS>(tab, cent);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int ratio = Hq / Hkv;
+  const int groups = (ratio + 3) / 4;
+  const int64_t base_row = (int64_t)bg * T;
+  const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
+  const int64_t ntiles_seq = (T + 15) / 16;
+
+  // A operands for head group 0 (kept in registers).
+  auto load_a = [&](int hg, u32x4 (&am)[4], u32x4 (&aq)[4]) {
+    const int slot = nl;             // A row
+    const int hl = slot & 3;         // head within the group
+    const int part = slot >> 2;      // 0 rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo
+    const int h = 4 * hg + hl;
+    const bool live = h < ratio;
+    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (live ? h : 0)) * 4 + part) * 128 + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
+      if (!live) v = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      am[s] = part < 2 ? v : z;
+      aq[s] = (PROD && part >= 2) ? v : z;
+    }
+  };
+  u32x4 am0[4], aq0[4];
+  load_a(0, am0, aq0);
+  // sketch constant K of the lane's head (4 hg + g) after the reduction
+  auto load_kc = [&](int hg) -> float {
+    const int h = 4 * hg + g;
+    return (PROD && h < ratio) ? kconst[(int64_t)b * Hq + kvh * ratio + h] : 0.f;
+  };
+  const float kc0 = load_kc(0);
+
+  // Ping-pong over two tile buffers (no register copies), so the next tile's loads stay in flight
+  // while the current one is scored and the wait before scoring counts only the older loads.
+  auto score_tile = [&](const KeyTile<BITS, PROD>& cur, int64_t ti) {
+    const int64_t tile = tile0 + ti;
+    const int64_t t = tile * 16 + nl;
+    const bool valid = t < T;
+    const float nrm = cur.nrm;
+    const float gam = cur.gam;
+    u32x4 bk[4], bz[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS>(cur.w, s, tab);
+    if constexpr (PROD) sign_operand(cur.zw, bz);
+    for (int hg = 0; hg < groups; ++hg) {
+      u32x4 am[4], aq[4];
+      if (hg == 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { am[s] = am0[s]; aq[s] = aq0[s]; }
+      } else {
+        load_a(hg, am, aq);
+      }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc = mfma_f16(am[s], bk[s], acc);
+        if constexpr (PROD) acc = mfma_f16(aq[s], bz[s], acc);
+      }
+      const float sc = g < 2 ? nrm : 2.f * gam;
+      const float v0 = acc[0] * sc, v1 = acc[1] * sc, v2 = acc[2] * sc, v3 = acc[3] * sc;
+      const bool lowg = g < 2;
+      float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
+      const float s0 = lowg ? v2 : v0, s1 = lowg ? v3 : v1;
+      k0 += __shfl_xor(s0, 32);
+      k1 += __shfl_xor(s1, 32);
+      const bool odd = g & 1;
+      float mine = odd ? k1 : k0;
+      const float other = odd ? k0 : k1;
+      mine += __shfl_xor(other, 16);
+      const int h = 4 * hg + g;
+      if constexpr (PROD) mine -= gam * (hg == 0 ? kc0 : load_kc(hg));
+      if (valid && h < ratio) scores[((int64_t)b * Hq + kvh * ratio + h) * T + t] = mine;
+    }
+  };
+  // Batches of kScoreBatch tiles: every load of a batch is issued before any tile of it is
+  // scored (straight-line code, so the waits are exact), and the batch's latency is paid once.
+  int64_t last = tiles_per_wave;
+  if (ntiles_seq - tile0 < last) last = ntiles_seq - tile0;
+  for (int64_t tb = 0; tb < last; tb += kScoreBatch) {
+    KeyTile<BITS, PROD> kt[kScoreBatch];
+#pragma unroll
+    for (int u = 0; u < kScoreBatch; ++u)
+      load_key_tile<BITS, PROD>(idx, norms, qbits, rnorms, base_row, T, tile0 + tb + u, nl, g, kt[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kScoreBatch; ++u)
+      if (tb + u < last) score_tile(kt[u], tb + u);
+  }
+}
+
+template <int BITS, bool PROD>
+hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                         float* scores, void* ws, hipStream_t st) {
+  const int ratio = Hq / Hkv;
+  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, ratio, rot->rt32_dev,
+                     PROD ? qjl->st32_dev : nullptr, qws, kconst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (T + 15) / 16;
+  // enough blocks to fill the device about four times over
+  const int64_t target = (int64_t)num_cus() * 4;
+  const int64_t seqs = (int64_t)B * Hkv;
+  int64_t tpw = (tiles * seqs + target * kScoreWaves - 1) / (target * kScoreWaves);
+  tpw = (tpw + kScoreBatch - 1) / kScoreBatch * kScoreBatch;
+  if (tpw < kScoreBatch) tpw = kScoreBatch;
+  if (tpw > 64) tpw = 64;
+  const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
+  hipLaunchKernelGGL((k_scores_d128<BITS, PROD>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
+                     0, st, qws, kconst, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
+                     PROD ? K->rnorms : nullptr, cb, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,
+                           uint16_t* qws, float* kconst, hipStream_t st) {
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, Hq / Hkv, rt, st_mat, qws,
+                     kconst);
+  return hipGetLastError();
+}
+
+size_t scores_workspace_bytes(int B, int Hq, int d) {
+  (void)d;
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  return qbytes + (size_t)B * Hq * sizeof(float);
+}
+
+hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                         float* scores, void* ws, hipStream_t st) {
+  const bool prod = K->mode == TQ_MODE_PROD;
+  switch (cb.bits) {
+    case 1: return prod ? scores_launch<1, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<1, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 2: return prod ? scores_launch<2, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<2, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 3: return prod ? scores_launch<3, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<3, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+    case 4: return prod ? scores_launch<4, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
+                        : scores_launch<4, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq
