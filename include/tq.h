@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -128,7 +128,8 @@ tq_status tq_codebook_values(tq_codebook_t cb, double* centroids_host, double* t
 void tq_codebook_free(tq_codebook_t cb);
 
 /* Rotation handle: R generated once from `seed` and kept ([FP]: generated at init, shared by
- * all vectors).  d must be 128 for the fused encode kernels. */
+ * all vectors).  The device copies include MFMA fragments for the fused kernels (d = 128) or
+ * the general-d kernels (d a multiple of 128 in [256, 4096]); WHT needs d a power of two. */
 tq_status tq_make_rotation(int d, uint64_t seed, tq_rot_kind kind, tq_rotation_t* out);
 /* Rotation handle from a caller matrix (row-major d x d host fp64; treated as DENSE). */
 tq_status tq_rotation_from_matrix(int d, const double* r_host, tq_rotation_t* out);
@@ -156,15 +157,24 @@ size_t tq_packed_idx_words(int64_t n, int d, int bits, tq_layout layout);
  * b is the total bit budget per coordinate; cb must have b bits (MSE) or b - 1 bits (prod);
  * qjl must be non-NULL exactly for prod and bound to `rot`.  out->d, out->bits, out->mode,
  * out->n must describe the call; out->idx/norms (and qjl/rnorms for prod) are written.
- * A zero vector encodes to norm 0 and the indices of y = 0.  Supported: d = 128 (fused).
- * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED as above. */
+ * A zero vector encodes to norm 0 and the indices of y = 0.
+ * Supported d: 128 (one fused kernel; rows or token-blocked layout), or a multiple of 128 in
+ * [256, 4096] (rows layout; rotation as a tiled MFMA GEMM whose epilogue quantizes and packs;
+ * prod adds a second GEMM with S' on the residual, staged through ws_dev in chunks of vectors).
+ * ws_dev / ws_bytes: caller device workspace, at least tq_encode_workspace(n, d, b, mode) bytes
+ * is the size that needs a single chunk; any size that holds 128 vectors' residuals works
+ * (more launches).  It may be NULL when tq_encode_workspace returns 0.
+ * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED as above; TQ_ENOMEM if ws_bytes is too small. */
 tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_mode mode,
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* out,
-                    void* stream);
+                    void* ws_dev, size_t ws_bytes, void* stream);
+/* Workspace bytes for tq_encode of n vectors: 0 for MSE and for d = 128; for prod at other d,
+ * min(n, 131072) vectors x (d + d/128) fp32 values (residual rows and per-block partial norms). */
+size_t tq_encode_workspace(int64_t n, int d, int b, tq_mode mode);
 
 /* Rotated unit coordinates y = R x / ||x|| (fp32 [n, d]) and norms (fp32 [n]) exactly as the
  * encode kernel forms them before quantizing (same kernel, stores instead of packing).
- * For parity checks of the rotation.  d = 128. */
+ * For parity checks of the rotation.  d = 128, or a multiple of 128 in [256, 4096]. */
 tq_status tq_rotate(const void* x_dev, tq_dtype dt, int64_t n, int d, tq_rotation_t rot,
                     float* y_dev, float* norms_dev, void* stream);
 
@@ -204,6 +214,23 @@ tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, 
                          const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
                          tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
                          void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
+ * with k results per query (query operands, one chunk of scores, the running top-k). */
+size_t tq_search_workspace(int64_t nq, int64_t n, int d, int k);
+/* Maximum inner-product search over a TurboQuant_prod database ([FP] inner-product bias and the
+ * QJL fix; [TQ] TurboQuant_prod estimator; [FP] deployment: vector retrieval with the encoder
+ * as one matmul and a lookup).  For each query q_dev[i] (fp32 [nq, d]) the score of database
+ * vector j is s_j <R q, C[idx_j]> + gamma_j sqrt(pi/2)/d <S q, z_j>, and the k largest scores
+ * are written in descending order to top_s_dev [nq, k] fp32 with their indices to
+ * top_i_dev [nq, k] int64; equal scores order by the smaller index.  If n < k the tail holds
+ * -inf and index -1.  db: ROWS layout, prod mode, d a multiple of 128 in [128, 4096];
+ * 1 <= k <= 32.  ws_dev: at least tq_search_workspace(nq, n, d, k) bytes.
+ * Errors: TQ_EINVAL (null pointers, k out of range), TQ_ESHAPE (d mismatch), TQ_EUNSUPPORTED
+ * (layout, mode or d), TQ_ENOMEM (workspace). */
+tq_status tq_search_topk(const float* q_dev, int64_t nq, const tq_packed* db, tq_codebook_t cb,
+                         tq_rotation_t rot, tq_qjl_t qjl, int k, float* top_s_dev,
+                         int64_t* top_i_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ __all__ = [
     "Codebook", "Rotation", "QJL", "Packed", "codebook", "codebook_from_values", "make_rotation",
     "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
-    "decode_attn", "decode_attn_workspace",
+    "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -181,15 +181,25 @@ def _dtype_code(x):
     raise TQError(3, f"unsupported dtype {x.dtype}")
 
 
-def encode(x, b, mode, cb, rot, qjl=None, out=None, layout="rows"):
-    """Encode rows of x [n, d] (bf16 or fp32, contiguous, on the GPU) with b total bits."""
+def encode_workspace(n, d, b, mode):
+    return int(lib().tq_encode_workspace(n, d, b, MODE[mode]))
+
+
+def encode(x, b, mode, cb, rot, qjl=None, out=None, layout="rows", ws=None):
+    """Encode rows of x [n, d] (bf16 or fp32, contiguous, on the GPU) with b total bits.
+    ws: optional uint8 device workspace (prod at d != 128 needs one; allocated if absent)."""
+    torch = _torch()
     n, d = x.shape
     stage = b - 1 if mode == "prod" else b
     if out is None:
         out = alloc_packed(n, d, stage, mode, device=x.device, layout=layout)
+    need = encode_workspace(n, d, b, mode)
+    if ws is None and need > 0:
+        ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
     desc = out.descriptor()
     check(lib().tq_encode(_dptr(x), _dtype_code(x), n, d, b, MODE[mode], cb.ptr, rot.ptr,
-                          qjl.ptr if qjl is not None else None, ctypes.byref(desc), _stream()))
+                          qjl.ptr if qjl is not None else None, ctypes.byref(desc), _dptr(ws),
+                          ws.numel() * ws.element_size() if ws is not None else 0, _stream()))
     return out
 
 
@@ -262,4 +272,25 @@ def decode_attn(q, K, V, Hkv, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws
     check(lib().tq_decode_attn(_dptr(q), B, Hq, Hkv, T, ctypes.byref(kd), ctypes.byref(vd), cb_k.ptr, cb_v.ptr,
                                rot_k.ptr, rot_v.ptr, ctypes.c_float(scale), _dptr(out), _dptr(ws),
                                ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def search_workspace(nq, n, d, k):
+    return int(lib().tq_search_workspace(nq, n, d, k))
+
+
+def search_topk(q, db, k, cb, rot, qjl, ws=None, out=None):
+    """Top-k maximum inner-product search of q [nq, d] fp32 against a prod database (rows
+    layout): (scores [nq, k] fp32 descending, indices [nq, k] int64)."""
+    torch = _torch()
+    nq, d = q.shape
+    if out is None:
+        out = (torch.empty((nq, k), dtype=torch.float32, device=q.device),
+               torch.empty((nq, k), dtype=torch.int64, device=q.device))
+    need = search_workspace(nq, db.n, d, k)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    desc = db.descriptor()
+    check(lib().tq_search_topk(_dptr(q), nq, ctypes.byref(desc), cb.ptr, rot.ptr, qjl.ptr, k, _dptr(out[0]),
+                               _dptr(out[1]), _dptr(ws), ws.numel() * ws.element_size(), _stream()))
     return out

@@ -64,7 +64,10 @@ SIGNATURES = {
     "tq_decode_attn_workspace": (_SZ, [_I, _I, _I, _I64, _I]),
     "tq_decode_attn": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed), _P, _P,
                             _P, _P, ctypes.c_float, _P, _P, _SZ, _P]),
-    "tq_encode": (_I, [_P, _I, _I64, _I, _I, _I, _P, _P, _P, ctypes.POINTER(tq_packed), _P]),
+    "tq_encode": (_I, [_P, _I, _I64, _I, _I, _I, _P, _P, _P, ctypes.POINTER(tq_packed), _P, _SZ, _P]),
+    "tq_encode_workspace": (_SZ, [_I64, _I, _I, _I]),
+    "tq_search_workspace": (_SZ, [_I64, _I64, _I, _I]),
+    "tq_search_topk": (_I, [_P, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "tq_rotate": (_I, [_P, _I, _I64, _I, _P, _P, _P, _P]),
     "tq_quantize_rotated": (_I, [_P, _I64, _I, _P, _P, _P]),
     "tq_decode": (_I, [ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),

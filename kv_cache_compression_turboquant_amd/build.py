@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip"]
+SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip",
+           "tq_general.hip"]
 
 # Packed FP32 VALU instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,0 +1,703 @@
+// General-d TurboQuant encode (d a multiple of 128, 256 <= d <= 4096) and the top-k maximum
+// inner-product search over a TurboQuant_prod database.
+//
+// Encode ([TQ] official steps 1-4 and TurboQuant_prod): the rotation is a tiled GEMM,
+// y^T = R x^T, on bf16 MFMA.  A block owns 128 vectors x one 128-coordinate output block ob
+// and loops over the 128-wide contraction chunks kc; the chunk's pre-swizzled R fragments are
+// staged through LDS and shared by the four waves, while each wave streams its 32 vectors
+// straight from HBM as the B operand.  With the fragment row order of the d = 128 kernel, lane
+// (n, G) ends with coordinates 128 ob + 32 G .. + 31 of its vector, so the epilogue bucketizes
+// and packs whole words in registers.  The norm is accumulated from the B operand, so no
+// separate pass reads x.  Prod runs twice: the first GEMM also writes the rotated-domain
+// residual (fp32, unit scale) and per-block partial squared norms to a workspace, and the second
+// multiplies the residual by S' = S R^T, keeps the signs and forms gamma.
+//
+// Search ([FP] inner-product bias and QJL fix): the queries are rotated and sketched by the same
+// GEMM kernel, converted once into fp16 MFMA fragments, and the scores are a second GEMM whose B
+// operand is decoded from the packed database on the fly (centroids through an LDS table; QJL
+// signs as +-(gamma / s) sqrt(pi/2) / d, so one accumulator holds both terms).  Scores of one
+// chunk of the database go to the workspace, and a per-query kernel merges them into the
+// running top-k.
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+constexpr int kGWaves = 4;
+constexpr int kGTiles = 2;  // 16-vector tiles per wave
+static_assert(kGWaves * kGTiles * 16 == kGenVectors, "a block covers kGenVectors vectors");
+
+enum GenEpi { kEpiY = 0, kEpiMse = 1, kEpiRes = 2, kEpiSign = 3, kEpiRaw = 4 };
+
+// One lane's share of a 16-vector tile for one contraction chunk: 32 consecutive coordinates.
+template <bool BF16IN>
+__device__ __forceinline__ void load_gen(const void* __restrict__ x, int64_t n, int d, int64_t row0, int kc,
+                                         int nl, int g, RawTile<BF16IN>& t) {
+  int64_t r = row0 + nl;
+  if (r >= n) r = n - 1;
+  if constexpr (BF16IN) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + r * d + 128 * kc + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t.v[s] = src[s];
+  } else {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + r * d + 128 * kc + 32 * g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t.v[j] = src[j];
+  }
+}
+
+// bf16 B operand (hi, and lo for fp32 input) of the four instructions; optional sum of squares.
+template <bool BF16IN, bool NORM>
+__device__ __forceinline__ void to_operand(const RawTile<BF16IN>& t, u32x4 (&hi)[4], u32x4 (&lo)[4], float& ss) {
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      hi[s] = t.v[s];
+      if constexpr (NORM) {
+        // plain-array copy before the bit cast (see the d = 128 encode)
+        uint32_t wv[4];
+        __builtin_memcpy(wv, &t.v[s], sizeof(wv));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 p = __builtin_bit_cast(bf16x2, wv[j]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f32x4 a = t.v[2 * s], b = t.v[2 * s + 1];
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      u32x4 h4, l4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x2 pr = {v[2 * j], v[2 * j + 1]};
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        const f32x2 rem = {v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
+        h4[j] = h;
+        l4[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+        if constexpr (NORM) {
+          ss = fmaf(v[2 * j], v[2 * j], ss);
+          ss = fmaf(v[2 * j + 1], v[2 * j + 1], ss);
+        }
+      }
+      hi[s] = h4;
+      lo[s] = l4;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// The general-d GEMM.  Grid: (vector tile of 128) x (output block ob), ob fastest.
+//   kEpiY    : y_out = unit rotated coordinates, norms (block ob == 0)
+//   kEpiRaw  : y_out = post_scale * product (no normalisation)
+//   kEpiMse  : packed indices, norms
+//   kEpiRes  : as kEpiMse plus res_out = y_unit - C[idx] and rpart[row][ob] = sum of squares
+//   kEpiSign : x = residual rows; qjl_out = sign bits; block ob == 0 forms
+//              rnorm_out = norms * sqrt(sum_ob rpart)
+// ---------------------------------------------------------------------------------------
+template <int EPI, bool BF16IN, int APASS, int BITS>
+__global__ __launch_bounds__(kGWaves * 64, 2) void k_encode_gen(
+    const void* __restrict__ x, int64_t n, int d, const u32x4* __restrict__ frag, float post_scale,
+    CodebookArgs cb, float* __restrict__ norms, uint32_t* __restrict__ idx_out, float* __restrict__ y_out,
+    float* __restrict__ res_out, float* __restrict__ rpart, uint32_t* __restrict__ qjl_out,
+    float* __restrict__ rnorm_out) {
+  constexpr bool NORM = EPI != kEpiSign && EPI != kEpiRaw;
+  constexpr bool SPLIT = !BF16IN;
+  constexpr int H = 1 << (BITS - 1);
+  constexpr int PER = APASS * kFragU4 / (kGWaves * 64);
+  __shared__ u32x4 lds[APASS * kFragU4];
+  const int nb = d >> 7;
+  const int64_t vt = (int64_t)blockIdx.x / nb;
+  const int ob = (int)((int64_t)blockIdx.x % nb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t row0 = vt * kGenVectors + wave * (kGTiles * 16);
+
+  f32x4 acc[kGTiles][8];
+#pragma unroll
+  for (int j = 0; j < kGTiles; ++j)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[kGTiles];
+#pragma unroll
+  for (int j = 0; j < kGTiles; ++j) ss[j] = 0.f;
+
+  for (int kc = 0; kc < nb; ++kc) {
+    const u32x4* src = frag + (size_t)(ob * nb + kc) * 2 * kFragU4;
+    u32x4 stage[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) stage[i] = src[i * (kGWaves * 64) + threadIdx.x];
+    RawTile<BF16IN> raw[kGTiles];
+#pragma unroll
+    for (int j = 0; j < kGTiles; ++j) load_gen<BF16IN>(x, n, d, row0 + 16 * j, kc, nl, g, raw[j]);
+    __syncthreads();  // the previous chunk's fragments are no longer read
+#pragma unroll
+    for (int i = 0; i < PER; ++i) lds[i * (kGWaves * 64) + threadIdx.x] = stage[i];
+    u32x4 bx[kGTiles][4], bxl[kGTiles][4];
+#pragma unroll
+    for (int j = 0; j < kGTiles; ++j) to_operand<BF16IN, NORM>(raw[j], bx[j], bxl[j], ss[j]);
+    __syncthreads();
+    u32x4 cf[APASS][4], nf[APASS][4];
+    load_frags<APASS>(lds, 0, lane, cf);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t + 1 < 8) load_frags<APASS>(lds, t + 1, lane, nf);
+#pragma unroll
+      for (int j = 0; j < kGTiles; ++j) {
+        f32x4 a = acc[j][t];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          a = mfma_bf16(cf[0][s], bx[j][s], a);
+          if constexpr (SPLIT) a = mfma_bf16(cf[0][s], bxl[j][s], a);
+          if constexpr (APASS == 2) a = mfma_bf16(cf[1][s], bx[j][s], a);
+        }
+        acc[j][t] = a;
+      }
+      if (t + 1 < 8) {
+#pragma unroll
+        for (int p = 0; p < APASS; ++p)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) cf[p][s] = nf[p][s];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  const float inv_post = 1.0f / post_scale;
+#pragma unroll
+  for (int j = 0; j < kGTiles; ++j) {
+    const int64_t row = row0 + 16 * j + nl;
+    const bool valid = row < n;
+    if constexpr (EPI == kEpiSign) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bits |= (acc[j][t][r] >= 0.f ? 1u : 0u) << (4 * t + r);
+      if (valid) {
+        qjl_out[row * (d >> 5) + 4 * ob + g] = bits;
+        if (ob == 0 && g == 0) {
+          float sum = 0.f;
+          for (int o = 0; o < nb; ++o) sum += rpart[row * nb + o];
+          rnorm_out[row] = norms[row] * sqrtf(sum);
+        }
+      }
+    } else if constexpr (EPI == kEpiRaw) {
+      if (valid) {
+        f32x4* dst = reinterpret_cast<f32x4*>(y_out + row * d + 128 * ob + 32 * g);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dst[t] = acc[j][t] * post_scale;
+      }
+    } else {
+      float sq = ss[j];
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const float nrm = sqrtf(sq);
+      const bool live = nrm > 0.f;
+      const float scale = live ? post_scale / nrm : 0.f;  // raw product -> unit coordinate
+      if (valid && ob == 0 && g == 0) norms[row] = nrm;
+      if constexpr (EPI == kEpiY) {
+        if (valid) {
+          f32x4* dst = reinterpret_cast<f32x4*>(y_out + row * d + 128 * ob + 32 * g);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) dst[t] = acc[j][t] * scale;
+        }
+      } else {
+        // sign-magnitude decisions against per-vector thresholds t_p * ||x|| / post_scale, as in
+        // the d = 128 encode: idx = (m ^ sign) + K/2, m = #{p : |y| >= t_p}
+        float thr[H > 1 ? H - 1 : 1];
+        float mags[H];
+        const float tsc = nrm * inv_post;
+#pragma unroll
+        for (int p = 0; p < H - 1; ++p) thr[p] = live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY;
+#pragma unroll
+        for (int p = 0; p < H; ++p) mags[p] = live ? cb.cpos[p] : 0.f;
+        uint32_t w[BITS];
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) w[b] = 0;
+        float rs = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          f32x4 resv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float yv = acc[j][t][r];
+            const float ay = fabsf(yv);
+            uint32_t m = 0;
+            float mag = mags[0];
+#pragma unroll
+            for (int p = 0; p < H - 1; ++p) {
+              const bool ge = ay >= thr[p];
+              m += ge ? 1u : 0u;
+              if constexpr (EPI == kEpiRes) mag = ge ? mags[p + 1] : mag;
+            }
+            const uint32_t sgn = (uint32_t)(__float_as_int(yv) >> 31);
+            const uint32_t id = (m ^ sgn) + (uint32_t)H;
+            if constexpr (EPI == kEpiRes) {
+              const float cv =
+                  __uint_as_float((__float_as_uint(mag) & 0x7fffffffu) | (__float_as_uint(yv) & 0x80000000u));
+              const float res = fmaf(yv, scale, -cv);
+              resv[r] = res;
+              rs = fmaf(res, res, rs);
+            }
+            const int p = BITS * (4 * t + r), wi = p >> 5, sh = p & 31;
+            w[wi] |= id << sh;
+            if (sh + BITS > 32) w[wi + 1] |= id >> (32 - sh);
+          }
+          if constexpr (EPI == kEpiRes) {
+            if (valid) reinterpret_cast<f32x4*>(res_out + row * d + 128 * ob + 32 * g)[t] = resv;
+          }
+        }
+        if (valid) {
+          uint32_t* dst = idx_out + row * ((int64_t)d * BITS / 32) + 4 * BITS * ob + BITS * g;
+#pragma unroll
+          for (int b = 0; b < BITS; ++b) dst[b] = w[b];
+        }
+        if constexpr (EPI == kEpiRes) {
+          rs += __shfl_xor(rs, 16);
+          rs += __shfl_xor(rs, 32);
+          if (valid && g == 0) rpart[row * nb + ob] = rs;
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, bool BF16IN, int APASS, int BITS>
+hipError_t gen_launch(const void* x, int64_t n, int d, const uint16_t* frag, float post, const CodebookArgs& cb,
+                      float* norms, uint32_t* idx, float* y, float* res, float* rpart, uint32_t* qbits, float* rn,
+                      hipStream_t st) {
+  const int64_t nvt = (n + kGenVectors - 1) / kGenVectors;
+  const int64_t blocks = nvt * (d / 128);
+  hipLaunchKernelGGL((k_encode_gen<EPI, BF16IN, APASS, BITS>), dim3((unsigned)blocks), dim3(kGWaves * 64), 0, st,
+                     x, n, d, reinterpret_cast<const u32x4*>(frag), post, cb, norms, idx, y, res, rpart, qbits, rn);
+  return hipGetLastError();
+}
+
+template <int EPI, int BITS>
+hipError_t gen_dispatch(const void* x, bool bf16, int64_t n, int d, const uint16_t* frag, int passes, float post,
+                        const CodebookArgs& cb, float* norms, uint32_t* idx, float* y, float* res, float* rpart,
+                        hipStream_t st) {
+  if (bf16)
+    return passes == 1
+               ? gen_launch<EPI, true, 1, BITS>(x, n, d, frag, post, cb, norms, idx, y, res, rpart, nullptr, nullptr, st)
+               : gen_launch<EPI, true, 2, BITS>(x, n, d, frag, post, cb, norms, idx, y, res, rpart, nullptr, nullptr, st);
+  return passes == 1
+             ? gen_launch<EPI, false, 1, BITS>(x, n, d, frag, post, cb, norms, idx, y, res, rpart, nullptr, nullptr, st)
+             : gen_launch<EPI, false, 2, BITS>(x, n, d, frag, post, cb, norms, idx, y, res, rpart, nullptr, nullptr, st);
+}
+
+template <int EPI>
+hipError_t gen_dispatch_bits(const void* x, bool bf16, int64_t n, int d, const tq_rotation_s* rot,
+                             const CodebookArgs& cb, float* norms, uint32_t* idx, float* res, float* rpart,
+                             hipStream_t st) {
+  switch (cb.bits) {
+    case 1: return gen_dispatch<EPI, 1>(x, bf16, n, d, rot->gfrag_dev, rot->passes, rot->post_scale, cb, norms, idx, nullptr, res, rpart, st);
+    case 2: return gen_dispatch<EPI, 2>(x, bf16, n, d, rot->gfrag_dev, rot->passes, rot->post_scale, cb, norms, idx, nullptr, res, rpart, st);
+    case 3: return gen_dispatch<EPI, 3>(x, bf16, n, d, rot->gfrag_dev, rot->passes, rot->post_scale, cb, norms, idx, nullptr, res, rpart, st);
+    case 4: return gen_dispatch<EPI, 4>(x, bf16, n, d, rot->gfrag_dev, rot->passes, rot->post_scale, cb, norms, idx, nullptr, res, rpart, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------------------
+// Search.
+// ---------------------------------------------------------------------------------------
+constexpr int kSearchKeys = 256;           // database vectors per score block (64 per wave)
+constexpr int64_t kSearchChunk = 65536;    // database vectors per score chunk
+constexpr float kSketchScale = 1.0f / 1024.0f;  // query sketch scale; the key side carries 1024
+
+// Query operands in fp16 MFMA fragment order: block (qb, kc) = 4096 u32x4 laid out
+// [op][qt][s][lane]; element e of lane (m, g) = Q_op[128 qb + 16 qt + m][128 kc + 32 g + 8 s + e],
+// op 0 = unit rotated query, op 1 = its sketch times kSketchScale; rows past nq are zero.
+__global__ __launch_bounds__(256) void k_search_qfrag(const float* __restrict__ qr, const float* __restrict__ qs,
+                                                       int64_t nq, int d, u32x4* __restrict__ qf) {
+  const int nb = d >> 7;
+  const int64_t qb = (int64_t)blockIdx.x / nb;
+  const int kc = (int)((int64_t)blockIdx.x % nb);
+  u32x4* dst = qf + ((size_t)qb * nb + kc) * 4096;
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) {
+    const int lane = i & 63, s = (i >> 6) & 3, qt = (i >> 8) & 7, op = i >> 11;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t row = qb * 128 + 16 * qt + m;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row < nq) {
+      const float* src = (op ? qs : qr) + row * d + 128 * kc + 32 * g + 8 * s;
+      const float sc = op ? kSketchScale : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(src[2 * j] * sc));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(src[2 * j + 1] * sc));
+        v[j] = lo | (hi << 16);
+      }
+    }
+    dst[i] = v;
+  }
+}
+
+// Sign operand of 8 coordinates (bits 8 s .. 8 s + 7 of z): fp16 +-mag pairs.
+__device__ __forceinline__ u32x4 sign8(uint32_t z, int s, uint32_t magpair) {
+  const uint32_t nz = ~z >> (8 * s);
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = nz >> (2 * j);
+    v[j] = magpair | ((t & 1u) << 15) | ((t & 2u) << 30);
+  }
+  return v;
+}
+
+// Scores of 128 queries (block x) against 256 database vectors (block y) of one chunk:
+// out[q][j] = ||q|| s_j (<q_rot, C[idx_j]> + (gamma_j / s_j) sqrt(pi/2)/d <q_s, z_j>) with unit q.
+// One block per CU with the query operands double-buffered in LDS (2 x 64 KB): the loads of
+// contraction chunk kc + 1 (query fragments and the packed words) are in flight while chunk
+// kc's MFMAs run, and the accumulators (8 query tiles x 4 key tiles per wave) stay in registers.
+template <int BITS>
+__global__ __launch_bounds__(256, 1) void k_search_scores(
+    const u32x4* __restrict__ qf, const float* __restrict__ qnorm, int64_t nq, int d,
+    const uint32_t* __restrict__ idx, const float* __restrict__ norms, const uint32_t* __restrict__ qbits,
+    const float* __restrict__ rnorms, int64_t m, CodebookArgs cb, float* __restrict__ out, int64_t ldo) {
+  using DT = DecodeTable<BITS>;
+  __shared__ u32x4 lds[2][4096];
+  __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
+  __shared__ _Float16 cent[16];
+  if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
+  const int nb = d >> 7;
+  const int W = d * BITS / 32;
+  const int qb = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t key0 = (int64_t)blockIdx.y * kSearchKeys + wave * 64;
+  const float kz = 1.2533141373155002512f / (float)d / kSketchScale;  // sqrt(pi/2) / d, rescaled
+
+  float sk[4];
+  uint32_t magp[4];
+  const uint32_t* kp[4];
+  const uint32_t* zp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t r = key0 + 16 * j + nl;
+    if (r >= m) r = m - 1;
+    kp[j] = idx + r * W + BITS * g;
+    zp[j] = qbits + r * (d >> 5) + g;
+    const float s = norms[r];
+    sk[j] = s;
+    const float zf = s > 0.f ? rnorms[r] / s * kz : 0.f;
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)zf);
+    magp[j] = h | (h << 16);
+  }
+  const u32x4* qsrc = qf + (size_t)qb * nb * 4096;
+
+  // chunk 0
+  uint32_t kw[4][BITS], zw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) kw[j][b] = kp[j][b];
+    zw[j] = zp[j][0];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lds[0][i * 256 + threadIdx.x] = qsrc[i * 256 + threadIdx.x];
+  __syncthreads();
+  build_table<BITS>(tab, cent);
+  __syncthreads();
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int qt = 0; qt < 8; ++qt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kc = 0; kc < nb; ++kc) {
+    const int cur = kc & 1;
+    const bool more = kc + 1 < nb;
+    u32x4 stage[16];
+    uint32_t kwn[4][BITS], zwn[4];
+    if (more) {
+      const u32x4* src = qsrc + (size_t)(kc + 1) * 4096;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) stage[i] = src[i * 256 + threadIdx.x];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) kwn[j][b] = kp[j][4 * BITS * (kc + 1) + b];
+        zwn[j] = zp[j][4 * (kc + 1)];
+      }
+    }
+    const u32x4* lq = lds[cur];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 bm[4], bz[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bm[j] = decode_keys<BITS>(kw[j], s, tab);
+        bz[j] = sign8(zw[j], s, magp[j]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) {
+        const u32x4 ar = lq[(qt * 4 + s) * 64 + lane];
+        const u32x4 az = lq[((8 + qt) * 4 + s) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[qt][j] = mfma_f16(ar, bm[j], acc[qt][j]);
+          acc[qt][j] = mfma_f16(az, bz[j], acc[qt][j]);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lds[cur ^ 1][i * 256 + threadIdx.x] = stage[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) kw[j][b] = kwn[j][b];
+        zw[j] = zwn[j];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t key = key0 + 16 * j + nl;
+    if (key >= m) continue;
+#pragma unroll
+    for (int qt = 0; qt < 8; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t q = (int64_t)qb * 128 + 16 * qt + 4 * g + r;
+        if (q < nq) out[q * ldo + key] = qnorm[q] * sk[j] * acc[qt][j][r];
+      }
+  }
+}
+
+// (score, index) order of the results: larger score first, then the smaller index.
+__device__ __forceinline__ bool better(float a, int64_t ia, float b, int64_t ib) {
+  return a > b || (a == b && ia < ib);
+}
+
+// Merges one chunk of scores of query blockIdx.x into its running top-k (top_s / top_i, sorted;
+// ignored when `first`).  Each thread keeps a sorted list of KMAX entries over its strided share;
+// k rounds of a block-wide argmax then pick the results.
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ sc, int64_t ldo, int64_t m,
+                                                     int64_t base, int k, int first, float* __restrict__ top_s,
+                                                     int64_t* __restrict__ top_i) {
+  __shared__ float red_s[4];
+  __shared__ int64_t red_i[4];
+  __shared__ int red_t[4];
+  __shared__ int winner;
+  const int64_t q = blockIdx.x;
+  const float* row = sc + q * ldo;
+  float ls[KMAX];
+  int64_t li[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    ls[i] = -INFINITY;
+    li[i] = -1;
+  }
+  auto insert = [&](float v, int64_t id) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < k && better(v, id, ls[i], li[i])) {
+        const float ts = ls[i];
+        const int64_t ti = li[i];
+        ls[i] = v;
+        li[i] = id;
+        v = ts;
+        id = ti;
+      }
+    }
+  };
+  if (!first && threadIdx.x == 0)
+    for (int i = 0; i < k; ++i) insert(top_s[q * k + i], top_i[q * k + i]);
+  // the last live entry, kept in a register so the filter needs no dynamic index
+  float ks = -INFINITY;
+  int64_t ki = -1;
+  auto refresh = [&]() {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i == k - 1) {
+        ks = ls[i];
+        ki = li[i];
+      }
+  };
+  refresh();
+  for (int64_t j = threadIdx.x; j < m; j += blockDim.x) {
+    const float v = row[j];
+    const int64_t id = base + j;
+    if (better(v, id, ks, ki)) {
+      insert(v, id);
+      refresh();
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    float bs = ls[0];
+    int64_t bi = li[0];
+    int bt = threadIdx.x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float os = __shfl_xor(bs, off);
+      const int64_t oi = __shfl_xor(bi, off);
+      const int ot = __shfl_xor(bt, off);
+      if (better(os, oi, bs, bi) || (os == bs && oi == bi && ot < bt)) {
+        bs = os;
+        bi = oi;
+        bt = ot;
+      }
+    }
+    if (lane == 0) {
+      red_s[wave] = bs;
+      red_i[wave] = bi;
+      red_t[wave] = bt;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s0 = red_s[0];
+      int64_t i0 = red_i[0];
+      int t0 = red_t[0];
+      for (int w = 1; w < 4; ++w)
+        if (better(red_s[w], red_i[w], s0, i0) || (red_s[w] == s0 && red_i[w] == i0 && red_t[w] < t0)) {
+          s0 = red_s[w];
+          i0 = red_i[w];
+          t0 = red_t[w];
+        }
+      winner = t0;
+      top_s[q * k + r] = s0;
+      top_i[q * k + r] = i0;
+    }
+    __syncthreads();
+    if (threadIdx.x == winner) {
+#pragma unroll
+      for (int i = 0; i + 1 < KMAX; ++i) {
+        ls[i] = ls[i + 1];
+        li[i] = li[i + 1];
+      }
+      ls[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = -1;
+    }
+  }
+}
+
+template <int BITS>
+hipError_t search_scores_launch(const u32x4* qf, const float* qnorm, int64_t nq, int d, const tq_packed* db,
+                                int64_t base, int64_t m, const CodebookArgs& cb, float* out, int64_t ldo,
+                                hipStream_t st) {
+  const int W = d * BITS / 32;
+  const dim3 grid((unsigned)((nq + 127) / 128), (unsigned)((m + kSearchKeys - 1) / kSearchKeys));
+  hipLaunchKernelGGL((k_search_scores<BITS>), grid, dim3(256), 0, st, qf, qnorm, nq, d, db->idx + base * W,
+                     db->norms + base, db->qjl + base * (d / 32), db->rnorms + base, m, cb, out, ldo);
+  return hipGetLastError();
+}
+
+struct SearchLayout {
+  size_t qr, qs, qn, qf, sc, total;
+  int64_t chunk;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+SearchLayout search_layout(int64_t nq, int64_t n, int d) {
+  SearchLayout l;
+  const int64_t nqp = (nq + 127) / 128 * 128;
+  l.chunk = n < kSearchChunk ? (n > 0 ? n : 1) : kSearchChunk;
+  l.qr = 0;
+  l.qs = l.qr + align256((size_t)nqp * d * 4);
+  l.qn = l.qs + align256((size_t)nqp * d * 4);
+  l.qf = l.qn + align256((size_t)nqp * 4);
+  l.sc = l.qf + align256((size_t)(nqp / 128) * (d / 128) * 4096 * 16);
+  l.total = l.sc + align256((size_t)nq * l.chunk * 4);
+  return l;
+}
+
+}  // namespace
+
+size_t encode_general_ws_per_vector(int d) { return (size_t)d * 4 + (size_t)(d / 128) * 4; }
+
+hipError_t launch_encode_general(const void* x, bool bf16, int64_t n, int d, const tq_rotation_s* rot,
+                                 const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                 uint32_t* qjl_bits, float* rnorms, float* y_out, void* ws, size_t ws_bytes,
+                                 hipStream_t st) {
+  if (y_out)
+    return gen_dispatch<kEpiY, 1>(x, bf16, n, d, rot->gfrag_dev, rot->passes, rot->post_scale, cb, norms, nullptr,
+                                  y_out, nullptr, nullptr, st);
+  if (!qjl) return gen_dispatch_bits<kEpiMse>(x, bf16, n, d, rot, cb, norms, idx, nullptr, nullptr, st);
+  const size_t per = encode_general_ws_per_vector(d);
+  const int64_t cap = (int64_t)(ws_bytes / per);
+  const int64_t chunk = cap >= n ? n : cap / kGenVectors * kGenVectors;
+  if (chunk <= 0) return hipErrorInvalidValue;
+  float* res = static_cast<float*>(ws);
+  float* rpart = res + (size_t)chunk * d;
+  const int W = d * cb.bits / 32;
+  const size_t esz = bf16 ? 2 : 4;
+  for (int64_t base = 0; base < n; base += chunk) {
+    const int64_t m = n - base < chunk ? n - base : chunk;
+    const void* xb = static_cast<const char*>(x) + (size_t)base * d * esz;
+    hipError_t e = gen_dispatch_bits<kEpiRes>(xb, bf16, m, d, rot, cb, norms + base, idx + base * W, res, rpart, st);
+    if (e != hipSuccess) return e;
+    e = gen_launch<kEpiSign, false, 2, 1>(res, m, d, qjl->gfrag_dev, 1.0f, cb, norms + base, nullptr, nullptr, nullptr,
+                                          rpart, qjl_bits + base * (d / 32), rnorms + base, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+size_t search_workspace_bytes(int64_t nq, int64_t n, int d, int k) {
+  (void)k;
+  return search_layout(nq, n, d).total;
+}
+
+hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, const CodebookArgs& cb,
+                              const tq_rotation_s* rot, const tq_qjl_s* qjl, int k, float* top_s,
+                              int64_t* top_i, void* ws, hipStream_t st) {
+  const int d = db->d;
+  const SearchLayout l = search_layout(nq, db->n, d);
+  char* w = static_cast<char*>(ws);
+  float* qr = reinterpret_cast<float*>(w + l.qr);
+  float* qs = reinterpret_cast<float*>(w + l.qs);
+  float* qn = reinterpret_cast<float*>(w + l.qn);
+  u32x4* qf = reinterpret_cast<u32x4*>(w + l.qf);
+  float* sc = reinterpret_cast<float*>(w + l.sc);
+  // query prologue: unit rotated queries and norms, then the sketch S q / ||q|| = S' (R q / ||q||)
+  const uint16_t* rfrag = d == kFragD ? rot->frag_dev : rot->gfrag_dev;
+  const uint16_t* sfrag = d == kFragD ? qjl->frag_dev : qjl->gfrag_dev;
+  hipError_t e = gen_dispatch<kEpiY, 1>(q, false, nq, d, rfrag, rot->passes, rot->post_scale, cb, qn, nullptr, qr,
+                                        nullptr, nullptr, st);
+  if (e != hipSuccess) return e;
+  e = gen_launch<kEpiRaw, false, 2, 1>(qr, nq, d, sfrag, 1.0f, cb, nullptr, nullptr, qs, nullptr, nullptr, nullptr,
+                                       nullptr, st);
+  if (e != hipSuccess) return e;
+  const int64_t nqb = (nq + 127) / 128;
+  hipLaunchKernelGGL(k_search_qfrag, dim3((unsigned)(nqb * (d / 128))), dim3(256), 0, st, qr, qs, nq, d, qf);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = db->n;
+  int64_t base = 0;
+  do {
+    const int64_t m = n - base < l.chunk ? n - base : l.chunk;
+    if (m > 0) {
+      switch (cb.bits) {
+        case 1: e = search_scores_launch<1>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
+        case 2: e = search_scores_launch<2>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
+        case 3: e = search_scores_launch<3>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
+        case 4: e = search_scores_launch<4>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
+        default: return hipErrorInvalidValue;
+      }
+      if (e != hipSuccess) return e;
+    }
+    if (k <= 16)
+      hipLaunchKernelGGL(k_search_topk<16>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.chunk, m, base, k,
+                         base == 0 ? 1 : 0, top_s, top_i);
+    else
+      hipLaunchKernelGGL(k_search_topk<kSearchMaxK>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.chunk, m, base, k,
+                         base == 0 ? 1 : 0, top_s, top_i);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    base += m;
+  } while (base < n);
+  return hipSuccess;
+}
+
+}  // namespace tq

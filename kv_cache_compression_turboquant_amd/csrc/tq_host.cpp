@@ -284,6 +284,34 @@ void build_fragments(const double* m, double scale, std::vector<uint16_t>& out) 
         }
 }
 
+// Chunked fragments of a d x d matrix (d a multiple of 128) for the general-d GEMM kernels:
+// chunk (ob, kc) is the 128 x 128 block M[128 ob .., 128 kc ..] laid out exactly as
+// build_fragments lays out a d = 128 matrix; chunks follow each other as [ob][kc][pass].
+void build_fragments_g(const double* m, int d, double scale, std::vector<uint16_t>& out) {
+  const int nb = d / 128;
+  out.assign((size_t)nb * nb * 2 * tq::kFragElems, 0);
+  parallel_for(0, (int64_t)nb * nb, 1, [&](int64_t blk) {
+    const int ob = (int)(blk / nb), kc = (int)(blk % nb);
+    const size_t base = (size_t)blk * 2 * tq::kFragElems;
+    for (int t = 0; t < 8; ++t)
+      for (int s = 0; s < 4; ++s)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const int mm = lane % 16, g = lane / 16;
+            const int row = 128 * ob + 32 * (mm / 4) + 4 * t + (mm % 4);
+            const int col = 128 * kc + 32 * g + 8 * s + e;
+            const float v = (float)(m[(size_t)row * d + col] * scale);
+            const uint16_t hi = bf16_rne(v);
+            const uint16_t lo = bf16_rne(v - bf16_to_f(hi));
+            const size_t idx = (((size_t)t * 4 + s) * 64 + lane) * 8 + e;
+            out[base + idx] = hi;
+            out[base + tq::kFragElems + idx] = lo;
+          }
+  });
+}
+
+inline bool general_d(int d) { return d % 128 == 0 && d >= 256 && d <= 4096; }
+
 template <class T>
 tq_status upload(const std::vector<T>& host, T** dev, const char* what) {
   hipError_t e = hipMalloc((void**)dev, host.size() * sizeof(T));
@@ -303,6 +331,7 @@ void free_rotation(tq_rotation_s* r) {
   if (r->rt32_dev) hipFree(r->rt32_dev);
   if (r->frag_dev) hipFree(r->frag_dev);
   if (r->fragt_dev) hipFree(r->fragt_dev);
+  if (r->gfrag_dev) hipFree(r->gfrag_dev);
   delete r;
 }
 
@@ -311,6 +340,7 @@ void free_qjl(tq_qjl_s* q) {
   if (q->s32_dev) hipFree(q->s32_dev);
   if (q->st32_dev) hipFree(q->st32_dev);
   if (q->frag_dev) hipFree(q->frag_dev);
+  if (q->gfrag_dev) hipFree(q->gfrag_dev);
   delete q;
 }
 
@@ -344,6 +374,15 @@ tq_status finish_rotation(tq_rotation_s* r) {
     if (st != TQ_OK) return st;
     st = upload(fragt, &r->fragt_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
+  } else if (general_d(d)) {
+    std::vector<uint16_t> frag;
+    const bool wht = r->kind == TQ_ROT_WHT;
+    // WHT: sqrt(d) R has entries +-1, exact in bf16: one pass, scaled after the product.
+    build_fragments_g(r->r.data(), d, wht ? std::sqrt((double)d) : 1.0, frag);
+    r->passes = wht ? 1 : 2;
+    r->post_scale = wht ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+    st = upload(frag, &r->gfrag_dev, "upload rotation fragments");
+    if (st != TQ_OK) return st;
   }
   return TQ_OK;
 }
@@ -363,7 +402,7 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
     }
   tq_status st = upload(s32, &q->s32_dev, "upload qjl");
   if (st == TQ_OK) st = upload(st32, &q->st32_dev, "upload qjl transpose");
-  if (st == TQ_OK && d == tq::kFragD) {
+  if (st == TQ_OK && (d == tq::kFragD || general_d(d))) {
     // S' = S R^T in fp64
     std::vector<double> sp((size_t)d * d, 0.0);
     const double* sm = q->s.data();
@@ -376,8 +415,13 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
       }
     });
     std::vector<uint16_t> frag;
-    build_fragments(sp.data(), 1.0, frag);
-    st = upload(frag, &q->frag_dev, "upload qjl fragments");
+    if (d == tq::kFragD) {
+      build_fragments(sp.data(), 1.0, frag);
+      st = upload(frag, &q->frag_dev, "upload qjl fragments");
+    } else {
+      build_fragments_g(sp.data(), d, 1.0, frag);
+      st = upload(frag, &q->gfrag_dev, "upload qjl fragments");
+    }
   }
   if (st != TQ_OK) {
     free_qjl(q);
@@ -577,8 +621,8 @@ static tq_status check_packed(const tq_packed* p, int d, int bits, int mode, con
 }
 
 tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_mode mode,
-                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* out,
-                    void* stream) {
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* out, void* ws_dev,
+                    size_t ws_bytes, void* stream) {
   static const char* fn = "tq_encode";
   if (!cb || !rot || !out) return fail(TQ_EINVAL, "%s: null handle or output", fn);
   if (n < 0) return fail(TQ_EINVAL, "%s: negative n", fn);
@@ -597,22 +641,43 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   } else if (qjl) {
     return fail(TQ_EINVAL, "%s: qjl handle given for MSE mode", fn);
   }
-  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (fused path covers d=128)", fn, d);
-  if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the fused encode needs an antisymmetric codebook", fn);
+  if (d != tq::kFragD && !general_d(d))
+    return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d = 128, or a multiple of 128 in [256, 4096])", fn, d);
+  if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the encode kernels need an antisymmetric codebook", fn);
   tq_status st = check_packed(out, d, stage, mode, fn);
   if (st != TQ_OK) return st;
   if (out->n != n) return fail(TQ_ESHAPE, "%s: out->n=%lld, n=%lld", fn, (long long)out->n, (long long)n);
+  if (d != tq::kFragD && out->layout != TQ_LAYOUT_ROWS)
+    return fail(TQ_EUNSUPPORTED, "%s: the token-blocked layout needs d = 128", fn);
+  if (d != tq::kFragD && mode == TQ_MODE_PROD && n > 0) {
+    const size_t per = tq::encode_general_ws_per_vector(d);
+    if (!ws_dev) return fail(TQ_EINVAL, "%s: prod at d=%d needs a workspace", fn, d);
+    if (ws_bytes < per * (size_t)std::min<int64_t>(n, tq::kGenVectors))
+      return fail(TQ_ENOMEM, "%s: workspace of %zu bytes holds fewer than %d vectors (%zu bytes each)", fn,
+                  ws_bytes, tq::kGenVectors, per);
+  }
   if (n == 0) return ok();
+  const bool prod = mode == TQ_MODE_PROD;
+  if (d != tq::kFragD)
+    return check_launch(tq::launch_encode_general(x_dev, dt == TQ_BF16, n, d, rot, prod ? qjl : nullptr, cb->args,
+                                                  out->idx, out->norms, prod ? out->qjl : nullptr,
+                                                  prod ? out->rnorms : nullptr, nullptr, ws_dev, ws_bytes,
+                                                  as_stream(stream)),
+                        fn);
   if (out->layout == TQ_LAYOUT_TOKEN_BLOCKED)
     return check_launch(tq::launch_encode_vblock_d128(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx,
                                                       out->norms, as_stream(stream)),
                         fn);
-  return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, mode == TQ_MODE_PROD ? qjl : nullptr,
-                                             cb->args, out->idx, out->norms,
-                                             mode == TQ_MODE_PROD ? out->qjl : nullptr,
-                                             mode == TQ_MODE_PROD ? out->rnorms : nullptr, nullptr,
-                                             as_stream(stream)),
+  return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args,
+                                             out->idx, out->norms, prod ? out->qjl : nullptr,
+                                             prod ? out->rnorms : nullptr, nullptr, as_stream(stream)),
                       fn);
+}
+
+size_t tq_encode_workspace(int64_t n, int d, int b, tq_mode mode) {
+  (void)b;
+  if (n <= 0 || mode != TQ_MODE_PROD || d == tq::kFragD || !general_d(d)) return 0;
+  return tq::encode_general_ws_per_vector(d) * (size_t)std::min<int64_t>(n, tq::kEncodeChunk);
 }
 
 tq_status tq_rotate(const void* x_dev, tq_dtype dt, int64_t n, int d, tq_rotation_t rot,
@@ -623,10 +688,15 @@ tq_status tq_rotate(const void* x_dev, tq_dtype dt, int64_t n, int d, tq_rotatio
   if (n > 0 && (!x_dev || !y_dev || !norms_dev)) return fail(TQ_EINVAL, "%s: null buffer", fn);
   if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_EUNSUPPORTED, "%s: dtype must be f32 or bf16", fn);
   if (rot->d != d) return fail(TQ_ESHAPE, "%s: rotation d=%d, d=%d", fn, rot->d, d);
-  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported", fn, d);
+  if (d != tq::kFragD && !general_d(d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported", fn, d);
   if (n == 0) return ok();
   tq::CodebookArgs none{};
   none.bits = 1;
+  if (d != tq::kFragD)
+    return check_launch(tq::launch_encode_general(x_dev, dt == TQ_BF16, n, d, rot, nullptr, none, nullptr,
+                                                  norms_dev, nullptr, nullptr, y_dev, nullptr, 0,
+                                                  as_stream(stream)),
+                        fn);
   return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, nullptr, none, nullptr, norms_dev,
                                              nullptr, nullptr, y_dev, as_stream(stream)),
                       fn);
@@ -740,3 +810,34 @@ tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, 
 }
 
 }  // extern "C"
+
+size_t tq_search_workspace(int64_t nq, int64_t n, int d, int k) {
+  if (nq <= 0 || n < 0 || d <= 0 || d % 128 != 0 || k < 1 || k > tq::kSearchMaxK) return 0;
+  return tq::search_workspace_bytes(nq, n, d, k);
+}
+
+tq_status tq_search_topk(const float* q_dev, int64_t nq, const tq_packed* db, tq_codebook_t cb,
+                         tq_rotation_t rot, tq_qjl_t qjl, int k, float* top_s_dev, int64_t* top_i_dev,
+                         void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_search_topk";
+  if (!db || !cb || !rot || !qjl) return fail(TQ_EINVAL, "%s: null handle or database", fn);
+  if (nq < 0) return fail(TQ_EINVAL, "%s: negative nq", fn);
+  if (k < 1 || k > tq::kSearchMaxK) return fail(TQ_EINVAL, "%s: k=%d outside [1, %d]", fn, k, tq::kSearchMaxK);
+  const int d = db->d;
+  if (db->mode != TQ_MODE_PROD) return fail(TQ_EUNSUPPORTED, "%s: the database must be prod mode", fn);
+  if (db->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: the database must use the rows layout", fn);
+  if (d != tq::kFragD && !general_d(d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported", fn, d);
+  if (cb->d != d || rot->d != d || qjl->d != d)
+    return fail(TQ_ESHAPE, "%s: d=%d, codebook d=%d, rotation d=%d, qjl d=%d", fn, d, cb->d, rot->d, qjl->d);
+  if (cb->b != db->bits) return fail(TQ_ESHAPE, "%s: codebook has %d bits, database %d", fn, cb->b, db->bits);
+  if (qjl->rot_id != rot->id) return fail(TQ_EINVAL, "%s: qjl handle is bound to another rotation", fn);
+  tq_status st = check_packed(db, d, db->bits, TQ_MODE_PROD, fn);
+  if (st != TQ_OK) return st;
+  if (nq == 0) return ok();
+  if (!q_dev || !top_s_dev || !top_i_dev || !ws_dev) return fail(TQ_EINVAL, "%s: null buffer", fn);
+  const size_t need = tq::search_workspace_bytes(nq, db->n, d, k);
+  if (ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  return check_launch(tq::launch_search_topk(q_dev, nq, db, cb->args, rot, qjl, k, top_s_dev, top_i_dev, ws_dev,
+                                             as_stream(stream)),
+                      fn);
+}

@@ -56,6 +56,9 @@ struct tq_rotation_s {
   uint16_t* frag_dev = nullptr;   // bf16 fragments [2][kFragElems] (d = 128 only)
   uint16_t* fragt_dev = nullptr;  // bf16 B-operand fragments of R^T [2][kFragElems] (d = 128):
                                   // [pass][cb][s][lane][e] = R[8*(lane%16) + cb][32*(lane/16) + 8s + e]
+  uint16_t* gfrag_dev = nullptr;  // general d (multiple of 128, >= 256): A fragments of R, one
+                                  // (128 x 128) chunk per (output block ob, contraction block kc):
+                                  // [ob][kc][pass 0..1][kFragElems], each chunk laid out like frag_dev
   int passes = 2;                 // 1 when R is exactly representable after scaling
   float post_scale = 1.0f;        // y = post_scale * (fragments . x)
 };
@@ -68,6 +71,7 @@ struct tq_qjl_s {
   float* s32_dev = nullptr;       // fp32 S, row-major [d, d]
   float* st32_dev = nullptr;      // fp32 S^T, row-major [d, d]
   uint16_t* frag_dev = nullptr;   // bf16 fragments of S' = S R^T [2][kFragElems] (d = 128)
+  uint16_t* gfrag_dev = nullptr;  // general d: chunked A fragments of S', as tq_rotation_s::gfrag_dev
 };
 
 namespace tq {
@@ -96,6 +100,23 @@ hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, cons
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st);
 size_t scores_workspace_bytes(int B, int Hq, int d);
+// General d (multiple of 128 in [256, 4096]), rows layout.  y_out set: rotated unit
+// coordinates and norms only.  Prod (qjl set) stages the residual through ws in chunks.
+hipError_t launch_encode_general(const void* x, bool bf16, int64_t n, int d, const tq_rotation_s* rot,
+                                 const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                 uint32_t* qjl_bits, float* rnorms, float* y_out, void* ws, size_t ws_bytes,
+                                 hipStream_t st);
+size_t encode_general_ws_per_vector(int d);
+constexpr int64_t kEncodeChunk = 131072;  // vectors per prod chunk at the default workspace size
+constexpr int kGenVectors = 128;          // vectors per block of the general-d GEMM kernels
+
+// Top-k inner-product search over a prod database (rows layout, d a multiple of 128).
+size_t search_workspace_bytes(int64_t nq, int64_t n, int d, int k);
+hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, const CodebookArgs& cb,
+                              const tq_rotation_s* rot, const tq_qjl_s* qjl, int k, float* top_s,
+                              int64_t* top_i, void* ws, hipStream_t st);
+constexpr int kSearchMaxK = 32;
+
 // q_rot (and, with st_mat, the QJL sketch in sign-slot order plus the per-head constant) of
 // every query head, d = 128, into the score workspace layout.
 hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,

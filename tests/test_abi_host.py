@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(tq):
     for name in names:
         assert hasattr(raw, name), name
         assert name in _binding.SIGNATURES, f"binding lacks {name}"
-    assert tq.lib().tq_abi_version() == 1
+    assert tq.lib().tq_abi_version() == 2
 
 
 def test_splitmix_bit_identical(tq):
@@ -108,9 +108,11 @@ def test_error_paths(tq):
     assert lib.tq_packed_words(128, 3) == 12 and lib.tq_packed_words(100, 3) == 0
     # hot-path entry points validate before touching the device
     desc = tq.tq_packed(128, 3, 0, 0, 10, None, None, None, None)
-    assert lib.tq_encode(None, 1, 10, 128, 3, 0, None, None, None, ctypes.byref(desc), None) == 1
+    assert lib.tq_encode(None, 1, 10, 128, 3, 0, None, None, None, ctypes.byref(desc), None, 0, None) == 1
     cbh = tq.codebook(128, 2)
-    assert lib.tq_encode(None, 1, 10, 128, 3, 0, cbh.ptr, None, None, ctypes.byref(desc), None) == 1
+    assert lib.tq_encode(None, 1, 10, 128, 3, 0, cbh.ptr, None, None, ctypes.byref(desc), None, 0, None) == 1
+    # search validates its handles and k before anything else
+    assert lib.tq_search_topk(None, 4, ctypes.byref(desc), None, None, None, 10, None, None, None, 0, None) == 1
     assert lib.tq_scores(None, 1, 32, 5, 10, ctypes.byref(desc), cbh.ptr, None, None, None, None, 0, None) == 1
     assert lib.tq_quantize_rotated(None, 10, 64, cbh.ptr, None, None) == 1   # null buffers
     assert lib.tq_quantize_rotated(None, -1, 128, cbh.ptr, None, None) == 1
@@ -124,3 +126,20 @@ def test_codebook_from_values_checks(tq):
     cb = tq.codebook_from_values(4, [-0.6, 0.6])
     c, t = cb.values()
     assert t.tolist() == [0.0]
+
+
+def test_workspace_sizes(tq):
+    lib = tq.lib()
+    # encode: only prod away from d = 128 stages residual rows (d + d/128 floats per vector)
+    assert lib.tq_encode_workspace(1000, 128, 4, 1) == 0
+    assert lib.tq_encode_workspace(1000, 1536, 4, 0) == 0
+    assert lib.tq_encode_workspace(1000, 1536, 4, 1) == 1000 * (1536 + 12) * 4
+    assert lib.tq_encode_workspace(10 ** 6, 1536, 4, 1) == 131072 * (1536 + 12) * 4
+    assert lib.tq_encode_workspace(0, 1536, 4, 1) == 0
+    # search: rejected shapes report 0; the score chunk dominates at large n
+    assert lib.tq_search_workspace(1024, 10 ** 6, 1536, 0) == 0
+    assert lib.tq_search_workspace(1024, 10 ** 6, 1536, 33) == 0
+    assert lib.tq_search_workspace(1024, 10 ** 6, 1000, 10) == 0
+    big = lib.tq_search_workspace(1024, 10 ** 6, 1536, 10)
+    assert big >= 1024 * 65536 * 4 + 2 * 1024 * 1536 * 4
+    assert lib.tq_search_workspace(1024, 100, 1536, 10) < big
