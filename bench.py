@@ -245,6 +245,33 @@ def bench_other(name, steps, warmup):
         res.update({"bits": b, "encode_v_blocked_ms": enc_v_ms, "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6,
                     "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
                     "kv_positions_per_s": n / at_ms * 1e3})
+    elif name == "c5":
+        cfg = wl.CONFIGS["c5"]
+        n, d = cfg.n, cfg.d
+        nq, k = cfg.extra["queries"], cfg.extra["k"]
+        x = torch.empty((n, d), dtype=torch.float32, device=dev)
+        for lo, xc in wl.index_vectors(cfg):
+            x[lo:lo + xc.shape[0]].copy_(torch.from_numpy(xc))
+        q = torch.from_numpy(wl.index_queries(cfg)).to(dev)
+        rot = tq.make_rotation(d, cfg.rot_seed, "dense")
+        qjl = tq.make_qjl(d, cfg.qjl_seed, rot)
+        cb = tq.codebook(d, cfg.bits - 1)
+        p = tq.alloc_packed(n, d, cfg.bits - 1, "prod", device=dev)
+        ews = torch.empty((tq.encode_workspace(n, d, cfg.bits, "prod"),), dtype=torch.uint8, device=dev)
+        enc_ms = _timed(lambda i: tq.encode(x, cfg.bits, "prod", cb, rot, qjl, out=p, ws=ews), steps, warmup)
+        del x
+        sws = torch.empty((tq.search_workspace(nq, n, d, k),), dtype=torch.uint8, device=dev)
+        outs = (torch.empty((nq, k), device=dev), torch.empty((nq, k), dtype=torch.int64, device=dev))
+        se_ms = _timed(lambda i: tq.search_topk(q, p, k, cb, rot, qjl, ws=sws, out=outs), steps, warmup)
+        enc_flops = 4.0 * n * d * d            # R x and S' r, fp32-accurate (three bf16 passes each)
+        search_flops = 4.0 * nq * n * d        # <q_rot, c> and <q_s, z> per pair, fp16 operands
+        res.update({"encode_ms": enc_ms, "encode_vectors_per_s": n / enc_ms * 1e3,
+                    "encode_tflops": enc_flops / enc_ms / 1e9,
+                    "encode_frac_fp32_mfma": enc_flops / enc_ms / 1e9 / 157.3,
+                    "encode_frac_bf16_issued": 3 * enc_flops / enc_ms / 1e9 / 2500.0,
+                    "search_ms": se_ms, "search_scores_per_s": nq * n / se_ms * 1e3,
+                    "search_tflops": search_flops / se_ms / 1e9,
+                    "search_frac_fp16_mfma": search_flops / se_ms / 1e9 / 2500.0})
     print(json.dumps(res), flush=True)
 
 
@@ -255,7 +282,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4", "c5"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "

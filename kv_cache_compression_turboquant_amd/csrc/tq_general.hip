@@ -478,12 +478,15 @@ __device__ __forceinline__ bool better(float a, int64_t ia, float b, int64_t ib)
 }
 
 // Merges one chunk of scores of query blockIdx.x into its running top-k (top_s / top_i, sorted;
-// ignored when `first`).  Each thread keeps a sorted list of KMAX entries over its strided share;
-// k rounds of a block-wide argmax then pick the results.
+// ignored when `first`).  Every thread filters its strided share against the running k-th
+// result and keeps a sorted list of KMAX entries; k rounds of a block-wide argmax then pick the
+// results.  Scores are read as float4 batches (ldo is a multiple of 4) so that a thread's loads
+// are in flight together rather than one per data-dependent branch.
 template <int KMAX>
 __global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ sc, int64_t ldo, int64_t m,
                                                      int64_t base, int k, int first, float* __restrict__ top_s,
                                                      int64_t* __restrict__ top_i) {
+  constexpr int U = 8;  // float4 loads per thread per batch
   __shared__ float red_s[4];
   __shared__ int64_t red_i[4];
   __shared__ int red_t[4];
@@ -510,28 +513,45 @@ __global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ s
       }
     }
   };
-  if (!first && threadIdx.x == 0)
-    for (int i = 0; i < k; ++i) insert(top_s[q * k + i], top_i[q * k + i]);
-  // the last live entry, kept in a register so the filter needs no dynamic index
+  // the bound an element must beat: the running k-th result, then the thread's own k-th entry
   float ks = -INFINITY;
   int64_t ki = -1;
-  auto refresh = [&]() {
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i)
-      if (i == k - 1) {
-        ks = ls[i];
-        ki = li[i];
-      }
-  };
-  refresh();
-  for (int64_t j = threadIdx.x; j < m; j += blockDim.x) {
-    const float v = row[j];
-    const int64_t id = base + j;
+  if (!first) {
+    ks = top_s[q * k + k - 1];
+    ki = top_i[q * k + k - 1];
+    if (threadIdx.x == 0)
+      for (int i = 0; i < k; ++i) insert(top_s[q * k + i], top_i[q * k + i]);
+  }
+  auto consider = [&](float v, int64_t id) {
     if (better(v, id, ks, ki)) {
       insert(v, id);
-      refresh();
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i == k - 1 && better(ls[i], li[i], ks, ki)) {
+          ks = ls[i];
+          ki = li[i];
+        }
+    }
+  };
+  const int64_t m4 = m >> 2;
+  const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+  for (int64_t b0 = threadIdx.x; b0 < m4; b0 += (int64_t)blockDim.x * U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = b0 + (int64_t)u * blockDim.x;
+      v[u] = j < m4 ? row4[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = b0 + (int64_t)u * blockDim.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j < m4) consider(v[u][e], base + 4 * j + e);
     }
   }
+  for (int64_t j = 4 * m4 + threadIdx.x; j < m; j += blockDim.x) consider(row[j], base + j);
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = 0; r < k; ++r) {
     float bs = ls[0];
@@ -594,7 +614,8 @@ hipError_t search_scores_launch(const u32x4* qf, const float* qnorm, int64_t nq,
 
 struct SearchLayout {
   size_t qr, qs, qn, qf, sc, total;
-  int64_t chunk;
+  int64_t chunk;  // database vectors per score chunk
+  int64_t ldo;    // score row stride (a multiple of 64 floats)
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -603,12 +624,13 @@ SearchLayout search_layout(int64_t nq, int64_t n, int d) {
   SearchLayout l;
   const int64_t nqp = (nq + 127) / 128 * 128;
   l.chunk = n < kSearchChunk ? (n > 0 ? n : 1) : kSearchChunk;
+  l.ldo = (l.chunk + 63) / 64 * 64;
   l.qr = 0;
   l.qs = l.qr + align256((size_t)nqp * d * 4);
   l.qn = l.qs + align256((size_t)nqp * d * 4);
   l.qf = l.qn + align256((size_t)nqp * 4);
   l.sc = l.qf + align256((size_t)(nqp / 128) * (d / 128) * 4096 * 16);
-  l.total = l.sc + align256((size_t)nq * l.chunk * 4);
+  l.total = l.sc + align256((size_t)nq * l.ldo * 4);
   return l;
 }
 
@@ -679,19 +701,19 @@ hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, c
     const int64_t m = n - base < l.chunk ? n - base : l.chunk;
     if (m > 0) {
       switch (cb.bits) {
-        case 1: e = search_scores_launch<1>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
-        case 2: e = search_scores_launch<2>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
-        case 3: e = search_scores_launch<3>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
-        case 4: e = search_scores_launch<4>(qf, qn, nq, d, db, base, m, cb, sc, l.chunk, st); break;
+        case 1: e = search_scores_launch<1>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
+        case 2: e = search_scores_launch<2>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
+        case 3: e = search_scores_launch<3>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
+        case 4: e = search_scores_launch<4>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
         default: return hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;
     }
     if (k <= 16)
-      hipLaunchKernelGGL(k_search_topk<16>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.chunk, m, base, k,
+      hipLaunchKernelGGL(k_search_topk<16>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, m, base, k,
                          base == 0 ? 1 : 0, top_s, top_i);
     else
-      hipLaunchKernelGGL(k_search_topk<kSearchMaxK>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.chunk, m, base, k,
+      hipLaunchKernelGGL(k_search_topk<kSearchMaxK>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, m, base, k,
                          base == 0 ? 1 : 0, top_s, top_i);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

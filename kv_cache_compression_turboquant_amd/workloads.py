@@ -58,19 +58,26 @@ def kv_tensor_bf16(B, hkv, T, d, seed, outlier_seed, scale_seed=None, outlier_sc
     return out
 
 
-def lowrank_unit_vectors(n, d, rank, beta, seed_g, seed_u, seed_w, chunk=65536):
-    """n unit vectors g + sqrt(beta) U w, normalised; U = Q factor of a seeded Gaussian."""
+def iter_lowrank_unit_vectors(n, d, rank, beta, seed_g, seed_u, seed_w, chunk=65536):
+    """Yields (first row, rows) of n unit vectors g + sqrt(beta) U w, normalised, in chunks;
+    U = Q factor of a seeded Gaussian [d, rank]."""
     u, _ = np.linalg.qr(np.random.default_rng(seed_u).standard_normal((d, rank)))
     rg = np.random.default_rng(seed_g)
     rw = np.random.default_rng(seed_w)
-    out = np.empty((n, d), dtype=np.float32)
     for lo in range(0, n, chunk):
         hi = min(n, lo + chunk)
         g = rg.standard_normal((hi - lo, d))
         w = rw.standard_normal((hi - lo, rank))
         x = g + np.sqrt(beta) * (w @ u.T)
         x /= np.linalg.norm(x, axis=1, keepdims=True)
-        out[lo:hi] = x
+        yield lo, x.astype(np.float32)
+
+
+def lowrank_unit_vectors(n, d, rank, beta, seed_g, seed_u, seed_w, chunk=65536):
+    """n unit vectors g + sqrt(beta) U w (fp32 [n, d]), normalised; U = Q factor of a seeded Gaussian."""
+    out = np.empty((n, d), dtype=np.float32)
+    for lo, x in iter_lowrank_unit_vectors(n, d, rank, beta, seed_g, seed_u, seed_w, chunk):
+        out[lo:lo + x.shape[0]] = x
     return out
 
 
@@ -119,6 +126,16 @@ def kv_keys(cfg, T=None, B=None):
 
 def kv_values(cfg, T=None, B=None):
     return kv_tensor_bf16(B or cfg.B, cfg.hkv, T or cfg.T, cfg.d, seed=20, outlier_seed=21, scale_seed=None)
+
+
+def index_vectors(cfg):
+    """Database generator of the vector-index workload (seeds 0 / 30 / 31, beta 24, rank 64)."""
+    return iter_lowrank_unit_vectors(cfg.n, cfg.d, 64, 24.0, 0, 30, 31)
+
+
+def index_queries(cfg):
+    """The workload's queries: the same law, seeds 32 / 30 / 33."""
+    return lowrank_unit_vectors(cfg.extra["queries"], cfg.d, 64, 24.0, 32, 30, 33)
 
 
 def kv_queries(cfg, B=None):
