@@ -224,9 +224,12 @@ __global__ __launch_bounds__(256) void k_attn_d128(
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
-  using DK = DecodeTable<KB>;
-  using DV = DecodeTable<VB>;
-  __shared__ __attribute__((aligned(16))) uint8_t ktab[2 * DK::BYTES];
+  // replicated decode tables, at most 16 KB each so that two blocks fit a CU
+  constexpr int KC = table_copies<KB, true, 16384>();
+  constexpr int VC = table_copies<VB, false, 16384>();
+  using DK = DecodeTable<KB, true, KC>;
+  using DV = DecodeTable<VB, false, VC>;
+  __shared__ __attribute__((aligned(16))) uint8_t ktab[DK::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
   __shared__ float kcent[16];
   __shared__ _Float16 vcent[16];
@@ -238,11 +241,13 @@ __global__ __launch_bounds__(256) void k_attn_d128(
     vcent[threadIdx.x] = (_Float16)cbv.c[threadIdx.x];
   }
   __syncthreads();
-  build_table2<KB>(ktab, kcent);
-  build_table<VB>(vtab, vcent);
+  build_table2<KB, KC>(ktab, kcent);
+  build_table<VB, VC>(vtab, vcent);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
+  const uint8_t* ktabl = DK::lane_base(ktab, lane);
+  const uint8_t* vtabl = DV::lane_base(vtab, lane);
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const int g = lane >> 4;
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(256) void k_attn_d128(
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 khi, klo;
-        decode8_2<KB>(cur.kw[tt], 8 * KB * s, ktab, khi, klo);
+        decode8_2<KB, KC>(cur.kw[tt], 8 * KB * s, ktabl, khi, klo);
         d = mfma_f16(am[s], khi, d);
         d = mfma_f16(am2[s], klo, d);
       }
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(256) void k_attn_d128(
     }
     // B operand: the value chunks of octet g at coordinates 8 n .. 8 n + 7
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB>(cur.vw, 8 * VB * c, vtab), acc[c]);
+    for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB, VC>(cur.vw, 8 * VB * c, vtabl), acc[c]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     cur = nxt;

@@ -86,14 +86,32 @@ __device__ __forceinline__ void load_frags(const u32x4* lds, int c, int lane, u3
     for (int s = 0; s < 4; ++s) a[p][s] = lds[p * kFragU4 + (c * 4 + s) * 64 + lane];
 }
 
-template <int BITS>
+// Decode tables in LDS: a field of F packed bits (F = 6 for 3-bit indices, else 8) maps to the
+// fp16 centroids of its F / BITS coordinates (SPLIT: followed by their fp16 remainders
+// c - fp16(c)).  The table is stored COPIES times, interleaved entry by entry, and lane l reads
+// copy l % COPIES: with COPIES = 128 / entry bytes, the lanes that one LDS cycle serves (128
+// bytes) hit distinct banks whatever their fields.  Fewer copies trade conflicts for space.
+template <int BITS, bool SPLIT, int COPIES>
 struct DecodeTable {
   static constexpr int F = BITS == 3 ? 6 : 8;
-  static constexpr int PER = F / BITS;             // coordinates per field
+  static constexpr int PER = F / BITS;                    // coordinates per field
   static constexpr int ENTRIES = 1 << F;
-  static constexpr int BYTES = ENTRIES * PER * 2;  // fp16 entries
-  static constexpr int FIELDS = 8 / PER;           // fields per instruction (8 coordinates)
+  static constexpr int EB = PER * 2 * (SPLIT ? 2 : 1);    // bytes per entry
+  static constexpr int STRIDE = EB * COPIES;              // bytes between consecutive fields
+  static constexpr int BYTES = ENTRIES * STRIDE;
+  static constexpr int FIELDS = 8 / PER;                  // fields per instruction (8 coordinates)
+  __device__ static const uint8_t* lane_base(const uint8_t* tab, int lane) { return tab + (lane % COPIES) * EB; }
 };
+
+// Copies of a table within an LDS budget: conflict-free (128 / entry bytes) if it fits.
+template <int BITS, bool SPLIT, int BUDGET>
+constexpr int table_copies() {
+  constexpr int F = BITS == 3 ? 6 : 8;
+  constexpr int EB = (F / BITS) * 2 * (SPLIT ? 2 : 1);
+  constexpr int full = 128 / EB;
+  constexpr int fit = BUDGET / ((1 << F) * EB);
+  return full < fit ? full : (fit > 0 ? fit : 1);
+}
 
 // Bits [off, off + width) of a little-endian word array (off, width compile-time after unrolling).
 template <int N>
@@ -105,36 +123,38 @@ __device__ __forceinline__ uint32_t get_bits(const uint32_t (&w)[N], int off, in
 }
 
 // Eight consecutive BITS-bit indices starting at stream bit `off`, decoded to 8 fp16 values
-// (one MFMA operand) through the LDS table.
-template <int BITS, int N>
-__device__ __forceinline__ u32x4 decode8(const uint32_t (&w)[N], int off, const uint8_t* tab) {
+// (one MFMA operand) through the lane's copy of the table (tabl = DecodeTable::lane_base).
+template <int BITS, int COPIES, int N>
+__device__ __forceinline__ u32x4 decode8(const uint32_t (&w)[N], int off, const uint8_t* tabl) {
+  constexpr int S = DecodeTable<BITS, false, COPIES>::STRIDE;
   u32x4 out;
   if constexpr (BITS == 1) {
-    out = *reinterpret_cast<const u32x4*>(tab + get_bits(w, off, 8) * 16);
+    out = *reinterpret_cast<const u32x4*>(tabl + get_bits(w, off, 8) * S);
   } else if constexpr (BITS == 2) {
     const uint32_t f = get_bits(w, off, 16);
-    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + (f & 0xffu) * 8);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + (f >> 8) * 8);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(tabl + (f & 0xffu) * S);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(tabl + (f >> 8) * S);
     out = u32x4{a[0], a[1], b[0], b[1]};
   } else if constexpr (BITS == 3) {
     const uint32_t f = get_bits(w, off, 24);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tab + ((f >> (6 * j)) & 63u) * 4);
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tabl + ((f >> (6 * j)) & 63u) * S);
   } else {
     const uint32_t f = get_bits(w, off, 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tab + ((f >> (8 * j)) & 0xffu) * 4);
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(tabl + ((f >> (8 * j)) & 0xffu) * S);
   }
   return out;
 }
 
 // Split-precision table: each entry holds the PER fp16 centroids followed by the PER fp16
 // remainders c - fp16(c), so one read yields both B operands (hi, lo).
-template <int BITS>
+template <int BITS, int COPIES>
 __device__ __forceinline__ void build_table2(uint8_t* tab, const float* cent32) {
-  using DT = DecodeTable<BITS>;
-  for (int e = threadIdx.x; e < DT::ENTRIES; e += blockDim.x) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(tab + e * DT::PER * 4);
+  using DT = DecodeTable<BITS, true, COPIES>;
+  for (int i = threadIdx.x; i < DT::ENTRIES * COPIES; i += blockDim.x) {
+    const int e = i / COPIES;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(tab + i * DT::EB);
 #pragma unroll
     for (int j = 0; j < DT::PER; ++j) {
       const float c = cent32[(e >> (BITS * j)) & ((1 << BITS) - 1)];
@@ -146,16 +166,17 @@ __device__ __forceinline__ void build_table2(uint8_t* tab, const float* cent32) 
   }
 }
 
-template <int BITS, int N>
-__device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const uint8_t* tab, u32x4& hi, u32x4& lo) {
+template <int BITS, int COPIES, int N>
+__device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const uint8_t* tabl, u32x4& hi, u32x4& lo) {
+  constexpr int S = DecodeTable<BITS, true, COPIES>::STRIDE;
   if constexpr (BITS == 1) {
-    const uint8_t* e = tab + get_bits(w, off, 8) * 32;
+    const uint8_t* e = tabl + get_bits(w, off, 8) * S;
     hi = *reinterpret_cast<const u32x4*>(e);
     lo = *reinterpret_cast<const u32x4*>(e + 16);
   } else if constexpr (BITS == 2) {
     const uint32_t f = get_bits(w, off, 16);
-    const u32x4 a = *reinterpret_cast<const u32x4*>(tab + (f & 0xffu) * 16);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(tab + (f >> 8) * 16);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(tabl + (f & 0xffu) * S);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(tabl + (f >> 8) * S);
     hi = u32x4{a[0], a[1], b[0], b[1]};
     lo = u32x4{a[2], a[3], b[2], b[3]};
   } else {
@@ -163,7 +184,7 @@ __device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const
     constexpr int FW = BITS == 3 ? 6 : 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x2 e = *reinterpret_cast<const u32x2*>(tab + ((f >> (FW * j)) & ((1u << FW) - 1u)) * 8);
+      const u32x2 e = *reinterpret_cast<const u32x2*>(tabl + ((f >> (FW * j)) & ((1u << FW) - 1u)) * S);
       hi[j] = e[0];
       lo[j] = e[1];
     }
@@ -171,17 +192,18 @@ __device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const
 }
 
 // Keys: instruction s covers local coordinates 8 s .. 8 s + 7 of the lane's 32.
-template <int BITS>
-__device__ __forceinline__ u32x4 decode_keys(const uint32_t (&w)[BITS], int s, const uint8_t* tab) {
-  return decode8<BITS>(w, 8 * BITS * s, tab);
+template <int BITS, int COPIES>
+__device__ __forceinline__ u32x4 decode_keys(const uint32_t (&w)[BITS], int s, const uint8_t* tabl) {
+  return decode8<BITS, COPIES>(w, 8 * BITS * s, tabl);
 }
 
-// Builds the fp16 decode table of a codebook in LDS (cent: 16 fp16 centroids in LDS).
-template <int BITS>
+// Builds the replicated fp16 decode table of a codebook in LDS (cent: 16 fp16 centroids in LDS).
+template <int BITS, int COPIES>
 __device__ __forceinline__ void build_table(uint8_t* tab, const _Float16* cent) {
-  using DT = DecodeTable<BITS>;
-  for (int e = threadIdx.x; e < DT::ENTRIES; e += blockDim.x) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(tab + e * DT::PER * 2);
+  using DT = DecodeTable<BITS, false, COPIES>;
+  for (int i = threadIdx.x; i < DT::ENTRIES * COPIES; i += blockDim.x) {
+    const int e = i / COPIES;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(tab + i * DT::EB);
 #pragma unroll
     for (int j = 0; j < DT::PER; ++j)
       dst[j] = __builtin_bit_cast(uint16_t, cent[(e >> (BITS * j)) & ((1 << BITS) - 1)]);

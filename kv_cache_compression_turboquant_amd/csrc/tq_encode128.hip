@@ -38,34 +38,33 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
   constexpr int kWaves = EncShape<PROD>::kWaves;
   constexpr int H = 1 << (BITS - 1);      // centroids per sign
   __shared__ u32x4 lds[(RP + SP) * kFragU4];
-  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = frag_r[i];
-  if constexpr (PROD) {
-    for (int i = threadIdx.x; i < SP * kFragU4; i += blockDim.x) lds[RP * kFragU4 + i] = frag_s[i];
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const int g = lane >> 4;
   const int64_t ntiles = (n + 15) >> 4;
   const int64_t stride = (int64_t)gridDim.x * kWaves * NT;
-  int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * NT;
-  if (t0 >= ntiles) return;  // no barrier follows
+  int64_t tw = ((int64_t)blockIdx.x * kWaves + wave) * NT;
+
+  // Two tile groups in flight per wave, in two register sets used alternately (no copies, so
+  // each wait covers exactly the group about to be used).  The first loads are issued before
+  // the fragments are staged into LDS so that both latencies overlap.
+  // (Loads past the end read the clamped last row: unconditional loads keep the register sets
+  // fixed across iterations, where conditional ones would make the compiler copy them.)
+  RawTile<BF16IN> bufA[NT], bufB[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + t, nl, g, bufA[t]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + stride + t, nl, g, bufB[t]);
+  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = frag_r[i];
+  if constexpr (PROD) {
+    for (int i = threadIdx.x; i < SP * kFragU4; i += blockDim.x) lds[RP * kFragU4 + i] = frag_s[i];
+  }
+  __syncthreads();
+  if (tw >= ntiles) return;  // no barrier follows
 
   const float inv_post = 1.0f / post_scale;
-  RawTile<BF16IN> nxt[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, t0 + t, nl, g, nxt[t]);
-
-  for (; t0 < ntiles; t0 += stride) {
-    RawTile<BF16IN> cur[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
-    if (t0 + stride < ntiles) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, t0 + stride + t, nl, g, nxt[t]);
-    }
+  auto step = [&](RawTile<BF16IN> (&cur)[NT], const int64_t t0) {
 
     u32x4 bx[NT][4];      // bf16 x (or its hi part) for the 4 instructions
     u32x4 bxl[NT][4];     // bf16 low part of fp32 x
@@ -109,6 +108,9 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
       }
       ss[t] = acc2;
     }
+    // the raw registers are free again: fetch the group two strides ahead into them
+#pragma unroll
+    for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, t0 + 2 * stride + t, nl, g, cur[t]);
 
     // y^T blocks: acc[t][c] holds rows 32 G + 4 c + r of tile t
     f32x4 acc[NT][8];
@@ -248,6 +250,11 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
         }
       }
     }
+  };
+  for (; tw < ntiles; tw += 2 * stride) {
+    step(bufA, tw);
+    if (tw + stride >= ntiles) break;
+    step(bufB, tw + stride);
   }
 }
 

@@ -359,7 +359,9 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
     const u32x4* __restrict__ qf, const float* __restrict__ qnorm, int64_t nq, int d,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms, const uint32_t* __restrict__ qbits,
     const float* __restrict__ rnorms, int64_t m, CodebookArgs cb, float* __restrict__ out, int64_t ldo) {
-  using DT = DecodeTable<BITS>;
+  // the query operands take 128 KB of LDS: the decode table gets at most 8 KB
+  constexpr int TC = table_copies<BITS, false, 8192>();
+  using DT = DecodeTable<BITS, false, TC>;
   __shared__ u32x4 lds[2][4096];
   __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
   __shared__ _Float16 cent[16];
@@ -401,8 +403,9 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
 #pragma unroll
   for (int i = 0; i < 16; ++i) lds[0][i * 256 + threadIdx.x] = qsrc[i * 256 + threadIdx.x];
   __syncthreads();
-  build_table<BITS>(tab, cent);
+  build_table<BITS, TC>(tab, cent);
   __syncthreads();
+  const uint8_t* tabl = DT::lane_base(tab, lane);
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
       u32x4 bm[4], bz[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bm[j] = decode_keys<BITS>(kw[j], s, tab);
+        bm[j] = decode_keys<BITS, TC>(kw[j], s, tabl);
         bz[j] = sign8(zw[j], s, magp[j]);
       }
 #pragma unroll

@@ -45,59 +45,65 @@ __device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
 // ---------------------------------------------------------------------------------------
 constexpr int kQprepParts = 8;
 constexpr int kQprepThreads = 128 * kQprepParts;
+constexpr int kQprepHeads = 2;  // query heads per pass (bounds the live LDS operands per thread)
 
 __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
                                                             const float* __restrict__ rt,
                                                             const float* __restrict__ st,
                                                             uint16_t* __restrict__ ws,
                                                             float* __restrict__ kconst) {
-  __shared__ float qs[4][128];
-  __shared__ float part[2][kQprepParts][4][128];
-  __shared__ float sum[2][4][128];
+  constexpr int HG = kQprepHeads;
+  constexpr int KP = 128 / kQprepParts;
+  __shared__ float qs[HG][128];
+  __shared__ float part[2][kQprepParts][HG][128];
+  __shared__ float sum[2][HG][128];
   const int Hkv = Hq / ratio;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int h0 = kvh * ratio;
   const int j = threadIdx.x & 127, p = threadIdx.x >> 7;
   const int nmat = st ? 2 : 1;
-  for (int hc = 0; hc < ratio; hc += 4) {
-    const int nh = ratio - hc < 4 ? ratio - hc : 4;
+  for (int hc = 0; hc < ratio; hc += HG) {
+    const int nh = ratio - hc < HG ? ratio - hc : HG;
     __syncthreads();
-    if (threadIdx.x < 512) {
+    if (threadIdx.x < HG * 128) {
       const int hh = threadIdx.x >> 7;
       qs[hh][j] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
     }
     __syncthreads();
-    const int k0 = p * (128 / kQprepParts);
-    float rv[128 / kQprepParts], sv[128 / kQprepParts];
+    const int k0 = p * KP;
+    float ar[HG], as[HG];
 #pragma unroll
-    for (int k = 0; k < 128 / kQprepParts; ++k) rv[k] = rt[(k0 + k) * 128 + j];
-    if (st) {
+    for (int i = 0; i < HG; ++i) ar[i] = as[i] = 0.f;
+    {
+      float rv[KP];
 #pragma unroll
-      for (int k = 0; k < 128 / kQprepParts; ++k) sv[k] = st[(k0 + k) * 128 + j];
+      for (int k = 0; k < KP; ++k) rv[k] = rt[(k0 + k) * 128 + j];
+#pragma unroll
+      for (int k = 0; k < KP; ++k)
+#pragma unroll
+        for (int i = 0; i < HG; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
     }
-    float ar[4] = {0.f, 0.f, 0.f, 0.f}, as[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 128 / kQprepParts; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
     if (st) {
+      float sv[KP];
 #pragma unroll
-      for (int k = 0; k < 128 / kQprepParts; ++k)
+      for (int k = 0; k < KP; ++k) sv[k] = st[(k0 + k) * 128 + j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) as[i] = fmaf(sv[k], qs[i][k0 + k], as[i]);
+      for (int k = 0; k < KP; ++k)
+#pragma unroll
+        for (int i = 0; i < HG; ++i) as[i] = fmaf(sv[k], qs[i][k0 + k], as[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < HG; ++i) {
       part[0][p][i][j] = ar[i];
       part[1][p][i][j] = as[i];
     }
     __syncthreads();
-    // threads (m, j), m < nmat: the full sum of matrix m for the four heads
+    // threads (m, j), m < nmat: the full sum of matrix m for the heads of this pass
     if (threadIdx.x < 128 * nmat) {
       const int m = threadIdx.x >> 7;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < HG; ++i) {
         float a = 0.f;
 #pragma unroll
         for (int pp = 0; pp < kQprepParts; ++pp) a += part[m][pp][i][j];
@@ -110,7 +116,6 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
       for (int i = 0; i < nh; ++i) {
         uint16_t* o = ws + ((int64_t)b * Hq + h0 + hc + i) * 4 * 128;
         float v;
-        int mp = 0;
         if (m == 0) {
           v = sum[0][i][j];
         } else {
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
           // 32 G + c(s, e), scaled by 1 / beta
           const int G = j >> 5, s8 = (j & 31) >> 3, e = j & 7;
           const int c = 32 * G + sign_slot_coord(s8, e);
-          mp = sign_slot_mpos(4 * s8 + (e >> 1));
+          const int mp = sign_slot_mpos(4 * s8 + (e >> 1));
           v = sum[1][i][c] / kSignBeta[mp];
         }
         const _Float16 vh = (_Float16)v;
@@ -148,7 +153,8 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
 // (16 rows: rot hi / rot lo / sketch hi / sketch lo for 4 heads), B = decoded keys (columns =
 // 16 keys), so lane (n, G) receives the four partial sums of key n for slot group G.  Keys are
 // decoded from whole packed words through small LDS tables that map a field of F bits to
-// F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass.
+// F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass and
+// replicated so that the lanes of one LDS cycle read distinct banks.
 // ---------------------------------------------------------------------------------------
 constexpr int kScoreWaves = 4;
 constexpr int kScoreBatch = 8;
@@ -185,20 +191,22 @@ __device__ __forceinline__ void load_key_tile(const uint32_t* __restrict__ idx, 
 }
 
 template <int BITS, bool PROD>
-__global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
+__global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
     const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
     float* __restrict__ scores) {
-  using DT = DecodeTable<BITS>;
+  constexpr int TC = table_copies<BITS, false, 32768>();
+  using DT = DecodeTable<BITS, false, TC>;
   __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
   __shared__ _Float16 cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
   __syncthreads();
-  build_table<BITS>(tab, cent);
+  build_table<BITS, TC>(tab, cent);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
+  const uint8_t* tabl = DT::lane_base(tab, lane);
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const int g = lane >> 4;
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_scores_d128(
     const float gam = cur.gam;
     u32x4 bk[4], bz[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS>(cur.w, s, tab);
+    for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS, TC>(cur.w, s, tabl);
     if constexpr (PROD) sign_operand(cur.zw, bz);
     for (int hg = 0; hg < groups; ++hg) {
       u32x4 am[4], aq[4];
