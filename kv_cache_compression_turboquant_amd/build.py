@@ -24,25 +24,28 @@ def hipcc():
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose=False):
-    """Compiles every source into libtq.so for gfx950; raises on failure."""
+def build(verbose=False, defines=(), out=None, tmp=None):
+    """Compiles every source into libtq.so for gfx950; raises on failure.  `defines` (NAME=VALUE)
+    override the kernels' compile-time tuning defaults; `out` / `tmp` redirect the library and
+    the object directory."""
     objs = []
-    tmp = os.path.join(PKG, "_build")
+    out = out or LIB
+    tmp = tmp or os.path.join(PKG, "_build")
     os.makedirs(tmp, exist_ok=True)
     procs = []
     for src in SOURCES:
         obj = os.path.join(tmp, src + ".o")
         objs.append(obj)
         cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-c",
-               "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS,
+               "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *["-D" + d for d in defines],
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         # the host pass does not know the device feature flag: drop that notice
         lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
         if lines and (verbose or p.returncode != 0):
@@ -51,13 +54,13 @@ def build(verbose=False):
             failed.append(src)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp_lib = LIB + ".tmp"
+    tmp_lib = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib, *objs, "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp_lib, LIB)
-    return LIB
+    os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -186,7 +186,14 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 // The block merges its waves and writes (max, sum, acc[128]) per head; k_attn_combine merges the
 // splits and applies R_V^T.
 // ---------------------------------------------------------------------------------------
-constexpr int kAttnStepsPerBlock = 64;
+// Launch shape: each block takes `spb` 32-token steps of one (batch, kv head); spb is chosen at
+// launch so the grid is a whole number of rounds of resident blocks, and never below
+// kAttnMinSteps (which bounds the number of splits, hence the workspace).
+#ifndef TQ_ATTN_ROUNDS
+#define TQ_ATTN_ROUNDS 1
+#endif
+constexpr int kAttnMinSteps = 16;
+constexpr int kAttnRounds = TQ_ATTN_ROUNDS;
 constexpr int kAttnPart = 130;  // max, sum, 128 accumulators
 
 // One 32-token step of a wave: the lane's key words and norms for both 16-token tiles, the
@@ -220,7 +227,7 @@ __device__ __forceinline__ void load_attn_step(const uint32_t* __restrict__ kidx
 
 template <int KB, int VB>
 __global__ __launch_bounds__(256) void k_attn_d128(
-    const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit,
+    const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
@@ -256,8 +263,8 @@ __global__ __launch_bounds__(256) void k_attn_d128(
   const int ratio = Hq / Hkv;
   const int64_t row0 = (int64_t)bh * T, rowE = row0 + T;
   const int64_t blk_first = row0 >> 5, blk_end = ((rowE - 1) >> 5) + 1;
-  const int64_t bb = blk_first + (int64_t)blockIdx.x * kAttnStepsPerBlock;
-  const int64_t be = bb + kAttnStepsPerBlock < blk_end ? bb + kAttnStepsPerBlock : blk_end;
+  const int64_t bb = blk_first + (int64_t)blockIdx.x * spb;
+  const int64_t be = bb + spb < blk_end ? bb + spb : blk_end;
   const int64_t cnt = be > bb ? be - bb : 0;
   const int64_t per = (cnt + 3) / 4;
   const int64_t wb = bb + wave * per;
@@ -469,9 +476,21 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const 
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
   hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st);
   if (e != hipSuccess) return e;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_d128<KB, VB>, 256, 0) != hipSuccess || v <= 0) v = 2;
+    per_cu = v;
+  }
+  const int64_t seqs = (int64_t)B * Hkv;
   const int64_t steps = T / 32 + 2;
-  const int nsplit = (int)((steps + kAttnStepsPerBlock - 1) / kAttnStepsPerBlock);
-  hipLaunchKernelGGL((k_attn_d128<KB, VB>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit,
+  const int64_t target = (int64_t)num_cus() * per_cu * kAttnRounds;
+  const int64_t want = target / seqs > 0 ? target / seqs : 1;
+  int64_t spb = (steps + want - 1) / want;
+  spb = (spb + 3) / 4 * 4;
+  if (spb < kAttnMinSteps) spb = kAttnMinSteps;
+  const int nsplit = (int)((steps + spb - 1) / spb);
+  hipLaunchKernelGGL((k_attn_d128<KB, VB>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit, (int)spb,
                      K->idx, K->norms, V->idx, V->norms, K->n, cbk, cbv, scale, part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -517,7 +536,7 @@ size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d) {
   (void)d;
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   const int64_t steps = T / 32 + 2;
-  const int64_t nsplit = (steps + kAttnStepsPerBlock - 1) / kAttnStepsPerBlock;
+  const int64_t nsplit = (steps + kAttnMinSteps - 1) / kAttnMinSteps;  // the most splits a launch uses
   return qbytes + (size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float);
 }
 

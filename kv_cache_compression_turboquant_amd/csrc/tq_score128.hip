@@ -156,8 +156,16 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
 // F / BITS fp16 centroids (F = 6 for 3 bits, else 8), built by each block in one pass and
 // replicated so that the lanes of one LDS cycle read distinct banks.
 // ---------------------------------------------------------------------------------------
+// Launch shape (tuning defaults; overridable at build time).
+#ifndef TQ_SCORE_BATCH
+#define TQ_SCORE_BATCH 4
+#endif
+#ifndef TQ_SCORE_ROUNDS
+#define TQ_SCORE_ROUNDS 1
+#endif
 constexpr int kScoreWaves = 4;
-constexpr int kScoreBatch = 8;
+constexpr int kScoreBatch = TQ_SCORE_BATCH;   // key tiles loaded before any of them is scored
+constexpr int kScoreRounds = TQ_SCORE_ROUNDS; // target grid = this many rounds of resident blocks
 
 template <int BITS, bool PROD>
 struct KeyTile {
@@ -315,13 +323,22 @@ hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tiles = (T + 15) / 16;
-  // enough blocks to fill the device about four times over
-  const int64_t target = (int64_t)num_cus() * 4;
+  // Size the grid as a whole number of rounds of resident blocks (a partial last round would
+  // leave most of the device idle): blocks resident per CU come from the occupancy calculator.
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_scores_d128<BITS, PROD>, kScoreWaves * 64, 0) != hipSuccess ||
+        v <= 0)
+      v = 2;
+    per_cu = v;
+  }
+  const int64_t target = (int64_t)num_cus() * per_cu * kScoreRounds;
   const int64_t seqs = (int64_t)B * Hkv;
   int64_t tpw = (tiles * seqs + target * kScoreWaves - 1) / (target * kScoreWaves);
   tpw = (tpw + kScoreBatch - 1) / kScoreBatch * kScoreBatch;
   if (tpw < kScoreBatch) tpw = kScoreBatch;
-  if (tpw > 64) tpw = 64;
+  if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
   hipLaunchKernelGGL((k_scores_d128<BITS, PROD>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
                      0, st, qws, kconst, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
