@@ -15,8 +15,12 @@ LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip",
            "tq_general.hip"]
 
-# Packed FP32 VALU instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed FP32 VALU instructions are disabled for all device code.  MFMA results go to ordinary
+# VGPRs rather than accumulation registers: the kernels post-process their accumulators with
+# VALU code, and the AGPR form costs a copy in each direction per use (and, for the decode
+# attention, one wave per SIMD of occupancy).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def hipcc():

@@ -166,27 +166,34 @@ __device__ __forceinline__ void build_table2(uint8_t* tab, const float* cent32) 
   }
 }
 
+// (hi and lo are read separately, each straight into its operand registers: reading an entry
+// whole and splitting it costs register moves.)
 template <int BITS, int COPIES, int N>
 __device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const uint8_t* tabl, u32x4& hi, u32x4& lo) {
   constexpr int S = DecodeTable<BITS, true, COPIES>::STRIDE;
+  constexpr int H = DecodeTable<BITS, true, COPIES>::PER * 2;  // bytes of an entry's hi part
   if constexpr (BITS == 1) {
     const uint8_t* e = tabl + get_bits(w, off, 8) * S;
     hi = *reinterpret_cast<const u32x4*>(e);
-    lo = *reinterpret_cast<const u32x4*>(e + 16);
+    lo = *reinterpret_cast<const u32x4*>(e + H);
   } else if constexpr (BITS == 2) {
     const uint32_t f = get_bits(w, off, 16);
-    const u32x4 a = *reinterpret_cast<const u32x4*>(tabl + (f & 0xffu) * S);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(tabl + (f >> 8) * S);
-    hi = u32x4{a[0], a[1], b[0], b[1]};
-    lo = u32x4{a[2], a[3], b[2], b[3]};
+    const uint8_t* ea = tabl + (f & 0xffu) * S;
+    const uint8_t* eb = tabl + (f >> 8) * S;
+    const u32x2 ha = *reinterpret_cast<const u32x2*>(ea);
+    const u32x2 hb = *reinterpret_cast<const u32x2*>(eb);
+    const u32x2 la = *reinterpret_cast<const u32x2*>(ea + H);
+    const u32x2 lb = *reinterpret_cast<const u32x2*>(eb + H);
+    hi = u32x4{ha[0], ha[1], hb[0], hb[1]};
+    lo = u32x4{la[0], la[1], lb[0], lb[1]};
   } else {
     const uint32_t f = get_bits(w, off, BITS == 3 ? 24 : 32);
     constexpr int FW = BITS == 3 ? 6 : 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x2 e = *reinterpret_cast<const u32x2*>(tabl + ((f >> (FW * j)) & ((1u << FW) - 1u)) * S);
-      hi[j] = e[0];
-      lo[j] = e[1];
+      const uint8_t* e = tabl + ((f >> (FW * j)) & ((1u << FW) - 1u)) * S;
+      hi[j] = *reinterpret_cast<const uint32_t*>(e);
+      lo[j] = *reinterpret_cast<const uint32_t*>(e + H);
     }
   }
 }
