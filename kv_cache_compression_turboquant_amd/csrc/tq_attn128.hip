@@ -192,7 +192,11 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 #ifndef TQ_ATTN_ROUNDS
 #define TQ_ATTN_ROUNDS 1
 #endif
+#ifndef TQ_ATTN_BATCH
+#define TQ_ATTN_BATCH 2
+#endif
 constexpr int kAttnMinSteps = 16;
+constexpr int kAttnBatch = TQ_ATTN_BATCH;  // 32-token steps loaded together
 constexpr int kAttnRounds = TQ_ATTN_ROUNDS;
 constexpr int kAttnPart = 130;  // max, sum, 128 accumulators
 
@@ -226,7 +230,7 @@ __device__ __forceinline__ void load_attn_step(const uint32_t* __restrict__ kidx
 }
 
 template <int KB, int VB>
-__global__ __launch_bounds__(256) void k_attn_d128(
+__global__ __launch_bounds__(256, 3) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
@@ -292,11 +296,7 @@ __global__ __launch_bounds__(256) void k_attn_d128(
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads of the next 32-token step are issued before the current step is consumed.
-  AttnStep<KB, VB> cur, nxt;
-  if (wb < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, wb, nl, g, cur);
-  for (int64_t blk = wb; blk < we; ++blk) {
-    if (blk + 1 < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, blk + 1, nl, g, nxt);
+  auto step = [&](const AttnStep<KB, VB>& cur, const int64_t blk) {
     float lg[2], svv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -368,7 +368,18 @@ __global__ __launch_bounds__(256) void k_attn_d128(
     for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB, VC>(cur.vw, 8 * VB * c, vtabl), acc[c]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    cur = nxt;
+  };
+  // Batches of kAttnBatch steps: all their loads are issued before the first step is consumed
+  // (straight-line code, so each wait is exact and no registers are copied between steps).
+  for (int64_t b0 = wb; b0 < we; b0 += kAttnBatch) {
+    AttnStep<KB, VB> st[kAttnBatch];
+#pragma unroll
+    for (int u = 0; u < kAttnBatch; ++u)
+      if (b0 + u < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, b0 + u, nl, g, st[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kAttnBatch; ++u)
+      if (b0 + u < we) step(st[u], b0 + u);
   }
 
   // wave totals: sum over the 16 keys lanes; hi + lo accumulator rows
