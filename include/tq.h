@@ -200,6 +200,19 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
                     void* ws_dev, size_t ws_bytes, void* stream);
 
+/* The two stages of tq_scores, for callers that overlap the query prologue with other work (for
+ * instance the encode of the keys being appended) on another stream.
+ * tq_prepare_queries: q_rot = R q (fp16 hi/lo) and, when qjl is non-NULL, the QJL sketch S q
+ * with its per-head constants, for q_dev [B, Hq, d] fp32, written into ws_dev (at least
+ * tq_scores_workspace(B, Hq, d) bytes) ([SB] third layer: the query is rotated once).
+ * tq_scores_prepared: the scores of tq_scores from such a workspace.  The workspace must have been
+ * prepared with the same B, Hq, Hkv and rotation as the keys, and with the keys' qjl handle when K
+ * is prod mode (the device contents are not checked).  Errors as for tq_scores. */
+tq_status tq_prepare_queries(const float* q_dev, int B, int Hq, int Hkv, tq_rotation_t rot, tq_qjl_t qjl,
+                             void* ws_dev, size_t ws_bytes, void* stream);
+tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq, int Hkv, int64_t T,
+                             const tq_packed* K, tq_codebook_t cb, float* scores_dev, void* stream);
+
 /* Workspace bytes tq_decode_attn needs (query prologue plus per-split softmax partials). */
 size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d);
 /* Fused decode attention over compressed K and V ([RQ] chapter 1: softmax(q K^T / sqrt(d)) V;

@@ -18,6 +18,7 @@ __all__ = [
     "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
+    "prepare_queries", "scores_prepared",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -248,6 +249,29 @@ def scores(q, K, Hkv, cb, rot, qjl=None, out=None, ws=None):
     check(lib().tq_scores(_dptr(q), B, Hq, Hkv, T, ctypes.byref(desc), cb.ptr, rot.ptr,
                           qjl.ptr if qjl is not None else None, _dptr(out), _dptr(ws),
                           ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def prepare_queries(q, Hkv, rot, qjl=None, ws=None):
+    """Query prologue of the score path into a workspace (returned): q [B, Hq, d] fp32."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if ws is None:
+        ws = torch.empty((max(scores_workspace(B, Hq, d), 1),), dtype=torch.uint8, device=q.device)
+    check(lib().tq_prepare_queries(_dptr(q), B, Hq, Hkv, rot.ptr, qjl.ptr if qjl is not None else None, _dptr(ws),
+                                   ws.numel() * ws.element_size(), _stream()))
+    return ws
+
+
+def scores_prepared(ws, B, Hq, K, Hkv, cb, out=None):
+    """Scores [B, Hq, T] from a workspace filled by prepare_queries."""
+    torch = _torch()
+    T = K.n // max(B * Hkv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=ws.device)
+    desc = K.descriptor()
+    check(lib().tq_scores_prepared(_dptr(ws), ws.numel() * ws.element_size(), B, Hq, Hkv, T, ctypes.byref(desc),
+                                   cb.ptr, _dptr(out), _stream()))
     return out
 
 

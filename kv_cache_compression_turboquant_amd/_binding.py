@@ -72,6 +72,8 @@ SIGNATURES = {
     "tq_quantize_rotated": (_I, [_P, _I64, _I, _P, _P, _P]),
     "tq_decode": (_I, [ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),
     "tq_scores_workspace": (_SZ, [_I, _I, _I]),
+    "tq_prepare_queries": (_I, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "tq_scores_prepared": (_I, [_P, _SZ, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P]),
     "tq_scores": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _SZ, _P]),
 }
 

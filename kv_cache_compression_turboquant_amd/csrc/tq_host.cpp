@@ -737,32 +737,78 @@ size_t tq_scores_workspace(int B, int Hq, int d) {
   return tq::scores_workspace_bytes(B, Hq, d);
 }
 
-tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
-                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
-                    void* ws_dev, size_t ws_bytes, void* stream) {
-  static const char* fn = "tq_scores";
-  if (!K || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
-  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+// Shape rules shared by the score entry points.
+static tq_status check_score_heads(int B, int Hq, int Hkv, const char* fn) {
+  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
   const int ratio = Hq / Hkv;
   if (ratio > 4 && ratio % 4 != 0) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d must be <= 4 or a multiple of 4", fn, ratio);
   if (ratio > 64) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d above 64", fn, ratio);
   if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv=%lld above 65535", fn, (long long)B * Hkv);
-  const int d = rot->d;
+  return TQ_OK;
+}
+
+static tq_status check_score_keys(int B, int Hkv, int64_t T, const tq_packed* K, tq_codebook_t cb, int d,
+                                  const char* fn) {
+  if (T < 0) return fail(TQ_EINVAL, "%s: negative T", fn);
   tq_status st = check_packed(K, d, cb->b, K->mode, fn);
   if (st != TQ_OK) return st;
   if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: keys must use the ROWS layout", fn);
-  if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, rotation d=%d", fn, cb->d, d);
+  if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, keys d=%d", fn, cb->d, d);
   if (K->n != (int64_t)B * Hkv * T) return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*T=%lld", fn, (long long)K->n, (long long)B * Hkv * T);
+  if (K->mode != TQ_MODE_PROD && K->mode != TQ_MODE_MSE) return fail(TQ_EINVAL, "%s: bad mode", fn);
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  return TQ_OK;
+}
+
+tq_status tq_prepare_queries(const float* q_dev, int B, int Hq, int Hkv, tq_rotation_t rot, tq_qjl_t qjl,
+                             void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_prepare_queries";
+  if (!rot) return fail(TQ_EINVAL, "%s: null rotation", fn);
+  tq_status st = check_score_heads(B, Hq, Hkv, fn);
+  if (st != TQ_OK) return st;
+  const int d = rot->d;
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if (qjl && qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
+  if ((int64_t)B * Hq == 0) return ok();
+  if (!q_dev) return fail(TQ_EINVAL, "%s: null q", fn);
+  const size_t need = tq::scores_workspace_bytes(B, Hq, d);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_prepare_queries(q_dev, B, Hq, Hkv, rot, qjl, ws_dev, as_stream(stream)), fn);
+}
+
+tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq, int Hkv, int64_t T,
+                             const tq_packed* K, tq_codebook_t cb, float* scores_dev, void* stream) {
+  static const char* fn = "tq_scores_prepared";
+  if (!K || !cb) return fail(TQ_EINVAL, "%s: null argument", fn);
+  tq_status st = check_score_heads(B, Hq, Hkv, fn);
+  if (st != TQ_OK) return st;
+  st = check_score_keys(B, Hkv, T, K, cb, K->d, fn);
+  if (st != TQ_OK) return st;
+  if ((int64_t)B * Hq * T == 0) return ok();
+  if (!scores_dev) return fail(TQ_EINVAL, "%s: null scores", fn);
+  const size_t need = tq::scores_workspace_bytes(B, Hq, K->d);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_scores_prepared(B, Hq, Hkv, T, K, cb->args, scores_dev, ws_dev, as_stream(stream)),
+                      fn);
+}
+
+tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
+                    void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_scores";
+  if (!K || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
+  tq_status st = check_score_heads(B, Hq, Hkv, fn);
+  if (st != TQ_OK) return st;
+  const int d = rot->d;
+  st = check_score_keys(B, Hkv, T, K, cb, d, fn);
+  if (st != TQ_OK) return st;
   if (K->mode == TQ_MODE_PROD) {
     if (!qjl) return fail(TQ_EINVAL, "%s: prod keys need the qjl handle", fn);
     if (qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
-  } else if (K->mode == TQ_MODE_MSE) {
-    if (qjl) return fail(TQ_EINVAL, "%s: qjl handle given for MSE keys", fn);
-  } else {
-    return fail(TQ_EINVAL, "%s: bad mode", fn);
+  } else if (qjl) {
+    return fail(TQ_EINVAL, "%s: qjl handle given for MSE keys", fn);
   }
-  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
   if ((int64_t)B * Hq * T == 0) return ok();
   if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
   size_t need = tq::scores_workspace_bytes(B, Hq, d);

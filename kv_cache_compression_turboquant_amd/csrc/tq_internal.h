@@ -100,6 +100,11 @@ hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, cons
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st);
 size_t scores_workspace_bytes(int B, int Hq, int d);
+// The two stages of launch_scores: the query prologue into ws, then the score kernel from ws.
+hipError_t launch_prepare_queries(const float* q, int B, int Hq, int Hkv, const tq_rotation_s* rot,
+                                  const tq_qjl_s* qjl, void* ws, hipStream_t st);
+hipError_t launch_scores_prepared(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+                                  float* scores, const void* ws, hipStream_t st);
 // General d (multiple of 128 in [256, 4096]), rows layout.  y_out set: rotated unit
 // coordinates and norms only.  Prod (qjl set) stages the residual through ws in chunks.
 hipError_t launch_encode_general(const void* x, bool bf16, int64_t n, int d, const tq_rotation_s* rot,

@@ -311,17 +311,12 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
 }
 
 template <int BITS, bool PROD>
-hipError_t scores_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
-                         const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
-                         float* scores, void* ws, hipStream_t st) {
+hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+                         float* scores, const void* ws, hipStream_t st) {
   const int ratio = Hq / Hkv;
-  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const uint16_t* qws = static_cast<const uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
-  float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, ratio, rot->rt32_dev,
-                     PROD ? qjl->st32_dev : nullptr, qws, kconst);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const float* kconst = reinterpret_cast<const float*>(static_cast<const char*>(ws) + qbytes);
   const int64_t tiles = (T + 15) / 16;
   // Size the grid as a whole number of rounds of resident blocks (a partial last round would
   // leave most of the device idle): blocks resident per CU come from the occupancy calculator.
@@ -361,21 +356,36 @@ size_t scores_workspace_bytes(int B, int Hq, int d) {
   return qbytes + (size_t)B * Hq * sizeof(float);
 }
 
+hipError_t launch_prepare_queries(const float* q, int B, int Hq, int Hkv, const tq_rotation_s* rot,
+                                  const tq_qjl_s* qjl, void* ws, hipStream_t st) {
+  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
+  return launch_qprep128(q, B, Hq, Hkv, rot->rt32_dev, qjl ? qjl->st32_dev : nullptr, qws, kconst, st);
+}
+
+hipError_t launch_scores_prepared(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+                                  float* scores, const void* ws, hipStream_t st) {
+  const bool prod = K->mode == TQ_MODE_PROD;
+  switch (cb.bits) {
+    case 1: return prod ? scores_launch<1, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
+                        : scores_launch<1, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+    case 2: return prod ? scores_launch<2, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
+                        : scores_launch<2, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+    case 3: return prod ? scores_launch<3, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
+                        : scores_launch<3, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+    case 4: return prod ? scores_launch<4, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
+                        : scores_launch<4, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                          const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                          float* scores, void* ws, hipStream_t st) {
-  const bool prod = K->mode == TQ_MODE_PROD;
-  switch (cb.bits) {
-    case 1: return prod ? scores_launch<1, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
-                        : scores_launch<1, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
-    case 2: return prod ? scores_launch<2, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
-                        : scores_launch<2, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
-    case 3: return prod ? scores_launch<3, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
-                        : scores_launch<3, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
-    case 4: return prod ? scores_launch<4, true>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st)
-                        : scores_launch<4, false>(q, B, Hq, Hkv, T, K, cb, rot, qjl, scores, ws, st);
-  }
-  return hipErrorInvalidValue;
+  hipError_t e = launch_prepare_queries(q, B, Hq, Hkv, rot, K->mode == TQ_MODE_PROD ? qjl : nullptr, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_scores_prepared(B, Hq, Hkv, T, K, cb, scores, ws, st);
 }
 
 }  // namespace tq

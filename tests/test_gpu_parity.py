@@ -251,3 +251,26 @@ def test_error_codes_on_device(dev, rot_dense):
     with pytest.raises(tq.TQError) as ei:
         tq.scores(torch.zeros((1, 4, 128), device=dev), p, 1, cb3, rot_dense, ws=ws)
     assert ei.value.status == 4
+
+
+@pytest.mark.parametrize("mode,b", [("mse", 3), ("prod", 4)])
+def test_scores_prepared_matches_scores(dev, rot_dense, mode, b):
+    """The two stages (query prologue on a side stream, then the score kernel) give the very
+    scores of tq_scores: same kernels, same inputs."""
+    stage = b - 1 if mode == "prod" else b
+    qjl = tq.make_qjl(128, 2, rot_dense) if mode == "prod" else None
+    cb = tq.codebook(128, stage)
+    x, xt = _keys(700, hkv=4, B=2)
+    p = tq.encode(xt.to(dev), b, mode, cb, rot_dense, qjl)
+    q = torch.from_numpy(wl.gaussian((2, 16, 128), 12)).to(dev)
+    ref = tq.scores(q, p, 4, cb, rot_dense, qjl)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ws = tq.prepare_queries(q, 4, rot_dense, qjl)
+    torch.cuda.current_stream().wait_stream(side)
+    got = tq.scores_prepared(ws, 2, 16, p, 4, cb)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    with pytest.raises(tq.TQError):
+        tq.scores_prepared(ws[:16], 2, 16, p, 4, cb)
