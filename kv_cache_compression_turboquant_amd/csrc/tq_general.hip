@@ -351,17 +351,22 @@ __device__ __forceinline__ u32x4 sign8(uint32_t z, int s, uint32_t magpair) {
 
 // Scores of 128 queries (block x) against 256 database vectors (block y) of one chunk:
 // out[q][j] = ||q|| s_j (<q_rot, C[idx_j]> + (gamma_j / s_j) sqrt(pi/2)/d <q_s, z_j>) with unit q.
-// One block per CU with the query operands double-buffered in LDS (2 x 64 KB): the loads of
-// contraction chunk kc + 1 (query fragments and the packed words) are in flight while chunk
-// kc's MFMAs run, and the accumulators (8 query tiles x 4 key tiles per wave) stay in registers.
+// Eight waves per block, two per SIMD: wave w scores key group w % 4 (64 vectors, decoded by the
+// wave itself) against query half w / 4 (4 query tiles), so each wave holds 16 accumulator tiles.
+// The query operands are double-buffered in LDS (2 x 64 KB): the loads of contraction chunk
+// kc + 1 are in flight while chunk kc's MFMAs run.
+constexpr int kSearchWaves = 8;
+constexpr int kSearchThreads = kSearchWaves * 64;
+
 template <int BITS>
-__global__ __launch_bounds__(256, 1) void k_search_scores(
+__global__ __launch_bounds__(kSearchThreads, 1) void k_search_scores(
     const u32x4* __restrict__ qf, const float* __restrict__ qnorm, int64_t nq, int d,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms, const uint32_t* __restrict__ qbits,
     const float* __restrict__ rnorms, int64_t m, CodebookArgs cb, float* __restrict__ out, int64_t ldo) {
   // the query operands take 128 KB of LDS: the decode table gets at most 8 KB
   constexpr int TC = table_copies<BITS, false, 8192>();
   using DT = DecodeTable<BITS, false, TC>;
+  constexpr int PER = 4096 / kSearchThreads;  // staging loads per thread per chunk
   __shared__ u32x4 lds[2][4096];
   __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
   __shared__ _Float16 cent[16];
@@ -370,64 +375,57 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
   const int W = d * BITS / 32;
   const int qb = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = wave & 3, qh = wave >> 2;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t key0 = (int64_t)blockIdx.y * kSearchKeys + wave * 64;
+  const int64_t key0 = (int64_t)blockIdx.y * kSearchKeys + kg * 64;
   const float kz = 1.2533141373155002512f / (float)d / kSketchScale;  // sqrt(pi/2) / d, rescaled
 
   float sk[4];
   uint32_t magp[4];
-  const uint32_t* kp[4];
-  const uint32_t* zp[4];
+  uint32_t krow[4];  // row of each key tile's vector within the chunk (a chunk holds < 2^32 words)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int64_t r = key0 + 16 * j + nl;
     if (r >= m) r = m - 1;
-    kp[j] = idx + r * W + BITS * g;
-    zp[j] = qbits + r * (d >> 5) + g;
+    krow[j] = (uint32_t)r;
     const float s = norms[r];
     sk[j] = s;
     const float zf = s > 0.f ? rnorms[r] / s * kz : 0.f;
     const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)zf);
     magp[j] = h | (h << 16);
   }
+  const uint32_t* idxg = idx + BITS * g;
+  const uint32_t* zg = qbits + g;
   const u32x4* qsrc = qf + (size_t)qb * nb * 4096;
-
-  // chunk 0
-  uint32_t kw[4][BITS], zw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int b = 0; b < BITS; ++b) kw[j][b] = kp[j][b];
-    zw[j] = zp[j][0];
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) lds[0][i * 256 + threadIdx.x] = qsrc[i * 256 + threadIdx.x];
+  for (int i = 0; i < PER; ++i) lds[0][i * kSearchThreads + threadIdx.x] = qsrc[i * kSearchThreads + threadIdx.x];
   __syncthreads();
   build_table<BITS, TC>(tab, cent);
   __syncthreads();
   const uint8_t* tabl = DT::lane_base(tab, lane);
 
-  f32x4 acc[8][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int qt = 0; qt < 8; ++qt)
+  for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int kc = 0; kc < nb; ++kc) {
     const int cur = kc & 1;
     const bool more = kc + 1 < nb;
-    u32x4 stage[16];
-    uint32_t kwn[4][BITS], zwn[4];
+    uint32_t kw[4][BITS], zw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t* w = idxg + (size_t)krow[j] * W + 4 * BITS * kc;
+#pragma unroll
+      for (int b = 0; b < BITS; ++b) kw[j][b] = w[b];
+      zw[j] = zg[(size_t)krow[j] * (d >> 5) + 4 * kc];
+    }
+    u32x4 stage[PER];
     if (more) {
       const u32x4* src = qsrc + (size_t)(kc + 1) * 4096;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) stage[i] = src[i * 256 + threadIdx.x];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int b = 0; b < BITS; ++b) kwn[j][b] = kp[j][4 * BITS * (kc + 1) + b];
-        zwn[j] = zp[j][4 * (kc + 1)];
-      }
+      for (int i = 0; i < PER; ++i) stage[i] = src[i * kSearchThreads + threadIdx.x];
     }
     const u32x4* lq = lds[cur];
 #pragma unroll
@@ -439,25 +437,22 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
         bz[j] = sign8(zw[j], s, magp[j]);
       }
 #pragma unroll
-      for (int qt = 0; qt < 8; ++qt) {
+      for (int t = 0; t < 4; ++t) {
+        const int qt = 4 * qh + t;
         const u32x4 ar = lq[(qt * 4 + s) * 64 + lane];
         const u32x4 az = lq[((8 + qt) * 4 + s) * 64 + lane];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc[qt][j] = mfma_f16(ar, bm[j], acc[qt][j]);
-          acc[qt][j] = mfma_f16(az, bz[j], acc[qt][j]);
+          acc[t][j] = mfma_f16(ar, bm[j], acc[t][j]);
+          acc[t][j] = mfma_f16(az, bz[j], acc[t][j]);
         }
       }
+      // one contraction slice at a time (the other wave on the SIMD covers the latencies)
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lds[cur ^ 1][i * 256 + threadIdx.x] = stage[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int b = 0; b < BITS; ++b) kw[j][b] = kwn[j][b];
-        zw[j] = zwn[j];
-      }
+      for (int i = 0; i < PER; ++i) lds[cur ^ 1][i * kSearchThreads + threadIdx.x] = stage[i];
     }
     __syncthreads();
   }
@@ -466,11 +461,11 @@ __global__ __launch_bounds__(256, 1) void k_search_scores(
     const int64_t key = key0 + 16 * j + nl;
     if (key >= m) continue;
 #pragma unroll
-    for (int qt = 0; qt < 8; ++qt)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t q = (int64_t)qb * 128 + 16 * qt + 4 * g + r;
-        if (q < nq) out[q * ldo + key] = qnorm[q] * sk[j] * acc[qt][j][r];
+        const int64_t q = (int64_t)qb * 128 + 16 * (4 * qh + t) + 4 * g + r;
+        if (q < nq) out[q * ldo + key] = qnorm[q] * sk[j] * acc[t][j][r];
       }
   }
 }
@@ -610,7 +605,7 @@ hipError_t search_scores_launch(const u32x4* qf, const float* qnorm, int64_t nq,
                                 hipStream_t st) {
   const int W = d * BITS / 32;
   const dim3 grid((unsigned)((nq + 127) / 128), (unsigned)((m + kSearchKeys - 1) / kSearchKeys));
-  hipLaunchKernelGGL((k_search_scores<BITS>), grid, dim3(256), 0, st, qf, qnorm, nq, d, db->idx + base * W,
+  hipLaunchKernelGGL((k_search_scores<BITS>), grid, dim3(kSearchThreads), 0, st, qf, qnorm, nq, d, db->idx + base * W,
                      db->norms + base, db->qjl + base * (d / 32), db->rnorms + base, m, cb, out, ldo);
   return hipGetLastError();
 }
