@@ -23,15 +23,24 @@ __host__ __device__ __forceinline__ int sign_slot_coord(int s, int e) { return (
 // Mask position index (m - 8) of dword d.
 __host__ __device__ __forceinline__ int sign_slot_mpos(int d) { return d < 8 ? d : d - 8; }
 
+// (src & mask) | base in one instruction.  The compiler splits it in two when both constants
+// are literals (one scalar operand per instruction on this architecture): here the mask comes in
+// a VGPR that stays loop-invariant and the base is the scalar operand.
+__device__ __forceinline__ uint32_t and_or_vs(uint32_t src, uint32_t vmask, uint32_t sbase) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(src), "v"(vmask), "s"(sbase));
+  return r;
+}
+
 __device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
   const uint32_t zl = z << 8;
 #pragma unroll
   for (int d = 0; d < 16; ++d) {
     const int m = d < 8 ? d + 8 : d;
     const uint32_t src = d < 8 ? zl : z;
-    const uint32_t bases[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
-                               0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
-    bz[d >> 2][d & 3] = (src & ((1u << m) | (1u << (m + 16)))) | bases[m - 8];
+    constexpr uint32_t bases[8] = {0x3c003c00u, 0x3c003c00u, 0x38003800u, 0x34003400u,
+                                   0x2c002c00u, 0x1c001c00u, 0x00000000u, 0x3c003c00u};
+    bz[d >> 2][d & 3] = and_or_vs(src, (1u << m) | (1u << (m + 16)), bases[m - 8]);
   }
 }
 
@@ -198,7 +207,9 @@ __device__ __forceinline__ void load_key_tile(const uint32_t* __restrict__ idx, 
   }
 }
 
-template <int BITS, bool PROD>
+// MULTI: GQA ratio above 4, so each key is scored for several groups of 4 heads; otherwise the
+// kernel carries only the single-group path.
+template <int BITS, bool PROD, bool MULTI>
 __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   const int bg = blockIdx.y;
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int ratio = Hq / Hkv;
-  const int groups = (ratio + 3) / 4;
+  const int groups = MULTI ? (ratio + 3) / 4 : 1;
   const int64_t base_row = (int64_t)bg * T;
   const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t ntiles_seq = (T + 15) / 16;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     if constexpr (PROD) sign_operand(cur.zw, bz);
     for (int hg = 0; hg < groups; ++hg) {
       u32x4 am[4], aq[4];
-      if (hg == 0) {
+      if (!MULTI || hg == 0) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) { am[s] = am0[s]; aq[s] = aq0[s]; }
       } else {
@@ -310,8 +321,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   }
 }
 
-template <int BITS, bool PROD>
-hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+template <int BITS, bool PROD, bool MULTI>
+hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
                          float* scores, const void* ws, hipStream_t st) {
   const int ratio = Hq / Hkv;
   const uint16_t* qws = static_cast<const uint16_t*>(ws);
@@ -323,7 +334,7 @@ hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, 
   static int per_cu = 0;
   if (per_cu == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_scores_d128<BITS, PROD>, kScoreWaves * 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_scores_d128<BITS, PROD, MULTI>, kScoreWaves * 64, 0) != hipSuccess ||
         v <= 0)
       v = 2;
     per_cu = v;
@@ -335,10 +346,17 @@ hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, 
   if (tpw < kScoreBatch) tpw = kScoreBatch;
   if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
-  hipLaunchKernelGGL((k_scores_d128<BITS, PROD>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
+  hipLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
                      0, st, qws, kconst, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
                      PROD ? K->rnorms : nullptr, cb, scores);
   return hipGetLastError();
+}
+
+template <int BITS, bool PROD>
+hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+                         float* scores, const void* ws, hipStream_t st) {
+  return Hq / Hkv > 4 ? scores_launch_m<BITS, PROD, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
+                      : scores_launch_m<BITS, PROD, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
 }
 
 }  // namespace
