@@ -312,16 +312,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
         d = mfma_f16(am[s], khi, d);
         d = mfma_f16(am2[s], klo, d);
       }
-      const float sc = sk;
-      const float v0 = d[0] * sc, v1 = d[1] * sc, v2 = d[2] * sc, v3 = d[3] * sc;
-      const bool lowg = g < 2;
-      float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
-      const float s0 = lowg ? v2 : v0, s1 = lowg ? v3 : v1;
-      k0 += __shfl_xor(s0, 32);
-      k1 += __shfl_xor(s1, 32);
-      const bool odd = g & 1;
-      float mine = odd ? k1 : k0;
-      mine += __shfl_xor(odd ? k0 : k1, 16);
+      const float mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
       lg[tt] = (valid && g < ratio) ? mine * scale : -INFINITY;
     }
     // online softmax for head g

@@ -218,6 +218,21 @@ __device__ __forceinline__ void build_table(uint8_t* tab, const _Float16* cent) 
 }
 
 
+// Transpose-reduce of a 16 x 16 MFMA result whose rows are 4 parts x 4 heads: lane (n, g) holds
+// row 4 g + r = (part g, head r) of column n in v[r].  Returns, in lane (n, g), the sum over the
+// four parts of head g for column n.  The lane swaps exchange halves of the wave in registers
+// (permlane32: lanes l and l ^ 32; permlane16: rows 2k and 2k + 1); each returns the pair
+// {own, partner} ordered so that adding the two results needs no per-lane select.
+__device__ __forceinline__ float reduce_parts(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  // g < 2: parts g and g + 2 of heads 0 / 1; g >= 2: parts g - 2 and g of heads 2 / 3
+  const float k0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float k1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Raw input of one 16-vector tile held by a lane: 32 consecutive coordinates of one vector.
 template <bool BF16IN>
 struct RawTile;

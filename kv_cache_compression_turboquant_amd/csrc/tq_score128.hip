@@ -290,16 +290,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
         if constexpr (PROD) acc = mfma_f16(aq[s], bz[s], acc);
       }
       const float sc = g < 2 ? nrm : 2.f * gam;
-      const float v0 = acc[0] * sc, v1 = acc[1] * sc, v2 = acc[2] * sc, v3 = acc[3] * sc;
-      const bool lowg = g < 2;
-      float k0 = lowg ? v0 : v2, k1 = lowg ? v1 : v3;
-      const float s0 = lowg ? v2 : v0, s1 = lowg ? v3 : v1;
-      k0 += __shfl_xor(s0, 32);
-      k1 += __shfl_xor(s1, 32);
-      const bool odd = g & 1;
-      float mine = odd ? k1 : k0;
-      const float other = odd ? k0 : k1;
-      mine += __shfl_xor(other, 16);
+      float mine = reduce_parts(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
       const int h = 4 * hg + g;
       if constexpr (PROD) mine -= gam * (hg == 0 ? kc0 : load_kc(hg));
       if (valid && h < ratio) scores[((int64_t)b * Hq + kvh * ratio + h) * T + t] = mine;
