@@ -235,18 +235,20 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
-  // replicated decode tables, at most 16 KB each so that two blocks fit a CU
-  constexpr int KC = table_copies<KB, true, 16384>();
+  // replicated decode tables (K up to 32 KB, V up to 16 KB) so that three blocks fit a CU
+  constexpr int KC = table_copies<KB, true, 32768>();
   constexpr int VC = table_copies<VB, false, 16384>();
   using DK = DecodeTable<KB, true, KC>;
   using DV = DecodeTable<VB, false, VC>;
-  __shared__ __attribute__((aligned(16))) uint8_t ktab[DK::BYTES];
+  // the K table's storage is reused for the block's merge buffer once every wave has finished
+  constexpr int kMergeBytes = 4 * 4 * 128 * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) uint8_t ktab[DK::BYTES > kMergeBytes ? DK::BYTES : kMergeBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
   __shared__ float kcent[16];
   __shared__ _Float16 vcent[16];
-  __shared__ __attribute__((aligned(16))) float wl[4][4][32];
+  // weights strip, rows padded to 48 floats: the 4 lanes sharing a key index land in 2 banks, not 1
+  __shared__ __attribute__((aligned(16))) float wl[4][4][48];
   __shared__ float mm[4][4], ll[4][4];
-  __shared__ float accs[4][4][128];
   if (threadIdx.x < 16) {
     kcent[threadIdx.x] = cbk.c[threadIdx.x];
     vcent[threadIdx.x] = (_Float16)cbv.c[threadIdx.x];
@@ -376,6 +378,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
   // wave totals: sum over the 16 keys lanes; hi + lo accumulator rows
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) l_part += __shfl_xor(l_part, o);
+  __syncthreads();  // every wave is done with the K table: its storage becomes the merge buffer
+  float (*accs)[4][128] = reinterpret_cast<float (*)[4][128]>(ktab);
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll

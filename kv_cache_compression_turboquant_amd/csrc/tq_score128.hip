@@ -72,7 +72,8 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
   const int h0 = kvh * ratio;
   const int j = threadIdx.x & 127, p = threadIdx.x >> 7;
   const int nmat = st ? 2 : 1;
-  for (int hc = 0; hc < ratio; hc += HG) {
+  // blockIdx.y takes every gridDim.y-th group of HG heads (one group per block at launch)
+  for (int hc = HG * blockIdx.y; hc < ratio; hc += HG * gridDim.y) {
     const int nh = ratio - hc < HG ? ratio - hc : HG;
     __syncthreads();
     if (threadIdx.x < HG * 128) {
@@ -354,8 +355,9 @@ hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, 
 
 hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,
                            uint16_t* qws, float* kconst, hipStream_t st) {
-  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv), dim3(kQprepThreads), 0, st, q, Hq, Hq / Hkv, rt, st_mat, qws,
-                     kconst);
+  const int groups = (Hq / Hkv + kQprepHeads - 1) / kQprepHeads;
+  hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv, groups), dim3(kQprepThreads), 0, st, q, Hq, Hq / Hkv, rt, st_mat,
+                     qws, kconst);
   return hipGetLastError();
 }
 
