@@ -143,3 +143,29 @@ def test_workspace_sizes(tq):
     big = lib.tq_search_workspace(1024, 10 ** 6, 1536, 10)
     assert big >= 1024 * 65536 * 4 + 2 * 1024 * 1536 * 4
     assert lib.tq_search_workspace(1024, 100, 1536, 10) < big
+
+
+def test_split_score_entry_points_validate(tq):
+    """The query-prologue and prepared-score entry points reject bad shapes before any launch."""
+    lib = tq.lib()
+    cbh = tq.codebook(128, 3)
+    desc = tq.tq_packed(128, 3, 0, 0, 10, None, None, None, None)
+    # null rotation / handles
+    assert lib.tq_prepare_queries(None, 1, 32, 8, None, None, None, 0, None) == 1
+    assert lib.tq_scores_prepared(None, 0, 1, 32, 8, 10, None, cbh.ptr, None, None) == 1
+    # Hq not a multiple of Hkv; GQA ratio 6 unsupported
+    assert lib.tq_scores_prepared(None, 0, 1, 30, 8, 10, ctypes.byref(desc), cbh.ptr, None, None) == 2
+    assert lib.tq_scores_prepared(None, 0, 1, 48, 8, 10, ctypes.byref(desc), cbh.ptr, None, None) == 3
+    # a descriptor of 10 keys without buffers is rejected before its shape is looked at
+    assert lib.tq_scores_prepared(None, 0, 1, 32, 8, 10, ctypes.byref(desc), cbh.ptr, None, None) == 1
+    # empty work is fine without buffers
+    empty = tq.tq_packed(128, 3, 0, 0, 0, None, None, None, None)
+    assert lib.tq_scores_prepared(None, 0, 0, 32, 8, 0, ctypes.byref(empty), cbh.ptr, None, None) == 0
+
+
+def test_search_entry_point_validates(tq):
+    lib = tq.lib()
+    cbh = tq.codebook(128, 3)
+    mse = tq.tq_packed(128, 3, 0, 0, 10, None, None, None, None)
+    # handles first, then k range
+    assert lib.tq_search_topk(None, 4, ctypes.byref(mse), cbh.ptr, None, None, 10, None, None, None, 0, None) == 1
