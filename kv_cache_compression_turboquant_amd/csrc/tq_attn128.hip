@@ -198,7 +198,22 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 constexpr int kAttnMinSteps = 16;
 constexpr int kAttnBatch = TQ_ATTN_BATCH;  // 32-token steps loaded together
 constexpr int kAttnRounds = TQ_ATTN_ROUNDS;
-constexpr int kAttnPart = 130;  // max, sum, 128 accumulators
+constexpr int kAttnPart = 130;
+
+// The value held by a partner lane within the lane's row of 16, through DPP (no LDS): steps
+// 0..3 pair lanes by xor 1, xor 2, mirror within 8, mirror within 16, so four max-steps leave
+// every lane of a row with the row's maximum.
+__device__ __forceinline__ float row16_partner(float v, int step) {
+  const int x = __float_as_int(v);
+  int y;
+  switch (step) {
+    case 0: y = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: y = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: y = __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(y);
+}  // max, sum, 128 accumulators
 
 // One 32-token step of a wave: the lane's key words and norms for both 16-token tiles, the
 // value norms, and the value chunks of octet g at coordinates 8 n .. 8 n + 7.
@@ -320,7 +335,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
     // online softmax for head g
     float mx = fmaxf(lg[0], lg[1]);
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int o = 0; o < 4; ++o) mx = fmaxf(mx, row16_partner(mx, o));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
     const float w0 = lg[0] == -INFINITY ? 0.f : __expf(lg[0] - m_new);
@@ -332,7 +347,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
     if (__any(alpha < 1.f)) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 16 * r);
+        const float ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 16 * r));
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c][r] *= ar;
       }
@@ -349,10 +364,11 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
       const float v[8] = {a[0], a[1], a[2], a[3], c2[0], c2[1], c2[2], c2[3]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const _Float16 h0 = (_Float16)v[2 * j], h1 = (_Float16)v[2 * j + 1];
-        const _Float16 l0 = (_Float16)(v[2 * j] - (float)h0), l1 = (_Float16)(v[2 * j + 1] - (float)h1);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        // pack-and-convert pairs (round toward zero; the remainder carries what hi drops)
+        const auto hp = __builtin_amdgcn_cvt_pkrtz(v[2 * j], v[2 * j + 1]);
+        const auto lp = __builtin_amdgcn_cvt_pkrtz(v[2 * j] - (float)hp[0], v[2 * j + 1] - (float)hp[1]);
+        const uint32_t hi = __builtin_bit_cast(uint32_t, hp);
+        const uint32_t lo = __builtin_bit_cast(uint32_t, lp);
         aw[j] = prt == 0 ? hi : (prt == 1 ? lo : 0u);
       }
     }
