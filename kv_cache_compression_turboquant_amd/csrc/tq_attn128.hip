@@ -1,7 +1,7 @@
 // Value-cache encode in the token-blocked layout and the fused decode attention at d = 128:
 // scores from packed K, online softmax, P V on MFMA in V's rotated domain, split merge and
 // the inverse rotation.
-#include "tq_device.h"
+#include "tq_decode.h"
 
 namespace tq {
 namespace {

@@ -18,7 +18,7 @@
 // signs as +-(gamma / s) sqrt(pi/2) / d, so one accumulator holds both terms).  Scores of one
 // chunk of the database go to the workspace, and a per-query kernel merges them into the
 // running top-k.
-#include "tq_device.h"
+#include "tq_decode.h"
 
 namespace tq {
 namespace {

@@ -1,6 +1,6 @@
 // Query prologue (q_rot = R q, q_s = S q once per query head) and the compressed-key score
 // kernel at d = 128, MSE and TurboQuant_prod, with GQA sharing.
-#include "tq_device.h"
+#include "tq_decode.h"
 
 namespace tq {
 namespace {
