@@ -55,7 +55,7 @@ def traffic_from_profile(kernel_key, launches_bytes_key):
 
 
 COPY_PROBE_BYTES = 512 << 20
-HEADLINE_KERNEL = "k_encode_d128<3, false, true, false,"  # MSE b=3, bf16 keys, packed output
+HEADLINE_KERNEL = "k_encode_mse_d128<3, true, 2,"  # MSE b=3, bf16 keys, dense R (two passes)
 
 
 def copy_probe(torch, dev, reps=3):
@@ -380,7 +380,7 @@ def main():
                    "encode_kernel_ms": enc_ms, "score_path_ms": sc_ms,
                    "score_path_gbs": score_alg_bytes / (sc_ms * 1e-3) / 1e9,
                    "buffer_sets": nbuf},
-        "roofline": {"bound": "hbm", "kernel": "k_encode_d128 (MSE b=3, dense R, bf16 keys)",
+        "roofline": {"bound": "hbm", "kernel": "k_encode_mse_d128 (MSE b=3, dense R, bf16 keys)",
                      "timing": f"HIP events around the encode launch of every {EVENT_EVERY}th timed step",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -21,7 +21,17 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
   constexpr int H = 1 << (BITS - 1);
   constexpr int PB = 4 * BITS;              // bits of a 4-token piece
   __shared__ u32x4 lds[RP * kFragU4];
-  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = fragt[i];
+  {
+    // All loads first (one wait), each block starting at a different slice so that blocks
+    // reading the same fragments in lockstep do not all queue on one L2 channel.
+    constexpr int kStage = RP * kFragU4 / 256;
+    const int rot0 = (int)(blockIdx.x % kStage);
+    u32x4 stage[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) stage[j] = fragt[threadIdx.x + ((j + rot0) % kStage) * 256];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) lds[threadIdx.x + ((j + rot0) % kStage) * 256] = stage[j];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;

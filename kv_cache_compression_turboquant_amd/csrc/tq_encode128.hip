@@ -1,5 +1,7 @@
 // Fused TurboQuant encode at d = 128 (rows layout): norm, rotation on MFMA, bucketize, pack,
 // and for TurboQuant_prod the QJL sign sketch of the residual with its norm.
+#include <type_traits>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -47,21 +49,37 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
   int64_t tw = ((int64_t)blockIdx.x * kWaves + wave) * NT;
 
   // Two tile groups in flight per wave, in two register sets used alternately (no copies, so
-  // each wait covers exactly the group about to be used).  The first loads are issued before
-  // the fragments are staged into LDS so that both latencies overlap.
-  // (Loads past the end read the clamped last row: unconditional loads keep the register sets
-  // fixed across iterations, where conditional ones would make the compiler copy them.)
+  // each wait covers exactly the group about to be used).  (Loads past the end read the
+  // clamped last row: unconditional loads keep the register sets fixed across iterations, where
+  // conditional ones would make the compiler copy them.)
+  // All fragment loads are issued first, then the first tile loads, so the fragments' waits do
+  // not cover the tiles, which stay in flight while the fragments are written to LDS.  (A
+  // load-wait-store loop would wait out one memory latency per fragment, behind the tiles.)
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kTotal = (RP + SP) * kFragU4;
+  constexpr int kStage = (kTotal + kThreads - 1) / kThreads;
+  u32x4 stage[kStage];
+  // Blocks start at different slices (rotated by block index): every block reads the same
+  // fragments, and in lockstep they would all queue on one L2 channel at a time.
+  const int rot0 = (int)(blockIdx.x % kStage);
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int jr = j + rot0 < kStage ? j + rot0 : j + rot0 - kStage;
+    const int i = threadIdx.x + jr * kThreads;
+    if (kTotal % kThreads == 0 || i < kTotal) stage[j] = i < RP * kFragU4 ? frag_r[i] : frag_s[i - RP * kFragU4];
+  }
   RawTile<BF16IN> bufA[NT], bufB[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + t, nl, g, bufA[t]);
 #pragma unroll
   for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + stride + t, nl, g, bufB[t]);
-  for (int i = threadIdx.x; i < RP * kFragU4; i += blockDim.x) lds[i] = frag_r[i];
-  if constexpr (PROD) {
-    for (int i = threadIdx.x; i < SP * kFragU4; i += blockDim.x) lds[RP * kFragU4 + i] = frag_s[i];
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int jr = j + rot0 < kStage ? j + rot0 : j + rot0 - kStage;
+    const int i = threadIdx.x + jr * kThreads;
+    if (kTotal % kThreads == 0 || i < kTotal) lds[i] = stage[j];
   }
   __syncthreads();
-  if (tw >= ntiles) return;  // no barrier follows
 
   const float inv_post = 1.0f / post_scale;
   auto step = [&](RawTile<BF16IN> (&cur)[NT], const int64_t t0) {
@@ -251,11 +269,316 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
       }
     }
   };
-  for (; tw < ntiles; tw += 2 * stride) {
+  // The loop is entered unconditionally: an early exit here would let the compiler sink the tile
+  // loads above past the barrier.  A wave without a tile of its own (only in the last block)
+  // makes one pass over clamped rows and stores nothing, since every store checks its row.
+  for (;;) {
     step(bufA, tw);
     if (tw + stride >= ntiles) break;
     step(bufB, tw + stride);
+    tw += 2 * stride;
+    if (tw >= ntiles) break;
   }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// MSE encode, d = 128, with the quantizer interleaved into the rotation.  Block c's MFMAs give
+// each lane 4 coordinates of each of its vectors (rows 32 G + 4 c + r); those are bucketized and
+// packed while the next block's MFMAs run, so only two blocks of results are live at a time.
+//
+// Packing by shift-in: the blocks run from c = 7 down to 0, so the lane's coordinates come in
+// descending order and so do their stream bits (bit j of coordinate i is stream bit b i + j).
+// Each bit then enters its word from the bottom, w = 2 w + bit, which is one v_addc with the
+// bit as a lane mask: no shifts, selects or ORs per field.
+// The index of y is (m ^ sgn) + K/2 with m = #{p : |y| >= t_p} (the sign-magnitude form of the
+// antisymmetric codebook), so its top bit is [y >= 0] and its low bits are the bits of m, each
+// XNOR-ed with [y >= 0] (a scalar op on the lane masks).  m comes from a binary search over the
+// sorted positive thresholds: its bits are produced top first, exactly in push order.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint64_t lanes) {
+  uint32_t r;
+  uint64_t carry;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry) : "v"(w), "s"(lanes));
+  return r;
+}
+
+template <int BITS>
+struct Thr {
+  float t[BITS > 1 ? (1 << (BITS - 1)) - 1 : 1];
+};
+
+// Push the BITS index bits of lane-local coordinate LI (top bit first) for every tile.  Each
+// step is issued for all tiles before the next one, so that the dependent steps of one tile
+// (compare -> lane-mask op -> push) are separated by the independent work of the others.
+template <int BITS, int LI, int NT>
+__device__ __forceinline__ void push_index(const f32x4 (&v)[NT], const Thr<BITS> (&th)[NT], uint32_t (&w)[NT][BITS]) {
+  constexpr int P = BITS * LI;  // stream bit of the index's bit 0
+  constexpr int R = LI & 3;     // register of the block holding coordinate LI
+  float a[NT];
+  uint64_t pos[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    a[t] = fabsf(v[t][R]);
+    pos[t] = __builtin_amdgcn_ballot_w64(v[t][R] >= 0.f);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) w[t][(P + BITS - 1) >> 5] = push_bit(w[t][(P + BITS - 1) >> 5], pos[t]);
+  if constexpr (BITS == 2) {
+    uint64_t b0[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) b0[t] = __builtin_amdgcn_ballot_w64(a[t] >= th[t].t[0]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][P >> 5] = push_bit(w[t][P >> 5], ~(b0[t] ^ pos[t]));
+  } else if constexpr (BITS == 3) {
+    bool hi[NT];
+    uint64_t b1[NT], b0[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      hi[t] = a[t] >= th[t].t[1];
+      b1[t] = __builtin_amdgcn_ballot_w64(hi[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][(P + 1) >> 5] = push_bit(w[t][(P + 1) >> 5], ~(b1[t] ^ pos[t]));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) b0[t] = __builtin_amdgcn_ballot_w64(a[t] >= (hi[t] ? th[t].t[2] : th[t].t[0]));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][P >> 5] = push_bit(w[t][P >> 5], ~(b0[t] ^ pos[t]));
+  } else if constexpr (BITS == 4) {
+    bool h2[NT], h1[NT];
+    uint64_t b2[NT], b1[NT], b0[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      h2[t] = a[t] >= th[t].t[3];
+      b2[t] = __builtin_amdgcn_ballot_w64(h2[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][(P + 2) >> 5] = push_bit(w[t][(P + 2) >> 5], ~(b2[t] ^ pos[t]));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      h1[t] = a[t] >= (h2[t] ? th[t].t[5] : th[t].t[1]);
+      b1[t] = __builtin_amdgcn_ballot_w64(h1[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][(P + 1) >> 5] = push_bit(w[t][(P + 1) >> 5], ~(b1[t] ^ pos[t]));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float t0 = h1[t] ? (h2[t] ? th[t].t[6] : th[t].t[2]) : (h2[t] ? th[t].t[4] : th[t].t[0]);
+      b0[t] = __builtin_amdgcn_ballot_w64(a[t] >= t0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t][P >> 5] = push_bit(w[t][P >> 5], ~(b0[t] ^ pos[t]));
+  }
+}
+
+// Coordinates 4 C + 3 .. 4 C of every tile, in descending order.
+template <int BITS, int C, int NT>
+__device__ __forceinline__ void push_block(const f32x4 (&v)[NT], const Thr<BITS> (&th)[NT], uint32_t (&w)[NT][BITS]) {
+  push_index<BITS, 4 * C + 3, NT>(v, th, w);
+  push_index<BITS, 4 * C + 2, NT>(v, th, w);
+  push_index<BITS, 4 * C + 1, NT>(v, th, w);
+  push_index<BITS, 4 * C, NT>(v, th, w);
+}
+
+// Compile-time loop C = HI, HI - 1, .., 0 (the block index must be a constant for the bit offsets;
+// a plain loop of this size is not always unrolled).
+template <int C>
+struct BlockIdx {
+  static constexpr int value = C;
+};
+template <int C, typename F>
+__device__ __forceinline__ void for_blocks_down(F&& f) {
+  if constexpr (C >= 0) {
+    f(BlockIdx<C>{});
+    for_blocks_down<C - 1>(f);
+  }
+}
+
+constexpr int kMseWaves = 4;
+
+template <int BITS, bool BF16IN, int RP, int NT>
+__global__ __launch_bounds__(kMseWaves * 64, 2) void k_encode_mse_d128(
+    const void* __restrict__ x, int64_t n, const u32x4* __restrict__ frag_r, float post_scale,
+    CodebookArgs cb, uint32_t* __restrict__ idx_out, float* __restrict__ norms_out) {
+  constexpr int H = 1 << (BITS - 1);
+  constexpr int kThreads = kMseWaves * 64;
+  constexpr int kStage = RP * kFragU4 / kThreads;
+  static_assert(RP * kFragU4 % kThreads == 0, "staging split");
+  __shared__ u32x4 lds[RP * kFragU4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int64_t ntiles = (n + 15) >> 4;
+  const int64_t stride = (int64_t)gridDim.x * kMseWaves * NT;
+  int64_t tw = ((int64_t)blockIdx.x * kMseWaves + wave) * NT;
+
+  // Fragment loads first, then the first tile group only.  The next group's loads are spread
+  // over the MFMA blocks of the current step: a wave that issued several groups up front would
+  // stall on the issue of its loads (the memory pipeline accepts a bounded number) and reach
+  // the barrier, and its first MFMA, only once most of the device's requests had drained.
+  u32x4 stage[kStage];
+  const int rot0 = (int)(blockIdx.x % kStage);   // staggered start, as in k_encode_d128
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) stage[j] = frag_r[threadIdx.x + ((j + rot0) % kStage) * kThreads];
+  RawTile<BF16IN> bufA[NT], bufB[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + t, nl, g, bufA[t]);
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) lds[threadIdx.x + ((j + rot0) % kStage) * kThreads] = stage[j];
+  __syncthreads();
+
+  const float inv_post = 1.0f / post_scale;
+  // Loads of the next group: NV vector loads per tile, LPB of them issued per MFMA block.
+  constexpr int NV = BF16IN ? 4 : 8;
+  constexpr int LPB = (NT * NV + 7) / 8;
+  using Elem = typename std::conditional<BF16IN, u32x4, f32x4>::type;
+  auto step = [&](RawTile<BF16IN> (&cur)[NT], RawTile<BF16IN> (&nxt)[NT], const int64_t t0) {
+    const Elem* nsrc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = (t0 + stride + t) * 16 + nl;
+      const int64_t lrow = row < n ? row : n - 1;   // clamped: past the end reads the last row
+      nsrc[t] = reinterpret_cast<const Elem*>(static_cast<const char*>(x) + (lrow * 128 + 32 * g) * (BF16IN ? 2 : 4));
+    }
+    // B operands: bf16 input is used in place; fp32 input is split into bf16 hi + lo.
+    u32x4 bxh[BF16IN ? 1 : NT][4], bxl[BF16IN ? 1 : NT][4];
+    Thr<BITS> thr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float acc2 = 0.f;
+      if constexpr (BF16IN) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint32_t wv[4];
+          __builtin_memcpy(wv, &cur[t].v[s], sizeof(wv));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 p = __builtin_bit_cast(bf16x2, wv[j]);
+            acc2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc2, false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 a = cur[t].v[2 * s], b = cur[t].v[2 * s + 1];
+          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x2 pr = {v[2 * j], v[2 * j + 1]};
+            const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+            const f32x2 rem = {v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
+            bxh[t][s][j] = h;
+            bxl[t][s][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+            acc2 = fmaf(v[2 * j], v[2 * j], acc2);
+            acc2 = fmaf(v[2 * j + 1], v[2 * j + 1], acc2);
+          }
+        }
+      }
+      acc2 += __shfl_xor(acc2, 16);
+      acc2 += __shfl_xor(acc2, 32);
+      const float nrm = sqrtf(acc2);
+      const bool live = nrm > 0.f;
+      const int64_t row = (t0 + t) * 16 + nl;
+      if (row < n && g == 0) norms_out[row] = nrm;
+      // Decisions on the raw product against t_p * ||x|| / post_scale; a zero vector keeps every
+      // threshold at +inf (index K/2 everywhere).
+      const float tsc = nrm * inv_post;
+      if constexpr (H > 1) {
+#pragma unroll
+        for (int p = 0; p < H - 1; ++p) thr[t].t[p] = live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY;
+      }
+    }
+
+    uint32_t w[NT][BITS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) w[t][j] = 0;
+    // One fragment set only: each pass's fragments for the next block are read into the
+    // registers of the current one as soon as that pass's MFMAs have issued, and arrive during
+    // the other pass and the quantizer work.  Blocks run c = 7 .. 0 (push order).
+    f32x4 prev[NT];
+    u32x4 cf[RP][4];
+    load_frags<RP>(lds, 7, lane, cf);
+    for_blocks_down<7>([&](auto ci) {
+      constexpr int c = decltype(ci)::value;
+      f32x4 now[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) now[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if constexpr (BF16IN) {
+              now[t] = mfma_bf16(cf[p][s], cur[t].v[s], now[t]);
+            } else {
+              now[t] = mfma_bf16(cf[p][s], bxh[t][s], now[t]);
+              if (p == 0) now[t] = mfma_bf16(cf[p][s], bxl[t][s], now[t]);
+            }
+          }
+        if constexpr (c > 0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) cf[p][s] = lds[p * kFragU4 + ((c - 1) * 4 + s) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < LPB; ++k) {
+        constexpr int q0 = (7 - c) * LPB;
+        const int q = q0 + k;
+        if (q < NT * NV) nxt[q / NV].v[q % NV] = nsrc[q / NV][q % NV];
+      }
+      if constexpr (c < 7) push_block<BITS, c + 1, NT>(prev, thr, w);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) prev[t] = now[t];
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    push_block<BITS, 0, NT>(prev, thr, w);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = (t0 + t) * 16 + nl;
+      if (row < n) {
+        uint32_t* dst = idx_out + row * (4 * BITS) + BITS * g;
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) dst[j] = w[t][j];
+      }
+    }
+  };
+  // Entered unconditionally (an early exit would let the compiler sink the tile loads past the
+  // barrier); a wave without a tile of its own stores nothing, since every store checks its row.
+  for (;;) {
+    step(bufA, bufB, tw);
+    if (tw + stride >= ntiles) break;
+    step(bufB, bufA, tw + stride);
+    tw += 2 * stride;
+    if (tw >= ntiles) break;
+  }
+}
+
+template <int BITS, bool BF16IN, int RP>
+hipError_t mse_launch(const void* x, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                      uint32_t* idx, float* norms, hipStream_t st) {
+  constexpr int NT = BF16IN ? 2 : 1;
+  const int64_t ntiles = (n + 15) / 16;
+  const int64_t per_block = (int64_t)kMseWaves * NT;
+  int64_t blocks = (ntiles + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)num_cus() * 2;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
+                     st, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb, idx, norms);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t mse_dispatch(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                        uint32_t* idx, float* norms, hipStream_t st) {
+  if (bf16)
+    return rot->passes == 1 ? mse_launch<BITS, true, 1>(x, n, rot, cb, idx, norms, st)
+                            : mse_launch<BITS, true, 2>(x, n, rot, cb, idx, norms, st);
+  return rot->passes == 1 ? mse_launch<BITS, false, 1>(x, n, rot, cb, idx, norms, st)
+                          : mse_launch<BITS, false, 2>(x, n, rot, cb, idx, norms, st);
 }
 
 
@@ -300,6 +623,15 @@ hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rota
                               hipStream_t st) {
   if (y_out) return enc_dispatch_in<1, false, true>(x, bf16, n, rot, nullptr, cb, nullptr, norms, nullptr, nullptr, y_out, st);
   const bool prod = qjl != nullptr;
+  if (!prod) {
+    switch (cb.bits) {
+      case 1: return mse_dispatch<1>(x, bf16, n, rot, cb, idx, norms, st);
+      case 2: return mse_dispatch<2>(x, bf16, n, rot, cb, idx, norms, st);
+      case 3: return mse_dispatch<3>(x, bf16, n, rot, cb, idx, norms, st);
+      case 4: return mse_dispatch<4>(x, bf16, n, rot, cb, idx, norms, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (cb.bits) {
     case 1:
       return prod ? enc_dispatch_in<1, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)

@@ -124,17 +124,20 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void k_encode_gen(
 #pragma unroll
   for (int j = 0; j < kGTiles; ++j) ss[j] = 0.f;
 
+  // Blocks with the same output block read the same fragments in lockstep: each starts its
+  // staging at a different slice so that they do not all queue on one L2 channel.
+  const int rot0 = (int)(blockIdx.x % PER);
   for (int kc = 0; kc < nb; ++kc) {
     const u32x4* src = frag + (size_t)(ob * nb + kc) * 2 * kFragU4;
     u32x4 stage[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) stage[i] = src[i * (kGWaves * 64) + threadIdx.x];
+    for (int i = 0; i < PER; ++i) stage[i] = src[((i + rot0) % PER) * (kGWaves * 64) + threadIdx.x];
     RawTile<BF16IN> raw[kGTiles];
 #pragma unroll
     for (int j = 0; j < kGTiles; ++j) load_gen<BF16IN>(x, n, d, row0 + 16 * j, kc, nl, g, raw[j]);
     __syncthreads();  // the previous chunk's fragments are no longer read
 #pragma unroll
-    for (int i = 0; i < PER; ++i) lds[i * (kGWaves * 64) + threadIdx.x] = stage[i];
+    for (int i = 0; i < PER; ++i) lds[((i + rot0) % PER) * (kGWaves * 64) + threadIdx.x] = stage[i];
     u32x4 bx[kGTiles][4], bxl[kGTiles][4];
 #pragma unroll
     for (int j = 0; j < kGTiles; ++j) to_operand<BF16IN, NORM>(raw[j], bx[j], bxl[j], ss[j]);
