@@ -330,32 +330,32 @@ def main():
     outs = [torch.empty((cfg.B, cfg.hq, cfg.T), dtype=torch.float32, device=dev) for _ in range(nbuf)]
     ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
+    def step(i, timers=None):
         j = i % nbuf
-        if ev is not None:
-            ev[0].record()
+        if timers is not None:
+            timers.append(tq.timer_arm())
         tq.encode(xs[j], cfg.bits, "mse", cb, rot, out=packs[j])
-        if ev is not None:
-            ev[1].record()
         tq.scores(q, packs[j], cfg.hkv, cb, rot, out=outs[j], ws=ws)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps.  The encode kernel's duration is taken live with HIP events
-    # on the stream it runs on, around every EVENT_EVERY-th step's encode launch (an event pair
-    # on every step costs the queue a few microseconds per step on this runtime).
+    # Timed region: exactly K steps.  The encode kernel's duration is taken live, on every
+    # EVENT_EVERY-th step, with a pair of HIP events that the library attaches to that kernel's
+    # dispatch (hipExtLaunchKernel): they bracket the kernel alone, on the stream it runs on.
     EVENT_EVERY = 4
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, args.steps, EVENT_EVERY)}
+    timers = []
+    tq.timer_reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs.get(i))
+        step(args.warmup + i, timers if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
+    enc_ms = float(np.mean([tq.timer_read(t) for t in timers]))
+    tq.timer_reset()
 
     # outside the timed region: the score path alone (query prologue + score kernel)
     sc_ms = _timed(lambda i: tq.scores(q, packs[i % nbuf], cfg.hkv, cb, rot, out=outs[i % nbuf], ws=ws), 20, 2)
@@ -381,7 +381,7 @@ def main():
                    "score_path_gbs": score_alg_bytes / (sc_ms * 1e-3) / 1e9,
                    "buffer_sets": nbuf},
         "roofline": {"bound": "hbm", "kernel": "k_encode_mse_d128 (MSE b=3, dense R, bf16 keys)",
-                     "timing": f"HIP events around the encode launch of every {EVENT_EVERY}th timed step",
+                     "timing": f"HIP events attached to the encode kernel's dispatch on every {EVENT_EVERY}th timed step",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": enc_alg_bytes},

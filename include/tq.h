@@ -245,6 +245,20 @@ tq_status tq_search_topk(const float* q_dev, int64_t nq, const tq_packed* db, tq
                          tq_rotation_t rot, tq_qjl_t qjl, int k, float* top_s_dev,
                          int64_t* top_i_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
+/* Kernel timers, for measurement tools (not part of the method).  tq_timer_arm makes the next
+ * launch of the d = 128 rows-layout encode kernel on the calling thread (by tq_encode, or
+ * tq_rotate at d = 128) attach a pair of HIP events to the kernel's dispatch, so that the
+ * interval covers that kernel's execution alone (not the queue's own dispatch latency); other
+ * calls leave the timer armed.  Returns a timer
+ * id in [0, TQ_MAX_TIMERS), or -1 (TQ_ENOMEM in tq_last_error when every timer is in use,
+ * TQ_EDEVICE when no events can be created).  tq_timer_read waits for that kernel and writes
+ * its duration in milliseconds to *ms; TQ_EINVAL for an id that was not armed and launched.
+ * tq_timer_reset releases every timer (the events are kept for reuse). */
+#define TQ_MAX_TIMERS 256
+int tq_timer_arm(void);
+tq_status tq_timer_read(int id, float* ms);
+void tq_timer_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

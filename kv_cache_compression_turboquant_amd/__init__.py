@@ -18,7 +18,7 @@ __all__ = [
     "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
-    "prepare_queries", "scores_prepared",
+    "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -318,3 +318,23 @@ def search_topk(q, db, k, cb, rot, qjl, ws=None, out=None):
     check(lib().tq_search_topk(_dptr(q), nq, ctypes.byref(desc), cb.ptr, rot.ptr, qjl.ptr, k, _dptr(out[0]),
                                _dptr(out[1]), _dptr(ws), ws.numel() * ws.element_size(), _stream()))
     return out
+
+
+def timer_arm():
+    """Arm a kernel timer for the next d = 128 rows-layout encode launch on this thread; returns
+    its id (measurement helper: the events are attached to the kernel's own dispatch)."""
+    t = int(lib().tq_timer_arm())
+    if t < 0:
+        raise TQError(4, lib().tq_last_error().decode())
+    return t
+
+
+def timer_read(t):
+    """Duration in ms of the kernel launched under timer t (waits for it)."""
+    ms = ctypes.c_float()
+    check(lib().tq_timer_read(int(t), ctypes.byref(ms)))
+    return float(ms.value)
+
+
+def timer_reset():
+    lib().tq_timer_reset()

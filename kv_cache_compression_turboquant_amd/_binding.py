@@ -68,6 +68,9 @@ SIGNATURES = {
     "tq_encode_workspace": (_SZ, [_I64, _I, _I, _I]),
     "tq_search_workspace": (_SZ, [_I64, _I64, _I, _I]),
     "tq_search_topk": (_I, [_P, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "tq_timer_arm": (_I, []),
+    "tq_timer_read": (_I, [_I, ctypes.POINTER(ctypes.c_float)]),
+    "tq_timer_reset": (None, []),
     "tq_rotate": (_I, [_P, _I, _I64, _I, _P, _P, _P, _P]),
     "tq_quantize_rotated": (_I, [_P, _I64, _I, _P, _P, _P]),
     "tq_decode": (_I, [ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),

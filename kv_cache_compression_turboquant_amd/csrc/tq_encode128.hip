@@ -1,5 +1,7 @@
 // Fused TurboQuant encode at d = 128 (rows layout): norm, rotation on MFMA, bucketize, pack,
 // and for TurboQuant_prod the QJL sign sketch of the residual with its norm.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "tq_device.h"
@@ -566,6 +568,14 @@ hipError_t mse_launch(const void* x, int64_t n, const tq_rotation_s* rot, const 
   int64_t blocks = (ntiles + per_block - 1) / per_block;
   const int64_t cap = (int64_t)num_cus() * 2;
   if (blocks > cap) blocks = cap;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (take_armed_timer(&ev0, &ev1)) {
+    // events attached to the dispatch itself: they bracket the kernel's execution alone
+    hipExtLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
+                          st, ev0, ev1, 0, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb,
+                          idx, norms);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
                      st, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb, idx, norms);
   return hipGetLastError();
@@ -593,6 +603,15 @@ hipError_t enc_launch(const void* x, int64_t n, const tq_rotation_s* rot, const 
   int64_t blocks = (ntiles + per_block - 1) / per_block;
   const int64_t cap = (int64_t)num_cus() * EncShape<PROD>::kBlocksPerCU;
   if (blocks > cap) blocks = cap;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (take_armed_timer(&ev0, &ev1)) {
+    hipExtLaunchKernelGGL((k_encode_d128<BITS, PROD, BF16IN, STORE_Y, PASSES, NT>), dim3((unsigned)blocks),
+                          dim3(kWaves * 64), 0, st, ev0, ev1, 0, x, n,
+                          reinterpret_cast<const u32x4*>(rot->frag_dev),
+                          reinterpret_cast<const u32x4*>(qjl ? qjl->frag_dev : nullptr), rot->post_scale, cb, idx,
+                          norms, qbits, rnorms, y);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_encode_d128<BITS, PROD, BF16IN, STORE_Y, PASSES, NT>), dim3((unsigned)blocks),
                      dim3(kWaves * 64), 0, st, x, n,
                      reinterpret_cast<const u32x4*>(rot->frag_dev),

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <thread>
 #include <vector>
@@ -438,11 +439,74 @@ tq_status check_launch(hipError_t e, const char* what) {
   return TQ_OK;
 }
 
+// Kernel timers: event pairs created on first use, handed to one launch each.
+struct Timer {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false, launched = false;
+};
+std::mutex g_timer_mu;
+Timer g_timers[TQ_MAX_TIMERS];
+thread_local int g_armed_timer = -1;
+
 }  // namespace
+
+bool tq::take_armed_timer(hipEvent_t* start, hipEvent_t* stop) {
+  const int id = g_armed_timer;
+  if (id < 0) return false;
+  g_armed_timer = -1;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  *start = g_timers[id].start;
+  *stop = g_timers[id].stop;
+  g_timers[id].launched = true;
+  return true;
+}
 
 extern "C" {
 
 int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+int tq_timer_arm(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (int i = 0; i < TQ_MAX_TIMERS; ++i) {
+    Timer& t = g_timers[i];
+    if (t.used) continue;
+    if (!t.start && (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess)) {
+      if (t.start) (void)hipEventDestroy(t.start);
+      t.start = t.stop = nullptr;
+      fail(TQ_EDEVICE, "tq_timer_arm: cannot create HIP events");
+      return -1;
+    }
+    t.used = true;
+    t.launched = false;
+    g_armed_timer = i;
+    return i;
+  }
+  fail(TQ_ENOMEM, "tq_timer_arm: all %d timers in use", TQ_MAX_TIMERS);
+  return -1;
+}
+
+tq_status tq_timer_read(int id, float* ms) {
+  if (!ms || id < 0 || id >= TQ_MAX_TIMERS) return fail(TQ_EINVAL, "tq_timer_read: bad arguments");
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (!g_timers[id].used || !g_timers[id].launched)
+      return fail(TQ_EINVAL, "tq_timer_read: timer %d was not armed and launched", id);
+    a = g_timers[id].start;
+    b = g_timers[id].stop;
+  }
+  hipError_t e = hipEventSynchronize(b);
+  if (e != hipSuccess) return hip_fail(e, "tq_timer_read");
+  e = hipEventElapsedTime(ms, a, b);
+  if (e != hipSuccess) return hip_fail(e, "tq_timer_read");
+  return ok();
+}
+
+void tq_timer_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (Timer& t : g_timers) t.used = t.launched = false;
+  g_armed_timer = -1;
+}
 
 const char* tq_last_error(void) { return g_last_error.c_str(); }
 

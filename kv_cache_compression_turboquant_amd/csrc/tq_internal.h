@@ -79,6 +79,10 @@ namespace tq {
 // Compute units of the current device (cached per device).
 int num_cus();
 
+// The event pair armed by tq_timer_arm on this thread, if any, handed to the next launch that
+// supports timing (and disarmed); false when none is armed.
+bool take_armed_timer(hipEvent_t* start, hipEvent_t* stop);
+
 // Launchers (tq_encode128.hip, tq_misc.hip, tq_score128.hip, tq_attn128.hip).  All return the
 // HIP error of the launch.
 hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,

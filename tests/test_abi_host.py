@@ -169,3 +169,18 @@ def test_search_entry_point_validates(tq):
     mse = tq.tq_packed(128, 3, 0, 0, 10, None, None, None, None)
     # handles first, then k range
     assert lib.tq_search_topk(None, 4, ctypes.byref(mse), cbh.ptr, None, None, 10, None, None, None, 0, None) == 1
+
+
+def test_timer_entry_points(tq):
+    lib = tq.lib()
+    ms = ctypes.c_float()
+    lib.tq_timer_reset()
+    # ids never armed, or out of range, are rejected
+    assert lib.tq_timer_read(0, ctypes.byref(ms)) == 1
+    assert lib.tq_timer_read(-1, ctypes.byref(ms)) == 1
+    assert lib.tq_timer_read(256, ctypes.byref(ms)) == 1
+    assert lib.tq_timer_read(0, None) == 1
+    # without a device no events can be created: arming fails cleanly
+    t = lib.tq_timer_arm()
+    assert t == -1 or 0 <= t < 256
+    lib.tq_timer_reset()

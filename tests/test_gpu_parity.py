@@ -274,3 +274,20 @@ def test_scores_prepared_matches_scores(dev, rot_dense, mode, b):
     assert torch.equal(got, ref)
     with pytest.raises(tq.TQError):
         tq.scores_prepared(ws[:16], 2, 16, p, 4, cb)
+
+
+def test_kernel_timer(dev, rot_dense):
+    """The timer attached to a d = 128 encode launch reports a positive duration; ids are reusable
+    after a reset."""
+    cb = tq.codebook(128, 3)
+    x = _keys(4096, hkv=2)[1].to(dev)
+    tq.timer_reset()
+    t = tq.timer_arm()
+    tq.encode(x, 3, "mse", cb, rot_dense)
+    ms = tq.timer_read(t)
+    assert 0.0 < ms < 1000.0
+    tq.timer_reset()
+    assert tq.timer_arm() == t      # the first free id again
+    tq.encode(x, 3, "mse", cb, rot_dense)
+    assert tq.timer_read(t) > 0.0
+    tq.timer_reset()
