@@ -812,9 +812,16 @@ static tq_status check_score_heads(int B, int Hq, int Hkv, const char* fn) {
   return TQ_OK;
 }
 
+// Longest sequence the score and attention kernels take: their per-tile token offsets are
+// 32-bit (at most 64 bytes of packed words per token).
+constexpr int64_t kMaxSeqTokens = int64_t(1) << 25;
+
 static tq_status check_score_keys(int B, int Hkv, int64_t T, const tq_packed* K, tq_codebook_t cb, int d,
                                   const char* fn) {
   if (T < 0) return fail(TQ_EINVAL, "%s: negative T", fn);
+  if (T > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: T=%lld exceeds %lld tokens per sequence", fn, (long long)T,
+                (long long)kMaxSeqTokens);
   tq_status st = check_packed(K, d, cb->b, K->mode, fn);
   if (st != TQ_OK) return st;
   if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: keys must use the ROWS layout", fn);
@@ -849,6 +856,9 @@ tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq,
   if (st != TQ_OK) return st;
   st = check_score_keys(B, Hkv, T, K, cb, K->d, fn);
   if (st != TQ_OK) return st;
+  if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
+    return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
+                (long long)(Hq / Hkv) * T);
   if ((int64_t)B * Hq * T == 0) return ok();
   if (!scores_dev) return fail(TQ_EINVAL, "%s: null scores", fn);
   const size_t need = tq::scores_workspace_bytes(B, Hq, K->d);
@@ -867,6 +877,9 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
   const int d = rot->d;
   st = check_score_keys(B, Hkv, T, K, cb, d, fn);
   if (st != TQ_OK) return st;
+  if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
+    return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
+                (long long)(Hq / Hkv) * T);
   if (K->mode == TQ_MODE_PROD) {
     if (!qjl) return fail(TQ_EINVAL, "%s: prod keys need the qjl handle", fn);
     if (qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
@@ -895,6 +908,9 @@ tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, 
   if (!K || !V || !cb_k || !cb_v || !rot_k || !rot_v) return fail(TQ_EINVAL, "%s: null argument", fn);
   if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (T < 1) return fail(TQ_EINVAL, "%s: attention over an empty cache (T=%lld)", fn, (long long)T);
+  if (T > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: T=%lld exceeds %lld tokens per sequence", fn, (long long)T,
+                (long long)kMaxSeqTokens);
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
   const int ratio = Hq / Hkv;
   if (ratio != 1 && ratio != 2 && ratio != 4) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not in {1, 2, 4}", fn, ratio);

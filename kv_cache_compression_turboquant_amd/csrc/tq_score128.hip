@@ -185,23 +185,46 @@ struct KeyTile {
   float gam;
 };
 
+// Raw buffer resource over n bytes at p (untyped dword loads; the hardware range check returns
+// zero for any load at or past n bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+template <int W>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[W]) {
+  if constexpr (W == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (W == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (W == 3) {
+    typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  }
+}
+
+// The sequence's packed keys as buffer resources: each load is the resource plus one 32-bit
+// per-lane offset, and tokens past T read as zero (their scores are never stored).
+template <bool PROD>
+struct KeyBufs {
+  __amdgpu_buffer_rsrc_t idx, norms, qbits, rnorms;
+};
+
 // Lane (n, g) share of key tile `tile` of one sequence: its BITS words (coordinates 32 g ..),
-// norm, and for prod its sign word and scaled residual norm.  Rows past T are clamped.
+// norm, and for prod its sign word and scaled residual norm.
 template <int BITS, bool PROD>
-__device__ __forceinline__ void load_key_tile(const uint32_t* __restrict__ idx, const float* __restrict__ norms,
-                                              const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms,
-                                              int64_t base_row, int64_t T, int64_t tile, int nl, int g,
-                                              KeyTile<BITS, PROD>& k) {
-  int64_t t = tile * 16 + nl;
-  t = t < T ? t : T - 1;
-  const int64_t row = base_row + t;
-  const uint32_t* src = idx + row * (4 * BITS) + BITS * g;
-#pragma unroll
-  for (int j = 0; j < BITS; ++j) k.w[j] = src[j];
-  k.nrm = norms[row];
+__device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile, int nl, int g, KeyTile<BITS, PROD>& k) {
+  const uint32_t t = (uint32_t)tile * 16u + (uint32_t)nl;
+  buffer_words<BITS>(kb.idx, t * (16u * BITS) + (uint32_t)(4 * BITS * g), k.w);
+  k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.norms, t * 4u, 0, 0));
   if constexpr (PROD) {
-    k.zw = qbits[row * 4 + g];
-    k.gam = rnorms[row] * (kQjl / 128.0f);
+    k.zw = __builtin_amdgcn_raw_buffer_load_b32(kb.qbits, t * 16u + 4u * (uint32_t)g, 0, 0);
+    k.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.rnorms, t * 4u, 0, 0)) * (kQjl / 128.0f);
   } else {
     k.zw = 0;
     k.gam = 0.f;
@@ -235,6 +258,17 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   const int ratio = Hq / Hkv;
   const int groups = MULTI ? (ratio + 3) / 4 : 1;
   const int64_t base_row = (int64_t)bg * T;
+  // the host bounds T so that a sequence's packed words stay below 4 GB (32-bit offsets)
+  // this (batch, kv head)'s score rows, ratio x T floats (the host bounds ratio * T * 4 < 4 GB)
+  const __amdgpu_buffer_rsrc_t sbuf =
+      buffer_rsrc(scores + ((int64_t)b * Hq + kvh * ratio) * T, (uint32_t)ratio * (uint32_t)T * 4u);
+  KeyBufs<PROD> kb;
+  kb.idx = buffer_rsrc(idx + base_row * (4 * BITS), (uint32_t)T * (16u * BITS));
+  kb.norms = buffer_rsrc(norms + base_row, (uint32_t)T * 4u);
+  if constexpr (PROD) {
+    kb.qbits = buffer_rsrc(qbits + base_row * 4, (uint32_t)T * 16u);
+    kb.rnorms = buffer_rsrc(rnorms + base_row, (uint32_t)T * 4u);
+  }
   const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t ntiles_seq = (T + 15) / 16;
 
@@ -294,7 +328,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
       float mine = reduce_parts(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
       const int h = 4 * hg + g;
       if constexpr (PROD) mine -= gam * (hg == 0 ? kc0 : load_kc(hg));
-      if (valid && h < ratio) scores[((int64_t)b * Hq + kvh * ratio + h) * T + t] = mine;
+      if (valid && h < ratio)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), sbuf,
+                                              ((uint32_t)h * (uint32_t)T + (uint32_t)t) * 4u, 0, 0);
     }
   };
   // Batches of kScoreBatch tiles: every load of a batch is issued before any tile of it is
@@ -305,7 +341,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     KeyTile<BITS, PROD> kt[kScoreBatch];
 #pragma unroll
     for (int u = 0; u < kScoreBatch; ++u)
-      load_key_tile<BITS, PROD>(idx, norms, qbits, rnorms, base_row, T, tile0 + tb + u, nl, g, kt[u]);
+      load_key_tile<BITS, PROD>(kb, (int)(tile0 + tb + u), nl, g, kt[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kScoreBatch; ++u)
