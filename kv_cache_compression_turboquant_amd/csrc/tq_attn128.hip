@@ -235,23 +235,27 @@ struct AttnStep {
   uint32_t vw[2 * VB];
 };
 
+// One sequence's keys, key norms, value norms (from its first row) and value blocks (from its
+// first 32-row block) as buffer resources: each load is the resource plus one 32-bit per-lane
+// offset, and rows outside the sequence read as zero (the kernel masks them).
+struct AttnBufs {
+  __amdgpu_buffer_rsrc_t k, kn, vn, v;
+};
+
 template <int KB, int VB>
-__device__ __forceinline__ void load_attn_step(const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
-                                               const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm,
-                                               int64_t nrows, int64_t blk, int nl, int g, AttnStep<KB, VB>& st) {
+__device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0, int64_t blk_first, int64_t blk,
+                                               int nl, int g, AttnStep<KB, VB>& st) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int64_t r = blk * 32 + tt * 16 + nl;
-    const int64_t rl = r < nrows ? r : nrows - 1;
-    const uint32_t* src = kidx + rl * (4 * KB) + KB * g;
-#pragma unroll
-    for (int j = 0; j < KB; ++j) st.kw[tt][j] = src[j];
-    st.kn[tt] = knorm[rl];
-    st.vn[tt] = vnorm[rl];
+    // may wrap below zero for the first block of a sequence that starts mid-block: such
+    // offsets are past the resource's end and read zero
+    const uint32_t r = (uint32_t)(blk * 32 + tt * 16 + nl - row0);
+    buffer_words<KB>(ab.k, r * (16u * KB) + (uint32_t)(4 * KB * g), st.kw[tt]);
+    st.kn[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.kn, r * 4u, 0, 0));
+    st.vn[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.vn, r * 4u, 0, 0));
   }
-  const uint32_t* vs = vidx + blk * (128 * VB) + 32 * g * VB + 2 * nl * VB;
-#pragma unroll
-  for (int j = 0; j < 2 * VB; ++j) st.vw[j] = vs[j];
+  const uint32_t vb = (uint32_t)(blk - blk_first);
+  buffer_words<2 * VB>(ab.v, (vb * (128u * VB) + (uint32_t)(32 * g * VB + 2 * nl * VB)) * 4u, st.vw);
 }
 
 template <int KB, int VB>
@@ -300,6 +304,12 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
   const int64_t per = (cnt + 3) / 4;
   const int64_t wb = bb + wave * per;
   const int64_t we = wb + per < be ? wb + per : be;
+  // (the host bounds T so that a sequence's words stay below 2 GB: 32-bit offsets)
+  AttnBufs ab;
+  ab.k = buffer_rsrc(kidx + row0 * (4 * KB), (uint32_t)T * (16u * KB));
+  ab.kn = buffer_rsrc(knorm + row0, (uint32_t)T * 4u);
+  ab.vn = buffer_rsrc(vnorm + row0, (uint32_t)T * 4u);
+  ab.v = buffer_rsrc(vidx + blk_first * (128 * VB), (uint32_t)(blk_end - blk_first) * (512u * VB));
 
   // query slots against the centroids' fp16 part (am): rows 0-3 rotated-query hi (heads),
   // 4-7 lo; against the centroid remainders (am2): rows 8-11 hi.  Other rows zero.
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
     AttnStep<KB, VB> st[kAttnBatch];
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)
-      if (b0 + u < we) load_attn_step<KB, VB>(kidx, knorm, vidx, vnorm, nrows, b0 + u, nl, g, st[u]);
+      if (b0 + u < we) load_attn_step<KB, VB>(ab, row0, blk_first, b0 + u, nl, g, st[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)

@@ -155,6 +155,39 @@ __device__ __forceinline__ float reduce_parts(float v0, float v1, float v2, floa
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Raw buffer resource over n bytes at p (untyped dword loads; the hardware range check returns
+// zero for any load at or past n bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+template <int W>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[W]) {
+  if constexpr (W == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (W == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (W == 3) {
+    typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else if constexpr (W == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else {
+    // wider runs in pieces of at most four words
+    static_assert(W <= 8, "at most eight words");
+    uint32_t lo[4], hi[W - 4];
+    buffer_words<4>(r, off, lo);
+    buffer_words<W - 4>(r, off + 16u, hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = lo[j];
+#pragma unroll
+    for (int j = 0; j < W - 4; ++j) w[4 + j] = hi[j];
+  }
+}
+
 }  // namespace
 }  // namespace tq
 
