@@ -33,6 +33,8 @@ from .quantizer import (nearest_index, pack_bits, unpack_bits, pack_token_blocke
                         encode_prod, decode_prod, qjl_matrix, qjl_encode, qjl_correction, scores_mse, scores_prod,
                         quantize_rotated, EncodedMSE, EncodedProd, QJL_CONST)
 from .attention import decode_attention, topk
+from .kv_cache import (cache_rows, append_rows_mse, append_rows_prod, assign_token_blocked,
+                       append_token_blocked_mse, live_rows)
 
 __all__ = [
     "splitmix64", "uniform53", "gaussian", "rademacher",
@@ -42,4 +44,6 @@ __all__ = [
     "decode_prod", "qjl_matrix", "qjl_encode", "qjl_correction", "scores_mse", "scores_prod", "quantize_rotated",
     "EncodedMSE", "EncodedProd", "QJL_CONST",
     "decode_attention", "topk",
+    "cache_rows", "append_rows_mse", "append_rows_prod", "assign_token_blocked",
+    "append_token_blocked_mse", "live_rows",
 ]
