@@ -245,6 +245,52 @@ def bench_other(name, steps, warmup):
         res.update({"bits": b, "encode_v_blocked_ms": enc_v_ms, "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6,
                     "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
                     "kv_positions_per_s": n / at_ms * 1e3})
+    elif name in ("decode", "decodeb4"):
+        # Streaming decode over the long-context cache (batch 4, 8 KV heads, d = 128, GQA 4, K and V
+        # MSE at b bits): prefill the cache up to T0 tokens per sequence, then per step append one
+        # token's key and value per sequence and attend over the whole prefix.
+        cfg = wl.CONFIGS["c4"]
+        b = 2 if name == "decode" else 4
+        t_cap = cfg.T
+        t0 = t_cap - warmup - steps
+        rot = tq.make_rotation(cfg.d, 1)
+        cb = tq.codebook(cfg.d, b)
+        kc = tq.alloc_cache(cfg.B, cfg.hkv, t_cap, cfg.d, b, "mse", device=dev)
+        vc = tq.alloc_cache(cfg.B, cfg.hkv, t_cap, cfg.d, b, "mse", layout="blocked", device=dev)
+        kx = torch.from_numpy(wl.kv_keys(cfg).view(np.int16)).view(torch.bfloat16)
+        vx = torch.from_numpy(wl.kv_values(cfg).view(np.int16)).view(torch.bfloat16)
+        knew = kx[:, :, t0:].permute(2, 0, 1, 3).contiguous().to(dev)   # [steps, B, Hkv, d]
+        vnew = vx[:, :, t0:].permute(2, 0, 1, 3).contiguous().to(dev)
+        kpre = kx[:, :, :t0].contiguous().to(dev)
+        vpre = vx[:, :, :t0].contiguous().to(dev)
+        del kx, vx
+        pre_ms = _timed(lambda i: (tq.cache_append(kc, kpre, 0, cb, rot), tq.cache_append(vc, vpre, 0, cb, rot)), 2, 1)
+        del kpre, vpre
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        out = torch.empty((cfg.B, cfg.hq, cfg.d), device=dev)
+        ws = torch.empty(tq.decode_attn_workspace(cfg.B, cfg.hq, cfg.hkv, t_cap, cfg.d), dtype=torch.uint8, device=dev)
+
+        def append(i):
+            tq.cache_append(kc, knew[i].unsqueeze(2), t0 + i, cb, rot)
+            tq.cache_append(vc, vnew[i].unsqueeze(2), t0 + i, cb, rot)
+
+        def step(i):
+            append(i)
+            tq.decode_attn_cache(q, kc, vc, t0 + i + 1, cb, cb, rot, rot, out=out, ws=ws)
+
+        step_ms = _timed(step, steps, warmup)
+        # the parts alone: appends rewrite the same positions; attention over the full cache
+        app_ms = _timed(append, steps, 0)
+        at_ms = _timed(lambda i: tq.decode_attn_cache(q, kc, vc, t_cap, cb, cb, rot, rot, out=out, ws=ws), 20, 2)
+        n = cfg.B * cfg.hkv * t_cap
+        words = cfg.d * b // 32
+        at_bytes = 2 * n * (words * 4 + 4) + q.numel() * 4 + out.numel() * 4
+        pre_tokens = 2 * cfg.B * cfg.hkv * t0
+        res.update({"bits": b, "cache": [cfg.B, cfg.hkv, t_cap, cfg.d], "prefill_tokens": t0,
+                    "prefill_ms": pre_ms, "prefill_kv_vectors_per_s": pre_tokens / pre_ms * 1e3,
+                    "step_ms": step_ms, "decode_tokens_per_s": cfg.B / step_ms * 1e3,
+                    "append_ms": app_ms, "attn_full_ms": at_ms, "attn_gbs": at_bytes / at_ms / 1e6,
+                    "attn_hbm_frac": at_bytes / at_ms / 1e6 / HBM_PEAK_GBS})
     elif name == "c5":
         cfg = wl.CONFIGS["c5"]
         n, d = cfg.n, cfg.d
@@ -282,7 +328,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4", "c5"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4", "c5", "decode", "decodeb4"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "

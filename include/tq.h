@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -227,6 +227,49 @@ tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, 
                          const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
                          tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
                          void* ws_dev, size_t ws_bytes, void* stream);
+
+/* ---- streaming KV cache ---------------------------------------------------------------
+ * [TQ] KV-cache example (prefill and decode): prefill writes the prompt's compressed keys and
+ * values into the persistent cache; every decode step appends the new token's key and value to
+ * the end of the cache at once, then attends over everything cached.  The section after it:
+ * no online fitting is needed, so a token is quantized and written as soon as it exists.
+ * A cache holds B*H sequences of capacity T_cap tokens each: sequence s = b*H + h owns rows
+ * [s*T_cap, (s+1)*T_cap) of its packed buffers (cache->n == B*H*T_cap), all allocated once by
+ * the caller, whose initial contents do not matter.  Keys: ROWS layout, MSE or prod.  Values:
+ * TOKEN_BLOCKED layout, MSE, with T_cap a multiple of 32 so that every sequence owns whole
+ * blocks.  Only d = 128. */
+
+/* Encodes x_dev [B, H, n_new, d] (dtype dt, row-major) into rows pos .. pos+n_new-1 of every
+ * sequence of *cache, with the rules of tq_encode for b, mode, cb, rot and qjl.  Every other
+ * stored bit of the cache is left as it was, including the fields of other tokens that share a
+ * value block (those fields are cleared and set with atomic operations on disjoint bits), so
+ * appends to disjoint rows may run concurrently.  Appends of fewer than 64 tokens (decode
+ * steps) run one fp32 block per token; longer ones (prefill) run the fused MFMA encode kernels
+ * on whole rows, or on whole value blocks with the partial blocks at either end done per token.
+ * Errors: TQ_EINVAL (null pointers, negative sizes, pos + n_new > T_cap, bits, mode, qjl
+ * handle as for tq_encode); TQ_ESHAPE (cache->n != B*H*T_cap, codebook bits or d, TOKEN_BLOCKED
+ * with T_cap % 32 != 0); TQ_EUNSUPPORTED (d != 128, dtype, B*H > 65535, n_new >= 2^31). */
+tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos,
+                          int64_t T_cap, int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot,
+                          tq_qjl_t qjl, tq_packed* cache, void* stream);
+
+/* tq_scores over the first T rows (0 <= T <= T_cap) of every sequence of a key cache of capacity
+ * T_cap (K->n == B*Hkv*T_cap): scores_dev [B, Hq, T].  Otherwise as tq_scores, with
+ * TQ_EINVAL for T > T_cap. */
+tq_status tq_scores_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap,
+                          const tq_packed* K, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl,
+                          float* scores_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* tq_decode_attn over the first T rows (1 <= T <= T_cap) of every sequence of a key cache and a
+ * value cache of capacity T_cap (a multiple of 32; K->n == V->n == B*Hkv*T_cap).  Workspace:
+ * tq_decode_attn_workspace(B, Hq, Hkv, T, d) bytes (grows with T: size it with T_cap once to
+ * cover every decode step).  Errors as for tq_decode_attn; TQ_EINVAL for T > T_cap; TQ_ESHAPE
+ * for T_cap % 32 != 0. */
+tq_status tq_decode_attn_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap,
+                               const tq_packed* K, const tq_packed* V, tq_codebook_t cb_k,
+                               tq_codebook_t cb_v, tq_rotation_t rot_k, tq_rotation_t rot_v,
+                               float scale, float* out_dev, void* ws_dev, size_t ws_bytes,
+                               void* stream);
 
 /* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
  * with k results per query (query operands, one chunk of scores, the running top-k). */

@@ -19,6 +19,7 @@ __all__ = [
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
+    "KVCache", "alloc_cache", "cache_append", "scores_cache", "decode_attn_cache",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -296,6 +297,64 @@ def decode_attn(q, K, V, Hkv, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws
     check(lib().tq_decode_attn(_dptr(q), B, Hq, Hkv, T, ctypes.byref(kd), ctypes.byref(vd), cb_k.ptr, cb_v.ptr,
                                rot_k.ptr, rot_v.ptr, ctypes.c_float(scale), _dptr(out), _dptr(ws),
                                ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+class KVCache:
+    """A preallocated compressed cache of B*H sequences of capacity t_cap tokens (sequence
+    b*H + h owns rows [(b*H + h) t_cap, (b*H + h + 1) t_cap) of `packed`)."""
+
+    def __init__(self, B, H, t_cap, b, mode, packed):
+        self.B, self.H, self.t_cap, self.b, self.mode, self.packed = B, H, t_cap, b, mode, packed
+
+
+def alloc_cache(B, H, t_cap, d, b, mode="mse", layout="rows", device="cuda"):
+    """Caller-owned cache storage (uninitialised): keys in the rows layout (MSE or prod), values
+    in the token-blocked layout (MSE, t_cap a multiple of 32).  b is the total bit budget."""
+    stage = b - 1 if mode == "prod" else b
+    return KVCache(B, H, t_cap, b, mode, alloc_packed(B * H * t_cap, d, stage, mode, device=device, layout=layout))
+
+
+def cache_append(cache, x, pos, cb, rot, qjl=None):
+    """Encodes x [B, H, n_new, d] (bf16 or fp32, contiguous) into positions pos .. pos+n_new-1 of
+    every sequence of the cache."""
+    B, H, n_new, d = x.shape
+    desc = cache.packed.descriptor()
+    check(lib().tq_cache_append(_dptr(x), _dtype_code(x), B, H, n_new, pos, cache.t_cap, cache.b, MODE[cache.mode],
+                                cb.ptr, rot.ptr, qjl.ptr if qjl is not None else None, ctypes.byref(desc),
+                                _stream()))
+
+
+def scores_cache(q, cache, T, cb, rot, qjl=None, out=None, ws=None):
+    """Raw scores [B, Hq, T] of q [B, Hq, d] against the first T keys of every sequence."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((max(scores_workspace(B, Hq, d), 1),), dtype=torch.uint8, device=q.device)
+    desc = cache.packed.descriptor()
+    check(lib().tq_scores_cache(_dptr(q), B, Hq, cache.H, T, cache.t_cap, ctypes.byref(desc), cb.ptr, rot.ptr,
+                                qjl.ptr if qjl is not None else None, _dptr(out), _dptr(ws),
+                                ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def decode_attn_cache(q, kc, vc, T, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws=None):
+    """Decode attention of q [B, Hq, d] over the first T tokens of a key cache and a value cache."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((max(decode_attn_workspace(B, Hq, kc.H, kc.t_cap, d), 1),), dtype=torch.uint8,
+                         device=q.device)
+    kd, vd = kc.packed.descriptor(), vc.packed.descriptor()
+    check(lib().tq_decode_attn_cache(_dptr(q), B, Hq, kc.H, T, kc.t_cap, ctypes.byref(kd), ctypes.byref(vd), cb_k.ptr,
+                                     cb_v.ptr, rot_k.ptr, rot_v.ptr, ctypes.c_float(scale), _dptr(out), _dptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()))
     return out
 
 

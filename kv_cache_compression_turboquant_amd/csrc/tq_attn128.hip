@@ -1,6 +1,7 @@
 // Value-cache encode in the token-blocked layout and the fused decode attention at d = 128:
 // scores from packed K, online softmax, P V on MFMA in V's rotated domain, split merge and
 // the inverse rotation.
+#include "tq_cache.h"
 #include "tq_decode.h"
 
 namespace tq {
@@ -262,7 +263,7 @@ template <int KB, int VB>
 __global__ __launch_bounds__(256, 3) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
-    const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t nrows,
+    const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t seq_stride,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
   // replicated decode tables (K up to 32 KB, V up to 16 KB) so that three blocks fit a CU
   constexpr int KC = table_copies<KB, true, 32768>();
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_d128(
   const int bh = blockIdx.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int ratio = Hq / Hkv;
-  const int64_t row0 = (int64_t)bh * T, rowE = row0 + T;
+  // sequence bh: rows [bh * seq_stride, bh * seq_stride + T) (seq_stride = T, or a cache's capacity)
+  const int64_t row0 = (int64_t)bh * seq_stride, rowE = row0 + T;
   const int64_t blk_first = row0 >> 5, blk_end = ((rowE - 1) >> 5) + 1;
   const int64_t bb = blk_first + (int64_t)blockIdx.x * spb;
   const int64_t be = bb + spb < blk_end ? bb + spb : blk_end;
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
 }
 
 template <int KB, int VB>
-hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, const tq_packed* K,
                        const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
                        const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale, float* out,
                        void* ws, hipStream_t st) {
@@ -533,7 +535,7 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, const 
   if (spb < kAttnMinSteps) spb = kAttnMinSteps;
   const int nsplit = (int)((steps + spb - 1) / spb);
   hipLaunchKernelGGL((k_attn_d128<KB, VB>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit, (int)spb,
-                     K->idx, K->norms, V->idx, V->norms, K->n, cbk, cbv, scale, part);
+                     K->idx, K->norms, V->idx, V->norms, seq_stride, cbk, cbv, scale, part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(kCombineThreads), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
@@ -582,16 +584,24 @@ size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d) {
   return qbytes + (size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float);
 }
 
-hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
-                              const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
-                              const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale,
-                              float* out, void* ws, hipStream_t st) {
+hipError_t launch_decode_attn_strided(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+                                      const tq_packed* K, const tq_packed* V, const CodebookArgs& cbk,
+                                      const CodebookArgs& cbv, const tq_rotation_s* rot_k, const tq_rotation_s* rot_v,
+                                      float scale, float* out, void* ws, hipStream_t st) {
 #define TQ_ATTN(KB, VB) \
-  if (cbk.bits == KB && cbv.bits == VB) return attn_launch<KB, VB>(q, B, Hq, Hkv, T, K, V, cbk, cbv, rot_k, rot_v, scale, out, ws, st);
+  if (cbk.bits == KB && cbv.bits == VB) \
+    return attn_launch<KB, VB>(q, B, Hq, Hkv, T, seq_stride, K, V, cbk, cbv, rot_k, rot_v, scale, out, ws, st);
   TQ_ATTN(2, 2) TQ_ATTN(4, 4) TQ_ATTN(3, 3) TQ_ATTN(4, 2) TQ_ATTN(2, 4) TQ_ATTN(3, 2) TQ_ATTN(4, 3)
   TQ_ATTN(1, 1) TQ_ATTN(2, 3) TQ_ATTN(3, 4)
 #undef TQ_ATTN
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                              const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
+                              const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale,
+                              float* out, void* ws, hipStream_t st) {
+  return launch_decode_attn_strided(q, B, Hq, Hkv, T, T, K, V, cbk, cbv, rot_k, rot_v, scale, out, ws, st);
 }
 
 }  // namespace tq

@@ -18,6 +18,7 @@
 #include <thread>
 #include <vector>
 
+#include "tq_cache.h"
 #include "tq_internal.h"
 
 namespace {
@@ -816,9 +817,11 @@ static tq_status check_score_heads(int B, int Hq, int Hkv, const char* fn) {
 // 32-bit (at most 64 bytes of packed words per token).
 constexpr int64_t kMaxSeqTokens = int64_t(1) << 25;
 
-static tq_status check_score_keys(int B, int Hkv, int64_t T, const tq_packed* K, tq_codebook_t cb, int d,
-                                  const char* fn) {
+// rows: rows per sequence in K (T for a packed [B, Hkv, T] set, the capacity for a cache).
+static tq_status check_score_keys(int B, int Hkv, int64_t T, int64_t rows, const tq_packed* K, tq_codebook_t cb,
+                                  int d, const char* fn) {
   if (T < 0) return fail(TQ_EINVAL, "%s: negative T", fn);
+  if (rows < T) return fail(TQ_EINVAL, "%s: T=%lld exceeds the capacity %lld", fn, (long long)T, (long long)rows);
   if (T > kMaxSeqTokens)
     return fail(TQ_EUNSUPPORTED, "%s: T=%lld exceeds %lld tokens per sequence", fn, (long long)T,
                 (long long)kMaxSeqTokens);
@@ -826,7 +829,9 @@ static tq_status check_score_keys(int B, int Hkv, int64_t T, const tq_packed* K,
   if (st != TQ_OK) return st;
   if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: keys must use the ROWS layout", fn);
   if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, keys d=%d", fn, cb->d, d);
-  if (K->n != (int64_t)B * Hkv * T) return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*T=%lld", fn, (long long)K->n, (long long)B * Hkv * T);
+  if (K->n != (int64_t)B * Hkv * rows)
+    return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*%lld=%lld", fn, (long long)K->n, (long long)rows,
+                (long long)B * Hkv * rows);
   if (K->mode != TQ_MODE_PROD && K->mode != TQ_MODE_MSE) return fail(TQ_EINVAL, "%s: bad mode", fn);
   if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
   return TQ_OK;
@@ -854,7 +859,7 @@ tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq,
   if (!K || !cb) return fail(TQ_EINVAL, "%s: null argument", fn);
   tq_status st = check_score_heads(B, Hq, Hkv, fn);
   if (st != TQ_OK) return st;
-  st = check_score_keys(B, Hkv, T, K, cb, K->d, fn);
+  st = check_score_keys(B, Hkv, T, T, K, cb, K->d, fn);
   if (st != TQ_OK) return st;
   if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
     return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
@@ -867,16 +872,18 @@ tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq,
                       fn);
 }
 
-tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
-                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
-                    void* ws_dev, size_t ws_bytes, void* stream) {
-  static const char* fn = "tq_scores";
+static tq_status scores_impl(const char* fn, const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t rows,
+                             const tq_packed* K, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
+                             void* ws_dev, size_t ws_bytes, void* stream) {
   if (!K || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
   tq_status st = check_score_heads(B, Hq, Hkv, fn);
   if (st != TQ_OK) return st;
   const int d = rot->d;
-  st = check_score_keys(B, Hkv, T, K, cb, d, fn);
+  st = check_score_keys(B, Hkv, T, rows, K, cb, d, fn);
   if (st != TQ_OK) return st;
+  if (rows > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: capacity %lld exceeds %lld tokens per sequence", fn, (long long)rows,
+                (long long)kMaxSeqTokens);
   if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
     return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
                 (long long)(Hq / Hkv) * T);
@@ -890,9 +897,23 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
   if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
   size_t need = tq::scores_workspace_bytes(B, Hq, d);
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  return check_launch(tq::launch_scores(q_dev, B, Hq, Hkv, T, K, cb->args, rot, qjl, scores_dev, ws_dev,
-                                        as_stream(stream)),
-                      fn);
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = tq::launch_prepare_queries(q_dev, B, Hq, Hkv, rot, K->mode == TQ_MODE_PROD ? qjl : nullptr, ws_dev, hs);
+  if (e == hipSuccess) e = tq::launch_scores_strided(B, Hq, Hkv, T, rows, K, cb->args, scores_dev, ws_dev, hs);
+  return check_launch(e, fn);
+}
+
+tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                    tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
+                    void* ws_dev, size_t ws_bytes, void* stream) {
+  return scores_impl("tq_scores", q_dev, B, Hq, Hkv, T, T, K, cb, rot, qjl, scores_dev, ws_dev, ws_bytes, stream);
+}
+
+tq_status tq_scores_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap, const tq_packed* K,
+                          tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream) {
+  return scores_impl("tq_scores_cache", q_dev, B, Hq, Hkv, T, T_cap, K, cb, rot, qjl, scores_dev, ws_dev, ws_bytes,
+                     stream);
 }
 
 size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d) {
@@ -900,16 +921,20 @@ size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d) {
   return tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
 }
 
-tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
-                         const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
-                         tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
-                         void* ws_dev, size_t ws_bytes, void* stream) {
-  static const char* fn = "tq_decode_attn";
+// rows: rows per sequence in K and V (T for packed [B, Hkv, T] sets, the capacity for a cache,
+// which must then be a multiple of 32 so that every sequence owns whole value blocks).
+static tq_status decode_attn_impl(const char* fn, const float* q_dev, int B, int Hq, int Hkv, int64_t T,
+                                  int64_t rows, bool cache, const tq_packed* K, const tq_packed* V,
+                                  tq_codebook_t cb_k, tq_codebook_t cb_v, tq_rotation_t rot_k, tq_rotation_t rot_v,
+                                  float scale, float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   if (!K || !V || !cb_k || !cb_v || !rot_k || !rot_v) return fail(TQ_EINVAL, "%s: null argument", fn);
   if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (T < 1) return fail(TQ_EINVAL, "%s: attention over an empty cache (T=%lld)", fn, (long long)T);
-  if (T > kMaxSeqTokens)
-    return fail(TQ_EUNSUPPORTED, "%s: T=%lld exceeds %lld tokens per sequence", fn, (long long)T,
+  if (T > rows) return fail(TQ_EINVAL, "%s: T=%lld exceeds the capacity %lld", fn, (long long)T, (long long)rows);
+  if (cache && rows % 32 != 0)
+    return fail(TQ_ESHAPE, "%s: capacity %lld is not a multiple of 32 (value blocks)", fn, (long long)rows);
+  if (rows > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: %lld tokens per sequence exceed %lld", fn, (long long)rows,
                 (long long)kMaxSeqTokens);
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
   const int ratio = Hq / Hkv;
@@ -922,16 +947,76 @@ tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, 
   if (st != TQ_OK) return st;
   if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: K must use the ROWS layout", fn);
   if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED) return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout", fn);
-  const int64_t n = (int64_t)B * Hkv * T;
-  if (K->n != n || V->n != n) return fail(TQ_ESHAPE, "%s: K->n=%lld, V->n=%lld, B*Hkv*T=%lld", fn, (long long)K->n, (long long)V->n, (long long)n);
+  const int64_t n = (int64_t)B * Hkv * rows;
+  if (K->n != n || V->n != n)
+    return fail(TQ_ESHAPE, "%s: K->n=%lld, V->n=%lld, B*Hkv*%lld=%lld", fn, (long long)K->n, (long long)V->n,
+                (long long)rows, (long long)n);
   if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
   if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv above 65535", fn);
   if ((int64_t)B * Hq == 0) return ok();
   if (!q_dev || !out_dev) return fail(TQ_EINVAL, "%s: null q or out", fn);
   size_t need = tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  return check_launch(tq::launch_decode_attn(q_dev, B, Hq, Hkv, T, K, V, cb_k->args, cb_v->args, rot_k, rot_v,
-                                             scale, out_dev, ws_dev, as_stream(stream)),
+  return check_launch(tq::launch_decode_attn_strided(q_dev, B, Hq, Hkv, T, rows, K, V, cb_k->args, cb_v->args, rot_k,
+                                                     rot_v, scale, out_dev, ws_dev, as_stream(stream)),
+                      fn);
+}
+
+tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                         const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                         tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
+                         void* ws_dev, size_t ws_bytes, void* stream) {
+  return decode_attn_impl("tq_decode_attn", q_dev, B, Hq, Hkv, T, T, false, K, V, cb_k, cb_v, rot_k, rot_v, scale,
+                          out_dev, ws_dev, ws_bytes, stream);
+}
+
+tq_status tq_decode_attn_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap,
+                               const tq_packed* K, const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                               tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev, void* ws_dev,
+                               size_t ws_bytes, void* stream) {
+  return decode_attn_impl("tq_decode_attn_cache", q_dev, B, Hq, Hkv, T, T_cap, true, K, V, cb_k, cb_v, rot_k, rot_v,
+                          scale, out_dev, ws_dev, ws_bytes, stream);
+}
+
+tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos, int64_t T_cap,
+                          int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* cache,
+                          void* stream) {
+  static const char* fn = "tq_cache_append";
+  if (!cb || !rot || !cache) return fail(TQ_EINVAL, "%s: null handle or cache", fn);
+  if (B < 0 || H < 0 || n_new < 0 || pos < 0 || T_cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (pos > T_cap - n_new)
+    return fail(TQ_EINVAL, "%s: %lld tokens at position %lld overflow the capacity %lld", fn, (long long)n_new,
+                (long long)pos, (long long)T_cap);
+  if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_EUNSUPPORTED, "%s: dtype must be f32 or bf16", fn);
+  if (mode != TQ_MODE_MSE && mode != TQ_MODE_PROD) return fail(TQ_EINVAL, "%s: bad mode", fn);
+  const int stage = mode == TQ_MODE_PROD ? b - 1 : b;
+  if (stage < 1 || stage > tq::kMaxBits) return fail(TQ_EINVAL, "%s: bits b=%d invalid for this mode", fn, b);
+  if (cb->b != stage) return fail(TQ_ESHAPE, "%s: codebook has %d bits, mode needs %d", fn, cb->b, stage);
+  const int d = rot->d;
+  if (cb->d != d) return fail(TQ_ESHAPE, "%s: codebook d=%d, rotation d=%d", fn, cb->d, d);
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if (mode == TQ_MODE_PROD) {
+    if (!qjl) return fail(TQ_EINVAL, "%s: prod mode needs a qjl handle", fn);
+    if (qjl->d != d) return fail(TQ_ESHAPE, "%s: qjl d=%d", fn, qjl->d);
+    if (qjl->rot_id != rot->id) return fail(TQ_EINVAL, "%s: qjl handle is bound to another rotation", fn);
+  } else if (qjl) {
+    return fail(TQ_EINVAL, "%s: qjl handle given for MSE mode", fn);
+  }
+  if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the encode kernels need an antisymmetric codebook", fn);
+  tq_status st = check_packed(cache, d, stage, mode, fn);
+  if (st != TQ_OK) return st;
+  if (cache->n != (int64_t)B * H * T_cap)
+    return fail(TQ_ESHAPE, "%s: cache->n=%lld but B*H*T_cap=%lld", fn, (long long)cache->n, (long long)B * H * T_cap);
+  if (cache->layout == TQ_LAYOUT_TOKEN_BLOCKED && T_cap % 32 != 0)
+    return fail(TQ_ESHAPE, "%s: a token-blocked cache needs T_cap a multiple of 32 (T_cap=%lld)", fn,
+                (long long)T_cap);
+  if ((int64_t)B * H > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*H=%lld above 65535", fn, (long long)B * H);
+  if (n_new > INT32_MAX) return fail(TQ_EUNSUPPORTED, "%s: n_new above 2^31 - 1", fn);
+  if ((int64_t)B * H * n_new == 0) return ok();
+  if (!x_dev) return fail(TQ_EINVAL, "%s: null input", fn);
+  return check_launch(tq::launch_cache_append(x_dev, dt == TQ_BF16, (int64_t)B * H, n_new, pos, T_cap, rot,
+                                              mode == TQ_MODE_PROD ? qjl : nullptr, cb->args, cache,
+                                              as_stream(stream)),
                       fn);
 }
 

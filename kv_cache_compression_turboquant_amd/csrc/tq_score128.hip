@@ -1,5 +1,6 @@
 // Query prologue (q_rot = R q, q_s = S q once per query head) and the compressed-key score
 // kernel at d = 128, MSE and TurboQuant_prod, with GQA sharing.
+#include "tq_cache.h"
 #include "tq_decode.h"
 
 namespace tq {
@@ -212,7 +213,8 @@ __device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile,
 // kernel carries only the single-group path.
 template <int BITS, bool PROD, bool MULTI>
 __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
-    const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int tiles_per_wave,
+    const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+    int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
     const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
     float* __restrict__ scores) {
@@ -234,7 +236,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int ratio = Hq / Hkv;
   const int groups = MULTI ? (ratio + 3) / 4 : 1;
-  const int64_t base_row = (int64_t)bg * T;
+  // sequence bg: rows [bg * seq_stride, bg * seq_stride + T) (seq_stride = T, or a cache's capacity)
+  const int64_t base_row = (int64_t)bg * seq_stride;
   // the host bounds T so that a sequence's packed words stay below 4 GB (32-bit offsets)
   // this (batch, kv head)'s score rows, ratio x T floats (the host bounds ratio * T * 4 < 4 GB)
   const __amdgpu_buffer_rsrc_t sbuf =
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
 }
 
 template <int BITS, bool PROD, bool MULTI>
-hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, const tq_packed* K, const CodebookArgs& cb,
                          float* scores, const void* ws, hipStream_t st) {
   const int ratio = Hq / Hkv;
   const uint16_t* qws = static_cast<const uint16_t*>(ws);
@@ -352,16 +355,16 @@ hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, const tq_packed* K
   if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
   hipLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
-                     0, st, qws, kconst, Hq, Hkv, T, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
+                     0, st, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
                      PROD ? K->rnorms : nullptr, cb, scores);
   return hipGetLastError();
 }
 
 template <int BITS, bool PROD>
-hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, int64_t S, const tq_packed* K, const CodebookArgs& cb,
                          float* scores, const void* ws, hipStream_t st) {
-  return Hq / Hkv > 4 ? scores_launch_m<BITS, PROD, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
-                      : scores_launch_m<BITS, PROD, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+  return Hq / Hkv > 4 ? scores_launch_m<BITS, PROD, true>(B, Hq, Hkv, T, S, K, cb, scores, ws, st)
+                      : scores_launch_m<BITS, PROD, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
 }
 
 }  // namespace
@@ -388,20 +391,25 @@ hipError_t launch_prepare_queries(const float* q, int B, int Hq, int Hkv, const 
   return launch_qprep128(q, B, Hq, Hkv, rot->rt32_dev, qjl ? qjl->st32_dev : nullptr, qws, kconst, st);
 }
 
-hipError_t launch_scores_prepared(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
-                                  float* scores, const void* ws, hipStream_t st) {
+hipError_t launch_scores_strided(int B, int Hq, int Hkv, int64_t T, int64_t S, const tq_packed* K,
+                                 const CodebookArgs& cb, float* scores, const void* ws, hipStream_t st) {
   const bool prod = K->mode == TQ_MODE_PROD;
   switch (cb.bits) {
-    case 1: return prod ? scores_launch<1, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
-                        : scores_launch<1, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
-    case 2: return prod ? scores_launch<2, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
-                        : scores_launch<2, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
-    case 3: return prod ? scores_launch<3, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
-                        : scores_launch<3, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
-    case 4: return prod ? scores_launch<4, true>(B, Hq, Hkv, T, K, cb, scores, ws, st)
-                        : scores_launch<4, false>(B, Hq, Hkv, T, K, cb, scores, ws, st);
+    case 1: return prod ? scores_launch<1, true>(B, Hq, Hkv, T, S, K, cb, scores, ws, st)
+                        : scores_launch<1, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
+    case 2: return prod ? scores_launch<2, true>(B, Hq, Hkv, T, S, K, cb, scores, ws, st)
+                        : scores_launch<2, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
+    case 3: return prod ? scores_launch<3, true>(B, Hq, Hkv, T, S, K, cb, scores, ws, st)
+                        : scores_launch<3, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
+    case 4: return prod ? scores_launch<4, true>(B, Hq, Hkv, T, S, K, cb, scores, ws, st)
+                        : scores_launch<4, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scores_prepared(int B, int Hq, int Hkv, int64_t T, const tq_packed* K, const CodebookArgs& cb,
+                                  float* scores, const void* ws, hipStream_t st) {
+  return launch_scores_strided(B, Hq, Hkv, T, T, K, cb, scores, ws, st);
 }
 
 hipError_t launch_scores(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(tq):
     for name in names:
         assert hasattr(raw, name), name
         assert name in _binding.SIGNATURES, f"binding lacks {name}"
-    assert tq.lib().tq_abi_version() == 2
+    assert tq.lib().tq_abi_version() == 3
 
 
 def test_splitmix_bit_identical(tq):
@@ -184,3 +184,17 @@ def test_timer_entry_points(tq):
     t = lib.tq_timer_arm()
     assert t == -1 or 0 <= t < 256
     lib.tq_timer_reset()
+
+
+def test_cache_entry_points_validate(tq):
+    """The streaming-cache entry points reject missing handles and descriptors before any launch."""
+    lib = tq.lib()
+    cbh = tq.codebook(128, 3)
+    desc = tq.tq_packed(128, 3, 0, 0, 2 * 64, None, None, None, None)
+    # null rotation / cache
+    assert lib.tq_cache_append(None, 1, 1, 2, 1, 0, 64, 3, 0, cbh.ptr, None, None, ctypes.byref(desc), None) == 1
+    assert lib.tq_cache_append(None, 1, 1, 2, 1, 0, 64, 3, 0, cbh.ptr, None, None, None, None) == 1
+    assert lib.tq_scores_cache(None, 1, 8, 2, 10, 64, ctypes.byref(desc), cbh.ptr, None, None, None, None, 0,
+                               None) == 1
+    assert lib.tq_decode_attn_cache(None, 1, 8, 2, 10, 64, ctypes.byref(desc), ctypes.byref(desc), cbh.ptr, cbh.ptr,
+                                    None, None, ctypes.c_float(1.0), None, None, 0, None) == 1
