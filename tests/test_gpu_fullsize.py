@@ -10,6 +10,9 @@ computes one by one, or by properties that hold at any size:
 * Decode attention, 4 x 131072 tokens x 8 KV heads, K and V MSE at b = 2 and b = 4: two
   (sequence, KV head) groups, all four query heads of each, against oracle attention over the
   group's 131072 packed keys and values.
+* Streaming decode loop on caches of the same shape: a prefill of 131072 - 110 tokens, three
+  single-token appends, attention over the prefix: 2048 sampled prefill rows and every appended
+  row of both caches against the oracle's encode, and two groups' attention.
 * Vector index, 1e6 unit vectors d = 1536, prod b = 4, 1024 queries, top-10: 512 sampled
   database rows against the oracle's encode; for 6 sampled queries the returned scores equal
   the oracle's scores of the returned indices, and over the union of the returned keys and
@@ -154,6 +157,64 @@ def test_decode_attention_full_size_sampled(dev, b):
         vidx = oracle.unpack_token_blocked(vw.reshape(-1, cfg.d * b)[blk0:blk0 + cfg.T // 32], cfg.T, cfg.d, b)
         kn = kn_all[r0:r0 + cfg.T].astype(np.float64)
         vn = vn_all[r0:r0 + cfg.T].astype(np.float64)
+        heads = q[bi:bi + 1, g * ratio:(g + 1) * ratio].astype(np.float64)
+        ref = oracle.decode_attention(heads, kidx[None, None], kn[None, None], vidx[None, None], vn[None, None],
+                                      R128, R128, cb_o, cb_o, 1 / np.sqrt(cfg.d))[0]
+        vmax = np.max(np.linalg.norm(oracle.decode_mse(vidx, vn, R128, cb_o), axis=1))
+        err = np.abs(got[bi, g * ratio:(g + 1) * ratio] - ref)
+        assert np.all(err <= 1e-3 * vmax), (bi, g, float(err.max()), vmax)
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_decode_loop_full_size_sampled(dev, b):
+    """The streaming decode loop as bench.py runs it: caches of 4 x 8 KV heads x 131072 tokens,
+    prefilled to T0 = 131072 - 110 tokens in one append (fused encode on whole blocks, per-token
+    tail), then three single-token decode steps, then attention over T0 + 3 tokens."""
+    cfg = wl.CONFIGS["c4"]
+    t_cap, t0, steps = cfg.T, cfg.T - 110, 3
+    n_seq = cfg.B * cfg.hkv
+    print(f"decode loop: {cfg.B} x {cfg.hkv} x {t_cap}, prefill {t0}, b={b}", flush=True)
+    rot = tq.make_rotation(cfg.d, cfg.rot_seed)
+    cb, cb_o = tq.codebook(cfg.d, b), oracle.codebook(cfg.d, b)
+    kc = tq.alloc_cache(cfg.B, cfg.hkv, t_cap, cfg.d, b, "mse", device=dev)
+    vc = tq.alloc_cache(cfg.B, cfg.hkv, t_cap, cfg.d, b, "mse", layout="blocked", device=dev)
+    kbits, vbits = wl.kv_keys(cfg), wl.kv_values(cfg)
+    as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    tq.cache_append(kc, as_dev(kbits[:, :, :t0]), 0, cb, rot)
+    tq.cache_append(vc, as_dev(vbits[:, :, :t0]), 0, cb, rot)
+    for i in range(steps):
+        tq.cache_append(kc, as_dev(kbits[:, :, t0 + i:t0 + i + 1]), t0 + i, cb, rot)
+        tq.cache_append(vc, as_dev(vbits[:, :, t0 + i:t0 + i + 1]), t0 + i, cb, rot)
+    T = t0 + steps
+    q = wl.kv_queries(cfg)
+    out = tq.decode_attn_cache(torch.from_numpy(q).to(dev), kc, vc, T, cb, cb, rot, rot)
+    torch.cuda.synchronize()
+    kw, vw = to_np_words(kc.packed.idx), to_np_words(vc.packed.idx)
+    kn_all, vn_all = kc.packed.norms.cpu().numpy(), vc.packed.norms.cpu().numpy()
+    rng = np.random.default_rng(107)
+    # sampled prefill rows and every decode-step row, both caches, against the oracle's encode
+    seq = np.concatenate([rng.integers(0, n_seq, 2048), np.repeat(np.arange(n_seq), steps)])
+    tok = np.concatenate([rng.integers(0, t0, 2048), np.tile(np.arange(t0, T), n_seq)])
+    rows = seq * t_cap + tok
+    for bits_, words, norms, blocked in ((kbits, kw, kn_all, False), (vbits, vw, vn_all, True)):
+        x = wl.bf16_bits_to_f32(bits_.reshape(n_seq, t_cap, cfg.d)[seq, tok]).astype(np.float64)
+        enc = oracle.encode_mse(x, R128, cb_o)
+        if blocked:
+            gidx = np.stack([oracle.unpack_token_blocked(words.reshape(-1, cfg.d * b)[r // 32:r // 32 + 1], 32,
+                                                         cfg.d, b)[r % 32] for r in rows])
+        else:
+            gidx = oracle.unpack_bits(words[rows], cfg.d, b)
+        check_indices(gidx, enc.y, cb_o, f"decode loop {'V' if blocked else 'K'} b={b}")
+        np.testing.assert_allclose(norms[rows], enc.norms, rtol=1e-6)
+    got = out.cpu().numpy()
+    ratio = cfg.hq // cfg.hkv
+    for _ in range(2):
+        bi, g = int(rng.integers(0, cfg.B)), int(rng.integers(0, cfg.hkv))
+        r0 = (bi * cfg.hkv + g) * t_cap
+        kidx = oracle.unpack_bits(kw[r0:r0 + T], cfg.d, b)
+        vidx = oracle.unpack_token_blocked(vw.reshape(-1, cfg.d * b)[r0 // 32:(r0 + t_cap) // 32], t_cap, cfg.d, b)[:T]
+        kn = kn_all[r0:r0 + T].astype(np.float64)
+        vn = vn_all[r0:r0 + T].astype(np.float64)
         heads = q[bi:bi + 1, g * ratio:(g + 1) * ratio].astype(np.float64)
         ref = oracle.decode_attention(heads, kidx[None, None], kn[None, None], vidx[None, None], vn[None, None],
                                       R128, R128, cb_o, cb_o, 1 / np.sqrt(cfg.d))[0]
