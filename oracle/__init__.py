@@ -24,7 +24,7 @@ are marked "parity unpinned"; they are pinned only by structural and statistical
 """
 
 from .rng import splitmix64, uniform53, gaussian, rademacher
-from .rotation import (dense_rotation, wht_rotation, sylvester_hadamard,
+from .rotation import (dense_rotation, wht_rotation, block_wht_rotation, sylvester_hadamard,
                        rotation_from_matrix)
 from .codebook import (Codebook, lloyd_max_points, coordinate_weights, codebook,
                        codebook_from_values)
@@ -38,7 +38,7 @@ from .kv_cache import (cache_rows, append_rows_mse, append_rows_prod, assign_tok
 
 __all__ = [
     "splitmix64", "uniform53", "gaussian", "rademacher",
-    "dense_rotation", "wht_rotation", "sylvester_hadamard", "rotation_from_matrix",
+    "dense_rotation", "wht_rotation", "block_wht_rotation", "sylvester_hadamard", "rotation_from_matrix",
     "Codebook", "lloyd_max_points", "coordinate_weights", "codebook", "codebook_from_values",
     "nearest_index", "pack_bits", "unpack_bits", "pack_token_blocked", "unpack_token_blocked", "encode_mse", "decode_mse", "encode_prod",
     "decode_prod", "qjl_matrix", "qjl_encode", "qjl_correction", "scores_mse", "scores_prod", "quantize_rotated",

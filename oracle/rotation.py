@@ -13,6 +13,14 @@ Test infrastructure only (see the package docstring).
   normalisation or ordering; reading: R = (1/sqrt(d)) H_d diag(sigma) with the Sylvester
   Hadamard matrix and Rademacher signs sigma (signs applied before H).  The sign draw is parity
   unpinned; the matrix form is pinned by orthogonality and by its explicit Sylvester entries.
+* Block (group-32) randomized Hadamard rotation: "TurboQuant 和 RotorQuant 的真相", chapter 3
+  (splitting the 128 coordinates into 4 groups of 32, each rotated on its own, tried as a faster
+  rotation) and chapter 5 (small orthogonal blocks instead of a full-rank d x d transform);
+  "Sub-byte KV cache quantization with TurboQuant", engineering path (structured rotations in
+  place of the dense matrix).  Reading: R = (1/sqrt(g)) blockdiag(H_g, ..., H_g) diag(sigma)
+  with the same Sylvester H and Rademacher sigma as the full WHT, g = 32, for any d that is a
+  multiple of g (so also d that are not powers of two).  Pinned by orthogonality, by its block
+  structure, by equality with the full WHT when d = g, and by a per-group butterfly transform.
 """
 
 import numpy as np
@@ -45,6 +53,19 @@ def wht_rotation(d, seed):
     """Explicit matrix of the randomized Hadamard rotation (1/sqrt(d)) H diag(sigma)."""
     sigma = rademacher(seed, d)
     return sylvester_hadamard(d) * sigma[None, :] / np.sqrt(d)
+
+
+def block_wht_rotation(d, seed, group=32):
+    """Explicit matrix of the block randomized Hadamard rotation
+    (1/sqrt(g)) blockdiag(H_g, ..., H_g) diag(sigma); d must be a multiple of g."""
+    if group < 1 or d % group != 0:
+        raise ValueError("d must be a multiple of the group size")
+    sigma = rademacher(seed, d)
+    h = sylvester_hadamard(group)
+    r = np.zeros((d, d))
+    for k in range(0, d, group):
+        r[k:k + group, k:k + group] = h
+    return r * sigma[None, :] / np.sqrt(group)
 
 
 def rotation_from_matrix(m):

@@ -107,3 +107,27 @@ def test_wht_rotation_matches_butterfly():
     sigma = oracle.rademacher(1, d)
     u = np.random.default_rng(1).standard_normal((5, d))
     np.testing.assert_allclose(u @ r.T, _fwht(u * sigma) / np.sqrt(d), atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [128, 96, 1536])
+def test_block_wht_rotation_structure(d):
+    """Block (group-32) randomized Hadamard: orthogonal, zero outside the diagonal blocks, each
+    block the Sylvester H_32 times its slice of the signs, and equal to a per-group butterfly."""
+    g = 32
+    r = oracle.block_wht_rotation(d, 3, g)
+    assert np.max(np.abs(r.T @ r - np.eye(d))) <= 1e-13
+    sigma = oracle.rademacher(3, d)
+    blocks = np.arange(d) // g
+    assert np.all(r[blocks[:, None] != blocks[None, :]] == 0.0)
+    h = oracle.sylvester_hadamard(g)
+    for k in range(0, d, g):
+        np.testing.assert_array_equal(r[k:k + g, k:k + g], h * sigma[None, k:k + g] / np.sqrt(g))
+    u = np.random.default_rng(2).standard_normal((4, d))
+    ref = _fwht((u * sigma).reshape(4, d // g, g)).reshape(4, d) / np.sqrt(g)
+    np.testing.assert_allclose(u @ r.T, ref, atol=1e-13)
+
+
+def test_block_wht_reduces_to_full_wht():
+    np.testing.assert_array_equal(oracle.block_wht_rotation(32, 5, 32), oracle.wht_rotation(32, 5))
+    with pytest.raises(ValueError):
+        oracle.block_wht_rotation(100, 1, 32)
