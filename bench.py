@@ -194,9 +194,9 @@ def bench_other(name, steps, warmup):
     from kv_cache_compression_turboquant_amd import workloads as wl
     dev = torch.device("cuda:0")
     res = {"config": name}
-    if name in ("c3", "c3wht"):
+    if name in ("c3", "c3wht", "c3bwht"):
         cfg = wl.CONFIGS["c3"]
-        kind = "wht" if name == "c3wht" else "dense"
+        kind = {"c3": "dense", "c3wht": "wht", "c3bwht": "block_wht"}[name]
         n = cfg.B * cfg.hkv * cfg.T
         keys = torch.from_numpy(wl.kv_keys(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
         q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
@@ -328,7 +328,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c4b2", "c4b4", "c5", "decode", "decodeb4"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "

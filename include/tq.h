@@ -56,7 +56,11 @@ typedef enum tq_status {
 } tq_status;
 
 typedef enum tq_density { TQ_DENSITY_BETA = 0, TQ_DENSITY_GAUSS = 1 } tq_density;
-typedef enum tq_rot_kind { TQ_ROT_DENSE = 0, TQ_ROT_WHT = 1 } tq_rot_kind;
+/* Rotation kinds: DENSE = Q of the QR of a seeded Gaussian matrix; WHT = (1/sqrt(d)) H_d diag(sigma)
+ * (d a power of two); BLOCK_WHT = (1/sqrt(32)) blockdiag(H_32, ..., H_32) diag(sigma), d a multiple
+ * of 32 ([RQ] chapter 3: the 128 coordinates split into 4 groups of 32, each rotated on its own;
+ * chapter 5: small orthogonal blocks instead of a full-rank transform). */
+typedef enum tq_rot_kind { TQ_ROT_DENSE = 0, TQ_ROT_WHT = 1, TQ_ROT_BLOCK_WHT = 2 } tq_rot_kind;
 typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 typedef enum tq_mode { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1 } tq_mode;
 /* Storage layout of packed indices.  ROWS: row r is the LSB-first stream of vector r's d
@@ -111,8 +115,10 @@ tq_status tq_host_codebook(int d, int b, tq_density dens, double* centroids_host
                            double* thresholds_host);
 /* Rotation matrix R (d x d, row-major, y = R u): DENSE = Q of the QR of the seeded Gaussian
  * matrix with a non-negative triangular diagonal ([TQ] official step 1; [FP] rotation);
- * WHT = (1/sqrt(d)) H_d diag(sigma), Sylvester H, Rademacher sigma ([RQ] chapter 3).
- * Errors: TQ_EUNSUPPORTED for WHT with d not a power of two; TQ_EINVAL for d < 2. */
+ * WHT = (1/sqrt(d)) H_d diag(sigma), Sylvester H, Rademacher sigma ([RQ] chapter 3);
+ * BLOCK_WHT = the same with H_32 blocks on the diagonal and 1/sqrt(32).
+ * Errors: TQ_EUNSUPPORTED for WHT with d not a power of two or BLOCK_WHT with d not a multiple
+ * of 32; TQ_EINVAL for d < 2 or a bad kind. */
 tq_status tq_host_rotation(int d, uint64_t seed, tq_rot_kind kind, double* r_host);
 /* QJL matrix S (d x d, row-major, i.i.d. N(0,1) from stream `seed`). */
 tq_status tq_host_qjl_matrix(int d, uint64_t seed, double* s_host);

@@ -14,7 +14,7 @@ TQ_OK, TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EDEVICE = range(6)
 STATUS_NAMES = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EUNSUPPORTED",
                 4: "TQ_ENOMEM", 5: "TQ_EDEVICE"}
 DENSITY = {"beta": 0, "gauss": 1}
-ROT_KIND = {"dense": 0, "wht": 1}
+ROT_KIND = {"dense": 0, "wht": 1, "block_wht": 2}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE = {"mse": 0, "prod": 1}
 LAYOUT = {"rows": 0, "blocked": 1}

@@ -206,6 +206,17 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 #ifndef TQ_ATTN_BATCH
 #define TQ_ATTN_BATCH 2
 #endif
+// LDS budgets of the replicated K (split) and V decode tables, and the blocks per CU the kernel is
+// built for: full replication of both tables needs 64 KB, which fits two blocks per CU, not three.
+#ifndef TQ_ATTN_KBUDGET
+#define TQ_ATTN_KBUDGET 32768
+#endif
+#ifndef TQ_ATTN_VBUDGET
+#define TQ_ATTN_VBUDGET 16384
+#endif
+#ifndef TQ_ATTN_BLOCKS
+#define TQ_ATTN_BLOCKS 3
+#endif
 constexpr int kAttnMinSteps = 16;
 constexpr int kAttnBatch = TQ_ATTN_BATCH;  // 32-token steps loaded together
 constexpr int kAttnRounds = TQ_ATTN_ROUNDS;
@@ -260,14 +271,14 @@ __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0,
 }
 
 template <int KB, int VB>
-__global__ __launch_bounds__(256, 3) void k_attn_d128(
+__global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t seq_stride,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
   // replicated decode tables (K up to 32 KB, V up to 16 KB) so that three blocks fit a CU
-  constexpr int KC = table_copies<KB, true, 32768>();
-  constexpr int VC = table_copies<VB, false, 16384>();
+  constexpr int KC = table_copies<KB, true, TQ_ATTN_KBUDGET>();
+  constexpr int VC = table_copies<VB, false, TQ_ATTN_VBUDGET>();
   using DK = DecodeTable<KB, true, KC>;
   using DV = DecodeTable<VB, false, VC>;
   // the K table's storage is reused for the block's merge buffer once every wave has finished

@@ -152,6 +152,9 @@ void qr_rotation(int d, const double* g, double* r_out) {
 
 bool is_pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 
+// Group size of the block Hadamard rotation (TQ_ROT_BLOCK_WHT).
+constexpr int kBlockWhtGroup = 32;
+
 void hadamard_rotation(int d, uint64_t seed, double* r_out) {
   const double inv = 1.0 / std::sqrt((double)d);
   for (int j = 0; j < d; ++j) {
@@ -159,6 +162,23 @@ void hadamard_rotation(int d, uint64_t seed, double* r_out) {
     for (int i = 0; i < d; ++i) {
       int par = __builtin_popcount((unsigned)(i & j)) & 1;
       r_out[(size_t)i * d + j] = (par ? -1.0 : 1.0) * sigma * inv;
+    }
+  }
+}
+
+// Block randomized Hadamard: (1/sqrt(g)) blockdiag(H_g, ...) diag(sigma), the signs drawn as for
+// the full transform; d a multiple of g.
+void block_hadamard_rotation(int d, int g, uint64_t seed, double* r_out) {
+  const double inv = 1.0 / std::sqrt((double)g);
+  for (int j = 0; j < d; ++j) {
+    double sigma = (draw(seed, (uint64_t)j) >> 63) ? -1.0 : 1.0;
+    for (int i = 0; i < d; ++i) {
+      double v = 0.0;
+      if (i / g == j / g) {
+        int par = __builtin_popcount((unsigned)((i % g) & (j % g))) & 1;
+        v = (par ? -1.0 : 1.0) * sigma * inv;
+      }
+      r_out[(size_t)i * d + j] = v;
     }
   }
 }
@@ -360,12 +380,14 @@ tq_status finish_rotation(tq_rotation_s* r) {
   if (st != TQ_OK) return st;
   if (d == tq::kFragD) {
     std::vector<uint16_t> frag, fragt;
-    if (r->kind == TQ_ROT_WHT) {
-      // sqrt(d) R = H diag(sigma) has entries +-1: exact in bf16, one pass, scale after.
-      build_fragments(r->r.data(), std::sqrt((double)d), frag);
-      build_fragments_t(r->r.data(), std::sqrt((double)d), fragt);
+    if (r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT) {
+      // sqrt(g) R = H diag(sigma) (block diagonal for BLOCK_WHT, g = its group; g = d otherwise)
+      // has entries 0 and +-1: exact in bf16, one pass, scale after.
+      const double g = std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup));
+      build_fragments(r->r.data(), g, frag);
+      build_fragments_t(r->r.data(), g, fragt);
       r->passes = 1;
-      r->post_scale = (float)(1.0 / std::sqrt((double)d));
+      r->post_scale = (float)(1.0 / g);
     } else {
       build_fragments(r->r.data(), 1.0, frag);
       build_fragments_t(r->r.data(), 1.0, fragt);
@@ -378,11 +400,12 @@ tq_status finish_rotation(tq_rotation_s* r) {
     if (st != TQ_OK) return st;
   } else if (general_d(d)) {
     std::vector<uint16_t> frag;
-    const bool wht = r->kind == TQ_ROT_WHT;
-    // WHT: sqrt(d) R has entries +-1, exact in bf16: one pass, scaled after the product.
-    build_fragments_g(r->r.data(), d, wht ? std::sqrt((double)d) : 1.0, frag);
+    const bool wht = r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT;
+    // (block) WHT: sqrt(g) R has entries 0 and +-1, exact in bf16: one pass, scaled after the product.
+    const double g = std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup));
+    build_fragments_g(r->r.data(), d, wht ? g : 1.0, frag);
     r->passes = wht ? 1 : 2;
-    r->post_scale = wht ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+    r->post_scale = wht ? (float)(1.0 / g) : 1.0f;
     st = upload(frag, &r->gfrag_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
   }
@@ -536,6 +559,12 @@ tq_status tq_host_rotation(int d, uint64_t seed, tq_rot_kind kind, double* r_hos
   if (kind == TQ_ROT_WHT) {
     if (!is_pow2(d)) return fail(TQ_EUNSUPPORTED, "tq_host_rotation: Hadamard needs d = 2^k (d=%d)", d);
     hadamard_rotation(d, seed, r_host);
+    return ok();
+  }
+  if (kind == TQ_ROT_BLOCK_WHT) {
+    if (d % kBlockWhtGroup != 0)
+      return fail(TQ_EUNSUPPORTED, "tq_host_rotation: block Hadamard needs d a multiple of %d (d=%d)", kBlockWhtGroup, d);
+    block_hadamard_rotation(d, kBlockWhtGroup, seed, r_host);
     return ok();
   }
   if (kind != TQ_ROT_DENSE) return fail(TQ_EINVAL, "tq_host_rotation: bad kind");

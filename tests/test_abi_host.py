@@ -88,6 +88,13 @@ def test_wht_rotation_matches_oracle(tq):
         np.testing.assert_array_equal(tq.host_rotation(d, 1, "wht"), oracle.wht_rotation(d, 1))
 
 
+def test_block_wht_rotation_matches_oracle(tq):
+    for d in (32, 96, 128, 1536):
+        np.testing.assert_array_equal(tq.host_rotation(d, 3, "block_wht"), oracle.block_wht_rotation(d, 3, 32))
+    with pytest.raises(tq.TQError):
+        tq.host_rotation(100, 1, "block_wht")
+
+
 def test_qjl_matrix(tq):
     np.testing.assert_allclose(tq.host_qjl_matrix(128, 2), oracle.qjl_matrix(128, 2), rtol=1e-14, atol=1e-14)
 
