@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
 // ---------------------------------------------------------------------------------------
 // Launch shape (tuning defaults; overridable at build time).
 #ifndef TQ_SCORE_BATCH
-#define TQ_SCORE_BATCH 4
+#define TQ_SCORE_BATCH 8
 #endif
 #ifndef TQ_SCORE_ROUNDS
 #define TQ_SCORE_ROUNDS 1
@@ -252,25 +252,26 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t ntiles_seq = (T + 15) / 16;
 
-  // A operands for head group 0 (kept in registers).
-  auto load_a = [&](int hg, u32x4 (&am)[4], u32x4 (&aq)[4]) {
-    const int slot = nl;             // A row
-    const int hl = slot & 3;         // head within the group
-    const int part = slot >> 2;      // 0 rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo
+  // A operand for head group 0 (kept in registers): lane (n, g) holds row n = 4 part + head
+  // (part 0 rot hi, 1 rot lo, 2 sketch hi, 3 sketch lo), contraction slots 8 g .. 8 g + 7.  One
+  // register set feeds both products: in the key product rows 8-15 (sketch) meet the centroids,
+  // and in the sign product rows 0-7 (rotated query) meet the signs; those result rows are
+  // discarded, since each lane keeps the rows of its own half (g < 2: rows 0-7 of the key
+  // product; g >= 2: rows 8-15 of the sign product).  MSE zeroes the sketch rows.
+  auto load_a = [&](int hg, u32x4 (&a)[4]) {
+    const int hl = nl & 3;           // head within the group
+    const int part = nl >> 2;
     const int h = 4 * hg + hl;
-    const bool live = h < ratio;
-    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (live ? h : 0)) * 4 + part) * 128 + 32 * g;
+    const bool live = h < ratio && (PROD || part < 2);
+    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (h < ratio ? h : 0)) * 4 + part) * 128 + 32 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
-      if (!live) v = u32x4{0u, 0u, 0u, 0u};
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      am[s] = part < 2 ? v : z;
-      aq[s] = (PROD && part >= 2) ? v : z;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
+      a[s] = live ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  u32x4 am0[4], aq0[4];
-  load_a(0, am0, aq0);
+  u32x4 a0[4];
+  load_a(0, a0);
   // sketch constant K of the lane's head (4 hg + g) after the reduction
   auto load_kc = [&](int hg) -> float {
     const int h = 4 * hg + g;
@@ -291,18 +292,23 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS, TC>(cur.w, s, tabl);
     if constexpr (PROD) sign_operand(cur.zw, bz);
     for (int hg = 0; hg < groups; ++hg) {
-      u32x4 am[4], aq[4];
+      u32x4 a[4];
       if (!MULTI || hg == 0) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) { am[s] = am0[s]; aq[s] = aq0[s]; }
+        for (int s = 0; s < 4; ++s) a[s] = a0[s];
       } else {
-        load_a(hg, am, aq);
+        load_a(hg, a);
       }
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        acc = mfma_f16(am[s], bk[s], acc);
-        if constexpr (PROD) acc = mfma_f16(aq[s], bz[s], acc);
+        acc = mfma_f16(a[s], bk[s], acc);
+        if constexpr (PROD) accz = mfma_f16(a[s], bz[s], accz);
+      }
+      if constexpr (PROD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = g < 2 ? acc[r] : accz[r];
       }
       const float sc = g < 2 ? nrm : 2.f * gam;
       float mine = reduce_parts(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
