@@ -324,21 +324,33 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   ab.vn = buffer_rsrc(vnorm + row0, (uint32_t)T * 4u);
   ab.v = buffer_rsrc(vidx + blk_first * (128 * VB), (uint32_t)(blk_end - blk_first) * (512u * VB));
 
-  // query slots against the centroids' fp16 part (am): rows 0-3 rotated-query hi (heads),
-  // 4-7 lo; against the centroid remainders (am2): rows 8-11 hi.  Other rows zero.
-  u32x4 am[4], am2[4];
+  // A operand of the key product, in the split-slot order of decode_split_slot (each table
+  // entry's centroids and remainders side by side): rows 0-3 (heads) carry the rotated query's
+  // fp16 hi part against both halves, rows 4-7 its lo part against the centroids only (the lo x
+  // remainder term is below fp32 rounding); other rows zero.
+  using KS = SplitSlot<KB>;
+  u32x4 ak[8];
   {
     const int hl = nl & 3, prt = nl >> 2;
-    const bool live = hl < ratio && prt < 3;
-    const int src_part = prt == 1 ? 1 : 0;
-    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (hl < ratio ? hl : 0)) * 4 + src_part) * 128 + 32 * g;
+    const bool live = hl < ratio && prt < 2;
+    const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (hl < ratio ? hl : 0)) * 4 + (prt == 1 ? 1 : 0)) * 128 + 32 * g;
+    uint32_t qw[16];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * s);
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      am[s] = (live && prt < 2) ? v : z;
-      am2[s] = (live && prt == 2) ? v : z;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qw[4 * s + k] = live ? v[k] : 0u;
     }
+    auto qhalf = [&](int c) -> uint32_t { return (qw[c >> 1] >> (16 * (c & 1))) & 0xffffu; };
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int p0 = 8 * j + 2 * k, p1 = p0 + 1;
+        const uint32_t lo = (KS::half(p0) == 0 || prt == 0) ? qhalf(KS::coord(p0)) : 0u;
+        const uint32_t hi = (KS::half(p1) == 0 || prt == 0) ? qhalf(KS::coord(p1)) : 0u;
+        ak[j][k] = lo | (hi << 16);
+      }
   }
 
   float m_run = -INFINITY, l_part = 0.f;
@@ -356,12 +368,7 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
       svv[tt] = cur.vn[tt];
       f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 khi, klo;
-        decode8_2<KB, KC>(cur.kw[tt], 8 * KB * s, ktabl, khi, klo);
-        d = mfma_f16(am[s], khi, d);
-        d = mfma_f16(am2[s], klo, d);
-      }
+      for (int j = 0; j < 8; ++j) d = mfma_f16(ak[j], decode_split_slot<KB, KC>(cur.kw[tt], j, ktabl), d);
       const float mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
       lg[tt] = (valid && g < ratio) ? mine * scale : -INFINITY;
     }

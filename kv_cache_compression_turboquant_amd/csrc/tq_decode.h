@@ -70,7 +70,7 @@ __device__ __forceinline__ u32x4 decode8(const uint32_t (&w)[N], int off, const 
 }
 
 // Split-precision table: each entry holds the PER fp16 centroids followed by the PER fp16
-// remainders c - fp16(c), so one read yields both B operands (hi, lo).
+// remainders c - fp16(c) (read whole by decode_split_slot).
 template <int BITS, int COPIES>
 __device__ __forceinline__ void build_table2(uint8_t* tab, const float* cent32) {
   using DT = DecodeTable<BITS, true, COPIES>;
@@ -88,35 +88,33 @@ __device__ __forceinline__ void build_table2(uint8_t* tab, const float* cent32) 
   }
 }
 
-// (hi and lo are read separately, each straight into its operand registers: reading an entry
-// whole and splitting it costs register moves.)
+// Split-table operand with each entry's hi and lo values side by side in the contraction: the
+// lane's decoded stream lists, field after field, the PER fp16 centroids of the field's
+// coordinates, then their PER remainders; instruction j takes stream positions 8 j .. 8 j + 7,
+// which are whole entries (PER <= 4) or half an entry (PER = 8), so the LDS reads land in the
+// operand registers as they are.  SplitSlot gives the coordinate and half of a position; the
+// other operand must follow the same order.
+template <int BITS>
+struct SplitSlot {
+  static constexpr int PER = (BITS == 3 ? 6 : 8) / BITS;
+  // local coordinate (0..31) and half (0: centroid, 1: remainder) of stream position p (0..63)
+  __host__ __device__ static constexpr int coord(int p) { return (p / (2 * PER)) * PER + p % PER; }
+  __host__ __device__ static constexpr int half(int p) { return (p / PER) & 1; }
+};
+
 template <int BITS, int COPIES, int N>
-__device__ __forceinline__ void decode8_2(const uint32_t (&w)[N], int off, const uint8_t* tabl, u32x4& hi, u32x4& lo) {
-  constexpr int S = DecodeTable<BITS, true, COPIES>::STRIDE;
-  constexpr int H = DecodeTable<BITS, true, COPIES>::PER * 2;  // bytes of an entry's hi part
-  if constexpr (BITS == 1) {
-    const uint8_t* e = tabl + get_bits(w, off, 8) * S;
-    hi = *reinterpret_cast<const u32x4*>(e);
-    lo = *reinterpret_cast<const u32x4*>(e + H);
-  } else if constexpr (BITS == 2) {
-    const uint32_t f = get_bits(w, off, 16);
-    const uint8_t* ea = tabl + (f & 0xffu) * S;
-    const uint8_t* eb = tabl + (f >> 8) * S;
-    const u32x2 ha = *reinterpret_cast<const u32x2*>(ea);
-    const u32x2 hb = *reinterpret_cast<const u32x2*>(eb);
-    const u32x2 la = *reinterpret_cast<const u32x2*>(ea + H);
-    const u32x2 lb = *reinterpret_cast<const u32x2*>(eb + H);
-    hi = u32x4{ha[0], ha[1], hb[0], hb[1]};
-    lo = u32x4{la[0], la[1], lb[0], lb[1]};
+__device__ __forceinline__ u32x4 decode_split_slot(const uint32_t (&w)[N], int j, const uint8_t* tabl) {
+  using DT = DecodeTable<BITS, true, COPIES>;
+  constexpr int S = DT::STRIDE, F = DT::F, PER = DT::PER;
+  if constexpr (PER == 4) {
+    return *reinterpret_cast<const u32x4*>(tabl + get_bits(w, F * j, F) * S);
+  } else if constexpr (PER == 2) {
+    const uint32_t f = get_bits(w, 2 * F * j, 2 * F);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(tabl + (f & ((1u << F) - 1u)) * S);
+    const u32x2 c = *reinterpret_cast<const u32x2*>(tabl + (f >> F) * S);
+    return u32x4{a[0], a[1], c[0], c[1]};
   } else {
-    const uint32_t f = get_bits(w, off, BITS == 3 ? 24 : 32);
-    constexpr int FW = BITS == 3 ? 6 : 8;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* e = tabl + ((f >> (FW * j)) & ((1u << FW) - 1u)) * S;
-      hi[j] = *reinterpret_cast<const uint32_t*>(e);
-      lo[j] = *reinterpret_cast<const uint32_t*>(e + H);
-    }
+    return *reinterpret_cast<const u32x4*>(tabl + get_bits(w, F * (j >> 1), F) * S + 16 * (j & 1));
   }
 }
 
