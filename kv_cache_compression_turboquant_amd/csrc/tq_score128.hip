@@ -73,6 +73,16 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
   const int h0 = kvh * ratio;
   const int j = threadIdx.x & 127, p = threadIdx.x >> 7;
   const int nmat = st ? 2 : 1;
+  // The thread's slice of R^T and S^T column j does not depend on the queries: its loads are
+  // issued before the queries are staged, so the two memory latencies overlap.
+  const int k0 = p * KP;
+  float rv[KP], sv[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) rv[k] = rt[(k0 + k) * 128 + j];
+  if (st) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) sv[k] = st[(k0 + k) * 128 + j];
+  }
   // blockIdx.y takes every gridDim.y-th group of HG heads (one group per block at launch)
   for (int hc = HG * blockIdx.y; hc < ratio; hc += HG * gridDim.y) {
     const int nh = ratio - hc < HG ? ratio - hc : HG;
@@ -82,23 +92,14 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
       qs[hh][j] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
     }
     __syncthreads();
-    const int k0 = p * KP;
     float ar[HG], as[HG];
 #pragma unroll
     for (int i = 0; i < HG; ++i) ar[i] = as[i] = 0.f;
-    {
-      float rv[KP];
 #pragma unroll
-      for (int k = 0; k < KP; ++k) rv[k] = rt[(k0 + k) * 128 + j];
+    for (int k = 0; k < KP; ++k)
 #pragma unroll
-      for (int k = 0; k < KP; ++k)
-#pragma unroll
-        for (int i = 0; i < HG; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
-    }
+      for (int i = 0; i < HG; ++i) ar[i] = fmaf(rv[k], qs[i][k0 + k], ar[i]);
     if (st) {
-      float sv[KP];
-#pragma unroll
-      for (int k = 0; k < KP; ++k) sv[k] = st[(k0 + k) * 128 + j];
 #pragma unroll
       for (int k = 0; k < KP; ++k)
 #pragma unroll
