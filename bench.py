@@ -171,6 +171,94 @@ def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
                       f"and scored by their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
 
 
+def _cpu_info():
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cpu = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    return int(threads), cpu
+
+
+def cpu_baseline_decode(cfg, b, t_cap, budget_s=10.0):
+    """The oracle on a bounded sample of the decode loop: one decode step of one (sequence, KV
+    head) group (append the new key and value, then attention of its query heads over a prefix of
+    the cache), repeated on growing prefixes until the budget is spent; scaled to decode tokens/s
+    of the full step (every group at the full context length)."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    threads, cpu = _cpu_info()
+    rot = oracle.dense_rotation(cfg.d, cfg.rot_seed)
+    cb = oracle.codebook(cfg.d, b)
+    ratio = cfg.hq // cfg.hkv
+    T = 8192
+    kx = wl.bf16_bits_to_f32(wl.kv_keys(cfg, T=T, B=1)[0, 0]).astype(np.float64)
+    vx = wl.bf16_bits_to_f32(wl.kv_values(cfg, T=T, B=1)[0, 0]).astype(np.float64)
+    q = wl.kv_queries(cfg)[0:1, :ratio].astype(np.float64)
+    ke, ve = oracle.encode_mse(kx, rot, cb), oracle.encode_mse(vx, rot, cb)
+    tokens = 0
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        n = T - 1 - (steps % 64)
+        new_k = oracle.encode_mse(kx[n:n + 1], rot, cb)
+        new_v = oracle.encode_mse(vx[n:n + 1], rot, cb)
+        kidx = np.concatenate([ke.idx[:n], new_k.idx])[None, None]
+        vidx = np.concatenate([ve.idx[:n], new_v.idx])[None, None]
+        kn = np.concatenate([ke.norms[:n], new_k.norms])[None, None]
+        vn = np.concatenate([ve.norms[:n], new_v.norms])[None, None]
+        oracle.decode_attention(q, kidx, kn, vidx, vn, rot, rot, cb, cb, 1 / np.sqrt(cfg.d))
+        tokens += n + 1
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_token_group = dt / tokens                       # seconds per cached token of one group
+    step_s = per_token_group * t_cap * cfg.B * cfg.hkv  # one full decode step, every group
+    return {"value": cfg.B / step_s, "unit": "decode tokens/s (4 sequences per step)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} single-token decode steps of one (sequence, KV head) group over prefixes of "
+                      f"{T - 64}..{T} tokens (append key and value, attention of its {ratio} query heads) in "
+                      f"{dt:.1f} s, scaled to {cfg.B} x {cfg.hkv} groups x {t_cap} tokens; numpy fp64; {cpu}"}
+
+
+def cpu_baseline_prod(cfg, kind, budget_s=10.0):
+    """The oracle on a bounded sample of the prod workload: 4096-key chunks of one KV head slab
+    encoded (TurboQuant_prod b = 4) and scored by their query heads; keys/s and scores/s."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    threads, cpu = _cpu_info()
+    rot = {"dense": oracle.dense_rotation(cfg.d, 1), "wht": oracle.wht_rotation(cfg.d, 1),
+           "block_wht": oracle.block_wht_rotation(cfg.d, 1, 32)}[kind]
+    smat = oracle.qjl_matrix(cfg.d, 2)
+    cb = oracle.codebook(cfg.d, cfg.bits - 1)
+    ratio = cfg.hq // cfg.hkv
+    x = wl.bf16_bits_to_f32(wl.kv_keys(cfg, T=4096, B=1)[0, 0]).astype(np.float64)
+    q = wl.kv_queries(cfg)[0, :ratio].astype(np.float64)
+    keys = scores = 0
+    t0 = time.perf_counter()
+    while True:
+        encp = oracle.encode_prod(x, rot, cb, smat)
+        s = oracle.scores_prod(q, encp, rot, cb, smat)
+        keys += x.shape[0]
+        scores += s.size
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": scores / dt, "unit": "scores/s (prod encode + score of the sampled keys)", "cores": threads,
+            "kind": "oracle", "encode_vectors_per_s": keys / dt,
+            "sample": f"{keys} keys (4096-key chunks of one KV head slab, {kind} rotation) encoded and scored by "
+                      f"their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
+
+
 def _timed(fn, steps, warmup):
     """Mean ms of fn() over `steps` calls, HIP events on the current stream."""
     import torch
@@ -186,7 +274,7 @@ def _timed(fn, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def bench_other(name, steps, warmup):
+def bench_other(name, steps, warmup, cpu_budget=0.0):
     """Per-kernel timing of the other workloads (prod scores, decode attention): not the
     headline line; reports algorithmic GB/s against the HBM peak."""
     import torch
@@ -217,6 +305,8 @@ def bench_other(name, steps, warmup):
                     "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
                     "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
+        if cpu_budget > 0:
+            res["cpu_baseline"] = cpu_baseline_prod(cfg, kind, cpu_budget)
     elif name in ("c4b2", "c4b4"):
         cfg = wl.CONFIGS["c4"]
         b = 2 if name == "c4b2" else 4
@@ -291,6 +381,8 @@ def bench_other(name, steps, warmup):
                     "step_ms": step_ms, "decode_tokens_per_s": cfg.B / step_ms * 1e3,
                     "append_ms": app_ms, "attn_full_ms": at_ms, "attn_gbs": at_bytes / at_ms / 1e6,
                     "attn_hbm_frac": at_bytes / at_ms / 1e6 / HBM_PEAK_GBS})
+        if cpu_budget > 0:
+            res["cpu_baseline"] = cpu_baseline_decode(cfg, b, t_cap, cpu_budget)
     elif name == "c5":
         cfg = wl.CONFIGS["c5"]
         n, d = cfg.n, cfg.d
@@ -353,7 +445,7 @@ def main():
         print("bench.py: no HIP device", file=sys.stderr)
         sys.exit(1)
     if args.config != "c2":
-        bench_other(args.config, args.steps, args.warmup)
+        bench_other(args.config, args.steps, args.warmup, 0.0 if args.no_cpu_baseline else args.cpu_budget)
         return
     dev = torch.device("cuda:0")
     cfg = wl.CONFIGS["c2"]
