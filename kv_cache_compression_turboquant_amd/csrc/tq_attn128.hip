@@ -287,8 +287,11 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
   __shared__ float kcent[16];
   __shared__ _Float16 vcent[16];
-  // weights strip, rows padded to 48 floats: the 4 lanes sharing a key index land in 2 banks, not 1
-  __shared__ __attribute__((aligned(16))) float wl[4][4][48];
+  // Weights strip of each wave in fp16: part 0 the weights rounded to fp16, part 1 their
+  // remainders, part 2 zeros (the operand rows that carry nothing); a row per head, 32 tokens
+  // padded to 40 halves (80 bytes), so the 16-byte reads of different rows fall in distinct banks.
+  constexpr int kWRow = 40;
+  __shared__ __attribute__((aligned(16))) uint16_t wh[4][3][4][kWRow];
   __shared__ float mm[4][4], ll[4][4];
   if (threadIdx.x < 16) {
     kcent[threadIdx.x] = cbk.c[threadIdx.x];
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   __syncthreads();
   build_table2<KB, KC>(ktab, kcent);
   build_table<VB, VC>(vtab, vcent);
+  for (int i = threadIdx.x; i < 4 * 4 * kWRow; i += blockDim.x) wh[i / (4 * kWRow)][2][(i / kWRow) % 4][i % kWRow] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -353,6 +357,7 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
       }
   }
 
+  const uint16_t* wrow = &wh[wave][(nl >> 2) < 2 ? (nl >> 2) : 2][nl & 3][8 * g];
   float m_run = -INFINITY, l_part = 0.f;
   f32x4 acc[8];
 #pragma unroll
@@ -382,8 +387,17 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     const float w1 = lg[1] == -INFINITY ? 0.f : __expf(lg[1] - m_new);
     l_part = fmaf(l_part, alpha, w0 + w1);
     m_run = m_new;
-    wl[wave][g][nl] = w0 * svv[0];
-    wl[wave][g][16 + nl] = w1 * svv[1];
+    {
+      // the P V operand in fp16 hi + lo (round to nearest), formed once by the lane that owns the
+      // weight: token nl and 16 + nl of head g
+      const float p0 = w0 * svv[0], p1 = w1 * svv[1];
+      const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+      const _Float16 r0 = (_Float16)(p0 - (float)h0), r1 = (_Float16)(p1 - (float)h1);
+      wh[wave][0][g][nl] = __builtin_bit_cast(uint16_t, h0);
+      wh[wave][0][g][16 + nl] = __builtin_bit_cast(uint16_t, h1);
+      wh[wave][1][g][nl] = __builtin_bit_cast(uint16_t, r0);
+      wh[wave][1][g][16 + nl] = __builtin_bit_cast(uint16_t, r1);
+    }
     if (__any(alpha < 1.f)) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -395,23 +409,9 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // A operand: rows 0-3 weight hi per head, 4-7 weight lo, 8-15 zero; tokens 8 g .. 8 g + 7
-    u32x4 aw;
-    {
-      const int hm = nl & 3, prt = nl >> 2;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(&wl[wave][hm][8 * g]);
-      const f32x4 c2 = *reinterpret_cast<const f32x4*>(&wl[wave][hm][8 * g + 4]);
-      const float v[8] = {a[0], a[1], a[2], a[3], c2[0], c2[1], c2[2], c2[3]};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // pack-and-convert pairs (round toward zero; the remainder carries what hi drops)
-        const auto hp = __builtin_amdgcn_cvt_pkrtz(v[2 * j], v[2 * j + 1]);
-        const auto lp = __builtin_amdgcn_cvt_pkrtz(v[2 * j] - (float)hp[0], v[2 * j + 1] - (float)hp[1]);
-        const uint32_t hi = __builtin_bit_cast(uint32_t, hp);
-        const uint32_t lo = __builtin_bit_cast(uint32_t, lp);
-        aw[j] = prt == 0 ? hi : (prt == 1 ? lo : 0u);
-      }
-    }
+    // A operand: rows 0-3 the weights' fp16 part per head, 4-7 their remainders, 8-15 zero;
+    // tokens 8 g .. 8 g + 7, one read from the lane's fixed row of the strip
+    const u32x4 aw = *reinterpret_cast<const u32x4*>(wrow);
     // B operand: the value chunks of octet g at coordinates 8 n .. 8 n + 7
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, decode8<VB, VC>(cur.vw, 8 * VB * c, vtabl), acc[c]);
