@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void k_encode_vblock_d128(
 #define TQ_ATTN_ROUNDS 1
 #endif
 #ifndef TQ_ATTN_BATCH
-#define TQ_ATTN_BATCH 2
+#define TQ_ATTN_BATCH 1
 #endif
 // LDS budgets of the replicated K (split) and V decode tables, and the blocks per CU the kernel is
 // built for: full replication of both tables needs 64 KB, which fits two blocks per CU, not three.
