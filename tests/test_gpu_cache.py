@@ -245,3 +245,74 @@ def test_cache_errors(dev, rot):
     rows = oracle.live_rows(2, 64, 8).reshape(-1)
     assert np.all(kc.packed.norms.cpu().numpy()[rows] == 0.0)
     assert np.all(oracle.unpack_bits(to_np_words(kc.packed.idx)[rows], 128, 2) == 2)
+
+
+@pytest.mark.parametrize("hkv,hq,mode", [(2, 16, "prod"), (2, 16, "mse"), (4, 4, "mse"), (2, 4, "mse")])
+def test_scores_over_cache_gqa(dev, rot, hkv, hq, mode):
+    """Scores over a capacity-strided cache at GQA ratios 8 (several head groups per key), 1 and 2."""
+    B = 1
+    x, kt = _tokens(B, hkv, WRITTEN, "k")
+    b = 4 if mode == "prod" else 3
+    stage = b - 1 if mode == "prod" else b
+    cb, cbo = tq.codebook(128, stage), oracle.codebook(128, stage)
+    qjl = tq.make_qjl(128, 2, rot) if mode == "prod" else None
+    kc = tq.alloc_cache(B, hkv, T_CAP, 128, b, mode, device=dev)
+    _fill(kc, 600)
+    _run_plan(kc, kt, dev, cb, rot, qjl)
+    q = wl.gaussian((B, hq, 128), 14)
+    T = 150
+    sc = tq.scores_cache(torch.from_numpy(q).to(dev), kc, T, cb, rot, qjl)
+    torch.cuda.synchronize()
+    rows = oracle.live_rows(B * hkv, T_CAP, T).reshape(-1)
+    p = kc.packed
+    idx = oracle.unpack_bits(to_np_words(p.idx)[rows], 128, stage)
+    norms = p.norms.cpu().numpy().astype(np.float64)[rows]
+    gs = sc.cpu().numpy()
+    ratio = hq // hkv
+    for g in range(hkv):
+        sl = slice(g * T, (g + 1) * T)
+        heads = slice(g * ratio, (g + 1) * ratio)
+        qh = q[0, heads].astype(np.float64)
+        if mode == "prod":
+            sub = oracle.EncodedProd(mse=oracle.EncodedMSE(idx=idx[sl], words=None, norms=norms[sl], y=None),
+                                     z=unpack_z(to_np_words(p.qjl)[rows][sl], 128), qjl_words=None,
+                                     gamma=p.rnorms.cpu().numpy().astype(np.float64)[rows][sl], proj=None)
+            ref = oracle.scores_prod(qh, sub, R, cbo, S_MAT)
+        else:
+            ref = oracle.scores_mse(qh, idx[sl], norms[sl], R, cbo)
+        tol = 1e-3 * np.linalg.norm(qh, axis=1)[:, None] * norms[sl][None, :]
+        assert np.all(np.abs(gs[0, heads] - ref) <= tol), (g, mode)
+
+
+@pytest.mark.parametrize("hkv,hq", [(2, 2), (2, 4)])
+def test_decode_over_cache_gqa_and_fp32_values(dev, rot, hkv, hq):
+    """Attention over the cache at GQA ratios 1 and 2, with the values appended from fp32."""
+    B, kb, vb = 1, 3, 2
+    xk, kt = _tokens(B, hkv, WRITTEN, "k")
+    xv, vt = _tokens(B, hkv, WRITTEN, "v")
+    cbk, cbv = tq.codebook(128, kb), tq.codebook(128, vb)
+    cbko, cbvo = oracle.codebook(128, kb), oracle.codebook(128, vb)
+    kc = tq.alloc_cache(B, hkv, T_CAP, 128, kb, "mse", device=dev)
+    vc = tq.alloc_cache(B, hkv, T_CAP, 128, vb, "mse", layout="blocked", device=dev)
+    _fill(kc, 700)
+    _fill(vc, 800)
+    _run_plan(kc, kt, dev, cbk, rot)
+    _run_plan(vc, vt, dev, cbv, rot, dtype=torch.float32)
+    q = wl.gaussian((B, hq, 128), 15)
+    out = tq.decode_attn_cache(torch.from_numpy(q).to(dev), kc, vc, WRITTEN, cbk, cbv, rot, rot)
+    torch.cuda.synchronize()
+    rows = oracle.live_rows(B * hkv, T_CAP, WRITTEN).reshape(-1)
+    vidx_all = oracle.unpack_token_blocked(to_np_words(vc.packed.idx), B * hkv * T_CAP, 128, vb)
+    check_indices(vidx_all[rows], oracle.encode_mse(xv.reshape(-1, 128), R, cbvo).y, cbvo, "fp32 values")
+    kidx, kn = _prefix(to_np_words(kc.packed.idx), kc.packed.norms.cpu().numpy(), B * hkv, WRITTEN, kb, False)
+    vidx, vn = vidx_all[rows], vc.packed.norms.cpu().numpy().astype(np.float64)[rows]
+    ref = oracle.decode_attention(q.astype(np.float64), kidx.reshape(B, hkv, WRITTEN, 128),
+                                  kn.reshape(B, hkv, WRITTEN), vidx.reshape(B, hkv, WRITTEN, 128),
+                                  vn.reshape(B, hkv, WRITTEN), R, R, cbko, cbvo, 1 / np.sqrt(128))
+    got = out.cpu().numpy()
+    ratio = hq // hkv
+    for g in range(hkv):
+        sl = slice(g * WRITTEN, (g + 1) * WRITTEN)
+        vmax = np.max(np.linalg.norm(oracle.decode_mse(vidx[sl], vn[sl], R, cbvo), axis=1))
+        err = np.max(np.abs(got[0, g * ratio:(g + 1) * ratio] - ref[0, g * ratio:(g + 1) * ratio]))
+        assert err <= 1e-3 * vmax, (g, err, vmax)
