@@ -44,12 +44,21 @@ __global__ __launch_bounds__(128) void k_cache_append_d128(
     __syncthreads();
     return red[slot][0] + red[slot][1];
   };
+  // (m v)_j with m read column-wise (m[i * 128 + j]) and v in LDS: the thread's 128 loads are all
+  // issued before the first product, so the sum waits out one memory latency, not one per batch.
+  auto column_dot = [&](const float* __restrict__ m, const float* v) -> float {
+    float c[128];
+#pragma unroll
+    for (int i = 0; i < 128; ++i) c[i] = m[i * 128 + j];
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 128; ++i) a = fmaf(c[i], v[i], a);
+    return a;
+  };
   va[j] = xv;
   if (!BLOCKED && j < W) words[j] = 0u;
   const float s = sqrtf(block_sum(xv * xv, 0));  // (its barrier also publishes va and words)
-  float acc = 0.f;
-#pragma unroll 16
-  for (int i = 0; i < 128; ++i) acc = fmaf(rt32[i * 128 + j], va[i], acc);
+  const float acc = column_dot(rt32, va);
   const float y = s > 0.f ? acc / s : 0.f;
   const uint32_t k = bucketize<BITS>(y, cb);
 
@@ -78,14 +87,10 @@ __global__ __launch_bounds__(128) void k_cache_append_d128(
     const float r = s * (y - cb.c[k]);
     vb[j] = r;
     const float gamma = sqrtf(block_sum(r * r, 1));  // (publishes vb)
-    float ro = 0.f;  // (R^T r)_j: the residual in the original domain
-#pragma unroll 16
-    for (int i = 0; i < 128; ++i) ro = fmaf(r32[i * 128 + j], vb[i], ro);
+    const float ro = column_dot(r32, vb);  // (R^T r)_j: the residual in the original domain
     va[j] = ro;      // every thread finished reading va in the rotation (barrier above)
     __syncthreads();
-    float pr = 0.f;  // (S r)_j
-#pragma unroll 16
-    for (int i = 0; i < 128; ++i) pr = fmaf(st32[i * 128 + j], va[i], pr);
+    const float pr = column_dot(st32, va);  // (S r)_j
     const uint64_t z = __ballot(pr >= 0.f);
     if (lane == 0) {
       qbits[row * 4 + 2 * wave] = (uint32_t)z;
