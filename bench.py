@@ -383,6 +383,21 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "attn_hbm_frac": at_bytes / at_ms / 1e6 / HBM_PEAK_GBS})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_decode(cfg, b, t_cap, cpu_budget)
+    elif name == "peaks":
+        # Achievable HBM rates on this machine, for reading the fractions against a measured ceiling as
+        # well as the 8 TB/s spec: a plain device copy (reads and writes) and a read-only sum of
+        # 1 GiB, both torch's own kernels, buffers far larger than the last-level cache.
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        f = src.view(torch.float32)
+        out = torch.empty((), dtype=torch.float32, device=dev)
+        copy_ms = _timed(lambda i: dst.copy_(src), steps, warmup)
+        read_ms = _timed(lambda i: torch.sum(f, dim=0, out=out), steps, warmup)
+        res.update({"bytes": nbytes, "copy_ms": copy_ms, "copy_gbs": 2 * nbytes / copy_ms / 1e6,
+                    "copy_frac": 2 * nbytes / copy_ms / 1e6 / HBM_PEAK_GBS,
+                    "read_ms": read_ms, "read_gbs": nbytes / read_ms / 1e6,
+                    "read_frac": nbytes / read_ms / 1e6 / HBM_PEAK_GBS})
     elif name == "c5":
         cfg = wl.CONFIGS["c5"]
         n, d = cfg.n, cfg.d
@@ -420,7 +435,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4", "peaks"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "
