@@ -55,7 +55,10 @@ __device__ __forceinline__ void sign_operand(uint32_t z, u32x4 (&bz)[4]) {
 // ---------------------------------------------------------------------------------------
 constexpr int kQprepParts = 8;
 constexpr int kQprepThreads = 128 * kQprepParts;
-constexpr int kQprepHeads = 2;  // query heads per pass (bounds the live LDS operands per thread)
+#ifndef TQ_QPREP_HEADS
+#define TQ_QPREP_HEADS 2
+#endif
+constexpr int kQprepHeads = TQ_QPREP_HEADS;  // query heads per block pass (bounds the live LDS operands per thread)
 
 __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restrict__ q, int Hq, int ratio,
                                                             const float* __restrict__ rt,
