@@ -354,15 +354,14 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         kpre = kx[:, :, :t0].contiguous().to(dev)
         vpre = vx[:, :, :t0].contiguous().to(dev)
         del kx, vx
-        pre_ms = _timed(lambda i: (tq.cache_append(kc, kpre, 0, cb, rot), tq.cache_append(vc, vpre, 0, cb, rot)), 2, 1)
+        pre_ms = _timed(lambda i: tq.kv_append(kc, vc, kpre, vpre, 0, cb, cb, rot, rot), 2, 1)
         del kpre, vpre
         q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
         out = torch.empty((cfg.B, cfg.hq, cfg.d), device=dev)
         ws = torch.empty(tq.decode_attn_workspace(cfg.B, cfg.hq, cfg.hkv, t_cap, cfg.d), dtype=torch.uint8, device=dev)
 
         def append(i):
-            tq.cache_append(kc, knew[i].unsqueeze(2), t0 + i, cb, rot)
-            tq.cache_append(vc, vnew[i].unsqueeze(2), t0 + i, cb, rot)
+            tq.kv_append(kc, vc, knew[i].unsqueeze(2), vnew[i].unsqueeze(2), t0 + i, cb, cb, rot, rot)
 
         def step(i):
             append(i)

@@ -259,6 +259,17 @@ tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t 
                           int64_t T_cap, int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot,
                           tq_qjl_t qjl, tq_packed* cache, void* stream);
 
+/* A decode step's appends to both caches in one call: keys k_dev and values v_dev [B, H, n_new, d]
+ * (dtype dt) into rows pos .. pos+n_new-1 of a key cache K (ROWS layout, MSE, b_k bits, cb_k,
+ * rot_k) and a value cache V (TOKEN_BLOCKED layout, MSE, b_v bits, cb_v, rot_v) of the same
+ * geometry, with the results of two tq_cache_append calls.  Appends of fewer than 64 tokens run
+ * both caches in one launch (for the (b_k, b_v) pairs tq_decode_attn takes; others in two).
+ * Errors: those of tq_cache_append for either cache; TQ_EUNSUPPORTED for the wrong layouts. */
+tq_status tq_kv_append(const void* k_dev, const void* v_dev, tq_dtype dt, int B, int H, int64_t n_new,
+                       int64_t pos, int64_t T_cap, int b_k, int b_v, tq_codebook_t cb_k,
+                       tq_codebook_t cb_v, tq_rotation_t rot_k, tq_rotation_t rot_v, tq_packed* K,
+                       tq_packed* V, void* stream);
+
 /* tq_scores over the first T rows (0 <= T <= T_cap) of every sequence of a key cache of capacity
  * T_cap (K->n == B*Hkv*T_cap): scores_dev [B, Hq, T].  Otherwise as tq_scores, with
  * TQ_EINVAL for T > T_cap. */

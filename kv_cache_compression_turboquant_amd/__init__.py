@@ -19,7 +19,7 @@ __all__ = [
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
-    "KVCache", "alloc_cache", "cache_append", "scores_cache", "decode_attn_cache",
+    "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -323,6 +323,17 @@ def cache_append(cache, x, pos, cb, rot, qjl=None):
     check(lib().tq_cache_append(_dptr(x), _dtype_code(x), B, H, n_new, pos, cache.t_cap, cache.b, MODE[cache.mode],
                                 cb.ptr, rot.ptr, qjl.ptr if qjl is not None else None, ctypes.byref(desc),
                                 _stream()))
+
+
+def kv_append(kc, vc, k, v, pos, cb_k, cb_v, rot_k, rot_v):
+    """Appends keys k and values v [B, H, n_new, d] (same dtype, contiguous) at position pos of a
+    key cache (rows, MSE) and a value cache (token-blocked, MSE) in one call."""
+    B, H, n_new, d = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise TQError(2, "keys and values must have the same shape and dtype")
+    kd, vd = kc.packed.descriptor(), vc.packed.descriptor()
+    check(lib().tq_kv_append(_dptr(k), _dptr(v), _dtype_code(k), B, H, n_new, pos, kc.t_cap, kc.b, vc.b, cb_k.ptr,
+                             cb_v.ptr, rot_k.ptr, rot_v.ptr, ctypes.byref(kd), ctypes.byref(vd), _stream()))
 
 
 def scores_cache(q, cache, T, cb, rot, qjl=None, out=None, ws=None):

@@ -78,6 +78,8 @@ SIGNATURES = {
     "tq_prepare_queries": (_I, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "tq_scores_prepared": (_I, [_P, _SZ, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P]),
     "tq_scores": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _SZ, _P]),
+    "tq_kv_append": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, ctypes.POINTER(tq_packed),
+                          ctypes.POINTER(tq_packed), _P]),
     "tq_cache_append": (_I, [_P, _I, _I, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P, ctypes.POINTER(tq_packed), _P]),
     "tq_scores_cache": (_I, [_P, _I, _I, _I, _I64, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _SZ, _P]),
     "tq_decode_attn_cache": (_I, [_P, _I, _I, _I, _I64, _I64, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed),

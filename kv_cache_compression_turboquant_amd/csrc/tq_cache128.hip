@@ -21,9 +21,9 @@ namespace {
 // read coalesced (the transposed ones where the sum runs over rows).
 // ---------------------------------------------------------------------------------------
 template <int BITS, bool PROD, bool BLOCKED, bool BF16IN>
-__global__ __launch_bounds__(128) void k_cache_append_d128(
+__device__ __forceinline__ void append_token(
     const void* __restrict__ x, int64_t x_tokens, int64_t x_first, int64_t pos, int64_t t_cap,
-    const float* __restrict__ rt32, const float* __restrict__ r32, const float* __restrict__ st32, CodebookArgs cb,
+    const float* __restrict__ rt32, const float* __restrict__ r32, const float* __restrict__ st32, const CodebookArgs& cb,
     uint32_t* __restrict__ idx, float* __restrict__ norms, uint32_t* __restrict__ qbits, float* __restrict__ rnorms) {
   constexpr int W = 4 * BITS;  // words per row
   __shared__ float va[128], vb[128];
@@ -104,6 +104,44 @@ __global__ __launch_bounds__(128) void k_cache_append_d128(
   }
 }
 
+template <int BITS, bool PROD, bool BLOCKED, bool BF16IN>
+__global__ __launch_bounds__(128) void k_cache_append_d128(
+    const void* __restrict__ x, int64_t x_tokens, int64_t x_first, int64_t pos, int64_t t_cap,
+    const float* __restrict__ rt32, const float* __restrict__ r32, const float* __restrict__ st32, CodebookArgs cb,
+    uint32_t* __restrict__ idx, float* __restrict__ norms, uint32_t* __restrict__ qbits, float* __restrict__ rnorms) {
+  append_token<BITS, PROD, BLOCKED, BF16IN>(x, x_tokens, x_first, pos, t_cap, rt32, r32, st32, cb, idx, norms, qbits,
+                                            rnorms);
+}
+
+// One decode step's key and value appends in one launch: blockIdx.z = 0 appends to the key cache
+// (rows layout, MSE), 1 to the value cache (token-blocked, MSE); the two halves run side by side.
+template <int KB, int VB, bool BF16IN>
+__global__ __launch_bounds__(128) void k_kv_append_d128(
+    const void* __restrict__ xk, const void* __restrict__ xv, int64_t x_tokens, int64_t pos, int64_t t_cap,
+    const float* __restrict__ rtk, const float* __restrict__ rtv, CodebookArgs cbk, CodebookArgs cbv,
+    uint32_t* __restrict__ kidx, float* __restrict__ knorms, uint32_t* __restrict__ vidx, float* __restrict__ vnorms) {
+  if (blockIdx.z == 0)
+    append_token<KB, false, false, BF16IN>(xk, x_tokens, 0, pos, t_cap, rtk, nullptr, nullptr, cbk, kidx, knorms,
+                                           nullptr, nullptr);
+  else
+    append_token<VB, false, true, BF16IN>(xv, x_tokens, 0, pos, t_cap, rtv, nullptr, nullptr, cbv, vidx, vnorms,
+                                          nullptr, nullptr);
+}
+
+template <int KB, int VB>
+hipError_t kv_append_small(const void* xk, const void* xv, bool bf16, int64_t n_seq, int64_t n_new, int64_t pos,
+                           int64_t t_cap, const tq_rotation_s* rk, const tq_rotation_s* rv, const CodebookArgs& cbk,
+                           const CodebookArgs& cbv, const tq_packed* K, const tq_packed* V, hipStream_t st) {
+  const dim3 grid((unsigned)n_new, (unsigned)n_seq, 2);
+  if (bf16)
+    hipLaunchKernelGGL((k_kv_append_d128<KB, VB, true>), grid, dim3(128), 0, st, xk, xv, n_new, pos, t_cap,
+                       rk->rt32_dev, rv->rt32_dev, cbk, cbv, K->idx, K->norms, V->idx, V->norms);
+  else
+    hipLaunchKernelGGL((k_kv_append_d128<KB, VB, false>), grid, dim3(128), 0, st, xk, xv, n_new, pos, t_cap,
+                       rk->rt32_dev, rv->rt32_dev, cbk, cbv, K->idx, K->norms, V->idx, V->norms);
+  return hipGetLastError();
+}
+
 template <int BITS, bool PROD, bool BLOCKED>
 hipError_t append_small(const void* x, bool bf16, int64_t n_seq, int64_t x_tokens, int64_t x_first, int64_t count,
                         int64_t pos, int64_t t_cap, const tq_rotation_s* rot, const tq_qjl_s* qjl,
@@ -148,6 +186,27 @@ hipError_t append_range(const void* x, bool bf16, int64_t n_seq, int64_t n_new, 
 }
 
 }  // namespace
+
+hipError_t launch_kv_append(const void* xk, const void* xv, bool bf16, int64_t n_seq, int64_t n_new, int64_t pos,
+                            int64_t t_cap, const tq_rotation_s* rk, const tq_rotation_s* rv, const CodebookArgs& cbk,
+                            const CodebookArgs& cbv, const tq_packed* K, const tq_packed* V, hipStream_t st) {
+  if (n_new >= kAppendFusedMin) {
+    // long appends: each cache on its own (fused encode kernels on whole rows and blocks)
+    hipError_t e = launch_cache_append(xk, bf16, n_seq, n_new, pos, t_cap, rk, nullptr, cbk, K, st);
+    if (e != hipSuccess) return e;
+    return launch_cache_append(xv, bf16, n_seq, n_new, pos, t_cap, rv, nullptr, cbv, V, st);
+  }
+#define TQ_KVA(KB_, VB_) \
+  if (cbk.bits == KB_ && cbv.bits == VB_) \
+    return kv_append_small<KB_, VB_>(xk, xv, bf16, n_seq, n_new, pos, t_cap, rk, rv, cbk, cbv, K, V, st);
+  TQ_KVA(2, 2) TQ_KVA(4, 4) TQ_KVA(3, 3) TQ_KVA(4, 2) TQ_KVA(2, 4) TQ_KVA(3, 2) TQ_KVA(4, 3)
+  TQ_KVA(1, 1) TQ_KVA(2, 3) TQ_KVA(3, 4)
+#undef TQ_KVA
+  // other bit pairs: one launch per cache
+  hipError_t e = launch_cache_append(xk, bf16, n_seq, n_new, pos, t_cap, rk, nullptr, cbk, K, st);
+  if (e != hipSuccess) return e;
+  return launch_cache_append(xv, bf16, n_seq, n_new, pos, t_cap, rv, nullptr, cbv, V, st);
+}
 
 hipError_t launch_cache_append(const void* x, bool bf16, int64_t n_seq, int64_t n_new, int64_t pos, int64_t t_cap,
                                const tq_rotation_s* rot, const tq_qjl_s* qjl, const CodebookArgs& cb,

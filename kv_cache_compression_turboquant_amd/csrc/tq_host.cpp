@@ -1007,10 +1007,10 @@ tq_status tq_decode_attn_cache(const float* q_dev, int B, int Hq, int Hkv, int64
                           scale, out_dev, ws_dev, ws_bytes, stream);
 }
 
-tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos, int64_t T_cap,
-                          int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* cache,
-                          void* stream) {
-  static const char* fn = "tq_cache_append";
+// Argument checks of an append into one cache (shared by tq_cache_append and tq_kv_append).
+static tq_status check_cache_append(const char* fn, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos,
+                                    int64_t T_cap, int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot,
+                                    tq_qjl_t qjl, const tq_packed* cache) {
   if (!cb || !rot || !cache) return fail(TQ_EINVAL, "%s: null handle or cache", fn);
   if (B < 0 || H < 0 || n_new < 0 || pos < 0 || T_cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (pos > T_cap - n_new)
@@ -1041,11 +1041,38 @@ tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t 
                 (long long)T_cap);
   if ((int64_t)B * H > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*H=%lld above 65535", fn, (long long)B * H);
   if (n_new > INT32_MAX) return fail(TQ_EUNSUPPORTED, "%s: n_new above 2^31 - 1", fn);
+  return TQ_OK;
+}
+
+tq_status tq_cache_append(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos, int64_t T_cap,
+                          int b, tq_mode mode, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, tq_packed* cache,
+                          void* stream) {
+  static const char* fn = "tq_cache_append";
+  tq_status st = check_cache_append(fn, dt, B, H, n_new, pos, T_cap, b, mode, cb, rot, qjl, cache);
+  if (st != TQ_OK) return st;
   if ((int64_t)B * H * n_new == 0) return ok();
   if (!x_dev) return fail(TQ_EINVAL, "%s: null input", fn);
   return check_launch(tq::launch_cache_append(x_dev, dt == TQ_BF16, (int64_t)B * H, n_new, pos, T_cap, rot,
                                               mode == TQ_MODE_PROD ? qjl : nullptr, cb->args, cache,
                                               as_stream(stream)),
+                      fn);
+}
+
+tq_status tq_kv_append(const void* k_dev, const void* v_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos,
+                       int64_t T_cap, int b_k, int b_v, tq_codebook_t cb_k, tq_codebook_t cb_v, tq_rotation_t rot_k,
+                       tq_rotation_t rot_v, tq_packed* K, tq_packed* V, void* stream) {
+  static const char* fn = "tq_kv_append";
+  tq_status st = check_cache_append(fn, dt, B, H, n_new, pos, T_cap, b_k, TQ_MODE_MSE, cb_k, rot_k, nullptr, K);
+  if (st != TQ_OK) return st;
+  st = check_cache_append(fn, dt, B, H, n_new, pos, T_cap, b_v, TQ_MODE_MSE, cb_v, rot_v, nullptr, V);
+  if (st != TQ_OK) return st;
+  if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: the key cache must use the ROWS layout", fn);
+  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED)
+    return fail(TQ_EUNSUPPORTED, "%s: the value cache must use the TOKEN_BLOCKED layout", fn);
+  if ((int64_t)B * H * n_new == 0) return ok();
+  if (!k_dev || !v_dev) return fail(TQ_EINVAL, "%s: null input", fn);
+  return check_launch(tq::launch_kv_append(k_dev, v_dev, dt == TQ_BF16, (int64_t)B * H, n_new, pos, T_cap, rot_k,
+                                           rot_v, cb_k->args, cb_v->args, K, V, as_stream(stream)),
                       fn);
 }
 

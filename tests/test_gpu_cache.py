@@ -316,3 +316,32 @@ def test_decode_over_cache_gqa_and_fp32_values(dev, rot, hkv, hq):
         vmax = np.max(np.linalg.norm(oracle.decode_mse(vidx[sl], vn[sl], R, cbvo), axis=1))
         err = np.max(np.abs(got[0, g * ratio:(g + 1) * ratio] - ref[0, g * ratio:(g + 1) * ratio]))
         assert err <= 1e-3 * vmax, (g, err, vmax)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 2), (4, 3), (1, 4)])
+def test_kv_append_matches_separate_appends(dev, rot, kb, vb):
+    """The combined key and value append (one launch for short appends; (1, 4) takes the two-launch
+    fallback) leaves both caches bit-identical to two separate appends, over the whole plan."""
+    B, H = 2, 2
+    _, kt = _tokens(B, H, WRITTEN, "k")
+    _, vt = _tokens(B, H, WRITTEN, "v")
+    cbk, cbv = tq.codebook(128, kb), tq.codebook(128, vb)
+    caches = []
+    for seed in (900, 900):
+        kc = tq.alloc_cache(B, H, T_CAP, 128, kb, "mse", device=dev)
+        vc = tq.alloc_cache(B, H, T_CAP, 128, vb, "mse", layout="blocked", device=dev)
+        _fill(kc, seed)
+        _fill(vc, seed + 50)
+        caches.append((kc, vc))
+    for pos, n in PLAN:
+        k = kt[:, :, pos:pos + n].contiguous().to(dev)
+        v = vt[:, :, pos:pos + n].contiguous().to(dev)
+        tq.kv_append(caches[0][0], caches[0][1], k, v, pos, cbk, cbv, rot, rot)
+        tq.cache_append(caches[1][0], k, pos, cbk, rot)
+        tq.cache_append(caches[1][1], v, pos, cbv, rot)
+    torch.cuda.synchronize()
+    for a, b_ in zip(caches[0], caches[1]):
+        np.testing.assert_array_equal(to_np_words(a.packed.idx), to_np_words(b_.packed.idx))
+        np.testing.assert_array_equal(a.packed.norms.cpu().numpy(), b_.packed.norms.cpu().numpy())
+    with pytest.raises(tq.TQError):
+        tq.kv_append(caches[0][1], caches[0][0], k, v, 0, cbv, cbk, rot, rot)   # layouts swapped
