@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# fp32 FMA on the vector ALUs without packed-fp32 instructions (the library is built without them):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz, in TFLOP/s
+FP32_FMA_PEAK = 78.6
 CACHE_DEFEAT_BYTES = 1.5e9
 
 
@@ -259,6 +262,34 @@ def cpu_baseline_prod(cfg, kind, budget_s=10.0):
                       f"their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
 
 
+def cpu_baseline_split(cfg, bo, br, budget_s=10.0):
+    """The oracle on a bounded sample of the split-code workload: 4096-key chunks of one KV head
+    split-encoded (outlier half b_o bits, rest b_r) and scored by their query heads; scores/s."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    threads, cpu = _cpu_info()
+    r_o, r_r = oracle.dense_rotation(64, 3), oracle.dense_rotation(64, 4)
+    cb_o, cb_r = oracle.codebook(64, bo), oracle.codebook(64, br)
+    ratio = cfg.hq // cfg.hkv
+    x = wl.bf16_bits_to_f32(wl.kv_keys(cfg, T=4096, B=1)[:, :1]).astype(np.float64)
+    out = np.argsort(-np.mean(x * x, axis=(0, 2)), axis=1, kind="stable")[:, :64]
+    q = wl.kv_queries(cfg)[:, :ratio].astype(np.float64)
+    keys = scores = 0
+    t0 = time.perf_counter()
+    while True:
+        enc = oracle.encode_split(x, out, r_o, r_r, cb_o, cb_r)
+        s = oracle.scores_split(q, enc, r_o, r_r, cb_o, cb_r)
+        keys += x.shape[2]
+        scores += s.size
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": scores / dt, "unit": "scores/s (split encode + score of the sampled keys)", "cores": threads,
+            "kind": "oracle", "encode_vectors_per_s": keys / dt,
+            "sample": f"{keys} keys (4096-key chunks of one KV head, outlier half {bo} bits, rest {br}) encoded and "
+                      f"scored by their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
+
+
 def _timed(fn, steps, warmup):
     """Mean ms of fn() over `steps` calls, HIP events on the current stream."""
     import torch
@@ -382,6 +413,45 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "attn_hbm_frac": at_bytes / at_ms / 1e6 / HBM_PEAK_GBS})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_decode(cfg, b, t_cap, cpu_budget)
+    elif name in ("c2split", "c2split35"):
+        # Outlier-channel split codes on the KV-key workload (1 x 8 KV heads x 32768 tokens, 32 query
+        # heads): 2.5 bits per channel (outlier half 3 bits, rest 2) or 3.5 (4 and 3).  The 64
+        # outlier channels per head are those of largest mean square over the first 4096 tokens.
+        cfg = wl.CONFIGS["c2"]
+        bo, br = (3, 2) if name == "c2split" else (4, 3)
+        n = cfg.B * cfg.hkv * cfg.T
+        kb = wl.kv_keys(cfg)
+        xs = wl.bf16_bits_to_f32(kb[:, :, :4096]).astype(np.float64)
+        outl = np.argsort(-np.mean(xs * xs, axis=(0, 2)), axis=1, kind="stable")[:, :64]
+        del xs
+        keys = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        sp = tq.make_split(outl)
+        rot_o, rot_r = tq.make_rotation(64, 3), tq.make_rotation(64, 4)
+        cb_o, cb_r = tq.codebook(64, bo), tq.codebook(64, br)
+        nbuf = 3
+        packs = [(tq.alloc_packed(n, 64, bo, device=dev), tq.alloc_packed(n, 64, br, device=dev)) for _ in range(nbuf)]
+        outs = [torch.empty((cfg.B, cfg.hq, cfg.T), device=dev) for _ in range(nbuf)]
+        ws = torch.empty(tq.scores_split_workspace(cfg.B, cfg.hq), dtype=torch.uint8, device=dev)
+        enc = lambda i: tq.encode_split(keys, sp, cb_o, cb_r, rot_o, rot_r, out=packs[i % nbuf])
+        sco = lambda i: tq.scores_split(q, packs[i % nbuf], cfg.hkv, sp, cb_o, cb_r, rot_o, rot_r, out=outs[i % nbuf],
+                                        ws=ws)
+        enc_ms = _timed(enc, steps, warmup)
+        sc_ms = _timed(sco, steps, warmup)
+        step_ms = _timed(lambda i: (enc(i), sco(i)), steps, warmup)
+        words = 2 * (bo + br)
+        enc_bytes = n * (cfg.d * 2 + 4 * words + 8)
+        enc_flop = n * 2 * 2 * 64 * 64
+        sc_bytes = n * (4 * words + 8) + q.numel() * 4 + outs[0].numel() * 4
+        res.update({"bits_outlier": bo, "bits_rest": br, "bits_per_channel": (bo + br) / 2,
+                    "step_ms": step_ms, "scores_per_s_step": outs[0].numel() / step_ms * 1e3,
+                    "encode_ms": enc_ms, "encode_gbs": enc_bytes / enc_ms / 1e6,
+                    "encode_tflops": enc_flop / enc_ms / 1e9, "encode_alu_frac": enc_flop / enc_ms / 1e9 / FP32_FMA_PEAK,
+                    "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
+                    "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
+                    "scores_per_s": outs[0].numel() / sc_ms * 1e3})
+        if cpu_budget > 0:
+            res["cpu_baseline"] = cpu_baseline_split(cfg, bo, br, cpu_budget)
     elif name == "peaks":
         # Achievable HBM rates on this machine, for reading the fractions against a measured ceiling as
         # well as the 8 TB/s spec: a plain device copy (reads and writes) and a read-only sum of
@@ -434,7 +504,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4", "peaks"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4", "peaks", "c2split",
+                                                        "c2split35"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -75,6 +75,7 @@ typedef enum tq_layout { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_TOKEN_BLOCKED = 1 } tq_la
 typedef struct tq_codebook_s* tq_codebook_t;
 typedef struct tq_rotation_s* tq_rotation_t;
 typedef struct tq_qjl_s* tq_qjl_t;
+typedef struct tq_split_s* tq_split_t;
 
 /* A packed set of n encoded vectors, all buffers device memory owned by the caller.
  * Row r of idx holds the d indices of vector r as one LSB-first bit stream: coordinate i
@@ -287,6 +288,46 @@ tq_status tq_decode_attn_cache(const float* q_dev, int B, int Hq, int Hkv, int64
                                tq_codebook_t cb_v, tq_rotation_t rot_k, tq_rotation_t rot_v,
                                float scale, float* out_dev, void* ws_dev, size_t ws_bytes,
                                void* stream);
+
+/* ---- outlier-channel mixed precision (d = 128) ----------------------------------------
+ * [RQ] the asymmetric needs of K and V: keys need more bits, e.g. mixed precision with the
+ * outlier channels at more bits than the rest; [TQ] engineering data points: 2.5 and 3.5 bits
+ * per channel.  The pages fix no mechanism; this library's reading: per KV head, the caller
+ * names 64 outlier channels of the 128; each key vector becomes two TurboQuant_mse codes, its
+ * outlier half (channels in the listed order) at b_o bits and its other half (ascending channel
+ * order) at b_r bits, each half with its own norm, its own 64 x 64 rotation and the codebook of
+ * dimension 64: (b_o + b_r) / 2 bits per channel, 2.5 at (3, 2) and 3.5 at (4, 3). */
+
+/* Channel split of H KV heads: outliers_host [H, 64] int32, each row 64 distinct channels in
+ * [0, 128).  The handle keeps the per-head channel order (outliers as listed, then the rest
+ * ascending) on the current device.  d must be 128.  Errors: TQ_EINVAL (null pointers, H < 1,
+ * a repeated or out-of-range channel), TQ_EUNSUPPORTED (d != 128), TQ_EDEVICE. */
+tq_status tq_make_split(int H, int d, const int32_t* outliers_host, tq_split_t* out);
+void tq_split_free(tq_split_t split);
+
+/* Split encode of keys x_dev [B, H, T, 128] (dtype dt): out_o receives the outlier halves and
+ * out_r the other halves, each a ROWS-layout MSE packed set with d = 64 and n = B*H*T (bits =
+ * cb_o->b resp. cb_r->b; idx [n, 2*bits] words, norms [n] = the half's ||x_half||).  cb_o, cb_r:
+ * codebooks with d = 64; rot_o, rot_r: rotations with d = 64 (any kind).  Index decisions follow
+ * tq_encode's rule (ties to the upper index) on the half's fp32 rotation.  Errors: TQ_EINVAL (null
+ * pointers, negative sizes), TQ_ESHAPE (split->H != H, a handle or packed set with d != 64, n or
+ * bits mismatch), TQ_EUNSUPPORTED (dtype, layout, B*H > 65535, T > 2^25). */
+tq_status tq_encode_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t T, tq_split_t split,
+                          tq_codebook_t cb_o, tq_codebook_t cb_r, tq_rotation_t rot_o,
+                          tq_rotation_t rot_r, tq_packed* out_o, tq_packed* out_r, void* stream);
+
+/* Workspace bytes of tq_scores_split: the rotated queries, B*Hq*128 fp32. */
+size_t tq_scores_split_workspace(int B, int Hq);
+/* Raw scores <q, x_hat> of queries q_dev [B, Hq, 128] fp32 against split-coded keys K_o, K_r
+ * (as written by tq_encode_split for [B, Hkv, T]) into scores_dev [B, Hq, T] fp32: the sum over
+ * the two halves of s_half <R_half q_half, C_half[idx]>, q_half gathered through the channel
+ * order of the query head's KV head h // (Hq / Hkv).  Errors: as tq_encode_split for the keys and
+ * handles; TQ_ESHAPE (Hq not a positive multiple of Hkv); TQ_EUNSUPPORTED (Hq / Hkv above 64);
+ * TQ_ENOMEM (workspace). */
+tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
+                          const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o,
+                          tq_codebook_t cb_r, tq_rotation_t rot_o, tq_rotation_t rot_r,
+                          float* scores_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
  * with k results per query (query operands, one chunk of scores, the running top-k). */

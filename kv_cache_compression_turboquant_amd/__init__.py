@@ -20,6 +20,7 @@ __all__ = [
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
     "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
+    "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -366,6 +367,60 @@ def decode_attn_cache(q, kc, vc, T, cb_k, cb_v, rot_k, rot_v, scale=None, out=No
     check(lib().tq_decode_attn_cache(_dptr(q), B, Hq, kc.H, T, kc.t_cap, ctypes.byref(kd), ctypes.byref(vd), cb_k.ptr,
                                      cb_v.ptr, rot_k.ptr, rot_v.ptr, ctypes.c_float(scale), _dptr(out), _dptr(ws),
                                      ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+class Split(_Handle):
+    """Per-KV-head channel split of d = 128 keys: 64 outlier channels, then the rest."""
+    _free = "tq_split_free"
+
+    def __init__(self, ptr, outliers):
+        super().__init__(ptr)
+        self.outliers = outliers
+        self.H = outliers.shape[0]
+
+
+def make_split(outliers):
+    """outliers: [H, 64] integer channels (distinct per row, in [0, 128))."""
+    o = np.ascontiguousarray(np.asarray(outliers), dtype=np.int32)
+    if o.ndim != 2:
+        raise TQError(1, "outliers must be [H, 64]")
+    h = ctypes.c_void_p()
+    check(lib().tq_make_split(o.shape[0], 2 * o.shape[1], _np(o), ctypes.byref(h)))
+    return Split(h.value, o)
+
+
+def encode_split(x, split, cb_o, cb_r, rot_o, rot_r, out=None):
+    """Split encode of keys x [B, H, T, 128] (bf16 or fp32): (outlier codes, rest codes), each a
+    rows-layout MSE Packed with d = 64 and n = B*H*T."""
+    B, H, T, d = x.shape
+    n = B * H * T
+    if out is None:
+        out = (alloc_packed(n, 64, cb_o.b, "mse", device=x.device), alloc_packed(n, 64, cb_r.b, "mse", device=x.device))
+    do, dr = out[0].descriptor(), out[1].descriptor()
+    check(lib().tq_encode_split(_dptr(x), _dtype_code(x), B, H, T, split.ptr, cb_o.ptr, cb_r.ptr, rot_o.ptr,
+                                rot_r.ptr, ctypes.byref(do), ctypes.byref(dr), _stream()))
+    return out
+
+
+def scores_split_workspace(B, Hq):
+    return int(lib().tq_scores_split_workspace(B, Hq))
+
+
+def scores_split(q, K, Hkv, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
+    """Raw scores [B, Hq, T] of q [B, Hq, 128] fp32 against split codes K = (K_o, K_r) of keys
+    [B, Hkv, T]."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    T = K[0].n // max(B * Hkv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((max(scores_split_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
+    do, dr = K[0].descriptor(), K[1].descriptor()
+    check(lib().tq_scores_split(_dptr(q), B, Hq, Hkv, T, split.ptr, ctypes.byref(do), ctypes.byref(dr), cb_o.ptr,
+                                cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
+                                ws.numel() * ws.element_size(), _stream()))
     return out
 
 

@@ -84,6 +84,13 @@ SIGNATURES = {
     "tq_scores_cache": (_I, [_P, _I, _I, _I, _I64, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _SZ, _P]),
     "tq_decode_attn_cache": (_I, [_P, _I, _I, _I, _I64, _I64, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed),
                                   _P, _P, _P, _P, ctypes.c_float, _P, _P, _SZ, _P]),
+    "tq_make_split": (_I, [_I, _I, _P, ctypes.POINTER(_P)]),
+    "tq_split_free": (None, [_P]),
+    "tq_encode_split": (_I, [_P, _I, _I, _I, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(tq_packed),
+                             ctypes.POINTER(tq_packed), _P]),
+    "tq_scores_split_workspace": (_SZ, [_I, _I]),
+    "tq_scores_split": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed), _P, _P,
+                             _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

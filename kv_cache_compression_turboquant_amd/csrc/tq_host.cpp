@@ -20,6 +20,7 @@
 
 #include "tq_cache.h"
 #include "tq_internal.h"
+#include "tq_split.h"
 
 namespace {
 
@@ -1077,6 +1078,124 @@ tq_status tq_kv_append(const void* k_dev, const void* v_dev, tq_dtype dt, int B,
 }
 
 }  // extern "C"
+
+// ---- outlier-channel split codes (d = 128) ------------------------------------------------
+
+struct tq_split_s {
+  int H;
+  int device;
+  std::vector<int32_t> order;     // [H, 128]: outlier channels as listed, then the rest ascending
+  int32_t* order_dev = nullptr;
+};
+
+tq_status tq_make_split(int H, int d, const int32_t* outliers_host, tq_split_t* out) {
+  static const char* fn = "tq_make_split";
+  if (!out || !outliers_host || H < 1) return fail(TQ_EINVAL, "%s: bad arguments", fn);
+  if (d != tq::kSplitD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  std::vector<int32_t> order((size_t)H * tq::kSplitD);
+  for (int h = 0; h < H; ++h) {
+    bool seen[tq::kSplitD] = {};
+    const int32_t* o = outliers_host + (size_t)h * tq::kSplitHalf;
+    for (int i = 0; i < tq::kSplitHalf; ++i) {
+      if (o[i] < 0 || o[i] >= tq::kSplitD || seen[o[i]])
+        return fail(TQ_EINVAL, "%s: head %d: channel %d repeated or outside [0, 128)", fn, h, (int)o[i]);
+      seen[o[i]] = true;
+      order[(size_t)h * tq::kSplitD + i] = o[i];
+    }
+    int k = tq::kSplitHalf;
+    for (int c = 0; c < tq::kSplitD; ++c)
+      if (!seen[c]) order[(size_t)h * tq::kSplitD + k++] = c;
+  }
+  auto* sp = new (std::nothrow) tq_split_s();
+  if (!sp) return fail(TQ_ENOMEM, "host allocation failed");
+  sp->H = H;
+  hipGetDevice(&sp->device);
+  sp->order = std::move(order);
+  tq_status st = upload(sp->order, &sp->order_dev, "upload channel order");
+  if (st != TQ_OK) {
+    delete sp;
+    return st;
+  }
+  *out = sp;
+  return ok();
+}
+
+void tq_split_free(tq_split_t sp) {
+  if (!sp) return;
+  if (sp->order_dev) hipFree(sp->order_dev);
+  delete sp;
+}
+
+// Handles and both halves' packed sets of split-coded keys [B, H, T].
+static tq_status check_split_keys(int B, int H, int64_t T, tq_split_t sp, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                                  tq_rotation_t rot_o, tq_rotation_t rot_r, const tq_packed* K_o,
+                                  const tq_packed* K_r, const char* fn) {
+  if (!sp || !cb_o || !cb_r || !rot_o || !rot_r || !K_o || !K_r) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || H < 0 || T < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (sp->H != H) return fail(TQ_ESHAPE, "%s: split has %d heads, keys have %d", fn, sp->H, H);
+  if ((int64_t)B * H > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*H=%lld above 65535", fn, (long long)B * H);
+  if (T > kMaxSeqTokens) return fail(TQ_EUNSUPPORTED, "%s: T=%lld above %lld", fn, (long long)T, (long long)kMaxSeqTokens);
+  const int m = tq::kSplitHalf;
+  if (cb_o->d != m || cb_r->d != m) return fail(TQ_ESHAPE, "%s: codebooks need d=64", fn);
+  if (rot_o->d != m || rot_r->d != m) return fail(TQ_ESHAPE, "%s: rotations need d=64", fn);
+  tq_status st = check_packed(K_o, m, cb_o->b, TQ_MODE_MSE, fn);
+  if (st == TQ_OK) st = check_packed(K_r, m, cb_r->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  if (K_o->layout != TQ_LAYOUT_ROWS || K_r->layout != TQ_LAYOUT_ROWS)
+    return fail(TQ_EUNSUPPORTED, "%s: split codes use the ROWS layout", fn);
+  const int64_t n = (int64_t)B * H * T;
+  if (K_o->n != n || K_r->n != n)
+    return fail(TQ_ESHAPE, "%s: packed n=%lld/%lld but B*H*T=%lld", fn, (long long)K_o->n, (long long)K_r->n,
+                (long long)n);
+  return TQ_OK;
+}
+
+tq_status tq_encode_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t T, tq_split_t split,
+                          tq_codebook_t cb_o, tq_codebook_t cb_r, tq_rotation_t rot_o, tq_rotation_t rot_r,
+                          tq_packed* out_o, tq_packed* out_r, void* stream) {
+  static const char* fn = "tq_encode_split";
+  tq_status st = check_split_keys(B, H, T, split, cb_o, cb_r, rot_o, rot_r, out_o, out_r, fn);
+  if (st != TQ_OK) return st;
+  if (dt != TQ_BF16 && dt != TQ_F32) return fail(TQ_EUNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  if ((int64_t)B * H * T == 0) return ok();
+  if (!x_dev) return fail(TQ_EINVAL, "%s: null x", fn);
+  return check_launch(tq::launch_encode_split(x_dev, dt == TQ_BF16, (int64_t)B * H, H, T, split->order_dev,
+                                              rot_o->r32_dev, rot_r->r32_dev, cb_o->args, cb_r->args, out_o->idx,
+                                              out_o->norms, out_r->idx, out_r->norms, as_stream(stream)),
+                      fn);
+}
+
+size_t tq_scores_split_workspace(int B, int Hq) {
+  if (B < 0 || Hq < 0) return 0;
+  return (size_t)B * Hq * tq::kSplitD * sizeof(float);
+}
+
+tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
+                          const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                          tq_rotation_t rot_o, tq_rotation_t rot_r, float* scores_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_scores_split";
+  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0)
+    return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  if (Hq / Hkv > tq::kSplitMaxRatio)
+    return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d above %d", fn, Hq / Hkv, tq::kSplitMaxRatio);
+  tq_status st = check_split_keys(B, Hkv, T, split, cb_o, cb_r, rot_o, rot_r, K_o, K_r, fn);
+  if (st != TQ_OK) return st;
+  if ((int64_t)Hq * T >= (int64_t(1) << 30))
+    return fail(TQ_EUNSUPPORTED, "%s: Hq*T=%lld: a batch's score rows must stay below 4 GB", fn, (long long)Hq * T);
+  if ((int64_t)B * Hq * T == 0) return ok();
+  if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
+  const size_t need = tq_scores_split_workspace(B, Hq);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  hipStream_t hs = as_stream(stream);
+  float* qws = static_cast<float*>(ws_dev);
+  hipError_t e = tq::launch_qprep_split(q_dev, B, Hq, Hkv, split->order_dev, rot_o->rt32_dev, rot_r->rt32_dev, qws, hs);
+  if (e == hipSuccess)
+    e = tq::launch_scores_split(qws, B, Hq, Hkv, T, cb_o->b, cb_r->b, cb_o->args, cb_r->args, K_o->idx, K_o->norms,
+                                K_r->idx, K_r->norms, scores_dev, hs);
+  return check_launch(e, fn);
+}
 
 size_t tq_search_workspace(int64_t nq, int64_t n, int d, int k) {
   if (nq <= 0 || n < 0 || d <= 0 || d % 128 != 0 || k < 1 || k > tq::kSearchMaxK) return 0;

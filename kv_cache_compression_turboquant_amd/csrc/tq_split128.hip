@@ -1,0 +1,372 @@
+// Outlier-channel mixed precision at d = 128 ("TurboQuant 和 RotorQuant 的真相", the asymmetric
+// needs of K and V: outlier channels at more bits than the rest; "TurboQuant 详解", the
+// engineering data points at 2.5 and 3.5 bits per channel).  Every key vector is two
+// TurboQuant_mse codes: its 64 outlier channels (listed per KV head) at BO bits and its other
+// 64 channels at BR bits, each half with its own norm, its own 64 x 64 rotation and the
+// codebook of dimension 64.  A query's score is the sum of the two halves' scores, each
+// s <R q_half, C[idx]> in its own rotated domain.
+#include <type_traits>
+
+#include "tq_device.h"
+#include "tq_split.h"
+
+namespace tq {
+namespace {
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// ---------------------------------------------------------------------------------------
+// Encode.  A block of 8 waves takes 128 consecutive tokens of one sequence in two rounds of 64.
+// Each round stages its 64 vectors in LDS in channel order (outlier channels first, fp32), so
+// each half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
+// 0..3 (16 vectors each) and waves 4..7 the other halves, so a wave's bit width is uniform.
+// Lane (jl, vq) of a wave holds the 4 x 4 outputs (coordinates jl + 16 k, vectors 4 vq + u):
+// per step of 4 contraction terms it reads 4 rotation rows and 4 vectors (one 16-byte LDS read
+// each) for 64 FMAs.  The rotation rows are padded to 68 floats so that the 16 rows a wave reads
+// at once fall in distinct banks; vectors are padded to 132 floats for the norm sums.
+// Quantization compares the unnormalized product against s * t_k (s the half's norm), the
+// tie going up; a zero half (s = 0, product 0) compares 0 against the unscaled thresholds, so
+// it takes the index of y = 0.  Indices are ORed into per-vector words in LDS and stored after a
+// barrier.
+// Rows past T are staged as zeros and never stored.
+// ---------------------------------------------------------------------------------------
+constexpr int kEncWaves = 8;
+constexpr int kGroupRows = 16;                        // vectors per wave group per round
+constexpr int kRoundRows = 4 * kGroupRows;            // 64
+constexpr int kEncRounds = 2;
+constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 128
+constexpr int kRS = 68;
+constexpr int kXS = 132;
+
+template <int B, int OFF, int WT>
+__device__ __forceinline__ void quantize_pack(const float (&acc)[4][4], const float (&su)[4], const CodebookArgs& cb,
+                                              uint32_t (*wbuf)[WT], int vbase, int jl) {
+  constexpr int K = 1 << B;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float thr[K - 1];
+#pragma unroll
+    for (int q = 0; q < K - 1; ++q) thr[q] = su[u] > 0.f ? su[u] * cb.t[q] : cb.t[q];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t idx = 0;
+#pragma unroll
+      for (int q = 0; q < K - 1; ++q) idx += acc[k][u] >= thr[q] ? 1u : 0u;
+      const int p = (jl + 16 * k) * B, w = p >> 5, sh = p & 31;
+      atomicOr(&wbuf[vbase + u][OFF + w], idx << sh);
+      if (sh + B > 32) atomicOr(&wbuf[vbase + u][OFF + w + 1], idx >> (32 - sh));
+    }
+  }
+}
+
+template <int BO, int BR, bool BF16IN>
+__global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
+    const void* __restrict__ x, int64_t T, int H, const int32_t* __restrict__ order, const float* __restrict__ ro,
+    const float* __restrict__ rr, CodebookArgs cbo, CodebookArgs cbr, uint32_t* __restrict__ idx_o,
+    float* __restrict__ norm_o, uint32_t* __restrict__ idx_r, float* __restrict__ norm_r) {
+  constexpr int WO = 2 * BO, WR = 2 * BR, WT = WO + WR;
+  __shared__ __align__(16) float rs[2][64][kRS];
+  __shared__ __align__(16) float xs[4][kGroupRows][kXS];
+  __shared__ int inv[kSplitD];
+  __shared__ float nrm[2][kRoundRows];
+  __shared__ uint32_t wbuf[kRoundRows][WT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = wave >> 2, grp = wave & 3;
+  const int64_t seq = blockIdx.y;
+  const int h = (int)(seq % H);
+  const int64_t tblk = (int64_t)blockIdx.x * kEncBlockRows;
+
+  for (int e = tid; e < 2 * 64 * 64; e += kEncWaves * 64) {
+    const int p = e >> 12, r = (e >> 6) & 63, c = e & 63;
+    rs[p][r][c] = (p ? rr : ro)[r * 64 + c];
+  }
+  if (tid < kSplitD) inv[order[(int64_t)h * kSplitD + tid]] = tid;
+  __syncthreads();
+
+  const int jl = lane & 15, vq = lane >> 4;
+  const int ch = tid & 127, vs = tid >> 7;   // staging: channel ch of round vectors vs + 4 m
+  const int pc = inv[ch];
+
+  for (int round = 0; round < kEncRounds; ++round) {
+    const int64_t tr = tblk + (int64_t)round * kRoundRows;
+#pragma unroll 4
+    for (int m = 0; m < kRoundRows / 4; ++m) {
+      const int v = vs + 4 * m;
+      const int64_t t = tr + v;
+      float val = 0.f;
+      if (t < T) {
+        const int64_t src = (seq * T + t) * kSplitD + ch;
+        val = BF16IN ? bf16_val(static_cast<const uint16_t*>(x)[src]) : static_cast<const float*>(x)[src];
+      }
+      xs[v >> 4][v & 15][pc] = val;
+    }
+    for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) (&wbuf[0][0])[e] = 0u;
+    __syncthreads();
+
+    // The half's squared norm of vector (lane & 15): four partial sums of 16 squares, then
+    // summed across the four lane quarters.
+    float s2;
+    {
+      const float* row = &xs[grp][lane & 15][part * 64 + (lane >> 4) * 16];
+      s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row + i);
+        s2 = fmaf(a.x, a.x, s2);
+        s2 = fmaf(a.y, a.y, s2);
+        s2 = fmaf(a.z, a.z, s2);
+        s2 = fmaf(a.w, a.w, s2);
+      }
+      s2 += __shfl_xor(s2, 16);
+      s2 += __shfl_xor(s2, 32);
+    }
+    if (lane < kGroupRows) nrm[part][grp * kGroupRows + lane] = sqrtf(s2);
+    float su[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) su[u] = sqrtf(__shfl(s2, 4 * vq + u));
+
+    float acc[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[k][u] = 0.f;
+    const float* xb = &xs[grp][4 * vq][part * 64];
+    const float* rb = &rs[part][jl][0];
+#pragma unroll 4
+    for (int i = 0; i < 64; i += 4) {
+      f32x4 a[4], xv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = *reinterpret_cast<const f32x4*>(rb + 16 * k * kRS + i);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xv[u] = *reinterpret_cast<const f32x4*>(xb + u * kXS + i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[k][u] = fmaf(a[k].x, xv[u].x, acc[k][u]);
+          acc[k][u] = fmaf(a[k].y, xv[u].y, acc[k][u]);
+          acc[k][u] = fmaf(a[k].z, xv[u].z, acc[k][u]);
+          acc[k][u] = fmaf(a[k].w, xv[u].w, acc[k][u]);
+        }
+    }
+    const int vbase = grp * kGroupRows + 4 * vq;
+    if (part == 0)
+      quantize_pack<BO, 0, WT>(acc, su, cbo, wbuf, vbase, jl);
+    else
+      quantize_pack<BR, WO, WT>(acc, su, cbr, wbuf, vbase, jl);
+    __syncthreads();
+
+    for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) {
+      const int v = e / WT, w = e - v * WT;
+      const int64_t t = tr + v;
+      if (t < T) {
+        const int64_t row = seq * T + t;
+        if (w < WO)
+          idx_o[row * WO + w] = wbuf[v][w];
+        else
+          idx_r[row * WR + (w - WO)] = wbuf[v][w];
+      }
+    }
+    if (tid < 2 * kRoundRows) {
+      const int v = tid & (kRoundRows - 1);
+      const int64_t t = tr + v;
+      if (t < T) (tid < kRoundRows ? norm_o : norm_r)[seq * T + t] = nrm[tid / kRoundRows][v];
+    }
+    __syncthreads();  // the next round overwrites xs, wbuf and nrm
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Query prologue: one block of 128 threads per query head.  The query is gathered into the
+// channel order of its KV head; thread j then forms coordinate j & 63 of R_o q_O (j < 64) or of
+// R_r q_R, reading R^T row-major so that the threads' loads are consecutive.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_qprep_split(const float* __restrict__ q, int Hq, int Hkv,
+                                                     const int32_t* __restrict__ order, const float* __restrict__ rto,
+                                                     const float* __restrict__ rtr, float* __restrict__ qws) {
+  __shared__ float qs[kSplitD];
+  const int j = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int hq = (int)(bh % Hq), hk = hq / (Hq / Hkv);
+  qs[j] = q[bh * kSplitD + order[(int64_t)hk * kSplitD + j]];
+  __syncthreads();
+  const int part = j >> 6, jj = j & 63;
+  const float* rt = part ? rtr : rto;
+  float a = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < 64; ++i) a = fmaf(rt[i * 64 + jj], qs[part * 64 + i], a);
+  qws[bh * kSplitD + j] = a;
+}
+
+// ---------------------------------------------------------------------------------------
+// Scores: one thread per key (a block holds 256 consecutive tokens of one KV head).  The block
+// first stages the rotated queries of the KV head's query heads in LDS as [chunk][coordinate][4]
+// (4 heads per chunk, absent heads as zeros), so that one broadcast 16-byte read gives a
+// coordinate's 4 query values.  The thread loads its key's 2 BO + 2 BR words and two norms,
+// decodes each coordinate with a centroid table in LDS (at most 16 entries in distinct banks,
+// so lookups never conflict) and accumulates 4 heads per pass over the key.
+// Score = s_o <R_o q_O, C_o[idx_o]> + s_r <R_r q_R, C_r[idx_r]>.
+// ---------------------------------------------------------------------------------------
+constexpr int kScoreThreads = 256;
+constexpr int kMaxChunks = kSplitMaxRatio / 4;
+
+// 8 coordinates at a time.  The group's (at most two) packed words and its LDS offsets pass
+// through an empty asm that depends on the previous group's sums, so the optimizer cannot
+// compute every field and issue every LDS read of the pass at its top (which needs a register
+// per value and spills); each group decodes from its own copy of the words.
+template <int B, int NW>
+__device__ __forceinline__ void half_dot(const uint32_t (&w)[NW], const float* ctab, const float (*qs)[4],
+                                         f32x4& acc) {
+#pragma unroll
+  for (int i0 = 0; i0 < 64; i0 += 8) {
+    constexpr int kSpan = 8 * B;
+    const int wlo = (i0 * B) >> 5, whi = (i0 * B + kSpan - 1) >> 5;
+    uint32_t lo = w[wlo], hi = w[whi];
+    int base = i0, cbase = 0;
+    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(base), "+v"(cbase), "+v"(acc.x), "+v"(acc.y), "+v"(acc.z), "+v"(acc.w));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = (i0 + k) * B - 32 * wlo;   // bit offset of the field from word wlo
+      uint32_t f;
+      if (p + B <= 32)
+        f = lo >> p;
+      else if (p >= 32)
+        f = hi >> (p - 32);
+      else
+        f = (lo >> p) | (hi << (32 - p));
+      const float c = ctab[cbase + (int)(f & ((1u << B) - 1u))];
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(qs[base + k]);
+      acc.x = fmaf(qv.x, c, acc.x);
+      acc.y = fmaf(qv.y, c, acc.y);
+      acc.z = fmaf(qv.z, c, acc.z);
+      acc.w = fmaf(qv.w, c, acc.w);
+    }
+  }
+}
+
+template <int BO, int BR>
+__global__ __launch_bounds__(kScoreThreads) void k_scores_split_d128(
+    const float* __restrict__ qws, int Hq, int Hkv, int64_t T, CodebookArgs cbo, CodebookArgs cbr,
+    const uint32_t* __restrict__ idx_o, const float* __restrict__ norm_o, const uint32_t* __restrict__ idx_r,
+    const float* __restrict__ norm_r, float* __restrict__ scores) {
+  constexpr int WO = 2 * BO, WR = 2 * BR;
+  __shared__ float ctab[2][kMaxCentroids];
+  __shared__ __align__(16) float qs[kMaxChunks][kSplitD][4];
+  const int tid = threadIdx.x;
+  const int64_t seq = blockIdx.y;
+  const int b = (int)(seq / Hkv), hk = (int)(seq % Hkv);
+  const int ratio = Hq / Hkv;
+  const int nchunks = (ratio + 3) >> 2;
+  const int64_t hq_first = (int64_t)b * Hq + (int64_t)hk * ratio;
+  if (tid < kMaxCentroids)
+    ctab[0][tid] = cbo.c[tid];
+  else if (tid < 2 * kMaxCentroids)
+    ctab[1][tid - kMaxCentroids] = cbr.c[tid - kMaxCentroids];
+  for (int e = tid; e < nchunks * kSplitD * 4; e += kScoreThreads) {
+    const int g = e & 3, i = (e >> 2) & (kSplitD - 1), c = e >> 9;
+    const int head = 4 * c + g;
+    qs[c][i][g] = head < ratio ? qws[(hq_first + head) * kSplitD + i] : 0.f;
+  }
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kScoreThreads + tid;
+  const bool live = t < T;
+  const int64_t row = seq * T + (live ? t : T - 1);
+  uint32_t wo[WO], wr[WR];
+#pragma unroll
+  for (int i = 0; i < WO; i += 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(idx_o + row * WO + i);
+    wo[i] = v.x;
+    wo[i + 1] = v.y;
+  }
+#pragma unroll
+  for (int i = 0; i < WR; i += 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(idx_r + row * WR + i);
+    wr[i] = v.x;
+    wr[i + 1] = v.y;
+  }
+  const float so = norm_o[row], sr = norm_r[row];
+  for (int c = 0; c < nchunks; ++c) {
+    // The words are opaque to the optimizer here, so it decodes them again in every pass rather
+    // than hoisting all 128 decoded centroids out of the loop into registers.
+#pragma unroll
+    for (int k = 0; k < WO; ++k) asm volatile("" : "+v"(wo[k]));
+#pragma unroll
+    for (int k = 0; k < WR; ++k) asm volatile("" : "+v"(wr[k]));
+    f32x4 ao = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
+    half_dot<BO>(wo, ctab[0], &qs[c][0], ao);
+    half_dot<BR>(wr, ctab[1], &qs[c][64], ar);
+    const float r[4] = {so * ao.x + sr * ar.x, so * ao.y + sr * ar.y, so * ao.z + sr * ar.z, so * ao.w + sr * ar.w};
+    if (live) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (4 * c + g < ratio) scores[(hq_first + 4 * c + g) * T + t] = r[g];
+    }
+  }
+}
+
+// Calls f(IC<BO>, IC<BR>) for bit widths 1..4 each.
+template <int BO, typename F>
+hipError_t with_br(int br, F&& f) {
+  switch (br) {
+    case 1: return f(IC<BO>{}, IC<1>{});
+    case 2: return f(IC<BO>{}, IC<2>{});
+    case 3: return f(IC<BO>{}, IC<3>{});
+    case 4: return f(IC<BO>{}, IC<4>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename F>
+hipError_t with_bits(int bo, int br, F&& f) {
+  switch (bo) {
+    case 1: return with_br<1>(br, f);
+    case 2: return with_br<2>(br, f);
+    case 3: return with_br<3>(br, f);
+    case 4: return with_br<4>(br, f);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, int64_t T, const int32_t* order,
+                               const float* ro, const float* rr, const CodebookArgs& cbo, const CodebookArgs& cbr,
+                               uint32_t* idx_o, float* norm_o, uint32_t* idx_r, float* norm_r, hipStream_t st) {
+  if (n_seq <= 0 || T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + kEncBlockRows - 1) / kEncBlockRows), (unsigned)n_seq);
+  return with_bits(cbo.bits, cbr.bits, [&](auto bo, auto br) -> hipError_t {
+    constexpr int BO = decltype(bo)::value, BR = decltype(br)::value;
+    if (bf16)
+      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, true>), grid, dim3(kEncWaves * 64), 0, st, x, T, H, order, ro,
+                         rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+    else
+      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, false>), grid, dim3(kEncWaves * 64), 0, st, x, T, H, order, ro,
+                         rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_qprep_split(const float* q, int B, int Hq, int Hkv, const int32_t* order, const float* rto,
+                              const float* rtr, float* qws, hipStream_t st) {
+  if ((int64_t)B * Hq == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qprep_split, dim3((unsigned)((int64_t)B * Hq)), dim3(128), 0, st, q, Hq, Hkv, order, rto, rtr,
+                     qws);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_split(const float* qws, int B, int Hq, int Hkv, int64_t T, int bo, int br,
+                               const CodebookArgs& cbo, const CodebookArgs& cbr, const uint32_t* idx_o,
+                               const float* norm_o, const uint32_t* idx_r, const float* norm_r, float* scores,
+                               hipStream_t st) {
+  if ((int64_t)B * Hkv == 0 || T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + kScoreThreads - 1) / kScoreThreads), (unsigned)((int64_t)B * Hkv));
+  return with_bits(bo, br, [&](auto o, auto r) -> hipError_t {
+    hipLaunchKernelGGL((k_scores_split_d128<decltype(o)::value, decltype(r)::value>), grid, dim3(kScoreThreads), 0, st,
+                       qws, Hq, Hkv, T, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace tq

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(tq):
     for name in names:
         assert hasattr(raw, name), name
         assert name in _binding.SIGNATURES, f"binding lacks {name}"
-    assert tq.lib().tq_abi_version() == 3
+    assert tq.lib().tq_abi_version() == 4
 
 
 def test_splitmix_bit_identical(tq):
@@ -205,3 +205,28 @@ def test_cache_entry_points_validate(tq):
                                None) == 1
     assert lib.tq_decode_attn_cache(None, 1, 8, 2, 10, 64, ctypes.byref(desc), ctypes.byref(desc), cbh.ptr, cbh.ptr,
                                     None, None, ctypes.c_float(1.0), None, None, 0, None) == 1
+
+
+def test_split_entry_points_validate(tq):
+    """The outlier-channel split entry points reject bad channel lists and missing handles before
+    any device work, and size their workspace."""
+    lib = tq.lib()
+    h = ctypes.c_void_p()
+    good = np.tile(np.arange(64, dtype=np.int32), (2, 1))
+    rep = good.copy()
+    rep[1, 5] = rep[1, 6]                     # repeated channel
+    out = good.copy()
+    out[0, 0] = 128                           # outside [0, 128)
+    P = lambda a: ctypes.c_void_p(a.ctypes.data)
+    assert lib.tq_make_split(2, 128, P(rep), ctypes.byref(h)) == 1
+    assert lib.tq_make_split(2, 128, P(out), ctypes.byref(h)) == 1
+    assert lib.tq_make_split(0, 128, P(good), ctypes.byref(h)) == 1
+    assert lib.tq_make_split(2, 96, P(good), ctypes.byref(h)) == 3
+    assert lib.tq_make_split(2, 128, None, ctypes.byref(h)) == 1
+    cbh = tq.codebook(64, 3)
+    desc = tq.tq_packed(64, 3, 0, 0, 10, None, None, None, None)
+    assert lib.tq_encode_split(None, 1, 1, 2, 5, None, cbh.ptr, cbh.ptr, None, None, ctypes.byref(desc),
+                               ctypes.byref(desc), None) == 1
+    assert lib.tq_scores_split(None, 1, 8, 2, 5, None, ctypes.byref(desc), ctypes.byref(desc), cbh.ptr, cbh.ptr,
+                               None, None, None, None, 0, None) == 1
+    assert lib.tq_scores_split_workspace(2, 32) == 2 * 32 * 128 * 4
