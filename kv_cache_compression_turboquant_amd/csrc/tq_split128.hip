@@ -21,10 +21,13 @@ using IC = std::integral_constant<int, V>;
 // Each round stages its 64 vectors in LDS in channel order (outlier channels first, fp32), so
 // each half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
 // 0..3 (16 vectors each) and waves 4..7 the other halves, so a wave's bit width is uniform.
-// Lane (jl, vq) of a wave holds the 4 x 4 outputs (coordinates jl + 16 k, vectors 4 vq + u):
-// per step of 4 contraction terms it reads 4 rotation rows and 4 vectors (one 16-byte LDS read
-// each) for 64 FMAs.  The rotation rows are padded to 68 floats so that the 16 rows a wave reads
-// at once fall in distinct banks; vectors are padded to 132 floats for the norm sums.
+// The rotation is Y = R X on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32 products and
+// sums like the vector ALU): A = 16 rotation rows x 4 contraction terms, B = 4 terms x the
+// group's 16 vectors, 4 output blocks x 16 steps per half.  Lane l = n + 16 g supplies A row n,
+// B column n and contraction term g of each step and ends with coordinates 16 mb + 4 g + r of
+// vector n.  Both LDS operands are stored with the 16 steps of a term contiguous ([g][step]),
+// so one 16-byte read feeds 4 steps; rows are padded (68 and 132 floats) so that the 16 rows a
+// read touches fall in distinct banks.
 // Quantization compares the unnormalized product against s * t_k (s the half's norm), the
 // tie going up; a zero half (s = 0, product 0) compares 0 against the unscaled thresholds, so
 // it takes the index of y = 0.  Indices are ORed into per-vector words in LDS and stored after a
@@ -39,25 +42,25 @@ constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 128
 constexpr int kRS = 68;
 constexpr int kXS = 132;
 
+// acc[mb][r] = unnormalized coordinate 16 mb + 4 g + r of vector v (this lane's), s = its norm.
 template <int B, int OFF, int WT>
-__device__ __forceinline__ void quantize_pack(const float (&acc)[4][4], const float (&su)[4], const CodebookArgs& cb,
-                                              uint32_t (*wbuf)[WT], int vbase, int jl) {
+__device__ __forceinline__ void quantize_pack(const f32x4 (&acc)[4], float s, const CodebookArgs& cb,
+                                              uint32_t* __restrict__ words, int g) {
   constexpr int K = 1 << B;
+  float thr[K - 1];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float thr[K - 1];
+  for (int q = 0; q < K - 1; ++q) thr[q] = s > 0.f ? s * cb.t[q] : cb.t[q];
 #pragma unroll
-    for (int q = 0; q < K - 1; ++q) thr[q] = su[u] > 0.f ? su[u] * cb.t[q] : cb.t[q];
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int r = 0; r < 4; ++r) {
       uint32_t idx = 0;
 #pragma unroll
-      for (int q = 0; q < K - 1; ++q) idx += acc[k][u] >= thr[q] ? 1u : 0u;
-      const int p = (jl + 16 * k) * B, w = p >> 5, sh = p & 31;
-      atomicOr(&wbuf[vbase + u][OFF + w], idx << sh);
-      if (sh + B > 32) atomicOr(&wbuf[vbase + u][OFF + w + 1], idx >> (32 - sh));
+      for (int q = 0; q < K - 1; ++q) idx += acc[mb][r] >= thr[q] ? 1u : 0u;
+      const int p = (16 * mb + 4 * g + r) * B, w = p >> 5, sh = p & 31;
+      atomicOr(&words[OFF + w], idx << sh);
+      if (sh + B > 32) atomicOr(&words[OFF + w + 1], idx >> (32 - sh));
     }
-  }
 }
 
 template <int BO, int BR, bool BF16IN>
@@ -80,14 +83,15 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 
   for (int e = tid; e < 2 * 64 * 64; e += kEncWaves * 64) {
     const int p = e >> 12, r = (e >> 6) & 63, c = e & 63;
-    rs[p][r][c] = (p ? rr : ro)[r * 64 + c];
+    rs[p][r][(c & 3) * 16 + (c >> 2)] = (p ? rr : ro)[r * 64 + c];
   }
   if (tid < kSplitD) inv[order[(int64_t)h * kSplitD + tid]] = tid;
   __syncthreads();
 
-  const int jl = lane & 15, vq = lane >> 4;
+  const int ln = lane & 15, lg = lane >> 4;
   const int ch = tid & 127, vs = tid >> 7;   // staging: channel ch of round vectors vs + 4 m
-  const int pc = inv[ch];
+  // position of channel ch in the staged vector: its half, then [term][step] inside the half
+  const int pc = (inv[ch] & 64) | ((inv[ch] & 3) << 4) | ((inv[ch] >> 2) & 15);
 
   for (int round = 0; round < kEncRounds; ++round) {
     const int64_t tr = tblk + (int64_t)round * kRoundRows;
@@ -122,40 +126,30 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
       s2 += __shfl_xor(s2, 16);
       s2 += __shfl_xor(s2, 32);
     }
-    if (lane < kGroupRows) nrm[part][grp * kGroupRows + lane] = sqrtf(s2);
-    float su[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) su[u] = sqrtf(__shfl(s2, 4 * vq + u));
+    const float s = sqrtf(s2);   // the half's norm of vector ln (every lane quarter holds it)
+    if (lane < kGroupRows) nrm[part][grp * kGroupRows + lane] = s;
 
-    float acc[4][4];
+    f32x4 acc[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* xb = &xs[grp][ln][part * 64 + lg * 16];
+    const float* rb = &rs[part][ln][lg * 16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[k][u] = 0.f;
-    const float* xb = &xs[grp][4 * vq][part * 64];
-    const float* rb = &rs[part][jl][0];
-#pragma unroll 4
-    for (int i = 0; i < 64; i += 4) {
-      f32x4 a[4], xv[4];
+    for (int s0 = 0; s0 < 16; s0 += 4) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(xb + s0);
+      f32x4 a[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) a[k] = *reinterpret_cast<const f32x4*>(rb + 16 * k * kRS + i);
+      for (int mb = 0; mb < 4; ++mb) a[mb] = *reinterpret_cast<const f32x4*>(rb + 16 * mb * kRS + s0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xv[u] = *reinterpret_cast<const f32x4*>(xb + u * kXS + i);
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc[k][u] = fmaf(a[k].x, xv[u].x, acc[k][u]);
-          acc[k][u] = fmaf(a[k].y, xv[u].y, acc[k][u]);
-          acc[k][u] = fmaf(a[k].z, xv[u].z, acc[k][u]);
-          acc[k][u] = fmaf(a[k].w, xv[u].w, acc[k][u]);
-        }
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mb][e], b[e], acc[mb], 0, 0, 0);
     }
-    const int vbase = grp * kGroupRows + 4 * vq;
+    uint32_t* words = wbuf[grp * kGroupRows + ln];
     if (part == 0)
-      quantize_pack<BO, 0, WT>(acc, su, cbo, wbuf, vbase, jl);
+      quantize_pack<BO, 0, WT>(acc, s, cbo, words, lg);
     else
-      quantize_pack<BR, WO, WT>(acc, su, cbr, wbuf, vbase, jl);
+      quantize_pack<BR, WO, WT>(acc, s, cbr, words, lg);
     __syncthreads();
 
     for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) {
