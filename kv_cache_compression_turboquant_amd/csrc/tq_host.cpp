@@ -1159,6 +1159,7 @@ tq_status tq_encode_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t 
   if (dt != TQ_BF16 && dt != TQ_F32) return fail(TQ_EUNSUPPORTED, "%s: dtype %d", fn, (int)dt);
   if ((int64_t)B * H * T == 0) return ok();
   if (!x_dev) return fail(TQ_EINVAL, "%s: null x", fn);
+  if (reinterpret_cast<uintptr_t>(x_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: x must be 16-byte aligned", fn);
   return check_launch(tq::launch_encode_split(x_dev, dt == TQ_BF16, (int64_t)B * H, H, T, split->order_dev,
                                               rot_o->r32_dev, rot_r->r32_dev, cb_o->args, cb_r->args, out_o->idx,
                                               out_o->norms, out_r->idx, out_r->norms, as_stream(stream)),

@@ -51,16 +51,21 @@ __device__ __forceinline__ void quantize_pack(const f32x4 (&acc)[4], float s, co
 #pragma unroll
   for (int q = 0; q < K - 1; ++q) thr[q] = s > 0.f ? s * cb.t[q] : cb.t[q];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    // coordinates 16 mb + 4 g .. + 3 are consecutive: one 4 B-bit field, ORed in with at most two
+    // LDS atomics (the other three lanes of the vector fill the rest of the block's bits)
+    uint32_t f = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint32_t idx = 0;
 #pragma unroll
       for (int q = 0; q < K - 1; ++q) idx += acc[mb][r] >= thr[q] ? 1u : 0u;
-      const int p = (16 * mb + 4 * g + r) * B, w = p >> 5, sh = p & 31;
-      atomicOr(&words[OFF + w], idx << sh);
-      if (sh + B > 32) atomicOr(&words[OFF + w + 1], idx >> (32 - sh));
+      f |= idx << (r * B);
     }
+    const int p = (16 * mb + 4 * g) * B, w = p >> 5, sh = p & 31;
+    atomicOr(&words[OFF + w], f << sh);
+    if (sh + 4 * B > 32) atomicOr(&words[OFF + w + 1], f >> (32 - sh));
+  }
 }
 
 template <int BO, int BR, bool BF16IN>
@@ -89,22 +94,47 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
   __syncthreads();
 
   const int ln = lane & 15, lg = lane >> 4;
-  const int ch = tid & 127, vs = tid >> 7;   // staging: channel ch of round vectors vs + 4 m
-  // position of channel ch in the staged vector: its half, then [term][step] inside the half
-  const int pc = (inv[ch] & 64) | ((inv[ch] & 3) << 4) | ((inv[ch] >> 2) & 15);
+  // staging: thread tid loads channels c8 .. c8 + 7 of round vectors (tid >> 4) + 32 k, k = 0, 1,
+  // and writes each to its position in the staged vector: its half, then [term][step] inside it
+  const int c8 = (tid & 15) * 8, vs = tid >> 4;
+  int pos[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = inv[c8 + i];
+    pos[i] = (pc & 64) | ((pc & 3) << 4) | ((pc >> 2) & 15);
+  }
 
   for (int round = 0; round < kEncRounds; ++round) {
     const int64_t tr = tblk + (int64_t)round * kRoundRows;
-#pragma unroll 4
-    for (int m = 0; m < kRoundRows / 4; ++m) {
-      const int v = vs + 4 * m;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int v = vs + 32 * k;
       const int64_t t = tr + v;
-      float val = 0.f;
+      float val[8];
       if (t < T) {
-        const int64_t src = (seq * T + t) * kSplitD + ch;
-        val = BF16IN ? bf16_val(static_cast<const uint16_t*>(x)[src]) : static_cast<const float*>(x)[src];
+        const int64_t src = (seq * T + t) * kSplitD + c8;
+        if (BF16IN) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + src);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            val[2 * i] = bf16_val(w[i] & 0xffffu);
+            val[2 * i + 1] = bf16_val(w[i] >> 16);
+          }
+        } else {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + src);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + src + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            val[i] = a[i];
+            val[4 + i] = b[i];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) val[i] = 0.f;
       }
-      xs[v >> 4][v & 15][pc] = val;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[v >> 4][v & 15][pos[i]] = val[i];
     }
     for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) (&wbuf[0][0])[e] = 0u;
     __syncthreads();
