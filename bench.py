@@ -24,9 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# fp32 FMA on the vector ALUs without packed-fp32 instructions (the library is built without them):
-# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz, in TFLOP/s
-FP32_FMA_PEAK = 78.6
+# dense fp32 MFMA peak of the MI355X, TFLOP/s
+FP32_MFMA_PEAK = 157.3
 CACHE_DEFEAT_BYTES = 1.5e9
 
 
@@ -446,7 +445,7 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         res.update({"bits_outlier": bo, "bits_rest": br, "bits_per_channel": (bo + br) / 2,
                     "step_ms": step_ms, "scores_per_s_step": outs[0].numel() / step_ms * 1e3,
                     "encode_ms": enc_ms, "encode_gbs": enc_bytes / enc_ms / 1e6,
-                    "encode_tflops": enc_flop / enc_ms / 1e9, "encode_alu_frac": enc_flop / enc_ms / 1e9 / FP32_FMA_PEAK,
+                    "encode_tflops": enc_flop / enc_ms / 1e9, "encode_mfma_frac": enc_flop / enc_ms / 1e9 / FP32_MFMA_PEAK,
                     "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
                     "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
