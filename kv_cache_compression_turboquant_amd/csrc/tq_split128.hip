@@ -17,7 +17,8 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // ---------------------------------------------------------------------------------------
-// Encode.  A block of 8 waves takes 128 consecutive tokens of one sequence in two rounds of 64.
+// Encode.  A block of 8 waves takes 256 consecutive tokens of one sequence in four rounds of 64
+// (the next round's keys load into registers while the current one computes).
 // Each round stages its 64 vectors in LDS in channel order (outlier channels first, fp32), so
 // each half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
 // 0..3 (16 vectors each) and waves 4..7 the other halves, so a wave's bit width is uniform.
@@ -37,8 +38,8 @@ using IC = std::integral_constant<int, V>;
 constexpr int kEncWaves = 8;
 constexpr int kGroupRows = 16;                        // vectors per wave group per round
 constexpr int kRoundRows = 4 * kGroupRows;            // 64
-constexpr int kEncRounds = 2;
-constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 128
+constexpr int kEncRounds = 4;
+constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 256
 constexpr int kRS = 68;
 constexpr int kXS = 132;
 
@@ -104,40 +105,49 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     pos[i] = (pc & 64) | ((pc & 3) << 4) | ((pc >> 2) & 15);
   }
 
+  // The next round's keys are loaded into registers while the current round computes.
+  constexpr int NR = BF16IN ? 1 : 2;   // 16-byte loads per 8 channels
+  u32x4 raw[2][NR];
+  auto load_round = [&](int64_t tr) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t t = tr + vs + 32 * k;
+      if (t < T) {
+        const int64_t src = (seq * T + t) * kSplitD + c8;
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+          raw[k][j] = BF16IN ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + src)
+                             : *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + src + 4 * j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) raw[k][j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  load_round(tblk);
+
   for (int round = 0; round < kEncRounds; ++round) {
     const int64_t tr = tblk + (int64_t)round * kRoundRows;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int v = vs + 32 * k;
-      const int64_t t = tr + v;
       float val[8];
-      if (t < T) {
-        const int64_t src = (seq * T + t) * kSplitD + c8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         if (BF16IN) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + src);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            val[2 * i] = bf16_val(w[i] & 0xffffu);
-            val[2 * i + 1] = bf16_val(w[i] >> 16);
-          }
+          val[2 * i] = bf16_val(raw[k][0][i] & 0xffffu);
+          val[2 * i + 1] = bf16_val(raw[k][0][i] >> 16);
         } else {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + src);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + src + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            val[i] = a[i];
-            val[4 + i] = b[i];
-          }
+          val[i] = __uint_as_float(raw[k][0][i]);
+          val[4 + i] = __uint_as_float(raw[k][NR - 1][i]);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) val[i] = 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) xs[v >> 4][v & 15][pos[i]] = val[i];
     }
     for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) (&wbuf[0][0])[e] = 0u;
     __syncthreads();
+    if (round + 1 < kEncRounds) load_round(tr + kRoundRows);
 
     // The half's squared norm of vector (lane & 15): four partial sums of 16 squares, then
     // summed across the four lane quarters.
