@@ -22,13 +22,15 @@ using IC = std::integral_constant<int, V>;
 // Each round stages its 64 vectors in LDS in channel order (outlier channels first, fp32), so
 // each half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
 // 0..3 (16 vectors each) and waves 4..7 the other halves, so a wave's bit width is uniform.
-// The rotation is Y = R X on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32 products and
-// sums like the vector ALU): A = 16 rotation rows x 4 contraction terms, B = 4 terms x the
-// group's 16 vectors, 4 output blocks x 16 steps per half.  Lane l = n + 16 g supplies A row n,
-// B column n and contraction term g of each step and ends with coordinates 16 mb + 4 g + r of
-// vector n.  Both LDS operands are stored with the 16 steps of a term contiguous ([g][step]),
-// so one 16-byte read feeds 4 steps; rows are padded (68 and 132 floats) so that the 16 rows a
-// read touches fall in distinct banks.
+// The rotation is Y = R X on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with fp32 sums:
+// R as bf16 hi + lo (two passes, about 16 significant bits, as in the single-code encode), x as
+// bf16 (exact for bf16 keys; fp32 keys add a third pass with the low part of x).  A = 16
+// rotation rows x 32 contraction terms, B = 32 terms x the group's 16 vectors, 4 output blocks x
+// 2 steps per half.  Lane l = n + 16 g supplies A row n, B column n and terms 8 g .. 8 g + 7 of
+// each step and ends with coordinates 16 mb + 4 g + r of vector n.  The A fragments are built
+// once per block in LDS (lane-major, so the reads are conflict-free); the vectors are staged as
+// fp32 in channel order, rows padded to 132 floats so that the 16 rows a read touches fall in
+// distinct banks.
 // Quantization compares the unnormalized product against s * t_k (s the half's norm), the
 // tie going up; a zero half (s = 0, product 0) compares 0 against the unscaled thresholds, so
 // it takes the index of y = 0.  Indices are ORed into per-vector words in LDS and stored after a
@@ -40,7 +42,6 @@ constexpr int kGroupRows = 16;                        // vectors per wave group 
 constexpr int kRoundRows = 4 * kGroupRows;            // 64
 constexpr int kEncRounds = 4;
 constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 256
-constexpr int kRS = 68;
 constexpr int kXS = 132;
 
 // acc[mb][r] = unnormalized coordinate 16 mb + 4 g + r of vector v (this lane's), s = its norm.
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     const float* __restrict__ rr, CodebookArgs cbo, CodebookArgs cbr, uint32_t* __restrict__ idx_o,
     float* __restrict__ norm_o, uint32_t* __restrict__ idx_r, float* __restrict__ norm_r) {
   constexpr int WO = 2 * BO, WR = 2 * BR, WT = WO + WR;
-  __shared__ __align__(16) float rs[2][64][kRS];
+  __shared__ u32x4 afr[2][2][4][2][64];   // [half][hi, lo][out block][step][lane]: bf16 A fragments
   __shared__ __align__(16) float xs[4][kGroupRows][kXS];
   __shared__ int inv[kSplitD];
   __shared__ float nrm[2][kRoundRows];
@@ -87,23 +88,34 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
   const int h = (int)(seq % H);
   const int64_t tblk = (int64_t)blockIdx.x * kEncBlockRows;
 
-  for (int e = tid; e < 2 * 64 * 64; e += kEncWaves * 64) {
-    const int p = e >> 12, r = (e >> 6) & 63, c = e & 63;
-    rs[p][r][(c & 3) * 16 + (c >> 2)] = (p ? rr : ro)[r * 64 + c];
+  // A fragments: lane l = n + 16 g of (half p, block mb, step st) holds R[16 mb + n][32 st + 8 g + e],
+  // e = 0..7, as bf16 hi (round to nearest) and lo (the remainder, rounded)
+  for (int e = tid; e < 2 * 4 * 2 * 64; e += kEncWaves * 64) {
+    const int l = e & 63, st = (e >> 6) & 1, mb = (e >> 7) & 3, p = e >> 9;
+    const float* src = (p ? rr : ro) + (16 * mb + (l & 15)) * 64 + 32 * st + 8 * (l >> 4);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t h0 = bf16_bits(f[2 * w]), h1 = bf16_bits(f[2 * w + 1]);
+      hi[w] = h0 | (h1 << 16);
+      lo[w] = bf16_bits(f[2 * w] - bf16_val(h0)) | (bf16_bits(f[2 * w + 1] - bf16_val(h1)) << 16);
+    }
+    afr[p][0][mb][st][l] = hi;
+    afr[p][1][mb][st][l] = lo;
   }
   if (tid < kSplitD) inv[order[(int64_t)h * kSplitD + tid]] = tid;
   __syncthreads();
 
   const int ln = lane & 15, lg = lane >> 4;
   // staging: thread tid loads channels c8 .. c8 + 7 of round vectors (tid >> 4) + 32 k, k = 0, 1,
-  // and writes each to its position in the staged vector: its half, then [term][step] inside it
+  // and writes each to its position in the staged vector (outlier half first)
   const int c8 = (tid & 15) * 8, vs = tid >> 4;
   int pos[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pc = inv[c8 + i];
-    pos[i] = (pc & 64) | ((pc & 3) << 4) | ((pc >> 2) & 15);
-  }
+  for (int i = 0; i < 8; ++i) pos[i] = inv[c8 + i];
 
   // The next round's keys are loaded into registers while the current round computes.
   constexpr int NR = BF16IN ? 1 : 2;   // 16-byte loads per 8 channels
@@ -172,18 +184,26 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     f32x4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* xb = &xs[grp][ln][part * 64 + lg * 16];
-    const float* rb = &rs[part][ln][lg * 16];
+    const float* xb = &xs[grp][ln][part * 64 + 8 * lg];
 #pragma unroll
-    for (int s0 = 0; s0 < 16; s0 += 4) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(xb + s0);
-      f32x4 a[4];
+    for (int st = 0; st < 2; ++st) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(xb + 32 * st);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(xb + 32 * st + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      u32x4 bh, bl;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) a[mb] = *reinterpret_cast<const f32x4*>(rb + 16 * mb * kRS + s0);
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t h0 = bf16_bits(f[2 * w]), h1 = bf16_bits(f[2 * w + 1]);
+        bh[w] = h0 | (h1 << 16);
+        bl[w] = BF16IN ? 0u : (bf16_bits(f[2 * w] - bf16_val(h0)) | (bf16_bits(f[2 * w + 1] - bf16_val(h1)) << 16));
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mb][e], b[e], acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < 4; ++mb) {
+        const u32x4 ah = afr[part][0][mb][st][lane], al = afr[part][1][mb][st][lane];
+        acc[mb] = mfma_bf16(ah, bh, acc[mb]);
+        acc[mb] = mfma_bf16(al, bh, acc[mb]);
+        if (!BF16IN) acc[mb] = mfma_bf16(ah, bl, acc[mb]);
+      }
     }
     uint32_t* words = wbuf[grp * kGroupRows + ln];
     if (part == 0)
