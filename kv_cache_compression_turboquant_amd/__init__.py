@@ -394,6 +394,8 @@ def encode_split(x, split, cb_o, cb_r, rot_o, rot_r, out=None):
     """Split encode of keys x [B, H, T, 128] (bf16 or fp32): (outlier codes, rest codes), each a
     rows-layout MSE Packed with d = 64 and n = B*H*T."""
     B, H, T, d = x.shape
+    if not x.is_contiguous():
+        raise TQError(1, "encode_split: x must be contiguous")
     n = B * H * T
     if out is None:
         out = (alloc_packed(n, 64, cb_o.b, "mse", device=x.device), alloc_packed(n, 64, cb_r.b, "mse", device=x.device))
@@ -412,6 +414,8 @@ def scores_split(q, K, Hkv, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
     [B, Hkv, T]."""
     torch = _torch()
     B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise TQError(1, "scores_split: q must be contiguous")
     T = K[0].n // max(B * Hkv, 1)
     if out is None:
         out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
