@@ -43,6 +43,7 @@ constexpr int kRoundRows = 4 * kGroupRows;            // 64
 constexpr int kEncRounds = 4;
 constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 256
 constexpr int kXS = 132;
+constexpr int kXH = 136;
 
 // acc[mb][r] = unnormalized coordinate 16 mb + 4 g + r of vector v (this lane's), s = its norm.
 template <int B, int OFF, int WT>
@@ -77,7 +78,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     float* __restrict__ norm_o, uint32_t* __restrict__ idx_r, float* __restrict__ norm_r) {
   constexpr int WO = 2 * BO, WR = 2 * BR, WT = WO + WR;
   __shared__ u32x4 afr[2][2][4][2][64];   // [half][hi, lo][out block][step][lane]: bf16 A fragments
+  // staged vectors: fp32 rows of kXS floats, or for bf16 keys the bf16 values as they are, rows of
+  // kXH halves (both padded so that the 16 rows a 16-byte read touches fall in distinct banks)
   __shared__ __align__(16) float xs[4][kGroupRows][kXS];
+  uint16_t (*xh)[kGroupRows][kXH] = reinterpret_cast<uint16_t (*)[kGroupRows][kXH]>(&xs[0][0][0]);
   __shared__ int inv[kSplitD];
   __shared__ float nrm[2][kRoundRows];
   __shared__ uint32_t wbuf[kRoundRows][WT];
@@ -143,19 +147,19 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int v = vs + 32 * k;
-      float val[8];
+      if constexpr (BF16IN) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (BF16IN) {
-          val[2 * i] = bf16_val(raw[k][0][i] & 0xffffu);
-          val[2 * i + 1] = bf16_val(raw[k][0][i] >> 16);
-        } else {
-          val[i] = __uint_as_float(raw[k][0][i]);
-          val[4 + i] = __uint_as_float(raw[k][NR - 1][i]);
+        for (int i = 0; i < 4; ++i) {
+          xh[v >> 4][v & 15][pos[2 * i]] = (uint16_t)(raw[k][0][i] & 0xffffu);
+          xh[v >> 4][v & 15][pos[2 * i + 1]] = (uint16_t)(raw[k][0][i] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xs[v >> 4][v & 15][pos[i]] = __uint_as_float(raw[k][0][i]);
+          xs[v >> 4][v & 15][pos[4 + i]] = __uint_as_float(raw[k][NR - 1][i]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs[v >> 4][v & 15][pos[i]] = val[i];
     }
     for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) (&wbuf[0][0])[e] = 0u;
     __syncthreads();
@@ -163,17 +167,30 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 
     // The half's squared norm of vector (lane & 15): four partial sums of 16 squares, then
     // summed across the four lane quarters.
-    float s2;
+    float s2 = 0.f;
     {
-      const float* row = &xs[grp][lane & 15][part * 64 + (lane >> 4) * 16];
-      s2 = 0.f;
+      if constexpr (BF16IN) {
+        const uint16_t* row = &xh[grp][lane & 15][part * 64 + (lane >> 4) * 16];
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(row + i);
-        s2 = fmaf(a.x, a.x, s2);
-        s2 = fmaf(a.y, a.y, s2);
-        s2 = fmaf(a.z, a.z, s2);
-        s2 = fmaf(a.w, a.w, s2);
+        for (int i = 0; i < 16; i += 8) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(row + i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float lo = bf16_val(a[w] & 0xffffu), hi = bf16_val(a[w] >> 16);
+            s2 = fmaf(lo, lo, s2);
+            s2 = fmaf(hi, hi, s2);
+          }
+        }
+      } else {
+        const float* row = &xs[grp][lane & 15][part * 64 + (lane >> 4) * 16];
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(row + i);
+          s2 = fmaf(a.x, a.x, s2);
+          s2 = fmaf(a.y, a.y, s2);
+          s2 = fmaf(a.z, a.z, s2);
+          s2 = fmaf(a.w, a.w, s2);
+        }
       }
       s2 += __shfl_xor(s2, 16);
       s2 += __shfl_xor(s2, 32);
@@ -184,18 +201,23 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     f32x4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* xb = &xs[grp][ln][part * 64 + 8 * lg];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(xb + 32 * st);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(xb + 32 * st + 4);
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       u32x4 bh, bl;
+      if constexpr (BF16IN) {
+        bh = *reinterpret_cast<const u32x4*>(&xh[grp][ln][part * 64 + 32 * st + 8 * lg]);
+        bl = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const float* xb = &xs[grp][ln][part * 64 + 32 * st + 8 * lg];
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(xb);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(xb + 4);
+        const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t h0 = bf16_bits(f[2 * w]), h1 = bf16_bits(f[2 * w + 1]);
-        bh[w] = h0 | (h1 << 16);
-        bl[w] = BF16IN ? 0u : (bf16_bits(f[2 * w] - bf16_val(h0)) | (bf16_bits(f[2 * w + 1] - bf16_val(h1)) << 16));
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t h0 = bf16_bits(f[2 * w]), h1 = bf16_bits(f[2 * w + 1]);
+          bh[w] = h0 | (h1 << 16);
+          bl[w] = bf16_bits(f[2 * w] - bf16_val(h0)) | (bf16_bits(f[2 * w + 1] - bf16_val(h1)) << 16);
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
