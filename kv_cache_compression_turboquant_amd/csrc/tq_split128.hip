@@ -19,8 +19,8 @@ using IC = std::integral_constant<int, V>;
 // ---------------------------------------------------------------------------------------
 // Encode.  A block of 8 waves takes 256 consecutive tokens of one sequence in four rounds of 64
 // (the next round's keys load into registers while the current one computes).
-// Each round stages its 64 vectors in LDS in channel order (outlier channels first, fp32), so
-// each half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
+// Each round stages its 64 vectors in LDS in channel order (outlier channels first), so each
+// half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
 // 0..3 (16 vectors each) and waves 4..7 the other halves, so a wave's bit width is uniform.
 // The rotation is Y = R X on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with fp32 sums:
 // R as bf16 hi + lo (two passes, about 16 significant bits, as in the single-code encode), x as
@@ -28,9 +28,10 @@ using IC = std::integral_constant<int, V>;
 // rotation rows x 32 contraction terms, B = 32 terms x the group's 16 vectors, 4 output blocks x
 // 2 steps per half.  Lane l = n + 16 g supplies A row n, B column n and terms 8 g .. 8 g + 7 of
 // each step and ends with coordinates 16 mb + 4 g + r of vector n.  The A fragments are built
-// once per block in LDS (lane-major, so the reads are conflict-free); the vectors are staged as
-// fp32 in channel order, rows padded to 132 floats so that the 16 rows a read touches fall in
-// distinct banks.
+// once per block in LDS (lane-major, so the reads are conflict-free).  bf16 keys are staged as
+// they are (rows of 136 halves), so one 16-byte read is the B operand; fp32 keys are staged as
+// fp32 (rows of 132 floats) and split into hi and lo when read.  Both paddings put the 16 rows a
+// read touches in distinct banks.
 // Quantization compares the unnormalized product against s * t_k (s the half's norm), the
 // tie going up; a zero half (s = 0, product 0) compares 0 against the unscaled thresholds, so
 // it takes the index of y = 0.  Indices are ORed into per-vector words in LDS and stored after a
