@@ -83,7 +83,7 @@ def test_encode_split_matches_oracle(dev, rots, bo, br, dtype):
 
 
 @pytest.mark.parametrize("bo,br", [(3, 2), (4, 3)])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (2, 2), (16, 2), (6, 2), (12, 3)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (2, 2), (16, 2), (6, 2), (12, 3), (64, 1)])
 def test_scores_split_matches_oracle(dev, rots, bo, br, hq, hkv):
     B, T = 2, 300
     x, xt = _keys(B, hkv, T, seed=3)
@@ -169,6 +169,9 @@ def test_split_errors(dev, rots):
     with pytest.raises(tq.TQError) as e:            # bits of the packed set and the codebook differ
         tq.scores_split(torch.zeros((1, 8, 128), device=dev), (po, pr), 2, sp, tq.codebook(M, 4), cbr, *rots)
     assert e.value.status == 2
+    with pytest.raises(tq.TQError) as e:            # GQA ratio above the 64 the score kernel takes
+        tq.scores_split(torch.zeros((1, 130, 128), device=dev), (po, pr), 2, sp, cbo, cbr, *rots)
+    assert e.value.status == 3
     ws = torch.empty((16,), dtype=torch.uint8, device=dev)
     with pytest.raises(tq.TQError) as e:            # workspace too small
         tq.scores_split(torch.zeros((1, 8, 128), device=dev), (po, pr), 2, sp, cbo, cbr, *rots, ws=ws)
