@@ -17,7 +17,7 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // ---------------------------------------------------------------------------------------
-// Encode.  A block of 8 waves takes 256 consecutive tokens of one sequence in four rounds of 64
+// Encode.  A block of 8 waves takes 512 consecutive tokens of one sequence in eight rounds of 64
 // (the next round's keys load into registers while the current one computes).
 // Each round stages its 64 vectors in LDS in channel order (outlier channels first), so each
 // half is a contiguous 64-vector.  Waves 0..3 rotate the outlier halves of vector groups
@@ -41,8 +41,8 @@ using IC = std::integral_constant<int, V>;
 constexpr int kEncWaves = 8;
 constexpr int kGroupRows = 16;                        // vectors per wave group per round
 constexpr int kRoundRows = 4 * kGroupRows;            // 64
-constexpr int kEncRounds = 4;
-constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 256
+constexpr int kEncRounds = 8;
+constexpr int kEncBlockRows = kRoundRows * kEncRounds;  // 512
 constexpr int kXS = 132;
 constexpr int kXH = 136;
 
