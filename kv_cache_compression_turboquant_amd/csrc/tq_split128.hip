@@ -256,25 +256,30 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 }
 
 // ---------------------------------------------------------------------------------------
-// Query prologue: one block of 128 threads per query head.  The query is gathered into the
-// channel order of its KV head; thread j then forms coordinate j & 63 of R_o q_O (j < 64) or of
-// R_r q_R, reading R^T row-major so that the threads' loads are consecutive.
+// Query prologue: one block of 512 threads per query head.  The query is gathered into the
+// channel order of its KV head; thread (j, quarter) then sums 16 of the 64 terms of coordinate
+// j & 63 of R_o q_O (j < 64) or of R_r q_R, reading R^T row-major so that the threads' loads are
+// consecutive, and the four partial sums are added in LDS (short dependent chains: the kernel
+// is all latency).
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_qprep_split(const float* __restrict__ q, int Hq, int Hkv,
+__global__ __launch_bounds__(512) void k_qprep_split(const float* __restrict__ q, int Hq, int Hkv,
                                                      const int32_t* __restrict__ order, const float* __restrict__ rto,
                                                      const float* __restrict__ rtr, float* __restrict__ qws) {
   __shared__ float qs[kSplitD];
-  const int j = threadIdx.x;
+  __shared__ float part_sum[4][kSplitD];
+  const int tid = threadIdx.x, j = tid & (kSplitD - 1), quarter = tid >> 7;
   const int64_t bh = blockIdx.x;
   const int hq = (int)(bh % Hq), hk = hq / (Hq / Hkv);
-  qs[j] = q[bh * kSplitD + order[(int64_t)hk * kSplitD + j]];
+  if (tid < kSplitD) qs[j] = q[bh * kSplitD + order[(int64_t)hk * kSplitD + j]];
   __syncthreads();
-  const int part = j >> 6, jj = j & 63;
-  const float* rt = part ? rtr : rto;
+  const int half = j >> 6, jj = j & 63;
+  const float* rt = half ? rtr : rto;
   float a = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < 64; ++i) a = fmaf(rt[i * 64 + jj], qs[part * 64 + i], a);
-  qws[bh * kSplitD + j] = a;
+#pragma unroll
+  for (int i = 16 * quarter; i < 16 * quarter + 16; ++i) a = fmaf(rt[i * 64 + jj], qs[half * 64 + i], a);
+  part_sum[quarter][j] = a;
+  __syncthreads();
+  if (tid < kSplitD) qws[bh * kSplitD + j] = (part_sum[0][j] + part_sum[1][j]) + (part_sum[2][j] + part_sum[3][j]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -428,7 +433,7 @@ hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, i
 hipError_t launch_qprep_split(const float* q, int B, int Hq, int Hkv, const int32_t* order, const float* rto,
                               const float* rtr, float* qws, hipStream_t st) {
   if ((int64_t)B * Hq == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_qprep_split, dim3((unsigned)((int64_t)B * Hq)), dim3(128), 0, st, q, Hq, Hkv, order, rto, rtr,
+  hipLaunchKernelGGL(k_qprep_split, dim3((unsigned)((int64_t)B * Hq)), dim3(512), 0, st, q, Hq, Hkv, order, rto, rtr,
                      qws);
   return hipGetLastError();
 }
