@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -330,6 +330,24 @@ tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T,
                           const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o,
                           tq_codebook_t cb_r, tq_rotation_t rot_o, tq_rotation_t rot_r,
                           float* scores_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Split codes as a streaming key cache ([TQ] KV-cache example: each decode step appends the new
+ * token's key to the end of the cache; prefill writes the prompt's keys): keys x_dev
+ * [B, H, n_new, 128] (dtype dt) into rows pos .. pos + n_new - 1 of every sequence of split
+ * codes K_o, K_r of capacity T_cap (K_o->n == K_r->n == B*H*T_cap, sequence s owning rows
+ * [s*T_cap, (s+1)*T_cap)).  Every other row is left unchanged.  Otherwise as tq_encode_split,
+ * with TQ_EINVAL for pos + n_new > T_cap or negative n_new / pos. */
+tq_status tq_cache_append_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos,
+                                int64_t T_cap, tq_split_t split, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                                tq_rotation_t rot_o, tq_rotation_t rot_r, tq_packed* K_o, tq_packed* K_r,
+                                void* stream);
+/* tq_scores_split over the first T rows (0 <= T <= T_cap) of every sequence of such a cache:
+ * scores_dev [B, Hq, T].  Otherwise as tq_scores_split, with TQ_EINVAL for T > T_cap. */
+tq_status tq_scores_split_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap,
+                                tq_split_t split, const tq_packed* K_o, const tq_packed* K_r,
+                                tq_codebook_t cb_o, tq_codebook_t cb_r, tq_rotation_t rot_o,
+                                tq_rotation_t rot_r, float* scores_dev, void* ws_dev, size_t ws_bytes,
+                                void* stream);
 
 /* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
  * with k results per query (query operands, one chunk of scores, the running top-k). */

@@ -20,7 +20,8 @@ __all__ = [
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
     "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
-    "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace",
+    "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
+    "cache_append_split", "scores_split_cache",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -425,6 +426,43 @@ def scores_split(q, K, Hkv, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
     check(lib().tq_scores_split(_dptr(q), B, Hq, Hkv, T, split.ptr, ctypes.byref(do), ctypes.byref(dr), cb_o.ptr,
                                 cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
                                 ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def alloc_split_cache(B, H, t_cap, b_o, b_r, device="cuda"):
+    """Split codes of capacity t_cap per sequence: (outlier codes, rest codes), each with
+    B*H*t_cap rows (contents undefined until appended)."""
+    n = B * H * t_cap
+    return (alloc_packed(n, 64, b_o, "mse", device=device), alloc_packed(n, 64, b_r, "mse", device=device))
+
+
+def cache_append_split(K, x, pos, t_cap, split, cb_o, cb_r, rot_o, rot_r):
+    """Append keys x [B, H, n_new, 128] (bf16 or fp32) at row pos of every sequence of the split
+    cache K = (K_o, K_r) of capacity t_cap."""
+    if not x.is_contiguous():
+        raise TQError(1, "cache_append_split: x must be contiguous")
+    B, H, n_new, d = x.shape
+    do, dr = K[0].descriptor(), K[1].descriptor()
+    check(lib().tq_cache_append_split(_dptr(x), _dtype_code(x), B, H, n_new, pos, t_cap, split.ptr, cb_o.ptr,
+                                      cb_r.ptr, rot_o.ptr, rot_r.ptr, ctypes.byref(do), ctypes.byref(dr), _stream()))
+    return K
+
+
+def scores_split_cache(q, K, Hkv, T, t_cap, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
+    """Raw scores [B, Hq, T] of q [B, Hq, 128] fp32 over the first T rows of every sequence of the
+    split cache K = (K_o, K_r) of capacity t_cap."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise TQError(1, "scores_split_cache: q must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((max(scores_split_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
+    do, dr = K[0].descriptor(), K[1].descriptor()
+    check(lib().tq_scores_split_cache(_dptr(q), B, Hq, Hkv, T, t_cap, split.ptr, ctypes.byref(do), ctypes.byref(dr),
+                                      cb_o.ptr, cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
+                                      ws.numel() * ws.element_size(), _stream()))
     return out
 
 

@@ -89,6 +89,10 @@ SIGNATURES = {
     "tq_encode_split": (_I, [_P, _I, _I, _I, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(tq_packed),
                              ctypes.POINTER(tq_packed), _P]),
     "tq_scores_split_workspace": (_SZ, [_I, _I]),
+    "tq_cache_append_split": (_I, [_P, _I, _I, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(tq_packed),
+                                   ctypes.POINTER(tq_packed), _P]),
+    "tq_scores_split_cache": (_I, [_P, _I, _I, _I, _I64, _I64, _P, ctypes.POINTER(tq_packed),
+                                   ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tq_scores_split": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed), _P, _P,
                              _P, _P, _P, _P, _SZ, _P]),
 }

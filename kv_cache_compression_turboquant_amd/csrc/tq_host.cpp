@@ -1126,15 +1126,17 @@ void tq_split_free(tq_split_t sp) {
   delete sp;
 }
 
-// Handles and both halves' packed sets of split-coded keys [B, H, T].
-static tq_status check_split_keys(int B, int H, int64_t T, tq_split_t sp, tq_codebook_t cb_o, tq_codebook_t cb_r,
+// Handles and both halves' packed sets of split-coded keys: B * H sequences of `rows` rows each
+// (rows = T for a packed set, the capacity for a cache).
+static tq_status check_split_keys(int B, int H, int64_t rows, tq_split_t sp, tq_codebook_t cb_o, tq_codebook_t cb_r,
                                   tq_rotation_t rot_o, tq_rotation_t rot_r, const tq_packed* K_o,
                                   const tq_packed* K_r, const char* fn) {
   if (!sp || !cb_o || !cb_r || !rot_o || !rot_r || !K_o || !K_r) return fail(TQ_EINVAL, "%s: null argument", fn);
-  if (B < 0 || H < 0 || T < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (B < 0 || H < 0 || rows < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (sp->H != H) return fail(TQ_ESHAPE, "%s: split has %d heads, keys have %d", fn, sp->H, H);
   if ((int64_t)B * H > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*H=%lld above 65535", fn, (long long)B * H);
-  if (T > kMaxSeqTokens) return fail(TQ_EUNSUPPORTED, "%s: T=%lld above %lld", fn, (long long)T, (long long)kMaxSeqTokens);
+  if (rows > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: %lld rows per sequence above %lld", fn, (long long)rows, (long long)kMaxSeqTokens);
   const int m = tq::kSplitHalf;
   if (cb_o->d != m || cb_r->d != m) return fail(TQ_ESHAPE, "%s: codebooks need d=64", fn);
   if (rot_o->d != m || rot_r->d != m) return fail(TQ_ESHAPE, "%s: rotations need d=64", fn);
@@ -1143,27 +1145,47 @@ static tq_status check_split_keys(int B, int H, int64_t T, tq_split_t sp, tq_cod
   if (st != TQ_OK) return st;
   if (K_o->layout != TQ_LAYOUT_ROWS || K_r->layout != TQ_LAYOUT_ROWS)
     return fail(TQ_EUNSUPPORTED, "%s: split codes use the ROWS layout", fn);
-  const int64_t n = (int64_t)B * H * T;
+  const int64_t n = (int64_t)B * H * rows;
   if (K_o->n != n || K_r->n != n)
-    return fail(TQ_ESHAPE, "%s: packed n=%lld/%lld but B*H*T=%lld", fn, (long long)K_o->n, (long long)K_r->n,
-                (long long)n);
+    return fail(TQ_ESHAPE, "%s: packed n=%lld/%lld but B*H*%lld=%lld", fn, (long long)K_o->n, (long long)K_r->n,
+                (long long)rows, (long long)n);
   return TQ_OK;
+}
+
+// Encode of x [B, H, n_new, 128] into rows pos .. pos + n_new - 1 of every sequence of split codes
+// with `rows` rows per sequence.
+static tq_status encode_split_impl(const char* fn, const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new,
+                                   int64_t pos, int64_t rows, tq_split_t split, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                                   tq_rotation_t rot_o, tq_rotation_t rot_r, tq_packed* out_o, tq_packed* out_r,
+                                   void* stream) {
+  tq_status st = check_split_keys(B, H, rows, split, cb_o, cb_r, rot_o, rot_r, out_o, out_r, fn);
+  if (st != TQ_OK) return st;
+  if (n_new < 0 || pos < 0 || pos + n_new > rows)
+    return fail(TQ_EINVAL, "%s: rows %lld .. %lld outside the %lld rows per sequence", fn, (long long)pos,
+                (long long)(pos + n_new), (long long)rows);
+  if (dt != TQ_BF16 && dt != TQ_F32) return fail(TQ_EUNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  if ((int64_t)B * H * n_new == 0) return ok();
+  if (!x_dev) return fail(TQ_EINVAL, "%s: null x", fn);
+  if (reinterpret_cast<uintptr_t>(x_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: x must be 16-byte aligned", fn);
+  return check_launch(tq::launch_encode_split(x_dev, dt == TQ_BF16, (int64_t)B * H, H, n_new, rows, pos,
+                                              split->order_dev, rot_o->r32_dev, rot_r->r32_dev, cb_o->args, cb_r->args,
+                                              out_o->idx, out_o->norms, out_r->idx, out_r->norms, as_stream(stream)),
+                      fn);
 }
 
 tq_status tq_encode_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t T, tq_split_t split,
                           tq_codebook_t cb_o, tq_codebook_t cb_r, tq_rotation_t rot_o, tq_rotation_t rot_r,
                           tq_packed* out_o, tq_packed* out_r, void* stream) {
-  static const char* fn = "tq_encode_split";
-  tq_status st = check_split_keys(B, H, T, split, cb_o, cb_r, rot_o, rot_r, out_o, out_r, fn);
-  if (st != TQ_OK) return st;
-  if (dt != TQ_BF16 && dt != TQ_F32) return fail(TQ_EUNSUPPORTED, "%s: dtype %d", fn, (int)dt);
-  if ((int64_t)B * H * T == 0) return ok();
-  if (!x_dev) return fail(TQ_EINVAL, "%s: null x", fn);
-  if (reinterpret_cast<uintptr_t>(x_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: x must be 16-byte aligned", fn);
-  return check_launch(tq::launch_encode_split(x_dev, dt == TQ_BF16, (int64_t)B * H, H, T, split->order_dev,
-                                              rot_o->r32_dev, rot_r->r32_dev, cb_o->args, cb_r->args, out_o->idx,
-                                              out_o->norms, out_r->idx, out_r->norms, as_stream(stream)),
-                      fn);
+  return encode_split_impl("tq_encode_split", x_dev, dt, B, H, T, 0, T, split, cb_o, cb_r, rot_o, rot_r, out_o, out_r,
+                           stream);
+}
+
+tq_status tq_cache_append_split(const void* x_dev, tq_dtype dt, int B, int H, int64_t n_new, int64_t pos,
+                                int64_t T_cap, tq_split_t split, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                                tq_rotation_t rot_o, tq_rotation_t rot_r, tq_packed* K_o, tq_packed* K_r,
+                                void* stream) {
+  return encode_split_impl("tq_cache_append_split", x_dev, dt, B, H, n_new, pos, T_cap, split, cb_o, cb_r, rot_o,
+                           rot_r, K_o, K_r, stream);
 }
 
 size_t tq_scores_split_workspace(int B, int Hq) {
@@ -1171,18 +1193,19 @@ size_t tq_scores_split_workspace(int B, int Hq) {
   return (size_t)B * Hq * tq::kSplitD * sizeof(float);
 }
 
-tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
-                          const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o, tq_codebook_t cb_r,
-                          tq_rotation_t rot_o, tq_rotation_t rot_r, float* scores_dev, void* ws_dev,
-                          size_t ws_bytes, void* stream) {
-  static const char* fn = "tq_scores_split";
-  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+// Scores over the first T rows of every sequence of split codes with `rows` rows per sequence.
+static tq_status scores_split_impl(const char* fn, const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t rows,
+                                   tq_split_t split, const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o,
+                                   tq_codebook_t cb_r, tq_rotation_t rot_o, tq_rotation_t rot_r, float* scores_dev,
+                                   void* ws_dev, size_t ws_bytes, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0)
     return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
   if (Hq / Hkv > tq::kSplitMaxRatio)
     return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d above %d", fn, Hq / Hkv, tq::kSplitMaxRatio);
-  tq_status st = check_split_keys(B, Hkv, T, split, cb_o, cb_r, rot_o, rot_r, K_o, K_r, fn);
+  tq_status st = check_split_keys(B, Hkv, rows, split, cb_o, cb_r, rot_o, rot_r, K_o, K_r, fn);
   if (st != TQ_OK) return st;
+  if (T > rows) return fail(TQ_EINVAL, "%s: T=%lld exceeds the %lld rows per sequence", fn, (long long)T, (long long)rows);
   if ((int64_t)Hq * T >= (int64_t(1) << 30))
     return fail(TQ_EUNSUPPORTED, "%s: Hq*T=%lld: a batch's score rows must stay below 4 GB", fn, (long long)Hq * T);
   if ((int64_t)B * Hq * T == 0) return ok();
@@ -1193,9 +1216,25 @@ tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T,
   float* qws = static_cast<float*>(ws_dev);
   hipError_t e = tq::launch_qprep_split(q_dev, B, Hq, Hkv, split->order_dev, rot_o->rt32_dev, rot_r->rt32_dev, qws, hs);
   if (e == hipSuccess)
-    e = tq::launch_scores_split(qws, B, Hq, Hkv, T, cb_o->b, cb_r->b, cb_o->args, cb_r->args, K_o->idx, K_o->norms,
-                                K_r->idx, K_r->norms, scores_dev, hs);
+    e = tq::launch_scores_split(qws, B, Hq, Hkv, T, rows, cb_o->b, cb_r->b, cb_o->args, cb_r->args, K_o->idx,
+                                K_o->norms, K_r->idx, K_r->norms, scores_dev, hs);
   return check_launch(e, fn);
+}
+
+tq_status tq_scores_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
+                          const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                          tq_rotation_t rot_o, tq_rotation_t rot_r, float* scores_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream) {
+  return scores_split_impl("tq_scores_split", q_dev, B, Hq, Hkv, T, T, split, K_o, K_r, cb_o, cb_r, rot_o, rot_r,
+                           scores_dev, ws_dev, ws_bytes, stream);
+}
+
+tq_status tq_scores_split_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap, tq_split_t split,
+                                const tq_packed* K_o, const tq_packed* K_r, tq_codebook_t cb_o, tq_codebook_t cb_r,
+                                tq_rotation_t rot_o, tq_rotation_t rot_r, float* scores_dev, void* ws_dev,
+                                size_t ws_bytes, void* stream) {
+  return scores_split_impl("tq_scores_split_cache", q_dev, B, Hq, Hkv, T, T_cap, split, K_o, K_r, cb_o, cb_r, rot_o,
+                           rot_r, scores_dev, ws_dev, ws_bytes, stream);
 }
 
 size_t tq_search_workspace(int64_t nq, int64_t n, int d, int k) {

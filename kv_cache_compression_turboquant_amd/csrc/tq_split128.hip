@@ -74,7 +74,8 @@ __device__ __forceinline__ void quantize_pack(const f32x4 (&acc)[4], float s, co
 
 template <int BO, int BR, bool BF16IN>
 __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
-    const void* __restrict__ x, int64_t T, int H, const int32_t* __restrict__ order, const float* __restrict__ ro,
+    const void* __restrict__ x, int64_t T, int64_t out_stride, int64_t out_pos, int H, const int32_t* __restrict__ order,
+    const float* __restrict__ ro,
     const float* __restrict__ rr, CodebookArgs cbo, CodebookArgs cbr, uint32_t* __restrict__ idx_o,
     float* __restrict__ norm_o, uint32_t* __restrict__ idx_r, float* __restrict__ norm_r) {
   constexpr int WO = 2 * BO, WR = 2 * BR, WT = WO + WR;
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
       const int v = e / WT, w = e - v * WT;
       const int64_t t = tr + v;
       if (t < T) {
-        const int64_t row = seq * T + t;
+        const int64_t row = seq * out_stride + out_pos + t;
         if (w < WO)
           idx_o[row * WO + w] = wbuf[v][w];
         else
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     if (tid < 2 * kRoundRows) {
       const int v = tid & (kRoundRows - 1);
       const int64_t t = tr + v;
-      if (t < T) (tid < kRoundRows ? norm_o : norm_r)[seq * T + t] = nrm[tid / kRoundRows][v];
+      if (t < T) (tid < kRoundRows ? norm_o : norm_r)[seq * out_stride + out_pos + t] = nrm[tid / kRoundRows][v];
     }
     __syncthreads();  // the next round overwrites xs, wbuf and nrm
   }
@@ -330,7 +331,7 @@ __device__ __forceinline__ void half_dot(const uint32_t (&w)[NW], const float* c
 
 template <int BO, int BR>
 __global__ __launch_bounds__(kScoreThreads) void k_scores_split_d128(
-    const float* __restrict__ qws, int Hq, int Hkv, int64_t T, CodebookArgs cbo, CodebookArgs cbr,
+    const float* __restrict__ qws, int Hq, int Hkv, int64_t T, int64_t seq_stride, CodebookArgs cbo, CodebookArgs cbr,
     const uint32_t* __restrict__ idx_o, const float* __restrict__ norm_o, const uint32_t* __restrict__ idx_r,
     const float* __restrict__ norm_r, float* __restrict__ scores) {
   constexpr int WO = 2 * BO, WR = 2 * BR;
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores_split_d128(
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kScoreThreads + tid;
   const bool live = t < T;
-  const int64_t row = seq * T + (live ? t : T - 1);
+  const int64_t row = seq * seq_stride + (live ? t : T - 1);
   uint32_t wo[WO], wr[WR];
 #pragma unroll
   for (int i = 0; i < WO; i += 2) {
@@ -413,19 +414,20 @@ hipError_t with_bits(int bo, int br, F&& f) {
 
 }  // namespace
 
-hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, int64_t T, const int32_t* order,
-                               const float* ro, const float* rr, const CodebookArgs& cbo, const CodebookArgs& cbr,
-                               uint32_t* idx_o, float* norm_o, uint32_t* idx_r, float* norm_r, hipStream_t st) {
+hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, int64_t T, int64_t out_stride,
+                               int64_t pos, const int32_t* order, const float* ro, const float* rr,
+                               const CodebookArgs& cbo, const CodebookArgs& cbr, uint32_t* idx_o, float* norm_o,
+                               uint32_t* idx_r, float* norm_r, hipStream_t st) {
   if (n_seq <= 0 || T <= 0) return hipSuccess;
   const dim3 grid((unsigned)((T + kEncBlockRows - 1) / kEncBlockRows), (unsigned)n_seq);
   return with_bits(cbo.bits, cbr.bits, [&](auto bo, auto br) -> hipError_t {
     constexpr int BO = decltype(bo)::value, BR = decltype(br)::value;
     if (bf16)
-      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, true>), grid, dim3(kEncWaves * 64), 0, st, x, T, H, order, ro,
-                         rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, true>), grid, dim3(kEncWaves * 64), 0, st, x, T, out_stride, pos,
+                         H, order, ro, rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
     else
-      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, false>), grid, dim3(kEncWaves * 64), 0, st, x, T, H, order, ro,
-                         rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+      hipLaunchKernelGGL((k_encode_split_d128<BO, BR, false>), grid, dim3(kEncWaves * 64), 0, st, x, T, out_stride, pos,
+                         H, order, ro, rr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
     return hipGetLastError();
   });
 }
@@ -438,7 +440,7 @@ hipError_t launch_qprep_split(const float* q, int B, int Hq, int Hkv, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_scores_split(const float* qws, int B, int Hq, int Hkv, int64_t T, int bo, int br,
+hipError_t launch_scores_split(const float* qws, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, int bo, int br,
                                const CodebookArgs& cbo, const CodebookArgs& cbr, const uint32_t* idx_o,
                                const float* norm_o, const uint32_t* idx_r, const float* norm_r, float* scores,
                                hipStream_t st) {
@@ -446,7 +448,7 @@ hipError_t launch_scores_split(const float* qws, int B, int Hq, int Hkv, int64_t
   const dim3 grid((unsigned)((T + kScoreThreads - 1) / kScoreThreads), (unsigned)((int64_t)B * Hkv));
   return with_bits(bo, br, [&](auto o, auto r) -> hipError_t {
     hipLaunchKernelGGL((k_scores_split_d128<decltype(o)::value, decltype(r)::value>), grid, dim3(kScoreThreads), 0, st,
-                       qws, Hq, Hkv, T, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
+                       qws, Hq, Hkv, T, seq_stride, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
     return hipGetLastError();
   });
 }

@@ -224,3 +224,62 @@ def test_split_full_size_sampled(dev, rots):
         ref = no[r] * qo @ ocb_o.centroids[io[r]] + nr[r] * qr @ ocb_r.centroids[ir[r]]
         tol = 1e-3 * np.linalg.norm(q[0, h]) * np.hypot(no[r], nr[r])
         assert abs(sg[0, h, t] - ref) <= tol, (h, t)
+
+
+def test_split_cache_appends_and_scores(dev, rots):
+    # Split codes as a streaming key cache: seeded garbage, then appends of 37, 1, 100 and 1 tokens
+    # at increasing positions ("TurboQuant 详解", KV-cache example: prefill, then one token per
+    # decode step).  Every appended row matches the oracle's encode of that token; every other
+    # row keeps its garbage; scores over the written prefix match the oracle on the cache's codes.
+    B, H, T_CAP, bo, br = 2, 2, 160, 3, 2
+    plan = [(0, 37), (37, 1), (38, 100), (138, 1)]
+    written = 139
+    x, _ = _keys(B, H, T_CAP, seed=13)
+    out = _outliers(x)
+    sp = tq.make_split(out)
+    cbo, cbr = tq.codebook(M, bo), tq.codebook(M, br)
+    K = tq.alloc_split_cache(B, H, T_CAP, bo, br, device=dev)
+    rng = np.random.default_rng(14)
+    garbage = []
+    for p in K:
+        g = rng.integers(-2**31, 2**31, size=tuple(p.idx.shape), dtype=np.int64).astype(np.int32)
+        p.idx.copy_(torch.from_numpy(g))
+        p.norms.copy_(torch.from_numpy(rng.standard_normal(p.n).astype(np.float32)))
+        garbage.append((g.view(np.uint32).copy(), p.norms.cpu().numpy().copy()))
+    xb = torch.from_numpy(wl.f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).view(torch.bfloat16)
+    x = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
+    for pos, n_new in plan:
+        tq.cache_append_split(K, xb[:, :, pos:pos + n_new].contiguous().to(dev), pos, T_CAP, sp, cbo, cbr, *rots)
+    q = wl.gaussian((B, 8, 128), 23)
+    s = tq.scores_split_cache(torch.from_numpy(q).to(dev), K, H, written, T_CAP, sp, cbo, cbr, *rots)
+    torch.cuda.synchronize()
+    rows = (np.arange(B * H)[:, None] * T_CAP + np.arange(written)[None, :]).reshape(-1)
+    untouched = np.setdiff1d(np.arange(B * H * T_CAP), rows)
+    ocb = (oracle.codebook(M, bo), oracle.codebook(M, br))
+    enc = oracle.encode_split(x[:, :, :written], out, R_O, R_R, *ocb)
+    for p, part, cb, (gw, gn) in zip(K, (enc.outlier, enc.rest), ocb, garbage):
+        words = to_np_words(p.idx)
+        gidx = oracle.unpack_bits(words[rows], M, cb.b)
+        bad, _ = check_indices(gidx, part.y.reshape(-1, M), cb, "split cache")
+        np.testing.assert_array_equal(words[rows][~bad], part.words.reshape(-1, 2 * cb.b)[~bad])
+        np.testing.assert_allclose(p.norms.cpu().numpy()[rows], part.norms.reshape(-1), rtol=1e-6)
+        np.testing.assert_array_equal(words[untouched], gw[untouched])
+        np.testing.assert_array_equal(p.norms.cpu().numpy()[untouched], gn[untouched])
+    # scores over the prefix, on the cache's own codes
+    mk = lambda p, b: oracle.EncodedMSE(
+        idx=oracle.unpack_bits(to_np_words(p.idx)[rows], M, b).reshape(B, H, written, M), words=None,
+        norms=p.norms.cpu().numpy().astype(np.float64)[rows].reshape(B, H, written), y=None)
+    encg = oracle.EncodedSplit(order=oracle.channel_order(out, 128), outlier=mk(K[0], bo), rest=mk(K[1], br))
+    ref = oracle.scores_split(q, encg, R_O, R_R, *ocb)
+    knorm = np.sqrt(encg.outlier.norms ** 2 + encg.rest.norms ** 2)
+    for b in range(B):
+        for h in range(8):
+            tol = score_tolerance(q[b, h][None], knorm[b, h // 4])[0]
+            assert np.all(np.abs(s[b, h].cpu().numpy() - ref[b, h]) <= tol), (b, h)
+    # errors: past the capacity, prefix longer than the capacity
+    with pytest.raises(tq.TQError) as e:
+        tq.cache_append_split(K, xb[:, :, :30].contiguous().to(dev), 140, T_CAP, sp, cbo, cbr, *rots)
+    assert e.value.status == 1
+    with pytest.raises(tq.TQError) as e:
+        tq.scores_split_cache(torch.from_numpy(q).to(dev), K, H, T_CAP + 1, T_CAP, sp, cbo, cbr, *rots)
+    assert e.value.status == 1
