@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 
   for (int round = 0; round < kEncRounds; ++round) {
     const int64_t tr = tblk + (int64_t)round * kRoundRows;
+    if (tr >= T) break;   // the block's remaining rounds are past the end (the same for every thread)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int v = vs + 32 * k;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
     }
     for (int e = tid; e < kRoundRows * WT; e += kEncWaves * 64) (&wbuf[0][0])[e] = 0u;
     __syncthreads();
-    if (round + 1 < kEncRounds) load_round(tr + kRoundRows);
+    if (round + 1 < kEncRounds && tr + kRoundRows < T) load_round(tr + kRoundRows);
 
     // The half's squared norm of vector (lane & 15): four partial sums of 16 squares, then
     // summed across the four lane quarters.
