@@ -449,6 +449,44 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_split(cfg, bo, br, cpu_budget)
+    elif name == "c2splitdecode":
+        # Split keys as a streaming key cache on the KV-key workload (1 x 8 KV heads x 32768 tokens,
+        # 32 query heads, 2.5 bits per channel): prefill to T0 tokens in one append, then per step
+        # append one key per sequence and score the prefix.
+        cfg = wl.CONFIGS["c2"]
+        bo, br = 3, 2
+        t_cap = cfg.T
+        t0 = t_cap - warmup - steps
+        kb = wl.kv_keys(cfg)
+        xs = wl.bf16_bits_to_f32(kb[:, :, :4096]).astype(np.float64)
+        outl = np.argsort(-np.mean(xs * xs, axis=(0, 2)), axis=1, kind="stable")[:, :64]
+        del xs
+        keys = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        knew = keys[:, :, t0:].permute(2, 0, 1, 3).contiguous()        # [steps, B, Hkv, d]
+        kpre = keys[:, :, :t0].contiguous()
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        sp = tq.make_split(outl)
+        rot_o, rot_r = tq.make_rotation(64, 3), tq.make_rotation(64, 4)
+        cb_o, cb_r = tq.codebook(64, bo), tq.codebook(64, br)
+        K = tq.alloc_split_cache(cfg.B, cfg.hkv, t_cap, bo, br, device=dev)
+        out = torch.empty((cfg.B * cfg.hq * t_cap,), device=dev)
+        ws = torch.empty(tq.scores_split_workspace(cfg.B, cfg.hq), dtype=torch.uint8, device=dev)
+        pre_ms = _timed(lambda i: tq.cache_append_split(K, kpre, 0, t_cap, sp, cb_o, cb_r, rot_o, rot_r), 2, 1)
+
+        def append(i):
+            tq.cache_append_split(K, knew[i].unsqueeze(2), t0 + i, t_cap, sp, cb_o, cb_r, rot_o, rot_r)
+
+        def step(i):
+            append(i)
+            T = t0 + i + 1
+            tq.scores_split_cache(q, K, cfg.hkv, T, t_cap, sp, cb_o, cb_r, rot_o, rot_r,
+                                  out=out[:cfg.B * cfg.hq * T].view(cfg.B, cfg.hq, T), ws=ws)
+
+        step_ms = _timed(step, steps, warmup)
+        app_ms = _timed(append, steps, 0)
+        res.update({"bits_outlier": bo, "bits_rest": br, "cache": [cfg.B, cfg.hkv, t_cap, cfg.d], "prefill_tokens": t0,
+                    "prefill_ms": pre_ms, "step_ms": step_ms, "append_ms": app_ms,
+                    "decode_scores_per_s": cfg.hq * t_cap / step_ms * 1e3})
     elif name == "peaks":
         # Achievable HBM rates on this machine, for reading the fractions against a measured ceiling as
         # well as the 8 TB/s spec: a plain device copy (reads and writes) and a read-only sum of
@@ -502,7 +540,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4", "peaks", "c2split",
-                                                        "c2split35"],
+                                                        "c2split35", "c2splitdecode"],
                     help="c2 = the headline step; the others print per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "

@@ -457,6 +457,8 @@ def scores_split_cache(q, K, Hkv, T, t_cap, split, cb_o, cb_r, rot_o, rot_r, out
         raise TQError(1, "scores_split_cache: q must be contiguous")
     if out is None:
         out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if not out.is_contiguous() or out.numel() < B * Hq * T:
+        raise TQError(1, "scores_split_cache: out must be contiguous with B*Hq*T elements")
     if ws is None:
         ws = torch.empty((max(scores_split_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
     do, dr = K[0].descriptor(), K[1].descriptor()
