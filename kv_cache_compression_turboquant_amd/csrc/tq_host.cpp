@@ -1168,7 +1168,8 @@ static tq_status encode_split_impl(const char* fn, const void* x_dev, tq_dtype d
   if (!x_dev) return fail(TQ_EINVAL, "%s: null x", fn);
   if (reinterpret_cast<uintptr_t>(x_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: x must be 16-byte aligned", fn);
   return check_launch(tq::launch_encode_split(x_dev, dt == TQ_BF16, (int64_t)B * H, H, n_new, rows, pos,
-                                              split->order_dev, rot_o->r32_dev, rot_r->r32_dev, cb_o->args, cb_r->args,
+                                              split->order_dev, rot_o->r32_dev, rot_r->r32_dev, rot_o->rt32_dev,
+                                              rot_r->rt32_dev, cb_o->args, cb_r->args,
                                               out_o->idx, out_o->norms, out_r->idx, out_r->norms, as_stream(stream)),
                       fn);
 }

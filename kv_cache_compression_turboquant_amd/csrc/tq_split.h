@@ -14,11 +14,13 @@ constexpr int kSplitMaxRatio = 64;   // query heads per KV head the score kernel
 // order [H, 128] int32 on the device: per head, the outlier channels first, then the rest.
 // x [B * H, T, 128] bf16 or fp32 (T tokens per sequence); the codes of token t of sequence s go
 // to row s * out_stride + pos + t (out_stride = T, pos = 0 for a packed set; the capacity and the
-// append position for a cache).  ro / rr: fp32 row-major 64 x 64 rotations.
+// append position for a cache).  ro / rr: fp32 row-major 64 x 64 rotations, rto / rtr their
+// transposes.  Up to 32 tokens per sequence run one fp32 block per token; more run the MFMA
+// kernel on blocks of 512 tokens.
 hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, int64_t T, int64_t out_stride,
-                               int64_t pos, const int32_t* order, const float* ro, const float* rr,
-                               const CodebookArgs& cbo, const CodebookArgs& cbr, uint32_t* idx_o, float* norm_o,
-                               uint32_t* idx_r, float* norm_r, hipStream_t st);
+                               int64_t pos, const int32_t* order, const float* ro, const float* rr, const float* rto,
+                               const float* rtr, const CodebookArgs& cbo, const CodebookArgs& cbr, uint32_t* idx_o,
+                               float* norm_o, uint32_t* idx_r, float* norm_r, hipStream_t st);
 
 // Rotated queries: qws [B * Hq, 128] fp32 with entries 0..63 = R_o q_O and 64..127 = R_r q_R,
 // q_O and q_R gathered through the channel order of the query head's KV head.

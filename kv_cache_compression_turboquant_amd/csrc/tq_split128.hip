@@ -258,6 +258,63 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_encode_split_d128(
 }
 
 // ---------------------------------------------------------------------------------------
+// Short appends (a decode step's token): one block of 128 threads per (token, sequence).  Thread
+// p gathers channel order[p] of its key, so wave 0 holds the outlier half and wave 1 the rest;
+// each wave takes its half's norm with xor-shuffles, forms coordinate p & 63 of R x_half in fp32
+// (R^T read coalesced), bucketizes it against the thresholds scaled by the norm and ORs its field
+// into the key's words in LDS.
+// ---------------------------------------------------------------------------------------
+constexpr int64_t kSplitTokenMax = 32;   // appends of at most this many tokens per sequence
+
+template <int BO, int BR, bool BF16IN>
+__global__ __launch_bounds__(128) void k_append_split_token(
+    const void* __restrict__ x, int64_t T, int64_t out_stride, int64_t out_pos, int H,
+    const int32_t* __restrict__ order, const float* __restrict__ rto, const float* __restrict__ rtr, CodebookArgs cbo,
+    CodebookArgs cbr, uint32_t* __restrict__ idx_o, float* __restrict__ norm_o, uint32_t* __restrict__ idx_r,
+    float* __restrict__ norm_r) {
+  constexpr int WO = 2 * BO, WR = 2 * BR;
+  __shared__ float xs[kSplitD];
+  __shared__ uint32_t words[WO + WR];
+  const int p = threadIdx.x, lane = p & 63, half = p >> 6;
+  const int64_t seq = blockIdx.y, t = blockIdx.x;
+  const int h = (int)(seq % H);
+  const int64_t src = (seq * T + t) * kSplitD + order[(int64_t)h * kSplitD + p];
+  const float v = BF16IN ? bf16_val(static_cast<const uint16_t*>(x)[src]) : static_cast<const float*>(x)[src];
+  xs[p] = v;
+  if (p < WO + WR) words[p] = 0u;
+  float s2 = v * v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o);
+  const float s = sqrtf(s2);
+  __syncthreads();
+  const float* rt = half ? rtr : rto;
+  const float* xh = xs + half * 64;
+  float y = 0.f;
+#pragma unroll 16
+  for (int i = 0; i < 64; ++i) y = fmaf(rt[i * 64 + lane], xh[i], y);
+  const int64_t row = seq * out_stride + out_pos + t;
+  auto quantize = [&](const CodebookArgs& cb, auto bits, int off) {
+    constexpr int B = decltype(bits)::value;
+    uint32_t idx = 0;
+#pragma unroll
+    for (int q = 0; q < (1 << B) - 1; ++q) idx += y >= (s > 0.f ? s * cb.t[q] : cb.t[q]) ? 1u : 0u;
+    const int pb = lane * B, w = pb >> 5, sh = pb & 31;
+    atomicOr(&words[off + w], idx << sh);
+    if (sh + B > 32) atomicOr(&words[off + w + 1], idx >> (32 - sh));
+  };
+  if (half == 0)
+    quantize(cbo, IC<BO>{}, 0);
+  else
+    quantize(cbr, IC<BR>{}, WO);
+  __syncthreads();
+  if (p < WO)
+    idx_o[row * WO + p] = words[p];
+  else if (p < WO + WR)
+    idx_r[row * WR + (p - WO)] = words[p];
+  if (lane == 0) (half ? norm_r : norm_o)[row] = s;
+}
+
+// ---------------------------------------------------------------------------------------
 // Query prologue: one block of 512 threads per query head.  The query is gathered into the
 // channel order of its KV head; thread (j, quarter) then sums 16 of the 64 terms of coordinate
 // j & 63 of R_o q_O (j < 64) or of R_r q_R, reading R^T row-major so that the threads' loads are
@@ -416,10 +473,23 @@ hipError_t with_bits(int bo, int br, F&& f) {
 }  // namespace
 
 hipError_t launch_encode_split(const void* x, bool bf16, int64_t n_seq, int H, int64_t T, int64_t out_stride,
-                               int64_t pos, const int32_t* order, const float* ro, const float* rr,
-                               const CodebookArgs& cbo, const CodebookArgs& cbr, uint32_t* idx_o, float* norm_o,
-                               uint32_t* idx_r, float* norm_r, hipStream_t st) {
+                               int64_t pos, const int32_t* order, const float* ro, const float* rr, const float* rto,
+                               const float* rtr, const CodebookArgs& cbo, const CodebookArgs& cbr, uint32_t* idx_o,
+                               float* norm_o, uint32_t* idx_r, float* norm_r, hipStream_t st) {
   if (n_seq <= 0 || T <= 0) return hipSuccess;
+  if (T <= kSplitTokenMax) {
+    const dim3 tgrid((unsigned)T, (unsigned)n_seq);
+    return with_bits(cbo.bits, cbr.bits, [&](auto bo, auto br) -> hipError_t {
+      constexpr int BO = decltype(bo)::value, BR = decltype(br)::value;
+      if (bf16)
+        hipLaunchKernelGGL((k_append_split_token<BO, BR, true>), tgrid, dim3(128), 0, st, x, T, out_stride, pos, H,
+                           order, rto, rtr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+      else
+        hipLaunchKernelGGL((k_append_split_token<BO, BR, false>), tgrid, dim3(128), 0, st, x, T, out_stride, pos, H,
+                           order, rto, rtr, cbo, cbr, idx_o, norm_o, idx_r, norm_r);
+      return hipGetLastError();
+    });
+  }
   const dim3 grid((unsigned)((T + kEncBlockRows - 1) / kEncBlockRows), (unsigned)n_seq);
   return with_bits(cbo.bits, cbr.bits, [&](auto bo, auto br) -> hipError_t {
     constexpr int BO = decltype(bo)::value, BR = decltype(br)::value;

@@ -283,3 +283,31 @@ def test_split_cache_appends_and_scores(dev, rots):
     with pytest.raises(tq.TQError) as e:
         tq.scores_split_cache(torch.from_numpy(q).to(dev), K, H, T_CAP + 1, T_CAP, sp, cbo, cbr, *rots)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_short_encode_per_token_path(dev, rots, dtype):
+    # At most 32 tokens per sequence take the one-block-per-token kernel: its codes against the
+    # oracle, with a zero key and a key whose outlier half is zero among them.
+    B, H, T, bo, br = 2, 3, 9, 4, 3
+    x, _ = _keys(B, H, T, seed=17)
+    out = _outliers(x)
+    x[1, 2, 4] = 0.0
+    x[0, 1, 7][out[1]] = 0.0
+    if dtype == "f32":
+        x = x * (1.0 + 1e-3 * wl.gaussian(x.shape, 19))
+        xt = torch.from_numpy(x.astype(np.float32))
+        x = x.astype(np.float32).astype(np.float64)
+    else:
+        xt = torch.from_numpy(wl.f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).view(torch.bfloat16)
+    sp = tq.make_split(out)
+    po, pr = tq.encode_split(xt.to(dev), sp, tq.codebook(M, bo), tq.codebook(M, br), *rots)
+    torch.cuda.synchronize()
+    ocb_o, ocb_r = oracle.codebook(M, bo), oracle.codebook(M, br)
+    enc = oracle.encode_split(x, out, R_O, R_R, ocb_o, ocb_r)
+    _check_codes(po, enc.outlier, ocb_o, f"per-token outlier {dtype}")
+    _check_codes(pr, enc.rest, ocb_r, f"per-token rest {dtype}")
+    io = oracle.unpack_bits(to_np_words(po.idx), M, bo)
+    zero_row = (1 * H + 2) * T + 4
+    assert np.all(io[zero_row] == 1 << (bo - 1)) and po.norms[zero_row].item() == 0.0
+    assert np.all(io[(0 * H + 1) * T + 7] == 1 << (bo - 1))
