@@ -309,8 +309,9 @@ void tq_split_free(tq_split_t split);
  * out_r the other halves, each a ROWS-layout MSE packed set with d = 64 and n = B*H*T (bits =
  * cb_o->b resp. cb_r->b; idx [n, 2*bits] words, norms [n] = the half's ||x_half||).  cb_o, cb_r:
  * codebooks with d = 64; rot_o, rot_r: rotations with d = 64 (any kind).  Index decisions follow
- * tq_encode's rule (ties to the upper index) on the half's rotation, formed like tq_encode's
- * (R as bf16 hi + lo operands, fp32 sums).  x_dev must be 16-byte aligned.  Errors: TQ_EINVAL
+ * tq_encode's rule (ties to the upper index) on the half's rotation, formed in fp32 for up to
+ * 32 tokens per sequence and otherwise like tq_encode's (R as bf16 hi + lo operands, fp32 sums).
+ * x_dev must be 16-byte aligned.  Errors: TQ_EINVAL
  * (null pointers, negative sizes, misaligned x), TQ_ESHAPE (split->H != H, a handle or packed
  * set with d != 64, n or bits mismatch), TQ_EUNSUPPORTED (dtype, layout, B*H > 65535,
  * T > 2^25). */
