@@ -1,11 +1,13 @@
 """Benchmark of the TurboQuant hot path on one MI355X.
 
-One step = the whole path on one batch of the single-layer KV-key workload (Llama-3-8B shape:
-1 x 8 KV heads x 32768 tokens x d = 128, bf16 keys with outlier channels and log-normal
-per-token scale): TurboQuant_mse b = 3 encode of all 262144 keys (norm, dense rotation on MFMA,
-Lloyd-Max bucketize, bit-pack), then the decode-step scores of 32 query heads (GQA 4) over the
-packed keys.  Inputs are resident in HBM before timing; the step rotates through several input
-and output buffer sets whose total exceeds the last-level cache.
+One step = the whole path on one batch of the TurboQuant_prod workload (16 sequences x 8 KV heads x
+16384 tokens x d = 128, bf16 keys with outlier channels and a log-normal per-token scale):
+TurboQuant_prod b = 4 encode of all 2,097,152 keys (norm, dense rotation on MFMA, 3-bit Lloyd-Max
+bucketize, bit-pack, residual, 1-bit QJL sketch of the residual with S' on MFMA, residual norm),
+then the query prologue and the unbiased scores of 32 query heads per sequence (GQA 4) over the
+packed keys.  Inputs are resident in HBM before timing; the step rotates through several input and
+output buffer sets whose total exceeds the last-level cache.  The single-layer KV-key step (1 x 8 x
+32768 keys, MSE b = 3) is reported beside it as a nested secondary line.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this path runs on one GPU.
 """
@@ -27,20 +29,37 @@ HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 1.5e9
 
 
-# sources that make up the headline encode kernel: its counters stay valid while these are unchanged
-HEADLINE_SOURCES = ("tq_device.h", "tq_internal.h", "tq_encode128.hip")
+# Sources of each timed kernel: its counters stay valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "encode": ("tq_device.h", "tq_internal.h", "tq_encode128.hip"),
+    "scores": ("tq_device.h", "tq_internal.h", "tq_decode.h", "tq_cache.h", "tq_score128.hip"),
+}
+# (encode kernel, score kernel) of each step workload, as the profiler names them
+HEADLINE_KERNELS = {
+    "c3": ("k_encode_d128<3, true, true, false, 2, 1> (prod b=4, dense R, bf16 keys)",
+           "k_scores_d128<3, true, false> (prod, GQA 4)"),
+    "c2": ("k_encode_mse_d128<3, true, 2, 2> (MSE b=3, dense R, bf16 keys)",
+           "k_scores_d128<3, false, false> (MSE, GQA 4)"),
+}
+# name prefixes of those kernels in a rocprofv3 database (for the counter summary)
+PMC_KERNELS = {
+    "c3:encode": "k_encode_d128<3, true, true, false, 2,",
+    "c3:scores": "k_scores_d128<3, true, false>",
+    "c2:encode": "k_encode_mse_d128<3, true, 2,",
+    "c2:scores": "k_scores_d128<3, false, false>",
+}
 
 
-def kernel_source_hash():
+def kernel_source_hash(kind):
     h = hashlib.sha256()
-    for f in HEADLINE_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "kv_cache_compression_turboquant_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_key, launches_bytes_key):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the current
-    kernel sources; else None."""
+def traffic_from_profile(key):
+    """HBM bytes per launch of kernel `key` ("c3:encode", ...) from the committed counter summary,
+    if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -48,14 +67,13 @@ def traffic_from_profile(kernel_key, launches_bytes_key):
         data = json.load(open(path))
     except Exception:
         return None
-    ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    ent = data.get(key)
+    if not ent or ent.get("source_hash") != kernel_source_hash(key.split(":")[1]):
         return None
-    return ent.get(launches_bytes_key)
+    return ent.get("hbm_bytes_per_launch")
 
 
 COPY_PROBE_BYTES = 512 << 20
-HEADLINE_KERNEL = "k_encode_mse_d128<3, true, 2,"  # MSE b=3, bf16 keys, dense R (two passes)
 
 
 def copy_probe(torch, dev, reps=3):
@@ -112,16 +130,22 @@ def pmc_summary(fetch_db, write_db):
         table[_short(name)] = (name, len(fetch[name]), fb, wb)
         lines.append(f"{_short(name)[:60]:60s} {len(fetch[name]):10d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} "
                      f"{(fb + wb) / 1e6:10.2f}")
-    head = [v for k, v in table.items() if v[0].startswith("void tq::(anonymous namespace)::" + HEADLINE_KERNEL)]
-    out = {"_note": "HBM bytes per dispatch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) x 1024, each "
-                    "scaled by the copy-probe factor; valid only for the kernel sources of source_hash",
-           "k_encode_d128:c2": None}
-    if head:
-        name, nd, fb, wb = head[0]
-        out["k_encode_d128:c2"] = {"kernel": name[:120], "dispatches": nd, "fetch_bytes": fb, "write_bytes": wb,
-                                   "hbm_bytes_per_launch": fb + wb, "fetch_scale": ff, "write_scale": fw,
-                                   "source_hash": kernel_source_hash()}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        out = json.load(open(path))
+    except Exception:
+        out = {}
+    out["_note"] = ("HBM bytes per dispatch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) x 1024, each scaled "
+                    "by the copy-probe factor; valid only for the kernel sources of source_hash")
+    for key, prefix in PMC_KERNELS.items():
+        hit = [v for k, v in table.items() if v[0].startswith("void tq::(anonymous namespace)::" + prefix)]
+        if not hit:
+            continue
+        name, nd, fb, wb = hit[0]
+        out[key] = {"kernel": name[:120], "dispatches": nd, "fetch_bytes": fb, "write_bytes": wb,
+                    "hbm_bytes_per_launch": fb + wb, "fetch_scale": ff, "write_scale": fw,
+                    "source_hash": kernel_source_hash(key.split(":")[1])}
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print("\n".join(lines))
 
@@ -488,20 +512,41 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "prefill_ms": pre_ms, "step_ms": step_ms, "append_ms": app_ms,
                     "decode_scores_per_s": cfg.hq * t_cap / step_ms * 1e3})
     elif name == "peaks":
-        # Achievable HBM rates on this machine, for reading the fractions against a measured ceiling as
-        # well as the 8 TB/s spec: a plain device copy (reads and writes) and a read-only sum of
-        # 1 GiB, both torch's own kernels, buffers far larger than the last-level cache.
+        # Achievable ceilings on this machine, from the library's own measurement kernels: a streaming
+        # read and a streaming copy of 1 GiB (far larger than the last-level cache), swept over
+        # grid sizes; and independent MFMA chains of each operand type, swept over waves per SIMD.
         nbytes = 1 << 30
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
-        f = src.view(torch.float32)
-        out = torch.empty((), dtype=torch.float32, device=dev)
-        copy_ms = _timed(lambda i: dst.copy_(src), steps, warmup)
-        read_ms = _timed(lambda i: torch.sum(f, dim=0, out=out), steps, warmup)
-        res.update({"bytes": nbytes, "copy_ms": copy_ms, "copy_gbs": 2 * nbytes / copy_ms / 1e6,
-                    "copy_frac": 2 * nbytes / copy_ms / 1e6 / HBM_PEAK_GBS,
-                    "read_ms": read_ms, "read_gbs": nbytes / read_ms / 1e6,
-                    "read_frac": nbytes / read_ms / 1e6 / HBM_PEAK_GBS})
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        reads, copies = {}, {}
+        for per_cu in (2, 4, 8, 16):
+            blocks = cus * per_cu
+            reads[per_cu] = _timed(lambda i: tq.peak_read(src, blocks), steps, warmup)
+            copies[per_cu] = _timed(lambda i: tq.peak_copy(dst, src, blocks), steps, warmup)
+        br = min(reads, key=reads.get)
+        bc = min(copies, key=copies.get)
+        res.update({"bytes": nbytes, "cus": cus,
+                    "read_gbs_by_blocks_per_cu": {k: nbytes / v / 1e6 for k, v in reads.items()},
+                    "copy_gbs_by_blocks_per_cu": {k: 2 * nbytes / v / 1e6 for k, v in copies.items()},
+                    "read_gbs": nbytes / reads[br] / 1e6, "read_frac": nbytes / reads[br] / 1e6 / HBM_PEAK_GBS,
+                    "copy_gbs": 2 * nbytes / copies[bc] / 1e6,
+                    "copy_frac": 2 * nbytes / copies[bc] / 1e6 / HBM_PEAK_GBS})
+        del src, dst
+        mf = {}
+        for kind in tq.PEAK_MFMA_KINDS:
+            best = 0.0
+            for per_simd in (1, 2, 4):
+                blocks = cus * per_simd          # 4 waves per block: per_simd waves on each SIMD
+                out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+                flops = [0.0]
+
+                def run(i):
+                    flops[0] = tq.peak_mfma(kind, 2000, blocks, out)
+                ms = _timed(run, max(3, steps // 10), 1)
+                best = max(best, flops[0] / ms / 1e9)
+            mf[kind] = {"tflops": best, "frac_of_2500": best / 2500.0}
+        res["mfma"] = mf
     elif name == "c5":
         cfg = wl.CONFIGS["c5"]
         n, d = cfg.n, cfg.d
@@ -523,8 +568,8 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         enc_flops = 4.0 * n * d * d            # R x and S' r, fp32-accurate (three bf16 passes each)
         search_flops = 4.0 * nq * n * d        # <q_rot, c> and <q_s, z> per pair, fp16 operands
         res.update({"encode_ms": enc_ms, "encode_vectors_per_s": n / enc_ms * 1e3,
-                    "encode_tflops": enc_flops / enc_ms / 1e9,
-                    "encode_frac_fp32_mfma": enc_flops / enc_ms / 1e9 / 157.3,
+                    "encode_tflops_fp32_accurate": enc_flops / enc_ms / 1e9,
+                    "encode_bf16_passes_issued": 3,
                     "encode_frac_bf16_issued": 3 * enc_flops / enc_ms / 1e9 / 2500.0,
                     "search_ms": se_ms, "search_scores_per_s": nq * n / se_ms * 1e3,
                     "search_tflops": search_flops / se_ms / 1e9,
@@ -532,16 +577,121 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
     print(json.dumps(res), flush=True)
 
 
+def step_bench(name, steps, warmup, copy_probe_after=False, cpu_budget=0.0, event_every=4):
+    """One step = encode every key of the workload, then the query prologue and the scores of every
+    query head over the packed keys.  c3: TurboQuant_prod b = 4 (3-bit Lloyd-Max + 1-bit QJL) of
+    16 x 8 x 16384 bf16 keys, dense R; c2: TurboQuant_mse b = 3 of 1 x 8 x 32768 bf16 keys.
+    Returns the result dict (the bench line's fields)."""
+    import torch
+    import kv_cache_compression_turboquant_amd as tq
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[name]
+    prod = cfg.mode == "prod"
+    stage = cfg.bits - 1 if prod else cfg.bits
+    n = cfg.B * cfg.hkv * cfg.T
+    keys_bits = wl.kv_keys(cfg)
+    q_np = wl.kv_queries(cfg)
+
+    cb = tq.codebook(cfg.d, stage)
+    rot = tq.make_rotation(cfg.d, cfg.rot_seed, "dense")
+    qjl = tq.make_qjl(cfg.d, cfg.qjl_seed, rot) if prod else None
+    words = cfg.d * stage // 32
+    in_bytes = n * cfg.d * 2
+    row_bytes = words * 4 + 4 + ((cfg.d // 8 + 4) if prod else 0)   # indices + norm (+ signs + gamma)
+    out_bytes = n * row_bytes
+    score_bytes_out = cfg.B * cfg.hq * cfg.T * 4
+    per_set = in_bytes + out_bytes + score_bytes_out
+    nbuf = max(2, int(np.ceil(CACHE_DEFEAT_BYTES / per_set)))
+    base = torch.from_numpy(keys_bits.reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+    del keys_bits
+    xs = [base] + [base.clone() for _ in range(nbuf - 1)]
+    packs = [tq.alloc_packed(n, cfg.d, stage, cfg.mode, device=dev) for _ in range(nbuf)]
+    q = torch.from_numpy(q_np).to(dev)
+    outs = [torch.empty((cfg.B, cfg.hq, cfg.T), dtype=torch.float32, device=dev) for _ in range(nbuf)]
+    ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
+
+    def step(i, timers=None):
+        j = i % nbuf
+        if timers is not None:
+            timers[0].append(tq.timer_arm("encode"))
+            timers[1].append(tq.timer_arm("scores"))
+        tq.encode(xs[j], cfg.bits, cfg.mode, cb, rot, qjl, out=packs[j])
+        tq.scores(q, packs[j], cfg.hkv, cb, rot, qjl, out=outs[j], ws=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps.  The encode and score kernels' durations are taken live,
+    # on every event_every-th step, with HIP events that the library attaches to those kernels'
+    # dispatches (hipExtLaunchKernel): they bracket each kernel alone, on the stream it runs on.
+    timers = ([], [])
+    tq.timer_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, timers if i % event_every == 0 else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / steps
+    enc_ms = float(np.mean([tq.timer_read(t) for t in timers[0]]))
+    sc_ms = float(np.mean([tq.timer_read(t) for t in timers[1]]))
+    tq.timer_reset()
+
+    scores_per_step = cfg.B * cfg.hq * cfg.T
+    enc_alg_bytes = in_bytes + out_bytes
+    score_alg_bytes = out_bytes + cfg.B * cfg.hq * cfg.d * 4 + score_bytes_out
+    enc_gbs = enc_alg_bytes / (enc_ms * 1e-3) / 1e9
+    sc_gbs = score_alg_bytes / (sc_ms * 1e-3) / 1e9
+    # bf16 MFMA passes the encode issues per d x d product: R as hi + lo (x is exact in bf16);
+    # S' r as S'hi rhi + S'hi rlo + S'lo rhi
+    passes = 2 + (3 if prod else 0)
+    issued_flops = passes * 2.0 * cfg.d * cfg.d * n
+    enc_kernel, sc_kernel = HEADLINE_KERNELS[name]
+    res = {
+        "workload": cfg.workload, "keys": [cfg.B, cfg.hkv, cfg.T, cfg.d], "bits": cfg.bits,
+        "mode": cfg.mode, "query_heads": cfg.hq, "rotation": "dense QR (seed 1)" + (", S seed 2" if prod else ""),
+        "ms_per_step": step_s * 1e3, "scores_per_s": scores_per_step / step_s,
+        "encode_vectors_per_s": n / step_s, "encode_kernel_ms": enc_ms, "score_kernel_ms": sc_ms,
+        "buffer_sets": nbuf,
+        "roofline": {"bound": "hbm", "kernel": enc_kernel,
+                     "timing": f"HIP events attached to the kernel's dispatch on every {event_every}th timed step",
+                     "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile(name + ":encode"),
+                     "alg_bytes_per_launch": enc_alg_bytes,
+                     "mfma_issued": {"passes": passes, "tflops": issued_flops / (enc_ms * 1e-3) / 1e12,
+                                     "peak": 2500.0, "frac": issued_flops / (enc_ms * 1e-3) / 1e12 / 2500.0}},
+        "roofline_score": {"bound": "hbm", "kernel": sc_kernel,
+                           "timing": f"HIP events attached to the kernel's dispatch on every {event_every}th timed step",
+                           "achieved": sc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sc_gbs / HBM_PEAK_GBS,
+                           "traffic": traffic_from_profile(name + ":scores"),
+                           "alg_bytes_per_launch": score_alg_bytes},
+    }
+    if copy_probe_after:
+        copy_probe(torch, dev)
+    if cpu_budget > 0:
+        if prod:
+            res["cpu_baseline"] = cpu_baseline_prod(cfg, "dense", cpu_budget)
+        else:
+            res["cpu_baseline"] = cpu_baseline(cfg, wl.kv_keys(cfg), q_np, cpu_budget)
+    del xs, packs, outs, base
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode", "decodeb4", "peaks", "c2split",
-                                                        "c2split35", "c2splitdecode"],
-                    help="c2 = the headline step; the others print per-kernel timings only")
+    ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode"],
+                    help="c3 = the headline step (c2 is its nested secondary line); the others print "
+                         "per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "
                          "(the calibration for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -558,96 +708,41 @@ def main():
         sys.exit(2)
 
     import torch
-    import kv_cache_compression_turboquant_amd as tq
-    from kv_cache_compression_turboquant_amd import workloads as wl
-
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)
         sys.exit(1)
-    if args.config != "c2":
-        bench_other(args.config, args.steps, args.warmup, 0.0 if args.no_cpu_baseline else args.cpu_budget)
+    cpu_budget = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    if args.config not in ("c3", "c2"):
+        bench_other(args.config, args.steps, args.warmup, cpu_budget)
         return
-    dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS["c2"]
-    n = cfg.B * cfg.hkv * cfg.T
-    keys_bits = wl.kv_keys(cfg)
-    q_np = wl.kv_queries(cfg)
-
-    cb = tq.codebook(cfg.d, cfg.bits)
-    rot = tq.make_rotation(cfg.d, cfg.rot_seed, "dense")
-    in_bytes = n * cfg.d * 2
-    words = cfg.d * cfg.bits // 32
-    out_bytes = n * (words * 4 + 4)
-    score_bytes_out = cfg.B * cfg.hq * cfg.T * 4
-    per_set = in_bytes + out_bytes + score_bytes_out
-    nbuf = max(1, int(np.ceil(CACHE_DEFEAT_BYTES / per_set)))
-    base = torch.from_numpy(keys_bits.reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
-    xs = [base] + [base.clone() for _ in range(nbuf - 1)]
-    packs = [tq.alloc_packed(n, cfg.d, cfg.bits, "mse", device=dev) for _ in range(nbuf)]
-    q = torch.from_numpy(q_np).to(dev)
-    outs = [torch.empty((cfg.B, cfg.hq, cfg.T), dtype=torch.float32, device=dev) for _ in range(nbuf)]
-    ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
-
-    def step(i, timers=None):
-        j = i % nbuf
-        if timers is not None:
-            timers.append(tq.timer_arm())
-        tq.encode(xs[j], cfg.bits, "mse", cb, rot, out=packs[j])
-        tq.scores(q, packs[j], cfg.hkv, cb, rot, out=outs[j], ws=ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K steps.  The encode kernel's duration is taken live, on every
-    # EVENT_EVERY-th step, with a pair of HIP events that the library attaches to that kernel's
-    # dispatch (hipExtLaunchKernel): they bracket the kernel alone, on the stream it runs on.
-    EVENT_EVERY = 4
-    timers = []
-    tq.timer_reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, timers if i % EVENT_EVERY == 0 else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_s = (t1 - t0) / args.steps
-    enc_ms = float(np.mean([tq.timer_read(t) for t in timers]))
-    tq.timer_reset()
-
-    # outside the timed region: the score path alone (query prologue + score kernel)
-    sc_ms = _timed(lambda i: tq.scores(q, packs[i % nbuf], cfg.hkv, cb, rot, out=outs[i % nbuf], ws=ws), 20, 2)
-
-    scores_per_step = cfg.B * cfg.hq * cfg.T
-    enc_alg_bytes = in_bytes + out_bytes
-    score_alg_bytes = n * (words * 4 + 4) + cfg.B * cfg.hq * cfg.d * 4 + score_bytes_out
-    achieved = enc_alg_bytes / (enc_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile("k_encode_d128:c2", "hbm_bytes_per_launch")
-
+    print(f"bench.py: {args.config} step, {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    main_res = step_bench(args.config, args.steps, args.warmup, args.copy_probe, cpu_budget)
+    secondary = None
+    if args.config == "c3" and not args.no_secondary:
+        print("bench.py: secondary c2 step", file=sys.stderr, flush=True)
+        secondary = step_bench("c2", max(20, args.steps // 2), min(args.warmup, 5), False, 0.0)
+    r = main_res
     result = {
         "metric": "Q·K^T scores/s over packed keys + encode vectors/s; % of HBM roofline",
-        "value": scores_per_step / step_s,
+        "value": r["scores_per_s"],
         "unit": "scores/s (each step encodes all keys, then scores every query head)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.workload, "keys": [cfg.B, cfg.hkv, cfg.T, cfg.d], "bits": cfg.bits,
-                   "mode": cfg.mode, "query_heads": cfg.hq, "rotation": "dense QR (seed 1)",
-                   "encode_vectors_per_s": n / step_s,
-                   "encode_kernel_ms": enc_ms, "score_path_ms": sc_ms,
-                   "score_path_gbs": score_alg_bytes / (sc_ms * 1e-3) / 1e9,
-                   "buffer_sets": nbuf},
-        "roofline": {"bound": "hbm", "kernel": "k_encode_mse_d128 (MSE b=3, dense R, bf16 keys)",
-                     "timing": f"HIP events attached to the encode kernel's dispatch on every {EVENT_EVERY}th timed step",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": enc_alg_bytes},
+        "config": {k: r[k] for k in ("workload", "keys", "bits", "mode", "query_heads", "rotation",
+                                     "encode_vectors_per_s", "encode_kernel_ms", "score_kernel_ms", "buffer_sets")},
+        "roofline": r["roofline"],
+        "roofline_score": r["roofline_score"],
     }
-    if args.copy_probe:
-        copy_probe(torch, dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, keys_bits, q_np, args.cpu_budget)
+    if secondary is not None:
+        result["secondary"] = {"kv_keys_c2": {k: secondary[k] for k in (
+            "workload", "ms_per_step", "scores_per_s", "encode_vectors_per_s", "encode_kernel_ms",
+            "score_kernel_ms")}}
+        result["secondary"]["kv_keys_c2"]["encode_frac_hbm"] = secondary["roofline"]["frac"]
+        result["secondary"]["kv_keys_c2"]["score_frac_hbm"] = secondary["roofline_score"]["frac"]
+    if "cpu_baseline" in r:
+        result["cpu_baseline"] = r["cpu_baseline"]
     print(json.dumps(result), flush=True)
 
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 5
+#define TQ_ABI_VERSION 6
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -202,7 +202,8 @@ size_t tq_scores_workspace(int B, int Hq, int d);
  * [B, Hkv, T] (K->n == B*Hkv*T), into scores_dev [B, Hq, T] fp32.  The query is rotated once
  * ([SB] third layer); query head h reads kv head h / (Hq / Hkv) ([SB] GQA mapping).
  * MSE: s <R q, C[idx]>;  prod: plus gamma sqrt(pi/2)/d <S q, z> ([TQ] TurboQuant_prod;
- * [FP] QJL constant).  Requires Hq / Hkv in {1, 2, 4} when B*Hkv*T > 0; d = 128. */
+ * [FP] QJL constant).  The GQA ratio Hq / Hkv must be 1, 2, 3 or 4, or a multiple of 4 up to 64
+ * (TQ_EUNSUPPORTED otherwise); d = 128. */
 tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
                     void* ws_dev, size_t ws_bytes, void* stream);
@@ -380,6 +381,29 @@ tq_status tq_search_topk(const float* q_dev, int64_t nq, const tq_packed* db, tq
 int tq_timer_arm(void);
 tq_status tq_timer_read(int id, float* ms);
 void tq_timer_reset(void);
+/* Kernels a timer can be attached to.  ENCODE: the d = 128 rows-layout encode kernel (what
+ * tq_timer_arm arms).  SCORES: the d = 128 score kernel launched by tq_scores, tq_scores_prepared or
+ * tq_scores_cache (not the query prologue before it).  One timer per kind can be armed at a time
+ * on a thread; arming a kind again replaces the armed timer of that kind.  Returns as tq_timer_arm;
+ * TQ_EINVAL in tq_last_error (and -1) for an unknown kind. */
+typedef enum tq_timed_kernel { TQ_TIMED_ENCODE = 0, TQ_TIMED_SCORES = 1 } tq_timed_kernel;
+int tq_timer_arm_kernel(tq_timed_kernel which);
+
+/* ---- measurement ceilings (not part of the method) -----------------------------------
+ * Kernels that give the achievable rates the roofline fractions are read against.
+ * tq_peak_read: a streaming read of `bytes` (a multiple of 16) from src_dev by `blocks` blocks of
+ *   256 threads (grid-stride, four 16-byte loads in flight per thread); nothing is written
+ *   (sink_dev may be NULL: the kernel takes it but never stores to it).
+ * tq_peak_copy: the same pattern copying src_dev to dst_dev (`bytes` read and written).
+ * tq_peak_mfma: `blocks` blocks of 4 waves; each wave advances independent MFMA accumulator chains
+ *   `iters` times (8 chains of v_mfma_f32_16x16x32 or 4 chains of v_mfma_f32_32x32x16): kind 0 =
+ *   16x16x32 bf16, 1 = 32x32x16 bf16, 2 = 16x16x32 f16, 3 = 32x32x16 f16.  Every instruction is
+ *   16384 (16x16x32) or 32768 (32x32x16) flops; out_dev receives blocks * 256 floats.
+ * Errors: TQ_EINVAL (null buffers, bytes not a positive multiple of 16, blocks or iters < 1, bad
+ * kind), TQ_EDEVICE. */
+tq_status tq_peak_read(const void* src_dev, size_t bytes, int blocks, uint32_t* sink_dev, void* stream);
+tq_status tq_peak_copy(void* dst_dev, const void* src_dev, size_t bytes, int blocks, void* stream);
+tq_status tq_peak_mfma(int kind, int iters, int blocks, float* out_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ __all__ = [
     "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
     "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
-    "cache_append_split", "scores_split_cache",
+    "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -371,6 +371,41 @@ def decode_attn_cache(q, kc, vc, T, cb_k, cb_v, rot_k, rot_v, scale=None, out=No
     return out
 
 
+
+def _same_device(fn, *ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise TQError(1, f"{fn}: tensors on different devices {sorted(map(str, devs))}")
+
+
+def _check_split_keys_x(fn, x):
+    """Keys for the split entry points: contiguous [B, H, T, 128] bf16 or fp32 (the C functions
+    take no d and read 128 values per key)."""
+    torch = _torch()
+    if x.dim() != 4 or x.shape[3] != 128:
+        raise TQError(2, f"{fn}: x must be [B, H, T, 128], got {list(x.shape)}")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TQError(3, f"{fn}: x must be bf16 or fp32, got {x.dtype}")
+    if not x.is_contiguous():
+        raise TQError(1, f"{fn}: x must be contiguous")
+
+
+def _check_split_q(fn, q):
+    """Queries for the split score entry points: contiguous fp32 [B, Hq, 128]."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != 128:
+        raise TQError(2, f"{fn}: q must be [B, Hq, 128], got {list(q.shape)}")
+    if q.dtype != torch.float32:
+        raise TQError(3, f"{fn}: q must be fp32, got {q.dtype}")
+    if not q.is_contiguous():
+        raise TQError(1, f"{fn}: q must be contiguous")
+
+
+def _check_scores_out(fn, out, n):
+    torch = _torch()
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n:
+        raise TQError(1, f"{fn}: out must be contiguous fp32 with {n} elements")
+
 class Split(_Handle):
     """Per-KV-head channel split of d = 128 keys: 64 outlier channels, then the rest."""
     _free = "tq_split_free"
@@ -394,12 +429,12 @@ def make_split(outliers):
 def encode_split(x, split, cb_o, cb_r, rot_o, rot_r, out=None):
     """Split encode of keys x [B, H, T, 128] (bf16 or fp32): (outlier codes, rest codes), each a
     rows-layout MSE Packed with d = 64 and n = B*H*T."""
-    B, H, T, d = x.shape
-    if not x.is_contiguous():
-        raise TQError(1, "encode_split: x must be contiguous")
+    _check_split_keys_x("encode_split", x)
+    B, H, T, _ = x.shape
     n = B * H * T
     if out is None:
         out = (alloc_packed(n, 64, cb_o.b, "mse", device=x.device), alloc_packed(n, 64, cb_r.b, "mse", device=x.device))
+    _same_device("encode_split", x, out[0].idx, out[0].norms, out[1].idx, out[1].norms)
     do, dr = out[0].descriptor(), out[1].descriptor()
     check(lib().tq_encode_split(_dptr(x), _dtype_code(x), B, H, T, split.ptr, cb_o.ptr, cb_r.ptr, rot_o.ptr,
                                 rot_r.ptr, ctypes.byref(do), ctypes.byref(dr), _stream()))
@@ -414,14 +449,15 @@ def scores_split(q, K, Hkv, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
     """Raw scores [B, Hq, T] of q [B, Hq, 128] fp32 against split codes K = (K_o, K_r) of keys
     [B, Hkv, T]."""
     torch = _torch()
-    B, Hq, d = q.shape
-    if not q.is_contiguous():
-        raise TQError(1, "scores_split: q must be contiguous")
+    _check_split_q("scores_split", q)
+    B, Hq, _ = q.shape
     T = K[0].n // max(B * Hkv, 1)
     if out is None:
         out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check_scores_out("scores_split", out, B * Hq * T)
     if ws is None:
         ws = torch.empty((max(scores_split_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
+    _same_device("scores_split", q, out, ws, K[0].idx, K[0].norms, K[1].idx, K[1].norms)
     do, dr = K[0].descriptor(), K[1].descriptor()
     check(lib().tq_scores_split(_dptr(q), B, Hq, Hkv, T, split.ptr, ctypes.byref(do), ctypes.byref(dr), cb_o.ptr,
                                 cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
@@ -439,9 +475,9 @@ def alloc_split_cache(B, H, t_cap, b_o, b_r, device="cuda"):
 def cache_append_split(K, x, pos, t_cap, split, cb_o, cb_r, rot_o, rot_r):
     """Append keys x [B, H, n_new, 128] (bf16 or fp32) at row pos of every sequence of the split
     cache K = (K_o, K_r) of capacity t_cap."""
-    if not x.is_contiguous():
-        raise TQError(1, "cache_append_split: x must be contiguous")
-    B, H, n_new, d = x.shape
+    _check_split_keys_x("cache_append_split", x)
+    B, H, n_new, _ = x.shape
+    _same_device("cache_append_split", x, K[0].idx, K[0].norms, K[1].idx, K[1].norms)
     do, dr = K[0].descriptor(), K[1].descriptor()
     check(lib().tq_cache_append_split(_dptr(x), _dtype_code(x), B, H, n_new, pos, t_cap, split.ptr, cb_o.ptr,
                                       cb_r.ptr, rot_o.ptr, rot_r.ptr, ctypes.byref(do), ctypes.byref(dr), _stream()))
@@ -452,15 +488,14 @@ def scores_split_cache(q, K, Hkv, T, t_cap, split, cb_o, cb_r, rot_o, rot_r, out
     """Raw scores [B, Hq, T] of q [B, Hq, 128] fp32 over the first T rows of every sequence of the
     split cache K = (K_o, K_r) of capacity t_cap."""
     torch = _torch()
-    B, Hq, d = q.shape
-    if not q.is_contiguous():
-        raise TQError(1, "scores_split_cache: q must be contiguous")
+    _check_split_q("scores_split_cache", q)
+    B, Hq, _ = q.shape
     if out is None:
         out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
-    if not out.is_contiguous() or out.numel() < B * Hq * T:
-        raise TQError(1, "scores_split_cache: out must be contiguous with B*Hq*T elements")
+    _check_scores_out("scores_split_cache", out, B * Hq * T)
     if ws is None:
         ws = torch.empty((max(scores_split_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
+    _same_device("scores_split_cache", q, out, ws, K[0].idx, K[0].norms, K[1].idx, K[1].norms)
     do, dr = K[0].descriptor(), K[1].descriptor()
     check(lib().tq_scores_split_cache(_dptr(q), B, Hq, Hkv, T, t_cap, split.ptr, ctypes.byref(do), ctypes.byref(dr),
                                       cb_o.ptr, cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
@@ -489,10 +524,14 @@ def search_topk(q, db, k, cb, rot, qjl, ws=None, out=None):
     return out
 
 
-def timer_arm():
-    """Arm a kernel timer for the next d = 128 rows-layout encode launch on this thread; returns
-    its id (measurement helper: the events are attached to the kernel's own dispatch)."""
-    t = int(lib().tq_timer_arm())
+_TIMED = {"encode": 0, "scores": 1}
+
+
+def timer_arm(kernel="encode"):
+    """Arm a kernel timer for the next launch on this thread of the d = 128 rows-layout encode
+    kernel ("encode") or of the d = 128 score kernel ("scores"); returns its id (measurement
+    helper: the events are attached to the kernel's own dispatch)."""
+    t = int(lib().tq_timer_arm_kernel(_TIMED[kernel]))
     if t < 0:
         raise TQError(4, lib().tq_last_error().decode())
     return t
@@ -507,3 +546,32 @@ def timer_read(t):
 
 def timer_reset():
     lib().tq_timer_reset()
+
+
+def peak_read(src, blocks, sink=None):
+    """Measurement ceiling: a streaming read of the bytes of `src` (device tensor, size a multiple
+    of 16) by `blocks` blocks of 256 threads."""
+    nbytes = src.numel() * src.element_size()
+    check(lib().tq_peak_read(_dptr(src), nbytes, int(blocks), _dptr(sink), _stream()))
+
+
+def peak_copy(dst, src, blocks):
+    """Measurement ceiling: a streaming copy of src into dst (same byte size, a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise TQError(1, "peak_copy: dst and src differ in size")
+    check(lib().tq_peak_copy(_dptr(dst), _dptr(src), nbytes, int(blocks), _stream()))
+
+
+PEAK_MFMA_KINDS = {"bf16_16x16x32": (0, 8, 16384), "bf16_32x32x16": (1, 4, 32768),
+                   "f16_16x16x32": (2, 8, 16384), "f16_32x32x16": (3, 4, 32768)}
+
+
+def peak_mfma(kind, iters, blocks, out):
+    """Measurement ceiling: independent MFMA chains, `out` a device fp32 tensor of blocks * 256
+    elements.  Returns the flops the launch issues."""
+    code, chains, per_inst = PEAK_MFMA_KINDS[kind]
+    if out.numel() < blocks * 256:
+        raise TQError(1, "peak_mfma: out needs blocks * 256 floats")
+    check(lib().tq_peak_mfma(code, int(iters), int(blocks), _dptr(out), _stream()))
+    return float(blocks) * 4 * iters * chains * per_inst

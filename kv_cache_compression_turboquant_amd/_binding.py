@@ -71,6 +71,10 @@ SIGNATURES = {
     "tq_timer_arm": (_I, []),
     "tq_timer_read": (_I, [_I, ctypes.POINTER(ctypes.c_float)]),
     "tq_timer_reset": (None, []),
+    "tq_timer_arm_kernel": (_I, [_I]),
+    "tq_peak_read": (_I, [_P, _SZ, _I, _P, _P]),
+    "tq_peak_copy": (_I, [_P, _P, _SZ, _I, _P]),
+    "tq_peak_mfma": (_I, [_I, _I, _I, _P, _P]),
     "tq_rotate": (_I, [_P, _I, _I64, _I, _P, _P, _P, _P]),
     "tq_quantize_rotated": (_I, [_P, _I64, _I, _P, _P, _P]),
     "tq_decode": (_I, [ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),

@@ -471,14 +471,16 @@ struct Timer {
 };
 std::mutex g_timer_mu;
 Timer g_timers[TQ_MAX_TIMERS];
-thread_local int g_armed_timer = -1;
+constexpr int kTimedKinds = 2;
+thread_local int g_armed_timer[kTimedKinds] = {-1, -1};
 
 }  // namespace
 
-bool tq::take_armed_timer(hipEvent_t* start, hipEvent_t* stop) {
-  const int id = g_armed_timer;
+bool tq::take_armed_timer(int which, hipEvent_t* start, hipEvent_t* stop) {
+  if (which < 0 || which >= kTimedKinds) return false;
+  const int id = g_armed_timer[which];
   if (id < 0) return false;
-  g_armed_timer = -1;
+  g_armed_timer[which] = -1;
   std::lock_guard<std::mutex> lk(g_timer_mu);
   *start = g_timers[id].start;
   *stop = g_timers[id].stop;
@@ -490,8 +492,18 @@ extern "C" {
 
 int tq_abi_version(void) { return TQ_ABI_VERSION; }
 
-int tq_timer_arm(void) {
+int tq_timer_arm(void) { return tq_timer_arm_kernel(TQ_TIMED_ENCODE); }
+
+int tq_timer_arm_kernel(tq_timed_kernel which) {
+  if ((int)which < 0 || (int)which >= kTimedKinds) {
+    fail(TQ_EINVAL, "tq_timer_arm_kernel: unknown kernel kind %d", (int)which);
+    return -1;
+  }
   std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (g_armed_timer[which] >= 0) {           // re-arming a kind replaces its armed timer
+    g_timers[g_armed_timer[which]].used = false;
+    g_armed_timer[which] = -1;
+  }
   for (int i = 0; i < TQ_MAX_TIMERS; ++i) {
     Timer& t = g_timers[i];
     if (t.used) continue;
@@ -503,7 +515,7 @@ int tq_timer_arm(void) {
     }
     t.used = true;
     t.launched = false;
-    g_armed_timer = i;
+    g_armed_timer[which] = i;
     return i;
   }
   fail(TQ_ENOMEM, "tq_timer_arm: all %d timers in use", TQ_MAX_TIMERS);
@@ -530,7 +542,25 @@ tq_status tq_timer_read(int id, float* ms) {
 void tq_timer_reset(void) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   for (Timer& t : g_timers) t.used = t.launched = false;
-  g_armed_timer = -1;
+  for (int& a : g_armed_timer) a = -1;
+}
+
+tq_status tq_peak_read(const void* src_dev, size_t bytes, int blocks, uint32_t* sink_dev, void* stream) {
+  const char* fn = "tq_peak_read";
+  if (!src_dev || bytes == 0 || bytes % 16 != 0 || blocks < 1) return fail(TQ_EINVAL, "%s: bad arguments", fn);
+  return check_launch(tq::launch_peak_read(src_dev, (int64_t)bytes, blocks, sink_dev, as_stream(stream)), fn);
+}
+
+tq_status tq_peak_copy(void* dst_dev, const void* src_dev, size_t bytes, int blocks, void* stream) {
+  const char* fn = "tq_peak_copy";
+  if (!src_dev || !dst_dev || bytes == 0 || bytes % 16 != 0 || blocks < 1) return fail(TQ_EINVAL, "%s: bad arguments", fn);
+  return check_launch(tq::launch_peak_copy(dst_dev, src_dev, (int64_t)bytes, blocks, as_stream(stream)), fn);
+}
+
+tq_status tq_peak_mfma(int kind, int iters, int blocks, float* out_dev, void* stream) {
+  const char* fn = "tq_peak_mfma";
+  if (!out_dev || kind < 0 || kind > 3 || iters < 1 || blocks < 1) return fail(TQ_EINVAL, "%s: bad arguments", fn);
+  return check_launch(tq::launch_peak_mfma(kind, iters, blocks, out_dev, as_stream(stream)), fn);
 }
 
 const char* tq_last_error(void) { return g_last_error.c_str(); }

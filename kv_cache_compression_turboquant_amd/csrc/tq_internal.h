@@ -79,9 +79,17 @@ namespace tq {
 // Compute units of the current device (cached per device).
 int num_cus();
 
-// The event pair armed by tq_timer_arm on this thread, if any, handed to the next launch that
-// supports timing (and disarmed); false when none is armed.
-bool take_armed_timer(hipEvent_t* start, hipEvent_t* stop);
+// The event pair armed on this thread for kernel kind `which` (tq_timed_kernel), if any, handed
+// to the next launch of that kind (and disarmed); false when none is armed.
+bool take_armed_timer(int which, hipEvent_t* start, hipEvent_t* stop);
+inline bool take_armed_timer(hipEvent_t* start, hipEvent_t* stop) {
+  return take_armed_timer(TQ_TIMED_ENCODE, start, stop);
+}
+
+// Measurement ceilings (tq_peaks.hip).
+hipError_t launch_peak_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st);
+hipError_t launch_peak_copy(void* dst, const void* src, int64_t bytes, int blocks, hipStream_t st);
+hipError_t launch_peak_mfma(int kind, int iters, int blocks, float* out, hipStream_t st);
 
 // Launchers (tq_encode128.hip, tq_misc.hip, tq_score128.hip, tq_attn128.hip).  All return the
 // HIP error of the launch.

@@ -1,5 +1,7 @@
 // Query prologue (q_rot = R q, q_s = S q once per query head) and the compressed-key score
 // kernel at d = 128, MSE and TurboQuant_prod, with GQA sharing.
+#include <hip/hip_ext.h>
+
 #include "tq_cache.h"
 #include "tq_decode.h"
 
@@ -364,6 +366,14 @@ hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, int64_t seq_stride
   if (tpw < kScoreBatch) tpw = kScoreBatch;
   if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + tpw * kScoreWaves - 1) / (tpw * kScoreWaves);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (take_armed_timer(TQ_TIMED_SCORES, &ev0, &ev1)) {
+    // events attached to the dispatch itself: they bracket the kernel's execution alone
+    hipExtLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs),
+                          dim3(kScoreWaves * 64), 0, st, ev0, ev1, 0, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw,
+                          K->idx, K->norms, PROD ? K->qjl : nullptr, PROD ? K->rnorms : nullptr, cb, scores);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
                      0, st, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
                      PROD ? K->rnorms : nullptr, cb, scores);

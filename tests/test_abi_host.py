@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(tq):
     for name in names:
         assert hasattr(raw, name), name
         assert name in _binding.SIGNATURES, f"binding lacks {name}"
-    assert tq.lib().tq_abi_version() == 5
+    assert tq.lib().tq_abi_version() == 6
 
 
 def test_splitmix_bit_identical(tq):
@@ -190,7 +190,23 @@ def test_timer_entry_points(tq):
     # without a device no events can be created: arming fails cleanly
     t = lib.tq_timer_arm()
     assert t == -1 or 0 <= t < 256
+    assert lib.tq_timer_arm_kernel(7) == -1          # unknown kernel kind
+    assert b"unknown kernel kind" in lib.tq_last_error()
     lib.tq_timer_reset()
+
+
+def test_peak_entry_points_validate(tq):
+    """The measurement-ceiling kernels reject bad arguments before any launch."""
+    lib = tq.lib()
+    dummy = ctypes.c_void_p(16)
+    assert lib.tq_peak_read(None, 1024, 4, None, None) == 1
+    assert lib.tq_peak_read(dummy, 1000, 4, None, None) == 1      # not a multiple of 16
+    assert lib.tq_peak_read(dummy, 1024, 0, None, None) == 1
+    assert lib.tq_peak_copy(dummy, None, 1024, 4, None) == 1
+    assert lib.tq_peak_copy(dummy, dummy, 0, 4, None) == 1
+    assert lib.tq_peak_mfma(4, 10, 4, dummy, None) == 1           # unknown kind
+    assert lib.tq_peak_mfma(0, 0, 4, dummy, None) == 1
+    assert lib.tq_peak_mfma(0, 10, 4, None, None) == 1
 
 
 def test_cache_entry_points_validate(tq):
@@ -230,3 +246,37 @@ def test_split_entry_points_validate(tq):
     assert lib.tq_scores_split(None, 1, 8, 2, 5, None, ctypes.byref(desc), ctypes.byref(desc), cbh.ptr, cbh.ptr,
                                None, None, None, None, 0, None) == 1
     assert lib.tq_scores_split_workspace(2, 32) == 2 * 32 * 128 * 4
+
+
+def test_split_wrappers_reject_bad_tensors(tq):
+    """The Python split wrappers check shapes, dtypes, contiguity, output size and devices before
+    calling the library (its split functions take no d and read 128 values per key)."""
+    import torch
+    TQE = tq.TQError
+    sp = object()                      # never reached: every case fails in the wrapper
+    n = 1 * 2 * 5
+    K = (tq.alloc_packed(n, 64, 3, device="cpu"), tq.alloc_packed(n, 64, 2, device="cpu"))
+    # encode_split / cache_append_split: x must be contiguous [B, H, T, 128] bf16 or fp32
+    for fn in (lambda x: tq.encode_split(x, sp, None, None, None, None, out=K),
+               lambda x: tq.cache_append_split(K, x, 0, 5, sp, None, None, None, None)):
+        with pytest.raises(TQE, match=r"\[B, H, T, 128\]"):
+            fn(torch.zeros((1, 2, 5, 64)))
+        with pytest.raises(TQE, match=r"\[B, H, T, 128\]"):
+            fn(torch.zeros((2 * 5, 128)))
+        with pytest.raises(TQE, match="bf16 or fp32"):
+            fn(torch.zeros((1, 2, 5, 128), dtype=torch.float16))
+        with pytest.raises(TQE, match="contiguous"):
+            fn(torch.zeros((1, 5, 2, 128)).transpose(1, 2))
+    # scores_split / scores_split_cache: q must be contiguous fp32 [B, Hq, 128]; out sized B*Hq*T
+    for fn in (lambda q, out=None: tq.scores_split(q, K, 2, sp, None, None, None, None, out=out),
+               lambda q, out=None: tq.scores_split_cache(q, K, 2, 5, 5, sp, None, None, None, None, out=out)):
+        with pytest.raises(TQE, match=r"\[B, Hq, 128\]"):
+            fn(torch.zeros((1, 8, 64)))
+        with pytest.raises(TQE, match="fp32"):
+            fn(torch.zeros((1, 8, 128), dtype=torch.bfloat16))
+        with pytest.raises(TQE, match="contiguous"):
+            fn(torch.zeros((1, 128, 8)).transpose(1, 2))
+        with pytest.raises(TQE, match="out must be"):
+            fn(torch.zeros((1, 8, 128)), out=torch.zeros((1, 8, 4)))
+        with pytest.raises(TQE, match="out must be"):
+            fn(torch.zeros((1, 8, 128)), out=torch.zeros((1, 8, 5), dtype=torch.float64))

@@ -148,7 +148,8 @@ def _packed_to_oracle(p, d, bits, prod):
 
 
 @pytest.mark.parametrize("b,hkv,hq,T,B", [(3, 2, 8, 1000, 2), (2, 1, 32, 4096, 1), (4, 4, 8, 17, 1),
-                                         (1, 2, 4, 300, 1), (3, 8, 8, 64, 1), (2, 4, 8, 33, 3)])
+                                         (1, 2, 4, 300, 1), (3, 8, 8, 64, 1), (2, 4, 8, 33, 3),
+                                         (3, 2, 6, 257, 1)])
 def test_scores_mse_on_gpu_packed(dev, rot_dense, b, hkv, hq, T, B):
     x, xt = _keys(T, hkv=hkv, B=B)
     cb_o = oracle.codebook(128, b)

@@ -65,7 +65,7 @@ def _gpu_as_oracle(po, pr, B, H, T, order):
 @pytest.mark.parametrize("bo,br,dtype", [(3, 2, "bf16"), (4, 3, "bf16"), (2, 1, "bf16"), (4, 4, "f32"),
                                          (1, 4, "f32"), (3, 3, "bf16")])
 def test_encode_split_matches_oracle(dev, rots, bo, br, dtype):
-    B, H, T = 2, 2, 300                      # 300 = 2 blocks of 128 + a ragged 44
+    B, H, T = 2, 2, 300                      # 300 tokens: one 512-token block of the MFMA kernel, ragged
     x, xt = _keys(B, H, T, seed=bo * 10 + br)
     if dtype == "f32":
         x = x * (1.0 + 1e-3 * wl.gaussian(x.shape, 9))   # values off the bf16 grid
@@ -285,12 +285,15 @@ def test_split_cache_appends_and_scores(dev, rots):
     assert e.value.status == 1
 
 
+@pytest.mark.parametrize("bo,br", [(2, 1), (1, 4), (3, 2), (4, 3)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_short_encode_per_token_path(dev, rots, dtype):
-    # At most 32 tokens per sequence take the one-block-per-token kernel: its codes against the
-    # oracle, with a zero key and a key whose outlier half is zero among them.
-    B, H, T, bo, br = 2, 3, 9, 4, 3
-    x, _ = _keys(B, H, T, seed=17)
+@pytest.mark.parametrize("T", [9, 32, 33])
+def test_short_encode_per_token_path(dev, rots, dtype, bo, br, T):
+    # At most 32 tokens per sequence take the one-block-per-token kernel, 33 the MFMA kernel: the
+    # codes against the oracle on both sides of the switch, with a zero key and a key whose outlier
+    # half is zero among them.
+    B, H = 2, 3
+    x, _ = _keys(B, H, T, seed=17 + T)
     out = _outliers(x)
     x[1, 2, 4] = 0.0
     x[0, 1, 7][out[1]] = 0.0
