@@ -150,6 +150,21 @@ def pmc_summary(fetch_db, write_db):
     print("\n".join(lines))
 
 
+def trace_summary(db):
+    """Markdown table of a rocprofv3 --kernel-trace database: calls and mean / min / max duration
+    per kernel, longest total first."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = {}
+    for name, dur in con.execute("select name, duration from kernels"):
+        rows.setdefault(_short(name), []).append(float(dur) / 1e3)
+    lines = ["| kernel | calls | mean us | min us | max us | total us |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name[:90]}` | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} | "
+                     f"{np.sum(v):.1f} |")
+    print("\n".join(lines))
+
+
 def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same workload: one KV head slab of
     keys encoded and scored by the 4 query heads that share it (the full step is 8 such slabs of
@@ -695,12 +710,17 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run plain device copies of COPY_PROBE_BYTES "
                          "(the calibration for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace database; no GPU needed")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made with "
                          "--copy-probe into profiles/traffic.json and print the table; no GPU needed")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "

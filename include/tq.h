@@ -208,6 +208,19 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
                     void* ws_dev, size_t ws_bytes, void* stream);
 
+/* tq_scores for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels and results, with the query
+ * workspace taken from a static device array inside the library (tq_scores_noalloc_max_bytes()
+ * bytes, 4 MiB: up to 4080 query heads B*Hq) instead of a caller buffer.  Each GPU holds its own
+ * copy of that array until the process ends; its address is looked up on the first call on each
+ * device.  Nothing is allocated: no hipMalloc, no hipFree, no allocating library call.  Every call
+ * on one GPU uses the same array, so calls whose work overlaps on one GPU (other streams, other
+ * threads) race and may return wrong scores: serialise them.  Errors as for tq_scores, plus
+ * TQ_ENOMEM when tq_scores_workspace(B, Hq, d) exceeds the static size. */
+tq_status tq_scores_noalloc(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                            tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev, void* stream);
+size_t tq_scores_noalloc_max_bytes(void);
+
 /* The two stages of tq_scores, for callers that overlap the query prologue with other work (for
  * instance the encode of the keys being appended) on another stream.
  * tq_prepare_queries: q_rot = R q (fp16 hi/lo) and, when qjl is non-NULL, the QJL sketch S q

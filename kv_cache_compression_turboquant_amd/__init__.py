@@ -18,7 +18,7 @@ __all__ = [
     "rotation_from_matrix", "make_qjl", "qjl_from_matrix", "alloc_packed", "encode", "rotate",
     "quantize_rotated", "decode", "scores", "scores_workspace", "packed_words", "TQError",
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
-    "prepare_queries", "scores_prepared", "timer_arm", "timer_read", "timer_reset",
+    "prepare_queries", "scores_prepared", "scores_noalloc", "timer_arm", "timer_read", "timer_reset",
     "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
     "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
@@ -252,6 +252,21 @@ def scores(q, K, Hkv, cb, rot, qjl=None, out=None, ws=None):
     check(lib().tq_scores(_dptr(q), B, Hq, Hkv, T, ctypes.byref(desc), cb.ptr, rot.ptr,
                           qjl.ptr if qjl is not None else None, _dptr(out), _dptr(ws),
                           ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def scores_noalloc(q, K, Hkv, cb, rot, qjl=None, out=None):
+    """tq_scores with the query workspace in the library's static device scratch (no allocation
+    inside the call; `out` is allocated here only when not given).  Calls that overlap on one GPU
+    race on that scratch."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    T = K.n // max(B * Hkv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    desc = K.descriptor()
+    check(lib().tq_scores_noalloc(_dptr(q), B, Hq, Hkv, T, ctypes.byref(desc), cb.ptr, rot.ptr,
+                                  qjl.ptr if qjl is not None else None, _dptr(out), _stream()))
     return out
 
 

@@ -72,6 +72,8 @@ SIGNATURES = {
     "tq_timer_read": (_I, [_I, ctypes.POINTER(ctypes.c_float)]),
     "tq_timer_reset": (None, []),
     "tq_timer_arm_kernel": (_I, [_I]),
+    "tq_scores_noalloc": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),
+    "tq_scores_noalloc_max_bytes": (_SZ, []),
     "tq_peak_read": (_I, [_P, _SZ, _I, _P, _P]),
     "tq_peak_copy": (_I, [_P, _P, _SZ, _I, _P]),
     "tq_peak_mfma": (_I, [_I, _I, _I, _P, _P]),

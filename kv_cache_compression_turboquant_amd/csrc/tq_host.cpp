@@ -932,9 +932,10 @@ tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq,
                       fn);
 }
 
+// use_scratch: the workspace is the library's static scratch (ws_dev / ws_bytes ignored).
 static tq_status scores_impl(const char* fn, const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t rows,
                              const tq_packed* K, tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
-                             void* ws_dev, size_t ws_bytes, void* stream) {
+                             void* ws_dev, size_t ws_bytes, void* stream, bool use_scratch = false) {
   if (!K || !cb || !rot) return fail(TQ_EINVAL, "%s: null argument", fn);
   tq_status st = check_score_heads(B, Hq, Hkv, fn);
   if (st != TQ_OK) return st;
@@ -956,6 +957,14 @@ static tq_status scores_impl(const char* fn, const float* q_dev, int B, int Hq, 
   if ((int64_t)B * Hq * T == 0) return ok();
   if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
   size_t need = tq::scores_workspace_bytes(B, Hq, d);
+  if (use_scratch) {
+    if (need > tq::noalloc_scratch_bytes())
+      return fail(TQ_ENOMEM, "%s: B*Hq=%lld query heads need %zu bytes of scratch, above the static %zu bytes",
+                  fn, (long long)B * Hq, need, tq::noalloc_scratch_bytes());
+    hipError_t se = tq::noalloc_scratch(&ws_dev);
+    if (se != hipSuccess) return hip_fail(se, fn);
+    ws_bytes = tq::noalloc_scratch_bytes();
+  }
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
   hipStream_t hs = as_stream(stream);
   hipError_t e = tq::launch_prepare_queries(q_dev, B, Hq, Hkv, rot, K->mode == TQ_MODE_PROD ? qjl : nullptr, ws_dev, hs);
@@ -968,6 +977,14 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
                     void* ws_dev, size_t ws_bytes, void* stream) {
   return scores_impl("tq_scores", q_dev, B, Hq, Hkv, T, T, K, cb, rot, qjl, scores_dev, ws_dev, ws_bytes, stream);
 }
+
+tq_status tq_scores_noalloc(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
+                            tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev, void* stream) {
+  return scores_impl("tq_scores_noalloc", q_dev, B, Hq, Hkv, T, T, K, cb, rot, qjl, scores_dev, nullptr, 0, stream,
+                     true);
+}
+
+size_t tq_scores_noalloc_max_bytes(void) { return tq::noalloc_scratch_bytes(); }
 
 tq_status tq_scores_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T, int64_t T_cap, const tq_packed* K,
                           tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev, void* ws_dev,

@@ -86,6 +86,11 @@ inline bool take_armed_timer(hipEvent_t* start, hipEvent_t* stop) {
   return take_armed_timer(TQ_TIMED_ENCODE, start, stop);
 }
 
+// The static scratch of the allocation-free entry points (tq_noalloc.hip): its size, and the
+// current device's address of it (looked up on the first call on each device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 // Measurement ceilings (tq_peaks.hip).
 hipError_t launch_peak_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st);
 hipError_t launch_peak_copy(void* dst, const void* src, int64_t bytes, int blocks, hipStream_t st);
