@@ -83,7 +83,7 @@ def test_noalloc_rejects_more_heads_than_the_scratch_holds(dev):
     assert cap == 4 << 20
     rot = tq.make_rotation(D, 1, "dense")
     cb = tq.codebook(D, 3)
-    B, hkv, hq, T = 1, 1, 4096, 1       # 4096 query heads need more than 4 MiB
+    B, hkv, hq, T = 2, 64, 2048, 1      # 4096 query heads (GQA 32) need more than 4 MiB
     p = tq.alloc_packed(B * hkv * T, D, 3, "mse", device=dev)
     q = torch.zeros((B, hq, D), device=dev)
     with pytest.raises(tq.TQError) as e:
