@@ -651,6 +651,7 @@ hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rota
     }
     return hipErrorInvalidValue;
   }
+  if (prod && cb.bits <= 3) return launch_encode_prod_d128(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, st);
   switch (cb.bits) {
     case 1:
       return prod ? enc_dispatch_in<1, true, false>(x, bf16, n, rot, qjl, cb, idx, norms, qjl_bits, rnorms, nullptr, st)

@@ -307,6 +307,28 @@ void build_fragments(const double* m, double scale, std::vector<uint16_t>& out) 
         }
 }
 
+// Fragments of the d = 128 matrix m scaled by `scale` for v_mfma_f32_32x32x16_bf16 (A operand):
+// [pass][ob][s][lane][e] = M[o][c], i = lane % 32, j = lane / 32,
+// o = 64 ((i >> 2) & 1) + 16 ob + 4 (i >> 3) + (i & 3), c = 64 j + 8 s + e.  With this row order,
+// output block ob's register r in lane (i, j) is coordinate 64 j + 16 ob + r.
+void build_fragments32(const double* m, double scale, std::vector<uint16_t>& out) {
+  out.assign(2 * (size_t)tq::kFragElems, 0);
+  for (int ob = 0; ob < 4; ++ob)
+    for (int s = 0; s < 8; ++s)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          const int i = lane % 32, j = lane / 32;
+          const int row = 64 * ((i >> 2) & 1) + 16 * ob + 4 * (i >> 3) + (i & 3);
+          const int col = 64 * j + 8 * s + e;
+          const float v = (float)(m[(size_t)row * 128 + col] * scale);
+          const uint16_t hi = bf16_rne(v);
+          const uint16_t lo = bf16_rne(v - bf16_to_f(hi));
+          const size_t idx = (((size_t)ob * 8 + s) * 64 + lane) * 8 + e;
+          out[idx] = hi;
+          out[(size_t)tq::kFragElems + idx] = lo;
+        }
+}
+
 // Chunked fragments of a d x d matrix (d a multiple of 128) for the general-d GEMM kernels:
 // chunk (ob, kc) is the 128 x 128 block M[128 ob .., 128 kc ..] laid out exactly as
 // build_fragments lays out a d = 128 matrix; chunks follow each other as [ob][kc][pass].
@@ -354,6 +376,7 @@ void free_rotation(tq_rotation_s* r) {
   if (r->rt32_dev) hipFree(r->rt32_dev);
   if (r->frag_dev) hipFree(r->frag_dev);
   if (r->fragt_dev) hipFree(r->fragt_dev);
+  if (r->frag32_dev) hipFree(r->frag32_dev);
   if (r->gfrag_dev) hipFree(r->gfrag_dev);
   delete r;
 }
@@ -363,6 +386,7 @@ void free_qjl(tq_qjl_s* q) {
   if (q->s32_dev) hipFree(q->s32_dev);
   if (q->st32_dev) hipFree(q->st32_dev);
   if (q->frag_dev) hipFree(q->frag_dev);
+  if (q->frag32_dev) hipFree(q->frag32_dev);
   if (q->gfrag_dev) hipFree(q->gfrag_dev);
   delete q;
 }
@@ -380,24 +404,28 @@ tq_status finish_rotation(tq_rotation_s* r) {
   st = upload(rt32, &r->rt32_dev, "upload rotation transpose");
   if (st != TQ_OK) return st;
   if (d == tq::kFragD) {
-    std::vector<uint16_t> frag, fragt;
+    std::vector<uint16_t> frag, fragt, frag32;
     if (r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT) {
       // sqrt(g) R = H diag(sigma) (block diagonal for BLOCK_WHT, g = its group; g = d otherwise)
       // has entries 0 and +-1: exact in bf16, one pass, scale after.
       const double g = std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup));
       build_fragments(r->r.data(), g, frag);
       build_fragments_t(r->r.data(), g, fragt);
+      build_fragments32(r->r.data(), g, frag32);
       r->passes = 1;
       r->post_scale = (float)(1.0 / g);
     } else {
       build_fragments(r->r.data(), 1.0, frag);
       build_fragments_t(r->r.data(), 1.0, fragt);
+      build_fragments32(r->r.data(), 1.0, frag32);
       r->passes = 2;
       r->post_scale = 1.0f;
     }
     st = upload(frag, &r->frag_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
     st = upload(fragt, &r->fragt_dev, "upload rotation fragments");
+    if (st != TQ_OK) return st;
+    st = upload(frag32, &r->frag32_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
   } else if (general_d(d)) {
     std::vector<uint16_t> frag;
@@ -444,6 +472,10 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
     if (d == tq::kFragD) {
       build_fragments(sp.data(), 1.0, frag);
       st = upload(frag, &q->frag_dev, "upload qjl fragments");
+      if (st == TQ_OK) {
+        build_fragments32(sp.data(), 1.0, frag);
+        st = upload(frag, &q->frag32_dev, "upload qjl fragments");
+      }
     } else {
       build_fragments_g(sp.data(), d, 1.0, frag);
       st = upload(frag, &q->gfrag_dev, "upload qjl fragments");

@@ -59,6 +59,9 @@ struct tq_rotation_s {
   uint16_t* gfrag_dev = nullptr;  // general d (multiple of 128, >= 256): A fragments of R, one
                                   // (128 x 128) chunk per (output block ob, contraction block kc):
                                   // [ob][kc][pass 0..1][kFragElems], each chunk laid out like frag_dev
+  uint16_t* frag32_dev = nullptr; // d = 128: A fragments for v_mfma_f32_32x32x16_bf16 [2][kFragElems]:
+                                  // [pass][ob][s][lane][e] = R[o][c], i = lane % 32, j = lane / 32,
+                                  // o = 64 ((i >> 2) & 1) + 16 ob + 4 (i >> 3) + (i & 3), c = 64 j + 8 s + e
   int passes = 2;                 // 1 when R is exactly representable after scaling
   float post_scale = 1.0f;        // y = post_scale * (fragments . x)
 };
@@ -71,6 +74,7 @@ struct tq_qjl_s {
   float* s32_dev = nullptr;       // fp32 S, row-major [d, d]
   float* st32_dev = nullptr;      // fp32 S^T, row-major [d, d]
   uint16_t* frag_dev = nullptr;   // bf16 fragments of S' = S R^T [2][kFragElems] (d = 128)
+  uint16_t* frag32_dev = nullptr; // S' as 32 x 32 x 16 fragments, laid out as tq_rotation_s::frag32_dev
   uint16_t* gfrag_dev = nullptr;  // general d: chunked A fragments of S', as tq_rotation_s::gfrag_dev
 };
 
@@ -102,6 +106,10 @@ hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rota
                               const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx,
                               float* norms, uint32_t* qjl_bits, float* rnorms, float* y_out,
                               hipStream_t st);
+// TurboQuant_prod encode at d = 128 on the 32 x 32 x 16 matrix cores (tq_encode_prod128.hip).
+hipError_t launch_encode_prod_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                   const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                   uint32_t* qjl_bits, float* rnorms, hipStream_t st);
 hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const CodebookArgs& cb,
                                    uint32_t* idx, hipStream_t st);
 hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
