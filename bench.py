@@ -165,6 +165,25 @@ def trace_summary(db):
     print("\n".join(lines))
 
 
+def pmc_table(db):
+    """Markdown table of a rocprofv3 --pmc database: per kernel, the mean over dispatches of every
+    counter collected (values as the profiler reports them, summed over the device per dispatch)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    q = ("select k.name, p.counter_name, p.value from counters_collection p join kernels k "
+         "on p.dispatch_id = k.dispatch_id")
+    acc = {}
+    for name, cn, v in con.execute(q):
+        acc.setdefault(_short(name), {}).setdefault(cn, []).append(float(v))
+    counters = sorted({c for d in acc.values() for c in d})
+    lines = ["| kernel | dispatches | " + " | ".join(counters) + " |", "|---|---|" + "---|" * len(counters)]
+    for name, d in sorted(acc.items()):
+        nd = max(len(v) for v in d.values())
+        lines.append(f"| `{name[:70]}` | {nd} | " + " | ".join(
+            f"{np.mean(d[c]):.4g}" if c in d else "" for c in counters) + " |")
+    print("\n".join(lines))
+
+
 def cpu_baseline(cfg, keys_bits, q, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same workload: one KV head slab of
     keys encoded and scored by the 4 query heads that share it (the full step is 8 such slabs of
@@ -712,6 +731,8 @@ def main():
                          "(the calibration for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace database; no GPU needed")
+    ap.add_argument("--pmc-table", metavar="DB",
+                    help="print the per-kernel means of every counter in a rocprofv3 --pmc database; no GPU needed")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made with "
                          "--copy-probe into profiles/traffic.json and print the table; no GPU needed")
@@ -721,6 +742,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "

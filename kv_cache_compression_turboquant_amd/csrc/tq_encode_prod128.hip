@@ -15,7 +15,7 @@
 // 2 * BITS index words and 2 sign words.
 // Order of work per tile: the rotation's output blocks run ob = 3 .. 0; block ob + 1 is quantized
 // while block ob's MFMAs run.  The S' product starts with the instructions that read blocks 3 .. 1
-// before block 0 is quantized.  The next tile's loads are issued once x is dead.
+// before block 0 is quantized.  Loads of the tile after next are issued once x is dead.
 #include <hip/hip_ext.h>
 
 #include "tq_device.h"
@@ -190,13 +190,17 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
 #pragma unroll
     for (int k = 0; k < kStage; ++k) lds[threadIdx.x + ((k + rot0) % kStage) * kThreads] = stage[k];
   }
-  XRaw<BF16IN> xr;
-  load_x<BF16IN>(x, n, tw, lane, xr);
+  // bf16 input: two register sets in turn, so a tile's loads go out a whole tile before it is
+  // needed (fp32 input has one set: its raw tile is twice the size).
+  constexpr int NB = BF16IN ? 2 : 1;
+  XRaw<BF16IN> xa, xb;
+  load_x<BF16IN>(x, n, tw, lane, xa);
+  if constexpr (NB == 2) load_x<BF16IN>(x, n, tw + stride, lane, xb);
   __syncthreads();
 
   const float inv_post = 1.0f / post_scale;
   const u32x4* lds_s = lds + RP * kFrag32U4;
-  for (;;) {
+  auto step = [&](XRaw<BF16IN>& xr, const int64_t tw) {
     // ---- B operands of the rotation and the norm
     u32x4 bx[8], bxl[BF16IN ? 1 : 8];
     float ss = 0.f;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
     });
 
     // x is dead: the next tile's loads go out now and arrive during the second product
-    const int64_t tn = tw + stride;
+    const int64_t tn = tw + NB * stride;
     if (tn < ntiles) load_x<BF16IN>(x, n, tn, lane, xr);
 
     // ---- z^T = S' r^T.  Block 3's instructions that read residual blocks 3 .. 1 (s = 7 .. 2)
@@ -324,7 +328,16 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
         rnorm_out[row] = nrm * sqrtf(rs);
       }
     }
-    tw = tn;
+  };
+  // Entered unconditionally: a wave without a tile of its own (last block only) makes one pass
+  // over clamped rows and stores nothing.
+  for (;;) {
+    step(xa, tw);
+    if constexpr (NB == 2) {
+      if (tw + stride >= ntiles) break;
+      step(xb, tw + stride);
+    }
+    tw += NB * stride;
     if (tw >= ntiles) break;
   }
 }
