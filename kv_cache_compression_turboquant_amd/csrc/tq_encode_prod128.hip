@@ -15,7 +15,8 @@
 // 2 * BITS index words and 2 sign words.
 // Order of work per tile: the rotation's output blocks run ob = 3 .. 0; block ob + 1 is quantized
 // while block ob's MFMAs run.  The S' product starts with the instructions that read blocks 3 .. 1
-// before block 0 is quantized.  Loads of the tile after next are issued once x is dead.
+// while block 0 is quantized.  Loads of the tile after next are issued once x is dead.  Every
+// MFMA's A fragment is read from LDS a few instructions ahead.
 #include <hip/hip_ext.h>
 
 #include "tq_device.h"
@@ -26,6 +27,14 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kProdWaves = 8;
+// Tuning switch (build-time define): TQ_PROD_PRIO = 1 raises a wave's issue priority while it runs
+// the S' product (MFMA-heavy), so the other wave's quantizer (VALU-heavy) issues in its shadow.
+#ifndef TQ_PROD_PRIO
+#define TQ_PROD_PRIO 0
+#endif
+#ifndef TQ_PROD_NB
+#define TQ_PROD_NB 1
+#endif
 constexpr int kFrag32U4 = 2048;   // u32x4 per pass: 4 output blocks x 8 instructions x 64 lanes
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -91,11 +100,12 @@ __device__ __forceinline__ void down_from(F&& f) {
 
 // Per-vector quantizer state: thresholds t_p * ||x|| / post_scale against the raw product, the
 // non-negative centroids, and the raw-product -> unit-coordinate scale.
+// Named members rather than arrays: a select tree over an array's elements is otherwise turned
+// into a per-lane indexed load from LDS (with bank conflicts), slower than three selects.
 template <int BITS>
 struct QState {
-  static constexpr int H = 1 << (BITS - 1);
-  float thr[H > 1 ? H - 1 : 1];
-  float mag[H];
+  float t0, t1, t2;          // positive thresholds (BITS = 2: t0; BITS = 3: t0 < t1 < t2)
+  float m0, m1, m2, m3;      // non-negative centroids (BITS = 1: m0; 2: m0, m1; 3: m0 .. m3)
   float scale;
 };
 
@@ -112,50 +122,77 @@ __device__ __forceinline__ float quant_coord(float v, const QState<BITS>& q, uin
   const float a = fabsf(v);
   float mag;
   if constexpr (BITS == 1) {
-    mag = q.mag[0];
+    mag = q.m0;
   } else if constexpr (BITS == 2) {
-    const bool ge = a >= q.thr[0];
+    const bool ge = a >= q.t0;
     w[P >> 5] = shift_in(w[P >> 5], ~(__builtin_amdgcn_ballot_w64(ge) ^ pos));
-    mag = ge ? q.mag[1] : q.mag[0];
+    mag = ge ? q.m1 : q.m0;
   } else {
-    const bool hi = a >= q.thr[1];
+    const bool hi = a >= q.t1;
     w[(P + 1) >> 5] = shift_in(w[(P + 1) >> 5], ~(__builtin_amdgcn_ballot_w64(hi) ^ pos));
-    const bool lo = a >= (hi ? q.thr[2] : q.thr[0]);
+    const bool lo = a >= (hi ? q.t2 : q.t0);
     w[P >> 5] = shift_in(w[P >> 5], ~(__builtin_amdgcn_ballot_w64(lo) ^ pos));
-    mag = hi ? (lo ? q.mag[3] : q.mag[2]) : (lo ? q.mag[1] : q.mag[0]);
+    const float m_lo = lo ? q.m1 : q.m0;
+    const float m_hi = lo ? q.m3 : q.m2;
+    mag = hi ? m_hi : m_lo;
   }
   return fmaf(v, q.scale, nonneg ? -mag : mag);
 }
 
-// Quantize output block OB (coordinates 16 OB + 15 .. 16 OB, descending) and leave its residual
-// as bf16 hi / lo pairs in rh / rl (instruction s = 2 OB + (r >> 3), dword (r & 7) / 2).
-template <int BITS, int OB>
-__device__ __forceinline__ void quant_block(const f32x16& y, const QState<BITS>& q, uint32_t (&w)[2 * BITS],
-                                            u32x4 (&rh)[8], u32x4 (&rl)[8], float& rs) {
-  float res[16];
-  down_from<15>([&](auto rc) {
-    constexpr int r = decltype(rc)::value;
-    res[r] = quant_coord<BITS, 16 * OB + r>(y[r], q, w);
-  });
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    rs = fmaf(res[r], res[r], rs);
-    rs = fmaf(res[r + 1], res[r + 1], rs);
-    const f32x2 pr = {res[r], res[r + 1]};
-    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-    const f32x2 rem = {res[r] - __uint_as_float(h << 16), res[r + 1] - __uint_as_float(h & 0xffff0000u)};
-    const int s = 2 * OB + (r >> 3);
-    rh[s][(r & 7) >> 1] = h;
-    rl[s][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+// Quantize the pair of coordinates (R, R + 1) of output block OB (R even; R + 1 first, so a
+// lane's coordinates go in descending order), accumulate their squared residuals into rs and
+// leave the residuals as one bf16 hi / lo dword each in rh / rl (instruction s = 2 OB + (R >> 3),
+// dword (R & 7) / 2 of the second product's B operand).
+template <int BITS, int OB, int R>
+__device__ __forceinline__ void quant_pair(const f32x16& y, const QState<BITS>& q, uint32_t (&w)[2 * BITS],
+                                           u32x4 (&rh)[8], u32x4 (&rl)[8], float& rs) {
+  const float r1 = quant_coord<BITS, 16 * OB + R + 1>(y[R + 1], q, w);
+  const float r0 = quant_coord<BITS, 16 * OB + R>(y[R], q, w);
+  rs = fmaf(r0, r0, rs);
+  rs = fmaf(r1, r1, rs);
+  const f32x2 pr = {r0, r1};
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+  const f32x2 rem = {r0 - __uint_as_float(h << 16), r1 - __uint_as_float(h & 0xffff0000u)};
+  constexpr int s = 2 * OB + (R >> 3);
+  rh[s][(R & 7) >> 1] = h;
+  rl[s][(R & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
+}
+
+// Sign bits (z >= 0) of registers R and R - 1 of S' output block OB (sign index 16 OB + r of the
+// lane's 64), pushed in descending order into the lane's two sign words.
+template <int OB, int R>
+__device__ __forceinline__ void push_sign_pair(const f32x16& z, uint32_t (&qw)[2]) {
+  qw[OB >> 1] = shift_in(qw[OB >> 1], __builtin_amdgcn_ballot_w64(z[R] >= 0.f));
+  qw[OB >> 1] = shift_in(qw[OB >> 1], __builtin_amdgcn_ballot_w64(z[R - 1] >= 0.f));
+}
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Ci<B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
-// Sign bits of S' output block OB (sign index 16 OB + r of the lane's 64): pushed in descending
-// order into the lane's two sign words.
-template <int OB>
-__device__ __forceinline__ void push_signs(const f32x16& z, uint32_t (&qw)[2]) {
-#pragma unroll
-  for (int r = 15; r >= 0; --r) qw[OB >> 1] = shift_in(qw[OB >> 1], __builtin_amdgcn_ballot_w64(z[r] >= 0.f));
+// The matrix products of one tile as one flat sequence of 64 steps, each step's A fragments read
+// from LDS kRing steps ahead into a ring of registers (an LDS read waited on right before its MFMA
+// would expose the LDS latency at every instruction).  Steps 0 .. 31: the rotation, output block
+// ob = 3 - k / 8, instruction s = k % 8 (RP fragments).  Steps 32 .. 63: S', output block
+// ob = 3 - (k - 32) / 8, instruction s = 7 - (k - 32) % 8 (S' hi and lo).  The sequence repeats
+// from tile to tile, so the ring runs on across tiles.
+constexpr int kRing = 3;
+
+template <int RP, int K>
+__device__ __forceinline__ void load_step(const u32x4* lds, int lane, u32x4 (&slot)[2]) {
+  if constexpr (K < 32) {
+    constexpr int ob = 3 - (K >> 3), s = K & 7;
+    slot[0] = lds[(ob * 8 + s) * 64 + lane];
+    if constexpr (RP == 2) slot[1] = lds[kFrag32U4 + (ob * 8 + s) * 64 + lane];
+  } else {
+    constexpr int ob = 3 - ((K - 32) >> 3), s = 7 - ((K - 32) & 7);
+    slot[0] = lds[RP * kFrag32U4 + (ob * 8 + s) * 64 + lane];
+    slot[1] = lds[(RP + 1) * kFrag32U4 + (ob * 8 + s) * 64 + lane];
+  }
 }
 
 template <int BITS, bool BF16IN, int RP>
@@ -177,7 +214,7 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
   const int64_t stride = (int64_t)gridDim.x * kProdWaves;
   int64_t tw = (int64_t)blockIdx.x * kProdWaves + wave;
 
-  // Fragment loads first, then the first tile's, so the tile stays in flight across the staging.
+  // Fragment loads first, then the first tiles', so the tiles stay in flight across the staging.
   // Blocks start at different slices: every block reads the same fragments.
   {
     u32x4 stage[kStage];
@@ -190,32 +227,30 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
 #pragma unroll
     for (int k = 0; k < kStage; ++k) lds[threadIdx.x + ((k + rot0) % kStage) * kThreads] = stage[k];
   }
-  // bf16 input: two register sets in turn, so a tile's loads go out a whole tile before it is
-  // needed (fp32 input has one set: its raw tile is twice the size).
-  constexpr int NB = BF16IN ? 2 : 1;
+  // TQ_PROD_NB register sets of raw tiles in turn (1: the next tile's loads go out once x is dead;
+  // 2: a whole tile earlier, at the cost of 32 registers).  The loads are unconditional (rows past
+  // the end read the last row, never stored): a conditional load would leave the number of loads
+  // in flight unknown to the compiler, which then waits for all of them.
+  constexpr int NB = BF16IN ? TQ_PROD_NB : 1;
   XRaw<BF16IN> xa, xb;
   load_x<BF16IN>(x, n, tw, lane, xa);
   if constexpr (NB == 2) load_x<BF16IN>(x, n, tw + stride, lane, xb);
   __syncthreads();
 
+  u32x4 ring[kRing][2];
+  static_for<0, kRing>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    load_step<RP, k>(lds, lane, ring[k]);
+  });
+
   const float inv_post = 1.0f / post_scale;
-  const u32x4* lds_s = lds + RP * kFrag32U4;
   auto step = [&](XRaw<BF16IN>& xr, const int64_t tw) {
-    // ---- B operands of the rotation and the norm
+    // ---- B operands of the rotation
     u32x4 bx[8], bxl[BF16IN ? 1 : 8];
     float ss = 0.f;
     if constexpr (BF16IN) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bx[s] = xr.v[s];
-        uint32_t wv[4];
-        __builtin_memcpy(wv, &xr.v[s], sizeof(wv));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x2 p = __builtin_bit_cast(bf16x2, wv[k]);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
-        }
-      }
+      for (int s = 0; s < 8; ++s) bx[s] = xr.v[s];
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -233,87 +268,89 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
         }
       }
     }
-    ss += __shfl_xor(ss, 32);
-    const float nrm = sqrtf(ss);
-    const bool live = nrm > 0.f;
     QState<BITS> qs;
-    {
-      const float tsc = nrm * inv_post;
-#pragma unroll
-      for (int p = 0; p < H - 1; ++p) qs.thr[p] = live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY;
-#pragma unroll
-      for (int p = 0; p < H; ++p) qs.mag[p] = live ? cb.cpos[p] : 0.f;
-      qs.scale = live ? post_scale / nrm : 0.f;
-    }
-
-    // ---- y^T = R x^T, block by block (ob = 3 .. 0), the previous block quantized meanwhile
     uint32_t w[2 * BITS];
 #pragma unroll
     for (int k = 0; k < 2 * BITS; ++k) w[k] = 0;
     u32x4 rh[8], rl[8];
     float rs = 0.f;
-    f32x16 prev = zero16();
-    down_from<3>([&](auto obc) {
-      constexpr int ob = decltype(obc)::value;
-      f32x16 acc = zero16();
+    f32x16 acc = zero16(), prev = zero16();
+    float nrm = 0.f;
+
+    // ---- steps 0 .. 31: y^T = R x^T; block ob + 1 is quantized (two coordinates per step)
+    // during block ob's instructions; the norm is formed during block 3's.
+    static_for<0, 32>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ob = 3 - (k >> 3), s = k & 7;
+      if constexpr (s == 0) acc = zero16();
+      acc = mfma32(ring[k % kRing][0], bx[s], acc);
+      if constexpr (!BF16IN) acc = mfma32(ring[k % kRing][0], bxl[s], acc);
+      if constexpr (RP == 2) acc = mfma32(ring[k % kRing][1], bx[s], acc);
+      load_step<RP, (k + kRing) % 64>(lds, lane, ring[k % kRing]);
+      if constexpr (ob == 3) {
+        if constexpr (BF16IN) {
+          uint32_t wv[4];
+          __builtin_memcpy(wv, &bx[s], sizeof(wv));
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 a0 = lds[(ob * 8 + s) * 64 + lane];
-        acc = mfma32(a0, bx[s], acc);
-        if constexpr (!BF16IN) acc = mfma32(a0, bxl[s], acc);
-        if constexpr (RP == 2) acc = mfma32(lds[kFrag32U4 + (ob * 8 + s) * 64 + lane], bx[s], acc);
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 p2 = __builtin_bit_cast(bf16x2, wv[e]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss, false);
+          }
+        }
+        if constexpr (s == 7) {
+          ss += __shfl_xor(ss, 32);
+          nrm = sqrtf(ss);
+          const bool live = nrm > 0.f;
+          const float tsc = nrm * inv_post;
+          auto thr = [&](int p) { return p < H - 1 ? (live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY) : INFINITY; };
+          auto mag = [&](int p) { return p < H ? (live ? cb.cpos[p] : 0.f) : 0.f; };
+          qs.t0 = thr(0);
+          qs.t1 = thr(1);
+          qs.t2 = thr(2);
+          qs.m0 = mag(0);
+          qs.m1 = mag(1);
+          qs.m2 = mag(2);
+          qs.m3 = mag(3);
+          qs.scale = live ? post_scale / nrm : 0.f;
+        }
+      } else {
+        quant_pair<BITS, ob + 1, 14 - 2 * s>(prev, qs, w, rh, rl, rs);
       }
-      if constexpr (ob < 3) quant_block<BITS, ob + 1>(prev, qs, w, rh, rl, rs);
-      prev = acc;
+      if constexpr (s == 7) prev = acc;
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // x is dead: the next tile's loads go out now and arrive during the second product
-    const int64_t tn = tw + NB * stride;
-    if (tn < ntiles) load_x<BF16IN>(x, n, tn, lane, xr);
+    // x is dead: the loads of the tile after next go out now
+    load_x<BF16IN>(x, n, tw + NB * stride, lane, xr);
 
-    // ---- z^T = S' r^T.  Block 3's instructions that read residual blocks 3 .. 1 (s = 7 .. 2)
-    // first, then block 0 is quantized, then the rest.
+    // ---- steps 32 .. 63: z^T = S' r^T.  Block 3 runs s = 7 .. 0, so its first six steps read
+    // only residual blocks 3 .. 1 while block 0 is quantized (16 coordinates over those six steps);
+    // each later block pushes the previous block's 16 signs (two per step).
     uint32_t qw[2] = {0u, 0u};
-    f32x16 zprev = zero16();
-    {
-      f32x16 z = zero16();
-#pragma unroll
-      for (int s = 7; s >= 2; --s) {
-        const u32x4 sh = lds_s[(3 * 8 + s) * 64 + lane];
-        const u32x4 sl = lds_s[kFrag32U4 + (3 * 8 + s) * 64 + lane];
-        z = mfma32(sh, rh[s], z);
-        z = mfma32(sh, rl[s], z);
-        z = mfma32(sl, rh[s], z);
+    f32x16 z = zero16(), zprev = zero16();
+    if constexpr (TQ_PROD_PRIO) __builtin_amdgcn_s_setprio(2);
+    static_for<32, 64>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ob = 3 - ((k - 32) >> 3), s = 7 - ((k - 32) & 7), i = (k - 32) & 7;
+      if constexpr (i == 0) z = zero16();
+      z = mfma32(ring[k % kRing][0], rh[s], z);
+      z = mfma32(ring[k % kRing][0], rl[s], z);
+      z = mfma32(ring[k % kRing][1], rh[s], z);
+      load_step<RP, (k + kRing) % 64>(lds, lane, ring[k % kRing]);
+      if constexpr (ob == 3) {
+        // block 0's pairs (14, 15), (12, 13), .. (0, 1) over steps i = 0 .. 5
+        if constexpr (i < 6) {
+          constexpr int p0 = (i * 8) / 6, p1 = ((i + 1) * 8) / 6;   // pairs [p0, p1) of 8
+          static_for<p0, p1>([&](auto pc) { quant_pair<BITS, 0, 14 - 2 * decltype(pc)::value>(prev, qs, w, rh, rl, rs); });
+        }
+      } else {
+        push_sign_pair<ob + 1, 15 - 2 * i>(zprev, qw);
       }
-      quant_block<BITS, 0>(prev, qs, w, rh, rl, rs);
-#pragma unroll
-      for (int s = 1; s >= 0; --s) {
-        const u32x4 sh = lds_s[(3 * 8 + s) * 64 + lane];
-        const u32x4 sl = lds_s[kFrag32U4 + (3 * 8 + s) * 64 + lane];
-        z = mfma32(sh, rh[s], z);
-        z = mfma32(sh, rl[s], z);
-        z = mfma32(sl, rh[s], z);
-      }
-      zprev = z;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    down_from<2>([&](auto obc) {
-      constexpr int ob = decltype(obc)::value;
-      f32x16 z = zero16();
-#pragma unroll
-      for (int s = 7; s >= 0; --s) {
-        const u32x4 sh = lds_s[(ob * 8 + s) * 64 + lane];
-        const u32x4 sl = lds_s[kFrag32U4 + (ob * 8 + s) * 64 + lane];
-        z = mfma32(sh, rh[s], z);
-        z = mfma32(sh, rl[s], z);
-        z = mfma32(sl, rh[s], z);
-      }
-      push_signs<ob + 1>(zprev, qw);
-      zprev = z;
+      if constexpr (i == 7) zprev = z;
       __builtin_amdgcn_sched_barrier(0);
     });
-    push_signs<0>(zprev, qw);
+    static_for<0, 8>([&](auto ic) { push_sign_pair<0, 15 - 2 * decltype(ic)::value>(zprev, qw); });
+    if constexpr (TQ_PROD_PRIO) __builtin_amdgcn_s_setprio(0);
 
     // ---- stores
     rs += __shfl_xor(rs, 32);
