@@ -180,7 +180,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // ob = 3 - k / 8, instruction s = k % 8 (RP fragments).  Steps 32 .. 63: S', output block
 // ob = 3 - (k - 32) / 8, instruction s = 7 - (k - 32) % 8 (S' hi and lo).  The sequence repeats
 // from tile to tile, so the ring runs on across tiles.
-constexpr int kRing = 3;
+constexpr int kRing = 4;   // divides the 64 steps, so step k of every tile uses slot k % kRing
 
 template <int RP, int K>
 __device__ __forceinline__ void load_step(const u32x4* lds, int lane, u32x4 (&slot)[2]) {

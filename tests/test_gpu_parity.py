@@ -136,6 +136,30 @@ def test_encode_prod_parity(dev, rot_dense, rot_wht, kind):
     assert np.all(np.abs(g[ok] - encp.gamma[ok]) <= 2e-5 * encp.mse.norms[ok] + 1e-12)
 
 
+@pytest.mark.parametrize("kind,b", [("dense", 4), ("wht", 3), ("dense", 2)])
+def test_encode_prod_many_tiles_per_wave(dev, rot_dense, rot_wht, kind, b):
+    # 159857 keys: more 32-key tiles than the grid has waves, so every wave runs several
+    # tiles in a row (its fragment prefetch wraps from one tile into the next) and a ragged last tile.
+    rot, rmat = (rot_dense, R_DENSE) if kind == "dense" else (rot_wht, R_WHT)
+    qjl = tq.make_qjl(128, 2, rot)
+    x, xt = _keys(40000, hkv=4)
+    n = x.shape[0] - 143
+    x, xt = x[:n], xt[:n].contiguous()
+    cb_o = oracle.codebook(128, b - 1)
+    cb = tq.codebook(128, b - 1)
+    p = tq.encode(xt.to(dev), b, "prod", cb, rot, qjl)
+    torch.cuda.synchronize()
+    encp = oracle.encode_prod(x, rmat, cb_o, S_MAT)
+    gidx = oracle.unpack_bits(to_np_words(p.idx), 128, b - 1)
+    bad_rows, _ = check_indices(gidx, encp.mse.y, cb_o, f"prod stage {kind} b={b}")
+    gz = unpack_z(to_np_words(p.qjl), 128)
+    check_signs(gz, encp.proj, S_MAT, encp.mse.norms, ~bad_rows, f"prod signs {kind} b={b}")
+    g = p.rnorms.cpu().numpy()
+    ok = ~bad_rows
+    assert np.all(np.abs(g[ok] - encp.gamma[ok]) <= 2e-5 * encp.mse.norms[ok] + 1e-12)
+    np.testing.assert_allclose(p.norms.cpu().numpy(), encp.mse.norms, rtol=1e-6)
+
+
 def _packed_to_oracle(p, d, bits, prod):
     idx = oracle.unpack_bits(to_np_words(p.idx), d, bits)
     norms = p.norms.cpu().numpy().astype(np.float64)
