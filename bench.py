@@ -32,18 +32,19 @@ CACHE_DEFEAT_BYTES = 1.5e9
 # Sources of each timed kernel: its counters stay valid while these files are unchanged.
 KERNEL_SOURCES = {
     "encode": ("tq_device.h", "tq_internal.h", "tq_encode128.hip"),
+    "prod_encode": ("tq_device.h", "tq_internal.h", "tq_encode_prod128.hip"),
     "scores": ("tq_device.h", "tq_internal.h", "tq_decode.h", "tq_cache.h", "tq_score128.hip"),
 }
 # (encode kernel, score kernel) of each step workload, as the profiler names them
 HEADLINE_KERNELS = {
-    "c3": ("k_encode_d128<3, true, true, false, 2, 1> (prod b=4, dense R, bf16 keys)",
+    "c3": ("k_encode_prod_d128<3, true, 2> (prod b=4, dense R, bf16 keys)",
            "k_scores_d128<3, true, false> (prod, GQA 4)"),
     "c2": ("k_encode_mse_d128<3, true, 2, 2> (MSE b=3, dense R, bf16 keys)",
            "k_scores_d128<3, false, false> (MSE, GQA 4)"),
 }
 # name prefixes of those kernels in a rocprofv3 database (for the counter summary)
 PMC_KERNELS = {
-    "c3:encode": "k_encode_d128<3, true, true, false, 2,",
+    "c3:prod_encode": "k_encode_prod_d128<3, true, 2>",
     "c3:scores": "k_scores_d128<3, true, false>",
     "c2:encode": "k_encode_mse_d128<3, true, 2,",
     "c2:scores": "k_scores_d128<3, false, false>",
@@ -692,7 +693,7 @@ def step_bench(name, steps, warmup, copy_probe_after=False, cpu_budget=0.0, even
         "roofline": {"bound": "hbm", "kernel": enc_kernel,
                      "timing": f"HIP events attached to the kernel's dispatch on every {event_every}th timed step",
                      "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profile(name + ":encode"),
+                     "traffic": traffic_from_profile(name + (":prod_encode" if prod else ":encode")),
                      "alg_bytes_per_launch": enc_alg_bytes,
                      "mfma_issued": {"passes": passes, "tflops": issued_flops / (enc_ms * 1e-3) / 1e12,
                                      "peak": 2500.0, "frac": issued_flops / (enc_ms * 1e-3) / 1e12 / 2500.0}},

@@ -32,9 +32,7 @@ constexpr int kProdWaves = 8;
 #ifndef TQ_PROD_PRIO
 #define TQ_PROD_PRIO 0
 #endif
-#ifndef TQ_PROD_NB
-#define TQ_PROD_NB 1
-#endif
+
 constexpr int kFrag32U4 = 2048;   // u32x4 per pass: 4 output blocks x 8 instructions x 64 lanes
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -57,6 +55,12 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t lanes) {
   return r;
 }
 
+// Raw buffer resource over `bytes` bytes at p (loads past the end read zeros, stores past the end
+// are dropped, by the range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // A lane's 64 input coordinates of one vector.
 template <bool BF16IN>
 struct XRaw;
@@ -69,19 +73,26 @@ struct XRaw<false> {
   f32x4 v[16];
 };
 
+// Loads of tile `tile` through a buffer resource bounded by the tile's rows that exist: rows past
+// the end read zeros (never stored).  A buffer load may alias the kernel's buffer stores for all
+// the compiler knows, so it is not sunk past them to its use in the next tile (an ordinary load
+// from a restrict pointer would be, exposing the memory latency there).
 template <bool BF16IN>
 __device__ __forceinline__ void load_x(const void* x, int64_t n, int64_t tile, int lane, XRaw<BF16IN>& r) {
-  const int64_t row0 = tile * 32 + (lane & 31);
-  const int64_t row = row0 < n ? row0 : n - 1;    // past the end: the last row (never stored)
-  const int half = lane >> 5;
+  constexpr uint32_t kRow = BF16IN ? 256u : 512u;
+  const int64_t row0 = tile * 32;
+  const int64_t left = n - row0;
+  const uint32_t rows = left >= 32 ? 32u : (left > 0 ? (uint32_t)left : 0u);
+  const __amdgpu_buffer_rsrc_t rx =
+      store_rsrc(static_cast<const char*>(x) + (row0 < n ? row0 : 0) * kRow, rows * kRow);
+  const uint32_t off = (uint32_t)(lane & 31) * kRow + (uint32_t)(lane >> 5) * (kRow / 2);
   if constexpr (BF16IN) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + row * 128 + 64 * half);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) r.v[s] = src[s];
+    for (int s = 0; s < 8; ++s) r.v[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u * s, 0, 0);
   } else {
-    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + row * 128 + 64 * half);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) r.v[s] = src[s];
+    for (int s = 0; s < 16; ++s)
+      r.v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u * s, 0, 0));
   }
 }
 
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
   // rotation passes 0 .. RP-1, then S' hi, S' lo; each [ob][s][lane]
   __shared__ u32x4 lds[kTotal];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile bases in SGPRs
   const int half = lane >> 5;
   const int64_t ntiles = (n + 31) >> 5;
   const int64_t stride = (int64_t)gridDim.x * kProdWaves;
@@ -227,14 +238,11 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
 #pragma unroll
     for (int k = 0; k < kStage; ++k) lds[threadIdx.x + ((k + rot0) % kStage) * kThreads] = stage[k];
   }
-  // TQ_PROD_NB register sets of raw tiles in turn (1: the next tile's loads go out once x is dead;
-  // 2: a whole tile earlier, at the cost of 32 registers).  The loads are unconditional (rows past
-  // the end read the last row, never stored): a conditional load would leave the number of loads
-  // in flight unknown to the compiler, which then waits for all of them.
-  constexpr int NB = BF16IN ? TQ_PROD_NB : 1;
-  XRaw<BF16IN> xa, xb;
-  load_x<BF16IN>(x, n, tw, lane, xa);
-  if constexpr (NB == 2) load_x<BF16IN>(x, n, tw + stride, lane, xb);
+  // The tile loads are unconditional (rows past the end read the last row, never stored): a
+  // conditional load would leave the number of loads in flight unknown to the compiler, which then
+  // waits for all of them.
+  XRaw<BF16IN> xr;
+  load_x<BF16IN>(x, n, tw, lane, xr);
   __syncthreads();
 
   u32x4 ring[kRing][2];
@@ -244,7 +252,15 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
   });
 
   const float inv_post = 1.0f / post_scale;
-  auto step = [&](XRaw<BF16IN>& xr, const int64_t tw) {
+  // State a tile's rotation phase hands to its S' phase.
+  QState<BITS> qs;
+  uint32_t w[2 * BITS];
+  u32x4 rh[8], rl[8];
+  float rs, nrm;
+  f32x16 prev;
+
+  // ---- rotation phase of tile tw: steps 0 .. 31, then the loads of tile tw + stride
+  auto rphase = [&](const int64_t tw) {
     // ---- B operands of the rotation
     u32x4 bx[8], bxl[BF16IN ? 1 : 8];
     float ss = 0.f;
@@ -268,14 +284,11 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
         }
       }
     }
-    QState<BITS> qs;
-    uint32_t w[2 * BITS];
 #pragma unroll
     for (int k = 0; k < 2 * BITS; ++k) w[k] = 0;
-    u32x4 rh[8], rl[8];
-    float rs = 0.f;
-    f32x16 acc = zero16(), prev = zero16();
-    float nrm = 0.f;
+    rs = 0.f;
+    f32x16 acc = zero16();
+    prev = zero16();
 
     // ---- steps 0 .. 31: y^T = R x^T; block ob + 1 is quantized (two coordinates per step)
     // during block ob's instructions; the norm is formed during block 3's.
@@ -320,9 +333,13 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // x is dead: the loads of the tile after next go out now
-    load_x<BF16IN>(x, n, tw + NB * stride, lane, xr);
+    // x is dead: the next tile's loads go out now, to arrive during this tile's S' phase
+    load_x<BF16IN>(x, n, tw + stride, lane, xr);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
+  // ---- S' phase of tile tw, then its stores
+  auto sphase = [&](const int64_t tw) {
     // ---- steps 32 .. 63: z^T = S' r^T.  Block 3 runs s = 7 .. 0, so its first six steps read
     // only residual blocks 3 .. 1 while block 0 is quantized (16 coordinates over those six steps);
     // each later block pushes the previous block's 16 signs (two per step).
@@ -352,30 +369,40 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
     static_for<0, 8>([&](auto ic) { push_sign_pair<0, 15 - 2 * decltype(ic)::value>(zprev, qw); });
     if constexpr (TQ_PROD_PRIO) __builtin_amdgcn_s_setprio(0);
 
-    // ---- stores
+    // ---- stores, through buffer resources bounded by the tile's rows that exist: a row past the
+    // end is dropped by the range check.  Every store is unconditional, so the compiler keeps
+    // exact count of the memory operations in flight (a store under a branch makes it wait for
+    // all of them, the next tile's loads included, before the next tile starts).  Both halves of a
+    // vector hold the same norm and residual norm and both store them.
     rs += __shfl_xor(rs, 32);
-    const int64_t row = tw * 32 + (lane & 31);
-    if (row < n) {
-      uint32_t* dst = idx_out + row * (4 * BITS) + 2 * BITS * half;
+    const int64_t row0 = tw * 32;
+    const int64_t left = n - row0;
+    const uint32_t live_rows = left >= 32 ? 32u : (left > 0 ? (uint32_t)left : 0u);
+    const int i = lane & 31;
+    const __amdgpu_buffer_rsrc_t ridx = store_rsrc(idx_out + (row0 < n ? row0 : 0) * (4 * BITS), live_rows * (16u * BITS));
+    const __amdgpu_buffer_rsrc_t rq = store_rsrc(qjl_out + (row0 < n ? row0 : 0) * 4, live_rows * 16u);
+    const __amdgpu_buffer_rsrc_t rn = store_rsrc(norms_out + (row0 < n ? row0 : 0), live_rows * 4u);
+    const __amdgpu_buffer_rsrc_t rr = store_rsrc(rnorm_out + (row0 < n ? row0 : 0), live_rows * 4u);
 #pragma unroll
-      for (int k = 0; k < 2 * BITS; ++k) dst[k] = w[k];
-      *reinterpret_cast<u32x2*>(qjl_out + row * 4 + 2 * half) = u32x2{qw[0], qw[1]};
-      if (half == 0) {
-        norms_out[row] = nrm;
-        rnorm_out[row] = nrm * sqrtf(rs);
-      }
-    }
+    for (int k = 0; k < BITS; ++k)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2 * k], w[2 * k + 1]}, ridx,
+                                            (uint32_t)(i * (16 * BITS) + 8 * BITS * half + 8 * k), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{qw[0], qw[1]}, rq, (uint32_t)(i * 16 + 8 * half), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nrm), rn, (uint32_t)(i * 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nrm * sqrtf(rs)), rr, (uint32_t)(i * 4), 0, 0);
   };
+  // The loop is rotated so that it starts at an S' phase: on every path into its first
+  // instruction the latest memory operations are the same eight tile loads, so the compiler's
+  // wait counts there are exact (with the rotation phase first, the first entry, which has no
+  // stores behind the loads, would force a wait for every store of the previous tile).
   // Entered unconditionally: a wave without a tile of its own (last block only) makes one pass
   // over clamped rows and stores nothing.
+  rphase(tw);
   for (;;) {
-    step(xa, tw);
-    if constexpr (NB == 2) {
-      if (tw + stride >= ntiles) break;
-      step(xb, tw + stride);
-    }
-    tw += NB * stride;
+    sphase(tw);
+    tw += stride;
     if (tw >= ntiles) break;
+    rphase(tw);
   }
 }
 
