@@ -27,10 +27,10 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kProdWaves = 8;
-// Tuning switch (build-time define): TQ_PROD_PRIO = 1 raises a wave's issue priority while it runs
+// Tuning switch (build-time define): TQ_PROD_PRIO = 1 (default) raises a wave's issue priority while it runs
 // the S' product (MFMA-heavy), so the other wave's quantizer (VALU-heavy) issues in its shadow.
 #ifndef TQ_PROD_PRIO
-#define TQ_PROD_PRIO 0
+#define TQ_PROD_PRIO 1
 #endif
 
 constexpr int kFrag32U4 = 2048;   // u32x4 per pass: 4 output blocks x 8 instructions x 64 lanes
