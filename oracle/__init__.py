@@ -32,7 +32,7 @@ from .quantizer import (nearest_index, pack_bits, unpack_bits, pack_token_blocke
                         unpack_token_blocked, encode_mse, decode_mse,
                         encode_prod, decode_prod, qjl_matrix, qjl_encode, qjl_correction, scores_mse, scores_prod,
                         quantize_rotated, EncodedMSE, EncodedProd, QJL_CONST)
-from .attention import decode_attention, topk
+from .attention import decode_attention, prefill_attention, topk
 from .kv_cache import (cache_rows, append_rows_mse, append_rows_prod, assign_token_blocked,
                        append_token_blocked_mse, live_rows)
 from .split import channel_order, encode_split, decode_split, scores_split, EncodedSplit
@@ -45,7 +45,7 @@ __all__ = [
     "nearest_index", "pack_bits", "unpack_bits", "pack_token_blocked", "unpack_token_blocked", "encode_mse", "decode_mse", "encode_prod",
     "decode_prod", "qjl_matrix", "qjl_encode", "qjl_correction", "scores_mse", "scores_prod", "quantize_rotated",
     "EncodedMSE", "EncodedProd", "QJL_CONST",
-    "decode_attention", "topk",
+    "decode_attention", "prefill_attention", "topk",
     "cache_rows", "append_rows_mse", "append_rows_prod", "assign_token_blocked",
     "append_token_blocked_mse", "live_rows",
 ]
