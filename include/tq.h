@@ -303,6 +303,30 @@ tq_status tq_decode_attn_cache(const float* q_dev, int B, int Hq, int Hkv, int64
                                float scale, float* out_dev, void* ws_dev, size_t ws_bytes,
                                void* stream);
 
+/* Workspace bytes of tq_prefill_attn for a chunk of n_new tokens (the rotated queries, fp16 hi and
+ * lo): 512 bytes per query row B*Hq*n_new.  0 for d != 128. */
+size_t tq_prefill_attn_workspace(int B, int Hq, int64_t n_new, int d);
+/* Prefill of a chunk fused with attention over the compressed cache ([TQ] KV-cache example,
+ * prefill: the prompt's keys and values are compressed as they are written; decode section, second
+ * route: unpack, look up and scale inside the attention, never materialising K_hat or V_hat;
+ * [RQ] Flash Attention fusion section).  Appends keys k_dev and values v_dev [B, Hkv, n_new, d]
+ * (dtype dt) at rows pos .. pos + n_new - 1 of every sequence of the key cache K (ROWS, MSE, cb_k's
+ * bits) and the value cache V (TOKEN_BLOCKED, MSE, cb_v's bits) of capacity T_cap, exactly as
+ * tq_kv_append does, then writes out_dev[b, h, i] (fp32 [B, Hq, n_new, d]) =
+ *   sum_{t <= pos + i} softmax_t(scale <q[b,h,i], k_hat[b,g,t]>) v_hat[b,g,t],  g = h / (Hq/Hkv),
+ * for queries q_dev fp32 [B, Hq, n_new, d]: chunk token i sits at position pos + i and attends
+ * causally to every cached token up to itself (earlier chunks included).  Keys and values are read
+ * back from the packed caches inside the kernel (k_hat = s R_K^T C_K[idx], v_hat = s R_V^T C_V[idx]);
+ * the value sum runs in V's rotated domain and R_V^T is applied once per output row.
+ * d = 128; T_cap a multiple of 32; GQA ratio up to 64; (b_k, b_v) in {(1,1), (2,2), (3,3), (4,4),
+ * (2,3), (2,4), (3,2), (3,4), (4,2), (4,3)}.  ws_dev: tq_prefill_attn_workspace bytes.
+ * Errors: those of tq_kv_append for either cache; TQ_ESHAPE (Hq % Hkv, T_cap % 32); TQ_EUNSUPPORTED
+ * (ratio, bit pair, more than 2^31 - 1 query rows); TQ_ENOMEM (workspace); TQ_EINVAL (null pointers). */
+tq_status tq_prefill_attn(const float* q_dev, const void* k_dev, const void* v_dev, tq_dtype dt, int B, int Hq,
+                          int Hkv, int64_t n_new, int64_t pos, int64_t T_cap, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                          tq_rotation_t rot_k, tq_rotation_t rot_v, tq_packed* K, tq_packed* V, float scale,
+                          float* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* ---- outlier-channel mixed precision (d = 128) ----------------------------------------
  * [RQ] the asymmetric needs of K and V: keys need more bits, e.g. mixed precision with the
  * outlier channels at more bits than the rest; [TQ] engineering data points: 2.5 and 3.5 bits

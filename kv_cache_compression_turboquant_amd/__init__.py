@@ -20,6 +20,7 @@ __all__ = [
     "decode_attn", "decode_attn_workspace", "encode_workspace", "search_workspace", "search_topk",
     "prepare_queries", "scores_prepared", "scores_noalloc", "timer_arm", "timer_read", "timer_reset",
     "KVCache", "alloc_cache", "cache_append", "kv_append", "scores_cache", "decode_attn_cache",
+    "prefill_attn", "prefill_attn_workspace",
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
     "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
@@ -420,6 +421,35 @@ def _check_scores_out(fn, out, n):
     torch = _torch()
     if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n:
         raise TQError(1, f"{fn}: out must be contiguous fp32 with {n} elements")
+
+def prefill_attn_workspace(B, Hq, n_new, d=128):
+    return int(lib().tq_prefill_attn_workspace(B, Hq, n_new, d))
+
+
+def prefill_attn(q, kc, vc, k, v, pos, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws=None):
+    """Appends keys k and values v [B, Hkv, n_new, d] (same dtype, contiguous) at position pos of
+    the key cache kc (rows, MSE) and value cache vc (token-blocked, MSE), then returns the causal
+    attention [B, Hq, n_new, d] fp32 of the chunk's queries q [B, Hq, n_new, d] over the cache."""
+    torch = _torch()
+    B, Hq, n_new, d = q.shape
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4 or k.shape[2] != n_new:
+        raise TQError(2, "prefill_attn: k and v must be [B, Hkv, n_new, d] of one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise TQError(1, "prefill_attn: q, k and v must be contiguous")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((B, Hq, n_new, d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((max(prefill_attn_workspace(B, Hq, n_new, d), 1),), dtype=torch.uint8, device=q.device)
+    kd, vd = kc.packed.descriptor(), vc.packed.descriptor()
+    check(lib().tq_prefill_attn(_dptr(q), _dptr(k), _dptr(v), _dtype_code(k), B, Hq, Hkv, n_new, pos, kc.t_cap,
+                                cb_k.ptr, cb_v.ptr, rot_k.ptr, rot_v.ptr, ctypes.byref(kd), ctypes.byref(vd),
+                                ctypes.c_float(scale), _dptr(out), _dptr(ws), ws.numel() * ws.element_size(),
+                                _stream()))
+    return out
+
 
 class Split(_Handle):
     """Per-KV-head channel split of d = 128 keys: 64 outlier channels, then the rest."""

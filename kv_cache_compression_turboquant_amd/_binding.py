@@ -74,6 +74,9 @@ SIGNATURES = {
     "tq_timer_arm_kernel": (_I, [_I]),
     "tq_scores_noalloc": (_I, [_P, _I, _I, _I, _I64, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P]),
     "tq_scores_noalloc_max_bytes": (_SZ, []),
+    "tq_prefill_attn_workspace": (_SZ, [_I, _I, _I64, _I]),
+    "tq_prefill_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.POINTER(tq_packed),
+                             ctypes.POINTER(tq_packed), ctypes.c_float, _P, _P, _SZ, _P]),
     "tq_peak_read": (_I, [_P, _SZ, _I, _P, _P]),
     "tq_peak_copy": (_I, [_P, _P, _SZ, _I, _P]),
     "tq_peak_mfma": (_I, [_I, _I, _I, _P, _P]),

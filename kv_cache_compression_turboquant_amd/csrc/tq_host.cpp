@@ -1156,6 +1156,45 @@ tq_status tq_kv_append(const void* k_dev, const void* v_dev, tq_dtype dt, int B,
                       fn);
 }
 
+size_t tq_prefill_attn_workspace(int B, int Hq, int64_t n_new, int d) {
+  if (B < 0 || Hq < 0 || n_new < 0 || d != tq::kFragD) return 0;
+  return tq::prefill_attn_workspace_bytes(B, Hq, n_new);
+}
+
+tq_status tq_prefill_attn(const float* q_dev, const void* k_dev, const void* v_dev, tq_dtype dt, int B, int Hq,
+                          int Hkv, int64_t n_new, int64_t pos, int64_t T_cap, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                          tq_rotation_t rot_k, tq_rotation_t rot_v, tq_packed* K, tq_packed* V, float scale,
+                          float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_prefill_attn";
+  if (!cb_k || !cb_v || !rot_k || !rot_v || !K || !V) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || Hq < 0 || Hkv < 0 || n_new < 0 || pos < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  if (Hq / Hkv > 64) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d above 64", fn, Hq / Hkv);
+  // the append's own checks (bits, layouts, capacity, d, dtype) on both caches
+  tq_status st = check_cache_append(fn, dt, B, Hkv, n_new, pos, T_cap, cb_k->b, TQ_MODE_MSE, cb_k, rot_k, nullptr, K);
+  if (st != TQ_OK) return st;
+  st = check_cache_append(fn, dt, B, Hkv, n_new, pos, T_cap, cb_v->b, TQ_MODE_MSE, cb_v, rot_v, nullptr, V);
+  if (st != TQ_OK) return st;
+  if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: the key cache must use the ROWS layout", fn);
+  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED)
+    return fail(TQ_EUNSUPPORTED, "%s: the value cache must use the TOKEN_BLOCKED layout", fn);
+  if (T_cap % 32 != 0) return fail(TQ_ESHAPE, "%s: capacity %lld is not a multiple of 32", fn, (long long)T_cap);
+  if (T_cap > kMaxSeqTokens) return fail(TQ_EUNSUPPORTED, "%s: capacity above %lld tokens", fn, (long long)kMaxSeqTokens);
+  if ((int64_t)B * Hkv * n_new == 0) return ok();
+  if ((int64_t)B * Hq * n_new >= (int64_t(1) << 31))
+    return fail(TQ_EUNSUPPORTED, "%s: B*Hq*n_new above 2^31 - 1 query rows", fn);
+  if (!q_dev || !k_dev || !v_dev || !out_dev) return fail(TQ_EINVAL, "%s: null q, k, v or out", fn);
+  const size_t need = tq::prefill_attn_workspace_bytes(B, Hq, n_new);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = tq::launch_kv_append(k_dev, v_dev, dt == TQ_BF16, (int64_t)B * Hkv, n_new, pos, T_cap, rot_k, rot_v,
+                                      cb_k->args, cb_v->args, K, V, hs);
+  if (e == hipSuccess)
+    e = tq::launch_prefill_attn(q_dev, B, Hq, Hkv, n_new, pos, T_cap, K, V, cb_k->args, cb_v->args, rot_k, rot_v, scale,
+                                out_dev, ws_dev, hs);
+  return check_launch(e, fn);
+}
+
 }  // extern "C"
 
 // ---- outlier-channel split codes (d = 128) ------------------------------------------------

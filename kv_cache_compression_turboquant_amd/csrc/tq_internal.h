@@ -90,6 +90,14 @@ inline bool take_armed_timer(hipEvent_t* start, hipEvent_t* stop) {
   return take_armed_timer(TQ_TIMED_ENCODE, start, stop);
 }
 
+// Prefill attention over the caches after a chunk's append (tq_prefill128.hip): q [B, Hq, n_new,
+// 128] fp32 -> out [B, Hq, n_new, 128] fp32; ws holds the rotated queries.
+size_t prefill_attn_workspace_bytes(int B, int Hq, int64_t n_new);
+hipError_t launch_prefill_attn(const float* q, int B, int Hq, int Hkv, int64_t n_new, int64_t pos, int64_t t_cap,
+                               const tq_packed* K, const tq_packed* V, const CodebookArgs& cbk,
+                               const CodebookArgs& cbv, const tq_rotation_s* rot_k, const tq_rotation_s* rot_v,
+                               float scale, float* out, void* ws, hipStream_t st);
+
 // The static scratch of the allocation-free entry points (tq_noalloc.hip): its size, and the
 // current device's address of it (looked up on the first call on each device).
 size_t noalloc_scratch_bytes();

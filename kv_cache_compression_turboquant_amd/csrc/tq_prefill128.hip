@@ -1,0 +1,344 @@
+// Prefill attention fused with the compressed cache, d = 128 ("TurboQuant 详解", KV-cache
+// example: the prompt's keys and values are compressed as they are written; decode section, second
+// route: the cache is unpacked and looked up inside the attention, never materialised;
+// "TurboQuant 和 RotorQuant 的真相", Flash Attention fusion section).  A chunk of n_new tokens has
+// already been appended to the key cache (rows layout) and the value cache (token-blocked layout)
+// at positions pos ..; the query of chunk token i attends causally to cached tokens 0 .. pos + i.
+//
+// Flash-attention shape on the fp16 matrix cores, everything in the caches' rotated domains:
+//   scores^T = K_hat Q^T   A = 16 keys decoded from their packed rows (fp16 centroid hi, and the
+//                          remainder lo), B = 16 query tokens' R_K q (fp16 hi and lo);
+//                          three products (Khi Qhi + Klo Qhi + Khi Qlo) per 32 coordinates.
+//   O^T += V_hat^T P^T     A = value chunks (8 tokens of one coordinate) decoded from the staged
+//                          value block, B = the softmax weights times the value norms in fp16
+//                          hi and lo (two products).
+// With 16-key tile t's A rows laid out as keys 8 (i / 4) + 4 t + i % 4, the scores of a lane
+// (query n, lane group g) over a 32-key step are keys 8 g .. 8 g + 7: exactly the B operand the
+// P V product needs, so the weights never leave the lane's registers, and each query's softmax
+// reductions are across the four lane groups only.
+// A block is four waves of one (batch, kv head); each wave takes one (query head, 16-token tile)
+// item; the block's 32-key steps of packed keys, values and norms are staged in LDS (double
+// buffered) and shared by its waves.  The output stays in V's rotated domain; k_prefill_unrotate
+// applies R_V^T row by row.
+#include <hip/hip_runtime.h>
+
+#include "tq_cache.h"
+#include "tq_decode.h"
+
+namespace tq {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfTok = 16;          // query tokens of a wave's item
+constexpr int kPfQRows = 8;         // query rows per block of the rotation kernels
+
+// q_rot = R q (fp16 hi and lo) for `rows` query rows of 128: rt = R^T row-major, so thread j's
+// reads of column j are coalesced.  Eight rows per block, staged in LDS.
+__global__ __launch_bounds__(256) void k_prefill_qrot(const float* __restrict__ q, int64_t rows,
+                                                      const float* __restrict__ rt, uint16_t* __restrict__ qh,
+                                                      uint16_t* __restrict__ ql) {
+  __shared__ float qs[kPfQRows][128];
+  const int64_t r0 = (int64_t)blockIdx.x * kPfQRows;
+  for (int i = threadIdx.x; i < kPfQRows * 128; i += 256) {
+    const int64_t rr = r0 + (i >> 7);
+    qs[i >> 7][i & 127] = rr < rows ? q[rr * 128 + (i & 127)] : 0.f;
+  }
+  __syncthreads();
+  const int j = threadIdx.x & 127, hh = threadIdx.x >> 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 128; ++k) {
+    const float rv = rt[k * 128 + j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rv, qs[4 * hh + u][k], acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + 4 * hh + u;
+    if (row < rows) {
+      const _Float16 h = (_Float16)acc[u];
+      const _Float16 l = (_Float16)(acc[u] - (float)h);
+      qh[row * 128 + j] = __builtin_bit_cast(uint16_t, h);
+      ql[row * 128 + j] = __builtin_bit_cast(uint16_t, l);
+    }
+  }
+}
+
+// out[row] = R_V^T o[row] in place for `rows` rows of 128 (r = R_V row-major, coalesced over j).
+__global__ __launch_bounds__(256) void k_prefill_unrotate(float* __restrict__ o, int64_t rows,
+                                                          const float* __restrict__ r) {
+  __shared__ float os[kPfQRows][128];
+  const int64_t r0 = (int64_t)blockIdx.x * kPfQRows;
+  for (int i = threadIdx.x; i < kPfQRows * 128; i += 256) {
+    const int64_t rr = r0 + (i >> 7);
+    os[i >> 7][i & 127] = rr < rows ? o[rr * 128 + (i & 127)] : 0.f;
+  }
+  __syncthreads();
+  const int j = threadIdx.x & 127, hh = threadIdx.x >> 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 128; ++k) {
+    const float rv = r[k * 128 + j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rv, os[4 * hh + u][k], acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + 4 * hh + u;
+    if (row < rows) o[row * 128 + j] = acc[u];
+  }
+}
+
+// LDS budgets of the three decode tables (K centroid hi, K remainder lo, V).
+constexpr int kPfTableBudget = 12288;
+
+template <int KB, int VB>
+__global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
+    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql, int Hq, int Hkv, int64_t n_new, int64_t pos,
+    int64_t t_cap, const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
+    const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, CodebookArgs cbk, CodebookArgs cbv,
+    float scale, float* __restrict__ out) {
+  constexpr int KC = table_copies<KB, false, kPfTableBudget>();
+  constexpr int VC = table_copies<VB, false, kPfTableBudget>();
+  using DK = DecodeTable<KB, false, KC>;
+  using DV = DecodeTable<VB, false, VC>;
+  constexpr int KW = 32 * 4 * KB;        // words of a step's 32 key rows
+  constexpr int VW = 128 * VB;           // words of a step's value block
+  __shared__ __attribute__((aligned(16))) uint8_t ktab_h[DK::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ktab_l[DK::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
+  __shared__ _Float16 cent[3][16];
+  // staging, double buffered: key rows, value block (one word of padding for the last chunk's
+  // two-word read), key norms, value norms
+  __shared__ __attribute__((aligned(16))) uint32_t kst[2][KW];
+  __shared__ __attribute__((aligned(16))) uint32_t vst[2][VW + 4];
+  __shared__ float knst[2][32], vnst[2][32];
+
+  if (threadIdx.x < 16) {
+    const float ck = cbk.c[threadIdx.x];
+    const _Float16 hk = (_Float16)ck;
+    cent[0][threadIdx.x] = hk;
+    cent[1][threadIdx.x] = (_Float16)(ck - (float)hk);
+    cent[2][threadIdx.x] = (_Float16)cbv.c[threadIdx.x];
+  }
+  if (threadIdx.x < 8) {
+    vst[0][VW + (threadIdx.x & 3)] = 0u;
+    vst[1][VW + (threadIdx.x & 3)] = 0u;
+  }
+  __syncthreads();
+  build_table<KB, KC>(ktab_h, cent[0]);
+  build_table<KB, KC>(ktab_l, cent[1]);
+  build_table<VB, VC>(vtab, cent[2]);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const uint8_t* kth = DK::lane_base(ktab_h, lane);
+  const uint8_t* ktl = DK::lane_base(ktab_l, lane);
+  const uint8_t* vtl = DV::lane_base(vtab, lane);
+  const int bh = blockIdx.y;
+  const int b = bh / Hkv, kvh = bh % Hkv;
+  const int ratio = Hq / Hkv;
+  const int64_t ntile = (n_new + kPfTok - 1) / kPfTok;
+  // this wave's item: (16-token tile tau, query head hj of the kv head), items ordered tau-major
+  const int64_t item = (int64_t)blockIdx.x * kPfWaves + wave;
+  const int64_t tau = item / ratio;
+  const int hj = (int)(item % ratio);
+  const bool live = tau < ntile;
+  const int64_t tok0 = tau * kPfTok;
+  // the block's last live tile bounds the keys it needs: tokens 0 .. pos + (its last token)
+  int64_t tau_max = ((int64_t)blockIdx.x * kPfWaves + kPfWaves - 1) / ratio;
+  if (tau_max > ntile - 1) tau_max = ntile - 1;
+  const int64_t last_tok = (tau_max + 1) * kPfTok < n_new ? (tau_max + 1) * kPfTok - 1 : n_new - 1;
+  const int64_t kend = pos + last_tok + 1;            // keys [0, kend)
+  const int64_t nsteps = (kend + 31) >> 5;
+  // keys this wave needs: [0, pos + tok0 + 16)
+  const int64_t wave_keys = pos + tok0 + kPfTok;
+  const int64_t row0 = (int64_t)bh * t_cap;
+
+  // B operand of the key product: query token tok0 + n of head h, coordinates 32 g + 8 s .. + 7
+  u32x4 bqh[4], bql[4];
+  {
+    const int64_t tq = tok0 + nl < n_new ? tok0 + nl : n_new - 1;
+    const int64_t qrow = (((int64_t)b * Hq + kvh * ratio + hj) * n_new + (live ? tq : 0));
+    const u32x4* sh = reinterpret_cast<const u32x4*>(qh + qrow * 128 + 32 * g);
+    const u32x4* sl = reinterpret_cast<const u32x4*>(ql + qrow * 128 + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bqh[s] = sh[s];
+      bql[s] = sl[s];
+    }
+  }
+  const int64_t my_tok = pos + tok0 + nl;             // absolute position of the lane's query
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // cooperative staging of step st: u32x4 units 0 .. KW/4 - 1 keys, then VW/4 value words, then
+  // 8 + 8 units of norms
+  constexpr int kUK = KW / 4, kUV = VW / 4, kUnits = kUK + kUV + 16;
+  constexpr int kPer = (kUnits + kPfWaves * 64 - 1) / (kPfWaves * 64);
+  u32x4 stg[kPer];
+  auto fetch = [&](int64_t st) {
+    const int64_t key0 = st * 32;
+    const u32x4* ksrc = reinterpret_cast<const u32x4*>(kidx + (row0 + key0) * (4 * KB));
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vidx + ((row0 + key0) >> 5) * (128 * VB));
+    const u32x4* knsrc = reinterpret_cast<const u32x4*>(knorm + row0 + key0);
+    const u32x4* vnsrc = reinterpret_cast<const u32x4*>(vnorm + row0 + key0);
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int u = threadIdx.x + p * kPfWaves * 64;
+      if (u < kUK) stg[p] = ksrc[u];
+      else if (u < kUK + kUV) stg[p] = vsrc[u - kUK];
+      else if (u < kUK + kUV + 8) stg[p] = knsrc[u - kUK - kUV];
+      else if (u < kUnits) stg[p] = vnsrc[u - kUK - kUV - 8];
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int u = threadIdx.x + p * kPfWaves * 64;
+      if (u < kUK) reinterpret_cast<u32x4*>(kst[buf])[u] = stg[p];
+      else if (u < kUK + kUV) reinterpret_cast<u32x4*>(vst[buf])[u - kUK] = stg[p];
+      else if (u < kUK + kUV + 8) reinterpret_cast<u32x4*>(knst[buf])[u - kUK - kUV] = stg[p];
+      else if (u < kUnits) reinterpret_cast<u32x4*>(vnst[buf])[u - kUK - kUV - 8] = stg[p];
+    }
+  };
+
+  if (nsteps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int buf = (int)(st & 1);
+    if (st + 1 < nsteps) fetch(st + 1);
+    const int64_t key0 = st * 32;
+    if (live && key0 < wave_keys) {
+      // ---- scores^T for the step's 32 keys: tile t, lane (query nl, group g), register r is key
+      // 8 g + 4 t + r
+      float s[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kl = 8 * (nl >> 2) + 4 * t + (nl & 3);     // this lane's A row (key) of tile t
+        uint32_t kw[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) kw[j] = kst[buf][kl * (4 * KB) + KB * g + j];
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x4 ah = decode_keys<KB, KC>(kw, q4, kth);
+          const u32x4 al = decode_keys<KB, KC>(kw, q4, ktl);
+          d = mfma_f16(ah, bqh[q4], d);
+          d = mfma_f16(al, bqh[q4], d);
+          d = mfma_f16(ah, bql[q4], d);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int k = 8 * g + 4 * t + r;
+          const int64_t key = key0 + k;
+          s[4 * t + r] = key <= my_tok ? d[r] * knst[buf][k] * scale : -INFINITY;
+        }
+      }
+      // ---- online softmax of query nl (its 32 keys are spread over the four lane groups)
+      float mx = s[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
+      float psum = 0.f;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        const float p0 = s[k] == -INFINITY ? 0.f : __expf(s[k] - m_new);
+        const float p1 = s[k + 1] == -INFINITY ? 0.f : __expf(s[k + 1] - m_new);
+        psum += p0 + p1;
+        // masked keys give exactly 0 (rows past the written prefix may hold any bits, NaN norms too)
+        const float w0 = s[k] == -INFINITY ? 0.f : p0 * vnst[buf][8 * g + k];
+        const float w1 = s[k + 1] == -INFINITY ? 0.f : p1 * vnst[buf][8 * g + k + 1];
+        const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
+        const _Float16 r0 = (_Float16)(w0 - (float)h0), r1 = (_Float16)(w1 - (float)h1);
+        ph[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        pl[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+      }
+      l_run = fmaf(l_run, alpha, psum);
+      m_run = m_new;
+      if (alpha < 1.f) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] *= alpha;
+      }
+      const u32x4 bph = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      const u32x4 bpl = u32x4{pl[0], pl[1], pl[2], pl[3]};
+      // ---- O^T += V_hat^T P^T: A row m of block c is coordinate 16 c + m; lane (m, g) holds
+      // the chunk of octet g (keys 8 g .. 8 g + 7) at that coordinate
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int off = ((g * 128 + 16 * c + nl) * 8 * VB);
+        const uint32_t w2[2] = {vst[buf][off >> 5], vst[buf][(off >> 5) + 1]};
+        const u32x4 av = decode8<VB, VC>(w2, off & 31, vtl);
+        o[c] = mfma_f16(av, bph, o[c]);
+        o[c] = mfma_f16(av, bpl, o[c]);
+      }
+    }
+    if (st + 1 < nsteps) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- the lane's query nl: its sum over the four lane groups; coordinates 16 c + 4 g + r
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (live && tok0 + nl < n_new) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* dst = out + ((((int64_t)b * Hq + kvh * ratio + hj) * n_new) + tok0 + nl) * 128;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[16 * c + 4 * g + r] = o[c][r] * inv;
+  }
+}
+
+template <int KB, int VB>
+hipError_t prefill_launch(int B, int Hq, int Hkv, int64_t n_new, int64_t pos, int64_t t_cap, const tq_packed* K,
+                          const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv, float scale,
+                          const uint16_t* qh, const uint16_t* ql, float* out, hipStream_t st) {
+  const int ratio = Hq / Hkv;
+  const int64_t items = (n_new + kPfTok - 1) / kPfTok * ratio;
+  const int64_t blocks = (items + kPfWaves - 1) / kPfWaves;
+  hipLaunchKernelGGL((k_prefill_attn<KB, VB>), dim3((unsigned)blocks, (unsigned)(B * Hkv)), dim3(kPfWaves * 64), 0, st,
+                     qh, ql, Hq, Hkv, n_new, pos, t_cap, K->idx, K->norms, V->idx, V->norms, cbk, cbv, scale, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_attn_workspace_bytes(int B, int Hq, int64_t n_new) {
+  const size_t rows = (size_t)B * Hq * (size_t)n_new;
+  return ((rows * 128 * sizeof(uint16_t) + 255) & ~(size_t)255) * 2;
+}
+
+hipError_t launch_prefill_attn(const float* q, int B, int Hq, int Hkv, int64_t n_new, int64_t pos, int64_t t_cap,
+                               const tq_packed* K, const tq_packed* V, const CodebookArgs& cbk,
+                               const CodebookArgs& cbv, const tq_rotation_s* rot_k, const tq_rotation_s* rot_v,
+                               float scale, float* out, void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)B * Hq * n_new;
+  const size_t half = ((size_t)rows * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  uint16_t* qh = static_cast<uint16_t*>(ws);
+  uint16_t* ql = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
+  const unsigned rblocks = (unsigned)((rows + kPfQRows - 1) / kPfQRows);
+  hipLaunchKernelGGL(k_prefill_qrot, dim3(rblocks), dim3(256), 0, st, q, rows, rot_k->rt32_dev, qh, ql);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define TQ_PF(KB, VB) \
+  if (cbk.bits == KB && cbv.bits == VB) \
+    e = prefill_launch<KB, VB>(B, Hq, Hkv, n_new, pos, t_cap, K, V, cbk, cbv, scale, qh, ql, out, st); else
+  TQ_PF(2, 2) TQ_PF(4, 4) TQ_PF(3, 3) TQ_PF(4, 2) TQ_PF(2, 4) TQ_PF(3, 2) TQ_PF(4, 3) TQ_PF(1, 1) TQ_PF(2, 3)
+  TQ_PF(3, 4) return hipErrorInvalidValue;
+#undef TQ_PF
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prefill_unrotate, dim3(rblocks), dim3(256), 0, st, out, rows, rot_v->r32_dev);
+  return hipGetLastError();
+}
+
+}  // namespace tq

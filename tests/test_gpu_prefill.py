@@ -1,0 +1,129 @@
+"""GPU parity of the prefill path fused with attention (tq_prefill_attn, through the C ABI): a
+chunk's keys and values are appended to the compressed caches and its queries attend causally
+over everything cached, old chunks included.
+
+* The appended rows equal those of tq_kv_append on copies of the same caches, bit for bit.
+* The outputs match the oracle's prefill_attention on the GPU's own packed caches within
+  1e-3 * max_t ||v_hat_t|| (the attention tolerance of the decode path).
+* Caches start as seeded garbage, the rows past the written prefix hold NaN norms and random
+  words, which the causal mask must keep out; chunks are ragged against the 16-token query tiles
+  and the 32-token value blocks; GQA ratios 1, 2, 4 and 8; several K/V bit pairs; bf16 and fp32
+  inputs; errors."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_compression_turboquant_amd as tq
+from kv_cache_compression_turboquant_amd import workloads as wl
+from _parity import require_gpu, to_np_words
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+R = oracle.dense_rotation(D, 1)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def rot(dev):
+    return tq.make_rotation(D, 1)
+
+
+def _garbage(cache, seed):
+    g = torch.Generator().manual_seed(seed)
+    p = cache.packed
+    p.idx.copy_(torch.randint(-2**31, 2**31 - 1, p.idx.shape, dtype=torch.int32, generator=g))
+    p.norms.copy_(torch.full(p.norms.shape, float("nan")))
+
+
+def _oracle_out(kc, vc, B, hkv, q, pos, n_new, kb, vb):
+    t_cap = kc.t_cap
+    n = B * hkv * t_cap
+    live = pos + n_new
+    kidx = oracle.unpack_bits(to_np_words(kc.packed.idx), D, kb).reshape(B, hkv, t_cap, D)[:, :, :live]
+    vidx = oracle.unpack_token_blocked(to_np_words(vc.packed.idx), n, D, vb).reshape(B, hkv, t_cap, D)[:, :, :live]
+    kn = kc.packed.norms.cpu().numpy().astype(np.float64).reshape(B, hkv, t_cap)[:, :, :live]
+    vn = vc.packed.norms.cpu().numpy().astype(np.float64).reshape(B, hkv, t_cap)[:, :, :live]
+    ocb_v = oracle.codebook(D, vb)
+    ref = oracle.prefill_attention(q.astype(np.float64), kidx, kn, vidx, vn, pos, R, R, oracle.codebook(D, kb), ocb_v,
+                                   1 / np.sqrt(D))
+    vmax = np.array([[np.max(np.linalg.norm(oracle.decode_mse(vidx[b, g], vn[b, g], R, ocb_v), axis=1))
+                      for g in range(hkv)] for b in range(B)])
+    return ref, vmax
+
+
+def _run(dev, rot, B, hkv, hq, t_cap, plan, kb, vb, dtype=torch.bfloat16, seed=0):
+    cbk, cbv = tq.codebook(D, kb), tq.codebook(D, vb)
+    kc = tq.alloc_cache(B, hkv, t_cap, D, kb, "mse", device=dev)
+    vc = tq.alloc_cache(B, hkv, t_cap, D, vb, "mse", layout="blocked", device=dev)
+    _garbage(kc, seed + 1)
+    _garbage(vc, seed + 2)
+    total = plan[-1][0] + plan[-1][1]
+    kbits = wl.kv_tensor_bf16(B, hkv, total, D, seed=seed + 40, outlier_seed=10, scale_seed=seed + 41)
+    vbits = wl.kv_tensor_bf16(B, hkv, total, D, seed=seed + 42, outlier_seed=21, scale_seed=None)
+    kx = torch.from_numpy(kbits.view(np.int16)).view(torch.bfloat16)
+    vx = torch.from_numpy(vbits.view(np.int16)).view(torch.bfloat16)
+    if dtype == torch.float32:
+        kx = kx.float() * (1.0 + 1e-3 * torch.from_numpy(wl.gaussian(kx.shape, seed + 5)))
+        vx = vx.float() * (1.0 + 1e-3 * torch.from_numpy(wl.gaussian(vx.shape, seed + 6)))
+    q_all = wl.gaussian((B, hq, total, D), seed + 12)
+    ratio = hq // hkv
+    for pos, n_new in plan:
+        k = kx[:, :, pos:pos + n_new].contiguous().to(dev)
+        v = vx[:, :, pos:pos + n_new].contiguous().to(dev)
+        q = np.ascontiguousarray(q_all[:, :, pos:pos + n_new])
+        # the append itself: same bits as tq_kv_append on copies of the caches
+        kc2 = tq.KVCache(B, hkv, t_cap, kb, "mse", tq.Packed(D, kb, "mse", B * hkv * t_cap, kc.packed.idx.clone(),
+                                                             kc.packed.norms.clone()))
+        vc2 = tq.KVCache(B, hkv, t_cap, vb, "mse", tq.Packed(D, vb, "mse", B * hkv * t_cap, vc.packed.idx.clone(),
+                                                             vc.packed.norms.clone(), layout="blocked"))
+        tq.kv_append(kc2, vc2, k, v, pos, cbk, cbv, rot, rot)
+        out = tq.prefill_attn(torch.from_numpy(q).to(dev), kc, vc, k, v, pos, cbk, cbv, rot, rot)
+        torch.cuda.synchronize()
+        assert torch.equal(kc.packed.idx, kc2.packed.idx) and torch.equal(vc.packed.idx, vc2.packed.idx)
+        assert torch.equal(kc.packed.norms.nan_to_num(7.0), kc2.packed.norms.nan_to_num(7.0))
+        assert torch.equal(vc.packed.norms.nan_to_num(7.0), vc2.packed.norms.nan_to_num(7.0))
+        ref, vmax = _oracle_out(kc, vc, B, hkv, q, pos, n_new, kb, vb)
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got)), (pos, n_new)
+        for b in range(B):
+            for h in range(hq):
+                err = np.max(np.abs(got[b, h] - ref[b, h]))
+                assert err <= 1e-3 * vmax[b, h // ratio], (pos, n_new, b, h, err, vmax[b, h // ratio])
+
+
+@pytest.mark.parametrize("B,hkv,hq,kb,vb", [(1, 2, 8, 2, 2), (2, 1, 4, 4, 4), (1, 2, 4, 3, 2), (1, 1, 1, 4, 3),
+                                            (1, 1, 8, 2, 4)])
+def test_prefill_chunks_match_oracle(dev, rot, B, hkv, hq, kb, vb):
+    # a 45-token prompt, a 70-token chunk, a single token, then a 33-token chunk
+    _run(dev, rot, B, hkv, hq, 160, [(0, 45), (45, 70), (115, 1), (116, 33)], kb, vb, seed=kb * 10 + vb)
+
+
+def test_prefill_fp32_inputs_one_long_chunk(dev, rot):
+    _run(dev, rot, 1, 2, 4, 320, [(0, 300)], 3, 3, dtype=torch.float32, seed=3)
+
+
+def test_prefill_errors(dev, rot):
+    cb = tq.codebook(D, 2)
+    kc = tq.alloc_cache(1, 2, 64, D, 2, "mse", device=dev)
+    vc = tq.alloc_cache(1, 2, 64, D, 2, "mse", layout="blocked", device=dev)
+    k = torch.zeros((1, 2, 8, D), dtype=torch.bfloat16, device=dev)
+    q = torch.zeros((1, 8, 8, D), device=dev)
+    with pytest.raises(tq.TQError) as e:
+        tq.prefill_attn(q, kc, vc, k, k, 60, cb, cb, rot, rot)           # past the capacity
+    assert e.value.status == 1
+    with pytest.raises(tq.TQError) as e:
+        tq.prefill_attn(q, vc, kc, k, k, 0, cb, cb, rot, rot)            # caches swapped: layouts
+    assert e.value.status in (2, 3)
+    with pytest.raises(tq.TQError) as e:
+        tq.prefill_attn(torch.zeros((1, 5, 8, D), device=dev), kc, vc, k, k, 0, cb, cb, rot, rot)   # Hq % Hkv
+    assert e.value.status == 2
+    with pytest.raises(tq.TQError) as e:
+        tq.prefill_attn(q, kc, vc, k, k, 0, cb, cb, rot, rot, ws=torch.empty(16, dtype=torch.uint8, device=dev))
+    assert e.value.status == 4
