@@ -546,6 +546,36 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         res.update({"bits_outlier": bo, "bits_rest": br, "cache": [cfg.B, cfg.hkv, t_cap, cfg.d], "prefill_tokens": t0,
                     "prefill_ms": pre_ms, "step_ms": step_ms, "append_ms": app_ms,
                     "decode_scores_per_s": cfg.hq * t_cap / step_ms * 1e3})
+    elif name in ("prefill", "prefillb4"):
+        # Prefill fused with attention: a 16384-token prompt of one sequence (8 KV heads, 32 query
+        # heads, d = 128, bf16 K and V) appended to empty compressed caches (MSE, b = 2 or 4) in one
+        # chunk, and its causal attention over the packed caches.
+        b = 2 if name == "prefill" else 4
+        B, hkv, hq, T, d = 1, 8, 32, 16384, 128
+        rot = tq.make_rotation(d, 1)
+        cb = tq.codebook(d, b)
+        kc = tq.alloc_cache(B, hkv, T, d, b, "mse", device=dev)
+        vc = tq.alloc_cache(B, hkv, T, d, b, "mse", layout="blocked", device=dev)
+        k = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=0, outlier_seed=10, scale_seed=11).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        v = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=20, outlier_seed=21, scale_seed=None).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        q = torch.from_numpy(wl.gaussian((B, hq, T, d), 12)).to(dev)
+        out = torch.empty((B, hq, T, d), device=dev)
+        ws = torch.empty(tq.prefill_attn_workspace(B, hq, T, d), dtype=torch.uint8, device=dev)
+        pf_ms = _timed(lambda i: tq.prefill_attn(q, kc, vc, k, v, 0, cb, cb, rot, rot, out=out, ws=ws), steps, warmup)
+        app_ms = _timed(lambda i: tq.kv_append(kc, vc, k, v, 0, cb, cb, rot, rot), steps, warmup)
+        pairs = hq * T * (T + 1) / 2                       # visible (query, key) pairs, causal
+        alg = 4.0 * d * pairs                              # q.k and p.v per pair
+        # issued fp16 MFMA work: per 32-key step and 16 queries, 24 instructions for the scores (Khi Qhi,
+        # Klo Qhi, Khi Qlo) and 16 for P V (weights hi and lo), 16 x 16 x 32 x 2 flops each
+        steps32 = sum((16 * (t + 1) + 31) // 32 for t in range(T // 16))
+        issued = hq * steps32 * 40 * 16384.0
+        att_ms = pf_ms - app_ms
+        res.update({"bits": b, "prompt": [B, hkv, T, d], "query_heads": hq, "prefill_ms": pf_ms,
+                    "prefill_tokens_per_s": B * T / pf_ms * 1e3, "append_ms": app_ms,
+                    "attention_ms_est": att_ms, "alg_tflops": alg / att_ms / 1e9,
+                    "issued_f16_tflops": issued / att_ms / 1e9, "issued_frac_f16_peak": issued / att_ms / 1e9 / 2500.0})
     elif name == "peaks":
         # Achievable ceilings on this machine, from the library's own measurement kernels: a streaming
         # read and a streaming copy of 1 GiB (far larger than the last-level cache), swept over
@@ -724,7 +754,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
-                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode"],
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode",
+                                                        "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "
                          "per-kernel timings only")
     ap.add_argument("--copy-probe", action="store_true",
