@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 6
+#define TQ_ABI_VERSION 7
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -76,6 +76,7 @@ typedef struct tq_codebook_s* tq_codebook_t;
 typedef struct tq_rotation_s* tq_rotation_t;
 typedef struct tq_qjl_s* tq_qjl_t;
 typedef struct tq_split_s* tq_split_t;
+typedef struct tq_outlier8_s* tq_outlier8_t;
 
 /* A packed set of n encoded vectors, all buffers device memory owned by the caller.
  * Row r of idx holds the d indices of vector r as one LSB-first bit stream: coordinate i
@@ -387,6 +388,52 @@ tq_status tq_scores_split_cache(const float* q_dev, int B, int Hq, int Hkv, int6
                                 tq_codebook_t cb_o, tq_codebook_t cb_r, tq_rotation_t rot_o,
                                 tq_rotation_t rot_r, float* scores_dev, void* ws_dev, size_t ws_bytes,
                                 void* stream);
+
+/* ---- outlier channels at 8 bits (d = 128) --------------------------------------------
+ * [RQ] the asymmetric needs of K and V: one practice keeps a key's outlier channels at 8 bits
+ * and codes the other channels at 3.  The page fixes neither the outlier set nor the 8-bit
+ * format; this library's reading: per KV head the caller names n_o outlier channels (4, 8 or
+ * 16); a key's outlier channels become symmetric 8-bit integers with one scale per key,
+ * scale = max |x_c| / 127 over them and q_c = x_c / scale rounded to nearest even (fp32
+ * arithmetic; an all-zero outlier part gives scale 0 and q 0); the key with its outlier channels
+ * set to zero is coded by TurboQuant_mse at d = 128 exactly as tq_encode codes a whole key.  The
+ * reconstruction takes the rest channels from that code and x_c = scale * q_c on the outlier
+ * channels; 3 rest bits with 8 outliers is 3.5 bits per channel plus 64 bits of norms and scale. */
+
+/* Outlier sets of H KV heads: outliers_host [H, n_o] int32, each row n_o distinct channels in
+ * [0, 128), in any order.  The handle keeps, on the current device, each head's rest mask and
+ * its outlier channels in ascending order: slot k of a key's 8-bit part is the head's k-th
+ * smallest outlier channel.  d must be 128.  Errors: TQ_EINVAL (null pointers, H < 1, a repeated
+ * or out-of-range channel), TQ_EUNSUPPORTED (d != 128, n_o not 4, 8 or 16), TQ_EDEVICE. */
+tq_status tq_make_outlier8(int H, int d, int n_o, const int32_t* outliers_host, tq_outlier8_t* out);
+void tq_outlier8_free(tq_outlier8_t o);
+
+/* Encode of keys x_dev [B, H, T, 128] (dtype dt, 16-byte aligned) with the outlier sets `o`:
+ * rest receives the TurboQuant_mse code of every key with its outlier channels zeroed (ROWS
+ * layout, d = 128, bits = cb->b, n = B*H*T; norms = ||x_rest||), q8_dev [n, n_o] int8 the
+ * outlier values in slot order and scale_dev [n] fp32 their scales.  The rest code's index
+ * decisions follow tq_encode's.  Errors: TQ_EINVAL (null pointers, negative sizes, misaligned
+ * x), TQ_ESHAPE (o's head count != H, cb / rot / rest with d != 128, n or bits mismatch, rest in
+ * prod mode), TQ_EUNSUPPORTED (dtype, layout, n >= 2^31), TQ_EDEVICE. */
+tq_status tq_encode_outlier8(const void* x_dev, tq_dtype dt, int B, int H, int64_t T, tq_outlier8_t o,
+                             tq_codebook_t cb, tq_rotation_t rot, tq_packed* rest, int8_t* q8_dev,
+                             float* scale_dev, void* stream);
+
+/* Workspace bytes of tq_scores_outlier8: the score prologue of tq_scores plus the queries'
+ * outlier components, B*Hq*16 fp32. */
+size_t tq_scores_outlier8_workspace(int B, int Hq);
+/* Raw scores <q, x_hat> of queries q_dev [B, Hq, 128] fp32 against outlier-8 keys (rest, q8_dev,
+ * scale_dev as written by tq_encode_outlier8 for [B, Hkv, T]) into scores_dev [B, Hq, T] fp32:
+ * s <R q_rest, C[idx]> + scale <q_O, q8>, with q_rest the query restricted to the rest channels
+ * and q_O its outlier components, both taken through the outlier set of the query head's KV head
+ * h // (Hq / Hkv) ([SB] fused score kernel and GQA mapping).  The first term runs on the same
+ * fp16 matrix-core path as tq_scores, the second in fp32.  Errors: as tq_encode_outlier8 for the
+ * keys and handles; TQ_ESHAPE (Hq not a positive multiple of Hkv); TQ_EUNSUPPORTED (GQA ratio as
+ * tq_scores); TQ_ENOMEM (workspace). */
+tq_status tq_scores_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_outlier8_t o,
+                             const tq_packed* rest, const int8_t* q8_dev, const float* scale_dev,
+                             tq_codebook_t cb, tq_rotation_t rot, float* scores_dev, void* ws_dev,
+                             size_t ws_bytes, void* stream);
 
 /* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
  * with k results per query (query operands, one chunk of scores, the running top-k). */

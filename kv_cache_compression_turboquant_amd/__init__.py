@@ -23,6 +23,7 @@ __all__ = [
     "prefill_attn", "prefill_attn_workspace",
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
     "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
+    "Outlier8", "make_outlier8", "encode_outlier8", "scores_outlier8", "scores_outlier8_workspace",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -507,6 +508,76 @@ def scores_split(q, K, Hkv, split, cb_o, cb_r, rot_o, rot_r, out=None, ws=None):
     check(lib().tq_scores_split(_dptr(q), B, Hq, Hkv, T, split.ptr, ctypes.byref(do), ctypes.byref(dr), cb_o.ptr,
                                 cb_r.ptr, rot_o.ptr, rot_r.ptr, _dptr(out), _dptr(ws),
                                 ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+class Outlier8(_Handle):
+    """Per-KV-head outlier channels of d = 128 keys kept at 8 bits (4, 8 or 16 per head)."""
+    _free = "tq_outlier8_free"
+
+    def __init__(self, ptr, outliers):
+        super().__init__(ptr)
+        self.outliers = outliers
+        self.H, self.n_o = outliers.shape
+
+
+def make_outlier8(outliers):
+    """outliers: [H, n_o] integer channels (distinct per row, in [0, 128); n_o 4, 8 or 16).  Slot k
+    of a key's 8-bit part is the head's k-th smallest outlier channel."""
+    o = np.ascontiguousarray(np.asarray(outliers), dtype=np.int32)
+    if o.ndim != 2:
+        raise TQError(1, "outliers must be [H, n_o]")
+    h = ctypes.c_void_p()
+    check(lib().tq_make_outlier8(o.shape[0], 128, o.shape[1], _np(o), ctypes.byref(h)))
+    return Outlier8(h.value, np.sort(o, axis=1))
+
+
+def encode_outlier8(x, o, cb, rot, out=None):
+    """Outlier-8 encode of keys x [B, H, T, 128] (bf16 or fp32): (rest, q8, scale) with rest a
+    rows-layout MSE Packed (d = 128, n = B*H*T), q8 int8 [n, n_o] and scale fp32 [n]."""
+    torch = _torch()
+    _check_split_keys_x("encode_outlier8", x)
+    B, H, T, _ = x.shape
+    n = B * H * T
+    if out is None:
+        out = (alloc_packed(n, 128, cb.b, "mse", device=x.device),
+               torch.empty((n, o.n_o), dtype=torch.int8, device=x.device),
+               torch.empty((n,), dtype=torch.float32, device=x.device))
+    rest, q8, scale = out
+    if q8.dtype != torch.int8 or not q8.is_contiguous() or q8.numel() != n * o.n_o:
+        raise TQError(1, f"encode_outlier8: q8 must be contiguous int8 with {n * o.n_o} elements")
+    _check_scores_out("encode_outlier8", scale, n)
+    _same_device("encode_outlier8", x, rest.idx, rest.norms, q8, scale)
+    d = rest.descriptor()
+    check(lib().tq_encode_outlier8(_dptr(x), _dtype_code(x), B, H, T, o.ptr, cb.ptr, rot.ptr, ctypes.byref(d),
+                                   _dptr(q8), _dptr(scale), _stream()))
+    return out
+
+
+def scores_outlier8_workspace(B, Hq):
+    return int(lib().tq_scores_outlier8_workspace(B, Hq))
+
+
+def scores_outlier8(q, K, Hkv, o, cb, rot, out=None, ws=None):
+    """Raw scores [B, Hq, T] of q [B, Hq, 128] fp32 against outlier-8 keys K = (rest, q8, scale)
+    of keys [B, Hkv, T]."""
+    torch = _torch()
+    _check_split_q("scores_outlier8", q)
+    rest, q8, scale = K
+    B, Hq, _ = q.shape
+    T = rest.n // max(B * Hkv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check_scores_out("scores_outlier8", out, B * Hq * T)
+    if q8.dtype != torch.int8 or not q8.is_contiguous() or q8.numel() != rest.n * o.n_o:
+        raise TQError(1, f"scores_outlier8: q8 must be contiguous int8 with {rest.n * o.n_o} elements")
+    _check_scores_out("scores_outlier8", scale, rest.n)
+    if ws is None:
+        ws = torch.empty((max(scores_outlier8_workspace(B, Hq), 1),), dtype=torch.uint8, device=q.device)
+    _same_device("scores_outlier8", q, out, ws, rest.idx, rest.norms, q8, scale)
+    d = rest.descriptor()
+    check(lib().tq_scores_outlier8(_dptr(q), B, Hq, Hkv, T, o.ptr, ctypes.byref(d), _dptr(q8), _dptr(scale), cb.ptr,
+                                   rot.ptr, _dptr(out), _dptr(ws), ws.numel() * ws.element_size(), _stream()))
     return out
 
 

@@ -104,6 +104,12 @@ SIGNATURES = {
                                    ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tq_scores_split": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed), _P, _P,
                              _P, _P, _P, _P, _SZ, _P]),
+    "tq_make_outlier8": (_I, [_I, _I, _I, _P, ctypes.POINTER(_P)]),
+    "tq_outlier8_free": (None, [_P]),
+    "tq_encode_outlier8": (_I, [_P, _I, _I, _I, _I64, _P, _P, _P, ctypes.POINTER(tq_packed), _P, _P, _P]),
+    "tq_scores_outlier8_workspace": (_SZ, [_I, _I]),
+    "tq_scores_outlier8": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _P, _SZ,
+                                _P]),
 }
 
 _lib = None

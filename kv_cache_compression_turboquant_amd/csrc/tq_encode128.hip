@@ -398,10 +398,121 @@ __device__ __forceinline__ void for_blocks_down(F&& f) {
 
 constexpr int kMseWaves = 4;
 
-template <int BITS, bool BF16IN, int RP, int NT>
+// ---------------------------------------------------------------------------------------
+// Outlier-8 keys: the rest channels go through the MSE encode below with the outlier channels
+// zeroed, and the outlier channels become symmetric 8-bit integers with one absmax scale per
+// key.  Lane (n, G) holds channels 32 G .. 32 G + 31 of its row, so it takes bits of word G of
+// the head's rest mask, and slots NO/4 G .. NO/4 G + NO/4 - 1 of the head's outlier list, which
+// it gathers from x (the row was just read, so these loads hit in cache).
+// ---------------------------------------------------------------------------------------
+struct OTile {
+  uint32_t m;   // rest-mask word of the lane's channels
+  uint32_t c;   // the word of the outlier list holding the lane's slots
+};
+
+template <int NO>
+__device__ __forceinline__ void load_otile(const OutlierArgs& oa, int64_t n, int64_t tile, int nl, int g, OTile& o) {
+  if constexpr (NO > 0) {
+    const int64_t row = tile * 16 + nl;
+    const uint32_t lrow = (uint32_t)(row < n ? row : n - 1);   // the host bounds n below 2^31
+    const uint32_t h = (lrow / oa.T) % oa.H;
+    o.m = oa.mask[h * 4 + g];
+    o.c = oa.chan[h * 4 + ((g * (NO / 4)) >> 2)];
+  }
+}
+
+__device__ __forceinline__ uint32_t bit_ext(uint32_t m, int p) {   // 0 or 0xffffffff
+  return (uint32_t)((int32_t)(m << (31 - p)) >> 31);
+}
+
+template <bool BF16IN>
+__device__ __forceinline__ void apply_rest_mask(RawTile<BF16IN>& r, uint32_t m) {
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = 8 * s + 2 * j;
+        // bytes 0-1 from the low channel's mask, bytes 2-3 from the high one's
+        r.v[s][j] &= __builtin_amdgcn_perm(bit_ext(m, p + 1), bit_ext(m, p), 0x07060100u);
+      }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        r.v[s][k] = __uint_as_float(__float_as_uint(r.v[s][k]) & bit_ext(m, 4 * s + k));
+  }
+}
+
+template <int NO>
+struct OVals {
+  float v[NO > 0 ? NO / 4 : 1];
+};
+
+// The lane's outlier values of tile `tile` (rows past the end read the last row).
+template <int NO, bool BF16IN>
+__device__ __forceinline__ void gather_outliers(const void* x, int64_t n, int64_t tile, int nl, int g, const OTile& o,
+                                                OVals<NO>& ov) {
+  if constexpr (NO > 0) {
+    constexpr int NS = NO / 4;
+    const int64_t row = tile * 16 + nl;
+    const int64_t lrow = row < n ? row : n - 1;
+    const int b0 = (g * NS) & 3;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint32_t c = (o.c >> (8 * (b0 + i))) & 0xffu;
+      if constexpr (BF16IN) {
+        const uint16_t u = static_cast<const uint16_t*>(x)[lrow * 128 + c];
+        ov.v[i] = __uint_as_float((uint32_t)u << 16);
+      } else {
+        ov.v[i] = static_cast<const float*>(x)[lrow * 128 + c];
+      }
+    }
+  }
+}
+
+// scale = max |x_c| / 127 over the row's outlier channels (the four lanes of the row meet by
+// shuffles), q_c = x_c / scale rounded to nearest even; stores the lane's NO/4 bytes and, from
+// lane group 0, the scale.
+template <int NO>
+__device__ __forceinline__ void store_outliers(const OutlierArgs& oa, int64_t n, int64_t tile, int nl, int g,
+                                               const OVals<NO>& ov) {
+  if constexpr (NO > 0) {
+    constexpr int NS = NO / 4;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) a = fmaxf(a, fabsf(ov.v[i]));
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    const float sc = a / 127.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      float qv = sc > 0.f ? rintf(ov.v[i] / sc) : 0.f;
+      qv = fminf(fmaxf(qv, -127.f), 127.f);
+      packed |= ((uint32_t)(int32_t)qv & 0xffu) << (8 * i);
+    }
+    const int64_t row = tile * 16 + nl;
+    if (row < n) {
+      int8_t* dst = oa.q8 + row * NO + NS * g;
+      if constexpr (NS == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+      } else if constexpr (NS == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+      } else {
+        *dst = (int8_t)packed;
+      }
+      if (g == 0) oa.scale[row] = sc;
+    }
+  }
+}
+
+// NO > 0: outlier-8 keys (NO outlier channels per head, described by oa).
+template <int BITS, bool BF16IN, int RP, int NT, int NO>
 __global__ __launch_bounds__(kMseWaves * 64, 2) void k_encode_mse_d128(
     const void* __restrict__ x, int64_t n, const u32x4* __restrict__ frag_r, float post_scale,
-    CodebookArgs cb, uint32_t* __restrict__ idx_out, float* __restrict__ norms_out) {
+    CodebookArgs cb, uint32_t* __restrict__ idx_out, float* __restrict__ norms_out, OutlierArgs oa) {
   constexpr int H = 1 << (BITS - 1);
   constexpr int kThreads = kMseWaves * 64;
   constexpr int kStage = RP * kFragU4 / kThreads;
@@ -424,8 +535,11 @@ __global__ __launch_bounds__(kMseWaves * 64, 2) void k_encode_mse_d128(
 #pragma unroll
   for (int j = 0; j < kStage; ++j) stage[j] = frag_r[threadIdx.x + ((j + rot0) % kStage) * kThreads];
   RawTile<BF16IN> bufA[NT], bufB[NT];
+  OTile oA[NT], oB[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) load_tile<BF16IN>(x, n, tw + t, nl, g, bufA[t]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_otile<NO>(oa, n, tw + t, nl, g, oA[t]);
 #pragma unroll
   for (int j = 0; j < kStage; ++j) lds[threadIdx.x + ((j + rot0) % kStage) * kThreads] = stage[j];
   __syncthreads();
@@ -435,13 +549,24 @@ __global__ __launch_bounds__(kMseWaves * 64, 2) void k_encode_mse_d128(
   constexpr int NV = BF16IN ? 4 : 8;
   constexpr int LPB = (NT * NV + 7) / 8;
   using Elem = typename std::conditional<BF16IN, u32x4, f32x4>::type;
-  auto step = [&](RawTile<BF16IN> (&cur)[NT], RawTile<BF16IN> (&nxt)[NT], const int64_t t0) {
+  auto step = [&](RawTile<BF16IN> (&cur)[NT], RawTile<BF16IN> (&nxt)[NT], const OTile (&ocur)[NT], OTile (&onxt)[NT],
+                  const int64_t t0) {
     const Elem* nsrc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t row = (t0 + stride + t) * 16 + nl;
       const int64_t lrow = row < n ? row : n - 1;   // clamped: past the end reads the last row
       nsrc[t] = reinterpret_cast<const Elem*>(static_cast<const char*>(x) + (lrow * 128 + 32 * g) * (BF16IN ? 2 : 4));
+    }
+    OVals<NO> ov[NT];
+    if constexpr (NO > 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        apply_rest_mask<BF16IN>(cur[t], ocur[t].m);
+        gather_outliers<NO, BF16IN>(x, n, t0 + t, nl, g, ocur[t], ov[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load_otile<NO>(oa, n, t0 + stride + t, nl, g, onxt[t]);
     }
     // B operands: bf16 input is used in place; fp32 input is split into bf16 hi + lo.
     u32x4 bxh[BF16IN ? 1 : NT][4], bxl[BF16IN ? 1 : NT][4];
@@ -547,21 +672,25 @@ __global__ __launch_bounds__(kMseWaves * 64, 2) void k_encode_mse_d128(
         for (int j = 0; j < BITS; ++j) dst[j] = w[t][j];
       }
     }
+    if constexpr (NO > 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) store_outliers<NO>(oa, n, t0 + t, nl, g, ov[t]);
+    }
   };
   // Entered unconditionally (an early exit would let the compiler sink the tile loads past the
   // barrier); a wave without a tile of its own stores nothing, since every store checks its row.
   for (;;) {
-    step(bufA, bufB, tw);
+    step(bufA, bufB, oA, oB, tw);
     if (tw + stride >= ntiles) break;
-    step(bufB, bufA, tw + stride);
+    step(bufB, bufA, oB, oA, tw + stride);
     tw += 2 * stride;
     if (tw >= ntiles) break;
   }
 }
 
-template <int BITS, bool BF16IN, int RP>
+template <int BITS, bool BF16IN, int RP, int NO = 0>
 hipError_t mse_launch(const void* x, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
-                      uint32_t* idx, float* norms, hipStream_t st) {
+                      uint32_t* idx, float* norms, hipStream_t st, const OutlierArgs& oa = OutlierArgs{}) {
   constexpr int NT = BF16IN ? 2 : 1;
   const int64_t ntiles = (n + 15) / 16;
   const int64_t per_block = (int64_t)kMseWaves * NT;
@@ -571,14 +700,36 @@ hipError_t mse_launch(const void* x, int64_t n, const tq_rotation_s* rot, const 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (take_armed_timer(&ev0, &ev1)) {
     // events attached to the dispatch itself: they bracket the kernel's execution alone
-    hipExtLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
-                          st, ev0, ev1, 0, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb,
-                          idx, norms);
+    hipExtLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT, NO>), dim3((unsigned)blocks), dim3(kMseWaves * 64),
+                          0, st, ev0, ev1, 0, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb,
+                          idx, norms, oa);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
-                     st, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb, idx, norms);
+  hipLaunchKernelGGL((k_encode_mse_d128<BITS, BF16IN, RP, NT, NO>), dim3((unsigned)blocks), dim3(kMseWaves * 64), 0,
+                     st, x, n, reinterpret_cast<const u32x4*>(rot->frag_dev), rot->post_scale, cb, idx, norms, oa);
   return hipGetLastError();
+}
+
+template <int BITS, int NO>
+hipError_t outlier8_dispatch(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                             const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st) {
+  if (bf16)
+    return rot->passes == 1 ? mse_launch<BITS, true, 1, NO>(x, n, rot, cb, idx, norms, st, oa)
+                            : mse_launch<BITS, true, 2, NO>(x, n, rot, cb, idx, norms, st, oa);
+  return rot->passes == 1 ? mse_launch<BITS, false, 1, NO>(x, n, rot, cb, idx, norms, st, oa)
+                          : mse_launch<BITS, false, 2, NO>(x, n, rot, cb, idx, norms, st, oa);
+}
+
+template <int NO>
+hipError_t outlier8_bits(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                         const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st) {
+  switch (cb.bits) {
+    case 1: return outlier8_dispatch<1, NO>(x, bf16, n, rot, cb, oa, idx, norms, st);
+    case 2: return outlier8_dispatch<2, NO>(x, bf16, n, rot, cb, oa, idx, norms, st);
+    case 3: return outlier8_dispatch<3, NO>(x, bf16, n, rot, cb, oa, idx, norms, st);
+    case 4: return outlier8_dispatch<4, NO>(x, bf16, n, rot, cb, oa, idx, norms, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int BITS>
@@ -635,6 +786,16 @@ hipError_t enc_dispatch_in(const void* x, bool bf16, int64_t n, const tq_rotatio
 }
 
 }  // namespace
+
+hipError_t launch_encode_outlier8(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                                  const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st) {
+  switch (oa.no) {
+    case 4: return outlier8_bits<4>(x, bf16, n, rot, cb, oa, idx, norms, st);
+    case 8: return outlier8_bits<8>(x, bf16, n, rot, cb, oa, idx, norms, st);
+    case 16: return outlier8_bits<16>(x, bf16, n, rot, cb, oa, idx, norms, st);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                               const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx,

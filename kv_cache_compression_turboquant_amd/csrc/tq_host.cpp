@@ -1386,3 +1386,137 @@ tq_status tq_search_topk(const float* q_dev, int64_t nq, const tq_packed* db, tq
                                              as_stream(stream)),
                       fn);
 }
+
+// ---- outlier channels at 8 bits (d = 128) -------------------------------------------------
+
+struct tq_outlier8_s {
+  int H;
+  int no;
+  int device;
+  std::vector<uint32_t> table;    // [H][8]: rest-mask words 0..3, then the sorted channels as bytes
+  uint32_t* table_dev = nullptr;  // mask at [H][4], channels at H * 4 + [H][4]
+};
+
+tq_status tq_make_outlier8(int H, int d, int n_o, const int32_t* outliers_host, tq_outlier8_t* out) {
+  static const char* fn = "tq_make_outlier8";
+  if (!out || !outliers_host || H < 1) return fail(TQ_EINVAL, "%s: bad arguments", fn);
+  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if (n_o != 4 && n_o != 8 && n_o != 16) return fail(TQ_EUNSUPPORTED, "%s: n_o=%d (4, 8 or 16)", fn, n_o);
+  std::vector<uint32_t> table((size_t)H * 8, 0u);
+  for (int h = 0; h < H; ++h) {
+    bool seen[tq::kFragD] = {};
+    for (int i = 0; i < n_o; ++i) {
+      const int32_t c = outliers_host[(size_t)h * n_o + i];
+      if (c < 0 || c >= tq::kFragD || seen[c])
+        return fail(TQ_EINVAL, "%s: head %d: channel %d repeated or outside [0, 128)", fn, h, (int)c);
+      seen[c] = true;
+    }
+    uint32_t* mask = &table[(size_t)h * 4];
+    uint32_t* chan = &table[(size_t)H * 4 + (size_t)h * 4];
+    int k = 0;
+    for (int c = 0; c < tq::kFragD; ++c) {
+      if (seen[c]) {
+        chan[k >> 2] |= (uint32_t)c << (8 * (k & 3));
+        ++k;
+      } else {
+        mask[c >> 5] |= 1u << (c & 31);
+      }
+    }
+  }
+  auto* o = new (std::nothrow) tq_outlier8_s();
+  if (!o) return fail(TQ_ENOMEM, "host allocation failed");
+  o->H = H;
+  o->no = n_o;
+  hipGetDevice(&o->device);
+  o->table = std::move(table);
+  tq_status st = upload(o->table, &o->table_dev, "upload outlier sets");
+  if (st != TQ_OK) {
+    delete o;
+    return st;
+  }
+  *out = o;
+  return ok();
+}
+
+void tq_outlier8_free(tq_outlier8_t o) {
+  if (!o) return;
+  if (o->table_dev) hipFree(o->table_dev);
+  delete o;
+}
+
+static tq::OutlierArgs outlier8_args(tq_outlier8_t o, int64_t rows_per_seq) {
+  tq::OutlierArgs a;
+  a.mask = o->table_dev;
+  a.chan = o->table_dev + (size_t)o->H * 4;
+  a.T = (uint32_t)rows_per_seq;
+  a.H = (uint32_t)o->H;
+  a.no = o->no;
+  return a;
+}
+
+// Handles and the packed rest code of outlier-8 keys: B * H sequences of `rows` rows each.
+static tq_status check_outlier8_keys(int B, int H, int64_t rows, tq_outlier8_t o, tq_codebook_t cb,
+                                     tq_rotation_t rot, const tq_packed* rest, const char* fn) {
+  if (!o || !cb || !rot || !rest) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || H < 0 || rows < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (o->H != H) return fail(TQ_ESHAPE, "%s: outlier sets of %d heads, keys have %d", fn, o->H, H);
+  if (cb->d != tq::kFragD || rot->d != tq::kFragD) return fail(TQ_ESHAPE, "%s: codebook and rotation need d=128", fn);
+  tq_status st = check_packed(rest, tq::kFragD, cb->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  if (rest->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: the rest code uses the ROWS layout", fn);
+  const int64_t n = (int64_t)B * H * rows;
+  if (n >= (int64_t(1) << 31)) return fail(TQ_EUNSUPPORTED, "%s: %lld keys, at most 2^31 - 1", fn, (long long)n);
+  if (rest->n != n)
+    return fail(TQ_ESHAPE, "%s: rest n=%lld but B*H*%lld=%lld", fn, (long long)rest->n, (long long)rows, (long long)n);
+  return TQ_OK;
+}
+
+tq_status tq_encode_outlier8(const void* x_dev, tq_dtype dt, int B, int H, int64_t T, tq_outlier8_t o,
+                             tq_codebook_t cb, tq_rotation_t rot, tq_packed* rest, int8_t* q8_dev, float* scale_dev,
+                             void* stream) {
+  static const char* fn = "tq_encode_outlier8";
+  tq_status st = check_outlier8_keys(B, H, T, o, cb, rot, rest, fn);
+  if (st != TQ_OK) return st;
+  if (dt != TQ_BF16 && dt != TQ_F32) return fail(TQ_EUNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the encode kernels need an antisymmetric codebook", fn);
+  const int64_t n = (int64_t)B * H * T;
+  if (n == 0) return ok();
+  if (!x_dev || !q8_dev || !scale_dev) return fail(TQ_EINVAL, "%s: null x, q8 or scale", fn);
+  if (reinterpret_cast<uintptr_t>(x_dev) % 16 != 0 || reinterpret_cast<uintptr_t>(q8_dev) % 16 != 0)
+    return fail(TQ_EINVAL, "%s: x and q8 must be 16-byte aligned", fn);
+  tq::OutlierArgs a = outlier8_args(o, T);
+  a.q8 = q8_dev;
+  a.scale = scale_dev;
+  return check_launch(tq::launch_encode_outlier8(x_dev, dt == TQ_BF16, n, rot, cb->args, a, rest->idx, rest->norms,
+                                                 as_stream(stream)),
+                      fn);
+}
+
+size_t tq_scores_outlier8_workspace(int B, int Hq) {
+  if (B < 0 || Hq < 0) return 0;
+  return tq::scores_outlier8_workspace_bytes(B, Hq);
+}
+
+tq_status tq_scores_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_outlier8_t o,
+                             const tq_packed* rest, const int8_t* q8_dev, const float* scale_dev, tq_codebook_t cb,
+                             tq_rotation_t rot, float* scores_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_scores_outlier8";
+  tq_status st = check_score_heads(B, Hq, Hkv, fn);
+  if (st != TQ_OK) return st;
+  st = check_outlier8_keys(B, Hkv, T, o, cb, rot, rest, fn);
+  if (st != TQ_OK) return st;
+  if (T > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: T=%lld exceeds %lld tokens per sequence", fn, (long long)T,
+                (long long)kMaxSeqTokens);
+  if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
+    return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
+                (long long)(Hq / Hkv) * T);
+  if ((int64_t)B * Hq * T == 0) return ok();
+  if (!q_dev || !scores_dev || !q8_dev || !scale_dev) return fail(TQ_EINVAL, "%s: null q, scores, q8 or scale", fn);
+  if (reinterpret_cast<uintptr_t>(q8_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: q8 must be 16-byte aligned", fn);
+  const size_t need = tq::scores_outlier8_workspace_bytes(B, Hq);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_scores_outlier8(q_dev, B, Hq, Hkv, T, T, rest, q8_dev, scale_dev, cb->args, rot,
+                                                 outlier8_args(o, T), scores_dev, ws_dev, as_stream(stream)),
+                      fn);
+}

@@ -155,9 +155,37 @@ hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, c
                               int64_t* top_i, void* ws, hipStream_t st);
 constexpr int kSearchMaxK = 32;
 
+// Keys whose outlier channels are kept as 8-bit integers (d = 128): per KV head a rest mask (bit
+// c % 32 of word c / 32 set for a channel coded by TurboQuant_mse) and the head's NO outlier
+// channels in ascending order, one per byte (word k holds channels 4 k .. 4 k + 3).
+struct OutlierArgs {
+  const uint32_t* mask = nullptr;   // [H][4]
+  const uint32_t* chan = nullptr;   // [H][4]
+  int8_t* q8 = nullptr;             // [n][NO] encode output
+  float* scale = nullptr;           // [n] encode output
+  uint32_t T = 1;                   // rows per sequence: row r belongs to KV head (r / T) % H
+  uint32_t H = 1;
+  int no = 0;                       // outlier channels per head: 4, 8 or 16
+};
+constexpr int kOutlierMaxChannels = 16;
+
 // q_rot (and, with st_mat, the QJL sketch in sign-slot order plus the per-head constant) of
-// every query head, d = 128, into the score workspace layout.
+// every query head, d = 128, into the score workspace layout.  With oa.mask set, the query is
+// restricted to the rest channels of its KV head first, and its outlier components (fp32, in
+// the head's channel order) go to qo [B * Hq][16].
 hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,
-                           uint16_t* qws, float* kconst, hipStream_t st);
+                           uint16_t* qws, float* kconst, hipStream_t st, const OutlierArgs* oa = nullptr,
+                           float* qo = nullptr);
+
+// Outlier-8 keys (tq_encode128.hip, tq_score128.hip): x [n, 128] with n = sequences * oa.T, the
+// rest channels TurboQuant_mse at cb.bits into idx / norms, the outlier channels into oa.q8 /
+// oa.scale.  Scores: the score workspace followed by qo.
+hipError_t launch_encode_outlier8(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
+                                  const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st);
+size_t scores_outlier8_workspace_bytes(int B, int Hq);
+hipError_t launch_scores_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+                                  const tq_packed* K, const int8_t* q8, const float* oscale, const CodebookArgs& cb,
+                                  const tq_rotation_s* rot, const OutlierArgs& oa, float* scores, void* ws,
+                                  hipStream_t st);
 
 }  // namespace tq

@@ -66,7 +66,10 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
                                                             const float* __restrict__ rt,
                                                             const float* __restrict__ st,
                                                             uint16_t* __restrict__ ws,
-                                                            float* __restrict__ kconst) {
+                                                            float* __restrict__ kconst,
+                                                            const uint32_t* __restrict__ omask,
+                                                            const uint32_t* __restrict__ ochan, int no,
+                                                            float* __restrict__ qo) {
   constexpr int HG = kQprepHeads;
   constexpr int KP = 128 / kQprepParts;
   __shared__ float qs[HG][128];
@@ -94,7 +97,19 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
     __syncthreads();
     if (threadIdx.x < HG * 128) {
       const int hh = threadIdx.x >> 7;
-      qs[hh][j] = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
+      float v = hh < nh ? q[((int64_t)b * Hq + h0 + hc + hh) * 128 + j] : 0.f;
+      // outlier-8 keys: the rotated query sees only the rest channels of the KV head
+      if (omask && !((omask[kvh * 4 + (j >> 5)] >> (j & 31)) & 1u)) v = 0.f;
+      qs[hh][j] = v;
+    } else if (omask && threadIdx.x < HG * 128 + HG * kOutlierMaxChannels) {
+      // ... and the outlier components go to qo in the head's channel order
+      const int u = threadIdx.x - HG * 128;
+      const int hh = u / kOutlierMaxChannels, k = u % kOutlierMaxChannels;
+      if (hh < nh && k < no) {
+        const int c = (int)((ochan[kvh * 4 + (k >> 2)] >> (8 * (k & 3))) & 0xffu);
+        const int64_t hrow = (int64_t)b * Hq + h0 + hc + hh;
+        qo[hrow * kOutlierMaxChannels + k] = q[hrow * 128 + c];
+      }
     }
     __syncthreads();
     float ar[HG], as[HG];
@@ -184,26 +199,33 @@ constexpr int kScoreWaves = 4;
 constexpr int kScoreBatch = TQ_SCORE_BATCH;   // key tiles loaded before any of them is scored
 constexpr int kScoreRounds = TQ_SCORE_ROUNDS; // target grid = this many rounds of resident blocks
 
-template <int BITS, bool PROD>
+template <int BITS, bool PROD, int NO = 0>
 struct KeyTile {
   uint32_t w[BITS];
   float nrm;
   uint32_t zw;
   float gam;
+  uint32_t o8[NO > 0 ? NO / 4 : 1];   // outlier-8 keys: the key's NO int8 values
+  float osc;                          // and their scale
 };
 
 // The sequence's packed keys as buffer resources: each load is the resource plus one 32-bit
 // per-lane offset, and tokens past T read as zero (their scores are never stored).
 template <bool PROD>
 struct KeyBufs {
-  __amdgpu_buffer_rsrc_t idx, norms, qbits, rnorms;
+  __amdgpu_buffer_rsrc_t idx, norms, qbits, rnorms, q8, osc;
 };
 
 // Lane (n, g) share of key tile `tile` of one sequence: its BITS words (coordinates 32 g ..),
 // norm, and for prod its sign word and scaled residual norm.
-template <int BITS, bool PROD>
-__device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile, int nl, int g, KeyTile<BITS, PROD>& k) {
+template <int BITS, bool PROD, int NO>
+__device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile, int nl, int g,
+                                              KeyTile<BITS, PROD, NO>& k) {
   const uint32_t t = (uint32_t)tile * 16u + (uint32_t)nl;
+  if constexpr (NO > 0) {
+    buffer_words<NO / 4>(kb.q8, t * (uint32_t)NO, k.o8);
+    k.osc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.osc, t * 4u, 0, 0));
+  }
   buffer_words<BITS>(kb.idx, t * (16u * BITS) + (uint32_t)(4 * BITS * g), k.w);
   k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.norms, t * 4u, 0, 0));
   if constexpr (PROD) {
@@ -216,14 +238,16 @@ __device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile,
 }
 
 // MULTI: GQA ratio above 4, so each key is scored for several groups of 4 heads; otherwise the
-// kernel carries only the single-group path.
-template <int BITS, bool PROD, bool MULTI>
+// kernel carries only the single-group path.  NO > 0: outlier-8 keys, whose score adds
+// scale * <q_O, q8> (fp32, on the vector ALUs) to the rest channels' term; qo holds q_O.
+template <int BITS, bool PROD, bool MULTI, int NO>
 __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int64_t seq_stride,
     int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
     const uint32_t* __restrict__ qbits, const float* __restrict__ rnorms, CodebookArgs cb,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, const int8_t* __restrict__ q8, const float* __restrict__ oscale,
+    const float* __restrict__ qo) {
   constexpr int TC = table_copies<BITS, false, 32768>();
   using DT = DecodeTable<BITS, false, TC>;
   __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
@@ -255,6 +279,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     kb.qbits = buffer_rsrc(qbits + base_row * 4, (uint32_t)T * 16u);
     kb.rnorms = buffer_rsrc(rnorms + base_row, (uint32_t)T * 4u);
   }
+  if constexpr (NO > 0) {
+    kb.q8 = buffer_rsrc(q8 + base_row * NO, (uint32_t)T * (uint32_t)NO);
+    kb.osc = buffer_rsrc(oscale + base_row, (uint32_t)T * 4u);
+  }
   const int64_t tile0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t ntiles_seq = (T + 15) / 16;
 
@@ -284,10 +312,21 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     return (PROD && h < ratio) ? kconst[(int64_t)b * Hq + kvh * ratio + h] : 0.f;
   };
   const float kc0 = load_kc(0);
+  // q_O of the lane's head (4 hg + g), outlier-8 keys only
+  auto load_qo = [&](int hg, float (&v)[NO > 0 ? NO : 1]) {
+    const int h = 4 * hg + g;
+    const float* src = qo + ((int64_t)b * Hq + kvh * ratio + (h < ratio ? h : 0)) * kOutlierMaxChannels;
+#pragma unroll
+    for (int k = 0; k < (NO > 0 ? NO : 1); ++k) v[k] = NO > 0 ? src[k] : 0.f;
+  };
+  // (kept in registers for a single head group only: with several groups the registers of a
+  // batch of key tiles are needed for the keys)
+  float qo0[NO > 0 && !MULTI ? NO : 1];
+  if constexpr (NO > 0 && !MULTI) load_qo(0, qo0);
 
   // Ping-pong over two tile buffers (no register copies), so the next tile's loads stay in flight
   // while the current one is scored and the wait before scoring counts only the older loads.
-  auto score_tile = [&](const KeyTile<BITS, PROD>& cur, int64_t ti) {
+  auto score_tile = [&](const KeyTile<BITS, PROD, NO>& cur, int64_t ti) {
     const int64_t tile = tile0 + ti;
     const int64_t t = tile * 16 + nl;
     const bool valid = t < T;
@@ -297,6 +336,11 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
 #pragma unroll
     for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS, TC>(cur.w, s, tabl);
     if constexpr (PROD) sign_operand(cur.zw, bz);
+    float o8f[NO > 0 ? NO : 1];
+    if constexpr (NO > 0) {
+#pragma unroll
+      for (int k = 0; k < NO; ++k) o8f[k] = (float)((int32_t)(cur.o8[k >> 2] << (24 - 8 * (k & 3))) >> 24);
+    }
     for (int hg = 0; hg < groups; ++hg) {
       u32x4 a[4];
       if (!MULTI || hg == 0) {
@@ -320,6 +364,19 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
       float mine = reduce_parts(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
       const int h = 4 * hg + g;
       if constexpr (PROD) mine -= gam * (hg == 0 ? kc0 : load_kc(hg));
+      if constexpr (NO > 0) {
+        float qv[NO];
+        if constexpr (!MULTI) {
+#pragma unroll
+          for (int k = 0; k < NO; ++k) qv[k] = qo0[k];
+        } else {
+          load_qo(hg, qv);
+        }
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < NO; ++k) o = fmaf(o8f[k], qv[k], o);
+        mine = fmaf(cur.osc, o, mine);
+      }
       if (valid && h < ratio)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), sbuf,
                                               ((uint32_t)h * (uint32_t)T + (uint32_t)t) * 4u, 0, 0);
@@ -330,10 +387,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   int64_t last = tiles_per_wave;
   if (ntiles_seq - tile0 < last) last = ntiles_seq - tile0;
   for (int64_t tb = 0; tb < last; tb += kScoreBatch) {
-    KeyTile<BITS, PROD> kt[kScoreBatch];
+    KeyTile<BITS, PROD, NO> kt[kScoreBatch];
 #pragma unroll
     for (int u = 0; u < kScoreBatch; ++u)
-      load_key_tile<BITS, PROD>(kb, (int)(tile0 + tb + u), nl, g, kt[u]);
+      load_key_tile<BITS, PROD, NO>(kb, (int)(tile0 + tb + u), nl, g, kt[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kScoreBatch; ++u)
@@ -341,9 +398,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   }
 }
 
-template <int BITS, bool PROD, bool MULTI>
+template <int BITS, bool PROD, bool MULTI, int NO = 0>
 hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, const tq_packed* K, const CodebookArgs& cb,
-                         float* scores, const void* ws, hipStream_t st) {
+                         float* scores, const void* ws, hipStream_t st, const int8_t* q8 = nullptr,
+                         const float* oscale = nullptr, const float* qo = nullptr) {
   const int ratio = Hq / Hkv;
   const uint16_t* qws = static_cast<const uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
@@ -354,7 +412,7 @@ hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, int64_t seq_stride
   static int per_cu = 0;
   if (per_cu == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_scores_d128<BITS, PROD, MULTI>, kScoreWaves * 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_scores_d128<BITS, PROD, MULTI, NO>, kScoreWaves * 64, 0) != hipSuccess ||
         v <= 0)
       v = 2;
     per_cu = v;
@@ -369,14 +427,15 @@ hipError_t scores_launch_m(int B, int Hq, int Hkv, int64_t T, int64_t seq_stride
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (take_armed_timer(TQ_TIMED_SCORES, &ev0, &ev1)) {
     // events attached to the dispatch itself: they bracket the kernel's execution alone
-    hipExtLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs),
+    hipExtLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI, NO>), dim3((unsigned)chunks, (unsigned)seqs),
                           dim3(kScoreWaves * 64), 0, st, ev0, ev1, 0, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw,
-                          K->idx, K->norms, PROD ? K->qjl : nullptr, PROD ? K->rnorms : nullptr, cb, scores);
+                          K->idx, K->norms, PROD ? K->qjl : nullptr, PROD ? K->rnorms : nullptr, cb, scores, q8,
+                          oscale, qo);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI>), dim3((unsigned)chunks, (unsigned)seqs), dim3(kScoreWaves * 64),
-                     0, st, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw, K->idx, K->norms, PROD ? K->qjl : nullptr,
-                     PROD ? K->rnorms : nullptr, cb, scores);
+  hipLaunchKernelGGL((k_scores_d128<BITS, PROD, MULTI, NO>), dim3((unsigned)chunks, (unsigned)seqs),
+                     dim3(kScoreWaves * 64), 0, st, qws, kconst, Hq, Hkv, T, seq_stride, (int)tpw, K->idx, K->norms,
+                     PROD ? K->qjl : nullptr, PROD ? K->rnorms : nullptr, cb, scores, q8, oscale, qo);
   return hipGetLastError();
 }
 
@@ -387,14 +446,59 @@ hipError_t scores_launch(int B, int Hq, int Hkv, int64_t T, int64_t S, const tq_
                       : scores_launch_m<BITS, PROD, false>(B, Hq, Hkv, T, S, K, cb, scores, ws, st);
 }
 
+template <int BITS, int NO>
+hipError_t outlier8_scores_launch(int B, int Hq, int Hkv, int64_t T, int64_t S, const tq_packed* K,
+                                  const CodebookArgs& cb, float* scores, const void* ws, hipStream_t st,
+                                  const int8_t* q8, const float* oscale, const float* qo) {
+  return Hq / Hkv > 4 ? scores_launch_m<BITS, false, true, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo)
+                      : scores_launch_m<BITS, false, false, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo);
+}
+
+template <int NO>
+hipError_t outlier8_scores_bits(int B, int Hq, int Hkv, int64_t T, int64_t S, const tq_packed* K,
+                                const CodebookArgs& cb, float* scores, const void* ws, hipStream_t st,
+                                const int8_t* q8, const float* oscale, const float* qo) {
+  switch (cb.bits) {
+    case 1: return outlier8_scores_launch<1, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo);
+    case 2: return outlier8_scores_launch<2, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo);
+    case 3: return outlier8_scores_launch<3, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo);
+    case 4: return outlier8_scores_launch<4, NO>(B, Hq, Hkv, T, S, K, cb, scores, ws, st, q8, oscale, qo);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* rt, const float* st_mat,
-                           uint16_t* qws, float* kconst, hipStream_t st) {
+                           uint16_t* qws, float* kconst, hipStream_t st, const OutlierArgs* oa, float* qo) {
   const int groups = (Hq / Hkv + kQprepHeads - 1) / kQprepHeads;
   hipLaunchKernelGGL(k_qprep128, dim3(B * Hkv, groups), dim3(kQprepThreads), 0, st, q, Hq, Hq / Hkv, rt, st_mat,
-                     qws, kconst);
+                     qws, kconst, oa ? oa->mask : nullptr, oa ? oa->chan : nullptr, oa ? oa->no : 0, qo);
   return hipGetLastError();
+}
+
+size_t scores_outlier8_workspace_bytes(int B, int Hq) {
+  const size_t base = (scores_workspace_bytes(B, Hq, 128) + 255) & ~(size_t)255;
+  return base + (size_t)B * Hq * kOutlierMaxChannels * sizeof(float);
+}
+
+hipError_t launch_scores_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+                                  const tq_packed* K, const int8_t* q8, const float* oscale, const CodebookArgs& cb,
+                                  const tq_rotation_s* rot, const OutlierArgs& oa, float* scores, void* ws,
+                                  hipStream_t st) {
+  uint16_t* qws = static_cast<uint16_t*>(ws);
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  float* kconst = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
+  float* qo = reinterpret_cast<float*>(static_cast<char*>(ws) + ((scores_workspace_bytes(B, Hq, 128) + 255) &
+                                                                 ~(size_t)255));
+  hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot->rt32_dev, nullptr, qws, kconst, st, &oa, qo);
+  if (e != hipSuccess) return e;
+  switch (oa.no) {
+    case 4: return outlier8_scores_bits<4>(B, Hq, Hkv, T, seq_stride, K, cb, scores, ws, st, q8, oscale, qo);
+    case 8: return outlier8_scores_bits<8>(B, Hq, Hkv, T, seq_stride, K, cb, scores, ws, st, q8, oscale, qo);
+    case 16: return outlier8_scores_bits<16>(B, Hq, Hkv, T, seq_stride, K, cb, scores, ws, st, q8, oscale, qo);
+  }
+  return hipErrorInvalidValue;
 }
 
 size_t scores_workspace_bytes(int B, int Hq, int d) {

@@ -42,15 +42,19 @@ class EncodedOutlier8:
     scale: np.ndarray        # [B, H, T] float64
 
 
-def int8_absmax(v):
+def int8_absmax(v, dtype=np.float64):
     """Symmetric 8-bit quantization of rows v [..., n_o]: scale = max |v| / 127, q = round(v / scale)
-    (half to even).  Returns (q int8, scale float64); an all-zero row gives scale 0, q 0."""
-    v = np.asarray(v, dtype=np.float64)
+    (half to even).  Returns (q int8, scale); an all-zero row gives scale 0, q 0.
+
+    dtype is the precision of the two divisions (each correctly rounded); the page fixes none.
+    float64 is the reading; float32 takes the integer decisions in a float32 kernel's precision,
+    so that its codes can be compared bit for bit."""
+    v = np.asarray(v, dtype=dtype)
     amax = np.max(np.abs(v), axis=-1)
-    scale = amax / 127.0
-    safe = np.where(scale > 0, scale, 1.0)
+    scale = amax / dtype(127.0)
+    safe = np.where(scale > 0, scale, dtype(1.0))
     q = np.rint(v / safe[..., None])                  # numpy rint: half to even
-    q = np.where(scale[..., None] > 0, q, 0.0)
+    q = np.where(scale[..., None] > 0, q, dtype(0.0))
     return np.clip(q, -127, 127).astype(np.int8), scale
 
 
@@ -63,8 +67,9 @@ def rest_mask(outliers, d=128):
     return m
 
 
-def encode_outlier8(x, outliers, rotation, cb):
-    """x [B, H, T, 128]; outliers [H, n_o] (distinct channels per head)."""
+def encode_outlier8(x, outliers, rotation, cb, int8_dtype=np.float64):
+    """x [B, H, T, 128]; outliers [H, n_o] (distinct channels per head); int8_dtype: the precision
+    of the 8-bit decisions (see int8_absmax)."""
     x = np.asarray(x, dtype=np.float64)
     bsz, h, t, d = x.shape
     mask = rest_mask(outliers, d)
@@ -72,7 +77,7 @@ def encode_outlier8(x, outliers, rotation, cb):
     enc = encode_mse(xr.reshape(-1, d), rotation, cb)
     rest = EncodedMSE(idx=enc.idx.reshape(bsz, h, t, d), words=None, norms=enc.norms.reshape(bsz, h, t), y=None)
     xo = np.stack([x[:, hh][..., np.asarray(outliers)[hh]] for hh in range(h)], axis=1)   # [B, H, T, n_o]
-    q8, scale = int8_absmax(xo)
+    q8, scale = int8_absmax(xo, int8_dtype)
     return EncodedOutlier8(outliers=np.asarray(outliers), rest=rest, q8=q8, scale=scale)
 
 

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(tq):
     for name in names:
         assert hasattr(raw, name), name
         assert name in _binding.SIGNATURES, f"binding lacks {name}"
-    assert tq.lib().tq_abi_version() == 6
+    assert tq.lib().tq_abi_version() == 7
 
 
 def test_splitmix_bit_identical(tq):

@@ -1,0 +1,217 @@
+"""GPU parity of outlier-8 keys (outlier channels as symmetric 8-bit integers with a per-key
+scale, the other channels TurboQuant_mse at d = 128) against the oracle, through the C ABI.
+
+* Encode: the rest code's indices by the band rule against the oracle's encode of the key with
+  its outlier channels zeroed, its norms within 1e-6; the 8-bit values and scales bit for bit
+  against the oracle's quantizer taking its decisions in float32 (the kernel's precision).
+* Scores from the GPU's own codes against the oracle's score formula within
+  1e-3 * ||q|| * ||k_hat|| (the score tolerance of the other key formats).
+* Token counts that are not multiples of the 16-row tiles, so that tiles straddle KV heads;
+  bf16 and fp32 keys; 4, 8 and 16 outlier channels; GQA ratios 1, 3, 4 and 8; keys whose outlier
+  part or whole vector is zero; errors."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_compression_turboquant_amd as tq
+from kv_cache_compression_turboquant_amd import workloads as wl
+from _parity import check_indices, require_gpu, score_tolerance, to_np_words
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+R = oracle.dense_rotation(D, 1)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def rot(dev):
+    return tq.make_rotation(D, 1)
+
+
+def _keys(B, H, T, seed, dtype):
+    bits = wl.kv_tensor_bf16(B, H, T, D, seed=seed, outlier_seed=10, scale_seed=seed + 1)
+    x = wl.bf16_bits_to_f32(bits).astype(np.float64)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    if dtype == "f32":
+        x = (x * (1.0 + 1e-3 * wl.gaussian(x.shape, seed + 2))).astype(np.float32)
+        xt = torch.from_numpy(x)
+        x = x.astype(np.float64)
+    return x, xt
+
+
+def _outliers(x, n_o):
+    """Per KV head, the n_o channels of largest mean square (a calibration rule of the tests; the
+    library takes any list), in ascending channel order as the library stores them."""
+    ms = np.mean(x * x, axis=(0, 2))
+    return np.sort(np.argsort(-ms, axis=1, kind="stable")[:, :n_o], axis=1).astype(np.int32)
+
+
+def _check_encode(x, outl, rest, q8, scale, b, label):
+    B, H, T, _ = x.shape
+    ocb = oracle.codebook(D, b)
+    ref = oracle.encode_outlier8(x, outl, R, ocb, int8_dtype=np.float32)
+    np.testing.assert_array_equal(ref.rest.idx.reshape(-1, D), oracle.encode_mse(
+        (x * oracle.rest_mask(outl)[None, :, None, :]).reshape(-1, D), R, ocb).idx)
+    gidx = oracle.unpack_bits(to_np_words(rest.idx), D, b)
+    # the oracle's rotated coordinates of the masked keys decide the band
+    mask = oracle.rest_mask(outl)
+    xr = (x * mask[None, :, None, :]).reshape(-1, D)
+    enc = oracle.encode_mse(xr, R, ocb)
+    bad, _ = check_indices(gidx, enc.y, ocb, label)
+    np.testing.assert_array_equal(gidx[~bad], enc.idx[~bad])
+    np.testing.assert_allclose(rest.norms.cpu().numpy(), enc.norms, rtol=1e-6, atol=1e-30)
+    np.testing.assert_array_equal(q8.cpu().numpy().reshape(B, H, T, -1), ref.q8)
+    np.testing.assert_array_equal(scale.cpu().numpy().reshape(B, H, T), ref.scale)
+    return gidx
+
+
+def _gpu_as_oracle(outl, rest, q8, scale, B, H, T, b):
+    return oracle.EncodedOutlier8(
+        outliers=outl,
+        rest=oracle.EncodedMSE(idx=oracle.unpack_bits(to_np_words(rest.idx), D, b).reshape(B, H, T, D), words=None,
+                               norms=rest.norms.cpu().numpy().astype(np.float64).reshape(B, H, T), y=None),
+        q8=q8.cpu().numpy().reshape(B, H, T, -1), scale=scale.cpu().numpy().astype(np.float64).reshape(B, H, T))
+
+
+@pytest.mark.parametrize("n_o,b,dtype", [(4, 3, "bf16"), (8, 3, "bf16"), (16, 3, "bf16"), (8, 2, "bf16"),
+                                         (16, 4, "bf16"), (4, 1, "f32"), (8, 3, "f32"), (16, 2, "f32")])
+def test_encode_outlier8_matches_oracle(dev, rot, n_o, b, dtype):
+    B, H, T = 2, 3, 301                     # 301 tokens: tiles of 16 rows straddle heads
+    x, xt = _keys(B, H, T, seed=n_o * 10 + b, dtype=dtype)
+    outl = _outliers(x, n_o)
+    o = tq.make_outlier8(outl)
+    cb = tq.codebook(D, b)
+    rest, q8, scale = tq.encode_outlier8(xt.to(dev), o, cb, rot)
+    torch.cuda.synchronize()
+    _check_encode(x, outl, rest, q8, scale, b, f"outlier8 n_o={n_o} b={b} {dtype}")
+
+
+def test_encode_outlier8_unsorted_list_and_zero_parts(dev, rot):
+    B, H, T, n_o, b = 1, 2, 40, 8, 3
+    x, _ = _keys(B, H, T, seed=5, dtype="bf16")
+    outl = _outliers(x, n_o)
+    x[0, 0, 3][outl[0]] = 0.0               # outlier part zero: scale 0, q 0
+    x[0, 1, 7] = 0.0                        # whole key zero: norm 0
+    x[0, 1, 8][np.setdiff1d(np.arange(D), outl[1])] = 0.0   # rest part zero
+    xt = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)   # exact: every value is bf16
+    shuffled = np.stack([np.random.default_rng(h).permutation(outl[h]) for h in range(H)])
+    o = tq.make_outlier8(shuffled)          # any order; slots follow ascending channels
+    np.testing.assert_array_equal(o.outliers, outl)
+    rest, q8, scale = tq.encode_outlier8(xt.to(dev), o, tq.codebook(D, b), rot)
+    torch.cuda.synchronize()
+    _check_encode(x, outl, rest, q8, scale, b, "outlier8 zero parts")
+    sc = scale.cpu().numpy().reshape(B, H, T)
+    assert sc[0, 0, 3] == 0.0 and sc[0, 1, 7] == 0.0
+    assert rest.norms.cpu().numpy().reshape(B, H, T)[0, 1, 8] == 0.0
+
+
+@pytest.mark.parametrize("n_o,b", [(4, 3), (8, 3), (16, 4), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (2, 2), (6, 2), (16, 2), (32, 1)])
+def test_scores_outlier8_matches_oracle(dev, rot, n_o, b, hq, hkv):
+    B, T = 2, 300
+    x, xt = _keys(B, hkv, T, seed=3, dtype="bf16")
+    outl = _outliers(x, n_o)
+    o = tq.make_outlier8(outl)
+    cb = tq.codebook(D, b)
+    K = tq.encode_outlier8(xt.to(dev), o, cb, rot)
+    q = wl.gaussian((B, hq, D), 21)
+    s = tq.scores_outlier8(torch.from_numpy(q).to(dev), K, hkv, o, cb, rot)
+    torch.cuda.synchronize()
+    enc = _gpu_as_oracle(outl, *K, B, hkv, T, b)
+    ocb = oracle.codebook(D, b)
+    ref = oracle.scores_outlier8(q, enc, R, ocb)
+    knorm = np.linalg.norm(oracle.decode_outlier8(enc, R, ocb), axis=-1)      # [B, Hkv, T]
+    got = s.cpu().numpy()
+    ratio = hq // hkv
+    for bb in range(B):
+        for h in range(hq):
+            tol = score_tolerance(q[bb, h][None], knorm[bb, h // ratio])[0]
+            err = np.abs(got[bb, h] - ref[bb, h])
+            assert np.all(err <= tol), (bb, h, float(err.max()))
+
+
+def test_scores_outlier8_c2_shape_samples(dev, rot):
+    # 8 KV heads x 32768 tokens (the 32-head GQA decode shape), 3 rest bits, 8 outliers per head:
+    # 2048 sampled keys' codes against the oracle, and the scores of 256 of them.
+    B, hkv, hq, T, n_o, b = 1, 8, 32, 32768, 8, 3
+    bits = wl.kv_tensor_bf16(B, hkv, T, D, seed=77, outlier_seed=10, scale_seed=78)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    # the 4 generated outlier channels plus the 4 lowest channels not among them
+    outl = []
+    for h, ch in enumerate(wl.outlier_channels(hkv, D, 10)):
+        extra = [c for c in range(D) if c not in ch][:n_o - 4]
+        outl.append(sorted(list(ch) + extra))
+    outl = np.array(outl, dtype=np.int32)
+    o = tq.make_outlier8(outl)
+    cb = tq.codebook(D, b)
+    K = tq.encode_outlier8(xt.to(dev), o, cb, rot)
+    q = wl.gaussian((B, hq, D), 5)
+    s = tq.scores_outlier8(torch.from_numpy(q).to(dev), K, hkv, o, cb, rot)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(B * hkv * T, size=2048, replace=False))
+    x = wl.bf16_bits_to_f32(bits.reshape(-1, D)[rows]).astype(np.float64)
+    heads = (rows // T) % hkv
+    ocb = oracle.codebook(D, b)
+    rest, q8, scale = K
+    q8n, scn = q8.cpu().numpy(), scale.cpu().numpy()
+    gidx = oracle.unpack_bits(to_np_words(rest.idx)[rows], D, b)
+    masks = oracle.rest_mask(outl)[heads]
+    enc = oracle.encode_mse(x * masks, R, ocb)
+    bad, _ = check_indices(gidx, enc.y, ocb, "outlier8 samples")
+    np.testing.assert_array_equal(gidx[~bad], enc.idx[~bad])
+    xo = np.stack([x[i, outl[h]] for i, h in enumerate(heads)])
+    rq, rs = oracle.int8_absmax(xo, np.float32)
+    np.testing.assert_array_equal(q8n[rows], rq)
+    np.testing.assert_array_equal(scn[rows], rs)
+    # scores of the sampled keys from the GPU's own codes, all 32 query heads
+    norms = rest.norms.cpu().numpy()[rows].astype(np.float64)
+    got = s.cpu().numpy()                                  # [B, Hq, T]
+    for i, (r, h) in enumerate(zip(rows[:256], heads[:256])):
+        t = r % T
+        e1 = oracle.EncodedOutlier8(outliers=outl[h:h + 1],
+                                    rest=oracle.EncodedMSE(idx=gidx[i].reshape(1, 1, 1, D), words=None,
+                                                           norms=norms[i].reshape(1, 1, 1), y=None),
+                                    q8=q8n[r].reshape(1, 1, 1, -1), scale=np.float64(scn[r]).reshape(1, 1, 1))
+        qh = q[:, 4 * h:4 * h + 4]
+        ref = oracle.scores_outlier8(qh, e1, R, ocb)[0, :, 0]
+        kn = np.linalg.norm(oracle.decode_outlier8(e1, R, ocb))
+        tol = 1e-3 * np.linalg.norm(qh[0], axis=-1) * kn
+        assert np.all(np.abs(got[0, 4 * h:4 * h + 4, t] - ref) <= tol), (r, h)
+
+
+def test_outlier8_errors(dev, rot):
+    cb = tq.codebook(D, 3)
+    with pytest.raises(tq.TQError) as e:
+        tq.make_outlier8(np.zeros((2, 5), dtype=np.int32) + np.arange(5))       # n_o = 5
+    assert e.value.status == 3
+    with pytest.raises(tq.TQError) as e:
+        tq.make_outlier8(np.array([[1, 2, 3, 3]], dtype=np.int32))              # repeated channel
+    assert e.value.status == 1
+    with pytest.raises(tq.TQError) as e:
+        tq.make_outlier8(np.array([[1, 2, 3, 128]], dtype=np.int32))            # out of range
+    assert e.value.status == 1
+    o = tq.make_outlier8(np.array([[1, 2, 3, 4], [5, 6, 7, 8]], dtype=np.int32))
+    x = torch.zeros((1, 3, 16, D), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tq.TQError) as e:
+        tq.encode_outlier8(x, o, cb, rot)                                       # 3 heads, handle has 2
+    assert e.value.status == 2
+    x = torch.zeros((1, 2, 16, D), dtype=torch.bfloat16, device=dev)
+    K = tq.encode_outlier8(x, o, cb, rot)
+    with pytest.raises(tq.TQError) as e:
+        tq.scores_outlier8(torch.zeros((1, 5, D), device=dev), K, 2, o, cb, rot)    # Hq % Hkv
+    assert e.value.status == 2
+    with pytest.raises(tq.TQError) as e:
+        tq.scores_outlier8(torch.zeros((1, 4, D), device=dev), K, 2, o, cb, rot,
+                           ws=torch.empty(16, dtype=torch.uint8, device=dev))
+    assert e.value.status == 4
+    with pytest.raises(tq.TQError) as e:
+        tq.scores_outlier8(torch.zeros((1, 4, D), device=dev), K, 2, o, tq.codebook(D, 2), rot)   # bits
+    assert e.value.status == 2

@@ -38,6 +38,17 @@ def test_int8_absmax_is_the_nearest_level():
         np.testing.assert_array_equal(q, qb)
         if s > 0:
             assert np.max(np.abs(q)) == 127 and np.all(np.abs(v - s * q) <= s / 2 + 1e-12)
+    # float32 decisions: the same rule in float32 arithmetic (exact inputs, correctly rounded
+    # divisions), checked against the brute force on float32 scales
+    v = (rng.standard_normal(16) * 3).astype(np.float32)
+    q, s = o8.int8_absmax(v, np.float32)
+    assert s.dtype == np.float32 and s == np.float32(np.max(np.abs(v))) / np.float32(127)
+    levels = np.arange(-127, 128, dtype=np.float32)
+    for x, k in zip(v, q):
+        r = x / s                                   # float32, as the decision is taken
+        dist = np.abs(r.astype(np.float64) - levels)
+        best = levels[dist == dist.min()]
+        assert k == (best[0] if best.size == 1 else best[best % 2 == 0][0])
     # the printed ties: 2.5 -> 2, 3.5 -> 4, -2.5 -> -2 at scale 1
     q, s = o8.int8_absmax(np.array([127.0, 2.5, 3.5, -2.5]))
     assert s == 1.0 and list(q) == [127, 2, 4, -2]
