@@ -508,6 +508,43 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_split(cfg, bo, br, cpu_budget)
+    elif name == "c2o8":
+        # Outlier-8 keys on the KV-key workload (1 x 8 KV heads x 32768 tokens, 32 query heads): per
+        # KV head the 8 channels of largest mean square over the first 4096 tokens as int8 with a
+        # per-key scale, the other 120 channels TurboQuant_mse at 3 bits (d = 128).
+        cfg = wl.CONFIGS["c2"]
+        b, n_o = 3, 8
+        n = cfg.B * cfg.hkv * cfg.T
+        kb = wl.kv_keys(cfg)
+        xs = wl.bf16_bits_to_f32(kb[:, :, :4096]).astype(np.float64)
+        outl = np.argsort(-np.mean(xs * xs, axis=(0, 2)), axis=1, kind="stable")[:, :n_o]
+        del xs
+        keys = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        o = tq.make_outlier8(outl)
+        rot = tq.make_rotation(cfg.d, cfg.rot_seed)
+        cb = tq.codebook(cfg.d, b)
+        nbuf = 3
+        packs = [(tq.alloc_packed(n, cfg.d, b, device=dev), torch.empty((n, n_o), dtype=torch.int8, device=dev),
+                  torch.empty((n,), device=dev)) for _ in range(nbuf)]
+        outs = [torch.empty((cfg.B, cfg.hq, cfg.T), device=dev) for _ in range(nbuf)]
+        ws = torch.empty(tq.scores_outlier8_workspace(cfg.B, cfg.hq), dtype=torch.uint8, device=dev)
+        enc = lambda i: tq.encode_outlier8(keys, o, cb, rot, out=packs[i % nbuf])
+        sco = lambda i: tq.scores_outlier8(q, packs[i % nbuf], cfg.hkv, o, cb, rot, out=outs[i % nbuf], ws=ws)
+        enc_ms = _timed(enc, steps, warmup)
+        sc_ms = _timed(sco, steps, warmup)
+        step_ms = _timed(lambda i: (enc(i), sco(i)), steps, warmup)
+        code = 4 * (cfg.d * b // 32) + 4 + n_o + 4      # rest words, rest norm, int8 values, scale
+        enc_bytes = n * (cfg.d * 2 + code)
+        sc_bytes = n * code + q.numel() * 4 + outs[0].numel() * 4
+        res.update({"bits_rest": b, "outliers_per_head": n_o,
+                    "bits_per_channel": (b * (cfg.d - n_o) + 8 * n_o) / cfg.d,
+                    "step_ms": step_ms, "scores_per_s_step": outs[0].numel() / step_ms * 1e3,
+                    "encode_ms": enc_ms, "encode_gbs": enc_bytes / enc_ms / 1e6,
+                    "encode_hbm_frac": enc_bytes / enc_ms / 1e6 / HBM_PEAK_GBS,
+                    "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
+                    "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
+                    "scores_per_s": outs[0].numel() / sc_ms * 1e3})
     elif name == "c2splitdecode":
         # Split keys as a streaming key cache on the KV-key workload (1 x 8 KV heads x 32768 tokens,
         # 32 query heads, 2.5 bits per channel): prefill to T0 tokens in one append, then per step
@@ -754,7 +791,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
-                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode",
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode", "c2o8",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "
                          "per-kernel timings only")

@@ -28,8 +28,13 @@
  *    error nothing is enqueued, outputs are untouched, and tq_last_error() returns a
  *    thread-local message.  Asynchronous device faults surface at the caller's next
  *    synchronisation.  Non-finite inputs give unspecified (but in-bounds) results.
- *  - Sizes: 1 <= b <= 4 bits per index stage; d * b must be a multiple of 32; the fused
- *    kernels cover d = 128; other d in [64, 3072] use the general path where stated.
+ *  - Sizes: 1 <= b <= 4 bits per index stage; d * b must be a multiple of 32.  Vector length
+ *    d: the fused kernels cover d = 128, the head dimension of the KV workloads.  tq_encode,
+ *    tq_decode, tq_rotate and tq_search_topk also take d a multiple of 128 in [256, 4096] (the
+ *    embedding workloads, d = 1536 among them) on the general-d kernels.  The score, attention,
+ *    cache, prefill, split and outlier-8 entry points take d = 128 only and return
+ *    TQ_EUNSUPPORTED for any other d (head_dim 64 or 256 is not covered; d = 64 appears only as
+ *    the half-vectors of the split codes).
  */
 #ifndef TQ_H_
 #define TQ_H_

@@ -124,6 +124,41 @@ __device__ __forceinline__ u32x4 decode_keys(const uint32_t (&w)[BITS], int s, c
   return decode8<BITS, COPIES>(w, 8 * BITS * s, tabl);
 }
 
+// decode_keys with the table's own base and the lane's copy offset laneoff = (lane % COPIES) *
+// entry bytes kept apart: when the field stride is a power of two above laneoff, each address is
+// base + (field * stride | laneoff), one shift and one and-or per lookup, with the base folded
+// into the LDS instruction's offset.
+template <int BITS, int COPIES>
+__device__ __forceinline__ u32x4 decode_keys_or(const uint32_t (&w)[BITS], int s, const uint8_t* tab,
+                                                uint32_t laneoff) {
+  using DT = DecodeTable<BITS, false, COPIES>;
+  constexpr uint32_t S = DT::STRIDE;
+  if constexpr ((S & (S - 1)) != 0) {
+    return decode8<BITS, COPIES>(w, 8 * BITS * s, tab + laneoff);
+  } else {
+    auto at = [&](uint32_t field) { return tab + ((field * S) | laneoff); };
+    const int off = 8 * BITS * s;
+    u32x4 out;
+    if constexpr (BITS == 1) {
+      out = *reinterpret_cast<const u32x4*>(at(get_bits(w, off, 8)));
+    } else if constexpr (BITS == 2) {
+      const uint32_t f = get_bits(w, off, 16);
+      const u32x2 a = *reinterpret_cast<const u32x2*>(at(f & 0xffu));
+      const u32x2 b = *reinterpret_cast<const u32x2*>(at(f >> 8));
+      out = u32x4{a[0], a[1], b[0], b[1]};
+    } else if constexpr (BITS == 3) {
+      const uint32_t f = get_bits(w, off, 24);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(at((f >> (6 * j)) & 63u));
+    } else {
+      const uint32_t f = get_bits(w, off, 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(at((f >> (8 * j)) & 0xffu));
+    }
+    return out;
+  }
+}
+
 // Builds the replicated fp16 decode table of a codebook in LDS (cent: 16 fp16 centroids in LDS).
 template <int BITS, int COPIES>
 __device__ __forceinline__ void build_table(uint8_t* tab, const _Float16* cent) {

@@ -195,6 +195,15 @@ __global__ __launch_bounds__(kQprepThreads) void k_qprep128(const float* __restr
 #ifndef TQ_SCORE_ROUNDS
 #define TQ_SCORE_ROUNDS 1
 #endif
+#ifndef TQ_SCORE_PIPE
+#define TQ_SCORE_PIPE 1
+#endif
+#ifndef TQ_SCORE_SHARE
+#define TQ_SCORE_SHARE 1
+#endif
+#ifndef TQ_SCORE_MINB
+#define TQ_SCORE_MINB 3   // resident blocks per CU the register budget is sized for
+#endif
 constexpr int kScoreWaves = 4;
 constexpr int kScoreBatch = TQ_SCORE_BATCH;   // key tiles loaded before any of them is scored
 constexpr int kScoreRounds = TQ_SCORE_ROUNDS; // target grid = this many rounds of resident blocks
@@ -218,19 +227,24 @@ struct KeyBufs {
 
 // Lane (n, g) share of key tile `tile` of one sequence: its BITS words (coordinates 32 g ..),
 // norm, and for prod its sign word and scaled residual norm.
-template <int BITS, bool PROD, int NO>
+// PERKEY false: the per-key scalars (norm, residual norm, outlier scale) are left out; the
+// caller loads them for several tiles at once (see load_half).
+template <int BITS, bool PROD, int NO, bool PERKEY = true>
 __device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile, int nl, int g,
                                               KeyTile<BITS, PROD, NO>& k) {
   const uint32_t t = (uint32_t)tile * 16u + (uint32_t)nl;
   if constexpr (NO > 0) {
     buffer_words<NO / 4>(kb.q8, t * (uint32_t)NO, k.o8);
-    k.osc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.osc, t * 4u, 0, 0));
+    if constexpr (PERKEY)
+      k.osc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.osc, t * 4u, 0, 0));
   }
   buffer_words<BITS>(kb.idx, t * (16u * BITS) + (uint32_t)(4 * BITS * g), k.w);
-  k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.norms, t * 4u, 0, 0));
+  if constexpr (PERKEY) k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.norms, t * 4u, 0, 0));
   if constexpr (PROD) {
     k.zw = __builtin_amdgcn_raw_buffer_load_b32(kb.qbits, t * 16u + 4u * (uint32_t)g, 0, 0);
-    k.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.rnorms, t * 4u, 0, 0)) * (kQjl / 128.0f);
+    if constexpr (PERKEY)
+      k.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb.rnorms, t * 4u, 0, 0)) *
+              (kQjl / 128.0f);
   } else {
     k.zw = 0;
     k.gam = 0.f;
@@ -241,7 +255,7 @@ __device__ __forceinline__ void load_key_tile(const KeyBufs<PROD>& kb, int tile,
 // kernel carries only the single-group path.  NO > 0: outlier-8 keys, whose score adds
 // scale * <q_O, q8> (fp32, on the vector ALUs) to the rest channels' term; qo holds q_O.
 template <int BITS, bool PROD, bool MULTI, int NO>
-__global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
+__global__ __launch_bounds__(kScoreWaves * 64, TQ_SCORE_MINB) void k_scores_d128(
     const uint16_t* __restrict__ qws, const float* __restrict__ kconst, int Hq, int Hkv, int64_t T, int64_t seq_stride,
     int tiles_per_wave,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms,
@@ -258,8 +272,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const uint8_t* tabl = DT::lane_base(tab, lane);
-  const int wave = threadIdx.x >> 6;
+  const uint32_t laneoff = (uint32_t)(lane % TC) * DT::EB;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15;
   const int g = lane >> 4;
   const int bg = blockIdx.y;
@@ -306,6 +320,20 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   };
   u32x4 a0[4];
   load_a(0, a0);
+  // Prod keys with one head group: the key product reads the rotated-query rows (0-7) and the
+  // sign product the sketch rows (8-15) of two copies of the operand with the other rows zeroed,
+  // so both products accumulate into one result whose rows are already the ones each lane
+  // keeps (lanes of groups 0-1 hold rows 0-7, groups 2-3 rows 8-15): no per-lane select.  The
+  // zero rows add exact zeros, so every kept row sums the same terms in the same order.
+  constexpr bool kOneAcc = PROD && !MULTI;
+  u32x4 a0k[kOneAcc ? 4 : 1], a0z[kOneAcc ? 4 : 1];
+  if constexpr (kOneAcc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a0k[s] = nl < 8 ? a0[s] : u32x4{0u, 0u, 0u, 0u};
+      a0z[s] = nl < 8 ? u32x4{0u, 0u, 0u, 0u} : a0[s];
+    }
+  }
   // sketch constant K of the lane's head (4 hg + g) after the reduction
   auto load_kc = [&](int hg) -> float {
     const int h = 4 * hg + g;
@@ -327,14 +355,14 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
   // Ping-pong over two tile buffers (no register copies), so the next tile's loads stay in flight
   // while the current one is scored and the wait before scoring counts only the older loads.
   auto score_tile = [&](const KeyTile<BITS, PROD, NO>& cur, int64_t ti) {
-    const int64_t tile = tile0 + ti;
-    const int64_t t = tile * 16 + nl;
-    const bool valid = t < T;
+    // token of the lane's key (below 2^25 + 16: the host bounds T, and ti stays below `last`)
+    const uint32_t t = (uint32_t)(tile0 + ti) * 16u + (uint32_t)nl;
+    const bool valid = t < (uint32_t)T;
     const float nrm = cur.nrm;
     const float gam = cur.gam;
     u32x4 bk[4], bz[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bk[s] = decode_keys<BITS, TC>(cur.w, s, tabl);
+    for (int s = 0; s < 4; ++s) bk[s] = decode_keys_or<BITS, TC>(cur.w, s, tab, laneoff);
     if constexpr (PROD) sign_operand(cur.zw, bz);
     float o8f[NO > 0 ? NO : 1];
     if constexpr (NO > 0) {
@@ -350,15 +378,23 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
         load_a(hg, a);
       }
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kOneAcc) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        acc = mfma_f16(a[s], bk[s], acc);
-        if constexpr (PROD) accz = mfma_f16(a[s], bz[s], accz);
-      }
-      if constexpr (PROD) {
+        for (int s = 0; s < 4; ++s) {
+          acc = mfma_f16(a0k[s], bk[s], acc);
+          acc = mfma_f16(a0z[s], bz[s], acc);
+        }
+      } else {
+        f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = g < 2 ? acc[r] : accz[r];
+        for (int s = 0; s < 4; ++s) {
+          acc = mfma_f16(a[s], bk[s], acc);
+          if constexpr (PROD) accz = mfma_f16(a[s], bz[s], accz);
+        }
+        if constexpr (PROD) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = g < 2 ? acc[r] : accz[r];
+        }
       }
       const float sc = g < 2 ? nrm : 2.f * gam;
       float mine = reduce_parts(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
@@ -379,13 +415,88 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
       }
       if (valid && h < ratio)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), sbuf,
-                                              ((uint32_t)h * (uint32_t)T + (uint32_t)t) * 4u, 0, 0);
+                                              ((uint32_t)h * (uint32_t)T + t) * 4u, 0, 0);
     }
   };
-  // Batches of kScoreBatch tiles: every load of a batch is issued before any tile of it is
-  // scored (straight-line code, so the waits are exact), and the batch's latency is paid once.
   int64_t last = tiles_per_wave;
   if (ntiles_seq - tile0 < last) last = ntiles_seq - tile0;
+#if TQ_SCORE_PIPE
+  // Two half-batches A and B of kScoreBatch / 2 tiles in ping-pong: the loads of one half are in
+  // flight while the other half is scored, so a wave never waits for a whole batch's latency
+  // with nothing to do.  Loads past the sequence read zeros (buffer range), so they are issued
+  // unconditionally and every wait stays exact.
+  // Each half's loads go through resources based at its first key (scalar arithmetic only), so
+  // that every load address is a loop-invariant lane offset plus an immediate: no vector register
+  // is written to form an address, and none can collide with the sources of a store still in
+  // flight (a wait for such a store would also wait for every load issued before it).
+  // With TQ_SCORE_SHARE the per-key scalars of a half (up to 64 keys) come in one load per
+  // array, lane l holding key l of the half, and reach the lanes of tile u by a cross-lane
+  // permute: a third of the vector memory instructions of a tile, whose address queue limits
+  // the issue rate here.
+  constexpr int HB = kScoreBatch / 2;
+  constexpr bool kShare = TQ_SCORE_SHARE && HB <= 4;
+  struct HalfScalars {
+    float nrm, gam, osc;
+  };
+  KeyTile<BITS, PROD, NO> ka[HB], kbt[HB];
+  HalfScalars sa, sb;
+  auto load_half = [&](KeyTile<BITS, PROD, NO> (&kt)[HB], HalfScalars& hs, int64_t tb) {
+    const int64_t first = (tile0 + tb) * 16;
+    const int64_t rem = T - first;
+    const uint32_t nk = rem > 0 ? (uint32_t)rem : 0u;
+    const int64_t row = base_row + first;
+    KeyBufs<PROD> h;
+    h.idx = buffer_rsrc(idx + row * (4 * BITS), nk * (16u * BITS));
+    h.norms = buffer_rsrc(norms + row, nk * 4u);
+    if constexpr (PROD) {
+      h.qbits = buffer_rsrc(qbits + row * 4, nk * 16u);
+      h.rnorms = buffer_rsrc(rnorms + row, nk * 4u);
+    }
+    if constexpr (NO > 0) {
+      h.q8 = buffer_rsrc(q8 + row * NO, nk * (uint32_t)NO);
+      h.osc = buffer_rsrc(oscale + row, nk * 4u);
+    }
+#pragma unroll
+    for (int u = 0; u < HB; ++u) load_key_tile<BITS, PROD, NO, !kShare>(h, u, nl, g, kt[u]);
+    if constexpr (kShare) {
+      const uint32_t off = (uint32_t)lane * 4u;
+      hs.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(h.norms, off, 0, 0));
+      if constexpr (PROD)
+        hs.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(h.rnorms, off, 0, 0)) *
+                 (kQjl / 128.0f);
+      if constexpr (NO > 0) hs.osc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(h.osc, off, 0, 0));
+    }
+  };
+  auto score_half = [&](const KeyTile<BITS, PROD, NO> (&kt)[HB], const HalfScalars& hs, int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      if (tb + u < last) {
+        if constexpr (kShare) {
+          KeyTile<BITS, PROD, NO> k = kt[u];
+          const int src = (nl + 16 * u) << 2;
+          k.nrm = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(hs.nrm)));
+          if constexpr (PROD) k.gam = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(hs.gam)));
+          if constexpr (NO > 0) k.osc = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(hs.osc)));
+          score_tile(k, tb + u);
+        } else {
+          score_tile(kt[u], tb + u);
+        }
+      }
+    }
+  };
+  load_half(ka, sa, 0);
+  for (int64_t tb = 0; tb < last; tb += 2 * HB) {
+    load_half(kbt, sb, tb + HB);
+    __builtin_amdgcn_sched_barrier(0);
+    score_half(ka, sa, tb);
+    if (tb + HB >= last) break;
+    load_half(ka, sa, tb + 2 * HB);
+    __builtin_amdgcn_sched_barrier(0);
+    score_half(kbt, sb, tb + HB);
+  }
+#else
+  // Batches of kScoreBatch tiles: every load of a batch is issued before any tile of it is
+  // scored (straight-line code, so the waits are exact), and the batch's latency is paid once.
   for (int64_t tb = 0; tb < last; tb += kScoreBatch) {
     KeyTile<BITS, PROD, NO> kt[kScoreBatch];
 #pragma unroll
@@ -396,6 +507,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void k_scores_d128(
     for (int u = 0; u < kScoreBatch; ++u)
       if (tb + u < last) score_tile(kt[u], tb + u);
   }
+#endif
 }
 
 template <int BITS, bool PROD, bool MULTI, int NO = 0>
