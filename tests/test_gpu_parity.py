@@ -117,6 +117,26 @@ def test_encode_mse_c1_fp32_full(dev, rot_dense):
     assert abs(mse_g / mse_o - 1) < 0.01
 
 
+def test_scores_c1_fp32_full(dev, rot_dense):
+    # the tiny round trip's own inputs: 4096 fp32 N(0,1) vectors as one KV head of 4096 keys,
+    # scored by its 32 fp32 N(0,1) queries (GQA ratio 32, the multi-group path)
+    x32, q32 = wl.c1_inputs()
+    cb_o, cb = oracle.codebook(128, 2), tq.codebook(128, 2)
+    p = tq.encode(torch.from_numpy(x32).to(dev), 2, "mse", cb, rot_dense)
+    s = tq.scores(torch.from_numpy(q32.reshape(1, 32, 128)).to(dev), p, 1, cb, rot_dense)
+    torch.cuda.synchronize()
+    enc = _packed_to_oracle(p, 128, 2, False)
+    q = q32.astype(np.float64)
+    ref = oracle.scores_mse(q, enc.idx, enc.norms, R_DENSE, cb_o)          # [32, 4096]
+    err = np.abs(s.cpu().numpy()[0] - ref)
+    tol = score_tolerance(q, enc.norms)
+    assert np.all(err <= tol), float((err / tol).max())
+    # and the GPU's codes score like the oracle's own encode of the same vectors
+    own = oracle.encode_mse(x32.astype(np.float64), R_DENSE, cb_o)
+    ref_own = oracle.scores_mse(q, own.idx, own.norms, R_DENSE, cb_o)
+    assert np.mean(np.abs(ref - ref_own)) <= 1e-3 * np.mean(np.abs(ref_own))
+
+
 @pytest.mark.parametrize("kind", ["dense", "wht"])
 def test_encode_prod_parity(dev, rot_dense, rot_wht, kind):
     rot, rmat = (rot_dense, R_DENSE) if kind == "dense" else (rot_wht, R_WHT)
