@@ -110,3 +110,23 @@ def scores_outlier8(q, enc, rotation, cb):
             side = enc.scale[b, g] * (enc.q8[b, g].astype(np.float64) @ q[b, h][enc.outliers[g]])
             out[b, h] = main + side
     return out
+
+
+def decode_attention_outlier8(q, enc_k, v_idx, v_norms, rot_k, rot_v, cb_k, cb_v, scale):
+    """Decode attention with outlier-8 keys ("TurboQuant 和 RotorQuant 的真相", chapter 1 formula):
+    out[b, h] = sum_t softmax_t(scale <q[b,h], k_hat[b,g,t]>) v_hat[b,g,t], g = h // ratio, with
+    k_hat the outlier-8 reconstruction (its logits are scores_outlier8) and v_hat = s_v R_V^T C_V[idx].
+    q [B, Hq, 128]; v_idx [B, Hkv, T, 128]; v_norms [B, Hkv, T].  Returns float64 [B, Hq, 128]."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, d = q.shape
+    hkv = v_idx.shape[1]
+    ratio = hq // hkv
+    logits = scale * scores_outlier8(q, enc_k, rot_k, cb_k)              # [B, Hq, T]
+    out = np.zeros((bsz, hq, d))
+    for b in range(bsz):
+        for g in range(hkv):
+            v_hat = decode_mse(v_idx[b, g], v_norms[b, g], rot_v, cb_v)
+            for h in range(g * ratio, (g + 1) * ratio):
+                p = np.exp(logits[b, h] - np.max(logits[b, h]))
+                out[b, h] = (p / np.sum(p)) @ v_hat
+    return out

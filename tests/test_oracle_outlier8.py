@@ -6,6 +6,7 @@ formulas, and the d = 128 distortion of the rest code."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import outlier8 as o8
@@ -121,3 +122,27 @@ def test_rest_code_has_the_d128_distortion():
     # keeping only the rest channels of the reconstruction never increases the error on them
     restricted = full * np.repeat(mask, 1024, axis=0)
     assert np.all(np.sum((xr - restricted) ** 2, axis=1) <= np.sum((xr - full) ** 2, axis=1) + 1e-12)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (3, 3), (8, 1)])
+def test_decode_attention_matches_torch_sdpa(hq, hkv):
+    # softmax(scale q K_hat^T) V_hat by torch's scaled_dot_product_attention (float64, CPU) on the
+    # outlier-8 reconstruction of the keys and the decoded values
+    d, B, T, scale = 128, 2, 37, 1 / np.sqrt(128)
+    rot, cbk, cbv = oracle.dense_rotation(d, 1), oracle.codebook(d, 3), oracle.codebook(d, 2)
+    x, outl = _keys(B, hkv, T, 8, seed=hq)
+    enc = o8.encode_outlier8(x, outl, rot, cbk)
+    v = np.random.default_rng(7).standard_normal((B, hkv, T, d))
+    ve = oracle.encode_mse(v.reshape(-1, d), rot, cbv)
+    vi, vn = ve.idx.reshape(B, hkv, T, d), ve.norms.reshape(B, hkv, T)
+    q = np.random.default_rng(8).standard_normal((B, hq, d))
+    got = o8.decode_attention_outlier8(q, enc, vi, vn, rot, rot, cbk, cbv, scale)
+    k_hat = o8.decode_outlier8(enc, rot, cbk)
+    ratio = hq // hkv
+    for b in range(B):
+        for g in range(hkv):
+            v_hat = torch.from_numpy(oracle.decode_mse(vi[b, g], vn[b, g], rot, cbv))
+            qs = torch.from_numpy(q[b, g * ratio:(g + 1) * ratio]).unsqueeze(1)             # [ratio, 1, d]
+            kh = torch.from_numpy(k_hat[b, g]).expand(ratio, -1, -1)
+            ref = torch.nn.functional.scaled_dot_product_attention(qs, kh, v_hat.expand(ratio, -1, -1), scale=scale)
+            np.testing.assert_allclose(got[b, g * ratio:(g + 1) * ratio], ref[:, 0].numpy(), rtol=0, atol=1e-12)
