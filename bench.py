@@ -422,6 +422,38 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         res.update({"bits": b, "encode_v_blocked_ms": enc_v_ms, "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6,
                     "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
                     "kv_positions_per_s": n / at_ms * 1e3})
+    elif name == "c4o8":
+        # Decode attention with outlier-8 keys on the attention workload (4 x 131072 tokens x 8 KV
+        # heads, 32 query heads): keys with their 8 outlier channels per head (largest mean square
+        # over the first 4096 tokens) as int8 and the rest at 3 bits, values at 2 bits.
+        cfg = wl.CONFIGS["c4"]
+        kbits, vbits, n_o = 3, 2, 8
+        n = cfg.B * cfg.hkv * cfg.T
+        rot = tq.make_rotation(cfg.d, 1)
+        cbk, cbv = tq.codebook(cfg.d, kbits), tq.codebook(cfg.d, vbits)
+        kb = wl.kv_keys(cfg)
+        xs = wl.bf16_bits_to_f32(kb[0, :, :4096]).astype(np.float64)
+        outl = np.argsort(-np.mean(xs * xs, axis=1), axis=1, kind="stable")[:, :n_o]
+        del xs
+        o = tq.make_outlier8(outl)
+        kx = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        del kb
+        enc_k_ms = _timed(lambda i: tq.encode_outlier8(kx, o, cbk, rot), 3, 1)
+        K = tq.encode_outlier8(kx, o, cbk, rot)
+        del kx
+        vx = torch.from_numpy(wl.kv_values(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        V = tq.encode(vx, vbits, "mse", cbv, rot, layout="blocked")
+        del vx
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        out = torch.empty((cfg.B, cfg.hq, cfg.d), device=dev)
+        ws = torch.empty(tq.decode_attn_outlier8_workspace(cfg.B, cfg.hq, cfg.hkv, cfg.T), dtype=torch.uint8,
+                         device=dev)
+        at_ms = _timed(lambda i: tq.decode_attn_outlier8(q, K, V, cfg.hkv, o, cbk, cbv, rot, rot, out=out, ws=ws),
+                       steps, warmup)
+        bytes_ = n * (cfg.d * kbits // 8 + 4 + n_o + 4) + n * (cfg.d * vbits // 8 + 4) + q.numel() * 4 + out.numel() * 4
+        res.update({"bits_k_rest": kbits, "outliers_per_head": n_o, "bits_v": vbits, "encode_k_ms": enc_k_ms,
+                    "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6, "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
+                    "kv_positions_per_s": n / at_ms * 1e3})
     elif name in ("decode", "decodeb4"):
         # Streaming decode over the long-context cache (batch 4, 8 KV heads, d = 128, GQA 4, K and V
         # MSE at b bits): prefill the cache up to T0 tokens per sequence, then per step append one
@@ -791,7 +823,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
-                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode", "c2o8",
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode", "c2o8", "c4o8",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "
                          "per-kernel timings only")

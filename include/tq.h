@@ -440,6 +440,24 @@ tq_status tq_scores_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t
                              tq_codebook_t cb, tq_rotation_t rot, float* scores_dev, void* ws_dev,
                              size_t ws_bytes, void* stream);
 
+/* Workspace bytes of tq_decode_attn_outlier8: tq_decode_attn's plus the queries' outlier
+ * components (B*Hq*16 fp32). */
+size_t tq_decode_attn_outlier8_workspace(int B, int Hq, int Hkv, int64_t T);
+/* Fused decode attention with outlier-8 keys ([RQ] chapter 1: softmax(q K^T / sqrt(d)) V, and the
+ * asymmetric K/V needs: K with outlier channels at 8 bits, V at fewer bits): as tq_decode_attn,
+ * with the logit of key t for query head h equal to scale * (s_t <R q_rest, C_K[idx_t]> +
+ * scale_t <q_O, q8_t>), q_rest and q_O taken through the outlier set of h's KV head.  K, q8_dev,
+ * scale_dev: outlier-8 keys of [B, Hkv, T] as written by tq_encode_outlier8 (K: ROWS, MSE, d = 128,
+ * bits = cb_k->b); V: TOKEN_BLOCKED MSE values of [B, Hkv, T]; out_dev [B, Hq, 128] fp32.
+ * (K bits, V bits) must be one of tq_decode_attn's pairs; GQA ratio 1, 2 or 4; T >= 1.  Errors:
+ * as tq_encode_outlier8 for the keys and handles, as tq_decode_attn otherwise; TQ_ENOMEM
+ * (workspace); TQ_EDEVICE for a bit pair without a kernel. */
+tq_status tq_decode_attn_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_outlier8_t o,
+                                  const tq_packed* K, const int8_t* q8_dev, const float* scale_dev,
+                                  const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
+                                  tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,
+                                  void* ws_dev, size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_search_topk needs for nq queries against n database vectors of length d
  * with k results per query (query operands, one chunk of scores, the running top-k). */
 size_t tq_search_workspace(int64_t nq, int64_t n, int d, int k);

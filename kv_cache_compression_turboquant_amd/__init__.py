@@ -24,6 +24,7 @@ __all__ = [
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
     "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
     "Outlier8", "make_outlier8", "encode_outlier8", "scores_outlier8", "scores_outlier8_workspace",
+    "decode_attn_outlier8", "decode_attn_outlier8_workspace",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -578,6 +579,37 @@ def scores_outlier8(q, K, Hkv, o, cb, rot, out=None, ws=None):
     d = rest.descriptor()
     check(lib().tq_scores_outlier8(_dptr(q), B, Hq, Hkv, T, o.ptr, ctypes.byref(d), _dptr(q8), _dptr(scale), cb.ptr,
                                    rot.ptr, _dptr(out), _dptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def decode_attn_outlier8_workspace(B, Hq, Hkv, T):
+    return int(lib().tq_decode_attn_outlier8_workspace(B, Hq, Hkv, T))
+
+
+def decode_attn_outlier8(q, K, V, Hkv, o, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws=None):
+    """softmax(scale <q, k_hat>) v_hat for q [B, Hq, 128] fp32 with outlier-8 keys K = (rest, q8,
+    scale) and blocked-layout values V, both laid out [B, Hkv, T]."""
+    torch = _torch()
+    _check_split_q("decode_attn_outlier8", q)
+    rest, q8, sc = K
+    B, Hq, d = q.shape
+    T = rest.n // max(B * Hkv, 1)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check_scores_out("decode_attn_outlier8", out, B * Hq * d)
+    if q8.dtype != torch.int8 or not q8.is_contiguous() or q8.numel() != rest.n * o.n_o:
+        raise TQError(1, f"decode_attn_outlier8: q8 must be contiguous int8 with {rest.n * o.n_o} elements")
+    _check_scores_out("decode_attn_outlier8", sc, rest.n)
+    if ws is None:
+        ws = torch.empty((max(decode_attn_outlier8_workspace(B, Hq, Hkv, T), 1),), dtype=torch.uint8, device=q.device)
+    _same_device("decode_attn_outlier8", q, out, ws, rest.idx, rest.norms, q8, sc, V.idx, V.norms)
+    kd, vd = rest.descriptor(), V.descriptor()
+    check(lib().tq_decode_attn_outlier8(_dptr(q), B, Hq, Hkv, T, o.ptr, ctypes.byref(kd), _dptr(q8), _dptr(sc),
+                                        ctypes.byref(vd), cb_k.ptr, cb_v.ptr, rot_k.ptr, rot_v.ptr,
+                                        ctypes.c_float(scale), _dptr(out), _dptr(ws), ws.numel() * ws.element_size(),
+                                        _stream()))
     return out
 
 

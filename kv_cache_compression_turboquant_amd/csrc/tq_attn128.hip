@@ -239,30 +239,40 @@ __device__ __forceinline__ float row16_partner(float v, int step) {
 
 // One 32-token step of a wave: the lane's key words and norms for both 16-token tiles, the
 // value norms, and the value chunks of octet g at coordinates 8 n .. 8 n + 7.
-template <int KB, int VB>
+template <int KB, int VB, int NO = 0>
 struct AttnStep {
   uint32_t kw[2][KB];
   float kn[2];
   float vn[2];
   uint32_t vw[2 * VB];
+  uint32_t o8[2][NO > 0 ? NO / 4 : 1];   // outlier-8 keys: each key's NO int8 values
+  float osc[2];                          // and their scale
 };
 
 // One sequence's keys, key norms, value norms (from its first row) and value blocks (from its
 // first 32-row block) as buffer resources: each load is the resource plus one 32-bit per-lane
 // offset, and rows outside the sequence read as zero (the kernel masks them).
 struct AttnBufs {
-  __amdgpu_buffer_rsrc_t k, kn, vn, v;
+  __amdgpu_buffer_rsrc_t k, kn, vn, v, q8, osc;
 };
 
-template <int KB, int VB>
-__device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0, int64_t blk_first, int64_t blk,
-                                               int nl, int g, AttnStep<KB, VB>& st) {
+template <int KB, int VB, int NO>
+__device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0, int64_t T, int64_t blk_first,
+                                               int64_t blk, int nl, int g, AttnStep<KB, VB, NO>& st) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    // may wrap below zero for the first block of a sequence that starts mid-block: such
-    // offsets are past the resource's end and read zero
-    const uint32_t r = (uint32_t)(blk * 32 + tt * 16 + nl - row0);
+    // Rows before the sequence (the first block of a sequence that starts mid-block) take row T,
+    // the first row past the resources' ends, so they read zero (the kernel masks them).  A
+    // wrapped negative offset would not do: the compiler may form the second tile's offset as the
+    // first tile's plus an immediate, and the range check then rejects the second tile's valid
+    // rows of lanes whose first-tile row lies before the sequence.
+    const int64_t rs = blk * 32 + tt * 16 + nl - row0;
+    const uint32_t r = rs < 0 ? (uint32_t)T : (uint32_t)rs;
     buffer_words<KB>(ab.k, r * (16u * KB) + (uint32_t)(4 * KB * g), st.kw[tt]);
+    if constexpr (NO > 0) {
+      buffer_words<NO / 4>(ab.q8, r * (uint32_t)NO, st.o8[tt]);
+      st.osc[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.osc, r * 4u, 0, 0));
+    }
     st.kn[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.kn, r * 4u, 0, 0));
     st.vn[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.vn, r * 4u, 0, 0));
   }
@@ -270,12 +280,15 @@ __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0,
   buffer_words<2 * VB>(ab.v, (vb * (128u * VB) + (uint32_t)(32 * g * VB + 2 * nl * VB)) * 4u, st.vw);
 }
 
-template <int KB, int VB>
+// NO > 0: outlier-8 keys (the rest channels' code in kidx / knorm, the outlier channels' int8
+// values in q8 and scales in oscale); the logit adds scale * <q_O, q8> in fp32, q_O from qo.
+template <int KB, int VB, int NO>
 __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t seq_stride,
-    CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part) {
+    CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part, const int8_t* __restrict__ q8,
+    const float* __restrict__ oscale, const float* __restrict__ qo) {
   // replicated decode tables (K up to 32 KB, V up to 16 KB) so that three blocks fit a CU
   constexpr int KC = table_copies<KB, true, TQ_ATTN_KBUDGET>();
   constexpr int VC = table_copies<VB, false, TQ_ATTN_VBUDGET>();
@@ -327,6 +340,19 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   ab.kn = buffer_rsrc(knorm + row0, (uint32_t)T * 4u);
   ab.vn = buffer_rsrc(vnorm + row0, (uint32_t)T * 4u);
   ab.v = buffer_rsrc(vidx + blk_first * (128 * VB), (uint32_t)(blk_end - blk_first) * (512u * VB));
+  // q_O of the block's query heads, read from LDS when a logit needs it (held in registers it
+  // would push the kernel past its register budget); lanes of heads past the ratio read head 0
+  // and compute a logit that is discarded
+  __shared__ __attribute__((aligned(16))) float qos[4][NO > 0 ? NO : 4];
+  if constexpr (NO > 0) {
+    ab.q8 = buffer_rsrc(q8 + row0 * NO, (uint32_t)T * (uint32_t)NO);
+    ab.osc = buffer_rsrc(oscale + row0, (uint32_t)T * 4u);
+    if (threadIdx.x < 4 * NO) {
+      const int hh = threadIdx.x / NO, k = threadIdx.x % NO;
+      qos[hh][k] = qo[((int64_t)b * Hq + kvh * ratio + (hh < ratio ? hh : 0)) * kOutlierMaxChannels + k];
+    }
+    __syncthreads();
+  }
 
   // A operand of the key product, in the split-slot order of decode_split_slot (each table
   // entry's centroids and remainders side by side): rows 0-3 (heads) carry the rotated query's
@@ -363,7 +389,7 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const AttnStep<KB, VB>& cur, const int64_t blk) {
+  auto step = [&](const AttnStep<KB, VB, NO>& cur, const int64_t blk) {
     float lg[2], svv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -374,7 +400,18 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
       f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j) d = mfma_f16(ak[j], decode_split_slot<KB, KC>(cur.kw[tt], j, ktabl), d);
-      const float mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
+      float mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
+      if constexpr (NO > 0) {
+        float o = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < NO / 4; ++k4) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qos[g][4 * k4]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o = fmaf((float)((int32_t)(cur.o8[tt][k4] << (24 - 8 * k)) >> 24), qv[k], o);
+        }
+        mine = fmaf(cur.osc[tt], o, mine);
+      }
       lg[tt] = (valid && g < ratio) ? mine * scale : -INFINITY;
     }
     // online softmax for head g
@@ -421,10 +458,10 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   // Batches of kAttnBatch steps: all their loads are issued before the first step is consumed
   // (straight-line code, so each wait is exact and no registers are copied between steps).
   for (int64_t b0 = wb; b0 < we; b0 += kAttnBatch) {
-    AttnStep<KB, VB> st[kAttnBatch];
+    AttnStep<KB, VB, NO> st[kAttnBatch];
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)
-      if (b0 + u < we) load_attn_step<KB, VB>(ab, row0, blk_first, b0 + u, nl, g, st[u]);
+      if (b0 + u < we) load_attn_step<KB, VB, NO>(ab, row0, T, blk_first, b0 + u, nl, g, st[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)
@@ -527,21 +564,31 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
   if (t < 128) out[(int64_t)hg * 128 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
 }
 
-template <int KB, int VB>
+// The outlier-8 query components follow the split partials in the workspace.
+size_t attn_partials_bytes(int B, int Hkv, int64_t T) {
+  const int64_t steps = T / 32 + 2;
+  const int64_t nsplit = (steps + kAttnMinSteps - 1) / kAttnMinSteps;  // the most splits a launch uses
+  return ((size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float) + 255) & ~(size_t)255;
+}
+
+template <int KB, int VB, int NO = 0>
 hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, const tq_packed* K,
                        const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
                        const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale, float* out,
-                       void* ws, hipStream_t st) {
-  const int ratio = Hq / Hkv;
+                       void* ws, hipStream_t st, const OutlierArgs* oa = nullptr, const int8_t* q8 = nullptr,
+                       const float* oscale = nullptr) {
   uint16_t* qws = static_cast<uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-  hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st);
+  float* qo = NO > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes + attn_partials_bytes(B, Hkv, T))
+                     : nullptr;
+  hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st, NO > 0 ? oa : nullptr, qo);
   if (e != hipSuccess) return e;
   static int per_cu = 0;
   if (per_cu == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_d128<KB, VB>, 256, 0) != hipSuccess || v <= 0) v = 2;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_d128<KB, VB, NO>, 256, 0) != hipSuccess || v <= 0)
+      v = 2;
     per_cu = v;
   }
   const int64_t seqs = (int64_t)B * Hkv;
@@ -552,8 +599,8 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, int64_
   spb = (spb + 3) / 4 * 4;
   if (spb < kAttnMinSteps) spb = kAttnMinSteps;
   const int nsplit = (int)((steps + spb - 1) / spb);
-  hipLaunchKernelGGL((k_attn_d128<KB, VB>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit, (int)spb,
-                     K->idx, K->norms, V->idx, V->norms, seq_stride, cbk, cbv, scale, part);
+  hipLaunchKernelGGL((k_attn_d128<KB, VB, NO>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit,
+                     (int)spb, K->idx, K->norms, V->idx, V->norms, seq_stride, cbk, cbv, scale, part, q8, oscale, qo);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(kCombineThreads), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
@@ -600,6 +647,28 @@ size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d) {
   const int64_t steps = T / 32 + 2;
   const int64_t nsplit = (steps + kAttnMinSteps - 1) / kAttnMinSteps;  // the most splits a launch uses
   return qbytes + (size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float);
+}
+
+size_t decode_attn_outlier8_workspace_bytes(int B, int Hq, int Hkv, int64_t T) {
+  const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
+  return qbytes + attn_partials_bytes(B, Hkv, T) + (size_t)B * Hq * kOutlierMaxChannels * sizeof(float);
+}
+
+hipError_t launch_decode_attn_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+                                       const tq_packed* K, const int8_t* q8, const float* oscale, const tq_packed* V,
+                                       const CodebookArgs& cbk, const CodebookArgs& cbv, const tq_rotation_s* rot_k,
+                                       const tq_rotation_s* rot_v, const OutlierArgs& oa, float scale, float* out,
+                                       void* ws, hipStream_t st) {
+#define TQ_ATTN_O8(KB, VB, NO)                                                                                     \
+  if (cbk.bits == KB && cbv.bits == VB && oa.no == NO)                                                            \
+    return attn_launch<KB, VB, NO>(q, B, Hq, Hkv, T, seq_stride, K, V, cbk, cbv, rot_k, rot_v, scale, out, ws, st, \
+                                   &oa, q8, oscale);
+#define TQ_ATTN_O8_ALL(KB, VB) TQ_ATTN_O8(KB, VB, 4) TQ_ATTN_O8(KB, VB, 8) TQ_ATTN_O8(KB, VB, 16)
+  TQ_ATTN_O8_ALL(3, 2) TQ_ATTN_O8_ALL(3, 3) TQ_ATTN_O8_ALL(2, 2) TQ_ATTN_O8_ALL(4, 2) TQ_ATTN_O8_ALL(4, 4)
+  TQ_ATTN_O8_ALL(2, 4) TQ_ATTN_O8_ALL(4, 3) TQ_ATTN_O8_ALL(1, 1) TQ_ATTN_O8_ALL(2, 3) TQ_ATTN_O8_ALL(3, 4)
+#undef TQ_ATTN_O8_ALL
+#undef TQ_ATTN_O8
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_attn_strided(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,

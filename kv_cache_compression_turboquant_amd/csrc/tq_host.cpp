@@ -1520,3 +1520,42 @@ tq_status tq_scores_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t
                                                  outlier8_args(o, T), scores_dev, ws_dev, as_stream(stream)),
                       fn);
 }
+
+size_t tq_decode_attn_outlier8_workspace(int B, int Hq, int Hkv, int64_t T) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || T < 0) return 0;
+  return tq::decode_attn_outlier8_workspace_bytes(B, Hq, Hkv, T);
+}
+
+tq_status tq_decode_attn_outlier8(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_outlier8_t o,
+                                  const tq_packed* K, const int8_t* q8_dev, const float* scale_dev, const tq_packed* V,
+                                  tq_codebook_t cb_k, tq_codebook_t cb_v, tq_rotation_t rot_k, tq_rotation_t rot_v,
+                                  float scale, float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  static const char* fn = "tq_decode_attn_outlier8";
+  if (!V || !cb_v || !rot_v) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (T < 1) return fail(TQ_EINVAL, "%s: attention over an empty cache (T=%lld)", fn, (long long)T);
+  if (T > kMaxSeqTokens)
+    return fail(TQ_EUNSUPPORTED, "%s: %lld tokens per sequence exceed %lld", fn, (long long)T, (long long)kMaxSeqTokens);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0)
+    return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  const int ratio = Hq / Hkv;
+  if (ratio != 1 && ratio != 2 && ratio != 4) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not in {1, 2, 4}", fn, ratio);
+  tq_status st = check_outlier8_keys(B, Hkv, T, o, cb_k, rot_k, K, fn);
+  if (st != TQ_OK) return st;
+  if (rot_v->d != tq::kFragD || cb_v->d != tq::kFragD) return fail(TQ_ESHAPE, "%s: V handles need d=128", fn);
+  st = check_packed(V, tq::kFragD, cb_v->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED) return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout", fn);
+  if (V->n != (int64_t)B * Hkv * T)
+    return fail(TQ_ESHAPE, "%s: V->n=%lld, B*Hkv*T=%lld", fn, (long long)V->n, (long long)B * Hkv * T);
+  if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv above 65535", fn);
+  if ((int64_t)B * Hq == 0) return ok();
+  if (!q_dev || !out_dev || !q8_dev || !scale_dev) return fail(TQ_EINVAL, "%s: null q, out, q8 or scale", fn);
+  if (reinterpret_cast<uintptr_t>(q8_dev) % 16 != 0) return fail(TQ_EINVAL, "%s: q8 must be 16-byte aligned", fn);
+  const size_t need = tq::decode_attn_outlier8_workspace_bytes(B, Hq, Hkv, T);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_decode_attn_outlier8(q_dev, B, Hq, Hkv, T, T, K, q8_dev, scale_dev, V, cb_k->args,
+                                                      cb_v->args, rot_k, rot_v, outlier8_args(o, T), scale, out_dev,
+                                                      ws_dev, as_stream(stream)),
+                      fn);
+}

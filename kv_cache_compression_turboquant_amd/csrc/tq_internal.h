@@ -183,6 +183,14 @@ hipError_t launch_qprep128(const float* q, int B, int Hq, int Hkv, const float* 
 hipError_t launch_encode_outlier8(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
                                   const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st);
 size_t scores_outlier8_workspace_bytes(int B, int Hq);
+// Decode attention with outlier-8 keys (tq_attn128.hip): the workspace of launch_decode_attn
+// followed by qo.
+size_t decode_attn_outlier8_workspace_bytes(int B, int Hq, int Hkv, int64_t T);
+hipError_t launch_decode_attn_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
+                                       const tq_packed* K, const int8_t* q8, const float* oscale, const tq_packed* V,
+                                       const CodebookArgs& cbk, const CodebookArgs& cbv, const tq_rotation_s* rot_k,
+                                       const tq_rotation_s* rot_v, const OutlierArgs& oa, float scale, float* out,
+                                       void* ws, hipStream_t st);
 hipError_t launch_scores_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
                                   const tq_packed* K, const int8_t* q8, const float* oscale, const CodebookArgs& cb,
                                   const tq_rotation_s* rot, const OutlierArgs& oa, float* scores, void* ws,

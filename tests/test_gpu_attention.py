@@ -85,7 +85,10 @@ def _attn_case(dev, rot, B, hkv, hq, T, kb, vb):
 
 @pytest.mark.parametrize("B,hkv,hq,T,kb,vb", [
     (1, 2, 8, 1000, 2, 2), (2, 2, 8, 333, 4, 4), (1, 1, 4, 1, 2, 2), (1, 2, 2, 31, 3, 3),
-    (1, 4, 8, 33, 2, 4), (1, 1, 1, 5000, 2, 2), (2, 1, 4, 4097, 4, 2)])
+    (1, 4, 8, 33, 2, 4), (1, 1, 1, 5000, 2, 2), (2, 1, 4, 4097, 4, 2),
+    # sequences that start in the second half of a 32-token block (row offsets 154, 83 and 249):
+    # their first block's first 16-token tile lies wholly before the sequence
+    (2, 2, 2, 77, 2, 3), (2, 2, 4, 83, 3, 3)])
 def test_decode_attention_parity(dev, rot, B, hkv, hq, T, kb, vb):
     _attn_case(dev, rot, B, hkv, hq, T, kb, vb)
 

@@ -215,3 +215,52 @@ def test_outlier8_errors(dev, rot):
     with pytest.raises(tq.TQError) as e:
         tq.scores_outlier8(torch.zeros((1, 4, D), device=dev), K, 2, o, tq.codebook(D, 2), rot)   # bits
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("kb,vb,n_o,hq,hkv,T", [(3, 2, 8, 8, 2, 300), (4, 4, 16, 4, 2, 301), (2, 3, 4, 2, 2, 77),
+                                                (3, 3, 16, 4, 1, 1), (4, 2, 8, 4, 4, 64)])
+def test_decode_attn_outlier8_matches_oracle(dev, rot, kb, vb, n_o, hq, hkv, T):
+    B = 2
+    x, xt = _keys(B, hkv, T, seed=kb * 7 + n_o, dtype="bf16")
+    outl = _outliers(x, n_o)
+    o = tq.make_outlier8(outl)
+    cbk, cbv = tq.codebook(D, kb), tq.codebook(D, vb)
+    K = tq.encode_outlier8(xt.to(dev), o, cbk, rot)
+    vbits = wl.kv_tensor_bf16(B, hkv, T, D, seed=31, outlier_seed=21, scale_seed=None)
+    vt = torch.from_numpy(vbits.view(np.int16)).view(torch.bfloat16).reshape(-1, D).to(dev)
+    V = tq.encode(vt, vb, "mse", cbv, rot, layout="blocked")
+    q = wl.gaussian((B, hq, D), 41)
+    out = tq.decode_attn_outlier8(torch.from_numpy(q).to(dev), K, V, hkv, o, cbk, cbv, rot, rot)
+    torch.cuda.synchronize()
+    n = B * hkv * T
+    enc = _gpu_as_oracle(outl, *K, B, hkv, T, kb)
+    vidx = oracle.unpack_token_blocked(to_np_words(V.idx), n, D, vb).reshape(B, hkv, T, D)
+    vn = V.norms.cpu().numpy().astype(np.float64).reshape(B, hkv, T)
+    ocbv = oracle.codebook(D, vb)
+    ref = oracle.decode_attention_outlier8(q, enc, vidx, vn, R, R, oracle.codebook(D, kb), ocbv, 1 / np.sqrt(D))
+    got = out.cpu().numpy()
+    ratio = hq // hkv
+    for b in range(B):
+        for g in range(hkv):
+            vmax = np.max(np.linalg.norm(oracle.decode_mse(vidx[b, g], vn[b, g], R, ocbv), axis=1))
+            err = np.max(np.abs(got[b, g * ratio:(g + 1) * ratio] - ref[b, g * ratio:(g + 1) * ratio]))
+            assert err <= 1e-3 * vmax, (b, g, err, vmax)
+
+
+def test_decode_attn_outlier8_errors(dev, rot):
+    o = tq.make_outlier8(np.array([[1, 2, 3, 4], [5, 6, 7, 8]], dtype=np.int32))
+    cb = tq.codebook(D, 3)
+    x = torch.zeros((1, 2, 32, D), dtype=torch.bfloat16, device=dev)
+    K = tq.encode_outlier8(x, o, cb, rot)
+    V = tq.encode(x.reshape(-1, D), 3, "mse", cb, rot, layout="blocked")
+    with pytest.raises(tq.TQError) as e:
+        tq.decode_attn_outlier8(torch.zeros((1, 6, D), device=dev), K, V, 2, o, cb, cb, rot, rot)   # ratio 3
+    assert e.value.status == 3
+    with pytest.raises(tq.TQError) as e:
+        tq.decode_attn_outlier8(torch.zeros((1, 4, D), device=dev), K, V, 2, o, cb, cb, rot, rot,
+                                ws=torch.empty(64, dtype=torch.uint8, device=dev))
+    assert e.value.status == 4
+    Vr = tq.encode(x.reshape(-1, D), 3, "mse", cb, rot)                                         # rows layout
+    with pytest.raises(tq.TQError) as e:
+        tq.decode_attn_outlier8(torch.zeros((1, 4, D), device=dev), K, Vr, 2, o, cb, cb, rot, rot)
+    assert e.value.status == 3
