@@ -38,9 +38,9 @@ KERNEL_SOURCES = {
 # (encode kernel, score kernel) of each step workload, as the profiler names them
 HEADLINE_KERNELS = {
     "c3": ("k_encode_prod_d128<3, true, 2> (prod b=4, dense R, bf16 keys)",
-           "k_scores_d128<3, true, false> (prod, GQA 4)"),
-    "c2": ("k_encode_mse_d128<3, true, 2, 2> (MSE b=3, dense R, bf16 keys)",
-           "k_scores_d128<3, false, false> (MSE, GQA 4)"),
+           "k_scores_d128<3, true, false, 0> (prod, GQA 4)"),
+    "c2": ("k_encode_mse_d128<3, true, 2, 2, 0> (MSE b=3, dense R, bf16 keys)",
+           "k_scores_d128<3, false, false, 0> (MSE, GQA 4)"),
 }
 # name prefixes of those kernels in a rocprofv3 database (for the counter summary)
 PMC_KERNELS = {

@@ -441,8 +441,12 @@ __global__ __launch_bounds__(kScoreWaves * 64, TQ_SCORE_MINB) void k_scores_d128
   KeyTile<BITS, PROD, NO> ka[HB], kbt[HB];
   HalfScalars sa, sb;
   auto load_half = [&](KeyTile<BITS, PROD, NO> (&kt)[HB], HalfScalars& hs, int64_t tb) {
+    // the half's keys that lie inside both the sequence and the wave's own tiles: the loop's last
+    // prefetch runs past the wave's tiles, and those loads must neither read the next wave's keys
+    // nor cost traffic, so the range ends there (out-of-range loads read zero without memory access)
     const int64_t first = (tile0 + tb) * 16;
-    const int64_t rem = T - first;
+    int64_t rem = T - first;
+    if ((last - tb) * 16 < rem) rem = (last - tb) * 16;
     const uint32_t nk = rem > 0 ? (uint32_t)rem : 0u;
     const int64_t row = base_row + first;
     KeyBufs<PROD> h;
