@@ -266,7 +266,7 @@ __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0,
     // wrapped negative offset would not do: the compiler may form the second tile's offset as the
     // first tile's plus an immediate, and the range check then rejects the second tile's valid
     // rows of lanes whose first-tile row lies before the sequence.
-    const int64_t rs = blk * 32 + tt * 16 + nl - row0;
+    const int32_t rs = (int32_t)(blk * 32 - row0) + tt * 16 + nl;   // in [-31, T + 31]: T < 2^25
     const uint32_t r = rs < 0 ? (uint32_t)T : (uint32_t)rs;
     buffer_words<KB>(ab.k, r * (16u * KB) + (uint32_t)(4 * KB * g), st.kw[tt]);
     if constexpr (NO > 0) {
