@@ -501,15 +501,16 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "attn_hbm_frac": at_bytes / at_ms / 1e6 / HBM_PEAK_GBS})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_decode(cfg, b, t_cap, cpu_budget)
-    elif name in ("c2split", "c2split35"):
+    elif name in ("c2split", "c2split35", "c3split"):
         # Outlier-channel split codes on the KV-key workload (1 x 8 KV heads x 32768 tokens, 32 query
-        # heads): 2.5 bits per channel (outlier half 3 bits, rest 2) or 3.5 (4 and 3).  The 64
-        # outlier channels per head are those of largest mean square over the first 4096 tokens.
-        cfg = wl.CONFIGS["c2"]
-        bo, br = (3, 2) if name == "c2split" else (4, 3)
+        # heads): 2.5 bits per channel (outlier half 3 bits, rest 2) or 3.5 (4 and 3); c3split: 2.5
+        # bits on the prod workload's keys (16 x 8 KV heads x 16384 tokens).  The 64 outlier channels
+        # per head are those of largest mean square over the first 4096 tokens.
+        cfg = wl.CONFIGS["c3" if name == "c3split" else "c2"]
+        bo, br = (4, 3) if name == "c2split35" else (3, 2)
         n = cfg.B * cfg.hkv * cfg.T
         kb = wl.kv_keys(cfg)
-        xs = wl.bf16_bits_to_f32(kb[:, :, :4096]).astype(np.float64)
+        xs = wl.bf16_bits_to_f32(kb[:1, :, :4096]).astype(np.float64)
         outl = np.argsort(-np.mean(xs * xs, axis=(0, 2)), axis=1, kind="stable")[:, :64]
         del xs
         keys = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -823,7 +824,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
-                                                        "decodeb4", "peaks", "c2split", "c2split35", "c2splitdecode", "c2o8", "c4o8",
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c3split", "c2splitdecode", "c2o8", "c4o8",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "
                          "per-kernel timings only")

@@ -7,7 +7,7 @@
 // s <R q_half, C[idx]> in its own rotated domain.
 #include <type_traits>
 
-#include "tq_device.h"
+#include "tq_decode.h"
 #include "tq_split.h"
 
 namespace tq {
@@ -447,6 +447,214 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores_split_d128(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Split scores on the fp16 matrix cores.  Grid (key chunk, b * Hkv), 4 waves; a wave scores
+// tiles of 16 keys.  D = A B per 16-key tile with A = 16 query slots (rows 0-3: the rotated
+// query's fp16 hi part of 4 heads, rows 4-7 its lo part, rows 8-15 zero) and B = the 16 keys'
+// decoded centroids.  Each half's 64 coordinates are two 32-term instructions; lane (n, g) of
+// instruction s supplies coordinates 32 s + 8 g .. 32 s + 8 g + 7 of the half for key n: one
+// run of 8 B-bit indices, cut from two adjacent words by one funnel shift and decoded through the
+// half's replicated LDS table, so every lane decodes the same widths (no divergence between the
+// halves).  The two halves accumulate apart (their norms differ); s_o D_o + s_r D_r is then
+// reduced over the parts with the lane swaps of the single-code kernel, which leaves head g's
+// score of key n in lane (n, g).  Keys are read once for every query head of their KV head:
+// MULTI (more than 4 query heads per KV head) keeps the query operands of all groups of 4 heads
+// in LDS and runs the groups on the decoded keys.
+// ---------------------------------------------------------------------------------------
+constexpr int kSplitScoreWaves = 4;
+constexpr int kSplitTileBatch = 4;        // tiles loaded before any of them is scored
+constexpr int kSplitTableBudget = 16384;  // LDS bytes per half's decode table
+
+// Run s of lane group g in a half of B bits starts at bit (32 s + 8 g) B of the half's 2B-word
+// row.  The lane loads the two words from run_word on (never past the row: the last run lies in
+// the row's last word, so it is read as the high word of a pair) and shifts the pair right by
+// run_shift.
+template <int B>
+__device__ __forceinline__ uint32_t run_word(int s, int g) {
+  const uint32_t w = (uint32_t)((32 * s + 8 * g) * B) >> 5;
+  return w < 2u * B - 2u ? w : 2u * B - 2u;
+}
+template <int B>
+__device__ __forceinline__ uint32_t run_shift(int s, int g) {
+  return (uint32_t)((32 * s + 8 * g) * B) - 32u * run_word<B>(s, g);
+}
+__device__ __forceinline__ uint32_t pair_bits(uint32_t lo, uint32_t hi, uint32_t sh) {
+  return (uint32_t)((((uint64_t)hi << 32) | lo) >> sh);
+}
+
+// 8 indices of B bits in the low 8B bits of f, decoded into 8 fp16 centroids (one operand)
+// through the lane's copy of the table (addresses base + (field * stride | laneoff)).
+template <int B, int COPIES>
+__device__ __forceinline__ u32x4 decode_run(uint32_t f, const uint8_t* tab, uint32_t laneoff) {
+  using DT = DecodeTable<B, false, COPIES>;
+  constexpr uint32_t S = DT::STRIDE;
+  static_assert((S & (S - 1)) == 0, "field stride must be a power of two");
+  auto at = [&](uint32_t field) { return tab + ((field * S) | laneoff); };
+  u32x4 out;
+  if constexpr (B == 1) {
+    out = *reinterpret_cast<const u32x4*>(at(f & 0xffu));
+  } else if constexpr (B == 2) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(at(f & 0xffu));
+    const u32x2 b = *reinterpret_cast<const u32x2*>(at((f >> 8) & 0xffu));
+    out = u32x4{a[0], a[1], b[0], b[1]};
+  } else if constexpr (B == 3) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(at((f >> (6 * j)) & 63u));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = *reinterpret_cast<const uint32_t*>(at((f >> (8 * j)) & 0xffu));
+  }
+  return out;
+}
+
+// A key tile's share for lane (n, g): for each half and run the two words holding the run, and
+// the key's two norms.
+struct SplitTile {
+  uint32_t w[2][2][2];   // [half][run][lo, hi word]
+  float so, sr;
+};
+
+template <int BO, int BR, bool MULTI>
+__global__ __launch_bounds__(kSplitScoreWaves * 64, 2) void k_scores_split_mfma(
+    const float* __restrict__ qws, int Hq, int Hkv, int64_t T, int64_t seq_stride, int tiles_per_wave,
+    CodebookArgs cbo, CodebookArgs cbr, const uint32_t* __restrict__ idx_o, const float* __restrict__ norm_o,
+    const uint32_t* __restrict__ idx_r, const float* __restrict__ norm_r, float* __restrict__ scores) {
+  constexpr int TCO = table_copies<BO, false, kSplitTableBudget>();
+  constexpr int TCR = table_copies<BR, false, kSplitTableBudget>();
+  using DO = DecodeTable<BO, false, TCO>;
+  using DR = DecodeTable<BR, false, TCR>;
+  constexpr int WO = 2 * BO, WR = 2 * BR;   // words per half row
+  __shared__ __attribute__((aligned(16))) uint8_t tabo[DO::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tabr[DR::BYTES];
+  __shared__ _Float16 cent[2][16];
+  // MULTI: the query operands of every head of the KV head, [head][part][instruction][lane group]
+  __shared__ u32x4 qa[MULTI ? kSplitMaxRatio : 1][2][4][4];
+  const int ratio = Hq / Hkv;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int64_t hq_first = (int64_t)b * Hq + (int64_t)kvh * ratio;
+  if (threadIdx.x < 16) cent[0][threadIdx.x] = (_Float16)cbo.c[threadIdx.x];
+  else if (threadIdx.x < 32) cent[1][threadIdx.x - 16] = (_Float16)cbr.c[threadIdx.x - 16];
+  // The query operand of (head, part p, instruction i = 2 half + s, lane group g): coordinates
+  // 64 half + 32 s + 8 g .. + 7 of the head's rotated query, fp16 hi (p = 0) or lo (p = 1).
+  auto qfrag = [&](int head, int p, int i, int g) -> u32x4 {
+    const float* src = qws + (hq_first + head) * kSplitD + 64 * (i >> 1) + 32 * (i & 1) + 8 * g;
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = src[2 * k], x1 = src[2 * k + 1];
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 e0 = p ? (_Float16)(x0 - (float)h0) : h0;
+      const _Float16 e1 = p ? (_Float16)(x1 - (float)h1) : h1;
+      v[k] = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+    }
+    return v;
+  };
+  if constexpr (MULTI) {
+    for (int e = threadIdx.x; e < ratio * 32; e += blockDim.x) {
+      const int head = e >> 5, p = (e >> 4) & 1, i = (e >> 2) & 3, g = e & 3;
+      qa[head][p][i][g] = qfrag(head, p, i, g);
+    }
+  }
+  __syncthreads();
+  build_table<BO, TCO>(tabo, cent[0]);
+  build_table<BR, TCR>(tabr, cent[1]);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 15, g = lane >> 4;
+  const uint32_t lofo = (uint32_t)(lane % TCO) * DO::EB, lofr = (uint32_t)(lane % TCR) * DR::EB;
+  const int64_t base_row = (int64_t)bg * seq_stride;
+  const int64_t ntiles_seq = (T + 15) / 16;
+  const int64_t tile0 = ((int64_t)blockIdx.x * kSplitScoreWaves + wave) * tiles_per_wave;
+  int64_t last = tiles_per_wave;
+  if (ntiles_seq - tile0 < last) last = ntiles_seq - tile0;
+  // this (batch, kv head)'s score rows, ratio x T floats (the host bounds Hq * T * 4 < 4 GB)
+  const __amdgpu_buffer_rsrc_t sbuf = buffer_rsrc(scores + hq_first * T, (uint32_t)ratio * (uint32_t)T * 4u);
+
+  // query operands of head group 0 in registers (single group) -- row n = 4 part + head
+  const int hl = nl & 3, part = nl >> 2;
+  u32x4 a0[4];
+  if constexpr (!MULTI) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a0[i] = (part < 2 && hl < ratio) ? qfrag(hl, part, i, g) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // the lane's word offsets within a key's half row, per run
+  const uint32_t wio0 = run_word<BO>(0, g), wio1 = run_word<BO>(1, g);
+  const uint32_t wir0 = run_word<BR>(0, g), wir1 = run_word<BR>(1, g);
+  const uint32_t sho0 = run_shift<BO>(0, g), sho1 = run_shift<BO>(1, g);
+  const uint32_t shr0 = run_shift<BR>(0, g), shr1 = run_shift<BR>(1, g);
+
+  for (int64_t tb = 0; tb < last; tb += kSplitTileBatch) {
+    // resources based at the batch's first key and ending at the wave's last tile (or the
+    // sequence's end): loads past them read zero without touching memory
+    const int64_t first = (tile0 + tb) * 16;
+    int64_t rem = T - first;
+    if ((last - tb) * 16 < rem) rem = (last - tb) * 16;
+    const uint32_t nk = rem > 0 ? (uint32_t)rem : 0u;
+    const int64_t row = base_row + first;
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(idx_o + row * WO, nk * (4u * WO));
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(idx_r + row * WR, nk * (4u * WR));
+    const __amdgpu_buffer_rsrc_t no = buffer_rsrc(norm_o + row, nk * 4u);
+    const __amdgpu_buffer_rsrc_t nr = buffer_rsrc(norm_r + row, nk * 4u);
+    SplitTile kt[kSplitTileBatch];
+#pragma unroll
+    for (int u = 0; u < kSplitTileBatch; ++u) {
+      const uint32_t k = (uint32_t)(16 * u + nl);
+      const u32x2 o0 = __builtin_amdgcn_raw_buffer_load_b64(ro, (k * WO + wio0) * 4u, 0, 0);
+      const u32x2 o1 = __builtin_amdgcn_raw_buffer_load_b64(ro, (k * WO + wio1) * 4u, 0, 0);
+      const u32x2 r0 = __builtin_amdgcn_raw_buffer_load_b64(rr, (k * WR + wir0) * 4u, 0, 0);
+      const u32x2 r1 = __builtin_amdgcn_raw_buffer_load_b64(rr, (k * WR + wir1) * 4u, 0, 0);
+      kt[u].w[0][0][0] = o0[0]; kt[u].w[0][0][1] = o0[1];
+      kt[u].w[0][1][0] = o1[0]; kt[u].w[0][1][1] = o1[1];
+      kt[u].w[1][0][0] = r0[0]; kt[u].w[1][0][1] = r0[1];
+      kt[u].w[1][1][0] = r1[0]; kt[u].w[1][1][1] = r1[1];
+      kt[u].so = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(no, k * 4u, 0, 0));
+      kt[u].sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(nr, k * 4u, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kSplitTileBatch; ++u) {
+      if (tb + u >= last) break;
+      const SplitTile& c = kt[u];
+      u32x4 bo[2], br[2];
+      bo[0] = decode_run<BO, TCO>(pair_bits(c.w[0][0][0], c.w[0][0][1], sho0), tabo, lofo);
+      bo[1] = decode_run<BO, TCO>(pair_bits(c.w[0][1][0], c.w[0][1][1], sho1), tabo, lofo);
+      br[0] = decode_run<BR, TCR>(pair_bits(c.w[1][0][0], c.w[1][0][1], shr0), tabr, lofr);
+      br[1] = decode_run<BR, TCR>(pair_bits(c.w[1][1][0], c.w[1][1][1], shr1), tabr, lofr);
+      const uint32_t t = (uint32_t)(tile0 + tb + u) * 16u + (uint32_t)nl;
+      const bool valid = t < (uint32_t)T;
+      const int groups = MULTI ? (ratio + 3) / 4 : 1;
+      for (int hg = 0; hg < groups; ++hg) {
+        u32x4 a[4];
+        if constexpr (MULTI) {
+          const int head = 4 * hg + hl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = (part < 2 && head < ratio) ? qa[head][part][i][g] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = a0[i];
+        }
+        f32x4 ao = f32x4{0.f, 0.f, 0.f, 0.f}, ar = f32x4{0.f, 0.f, 0.f, 0.f};
+        ao = mfma_f16(a[0], bo[0], ao);
+        ao = mfma_f16(a[1], bo[1], ao);
+        ar = mfma_f16(a[2], br[0], ar);
+        ar = mfma_f16(a[3], br[1], ar);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(c.so, ao[r], c.sr * ar[r]);
+        const float mine = reduce_parts(v[0], v[1], v[2], v[3]);
+        const int h = 4 * hg + g;
+        if (valid && h < ratio)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), sbuf,
+                                                ((uint32_t)h * (uint32_t)T + t) * 4u, 0, 0);
+      }
+    }
+  }
+}
+
 // Calls f(IC<BO>, IC<BR>) for bit widths 1..4 each.
 template <int BO, typename F>
 hipError_t with_br(int br, F&& f) {
@@ -511,15 +719,46 @@ hipError_t launch_qprep_split(const float* q, int B, int Hq, int Hkv, const int3
   return hipGetLastError();
 }
 
+#ifndef TQ_SPLIT_SCORE_MFMA
+#define TQ_SPLIT_SCORE_MFMA 1
+#endif
+#ifndef TQ_SPLIT_BLOCKS_PER_CU
+#define TQ_SPLIT_BLOCKS_PER_CU 4
+#endif
+
 hipError_t launch_scores_split(const float* qws, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, int bo, int br,
                                const CodebookArgs& cbo, const CodebookArgs& cbr, const uint32_t* idx_o,
                                const float* norm_o, const uint32_t* idx_r, const float* norm_r, float* scores,
                                hipStream_t st) {
   if ((int64_t)B * Hkv == 0 || T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((T + kScoreThreads - 1) / kScoreThreads), (unsigned)((int64_t)B * Hkv));
+  if (!TQ_SPLIT_SCORE_MFMA) {
+    const dim3 grid((unsigned)((T + kScoreThreads - 1) / kScoreThreads), (unsigned)((int64_t)B * Hkv));
+    return with_bits(bo, br, [&](auto o, auto r) -> hipError_t {
+      hipLaunchKernelGGL((k_scores_split_d128<decltype(o)::value, decltype(r)::value>), grid, dim3(kScoreThreads), 0,
+                         st, qws, Hq, Hkv, T, seq_stride, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
+      return hipGetLastError();
+    });
+  }
+  // grid: TQ_SPLIT_BLOCKS_PER_CU blocks per CU over all sequences, whole batches of tiles per
+  // wave (each block builds two decode tables first, so a block wants tiles enough to amortise them)
+  const int64_t tiles = (T + 15) / 16;
+  const int64_t seqs = (int64_t)B * Hkv;
+  const int64_t target = (int64_t)num_cus() * TQ_SPLIT_BLOCKS_PER_CU;
+  int64_t tpw = (tiles * seqs + target * kSplitScoreWaves - 1) / (target * kSplitScoreWaves);
+  tpw = (tpw + kSplitTileBatch - 1) / kSplitTileBatch * kSplitTileBatch;
+  if (tpw < kSplitTileBatch) tpw = kSplitTileBatch;
+  if (tpw > 256) tpw = 256;
+  const int64_t chunks = (tiles + tpw * kSplitScoreWaves - 1) / (tpw * kSplitScoreWaves);
+  const dim3 grid((unsigned)chunks, (unsigned)seqs);
+  const bool multi = Hq / Hkv > 4;
   return with_bits(bo, br, [&](auto o, auto r) -> hipError_t {
-    hipLaunchKernelGGL((k_scores_split_d128<decltype(o)::value, decltype(r)::value>), grid, dim3(kScoreThreads), 0, st,
-                       qws, Hq, Hkv, T, seq_stride, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
+    constexpr int BO = decltype(o)::value, BR = decltype(r)::value;
+    if (multi)
+      hipLaunchKernelGGL((k_scores_split_mfma<BO, BR, true>), grid, dim3(kSplitScoreWaves * 64), 0, st, qws, Hq, Hkv, T,
+                         seq_stride, (int)tpw, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
+    else
+      hipLaunchKernelGGL((k_scores_split_mfma<BO, BR, false>), grid, dim3(kSplitScoreWaves * 64), 0, st, qws, Hq, Hkv,
+                         T, seq_stride, (int)tpw, cbo, cbr, idx_o, norm_o, idx_r, norm_r, scores);
     return hipGetLastError();
   });
 }
