@@ -35,14 +35,15 @@ from .quantizer import (nearest_index, pack_bits, unpack_bits, pack_token_blocke
 from .attention import decode_attention, prefill_attention, topk
 from .kv_cache import (cache_rows, append_rows_mse, append_rows_prod, assign_token_blocked,
                        append_token_blocked_mse, live_rows)
-from .split import channel_order, encode_split, decode_split, scores_split, EncodedSplit
+from .split import (channel_order, encode_split, decode_split, scores_split, decode_attention_split,
+                    EncodedSplit)
 from .outlier8 import (int8_absmax, rest_mask, encode_outlier8, decode_outlier8, scores_outlier8,
                        decode_attention_outlier8, EncodedOutlier8)
 
 __all__ = [
     "int8_absmax", "rest_mask", "encode_outlier8", "decode_outlier8", "scores_outlier8", "EncodedOutlier8",
     "decode_attention_outlier8",
-    "channel_order", "encode_split", "decode_split", "scores_split", "EncodedSplit",
+    "channel_order", "encode_split", "decode_split", "scores_split", "decode_attention_split", "EncodedSplit",
     "splitmix64", "uniform53", "gaussian", "rademacher",
     "dense_rotation", "wht_rotation", "block_wht_rotation", "sylvester_hadamard", "rotation_from_matrix",
     "Codebook", "lloyd_max_points", "coordinate_weights", "codebook", "codebook_from_values",

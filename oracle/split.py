@@ -89,3 +89,23 @@ def scores_split(q, enc, rot_o, rot_r, cb_o, cb_r):
     ratio = q.shape[1] // xhat.shape[1]
     return np.stack([xhat[:, h // ratio] @ q[:, h][..., None] for h in range(q.shape[1])],
                     axis=1)[..., 0]
+
+
+def decode_attention_split(q, enc, v_idx, v_norms, rot_o, rot_r, rot_v, cb_o, cb_r, cb_v, scale):
+    """Decode attention with split-coded keys ("TurboQuant 和 RotorQuant 的真相", chapter 1 formula):
+    out[b, h] = sum_t softmax_t(scale <q[b,h], k_hat[b,g,t]>) v_hat[b,g,t], g = h // ratio, with
+    k_hat the split reconstruction (its logits are scores_split) and v_hat = s_v R_V^T C_V[idx].
+    q [B, Hq, d]; v_idx [B, Hkv, T, d]; v_norms [B, Hkv, T].  Returns float64 [B, Hq, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, d = q.shape
+    hkv = v_idx.shape[1]
+    ratio = hq // hkv
+    logits = scale * scores_split(q, enc, rot_o, rot_r, cb_o, cb_r)      # [B, Hq, T]
+    out = np.zeros((bsz, hq, d))
+    for b in range(bsz):
+        for g in range(hkv):
+            v_hat = decode_mse(v_idx[b, g], v_norms[b, g], rot_v, cb_v)
+            for h in range(g * ratio, (g + 1) * ratio):
+                p = np.exp(logits[b, h] - np.max(logits[b, h]))
+                out[b, h] = (p / np.sum(p)) @ v_hat
+    return out

@@ -3,6 +3,7 @@ channel relabelling, the score in the two rotated domains element by element, an
 distortion against the exact value of its codebook."""
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -122,3 +123,30 @@ def test_part_distortion_matches_the_codebook(bo, br):
         assert abs(m - _dmse_quadrature(M, b)) < 4 * se
     tot = np.sum((x - xh) ** 2) / np.sum(x ** 2)
     assert _dmse_quadrature(M, bo) < tot < _dmse_quadrature(M, br)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (2, 2), (8, 1)])
+def test_decode_attention_matches_torch_sdpa(hq, hkv):
+    # softmax(scale q K_hat^T) V_hat by torch's scaled_dot_product_attention (float64, CPU) on the
+    # split reconstruction of the keys and the decoded values
+    d, m, B, T, scale = 16, 8, 2, 29, 0.37
+    rng = np.random.default_rng(hq + 10 * hkv)
+    x = rng.standard_normal((B, hkv, T, d)) * rng.lognormal(0, 0.5, (B, hkv, T, 1))
+    outl = np.stack([rng.permutation(d)[:m] for _ in range(hkv)])
+    ro, rr, rv = oracle.dense_rotation(m, 3), oracle.dense_rotation(m, 4), oracle.dense_rotation(d, 1)
+    co, cr, cv = oracle.codebook(m, 3), oracle.codebook(m, 2), oracle.codebook(d, 2)
+    enc = oracle.encode_split(x, outl, ro, rr, co, cr)
+    v = rng.standard_normal((B, hkv, T, d))
+    ve = oracle.encode_mse(v.reshape(-1, d), rv, cv)
+    vi, vn = ve.idx.reshape(B, hkv, T, d), ve.norms.reshape(B, hkv, T)
+    q = rng.standard_normal((B, hq, d))
+    got = oracle.decode_attention_split(q, enc, vi, vn, ro, rr, rv, co, cr, cv, scale)
+    k_hat = oracle.decode_split(enc, ro, rr, co, cr)
+    ratio = hq // hkv
+    for b in range(B):
+        for g in range(hkv):
+            v_hat = torch.from_numpy(oracle.decode_mse(vi[b, g], vn[b, g], rv, cv))
+            qs = torch.from_numpy(q[b, g * ratio:(g + 1) * ratio]).unsqueeze(1)
+            kh = torch.from_numpy(k_hat[b, g]).expand(ratio, -1, -1)
+            ref = torch.nn.functional.scaled_dot_product_attention(qs, kh, v_hat.expand(ratio, -1, -1), scale=scale)
+            np.testing.assert_allclose(got[b, g * ratio:(g + 1) * ratio], ref[:, 0].numpy(), rtol=0, atol=1e-12)
