@@ -454,6 +454,36 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         res.update({"bits_k_rest": kbits, "outliers_per_head": n_o, "bits_v": vbits, "encode_k_ms": enc_k_ms,
                     "attn_ms": at_ms, "attn_gbs": bytes_ / at_ms / 1e6, "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
                     "kv_positions_per_s": n / at_ms * 1e3})
+    elif name == "c4split":
+        # Decode attention with split keys on the attention workload (4 x 131072 tokens x 8 KV heads,
+        # 32 query heads): keys at 2.5 bits per channel (outlier half 3 bits, rest 2; the 64 channels
+        # of largest mean square over the first 4096 tokens), values at 2 bits.
+        cfg = wl.CONFIGS["c4"]
+        bo, br, vbits = 3, 2, 2
+        n = cfg.B * cfg.hkv * cfg.T
+        kb = wl.kv_keys(cfg)
+        xs = wl.bf16_bits_to_f32(kb[:1, :, :4096]).astype(np.float64)
+        outl = np.argsort(-np.mean(xs * xs, axis=(0, 2)), axis=1, kind="stable")[:, :64]
+        del xs
+        sp = tq.make_split(outl)
+        rot_o, rot_r, rot_v = tq.make_rotation(64, 3), tq.make_rotation(64, 4), tq.make_rotation(cfg.d, 1)
+        cbo, cbr, cbv = tq.codebook(64, bo), tq.codebook(64, br), tq.codebook(cfg.d, vbits)
+        kx = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        del kb
+        K = tq.encode_split(kx, sp, cbo, cbr, rot_o, rot_r)
+        del kx
+        vx = torch.from_numpy(wl.kv_values(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        V = tq.encode(vx, vbits, "mse", cbv, rot_v, layout="blocked")
+        del vx
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        out = torch.empty((cfg.B, cfg.hq, cfg.d), device=dev)
+        ws = torch.empty(tq.decode_attn_split_workspace(cfg.B, cfg.hq, cfg.hkv, cfg.T), dtype=torch.uint8, device=dev)
+        at_ms = _timed(lambda i: tq.decode_attn_split(q, K, V, cfg.hkv, sp, cbo, cbr, cbv, rot_o, rot_r, rot_v, out=out,
+                                                      ws=ws), steps, warmup)
+        bytes_ = n * (8 * (bo + br) + 8) + n * (cfg.d * vbits // 8 + 4) + q.numel() * 4 + out.numel() * 4
+        res.update({"bits_outlier": bo, "bits_rest": br, "bits_v": vbits, "attn_ms": at_ms,
+                    "attn_gbs": bytes_ / at_ms / 1e6, "attn_hbm_frac": bytes_ / at_ms / 1e6 / HBM_PEAK_GBS,
+                    "kv_positions_per_s": n / at_ms * 1e3})
     elif name in ("decode", "decodeb4"):
         # Streaming decode over the long-context cache (batch 4, 8 KV heads, d = 128, GQA 4, K and V
         # MSE at b bits): prefill the cache up to T0 tokens per sequence, then per step append one
@@ -824,7 +854,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
-                                                        "decodeb4", "peaks", "c2split", "c2split35", "c3split", "c2splitdecode", "c2o8", "c4o8",
+                                                        "decodeb4", "peaks", "c2split", "c2split35", "c3split", "c2splitdecode", "c2o8", "c4o8", "c4split",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "
                          "per-kernel timings only")

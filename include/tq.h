@@ -394,6 +394,22 @@ tq_status tq_scores_split_cache(const float* q_dev, int B, int Hq, int Hkv, int6
                                 tq_rotation_t rot_r, float* scores_dev, void* ws_dev, size_t ws_bytes,
                                 void* stream);
 
+/* Workspace bytes of tq_decode_attn_split (as tq_decode_attn's at d = 128). */
+size_t tq_decode_attn_split_workspace(int B, int Hq, int Hkv, int64_t T);
+/* Fused decode attention with split-coded keys ([RQ] chapter 1 formula and the asymmetric K/V
+ * needs): as tq_decode_attn, with the logit of key t for query head h equal to scale * (the sum
+ * over the two halves of s_half <R_half q_half, C_half[idx_half]>), q_half gathered through the
+ * channel order of h's KV head.  K_o, K_r: split keys of [B, Hkv, T] as written by
+ * tq_encode_split; V: TOKEN_BLOCKED MSE values of [B, Hkv, T] with d = 128; out_dev [B, Hq, 128]
+ * fp32.  (b_o, b_r) must be (3, 2) or (4, 3) (2.5 and 3.5 bits per channel) and b_v 2, 3 or 4;
+ * GQA ratio 1, 2 or 4; T >= 1.  Errors: as tq_scores_split for the keys and handles, as
+ * tq_decode_attn otherwise; TQ_EUNSUPPORTED for other bit widths. */
+tq_status tq_decode_attn_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
+                               const tq_packed* K_o, const tq_packed* K_r, const tq_packed* V,
+                               tq_codebook_t cb_o, tq_codebook_t cb_r, tq_codebook_t cb_v,
+                               tq_rotation_t rot_o, tq_rotation_t rot_r, tq_rotation_t rot_v, float scale,
+                               float* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* ---- outlier channels at 8 bits (d = 128) --------------------------------------------
  * [RQ] the asymmetric needs of K and V: one practice keeps a key's outlier channels at 8 bits
  * and codes the other channels at 3.  The page fixes neither the outlier set nor the 8-bit

@@ -24,7 +24,7 @@ __all__ = [
     "Split", "make_split", "encode_split", "scores_split", "scores_split_workspace", "alloc_split_cache",
     "cache_append_split", "scores_split_cache", "peak_read", "peak_copy", "peak_mfma",
     "Outlier8", "make_outlier8", "encode_outlier8", "scores_outlier8", "scores_outlier8_workspace",
-    "decode_attn_outlier8", "decode_attn_outlier8_workspace",
+    "decode_attn_outlier8", "decode_attn_outlier8_workspace", "decode_attn_split", "decode_attn_split_workspace",
     "host_splitmix64", "host_gaussian", "host_codebook", "host_rotation", "host_qjl_matrix",
 ]
 
@@ -610,6 +610,33 @@ def decode_attn_outlier8(q, K, V, Hkv, o, cb_k, cb_v, rot_k, rot_v, scale=None, 
                                         ctypes.byref(vd), cb_k.ptr, cb_v.ptr, rot_k.ptr, rot_v.ptr,
                                         ctypes.c_float(scale), _dptr(out), _dptr(ws), ws.numel() * ws.element_size(),
                                         _stream()))
+    return out
+
+
+def decode_attn_split_workspace(B, Hq, Hkv, T):
+    return int(lib().tq_decode_attn_split_workspace(B, Hq, Hkv, T))
+
+
+def decode_attn_split(q, K, V, Hkv, split, cb_o, cb_r, cb_v, rot_o, rot_r, rot_v, scale=None, out=None, ws=None):
+    """softmax(scale <q, k_hat>) v_hat for q [B, Hq, 128] fp32 with split keys K = (K_o, K_r) and
+    blocked-layout values V, both laid out [B, Hkv, T]."""
+    torch = _torch()
+    _check_split_q("decode_attn_split", q)
+    B, Hq, d = q.shape
+    T = K[0].n // max(B * Hkv, 1)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check_scores_out("decode_attn_split", out, B * Hq * d)
+    if ws is None:
+        ws = torch.empty((max(decode_attn_split_workspace(B, Hq, Hkv, T), 1),), dtype=torch.uint8, device=q.device)
+    _same_device("decode_attn_split", q, out, ws, K[0].idx, K[0].norms, K[1].idx, K[1].norms, V.idx, V.norms)
+    do, dr, dv = K[0].descriptor(), K[1].descriptor(), V.descriptor()
+    check(lib().tq_decode_attn_split(_dptr(q), B, Hq, Hkv, T, split.ptr, ctypes.byref(do), ctypes.byref(dr),
+                                     ctypes.byref(dv), cb_o.ptr, cb_r.ptr, cb_v.ptr, rot_o.ptr, rot_r.ptr, rot_v.ptr,
+                                     ctypes.c_float(scale), _dptr(out), _dptr(ws), ws.numel() * ws.element_size(),
+                                     _stream()))
     return out
 
 

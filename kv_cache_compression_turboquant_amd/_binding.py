@@ -109,6 +109,9 @@ SIGNATURES = {
     "tq_encode_outlier8": (_I, [_P, _I, _I, _I, _I64, _P, _P, _P, ctypes.POINTER(tq_packed), _P, _P, _P]),
     "tq_scores_outlier8_workspace": (_SZ, [_I, _I]),
     "tq_decode_attn_outlier8_workspace": (_SZ, [_I, _I, _I, _I64]),
+    "tq_decode_attn_split_workspace": (_SZ, [_I, _I, _I, _I64]),
+    "tq_decode_attn_split": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), ctypes.POINTER(tq_packed),
+                                  ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _SZ, _P]),
     "tq_decode_attn_outlier8": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), _P, _P,
                                      ctypes.POINTER(tq_packed), _P, _P, _P, _P, ctypes.c_float, _P, _P, _SZ, _P]),
     "tq_scores_outlier8": (_I, [_P, _I, _I, _I, _I64, _P, ctypes.POINTER(tq_packed), _P, _P, _P, _P, _P, _P, _SZ,

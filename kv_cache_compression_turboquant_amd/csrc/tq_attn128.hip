@@ -3,6 +3,7 @@
 // the inverse rotation.
 #include "tq_cache.h"
 #include "tq_decode.h"
+#include "tq_split.h"
 
 namespace tq {
 namespace {
@@ -247,16 +248,31 @@ struct AttnStep {
   uint32_t vw[2 * VB];
   uint32_t o8[2][NO > 0 ? NO / 4 : 1];   // outlier-8 keys: each key's NO int8 values
   float osc[2];                          // and their scale
+  uint32_t kwr[2][2];                    // split keys: the lane's two-word window of the rest half
+  float knr[2];                          // and the rest half's norm (kw / kn: the outlier half)
 };
 
 // One sequence's keys, key norms, value norms (from its first row) and value blocks (from its
 // first 32-row block) as buffer resources: each load is the resource plus one 32-bit per-lane
 // offset, and rows outside the sequence read as zero (the kernel masks them).
 struct AttnBufs {
-  __amdgpu_buffer_rsrc_t k, kn, vn, v, q8, osc;
+  __amdgpu_buffer_rsrc_t k, kn, vn, v, q8, osc, kr, knr;
 };
 
-template <int KB, int VB, int NO>
+// Split keys: lane group g takes coordinates 16 g .. 16 g + 15 of each half (64 coordinates of B
+// bits, 2B words per row).  The lane reads a two-word window from split_word on (never past the
+// row) and shifts it right by split_shift, which leaves its 16 indices at bit 0.
+template <int B>
+__device__ __forceinline__ uint32_t split_word(int g) {
+  const uint32_t w = (uint32_t)(16 * g * B) >> 5;
+  return w < 2u * B - 2u ? w : 2u * B - 2u;
+}
+template <int B>
+__device__ __forceinline__ uint32_t split_shift(int g) {
+  return (uint32_t)(16 * g * B) - 32u * split_word<B>(g);
+}
+
+template <int KB, int VB, int NO, int BR>
 __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0, int64_t T, int64_t blk_first,
                                                int64_t blk, int nl, int g, AttnStep<KB, VB, NO>& st) {
 #pragma unroll
@@ -268,7 +284,17 @@ __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0,
     // rows of lanes whose first-tile row lies before the sequence.
     const int32_t rs = (int32_t)(blk * 32 - row0) + tt * 16 + nl;   // in [-31, T + 31]: T < 2^25
     const uint32_t r = rs < 0 ? (uint32_t)T : (uint32_t)rs;
-    buffer_words<KB>(ab.k, r * (16u * KB) + (uint32_t)(4 * KB * g), st.kw[tt]);
+    if constexpr (BR > 0) {
+      const u32x2 o = __builtin_amdgcn_raw_buffer_load_b64(ab.k, (r * (2u * KB) + split_word<KB>(g)) * 4u, 0, 0);
+      const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(ab.kr, (r * (2u * BR) + split_word<BR>(g)) * 4u, 0, 0);
+      st.kw[tt][0] = o[0];
+      st.kw[tt][1] = o[1];
+      st.kwr[tt][0] = q[0];
+      st.kwr[tt][1] = q[1];
+      st.knr[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.knr, r * 4u, 0, 0));
+    } else {
+      buffer_words<KB>(ab.k, r * (16u * KB) + (uint32_t)(4 * KB * g), st.kw[tt]);
+    }
     if constexpr (NO > 0) {
       buffer_words<NO / 4>(ab.q8, r * (uint32_t)NO, st.o8[tt]);
       st.osc[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ab.osc, r * 4u, 0, 0));
@@ -282,23 +308,36 @@ __device__ __forceinline__ void load_attn_step(const AttnBufs& ab, int64_t row0,
 
 // NO > 0: outlier-8 keys (the rest channels' code in kidx / knorm, the outlier channels' int8
 // values in q8 and scales in oscale); the logit adds scale * <q_O, q8> in fp32, q_O from qo.
-template <int KB, int VB, int NO>
+//
+// BR > 0: split keys (the outlier halves at KB bits in kidx / knorm, the rest halves at BR bits in
+// kidx_r / knorm_r, each half 64 coordinates in its own rotated domain); qws then holds the fp32
+// rotated queries [B * Hq][128] of the split prologue (R_o q_O, then R_r q_R).  Lane group g
+// takes coordinates 16 g .. 16 g + 15 of each half, the two halves accumulate apart and are
+// scaled by their own norms before the parts are reduced.
+template <int KB, int VB, int NO, int BR>
 __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     const uint16_t* __restrict__ qws, int Hq, int Hkv, int64_t T, int nsplit, int spb,
     const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, int64_t seq_stride,
     CodebookArgs cbk, CodebookArgs cbv, float scale, float* __restrict__ part, const int8_t* __restrict__ q8,
-    const float* __restrict__ oscale, const float* __restrict__ qo) {
-  // replicated decode tables (K up to 32 KB, V up to 16 KB) so that three blocks fit a CU
-  constexpr int KC = table_copies<KB, true, TQ_ATTN_KBUDGET>();
+    const float* __restrict__ oscale, const float* __restrict__ qo, const uint32_t* __restrict__ kidx_r,
+    const float* __restrict__ knorm_r, CodebookArgs cbr) {
+  constexpr bool SPLIT = BR > 0;
+  static_assert(!SPLIT || (KB >= 2 && NO == 0), "split keys: outlier half of 2 to 4 bits, no int8 outliers");
+  // replicated decode tables (K up to 32 KB, split keys two of up to 16 KB, V up to 16 KB) so that
+  // three blocks fit a CU
+  constexpr int KC = table_copies<KB, true, SPLIT ? TQ_ATTN_KBUDGET / 2 : TQ_ATTN_KBUDGET>();
+  constexpr int RC = table_copies<SPLIT ? BR : 1, true, TQ_ATTN_KBUDGET / 2>();
   constexpr int VC = table_copies<VB, false, TQ_ATTN_VBUDGET>();
   using DK = DecodeTable<KB, true, KC>;
+  using DR = DecodeTable<SPLIT ? BR : 1, true, RC>;
   using DV = DecodeTable<VB, false, VC>;
-  // the K table's storage is reused for the block's merge buffer once every wave has finished
+  // the K tables' storage is reused for the block's merge buffer once every wave has finished
   constexpr int kMergeBytes = 4 * 4 * 128 * (int)sizeof(float);
-  __shared__ __attribute__((aligned(16))) uint8_t ktab[DK::BYTES > kMergeBytes ? DK::BYTES : kMergeBytes];
+  constexpr int kKTabBytes = DK::BYTES + (SPLIT ? DR::BYTES : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t ktab[kKTabBytes > kMergeBytes ? kKTabBytes : kMergeBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vtab[DV::BYTES];
-  __shared__ float kcent[16];
+  __shared__ float kcent[2][16];
   __shared__ _Float16 vcent[16];
   // Weights strip of each wave in fp16: part 0 the weights rounded to fp16, part 1 their
   // remainders, part 2 zeros (the operand rows that carry nothing); a row per head, 32 tokens
@@ -307,17 +346,20 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   __shared__ __attribute__((aligned(16))) uint16_t wh[4][3][4][kWRow];
   __shared__ float mm[4][4], ll[4][4];
   if (threadIdx.x < 16) {
-    kcent[threadIdx.x] = cbk.c[threadIdx.x];
+    kcent[0][threadIdx.x] = cbk.c[threadIdx.x];
+    kcent[1][threadIdx.x] = cbr.c[threadIdx.x];
     vcent[threadIdx.x] = (_Float16)cbv.c[threadIdx.x];
   }
   __syncthreads();
-  build_table2<KB, KC>(ktab, kcent);
+  build_table2<KB, KC>(ktab, kcent[0]);
+  if constexpr (SPLIT) build_table2<BR, RC>(ktab + DK::BYTES, kcent[1]);
   build_table<VB, VC>(vtab, vcent);
   for (int i = threadIdx.x; i < 4 * 4 * kWRow; i += blockDim.x) wh[i / (4 * kWRow)][2][(i / kWRow) % 4][i % kWRow] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const uint8_t* ktabl = DK::lane_base(ktab, lane);
+  const uint8_t* rtabl = DR::lane_base(ktab + DK::BYTES, lane);
   const uint8_t* vtabl = DV::lane_base(vtab, lane);
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15;
@@ -340,6 +382,12 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   ab.kn = buffer_rsrc(knorm + row0, (uint32_t)T * 4u);
   ab.vn = buffer_rsrc(vnorm + row0, (uint32_t)T * 4u);
   ab.v = buffer_rsrc(vidx + blk_first * (128 * VB), (uint32_t)(blk_end - blk_first) * (512u * VB));
+  if constexpr (SPLIT) {
+    // half rows of 2 KB and 2 BR words
+    ab.k = buffer_rsrc(kidx + row0 * (2 * KB), (uint32_t)T * (8u * KB));
+    ab.kr = buffer_rsrc(kidx_r + row0 * (2 * BR), (uint32_t)T * (8u * BR));
+    ab.knr = buffer_rsrc(knorm_r + row0, (uint32_t)T * 4u);
+  }
   // q_O of the block's query heads, read from LDS when a logit needs it (held in registers it
   // would push the kernel past its register budget); lanes of heads past the ratio read head 0
   // and compute a logit that is discarded
@@ -360,7 +408,32 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
   // remainder term is below fp32 rounding); other rows zero.
   using KS = SplitSlot<KB>;
   u32x4 ak[8];
-  {
+  if constexpr (SPLIT) {
+    // instructions 0-3 the outlier half, 4-7 the rest half; lane group g holds the half's
+    // coordinates 16 g .. 16 g + 15 in the split-slot order of that half's bit width
+    using KR = SplitSlot<BR>;
+    const int hl = nl & 3, prt = nl >> 2;
+    const bool live = hl < ratio && prt < 2;
+    const float* qf = reinterpret_cast<const float*>(qws) + ((int64_t)b * Hq + kvh * ratio + (hl < ratio ? hl : 0)) * 128;
+    auto qpart = [&](int c) -> uint32_t {   // fp16 hi (prt 0) or lo (prt 1) of query coordinate c
+      const float v = live ? qf[c] : 0.f;
+      const _Float16 hi = (_Float16)v;
+      const _Float16 out = prt == 0 ? hi : (_Float16)(v - (float)hi);
+      return __builtin_bit_cast(uint16_t, out);
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int half = j >> 2;
+        const int p0 = 8 * (j & 3) + 2 * k, p1 = p0 + 1;
+        const int c0 = half ? KR::coord(p0) : KS::coord(p0), c1 = half ? KR::coord(p1) : KS::coord(p1);
+        const int h0 = half ? KR::half(p0) : KS::half(p0), h1 = half ? KR::half(p1) : KS::half(p1);
+        const uint32_t lo = (h0 == 0 || prt == 0) ? qpart(64 * half + 16 * g + c0) : 0u;
+        const uint32_t hi = (h1 == 0 || prt == 0) ? qpart(64 * half + 16 * g + c1) : 0u;
+        ak[j][k] = lo | (hi << 16);
+      }
+  } else {
     const int hl = nl & 3, prt = nl >> 2;
     const bool live = hl < ratio && prt < 2;
     const uint16_t* src = qws + (((int64_t)b * Hq + kvh * ratio + (hl < ratio ? hl : 0)) * 4 + (prt == 1 ? 1 : 0)) * 128 + 32 * g;
@@ -397,10 +470,27 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
       const bool valid = r >= row0 && r < rowE;
       const float sk = cur.kn[tt];
       svv[tt] = cur.vn[tt];
-      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+      float mine;
+      if constexpr (SPLIT) {
+        const uint64_t wo = ((uint64_t)cur.kw[tt][1] << 32 | cur.kw[tt][0]) >> split_shift<KB>(g);
+        const uint64_t wr = ((uint64_t)cur.kwr[tt][1] << 32 | cur.kwr[tt][0]) >> split_shift<BR>(g);
+        const uint32_t wo2[2] = {(uint32_t)wo, (uint32_t)(wo >> 32)};
+        const uint32_t wr2[2] = {(uint32_t)wr, (uint32_t)(wr >> 32)};
+        f32x4 dout = f32x4{0.f, 0.f, 0.f, 0.f}, drest = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d = mfma_f16(ak[j], decode_split_slot<KB, KC>(cur.kw[tt], j, ktabl), d);
-      float mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
+        for (int j = 0; j < 4; ++j) {
+          dout = mfma_f16(ak[j], decode_split_slot<KB, KC>(wo2, j, ktabl), dout);
+          drest = mfma_f16(ak[4 + j], decode_split_slot<BR, RC>(wr2, j, rtabl), drest);
+        }
+        const float sr = cur.knr[tt];
+        mine = reduce_parts(fmaf(dout[0], sk, drest[0] * sr), fmaf(dout[1], sk, drest[1] * sr),
+                            fmaf(dout[2], sk, drest[2] * sr), fmaf(dout[3], sk, drest[3] * sr));
+      } else {
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d = mfma_f16(ak[j], decode_split_slot<KB, KC>(cur.kw[tt], j, ktabl), d);
+        mine = reduce_parts(d[0] * sk, d[1] * sk, d[2] * sk, d[3] * sk);
+      }
       if constexpr (NO > 0) {
         float o = 0.f;
 #pragma unroll
@@ -461,7 +551,7 @@ __global__ __launch_bounds__(256, TQ_ATTN_BLOCKS) void k_attn_d128(
     AttnStep<KB, VB, NO> st[kAttnBatch];
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)
-      if (b0 + u < we) load_attn_step<KB, VB, NO>(ab, row0, T, blk_first, b0 + u, nl, g, st[u]);
+      if (b0 + u < we) load_attn_step<KB, VB, NO, BR>(ab, row0, T, blk_first, b0 + u, nl, g, st[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u)
@@ -571,23 +661,37 @@ size_t attn_partials_bytes(int B, int Hkv, int64_t T) {
   return ((size_t)B * Hkv * nsplit * 4 * kAttnPart * sizeof(float) + 255) & ~(size_t)255;
 }
 
-template <int KB, int VB, int NO = 0>
+// Split keys for attn_launch: the rest halves' packed set and codebook, and the split prologue's
+// inputs (channel order and the halves' R^T).
+struct SplitAttnArgs {
+  const tq_packed* Kr = nullptr;
+  CodebookArgs cbr{};
+  const int32_t* order = nullptr;
+  const float* rto = nullptr;
+  const float* rtr = nullptr;
+};
+
+template <int KB, int VB, int NO = 0, int BR = 0>
 hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride, const tq_packed* K,
                        const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
                        const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale, float* out,
                        void* ws, hipStream_t st, const OutlierArgs* oa = nullptr, const int8_t* q8 = nullptr,
-                       const float* oscale = nullptr) {
+                       const float* oscale = nullptr, const SplitAttnArgs* sa = nullptr) {
   uint16_t* qws = static_cast<uint16_t*>(ws);
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
   float* qo = NO > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes + attn_partials_bytes(B, Hkv, T))
                      : nullptr;
-  hipError_t e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st, NO > 0 ? oa : nullptr, qo);
+  hipError_t e;
+  if constexpr (BR > 0)   // fp32 [B * Hq][128] rotated split queries (the first half of the query region)
+    e = launch_qprep_split(q, B, Hq, Hkv, sa->order, sa->rto, sa->rtr, reinterpret_cast<float*>(qws), st);
+  else
+    e = launch_qprep128(q, B, Hq, Hkv, rot_k->rt32_dev, nullptr, qws, nullptr, st, NO > 0 ? oa : nullptr, qo);
   if (e != hipSuccess) return e;
   static int per_cu = 0;
   if (per_cu == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_d128<KB, VB, NO>, 256, 0) != hipSuccess || v <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_attn_d128<KB, VB, NO, BR>, 256, 0) != hipSuccess || v <= 0)
       v = 2;
     per_cu = v;
   }
@@ -599,8 +703,9 @@ hipError_t attn_launch(const float* q, int B, int Hq, int Hkv, int64_t T, int64_
   spb = (spb + 3) / 4 * 4;
   if (spb < kAttnMinSteps) spb = kAttnMinSteps;
   const int nsplit = (int)((steps + spb - 1) / spb);
-  hipLaunchKernelGGL((k_attn_d128<KB, VB, NO>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit,
-                     (int)spb, K->idx, K->norms, V->idx, V->norms, seq_stride, cbk, cbv, scale, part, q8, oscale, qo);
+  hipLaunchKernelGGL((k_attn_d128<KB, VB, NO, BR>), dim3(nsplit, B * Hkv), dim3(256), 0, st, qws, Hq, Hkv, T, nsplit,
+                     (int)spb, K->idx, K->norms, V->idx, V->norms, seq_stride, cbk, cbv, scale, part, q8, oscale, qo,
+                     BR > 0 ? sa->Kr->idx : nullptr, BR > 0 ? sa->Kr->norms : nullptr, BR > 0 ? sa->cbr : cbk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(B * Hq), dim3(kCombineThreads), 0, st, part, Hq, Hkv, nsplit, rot_v->r32_dev, out);
@@ -652,6 +757,27 @@ size_t decode_attn_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d) {
 size_t decode_attn_outlier8_workspace_bytes(int B, int Hq, int Hkv, int64_t T) {
   const size_t qbytes = ((size_t)B * Hq * 4 * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
   return qbytes + attn_partials_bytes(B, Hkv, T) + (size_t)B * Hq * kOutlierMaxChannels * sizeof(float);
+}
+
+hipError_t launch_decode_attn_split(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* Ko,
+                                    const tq_packed* Kr, const tq_packed* V, const CodebookArgs& cbo,
+                                    const CodebookArgs& cbr, const CodebookArgs& cbv, const int32_t* order,
+                                    const float* rto, const float* rtr, const tq_rotation_s* rot_v, float scale,
+                                    float* out, void* ws, hipStream_t st) {
+  SplitAttnArgs sa;
+  sa.Kr = Kr;
+  sa.cbr = cbr;
+  sa.order = order;
+  sa.rto = rto;
+  sa.rtr = rtr;
+#define TQ_ATTN_SPLIT(BO, BR, VB)                                                                                   \
+  if (cbo.bits == BO && cbr.bits == BR && cbv.bits == VB)                                                        \
+    return attn_launch<BO, VB, 0, BR>(q, B, Hq, Hkv, T, T, Ko, V, cbo, cbv, nullptr, rot_v, scale, out, ws, st,   \
+                                      nullptr, nullptr, nullptr, &sa);
+  TQ_ATTN_SPLIT(3, 2, 2) TQ_ATTN_SPLIT(3, 2, 3) TQ_ATTN_SPLIT(3, 2, 4)
+  TQ_ATTN_SPLIT(4, 3, 2) TQ_ATTN_SPLIT(4, 3, 3) TQ_ATTN_SPLIT(4, 3, 4)
+#undef TQ_ATTN_SPLIT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_attn_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,

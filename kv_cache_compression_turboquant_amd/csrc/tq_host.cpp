@@ -1559,3 +1559,43 @@ tq_status tq_decode_attn_outlier8(const float* q_dev, int B, int Hq, int Hkv, in
                                                       ws_dev, as_stream(stream)),
                       fn);
 }
+
+size_t tq_decode_attn_split_workspace(int B, int Hq, int Hkv, int64_t T) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || T < 0) return 0;
+  return tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, tq::kSplitD);
+}
+
+tq_status tq_decode_attn_split(const float* q_dev, int B, int Hq, int Hkv, int64_t T, tq_split_t split,
+                               const tq_packed* K_o, const tq_packed* K_r, const tq_packed* V, tq_codebook_t cb_o,
+                               tq_codebook_t cb_r, tq_codebook_t cb_v, tq_rotation_t rot_o, tq_rotation_t rot_r,
+                               tq_rotation_t rot_v, float scale, float* out_dev, void* ws_dev, size_t ws_bytes,
+                               void* stream) {
+  static const char* fn = "tq_decode_attn_split";
+  if (!V || !cb_v || !rot_v) return fail(TQ_EINVAL, "%s: null argument", fn);
+  if (B < 0 || Hq < 0 || Hkv < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (T < 1) return fail(TQ_EINVAL, "%s: attention over an empty cache (T=%lld)", fn, (long long)T);
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0)
+    return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  const int ratio = Hq / Hkv;
+  if (ratio != 1 && ratio != 2 && ratio != 4) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not in {1, 2, 4}", fn, ratio);
+  tq_status st = check_split_keys(B, Hkv, T, split, cb_o, cb_r, rot_o, rot_r, K_o, K_r, fn);
+  if (st != TQ_OK) return st;
+  if (rot_v->d != tq::kSplitD || cb_v->d != tq::kSplitD) return fail(TQ_ESHAPE, "%s: V handles need d=128", fn);
+  st = check_packed(V, tq::kSplitD, cb_v->b, TQ_MODE_MSE, fn);
+  if (st != TQ_OK) return st;
+  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED) return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout", fn);
+  if (V->n != (int64_t)B * Hkv * T)
+    return fail(TQ_ESHAPE, "%s: V->n=%lld, B*Hkv*T=%lld", fn, (long long)V->n, (long long)B * Hkv * T);
+  const bool pair_ok = (cb_o->b == 3 && cb_r->b == 2) || (cb_o->b == 4 && cb_r->b == 3);
+  if (!pair_ok || cb_v->b < 2)
+    return fail(TQ_EUNSUPPORTED, "%s: (b_o, b_r, b_v) = (%d, %d, %d): needs (3, 2) or (4, 3) and b_v in 2..4", fn,
+                cb_o->b, cb_r->b, cb_v->b);
+  if ((int64_t)B * Hq == 0) return ok();
+  if (!q_dev || !out_dev) return fail(TQ_EINVAL, "%s: null q or out", fn);
+  const size_t need = tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, tq::kSplitD);
+  if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  return check_launch(tq::launch_decode_attn_split(q_dev, B, Hq, Hkv, T, K_o, K_r, V, cb_o->args, cb_r->args,
+                                                   cb_v->args, split->order_dev, rot_o->rt32_dev, rot_r->rt32_dev,
+                                                   rot_v, scale, out_dev, ws_dev, as_stream(stream)),
+                      fn);
+}

@@ -186,6 +186,13 @@ size_t scores_outlier8_workspace_bytes(int B, int Hq);
 // Decode attention with outlier-8 keys (tq_attn128.hip): the workspace of launch_decode_attn
 // followed by qo.
 size_t decode_attn_outlier8_workspace_bytes(int B, int Hq, int Hkv, int64_t T);
+// Decode attention with split keys (tq_attn128.hip): the workspace of launch_decode_attn (its
+// query region holds the fp32 rotated split queries).  (b_o, b_r) in {(3, 2), (4, 3)}.
+hipError_t launch_decode_attn_split(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* Ko,
+                                    const tq_packed* Kr, const tq_packed* V, const CodebookArgs& cbo,
+                                    const CodebookArgs& cbr, const CodebookArgs& cbv, const int32_t* order,
+                                    const float* rto, const float* rtr, const tq_rotation_s* rot_v, float scale,
+                                    float* out, void* ws, hipStream_t st);
 hipError_t launch_decode_attn_outlier8(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t seq_stride,
                                        const tq_packed* K, const int8_t* q8, const float* oscale, const tq_packed* V,
                                        const CodebookArgs& cbk, const CodebookArgs& cbv, const tq_rotation_s* rot_k,

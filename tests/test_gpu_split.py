@@ -314,3 +314,54 @@ def test_short_encode_per_token_path(dev, rots, dtype, bo, br, T):
     zero_row = (1 * H + 2) * T + 4
     assert np.all(io[zero_row] == 1 << (bo - 1)) and po.norms[zero_row].item() == 0.0
     assert np.all(io[(0 * H + 1) * T + 7] == 1 << (bo - 1))
+
+
+@pytest.mark.parametrize("bo,br,vb,hq,hkv,T", [(3, 2, 2, 8, 2, 300), (4, 3, 3, 4, 2, 77), (3, 2, 4, 2, 2, 33),
+                                               (4, 3, 2, 4, 1, 1), (3, 2, 3, 4, 2, 1000)])
+def test_decode_attn_split_matches_oracle(dev, rots, bo, br, vb, hq, hkv, T):
+    # split keys inside decode attention, against the oracle on the GPU's own codes; T = 77 with
+    # two sequences per batch puts sequences that start in the second half of a 32-token block
+    B = 2
+    x, xt = _keys(B, hkv, T, seed=bo * 10 + vb)
+    out = _outliers(x)
+    sp = tq.make_split(out)
+    cbo, cbr, cbv = tq.codebook(M, bo), tq.codebook(M, br), tq.codebook(128, vb)
+    rot_v = tq.make_rotation(128, 1)
+    K = tq.encode_split(xt.to(dev), sp, cbo, cbr, *rots)
+    vbits = wl.kv_tensor_bf16(B, hkv, T, 128, seed=33, outlier_seed=21, scale_seed=None)
+    vt = torch.from_numpy(vbits.view(np.int16)).view(torch.bfloat16).reshape(-1, 128).to(dev)
+    V = tq.encode(vt, vb, "mse", cbv, rot_v, layout="blocked")
+    q = wl.gaussian((B, hq, 128), 44)
+    got = tq.decode_attn_split(torch.from_numpy(q).to(dev), K, V, hkv, sp, cbo, cbr, cbv, *rots, rot_v).cpu().numpy()
+    torch.cuda.synchronize()
+    n = B * hkv * T
+    enc = _gpu_as_oracle(K[0], K[1], B, hkv, T, oracle.channel_order(out, 128))
+    R_V = oracle.dense_rotation(128, 1)
+    ocbv = oracle.codebook(128, vb)
+    vidx = oracle.unpack_token_blocked(to_np_words(V.idx), n, 128, vb).reshape(B, hkv, T, 128)
+    vn = V.norms.cpu().numpy().astype(np.float64).reshape(B, hkv, T)
+    ref = oracle.decode_attention_split(q, enc, vidx, vn, R_O, R_R, R_V, oracle.codebook(M, bo), oracle.codebook(M, br),
+                                        ocbv, 1 / np.sqrt(128))
+    ratio = hq // hkv
+    for b in range(B):
+        for g in range(hkv):
+            vmax = np.max(np.linalg.norm(oracle.decode_mse(vidx[b, g], vn[b, g], R_V, ocbv), axis=1))
+            err = np.max(np.abs(got[b, g * ratio:(g + 1) * ratio] - ref[b, g * ratio:(g + 1) * ratio]))
+            assert err <= 1e-3 * vmax, (b, g, err, vmax)
+
+
+def test_decode_attn_split_errors(dev, rots):
+    x, xt = _keys(1, 2, 32, seed=1)
+    sp = tq.make_split(_outliers(x))
+    cbv, rot_v = tq.codebook(128, 2), tq.make_rotation(128, 1)
+    V = tq.encode(xt.reshape(-1, 128).to(dev), 2, "mse", cbv, rot_v, layout="blocked")
+    K = tq.encode_split(xt.to(dev), sp, tq.codebook(M, 2), tq.codebook(M, 2), *rots)
+    with pytest.raises(tq.TQError) as e:       # (2, 2) halves: no kernel
+        tq.decode_attn_split(torch.zeros((1, 4, 128), device=dev), K, V, 2, sp, tq.codebook(M, 2), tq.codebook(M, 2),
+                             cbv, *rots, rot_v)
+    assert e.value.status == 3
+    K = tq.encode_split(xt.to(dev), sp, tq.codebook(M, 3), tq.codebook(M, 2), *rots)
+    with pytest.raises(tq.TQError) as e:       # GQA ratio 3
+        tq.decode_attn_split(torch.zeros((1, 6, 128), device=dev), K, V, 2, sp, tq.codebook(M, 3), tq.codebook(M, 2),
+                             cbv, *rots, rot_v)
+    assert e.value.status == 3
