@@ -308,8 +308,11 @@ hipError_t gen_dispatch_bits(const void* x, bool bf16, int64_t n, int d, const t
 // ---------------------------------------------------------------------------------------
 // Search.
 // ---------------------------------------------------------------------------------------
-constexpr int kSearchKeys = 256;           // database vectors per score block (64 per wave)
+constexpr int kSearchKeys = 512;           // database vectors per score block (64 per wave)
 constexpr int64_t kSearchChunk = 65536;    // database vectors per score chunk
+// The first chunk keeps every score (there is no running k-th result yet) and its merge inserts
+// often, so it is kept short; the chunks after it keep only what beats the running k-th result.
+constexpr int64_t kSearchFirstChunk = 4096;
 constexpr float kSketchScale = 1.0f / 1024.0f;  // query sketch scale; the key side carries 1024
 
 // Query operands in fp16 MFMA fragment order: block (qb, kc) = 4096 u32x4 laid out
@@ -340,48 +343,121 @@ __global__ __launch_bounds__(256) void k_search_qfrag(const float* __restrict__ 
   }
 }
 
-// Sign operand of 8 coordinates (bits 8 s .. 8 s + 7 of z): fp16 +-mag pairs.
-__device__ __forceinline__ u32x4 sign8(uint32_t z, int s, uint32_t magpair) {
-  const uint32_t nz = ~z >> (8 * s);
+// Sign operands of the lane's 32 coordinates of a contraction chunk (sign bits z, bit c for
+// coordinate c): the fp16 pair {+-mag, +-mag} of coordinates 2 i, 2 i + 1, negative where the
+// bit is 0.  sign_pairs arranges the inverted bits once per chunk so that one shift puts both bits
+// of a pair on the fp16 sign positions 15 and 31: zp[0] holds coordinates 0..15 (coordinate 2 i
+// at bit 2 i, 2 i + 1 at bit 2 i + 16), zp[1] coordinates 16..31 the same way.
+__device__ __forceinline__ void sign_pairs(uint32_t z, uint32_t (&zp)[2]) {
+  const uint32_t nz = ~z;
+  zp[0] = (nz & 0x5555u) | ((nz << 15) & 0x55550000u);
+  zp[1] = ((nz >> 16) & 0x5555u) | ((nz >> 1) & 0x55550000u);
+}
+
+// The operand of instruction s (coordinates 8 s .. 8 s + 7).
+__device__ __forceinline__ u32x4 sign8(const uint32_t (&zp)[2], int s, uint32_t magpair) {
+  const uint32_t w = zp[s >> 1];
   u32x4 v;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t t = nz >> (2 * j);
-    v[j] = magpair | ((t & 1u) << 15) | ((t & 2u) << 30);
+    const int i = 4 * (s & 1) + j;  // pair within the 16-coordinate half
+    v[j] = ((w << (15 - 2 * i)) & 0x80008000u) | magpair;
   }
   return v;
 }
 
-// Scores of 128 queries (block x) against 256 database vectors (block y) of one chunk:
-// out[q][j] = ||q|| s_j (<q_rot, C[idx_j]> + (gamma_j / s_j) sqrt(pi/2)/d <q_s, z_j>) with unit q.
-// Eight waves per block, two per SIMD: wave w scores key group w % 4 (64 vectors, decoded by the
-// wave itself) against query half w / 4 (4 query tiles), so each wave holds 16 accumulator tiles.
-// The query operands are double-buffered in LDS (2 x 64 KB): the loads of contraction chunk
-// kc + 1 are in flight while chunk kc's MFMAs run.
+// Scores of 128 queries against 512 database vectors of one chunk, one block per (query block,
+// key block) tile: out[q][j] = ||q|| s_j (<q_rot, C[idx_j]> + (gamma_j / s_j) sqrt(pi/2)/d <q_s, z_j>)
+// with unit q.  Eight waves, two per SIMD; wave w decodes its own 64 vectors once per contraction
+// slice and multiplies them against all 128 queries (8 query tiles x 4 key tiles = 32 accumulator
+// tiles), so each decoded operand feeds 16 MFMAs.  The query operands of contraction chunk kc + 1
+// stream from memory straight into the second LDS buffer (2 x 64 KB), and the key words of kc + 1
+// into registers, while chunk kc's MFMAs run.
+//
+// Only scores that can still enter a query's top-k are kept: with kth (the running k-th score of
+// every query, from the chunks before) a score is written only if it is strictly larger (an equal
+// score loses to the earlier, smaller index), and masks[q][64-vector group] gets one bit per
+// written score; without kth (the first chunk) every score of a vector below m is written.
 constexpr int kSearchWaves = 8;
 constexpr int kSearchThreads = kSearchWaves * 64;
+static_assert(kSearchKeys == kSearchWaves * 64, "one 64-vector group per wave");
+static_assert(kSearchChunk % kSearchKeys == 0 && kSearchFirstChunk % kSearchKeys == 0, "chunks hold whole key blocks");
+
+__device__ __forceinline__ void lds_dma16(const u32x4* src, u32x4* wave_dst) {
+  // each lane's 16 bytes land at wave_dst + lane (the destination is the wave's base)
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// The lane's key words of contraction chunk kc: for key tile j, the BITS index words of its 32
+// coordinates (byte offset krow[j] * wb + gi in the index resource) and its sign word (krow[j] * zb
+// + gz in the sign resource); the chunk's offset goes in the scalar offset.
+template <int BITS>
+__device__ __forceinline__ void search_key_words(__amdgpu_buffer_rsrc_t ri, __amdgpu_buffer_rsrc_t rz,
+                                                 const uint32_t (&krow)[4], uint32_t wb, uint32_t zb, uint32_t gi,
+                                                 uint32_t gz, int kc, uint32_t (&kw)[4][BITS], uint32_t (&zw)[4]) {
+  typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t oi = krow[j] * wb + gi, si = 16u * BITS * (uint32_t)kc;
+    if constexpr (BITS == 1) {
+      kw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(ri, oi, si, 0);
+    } else if constexpr (BITS == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ri, oi, si, 0);
+      kw[j][0] = v[0]; kw[j][1] = v[1];
+    } else if constexpr (BITS == 3) {
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(ri, oi, si, 0);
+      kw[j][0] = v[0]; kw[j][1] = v[1]; kw[j][2] = v[2];
+    } else {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ri, oi, si, 0);
+      kw[j][0] = v[0]; kw[j][1] = v[1]; kw[j][2] = v[2]; kw[j][3] = v[3];
+    }
+    zw[j] = __builtin_amdgcn_raw_buffer_load_b32(rz, krow[j] * zb + gz, 16u * (uint32_t)kc, 0);
+  }
+}
 
 template <int BITS>
 __global__ __launch_bounds__(kSearchThreads, 1) void k_search_scores(
     const u32x4* __restrict__ qf, const float* __restrict__ qnorm, int64_t nq, int d,
     const uint32_t* __restrict__ idx, const float* __restrict__ norms, const uint32_t* __restrict__ qbits,
-    const float* __restrict__ rnorms, int64_t m, CodebookArgs cb, float* __restrict__ out, int64_t ldo) {
+    const float* __restrict__ rnorms, int64_t m, CodebookArgs cb, const float* __restrict__ kth, int k,
+    float* __restrict__ out, int64_t ldo, uint64_t* __restrict__ masks, int64_t ldm) {
   // the query operands take 128 KB of LDS: the decode table gets at most 8 KB
   constexpr int TC = table_copies<BITS, false, 8192>();
   using DT = DecodeTable<BITS, false, TC>;
-  constexpr int PER = 4096 / kSearchThreads;  // staging loads per thread per chunk
-  __shared__ u32x4 lds[2][4096];
-  __shared__ __attribute__((aligned(16))) uint8_t tab[DT::BYTES];
-  __shared__ _Float16 cent[16];
+  constexpr int PER = 4096 / kSearchThreads;  // query-operand loads per thread per chunk
+  // one LDS array: the decode table first (at address 0, so that its lookups add no base), then
+  // the two query-operand buffers, then the fp16 centroids
+  // the two query-operand buffers, then the fp16 centroids and the block's query norms and kept-
+  // score bounds (the epilogue reads them from here rather than waiting on memory per query)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DT::BYTES + 2 * 4096 * 16 + 32 + 2 * 128 * 4];
+  uint8_t* const tab = smem;
+  u32x4 (*const lds)[4096] = reinterpret_cast<u32x4 (*)[4096]>(smem + DT::BYTES);
+  _Float16* const cent = reinterpret_cast<_Float16*>(smem + DT::BYTES + 2 * 4096 * 16);
+  float* const qn_s = reinterpret_cast<float*>(smem + DT::BYTES + 2 * 4096 * 16 + 32);
+  float* const th_s = qn_s + 128;
   if (threadIdx.x < 16) cent[threadIdx.x] = (_Float16)cb.c[threadIdx.x];
+  // Tile of this block.  Blocks go to the eight XCDs in turn (block L to XCD L % 8); when the
+  // grid divides evenly, the tiles are dealt so that each XCD holds consecutive ones, and the
+  // query blocks of one key block, which read the same database words, share an L2.
+  const unsigned nqb = (unsigned)((nq + 127) / 128);
+  unsigned tile = blockIdx.x;
+  if (gridDim.x % 8 == 0) tile = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const unsigned qb = tile % nqb, kb = tile / nqb;
   const int nb = d >> 7;
-  const int W = d * BITS / 32;
-  const int qb = blockIdx.x;
+  const int W = d * BITS / 32, dz = d >> 5;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kg = wave & 3, qh = wave >> 2;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t key0 = (int64_t)blockIdx.y * kSearchKeys + kg * 64;
+  const int64_t key0 = (int64_t)kb * kSearchKeys + wave * 64;
   const float kz = 1.2533141373155002512f / (float)d / kSketchScale;  // sqrt(pi/2) / d, rescaled
+
+  const u32x4* qsrc = qf + (size_t)qb * nb * 4096;
+  u32x4* const wdst0 = &lds[0][wave * 64];
+  u32x4* const wdst1 = &lds[1][wave * 64];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) lds_dma16(qsrc + i * kSearchThreads + threadIdx.x, wdst0 + i * kSearchThreads);
 
   float sk[4];
   uint32_t magp[4];
@@ -397,79 +473,116 @@ __global__ __launch_bounds__(kSearchThreads, 1) void k_search_scores(
     const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)zf);
     magp[j] = h | (h << 16);
   }
-  const uint32_t* idxg = idx + BITS * g;
-  const uint32_t* zg = qbits + g;
-  const u32x4* qsrc = qf + (size_t)qb * nb * 4096;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) lds[0][i * kSearchThreads + threadIdx.x] = qsrc[i * kSearchThreads + threadIdx.x];
-  __syncthreads();
+  if (threadIdx.x < 128) {
+    // query norm, and the bound a kept score must beat: the running k-th score (+inf past nq)
+    const int64_t q = (int64_t)qb * 128 + threadIdx.x;
+    const bool vq = q < nq;
+    qn_s[threadIdx.x] = vq ? qnorm[q] : 0.f;
+    th_s[threadIdx.x] = !vq ? INFINITY : (kth != nullptr ? kth[q * k + k - 1] : -INFINITY);
+  }
+  // key words through buffer resources over the chunk (m * W and m * d / 32 words, < 2^32 bytes)
+  const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(idx, (uint32_t)(m * W * 4));
+  const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(qbits, (uint32_t)(m * dz * 4));
+  const uint32_t wb = 4u * W, zb = 4u * dz, gi = 4u * BITS * g, gz = 4u * g;
+  uint32_t kw[4][BITS], zw[4];
+  search_key_words<BITS>(ri, rz, krow, wb, zb, gi, gz, 0, kw, zw);
+  __syncthreads();  // centroids
   build_table<BITS, TC>(tab, cent);
-  __syncthreads();
-  const uint8_t* tabl = DT::lane_base(tab, lane);
+  wait_vm_all();
+  __syncthreads();  // table and the first query operands
+  const uint32_t laneoff = (uint32_t)(lane % TC) * DT::EB;
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt)
+  for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int kc = 0; kc < nb; ++kc) {
     const int cur = kc & 1;
     const bool more = kc + 1 < nb;
-    uint32_t kw[4][BITS], zw[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t* w = idxg + (size_t)krow[j] * W + 4 * BITS * kc;
-#pragma unroll
-      for (int b = 0; b < BITS; ++b) kw[j][b] = w[b];
-      zw[j] = zg[(size_t)krow[j] * (d >> 5) + 4 * kc];
-    }
-    u32x4 stage[PER];
+    uint32_t nkw[4][BITS], nzw[4];
     if (more) {
-      const u32x4* src = qsrc + (size_t)(kc + 1) * 4096;
+      search_key_words<BITS>(ri, rz, krow, wb, zb, gi, gz, kc + 1, nkw, nzw);
+      const u32x4* src = qsrc + (size_t)(kc + 1) * 4096 + threadIdx.x;
+      u32x4* dst = cur ? wdst0 : wdst1;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) stage[i] = src[i * kSearchThreads + threadIdx.x];
+      for (int i = 0; i < PER; ++i) lds_dma16(src + i * kSearchThreads, dst + i * kSearchThreads);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) nkw[j][b] = 0u;
+        nzw[j] = 0u;
+      }
     }
     const u32x4* lq = lds[cur];
+    uint32_t zp[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sign_pairs(zw[j], zp[j]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 bm[4], bz[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bm[j] = decode_keys<BITS, TC>(kw[j], s, tabl);
-        bz[j] = sign8(zw[j], s, magp[j]);
+        bm[j] = decode_keys_or<BITS, TC>(kw[j], s, tab, laneoff);
+        bz[j] = sign8(zp[j], s, magp[j]);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int qt = 4 * qh + t;
-        const u32x4 ar = lq[(qt * 4 + s) * 64 + lane];
-        const u32x4 az = lq[((8 + qt) * 4 + s) * 64 + lane];
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 ar = lq[(t * 4 + s) * 64 + lane];
+        const u32x4 az = lq[((8 + t) * 4 + s) * 64 + lane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[t][j] = mfma_f16(ar, bm[j], acc[t][j]);
-          acc[t][j] = mfma_f16(az, bz[j], acc[t][j]);
-        }
+        for (int j = 0; j < 4; ++j) acc[t][j] = mfma_f16(ar, bm[j], acc[t][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[t][j] = mfma_f16(az, bz[j], acc[t][j]);
       }
       // one contraction slice at a time (the other wave on the SIMD covers the latencies)
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
+    wait_vm_all();     // next chunk's query operands (in LDS) and key words
+    __syncthreads();   // every wave is done with lds[cur] and sees lds[cur ^ 1]
 #pragma unroll
-      for (int i = 0; i < PER; ++i) lds[cur ^ 1][i * kSearchThreads + threadIdx.x] = stage[i];
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < BITS; ++b) kw[j][b] = nkw[j][b];
+      zw[j] = nzw[j];
     }
-    __syncthreads();
   }
+
+  // Epilogue: lane (nl, g) holds query 16 t + 4 g + r against vector 16 j + nl of the wave's group.
+  // A wave past the chunk's last vector writes nothing (its group is no column of masks).
+  if (key0 >= m) return;
+  const int64_t gcol = (int64_t)kb * kSearchWaves + wave;
+  bool kok[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t key = key0 + 16 * j + nl;
-    if (key >= m) continue;
+  for (int j = 0; j < 4; ++j) kok[j] = key0 + 16 * j + nl < m;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 8; ++t) {
+    const f32x4 qn4 = *reinterpret_cast<const f32x4*>(qn_s + 16 * t + 4 * g);
+    const f32x4 th4 = *reinterpret_cast<const f32x4*>(th_s + 16 * t + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t q = (int64_t)qb * 128 + 16 * (4 * qh + t) + 4 * g + r;
-        if (q < nq) out[q * ldo + key] = qnorm[q] * sk[j] * acc[t][j][r];
+    for (int r = 0; r < 4; ++r) {
+      const int64_t q = (int64_t)qb * 128 + 16 * t + 4 * g + r;
+      float v[4];
+      bool pass[4], any = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = qn4[r] * sk[j] * acc[t][j][r];
+        pass[j] = kok[j] && v[j] > th4[r];  // th4 is +inf past nq
+        any = any || pass[j];
       }
+      uint64_t bits = 0;
+      if (__ballot(any) != 0ull) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (pass[j]) out[q * ldo + key0 + 16 * j + nl] = v[j];
+          const uint64_t b = __ballot(pass[j]);
+          bits |= ((b >> (16 * g)) & 0xffffull) << (16 * j);
+        }
+      }
+      if (nl == 0 && q < nq) masks[q * ldm + gcol] = bits;
+    }
   }
 }
 
@@ -478,16 +591,19 @@ __device__ __forceinline__ bool better(float a, int64_t ia, float b, int64_t ib)
   return a > b || (a == b && ia < ib);
 }
 
-// Merges one chunk of scores of query blockIdx.x into its running top-k (top_s / top_i, sorted;
-// ignored when `first`).  Every thread filters its strided share against the running k-th
-// result and keeps a sorted list of KMAX entries; k rounds of a block-wide argmax then pick the
-// results.  Scores are read as float4 batches (ldo is a multiple of 4) so that a thread's loads
-// are in flight together rather than one per data-dependent branch.
+// Merges the kept scores of one chunk (see k_search_scores) of query blockIdx.x into its running
+// top-k (top_s / top_i, sorted; ignored when `first`).  Thread i owns the 64-vector groups i,
+// i + 256, ...: it loads all their masks at once, and for a group with bits set it reads the
+// float4 batches of the group that hold kept scores.  When no score of the chunk was kept for
+// the query, the running top-k stands and the block returns after the masks.  Every thread
+// filters what it reads against the running k-th result and keeps a sorted list of KMAX entries;
+// k rounds of a block-wide argmax then pick the results.
 template <int KMAX>
-__global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ sc, int64_t ldo, int64_t m,
+__global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ sc, int64_t ldo,
+                                                     const uint64_t* __restrict__ masks, int64_t ldm, int64_t ngroups,
                                                      int64_t base, int k, int first, float* __restrict__ top_s,
                                                      int64_t* __restrict__ top_i) {
-  constexpr int U = 8;  // float4 loads per thread per batch
+  constexpr int G = 4;  // groups per thread per pass (a full chunk has 1024)
   __shared__ float red_s[4];
   __shared__ int64_t red_i[4];
   __shared__ int red_t[4];
@@ -514,6 +630,19 @@ __global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ s
       }
     }
   };
+  // this thread's groups (a chunk has at most 256 G) and their masks
+  static_assert(kSearchChunk / 64 <= 256 * G, "one pass over the groups");
+  const uint64_t* mrow = masks + q * ldm;
+  uint64_t mk[G];
+  int any = 0;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int64_t gi = threadIdx.x + (int64_t)u * blockDim.x;
+    mk[u] = gi < ngroups ? mrow[gi] : 0ull;
+    any |= mk[u] != 0ull;
+  }
+  // nothing of this chunk beat the running k-th result: the running top-k stands
+  if (!__syncthreads_or(any) && !first) return;
   // the bound an element must beat: the running k-th result, then the thread's own k-th entry
   float ks = -INFINITY;
   int64_t ki = -1;
@@ -534,24 +663,27 @@ __global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ s
         }
     }
   };
-  const int64_t m4 = m >> 2;
   const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
-  for (int64_t b0 = threadIdx.x; b0 < m4; b0 += (int64_t)blockDim.x * U) {
-    f32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = b0 + (int64_t)u * blockDim.x;
-      v[u] = j < m4 ? row4[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
+  for (int u = 0; u < G; ++u) {
+    if (mk[u] == 0ull) continue;
+    const int64_t gi = threadIdx.x + (int64_t)u * blockDim.x;
+    // four batches of four float4 loads (16 scores each)
+#pragma unroll 1
+    for (int c0 = 0; c0 < 16; c0 += 4) {
+      const uint32_t bits = (uint32_t)(mk[u] >> (4 * c0)) & 0xffffu;
+      if (bits == 0) continue;
+      f32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = b0 + (int64_t)u * blockDim.x;
+      for (int c = 0; c < 4; ++c)
+        v[c] = (bits >> (4 * c)) & 15u ? row4[gi * 16 + c0 + c] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j < m4) consider(v[u][e], base + 4 * j + e);
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((bits >> (4 * c + e)) & 1u) consider(v[c][e], base + gi * 64 + 4 * (c0 + c) + e);
     }
   }
-  for (int64_t j = 4 * m4 + threadIdx.x; j < m; j += blockDim.x) consider(row[j], base + j);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = 0; r < k; ++r) {
@@ -604,19 +736,22 @@ __global__ __launch_bounds__(256) void k_search_topk(const float* __restrict__ s
 
 template <int BITS>
 hipError_t search_scores_launch(const u32x4* qf, const float* qnorm, int64_t nq, int d, const tq_packed* db,
-                                int64_t base, int64_t m, const CodebookArgs& cb, float* out, int64_t ldo,
-                                hipStream_t st) {
+                                int64_t base, int64_t m, const CodebookArgs& cb, const float* kth, int k, float* out,
+                                int64_t ldo, uint64_t* masks, int64_t ldm, hipStream_t st) {
   const int W = d * BITS / 32;
-  const dim3 grid((unsigned)((nq + 127) / 128), (unsigned)((m + kSearchKeys - 1) / kSearchKeys));
-  hipLaunchKernelGGL((k_search_scores<BITS>), grid, dim3(kSearchThreads), 0, st, qf, qnorm, nq, d, db->idx + base * W,
-                     db->norms + base, db->qjl + base * (d / 32), db->rnorms + base, m, cb, out, ldo);
+  const int64_t blocks = (nq + 127) / 128 * ((m + kSearchKeys - 1) / kSearchKeys);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_search_scores<BITS>), dim3((unsigned)blocks), dim3(kSearchThreads), 0, st, qf, qnorm, nq, d,
+                     db->idx + base * W, db->norms + base, db->qjl + base * (d / 32), db->rnorms + base, m, cb, kth, k,
+                     out, ldo, masks, ldm);
   return hipGetLastError();
 }
 
 struct SearchLayout {
-  size_t qr, qs, qn, qf, sc, total;
+  size_t qr, qs, qn, qf, sc, mk, total;
   int64_t chunk;  // database vectors per score chunk
   int64_t ldo;    // score row stride (a multiple of 64 floats)
+  int64_t ldm;    // mask row stride: 64-vector groups per chunk
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -630,8 +765,10 @@ SearchLayout search_layout(int64_t nq, int64_t n, int d) {
   l.qs = l.qr + align256((size_t)nqp * d * 4);
   l.qn = l.qs + align256((size_t)nqp * d * 4);
   l.qf = l.qn + align256((size_t)nqp * 4);
+  l.ldm = l.ldo / 64;
   l.sc = l.qf + align256((size_t)(nqp / 128) * (d / 128) * 4096 * 16);
-  l.total = l.sc + align256((size_t)nq * l.ldo * 4);
+  l.mk = l.sc + align256((size_t)nq * l.ldo * 4);
+  l.total = l.mk + align256((size_t)nq * l.ldm * 8);
   return l;
 }
 
@@ -683,6 +820,7 @@ hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, c
   float* qn = reinterpret_cast<float*>(w + l.qn);
   u32x4* qf = reinterpret_cast<u32x4*>(w + l.qf);
   float* sc = reinterpret_cast<float*>(w + l.sc);
+  uint64_t* mk = reinterpret_cast<uint64_t*>(w + l.mk);
   // query prologue: unit rotated queries and norms, then the sketch S q / ||q|| = S' (R q / ||q||)
   const uint16_t* rfrag = d == kFragD ? rot->frag_dev : rot->gfrag_dev;
   const uint16_t* sfrag = d == kFragD ? qjl->frag_dev : qjl->gfrag_dev;
@@ -699,23 +837,27 @@ hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, c
   const int64_t n = db->n;
   int64_t base = 0;
   do {
-    const int64_t m = n - base < l.chunk ? n - base : l.chunk;
+    const int64_t cap = base == 0 ? kSearchFirstChunk : l.chunk;
+    const int64_t m = n - base < cap ? n - base : cap;
+    // after the first chunk the running k-th scores decide which scores are kept
+    const float* kth = base == 0 ? nullptr : top_s;
     if (m > 0) {
       switch (cb.bits) {
-        case 1: e = search_scores_launch<1>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
-        case 2: e = search_scores_launch<2>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
-        case 3: e = search_scores_launch<3>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
-        case 4: e = search_scores_launch<4>(qf, qn, nq, d, db, base, m, cb, sc, l.ldo, st); break;
+        case 1: e = search_scores_launch<1>(qf, qn, nq, d, db, base, m, cb, kth, k, sc, l.ldo, mk, l.ldm, st); break;
+        case 2: e = search_scores_launch<2>(qf, qn, nq, d, db, base, m, cb, kth, k, sc, l.ldo, mk, l.ldm, st); break;
+        case 3: e = search_scores_launch<3>(qf, qn, nq, d, db, base, m, cb, kth, k, sc, l.ldo, mk, l.ldm, st); break;
+        case 4: e = search_scores_launch<4>(qf, qn, nq, d, db, base, m, cb, kth, k, sc, l.ldo, mk, l.ldm, st); break;
         default: return hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;
     }
+    const int64_t groups = (m + 63) / 64;
     if (k <= 16)
-      hipLaunchKernelGGL(k_search_topk<16>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, m, base, k,
+      hipLaunchKernelGGL(k_search_topk<16>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, mk, l.ldm, groups, base, k,
                          base == 0 ? 1 : 0, top_s, top_i);
     else
-      hipLaunchKernelGGL(k_search_topk<kSearchMaxK>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, m, base, k,
-                         base == 0 ? 1 : 0, top_s, top_i);
+      hipLaunchKernelGGL(k_search_topk<kSearchMaxK>, dim3((unsigned)nq), dim3(256), 0, st, sc, l.ldo, mk, l.ldm, groups,
+                         base, k, base == 0 ? 1 : 0, top_s, top_i);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     base += m;

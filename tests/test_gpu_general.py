@@ -144,7 +144,8 @@ def _check_topk(got_s, got_i, ref_scores, k, tol):
             assert np.all(got_i[i, kk:] == -1) and np.all(np.isneginf(got_s[i, kk:]))
 
 
-@pytest.mark.parametrize("n,nq,k", [(3000, 100, 10), (70000, 20, 10), (5, 3, 10), (1000, 130, 32), (513, 1, 1)])
+@pytest.mark.parametrize("n,nq,k", [(3000, 100, 10), (70000, 20, 10), (5, 3, 10), (1000, 130, 32), (513, 1, 1),
+                                    (4100, 7, 5)])
 def test_search_topk(dev, handles, mats, n, nq, k):
     rot, qjl = handles
     rmat, smat = mats
@@ -176,6 +177,76 @@ def test_search_topk_d128(dev):
                              oracle.qjl_matrix(128, 2))
     tol = 1e-3 * np.linalg.norm(q, axis=1) * np.max(p.norms.cpu().numpy())
     _check_topk(top_s.cpu().numpy(), top_i.cpu().numpy(), ref, 10, tol)
+
+
+def _d128_handles():
+    rot = tq.make_rotation(128, 3, "wht")
+    return rot, tq.make_qjl(128, 4, rot), tq.codebook(128, 3)
+
+
+def _d128_ref(p, q):
+    encp = _packed_prod(p, 128, 3)
+    return oracle.scores_prod(q.astype(np.float64), encp, oracle.wht_rotation(128, 3), oracle.codebook(128, 3),
+                              oracle.qjl_matrix(128, 4))
+
+
+def test_search_topk_rising_scores(dev):
+    # Scores that rise with the index: every chunk after the first beats the running k-th result
+    # many times over, so the kept-score masks carry many bits in every chunk (a short first
+    # chunk, then chunks of 65536 vectors, the last one ragged).
+    rot, qjl, cb = _d128_handles()
+    n, nq = 230_000, 12
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    alpha = np.linspace(0.2, 3.0, n)[:, None]
+    x = (alpha * u[None, :] + 0.3 * rng.standard_normal((n, 128))).astype(np.float32)
+    q = (u[None, :] + 0.2 * rng.standard_normal((nq, 128))).astype(np.float32)
+    p = tq.encode(torch.from_numpy(x).to(dev), 4, "prod", cb, rot, qjl)
+    for k in (1, 10, 32):
+        top_s, top_i = tq.search_topk(torch.from_numpy(q).to(dev), p, k, cb, rot, qjl)
+        torch.cuda.synchronize()
+        ref = _d128_ref(p, q)
+        tol = 1e-3 * np.linalg.norm(q, axis=1) * np.max(p.norms.cpu().numpy())
+        _check_topk(top_s.cpu().numpy(), top_i.cpu().numpy(), ref, k, tol)
+
+
+def test_search_topk_equal_scores_across_chunks(dev):
+    # Rows copied within a chunk and across chunks encode to the same bits and so score the same;
+    # equal scores rank by the smaller index, and a copy in a later chunk that only equals the
+    # running k-th result is not kept.  Query i gets its own strong row, copied three times: into
+    # the next 512-vector block and into two later chunks (vectors 65536 and 131072 on lie in
+    # different chunks whatever the first chunk's length, which is at most 65536).
+    rot, qjl, cb = _d128_handles()
+    n, nq = 140_000, 6
+    x = wl.gaussian((n, 128), 21).astype(np.float32) * 0.05
+    q = wl.gaussian((nq, 128), 22).astype(np.float32)
+    copies = []
+    for i in range(nq):
+        src = 1000 + 7919 * i
+        dst = [src + 600 + 3 * i,              # the next 512-vector block
+               65536 + 123 * i + 5,
+               131072 + 17 * i + 1]
+        x[src] = 4.0 * q[i] / np.linalg.norm(q[i])
+        for j in dst:
+            x[j] = x[src]
+        copies.append(sorted([src] + dst))
+    p = tq.encode(torch.from_numpy(x).to(dev), 4, "prod", cb, rot, qjl)
+    words, norms = to_np_words(p.idx), p.norms.cpu().numpy()
+    for c in copies:
+        assert all(np.array_equal(words[c[0]], words[j]) and norms[c[0]] == norms[j] for j in c[1:])
+    ref = _d128_ref(p, q)
+    for k in (1, 2, 3, 4, 5):
+        top_s, top_i = tq.search_topk(torch.from_numpy(q).to(dev), p, k, cb, rot, qjl)
+        torch.cuda.synchronize()
+        gs, gi = top_s.cpu().numpy(), top_i.cpu().numpy()
+        for i in range(nq):
+            assert np.argmax(ref[i]) in copies[i]
+            m = min(k, 4)
+            assert gi[i, :m].tolist() == copies[i][:m], (k, i, gi[i].tolist(), copies[i])
+            assert np.all(gs[i, :m] == gs[i, 0]), (k, i, gs[i].tolist())
+            if k == 5:
+                assert gi[i, 4] not in copies[i] and gs[i, 4] < gs[i, 0]
 
 
 def test_search_errors(dev, handles):
