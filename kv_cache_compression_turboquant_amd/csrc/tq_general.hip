@@ -3,9 +3,10 @@
 //
 // Encode ([TQ] official steps 1-4 and TurboQuant_prod): the rotation is a tiled GEMM,
 // y^T = R x^T, on bf16 MFMA.  A block owns 128 vectors x one 128-coordinate output block ob
-// and loops over the 128-wide contraction chunks kc; the chunk's pre-swizzled R fragments are
-// staged through LDS and shared by the four waves, while each wave streams its 32 vectors
-// straight from HBM as the B operand.  With the fragment row order of the d = 128 kernel, lane
+// and loops over the contraction in halves of 64 coordinates; each half's pre-swizzled R
+// fragments stream into one of two LDS buffers (direct-to-LDS loads) and are shared by the four
+// waves, while each wave streams its 32 vectors from HBM as the B operand, one half ahead.
+// With the fragment row order of the d = 128 kernel, lane
 // (n, G) ends with coordinates 128 ob + 32 G .. + 31 of its vector, so the epilogue bucketizes
 // and packs whole words in registers.  The norm is accumulated from the B operand, so no
 // separate pass reads x.  Prod runs twice: the first GEMM also writes the rotated-domain
@@ -15,9 +16,9 @@
 // Search ([FP] inner-product bias and QJL fix): the queries are rotated and sketched by the same
 // GEMM kernel, converted once into fp16 MFMA fragments, and the scores are a second GEMM whose B
 // operand is decoded from the packed database on the fly (centroids through an LDS table; QJL
-// signs as +-(gamma / s) sqrt(pi/2) / d, so one accumulator holds both terms).  Scores of one
-// chunk of the database go to the workspace, and a per-query kernel merges them into the
-// running top-k.
+// signs as +-(gamma / s) sqrt(pi/2) / d, so one accumulator holds both terms).  The database is
+// scored in chunks; the scores of a chunk that can still enter a query's top-k go to the
+// workspace, and a per-query kernel merges them into the running top-k.
 #include "tq_decode.h"
 
 namespace tq {
@@ -29,29 +30,56 @@ static_assert(kGWaves * kGTiles * 16 == kGenVectors, "a block covers kGenVectors
 
 enum GenEpi { kEpiY = 0, kEpiMse = 1, kEpiRes = 2, kEpiSign = 3, kEpiRaw = 4 };
 
-// One lane's share of a 16-vector tile for one contraction chunk: 32 consecutive coordinates.
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at wave_dst + l, wave_dst being
+// the same for the whole wave.
+__device__ __forceinline__ void lds_dma16(const u32x4* src, u32x4* wave_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// A lane's input coordinates of one half chunk: for lane group g, coordinates 64 h + 8 g .. + 7 and
+// 64 h + 32 + 8 g .. + 7 of the chunk (the B operand of instructions 2 h and 2 h + 1, in the
+// column order of the general-d fragments).
 template <bool BF16IN>
-__device__ __forceinline__ void load_gen(const void* __restrict__ x, int64_t n, int d, int64_t row0, int kc,
-                                         int nl, int g, RawTile<BF16IN>& t) {
+struct RawHalf;
+template <>
+struct RawHalf<true> {
+  u32x4 v[2];
+};
+template <>
+struct RawHalf<false> {
+  f32x4 v[4];
+};
+
+template <bool BF16IN>
+__device__ __forceinline__ void load_gen_half(const void* __restrict__ x, int64_t n, int d, int64_t row0, int kc,
+                                              int h, int nl, int g, RawHalf<BF16IN>& t) {
   int64_t r = row0 + nl;
   if (r >= n) r = n - 1;
+  const int64_t off = r * d + 128 * kc + 64 * h + 8 * g;
   if constexpr (BF16IN) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + r * d + 128 * kc + 32 * g);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) t.v[s] = src[s];
+    const uint16_t* src = static_cast<const uint16_t*>(x) + off;
+    t.v[0] = *reinterpret_cast<const u32x4*>(src);
+    t.v[1] = *reinterpret_cast<const u32x4*>(src + 32);
   } else {
-    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + r * d + 128 * kc + 32 * g);
+    const float* src = static_cast<const float*>(x) + off;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t.v[j] = src[j];
+    for (int i = 0; i < 2; ++i) {
+      t.v[2 * i] = *reinterpret_cast<const f32x4*>(src + 32 * i);
+      t.v[2 * i + 1] = *reinterpret_cast<const f32x4*>(src + 32 * i + 4);
+    }
   }
 }
 
-// bf16 B operand (hi, and lo for fp32 input) of the four instructions; optional sum of squares.
+// bf16 B operands (hi, and lo for fp32 input) of the half's two instructions; optional sum of
+// squares of the coordinates.
 template <bool BF16IN, bool NORM>
-__device__ __forceinline__ void to_operand(const RawTile<BF16IN>& t, u32x4 (&hi)[4], u32x4 (&lo)[4], float& ss) {
+__device__ __forceinline__ void half_operand(const RawHalf<BF16IN>& t, u32x4 (&hi)[2], u32x4 (&lo)[2], float& ss) {
   if constexpr (BF16IN) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       hi[s] = t.v[s];
       if constexpr (NORM) {
         // plain-array copy before the bit cast (see the d = 128 encode)
@@ -66,16 +94,16 @@ __device__ __forceinline__ void to_operand(const RawTile<BF16IN>& t, u32x4 (&hi)
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       const f32x4 a = t.v[2 * s], b = t.v[2 * s + 1];
       const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       u32x4 h4, l4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x2 pr = {v[2 * j], v[2 * j + 1]};
-        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-        const f32x2 rem = {v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
-        h4[j] = h;
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        const f32x2 rem = {v[2 * j] - __uint_as_float(hb << 16), v[2 * j + 1] - __uint_as_float(hb & 0xffff0000u)};
+        h4[j] = hb;
         l4[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
         if constexpr (NORM) {
           ss = fmaf(v[2 * j], v[2 * j], ss);
@@ -102,15 +130,26 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void k_encode_gen(
     const void* __restrict__ x, int64_t n, int d, const u32x4* __restrict__ frag, float post_scale,
     CodebookArgs cb, float* __restrict__ norms, uint32_t* __restrict__ idx_out, float* __restrict__ y_out,
     float* __restrict__ res_out, float* __restrict__ rpart, uint32_t* __restrict__ qjl_out,
-    float* __restrict__ rnorm_out) {
+    float* __restrict__ rnorm_out, int og) {
   constexpr bool NORM = EPI != kEpiSign && EPI != kEpiRaw;
   constexpr bool SPLIT = !BF16IN;
   constexpr int H = 1 << (BITS - 1);
-  constexpr int PER = APASS * kFragU4 / (kGWaves * 64);
-  __shared__ u32x4 lds[APASS * kFragU4];
+  // the fragments of one half chunk (64 coordinates): APASS x 8 output tiles x 2 instructions
+  constexpr int HALF = APASS * 1024;
+  __shared__ u32x4 lds[2][HALF];
   const int nb = d >> 7;
-  const int64_t vt = (int64_t)blockIdx.x / nb;
-  const int ob = (int)((int64_t)blockIdx.x % nb);
+  int64_t vt = (int64_t)blockIdx.x / nb;
+  int ob = (int)((int64_t)blockIdx.x % nb);
+  if (og > 0) {
+    // Blocks go to the eight XCDs in turn (block L to XCD L % 8).  XCD x takes the output blocks
+    // of group x % og (whose R fragments stay in its L2) for every (8 / og)-th vector tile, and
+    // takes a tile's output blocks one after the other, so that they run together and read the
+    // tile's input rows from L2 once.  (The host sets og only where this is a bijection.)
+    const int64_t L = blockIdx.x, slot = L / 8;
+    const int xcd = (int)(L % 8), per = nb / og;
+    ob = (xcd % og) * per + (int)(slot % per);
+    vt = (slot / per) * (8 / og) + xcd / og;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int64_t row0 = vt * kGenVectors + wave * (kGTiles * 16);
@@ -124,48 +163,74 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void k_encode_gen(
 #pragma unroll
   for (int j = 0; j < kGTiles; ++j) ss[j] = 0.f;
 
-  // Blocks with the same output block read the same fragments in lockstep: each starts its
-  // staging at a different slice so that they do not all queue on one L2 channel.
-  const int rot0 = (int)(blockIdx.x % PER);
-  for (int kc = 0; kc < nb; ++kc) {
-    const u32x4* src = frag + (size_t)(ob * nb + kc) * 2 * kFragU4;
-    u32x4 stage[PER];
+  // The contraction runs in half chunks of 64 coordinates (instructions 2 h, 2 h + 1 of chunk
+  // kc).  While half q is multiplied, its successor's fragments stream into the other LDS buffer
+  // (direct-to-LDS loads, element e = p x 1024 + t x 128 + 64 i + lane) and each wave's next
+  // input coordinates into the registers half q has just converted, so every load has a whole
+  // half of MFMAs to arrive.
+  const u32x4* fsrc = frag + (size_t)ob * nb * 2 * kFragU4;
+  auto issue_frags = [&](int q) {
+    const u32x4* src = fsrc + (size_t)(q >> 1) * 2 * kFragU4 + (q & 1) * 128;
+    u32x4* dst = lds[q & 1];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) stage[i] = src[((i + rot0) % PER) * (kGWaves * 64) + threadIdx.x];
-    RawTile<BF16IN> raw[kGTiles];
+    for (int u = 0; u < HALF / (kGWaves * 64); ++u) {
+      const int e = u * (kGWaves * 64) + threadIdx.x;
+      lds_dma16(src + (e >> 10) * kFragU4 + ((e >> 7) & 7) * 256 + (e & 127), dst + u * (kGWaves * 64) + wave * 64);
+    }
+  };
+  const int nq = 2 * nb;
+  RawHalf<BF16IN> raw[kGTiles];
+  issue_frags(0);
 #pragma unroll
-    for (int j = 0; j < kGTiles; ++j) load_gen<BF16IN>(x, n, d, row0 + 16 * j, kc, nl, g, raw[j]);
-    __syncthreads();  // the previous chunk's fragments are no longer read
+  for (int j = 0; j < kGTiles; ++j) load_gen_half<BF16IN>(x, n, d, row0 + 16 * j, 0, 0, nl, g, raw[j]);
+  wait_vm_all();
+  __syncthreads();
+  for (int q = 0; q < nq; ++q) {
+    u32x4 bx[kGTiles][2], bxl[kGTiles][2];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) lds[((i + rot0) % PER) * (kGWaves * 64) + threadIdx.x] = stage[i];
-    u32x4 bx[kGTiles][4], bxl[kGTiles][4];
+    for (int j = 0; j < kGTiles; ++j) half_operand<BF16IN, NORM>(raw[j], bx[j], bxl[j], ss[j]);
+    if (q + 1 < nq) {
+      issue_frags(q + 1);
 #pragma unroll
-    for (int j = 0; j < kGTiles; ++j) to_operand<BF16IN, NORM>(raw[j], bx[j], bxl[j], ss[j]);
-    __syncthreads();
-    u32x4 cf[APASS][4], nf[APASS][4];
-    load_frags<APASS>(lds, 0, lane, cf);
+      for (int j = 0; j < kGTiles; ++j)
+        load_gen_half<BF16IN>(x, n, d, row0 + 16 * j, (q + 1) >> 1, (q + 1) & 1, nl, g, raw[j]);
+    }
+    const u32x4* lq = lds[q & 1];
+    u32x4 cf[APASS][2], nf[APASS][2];
+#pragma unroll
+    for (int p = 0; p < APASS; ++p)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) cf[p][i] = lq[p * 1024 + i * 64 + lane];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (t + 1 < 8) load_frags<APASS>(lds, t + 1, lane, nf);
+      if (t + 1 < 8) {
+#pragma unroll
+        for (int p = 0; p < APASS; ++p)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) nf[p][i] = lq[p * 1024 + (t + 1) * 128 + i * 64 + lane];
+      }
 #pragma unroll
       for (int j = 0; j < kGTiles; ++j) {
         f32x4 a = acc[j][t];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          a = mfma_bf16(cf[0][s], bx[j][s], a);
-          if constexpr (SPLIT) a = mfma_bf16(cf[0][s], bxl[j][s], a);
-          if constexpr (APASS == 2) a = mfma_bf16(cf[1][s], bx[j][s], a);
+        for (int i = 0; i < 2; ++i) {
+          a = mfma_bf16(cf[0][i], bx[j][i], a);
+          if constexpr (SPLIT) a = mfma_bf16(cf[0][i], bxl[j][i], a);
+          if constexpr (APASS == 2) a = mfma_bf16(cf[1][i], bx[j][i], a);
         }
         acc[j][t] = a;
+        __builtin_amdgcn_sched_barrier(0);  // one accumulator's MFMAs back to back
       }
       if (t + 1 < 8) {
 #pragma unroll
         for (int p = 0; p < APASS; ++p)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) cf[p][s] = nf[p][s];
+          for (int i = 0; i < 2; ++i) cf[p][i] = nf[p][i];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vm_all();   // the next half's fragments (in LDS) and input coordinates
+    __syncthreads();  // every wave is done with lds[q & 1] and sees lds[(q + 1) & 1]
   }
 
   const float inv_post = 1.0f / post_scale;
@@ -273,9 +338,20 @@ hipError_t gen_launch(const void* x, int64_t n, int d, const uint16_t* frag, flo
                       float* norms, uint32_t* idx, float* y, float* res, float* rpart, uint32_t* qbits, float* rn,
                       hipStream_t st) {
   const int64_t nvt = (n + kGenVectors - 1) / kGenVectors;
-  const int64_t blocks = nvt * (d / 128);
+  const int nb = d / 128;
+  const int64_t blocks = nvt * nb;
+  // output-block groups per XCD mapping: the fewest groups (most output blocks per XCD) whose R
+  // fragments fit a share of an XCD's 4 MB L2; 0 keeps the plain order
+  int og = 0;
+  for (int c : {1, 2, 4, 8}) {
+    const size_t rbytes = (size_t)(nb / c) * 128 * d * 2 * APASS;
+    if (nb % c == 0 && nvt % (8 / c) == 0 && rbytes <= (size_t)5 << 19) {
+      og = c;
+      break;
+    }
+  }
   hipLaunchKernelGGL((k_encode_gen<EPI, BF16IN, APASS, BITS>), dim3((unsigned)blocks), dim3(kGWaves * 64), 0, st,
-                     x, n, d, reinterpret_cast<const u32x4*>(frag), post, cb, norms, idx, y, res, rpart, qbits, rn);
+                     x, n, d, reinterpret_cast<const u32x4*>(frag), post, cb, norms, idx, y, res, rpart, qbits, rn, og);
   return hipGetLastError();
 }
 
@@ -382,14 +458,6 @@ constexpr int kSearchWaves = 8;
 constexpr int kSearchThreads = kSearchWaves * 64;
 static_assert(kSearchKeys == kSearchWaves * 64, "one 64-vector group per wave");
 static_assert(kSearchChunk % kSearchKeys == 0 && kSearchFirstChunk % kSearchKeys == 0, "chunks hold whole key blocks");
-
-__device__ __forceinline__ void lds_dma16(const u32x4* src, u32x4* wave_dst) {
-  // each lane's 16 bytes land at wave_dst + lane (the destination is the wave's base)
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 // The lane's key words of contraction chunk kc: for key tile j, the BITS index words of its 32
 // coordinates (byte offset krow[j] * wb + gi in the index resource) and its sign word (krow[j] * zb
@@ -822,8 +890,8 @@ hipError_t launch_search_topk(const float* q, int64_t nq, const tq_packed* db, c
   float* sc = reinterpret_cast<float*>(w + l.sc);
   uint64_t* mk = reinterpret_cast<uint64_t*>(w + l.mk);
   // query prologue: unit rotated queries and norms, then the sketch S q / ||q|| = S' (R q / ||q||)
-  const uint16_t* rfrag = d == kFragD ? rot->frag_dev : rot->gfrag_dev;
-  const uint16_t* sfrag = d == kFragD ? qjl->frag_dev : qjl->gfrag_dev;
+  const uint16_t* rfrag = rot->gfrag_dev;
+  const uint16_t* sfrag = qjl->gfrag_dev;
   hipError_t e = gen_dispatch<kEpiY, 1>(q, false, nq, d, rfrag, rot->passes, rot->post_scale, cb, qn, nullptr, qr,
                                         nullptr, nullptr, st);
   if (e != hipSuccess) return e;

@@ -330,8 +330,10 @@ void build_fragments32(const double* m, double scale, std::vector<uint16_t>& out
 }
 
 // Chunked fragments of a d x d matrix (d a multiple of 128) for the general-d GEMM kernels:
-// chunk (ob, kc) is the 128 x 128 block M[128 ob .., 128 kc ..] laid out exactly as
-// build_fragments lays out a d = 128 matrix; chunks follow each other as [ob][kc][pass].
+// chunk (ob, kc) is the 128 x 128 block M[128 ob .., 128 kc ..] with build_fragments' row order,
+// but instruction s of lane group g takes columns 32 s + 8 g .. + 7 of the chunk, so that
+// instructions 2 h and 2 h + 1 span the contiguous columns 64 h .. 64 h + 63 (the GEMM streams its
+// input in such halves); chunks follow each other as [ob][kc][pass].
 void build_fragments_g(const double* m, int d, double scale, std::vector<uint16_t>& out) {
   const int nb = d / 128;
   out.assign((size_t)nb * nb * 2 * tq::kFragElems, 0);
@@ -344,7 +346,7 @@ void build_fragments_g(const double* m, int d, double scale, std::vector<uint16_
           for (int e = 0; e < 8; ++e) {
             const int mm = lane % 16, g = lane / 16;
             const int row = 128 * ob + 32 * (mm / 4) + 4 * t + (mm % 4);
-            const int col = 128 * kc + 32 * g + 8 * s + e;
+            const int col = 128 * kc + 32 * s + 8 * g + e;
             const float v = (float)(m[(size_t)row * d + col] * scale);
             const uint16_t hi = bf16_rne(v);
             const uint16_t lo = bf16_rne(v - bf16_to_f(hi));
@@ -427,6 +429,12 @@ tq_status finish_rotation(tq_rotation_s* r) {
     if (st != TQ_OK) return st;
     st = upload(frag32, &r->frag32_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
+    // the general-d layout too: the search's query prologue runs the general-d GEMM at any d
+    const bool wht = r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT;
+    build_fragments_g(r->r.data(), d, wht ? std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup)) : 1.0,
+                      frag);
+    st = upload(frag, &r->gfrag_dev, "upload rotation fragments");
+    if (st != TQ_OK) return st;
   } else if (general_d(d)) {
     std::vector<uint16_t> frag;
     const bool wht = r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT;
@@ -475,6 +483,11 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
       if (st == TQ_OK) {
         build_fragments32(sp.data(), 1.0, frag);
         st = upload(frag, &q->frag32_dev, "upload qjl fragments");
+      }
+      if (st == TQ_OK) {
+        // the general-d layout too, for the search's query prologue
+        build_fragments_g(sp.data(), d, 1.0, frag);
+        st = upload(frag, &q->gfrag_dev, "upload qjl fragments");
       }
     } else {
       build_fragments_g(sp.data(), d, 1.0, frag);

@@ -56,9 +56,10 @@ struct tq_rotation_s {
   uint16_t* frag_dev = nullptr;   // bf16 fragments [2][kFragElems] (d = 128 only)
   uint16_t* fragt_dev = nullptr;  // bf16 B-operand fragments of R^T [2][kFragElems] (d = 128):
                                   // [pass][cb][s][lane][e] = R[8*(lane%16) + cb][32*(lane/16) + 8s + e]
-  uint16_t* gfrag_dev = nullptr;  // general d (multiple of 128, >= 256): A fragments of R, one
+  uint16_t* gfrag_dev = nullptr;  // general-d GEMM (any d, d = 128 included): A fragments of R, one
                                   // (128 x 128) chunk per (output block ob, contraction block kc):
-                                  // [ob][kc][pass 0..1][kFragElems], each chunk laid out like frag_dev
+                                  // [ob][kc][pass 0..1][kFragElems], rows as in frag_dev, columns
+                                  // 32 s + 8 g + e for instruction s of lane group g
   uint16_t* frag32_dev = nullptr; // d = 128: A fragments for v_mfma_f32_32x32x16_bf16 [2][kFragElems]:
                                   // [pass][ob][s][lane][e] = R[o][c], i = lane % 32, j = lane / 32,
                                   // o = 64 ((i >> 2) & 1) + 16 ob + 4 (i >> 3) + (i & 3), c = 64 j + 8 s + e
