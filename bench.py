@@ -394,6 +394,32 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
         if cpu_budget > 0:
             res["cpu_baseline"] = cpu_baseline_prod(cfg, kind, cpu_budget)
+    elif name in ("c3mse", "c3msewht", "c3msebwht"):
+        # TurboQuant_mse (b = 3) of the C3 keys: dense R on the matrix cores against the randomized
+        # Hadamard rotations as the in-register butterfly transform
+        cfg = wl.CONFIGS["c3"]
+        kind = {"c3mse": "dense", "c3msewht": "wht", "c3msebwht": "block_wht"}[name]
+        b = cfg.bits - 1
+        n = cfg.B * cfg.hkv * cfg.T
+        keys = torch.from_numpy(wl.kv_keys(cfg).reshape(n, cfg.d).view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(wl.kv_queries(cfg)).to(dev)
+        rot = tq.make_rotation(cfg.d, 1, kind)
+        cb = tq.codebook(cfg.d, b)
+        nbuf = 3
+        packs = [tq.alloc_packed(n, cfg.d, b, "mse", device=dev) for _ in range(nbuf)]
+        outs = [torch.empty((cfg.B, cfg.hq, cfg.T), device=dev) for _ in range(nbuf)]
+        ws = torch.empty(tq.scores_workspace(cfg.B, cfg.hq, cfg.d), dtype=torch.uint8, device=dev)
+        enc_ms = _timed(lambda i: tq.encode(keys, b, "mse", cb, rot, out=packs[i % nbuf]), steps, warmup)
+        sc_ms = _timed(lambda i: tq.scores(q, packs[i % nbuf], cfg.hkv, cb, rot, out=outs[i % nbuf], ws=ws),
+                       steps, warmup)
+        enc_bytes = n * (cfg.d * 2 + cfg.d * b // 8 + 4)
+        sc_bytes = n * (cfg.d * b // 8 + 4) + q.numel() * 4 + outs[0].numel() * 4
+        res.update({"rotation": kind, "encode_ms": enc_ms, "encode_gbs": enc_bytes / enc_ms / 1e6,
+                    "encode_hbm_frac": enc_bytes / enc_ms / 1e6 / HBM_PEAK_GBS,
+                    "encode_vectors_per_s": n / enc_ms * 1e3,
+                    "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
+                    "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
+                    "scores_per_s": outs[0].numel() / sc_ms * 1e3})
     elif name in ("c4b2", "c4b4"):
         cfg = wl.CONFIGS["c4"]
         b = 2 if name == "c4b2" else 4
@@ -853,7 +879,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c4b2", "c4b4", "c5", "decode",
+    ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c3mse", "c3msewht", "c3msebwht", "c4b2", "c4b4", "c5", "decode",
                                                         "decodeb4", "peaks", "c2split", "c2split35", "c3split", "c2splitdecode", "c2o8", "c4o8", "c4split",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "

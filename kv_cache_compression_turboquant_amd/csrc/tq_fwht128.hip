@@ -1,0 +1,177 @@
+// TurboQuant_mse encode at d = 128 with the randomized Hadamard rotation done as a fast
+// Walsh-Hadamard transform in registers ("TurboQuant 和 RotorQuant 的真相", chapter 3, the
+// custom WHT kernel; "Sub-byte KV cache quantization with TurboQuant", engineering path: the
+// transform as an O(d log d) butterfly rather than a d x d product).
+//
+// R = H diag(sigma) / sqrt(d) (or, for the block rotation, blockdiag(H_32) diag(sigma) / sqrt(32)),
+// so y = R x takes a sign flip and the butterflies of H.  Four consecutive lanes hold one vector,
+// lane u of the quad coordinates 32 u .. 32 u + 31:
+//   * the sign flip is an XOR of the fp32 sign bits with the lane's 32 bits of sigma;
+//   * butterfly stages over coordinate bits 0..4 run inside the lane's registers;
+//   * stages over bits 5 and 6 (the full transform only) exchange registers with the partner
+//     lane u ^ 1, then u ^ 2, through DPP quad permutes, the butterfly being one fma with +-1;
+//   * the norm is the lane's sum of squares reduced over the quad the same way.
+// The Hadamard output keeps the input's index order, so each lane then owns the rotated
+// coordinates 32 u .. 32 u + 31: it quantizes them (sign-magnitude thresholds scaled by the norm,
+// as the MFMA encode) and writes its BITS words of the packed row itself.  No LDS, no MFMA.
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+constexpr int kFwhtThreads = 256;  // 64 vectors per block
+
+// Partner value in lane ^ 1 (CTRL 0xB1) or lane ^ 2 (CTRL 0x4E) of the quad.
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int BITS, bool BF16IN, bool FULL>
+__global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* __restrict__ x, int64_t n,
+                                                                   uint4 sigma, float rscale, CodebookArgs cb,
+                                                                   uint32_t* __restrict__ idx_out,
+                                                                   float* __restrict__ norms) {
+  constexpr int H = 1 << (BITS - 1);
+  const int lane = threadIdx.x & 63;
+  const int u = lane & 3;
+  const int64_t row = ((int64_t)blockIdx.x * kFwhtThreads + threadIdx.x) >> 2;
+  const int64_t r = row < n ? row : n - 1;
+
+  // the lane's 32 input coordinates
+  float v[32];
+  if constexpr (BF16IN) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + r * 128 + 32 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
+  } else {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + r * 128 + 32 * u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 w = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+    }
+  }
+
+  // norm over the quad
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss = fmaf(v[i], v[i], ss);
+  ss += quad_swap<0xB1>(ss);
+  ss += quad_swap<0x4E>(ss);
+  const float nrm = sqrtf(ss);
+
+  // sign flip: bit i of the lane's sigma word is 1 where sigma = -1
+  const uint32_t sw = u == 0 ? sigma.x : u == 1 ? sigma.y : u == 2 ? sigma.z : sigma.w;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sw >> i) & 1u) << 31));
+
+  // butterflies over coordinate bits 0..4, inside the lane
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  if constexpr (FULL) {
+    // bits 5 and 6: the partner lane holds the other half of each pair; the upper lane keeps a - b
+    const float s1 = (u & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = fmaf(s1, v[i], quad_swap<0xB1>(v[i]));
+    const float s2 = (u & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = fmaf(s2, v[i], quad_swap<0x4E>(v[i]));
+  }
+
+  // Sign-magnitude decisions against the thresholds t_p * ||x|| / rscale (v is sqrt(g) times the
+  // unit coordinate's scale): idx = (m ^ sign) + K/2, m = #{p : |v| >= t_p}; a zero vector gives
+  // K/2 everywhere (thresholds +inf, and its -0 coordinates counted as non-negative).
+  const bool live = nrm > 0.f;
+  const float tsc = nrm * rscale;
+  float thr[H > 1 ? H - 1 : 1];
+#pragma unroll
+  for (int p = 0; p < H - 1; ++p) thr[p] = live ? __int_as_float(cb.tpos[p]) * tsc : INFINITY;
+  uint32_t w[BITS];
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) w[b] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = v[i];
+    const float a = fabsf(y);
+    uint32_t m = 0;
+    if constexpr (BITS == 2) {
+      m = a >= thr[0] ? 1u : 0u;
+    } else if constexpr (BITS == 3) {
+      const bool hi = a >= thr[1];
+      const bool lo = a >= (hi ? thr[2] : thr[0]);
+      m = (hi ? 2u : 0u) | (lo ? 1u : 0u);
+    } else if constexpr (BITS == 4) {
+      const bool b2 = a >= thr[3];
+      const bool b1 = a >= (b2 ? thr[5] : thr[1]);
+      const float t0 = b2 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]);
+      const bool b0 = a >= t0;
+      m = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+    }
+    const uint32_t sgn = live ? (uint32_t)(__float_as_int(y) >> 31) : 0u;
+    const uint32_t id = ((m ^ sgn) + (uint32_t)H) & ((1u << BITS) - 1u);
+    const int p = BITS * i, wi = p >> 5, sh = p & 31;
+    w[wi] |= id << sh;
+    if (sh + BITS > 32) w[wi + 1] |= id >> (32 - sh);
+  }
+  if (row < n) {
+    uint32_t* dst = idx_out + row * (4 * BITS) + BITS * u;
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) dst[b] = w[b];
+    if (u == 0) norms[row] = nrm;
+  }
+}
+
+template <int BITS, bool BF16IN>
+hipError_t fwht_launch(const void* x, int64_t n, bool full, uint4 sigma, float rscale, const CodebookArgs& cb,
+                       uint32_t* idx, float* norms, hipStream_t st) {
+  const int64_t blocks = (n * 4 + kFwhtThreads - 1) / kFwhtThreads;
+  if (full)
+    hipLaunchKernelGGL((k_encode_fwht_d128<BITS, BF16IN, true>), dim3((unsigned)blocks), dim3(kFwhtThreads), 0, st,
+                       x, n, sigma, rscale, cb, idx, norms);
+  else
+    hipLaunchKernelGGL((k_encode_fwht_d128<BITS, BF16IN, false>), dim3((unsigned)blocks), dim3(kFwhtThreads), 0,
+                       st, x, n, sigma, rscale, cb, idx, norms);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t fwht_dispatch(const void* x, bool bf16, int64_t n, bool full, uint4 sigma, float rscale,
+                         const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st) {
+  return bf16 ? fwht_launch<BITS, true>(x, n, full, sigma, rscale, cb, idx, norms, st)
+              : fwht_launch<BITS, false>(x, n, full, sigma, rscale, cb, idx, norms, st);
+}
+
+}  // namespace
+
+hipError_t launch_encode_fwht_d128(const void* x, bool bf16, int64_t n, bool full, const uint32_t sigma_bits[4],
+                                   float rscale, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                   hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n > ((int64_t)1 << 40)) return hipErrorInvalidValue;
+  const uint4 sigma = make_uint4(sigma_bits[0], sigma_bits[1], sigma_bits[2], sigma_bits[3]);
+  switch (cb.bits) {
+    case 1: return fwht_dispatch<1>(x, bf16, n, full, sigma, rscale, cb, idx, norms, st);
+    case 2: return fwht_dispatch<2>(x, bf16, n, full, sigma, rscale, cb, idx, norms, st);
+    case 3: return fwht_dispatch<3>(x, bf16, n, full, sigma, rscale, cb, idx, norms, st);
+    case 4: return fwht_dispatch<4>(x, bf16, n, full, sigma, rscale, cb, idx, norms, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -838,6 +838,19 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
     return check_launch(tq::launch_encode_vblock_d128(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx,
                                                       out->norms, as_stream(stream)),
                         fn);
+  if (!prod && (rot->kind == TQ_ROT_WHT || rot->kind == TQ_ROT_BLOCK_WHT) && cb->args.sym) {
+    // randomized Hadamard: the butterfly transform in registers.  R = H_g-blocks diag(sigma) / sqrt(g)
+    // and the first row of each Hadamard block is all ones, so sigma_j is the sign of R's entry in
+    // the first row of j's block.
+    const bool full = rot->kind == TQ_ROT_WHT;
+    const int g = full ? tq::kFragD : kBlockWhtGroup;
+    uint32_t sigma[4] = {0, 0, 0, 0};
+    for (int j = 0; j < tq::kFragD; ++j)
+      if (rot->r[(size_t)(j / g * g) * tq::kFragD + j] < 0.0) sigma[j >> 5] |= 1u << (j & 31);
+    return check_launch(tq::launch_encode_fwht_d128(x_dev, dt == TQ_BF16, n, full, sigma, (float)std::sqrt((double)g),
+                                                    cb->args, out->idx, out->norms, as_stream(stream)),
+                        fn);
+  }
   return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args,
                                              out->idx, out->norms, prod ? out->qjl : nullptr,
                                              prod ? out->rnorms : nullptr, nullptr, as_stream(stream)),

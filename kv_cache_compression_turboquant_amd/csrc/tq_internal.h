@@ -123,6 +123,13 @@ hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const Codeb
                                    uint32_t* idx, hipStream_t st);
 hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
                          const tq_qjl_s* qjl, float* xhat, hipStream_t st);
+// TurboQuant_mse encode at d = 128 (rows layout) for the randomized Hadamard rotations, as a
+// fast Walsh-Hadamard transform in registers: full = true for H diag(sigma) / sqrt(128), false for
+// blockdiag(H_32) diag(sigma) / sqrt(32); sigma_bits bit j set where sigma_j = -1; rscale = sqrt
+// of the Hadamard size.  Needs a symmetric codebook (cb.sym).
+hipError_t launch_encode_fwht_d128(const void* x, bool bf16, int64_t n, bool full, const uint32_t sigma_bits[4],
+                                   float rscale, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                   hipStream_t st);
 hipError_t launch_encode_vblock_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                                      const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);
 hipError_t launch_decode_attn(const float* q, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
