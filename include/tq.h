@@ -31,10 +31,12 @@
  *  - Sizes: 1 <= b <= 4 bits per index stage; d * b must be a multiple of 32.  Vector length
  *    d: the fused kernels cover d = 128, the head dimension of the KV workloads.  tq_encode,
  *    tq_decode, tq_rotate and tq_search_topk also take d a multiple of 128 in [256, 4096] (the
- *    embedding workloads, d = 1536 among them) on the general-d kernels.  The score, attention,
- *    cache, prefill, split and outlier-8 entry points take d = 128 only and return
- *    TQ_EUNSUPPORTED for any other d (head_dim 64 or 256 is not covered; d = 64 appears only as
- *    the half-vectors of the split codes).
+ *    embedding workloads, d = 1536 among them) on the general-d kernels.  Head dims 64 and 256
+ *    ("Sub-byte KV cache quantization with TurboQuant", deployment checklist: the codebook d is
+ *    the model's head_dim): tq_encode (rows layout; d = 64 on its own kernel), tq_scores,
+ *    tq_scores_cache and tq_decode_attn (V in the rows layout) take them on the kernels of
+ *    csrc/tq_kvgen.hip.  The prepared and static-scratch scores, the cache appends, prefill, split
+ *    and outlier-8 entry points take d = 128 only.  Any other d returns TQ_EUNSUPPORTED.
  */
 #ifndef TQ_H_
 #define TQ_H_
@@ -171,7 +173,9 @@ size_t tq_packed_idx_words(int64_t n, int d, int bits, tq_layout layout);
  * qjl must be non-NULL exactly for prod and bound to `rot`.  out->d, out->bits, out->mode,
  * out->n must describe the call; out->idx/norms (and qjl/rnorms for prod) are written.
  * A zero vector encodes to norm 0 and the indices of y = 0.
- * Supported d: 128 (one fused kernel; rows or token-blocked layout), or a multiple of 128 in
+ * Supported d: 128 (one fused kernel; rows or token-blocked layout; the randomized Hadamard
+ * rotations in MSE mode as a butterfly transform in registers), 64 (rows layout; one wave per
+ * vector, the rotation and the QJL sketch as fp32 matrix-vector products), or a multiple of 128 in
  * [256, 4096] (rows layout; rotation as a tiled MFMA GEMM whose epilogue quantizes and packs;
  * prod adds a second GEMM with S' on the residual, staged through ws_dev in chunks of vectors).
  * ws_dev / ws_bytes: caller device workspace, at least tq_encode_workspace(n, d, b, mode) bytes
@@ -209,7 +213,8 @@ size_t tq_scores_workspace(int B, int Hq, int d);
  * ([SB] third layer); query head h reads kv head h / (Hq / Hkv) ([SB] GQA mapping).
  * MSE: s <R q, C[idx]>;  prod: plus gamma sqrt(pi/2)/d <S q, z> ([TQ] TurboQuant_prod;
  * [FP] QJL constant).  The GQA ratio Hq / Hkv must be 1, 2, 3 or 4, or a multiple of 4 up to 64
- * (TQ_EUNSUPPORTED otherwise); d = 128. */
+ * (TQ_EUNSUPPORTED otherwise); d = 128, 64 or 256 (the last two: R q and S q in fp32, one thread
+ * per key). */
 tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                     tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev,
                     void* ws_dev, size_t ws_bytes, void* stream);
@@ -222,7 +227,7 @@ tq_status tq_scores(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const
  * device.  Nothing is allocated: no hipMalloc, no hipFree, no allocating library call.  Every call
  * on one GPU uses the same array, so calls whose work overlaps on one GPU (other streams, other
  * threads) race and may return wrong scores: serialise them.  Errors as for tq_scores, plus
- * TQ_ENOMEM when tq_scores_workspace(B, Hq, d) exceeds the static size. */
+ * TQ_ENOMEM when tq_scores_workspace(B, Hq, d) exceeds the static size; d = 128 only. */
 tq_status tq_scores_noalloc(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                             tq_codebook_t cb, tq_rotation_t rot, tq_qjl_t qjl, float* scores_dev, void* stream);
 size_t tq_scores_noalloc_max_bytes(void);
@@ -234,7 +239,7 @@ size_t tq_scores_noalloc_max_bytes(void);
  * tq_scores_workspace(B, Hq, d) bytes) ([SB] third layer: the query is rotated once).
  * tq_scores_prepared: the scores of tq_scores from such a workspace.  The workspace must have been
  * prepared with the same B, Hq, Hkv and rotation as the keys, and with the keys' qjl handle when K
- * is prod mode (the device contents are not checked).  Errors as for tq_scores. */
+ * is prod mode (the device contents are not checked).  Errors as for tq_scores; d = 128 only. */
 tq_status tq_prepare_queries(const float* q_dev, int B, int Hq, int Hkv, tq_rotation_t rot, tq_qjl_t qjl,
                              void* ws_dev, size_t ws_bytes, void* stream);
 tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq, int Hkv, int64_t T,
@@ -247,9 +252,10 @@ size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d);
  * never materialising K_hat or V_hat; K and V stored TurboQuant_mse per [SB]).
  * out[b, h] = sum_t softmax_t(scale * <q[b,h], k_hat[b,g,t]>) v_hat[b,g,t], g = h / (Hq/Hkv),
  * k_hat = s_k R_K^T C_K[idx], v_hat = s_v R_V^T C_V[idx].  q_dev [B, Hq, d] fp32; K: ROWS
- * layout, MSE, n = B*Hkv*T; V: TOKEN_BLOCKED layout, MSE, n = B*Hkv*T; out_dev [B, Hq, d] fp32.
- * The value sum is accumulated in V's rotated domain and R_V^T is applied once per head.
- * Requires d = 128, T >= 1, Hq/Hkv in {1, 2, 4}.  Errors as for tq_scores; TQ_EINVAL for T < 1. */
+ * layout, MSE, n = B*Hkv*T; V: MSE, n = B*Hkv*T, TOKEN_BLOCKED layout at d = 128 and ROWS layout
+ * at d = 64 or 256; out_dev [B, Hq, d] fp32.  The value sum is accumulated in V's rotated domain
+ * and R_V^T is applied once per head.  Requires T >= 1 and d = 128 with Hq/Hkv in {1, 2, 4}, or
+ * d = 64 or 256 with Hq/Hkv <= 8.  Errors as for tq_scores; TQ_EINVAL for T < 1. */
 tq_status tq_decode_attn(const float* q_dev, int B, int Hq, int Hkv, int64_t T, const tq_packed* K,
                          const tq_packed* V, tq_codebook_t cb_k, tq_codebook_t cb_v,
                          tq_rotation_t rot_k, tq_rotation_t rot_v, float scale, float* out_dev,

@@ -301,8 +301,8 @@ def decode_attn_workspace(B, Hq, Hkv, T, d):
 
 
 def decode_attn(q, K, V, Hkv, cb_k, cb_v, rot_k, rot_v, scale=None, out=None, ws=None):
-    """softmax(scale <q, k_hat>) v_hat for q [B, Hq, d] fp32; K rows-layout, V blocked-layout,
-    both laid out [B, Hkv, T]."""
+    """softmax(scale <q, k_hat>) v_hat for q [B, Hq, d] fp32; K rows-layout, V blocked-layout at
+    d = 128 (rows-layout at d = 64 or 256), both laid out [B, Hkv, T]."""
     torch = _torch()
     B, Hq, d = q.shape
     T = K.n // max(B * Hkv, 1)

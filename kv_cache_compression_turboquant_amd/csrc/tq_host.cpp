@@ -811,15 +811,15 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   } else if (qjl) {
     return fail(TQ_EINVAL, "%s: qjl handle given for MSE mode", fn);
   }
-  if (d != tq::kFragD && !general_d(d))
-    return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d = 128, or a multiple of 128 in [256, 4096])", fn, d);
+  if (d != tq::kFragD && d != 64 && !general_d(d))
+    return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d = 64, 128, or a multiple of 128 in [256, 4096])", fn, d);
   if (!cb->args.sym) return fail(TQ_EUNSUPPORTED, "%s: the encode kernels need an antisymmetric codebook", fn);
   tq_status st = check_packed(out, d, stage, mode, fn);
   if (st != TQ_OK) return st;
   if (out->n != n) return fail(TQ_ESHAPE, "%s: out->n=%lld, n=%lld", fn, (long long)out->n, (long long)n);
   if (d != tq::kFragD && out->layout != TQ_LAYOUT_ROWS)
     return fail(TQ_EUNSUPPORTED, "%s: the token-blocked layout needs d = 128", fn);
-  if (d != tq::kFragD && mode == TQ_MODE_PROD && n > 0) {
+  if (general_d(d) && mode == TQ_MODE_PROD && n > 0) {
     const size_t per = tq::encode_general_ws_per_vector(d);
     if (!ws_dev) return fail(TQ_EINVAL, "%s: prod at d=%d needs a workspace", fn, d);
     if (ws_bytes < per * (size_t)std::min<int64_t>(n, tq::kGenVectors))
@@ -828,6 +828,11 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   }
   if (n == 0) return ok();
   const bool prod = mode == TQ_MODE_PROD;
+  if (d == 64)
+    return check_launch(tq::launch_encode_d64(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args, out->idx,
+                                              out->norms, prod ? out->qjl : nullptr, prod ? out->rnorms : nullptr,
+                                              as_stream(stream)),
+                        fn);
   if (d != tq::kFragD)
     return check_launch(tq::launch_encode_general(x_dev, dt == TQ_BF16, n, d, rot, prod ? qjl : nullptr, cb->args,
                                                   out->idx, out->norms, prod ? out->qjl : nullptr,
@@ -915,9 +920,12 @@ tq_status tq_decode(const tq_packed* p, tq_codebook_t cb, tq_rotation_t rot, tq_
   return check_launch(tq::launch_decode(p, cb->args, rot, qjl, xhat_dev, as_stream(stream)), fn);
 }
 
+// Head dims with the KV-side kernels of csrc/tq_kvgen.hip (d = 128 has its own).
+static bool kv_generic_d(int d) { return d == 64 || d == 256; }
+
 size_t tq_scores_workspace(int B, int Hq, int d) {
   if (B < 0 || Hq < 0 || d <= 0) return 0;
-  return tq::scores_workspace_bytes(B, Hq, d);
+  return kv_generic_d(d) ? tq::kv_gen_query_bytes(B, Hq, d) : tq::scores_workspace_bytes(B, Hq, d);
 }
 
 // Shape rules shared by the score entry points.
@@ -951,7 +959,7 @@ static tq_status check_score_keys(int B, int Hkv, int64_t T, int64_t rows, const
     return fail(TQ_ESHAPE, "%s: K->n=%lld but B*Hkv*%lld=%lld", fn, (long long)K->n, (long long)rows,
                 (long long)B * Hkv * rows);
   if (K->mode != TQ_MODE_PROD && K->mode != TQ_MODE_MSE) return fail(TQ_EINVAL, "%s: bad mode", fn);
-  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if (d != tq::kFragD && !kv_generic_d(d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (64, 128, 256)", fn, d);
   return TQ_OK;
 }
 
@@ -979,6 +987,7 @@ tq_status tq_scores_prepared(const void* ws_dev, size_t ws_bytes, int B, int Hq,
   if (st != TQ_OK) return st;
   st = check_score_keys(B, Hkv, T, T, K, cb, K->d, fn);
   if (st != TQ_OK) return st;
+  if (K->d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, K->d);
   if ((int64_t)(Hq / Hkv) * T >= (int64_t(1) << 30))
     return fail(TQ_EUNSUPPORTED, "%s: (Hq/Hkv)*T=%lld: a kv head's score rows must stay below 4 GB", fn,
                 (long long)(Hq / Hkv) * T);
@@ -1014,7 +1023,9 @@ static tq_status scores_impl(const char* fn, const float* q_dev, int B, int Hq, 
   }
   if ((int64_t)B * Hq * T == 0) return ok();
   if (!q_dev || !scores_dev) return fail(TQ_EINVAL, "%s: null q or scores", fn);
-  size_t need = tq::scores_workspace_bytes(B, Hq, d);
+  const bool gen = d != tq::kFragD;
+  size_t need = gen ? tq::kv_gen_query_bytes(B, Hq, d) : tq::scores_workspace_bytes(B, Hq, d);
+  if (use_scratch && gen) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
   if (use_scratch) {
     if (need > tq::noalloc_scratch_bytes())
       return fail(TQ_ENOMEM, "%s: B*Hq=%lld query heads need %zu bytes of scratch, above the static %zu bytes",
@@ -1025,6 +1036,10 @@ static tq_status scores_impl(const char* fn, const float* q_dev, int B, int Hq, 
   }
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
   hipStream_t hs = as_stream(stream);
+  if (gen)
+    return check_launch(tq::launch_scores_gen(q_dev, B, Hq, Hkv, T, rows, K, cb->args, rot,
+                                              K->mode == TQ_MODE_PROD ? qjl : nullptr, scores_dev, ws_dev, hs),
+                        fn);
   hipError_t e = tq::launch_prepare_queries(q_dev, B, Hq, Hkv, rot, K->mode == TQ_MODE_PROD ? qjl : nullptr, ws_dev, hs);
   if (e == hipSuccess) e = tq::launch_scores_strided(B, Hq, Hkv, T, rows, K, cb->args, scores_dev, ws_dev, hs);
   return check_launch(e, fn);
@@ -1053,7 +1068,8 @@ tq_status tq_scores_cache(const float* q_dev, int B, int Hq, int Hkv, int64_t T,
 
 size_t tq_decode_attn_workspace(int B, int Hq, int Hkv, int64_t T, int d) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || d <= 0) return 0;
-  return tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
+  return kv_generic_d(d) ? tq::attn_gen_workspace_bytes(B, Hq, Hkv, T, d)
+                         : tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
 }
 
 // rows: rows per sequence in K and V (T for packed [B, Hkv, T] sets, the capacity for a cache,
@@ -1073,25 +1089,34 @@ static tq_status decode_attn_impl(const char* fn, const float* q_dev, int B, int
                 (long long)kMaxSeqTokens);
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return fail(TQ_ESHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
   const int ratio = Hq / Hkv;
-  if (ratio != 1 && ratio != 2 && ratio != 4) return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not in {1, 2, 4}", fn, ratio);
   const int d = rot_k->d;
+  const bool gen = kv_generic_d(d);
+  if (gen ? ratio > 8 : (ratio != 1 && ratio != 2 && ratio != 4))
+    return fail(TQ_EUNSUPPORTED, "%s: GQA ratio %d not supported at d=%d (%s)", fn, ratio, d,
+                gen ? "at most 8" : "1, 2 or 4");
   if (rot_v->d != d || cb_k->d != d || cb_v->d != d) return fail(TQ_ESHAPE, "%s: d mismatch between handles", fn);
   tq_status st = check_packed(K, d, cb_k->b, TQ_MODE_MSE, fn);
   if (st != TQ_OK) return st;
   st = check_packed(V, d, cb_v->b, TQ_MODE_MSE, fn);
   if (st != TQ_OK) return st;
   if (K->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: K must use the ROWS layout", fn);
-  if (V->layout != TQ_LAYOUT_TOKEN_BLOCKED) return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout", fn);
+  if (!gen && V->layout != TQ_LAYOUT_TOKEN_BLOCKED)
+    return fail(TQ_EUNSUPPORTED, "%s: V must use the TOKEN_BLOCKED layout at d=128", fn);
+  if (gen && V->layout != TQ_LAYOUT_ROWS) return fail(TQ_EUNSUPPORTED, "%s: V must use the ROWS layout at d=%d", fn, d);
   const int64_t n = (int64_t)B * Hkv * rows;
   if (K->n != n || V->n != n)
     return fail(TQ_ESHAPE, "%s: K->n=%lld, V->n=%lld, B*Hkv*%lld=%lld", fn, (long long)K->n, (long long)V->n,
                 (long long)rows, (long long)n);
-  if (d != tq::kFragD) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (d=128)", fn, d);
+  if (d != tq::kFragD && !gen) return fail(TQ_EUNSUPPORTED, "%s: d=%d not supported (64, 128, 256)", fn, d);
   if ((int64_t)B * Hkv > 65535) return fail(TQ_EUNSUPPORTED, "%s: B*Hkv above 65535", fn);
   if ((int64_t)B * Hq == 0) return ok();
   if (!q_dev || !out_dev) return fail(TQ_EINVAL, "%s: null q or out", fn);
-  size_t need = tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
+  size_t need = gen ? tq::attn_gen_workspace_bytes(B, Hq, Hkv, T, d) : tq::decode_attn_workspace_bytes(B, Hq, Hkv, T, d);
   if (!ws_dev || ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (gen)
+    return check_launch(tq::launch_decode_attn_gen(q_dev, B, Hq, Hkv, T, rows, K, V, cb_k->args, cb_v->args, rot_k,
+                                                   rot_v, scale, out_dev, ws_dev, as_stream(stream)),
+                        fn);
   return check_launch(tq::launch_decode_attn_strided(q_dev, B, Hq, Hkv, T, rows, K, V, cb_k->args, cb_v->args, rot_k,
                                                      rot_v, scale, out_dev, ws_dev, as_stream(stream)),
                       fn);

@@ -123,6 +123,23 @@ hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const Codeb
                                    uint32_t* idx, hipStream_t st);
 hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
                          const tq_qjl_s* qjl, float* xhat, hipStream_t st);
+// Head dims 64 and 256 on the KV side (rows layout throughout): scores of queries q [B, Hq, d] over
+// packed keys at rows (b Hkv + g) rows + t; decode attention over packed K and V (MSE, rows layout,
+// GQA ratio <= 8); the d = 64 encode (MSE, or prod with qjl).  Workspaces: kv_gen_query_bytes for
+// the scores, attn_gen_workspace_bytes for the attention.
+size_t kv_gen_query_bytes(int B, int Hq, int d);
+size_t attn_gen_workspace_bytes(int B, int Hq, int Hkv, int64_t T, int d);
+hipError_t launch_scores_gen(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t rows, const tq_packed* K,
+                             const CodebookArgs& cb, const tq_rotation_s* rot, const tq_qjl_s* qjl, float* scores,
+                             void* ws, hipStream_t st);
+hipError_t launch_decode_attn_gen(const float* q, int B, int Hq, int Hkv, int64_t T, int64_t rows, const tq_packed* K,
+                                  const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
+                                  const tq_rotation_s* rot_k, const tq_rotation_s* rot_v, float scale, float* out,
+                                  void* ws, hipStream_t st);
+hipError_t launch_encode_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
+                             const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits, float* rnorms,
+                             hipStream_t st);
+
 // TurboQuant_mse encode at d = 128 (rows layout) for the randomized Hadamard rotations, as a
 // fast Walsh-Hadamard transform in registers: full = true for H diag(sigma) / sqrt(128), false for
 // blockdiag(H_32) diag(sigma) / sqrt(32); sigma_bits bit j set where sigma_j = -1; rscale = sqrt
