@@ -420,6 +420,41 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
                     "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
+    elif name in ("hd64", "hd256"):
+        # head dims 64 and 256: scores and decode attention of 32 query heads over 4 x 8 x 32768 keys
+        # and values (MSE, 4-bit keys, 2-bit values, dense R, bf16 inputs from the KV generator)
+        d = 64 if name == "hd64" else 256
+        B, hkv, hq, T, kb, vb = 4, 8, 32, 32768, 4, 2
+        n = B * hkv * T
+        rot = tq.make_rotation(d, 1)
+        cbk, cbv = tq.codebook(d, kb), tq.codebook(d, vb)
+        kx = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=1, outlier_seed=2, scale_seed=3)
+                              .reshape(n, d).view(np.int16)).to(dev).view(torch.bfloat16)
+        K = tq.encode(kx, kb, "mse", cbk, rot)
+        del kx
+        vx = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=4, outlier_seed=5, scale_seed=None)
+                              .reshape(n, d).view(np.int16)).to(dev).view(torch.bfloat16)
+        V = tq.encode(vx, vb, "mse", cbv, rot)
+        enc_ms = _timed(lambda i: tq.encode(vx, vb, "mse", cbv, rot, out=V), steps, warmup)
+        del vx
+        q = torch.from_numpy(wl.gaussian((B, hq, d), 6)).to(dev)
+        sc = torch.empty((B, hq, T), device=dev)
+        sws = torch.empty((tq.scores_workspace(B, hq, d),), dtype=torch.uint8, device=dev)
+        sc_ms = _timed(lambda i: tq.scores(q, K, hkv, cbk, rot, out=sc, ws=sws), steps, warmup)
+        out = torch.empty((B, hq, d), device=dev)
+        aws = torch.empty((tq.decode_attn_workspace(B, hq, hkv, T, d),), dtype=torch.uint8, device=dev)
+        at_ms = _timed(lambda i: tq.decode_attn(q, K, V, hkv, cbk, cbv, rot, rot, out=out, ws=aws), steps, warmup)
+        kbytes = n * (d * kb // 8 + 4)
+        vbytes = n * (d * vb // 8 + 4)
+        sc_bytes = kbytes + sc.numel() * 4
+        res.update({"head_dim": d, "keys": [B, hkv, T], "query_heads": hq, "k_bits": kb, "v_bits": vb,
+                    "value_encode_ms": enc_ms, "value_encode_frac_hbm": n * (2 * d + d * vb // 8 + 4) / enc_ms / 1e6
+                    / HBM_PEAK_GBS,
+                    "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
+                    "scores_frac_hbm": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
+                    "attention_ms": at_ms, "attention_gbs": (kbytes + vbytes) / at_ms / 1e6,
+                    "attention_frac_hbm": (kbytes + vbytes) / at_ms / 1e6 / HBM_PEAK_GBS,
+                    "kv_positions_per_s": n / at_ms * 1e3})
     elif name in ("c4b2", "c4b4"):
         cfg = wl.CONFIGS["c4"]
         b = 2 if name == "c4b2" else 4
@@ -879,7 +914,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the nested KV-key (c2) step line")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c3mse", "c3msewht", "c3msebwht", "c4b2", "c4b4", "c5", "decode",
+    ap.add_argument("--config", default="c3", choices=["c3", "c2", "c3wht", "c3bwht", "c3mse", "c3msewht", "c3msebwht", "hd64", "hd256", "c4b2", "c4b4", "c5", "decode",
                                                         "decodeb4", "peaks", "c2split", "c2split35", "c3split", "c2splitdecode", "c2o8", "c4o8", "c4split",
                                                         "prefill", "prefillb4"],
                     help="c3 = the headline step (c2 is its nested secondary line); the others print "

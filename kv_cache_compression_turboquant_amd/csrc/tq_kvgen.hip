@@ -35,7 +35,7 @@ __device__ __forceinline__ void gen_for(F&& f) {
 
 constexpr int kGenThreads = 256;
 constexpr int kGenHeadGroup = 8;   // query heads staged at once
-constexpr int kGenAttnTiles = 16;  // 256-key tiles per attention range
+constexpr int kGenAttnTiles = 4;   // 256-key tiles per attention range
 
 // ---------------------------------------------------------------------------------------
 // Query prologue: ws[h] = {R q_h (d floats), S q_h (d floats)}; one block of d threads per head.
@@ -186,11 +186,62 @@ __global__ __launch_bounds__(kGenThreads) void k_scores_gen(const float* __restr
 }
 
 // ---------------------------------------------------------------------------------------
-// Decode attention, one range of kGenAttnTiles tiles of one sequence per block; NH = the GQA
-// ratio (<= 8).  Partials per (sequence, range, head): m, l, then D accumulators.
+// Decode attention, one range of kGenAttnTiles tiles of one sequence per block; the GQA ratio
+// (<= 8) heads of the sequence's kv head at once.  Per tile of 256 keys:
+//   1. thread t stages key t's index words, its value's words and norms in LDS (one round of
+//      loads per tile);
+//   2. thread t forms key t's logits from the staged words (32 coordinates at a time);
+//   3. online softmax per head (block reductions); p * s_v per (head, key) into LDS;
+//   4. P V: thread (g4, kp) owns coordinates 4 g4 .. 4 g4 + 3 and the keys kp, kp + KP, ... of
+//      the tile, so one value word read serves its four coordinates.
+// Partials per (sequence, range, head): m, l, then D accumulators.
 // ---------------------------------------------------------------------------------------
 template <int D>
 constexpr int attn_gen_part() { return D + 2; }
+
+// Logits of one key whose index words sit in LDS (row kw, BITS words per 32 coordinates).
+template <int D, int BITS, int NH>
+__device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, const float* qh, const float* cent,
+                                                   int nh, float (&out)[NH]) {
+  float acc[NH];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) acc[k] = 0.f;
+#pragma unroll 1
+  for (int c = 0; c < D / 32; ++c) {
+    uint32_t wc[BITS];
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) wc[b] = kw[c * BITS + b];
+    float cv[32];
+    gen_for<0, 32>([&](auto ee) {
+      constexpr int e = decltype(ee)::value;
+      cv[e] = cent[field<BITS, e>(wc)];
+    });
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      if (k < nh) {
+        const f32x4* qr4 = reinterpret_cast<const f32x4*>(qh + k * 2 * D + 32 * c);
+#pragma unroll
+        for (int e4 = 0; e4 < 8; ++e4) {
+          const f32x4 qv = qr4[e4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[k] = fmaf(qv[e], cv[4 * e4 + e], acc[k]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NH; ++k) out[k] = s * acc[k];
+}
+
+template <int D, int KB, int VB>
+struct AttnGenLds {
+  static constexpr int WK = D * KB / 32, WV = D * VB / 32;
+  static constexpr int SK = WK + 1, SV = WV + 1;  // odd row strides: a thread's row reads hit distinct banks
+  static constexpr int KP = kGenThreads / (D / 4);  // key phases of the P V step
+  static constexpr int TILE_WORDS = kGenThreads * (SK + SV);
+  static constexpr int RED_WORDS = (KP - 1) * kGenHeadGroup * D;  // phase partials, after the last tile
+  static constexpr int REGION = TILE_WORDS > RED_WORDS ? TILE_WORDS : RED_WORDS;
+};
 
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restrict__ ws, int Hq, int Hkv, int64_t T,
@@ -200,16 +251,18 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
                                                          const uint32_t* __restrict__ vidx,
                                                          const float* __restrict__ vnorm, CodebookArgs cbk,
                                                          CodebookArgs cbv, float* __restrict__ parts) {
-  constexpr int WV = D * VB / 32;
-  constexpr int KP = kGenThreads / D;  // key phases of the P V step
+  using L = AttnGenLds<D, KB, VB>;
   constexpr int P = attn_gen_part<D>();
+  constexpr int KP = L::KP;
   __shared__ __attribute__((aligned(16))) float qh[kGenHeadGroup * 2 * D];
   __shared__ float centk[16], centv[16];
-  __shared__ float prob[kGenHeadGroup][kGenThreads];
-  __shared__ uint32_t vw[kGenThreads][WV + 1];  // +1: consecutive keys start on different banks
-  __shared__ float vs[kGenThreads];
+  __shared__ float pv[kGenHeadGroup][kGenThreads];   // p * s_v
+  __shared__ float ksn[kGenThreads];
   __shared__ float red[kGenHeadGroup][kGenThreads / 64];
-  __shared__ float accred[KP > 1 ? KP - 1 : 1][kGenHeadGroup][D];
+  __shared__ uint32_t region[L::REGION];
+  uint32_t* const kws = region;                         // [256][SK]
+  uint32_t* const vws = region + kGenThreads * L::SK;   // [256][SV]
+  float* const accred = reinterpret_cast<float*>(region);
   if (threadIdx.x < 16) {
     centk[threadIdx.x] = cbk.c[threadIdx.x];
     centv[threadIdx.x] = cbv.c[threadIdx.x];
@@ -219,14 +272,15 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
   const int nh = Hq / Hkv;
   const int64_t h0 = (int64_t)b * Hq + (int64_t)g * nh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ci = threadIdx.x % D, kp = threadIdx.x / D;
+  const int g4 = threadIdx.x % (D / 4), kp = threadIdx.x / (D / 4);
   stage_heads<D>(ws, h0, nh, qh);
-  float m[kGenHeadGroup], l[kGenHeadGroup], acc[kGenHeadGroup];
+  float m[kGenHeadGroup], l[kGenHeadGroup], acc[kGenHeadGroup][4];
 #pragma unroll
   for (int k = 0; k < kGenHeadGroup; ++k) {
     m[k] = -INFINITY;
     l[k] = 0.f;
-    acc[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[k][e] = 0.f;
   }
   const int64_t tile0 = (int64_t)split * kGenAttnTiles;
   const int64_t ntiles = (T + kGenThreads - 1) / kGenThreads;
@@ -234,18 +288,23 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
   for (int64_t tile = tile0; tile < tile1; ++tile) {
     const int64_t t = tile * kGenThreads + threadIdx.x;
     const bool valid = t < T;
-    const int64_t row = (int64_t)bg * rows + t;
-    __syncthreads();  // the previous tile's prob / vw / vs reads are done; qh staged
-    // this thread's key: logits of the group's heads
-    GenKey<D, KB, false> key;
-    load_gen_key<D, KB, false>(kidx, knorm, nullptr, nullptr, row, valid, key);
-    float lg[kGenHeadGroup];
-    gen_key_scores<D, KB, false, kGenHeadGroup>(key, qh, qh + D, centk, nh, lg);
-    // this thread's value words into LDS
+    const int64_t row = (int64_t)bg * rows + (valid ? t : 0);
+    __syncthreads();  // the previous tile's LDS reads are done (and qh is staged)
+    // 1. stage this thread's key and value words
+    {
+      const uint32_t* ks = kidx + row * L::WK;
+      const uint32_t* vs = vidx + row * L::WV;
 #pragma unroll
-    for (int i = 0; i < WV; ++i) vw[threadIdx.x][i] = valid ? vidx[row * WV + i] : 0u;
-    vs[threadIdx.x] = valid ? vnorm[row] : 0.f;
-    // tile maximum per head
+      for (int i = 0; i < L::WK; ++i) kws[threadIdx.x * L::SK + i] = ks[i];
+#pragma unroll
+      for (int i = 0; i < L::WV; ++i) vws[threadIdx.x * L::SV + i] = vs[i];
+      ksn[threadIdx.x] = valid ? knorm[row] : 0.f;
+    }
+    const float vsn = valid ? vnorm[row] : 0.f;
+    // 2. logits (a thread reads only its own staged row here)
+    float lg[kGenHeadGroup];
+    gen_key_logits_lds<D, KB, kGenHeadGroup>(kws + threadIdx.x * L::SK, ksn[threadIdx.x], qh, centk, nh, lg);
+    // 3. online softmax per head
 #pragma unroll
     for (int k = 0; k < kGenHeadGroup; ++k) {
       lg[k] = valid ? lg[k] * scale : -INFINITY;
@@ -255,37 +314,48 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
       if (lane == 0) red[k][wave] = mx;
     }
     __syncthreads();
-    float alpha[kGenHeadGroup];
+    float pk[kGenHeadGroup];  // this thread's key's probabilities (for l)
 #pragma unroll
     for (int k = 0; k < kGenHeadGroup; ++k) {
       float mx = red[k][0];
 #pragma unroll
       for (int w = 1; w < kGenThreads / 64; ++w) mx = fmaxf(mx, red[k][w]);
       const float mn = fmaxf(m[k], mx);
-      // a head past nh, or a tile of padding only, keeps m = -inf: no rescale, p = 0
-      alpha[k] = mn == -INFINITY ? 1.f : __expf(m[k] - mn);
+      const float alpha = mn == -INFINITY ? 1.f : __expf(m[k] - mn);
       const float p = mn == -INFINITY ? 0.f : __expf(lg[k] - mn);
-      prob[k][threadIdx.x] = p;
+      pv[k][threadIdx.x] = p * vsn;
+      pk[k] = p;
       m[k] = mn;
-      acc[k] *= alpha[k];
-      l[k] *= alpha[k];
-    }
-    __syncthreads();  // red reused below; prob, vw, vs visible
-    // P V: thread (ci, kp) takes keys kp, kp + KP, ... of the tile for coordinate ci
-    for (int tt = kp; tt < kGenThreads; tt += KP) {
-      const int bitpos = VB * ci;
-      const int wi = bitpos >> 5, sh = bitpos & 31;
-      uint32_t f = vw[tt][wi] >> sh;
-      if (sh + VB > 32) f |= vw[tt][wi + 1] << (32 - sh);
-      const float v = centv[f & ((1u << VB) - 1u)] * vs[tt];
+      l[k] *= alpha;
 #pragma unroll
-      for (int k = 0; k < kGenHeadGroup; ++k)
-        if (k < nh) acc[k] = fmaf(prob[k][tt], v, acc[k]);
+      for (int e = 0; e < 4; ++e) acc[k][e] *= alpha;
     }
-    // l: sum of the tile's probabilities (every thread keeps the same total)
+    __syncthreads();  // pv and the staged value words are visible; red is free
+    // 4. P V over coordinates 4 g4 .. 4 g4 + 3
+    {
+      const int bitpos = 4 * VB * g4;
+      const int wi = bitpos >> 5, sh = bitpos & 31;
+#pragma unroll 4
+      for (int tt = kp; tt < kGenThreads; tt += KP) {
+        uint32_t f = vws[tt * L::SV + wi] >> sh;
+        if (sh + 4 * VB > 32) f |= vws[tt * L::SV + wi + 1] << (32 - sh);
+        float cv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cv[e] = centv[(f >> (VB * e)) & ((1u << VB) - 1u)];
+#pragma unroll
+        for (int k = 0; k < kGenHeadGroup; ++k) {
+          if (k < nh) {
+            const float p = pv[k][tt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(p, cv[e], acc[k][e]);
+          }
+        }
+      }
+    }
+    // l: the tile's probabilities summed over the block
 #pragma unroll
     for (int k = 0; k < kGenHeadGroup; ++k) {
-      float sm = prob[k][threadIdx.x];
+      float sm = pk[k];
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
       if (lane == 0) red[k][wave] = sm;
@@ -299,31 +369,32 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
       l[k] += sm;
     }
   }
-  // merge the key phases (D = 64: four phases) and write the partials
-  if constexpr (KP > 1) {
-    __syncthreads();
-    if (kp > 0) {
+  // merge the key phases through LDS (the tile region is free now) and write the partials
+  __syncthreads();
+  if (kp > 0) {
 #pragma unroll
-      for (int k = 0; k < kGenHeadGroup; ++k) accred[kp - 1][k][ci] = acc[k];
-    }
-    __syncthreads();
-    if (kp == 0) {
+    for (int k = 0; k < kGenHeadGroup; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) accred[((kp - 1) * kGenHeadGroup + k) * D + 4 * g4 + e] = acc[k][e];
+  }
+  __syncthreads();
+  if (kp == 0) {
+#pragma unroll 1
+    for (int p = 0; p < KP - 1; ++p)
 #pragma unroll
       for (int k = 0; k < kGenHeadGroup; ++k)
 #pragma unroll
-        for (int p = 0; p < KP - 1; ++p) acc[k] += accred[p][k][ci];
-    }
-  }
-  if (kp == 0) {
+        for (int e = 0; e < 4; ++e) acc[k][e] += accred[(p * kGenHeadGroup + k) * D + 4 * g4 + e];
     float* dst = parts + ((int64_t)bg * nsplit + split) * kGenHeadGroup * P;
 #pragma unroll
     for (int k = 0; k < kGenHeadGroup; ++k) {
       if (k < nh) {
-        if (ci == 0) {
+        if (g4 == 0) {
           dst[k * P] = m[k];
           dst[k * P + 1] = l[k];
         }
-        dst[k * P + 2 + ci] = acc[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[k * P + 2 + 4 * g4 + e] = acc[k][e];
       }
     }
   }
