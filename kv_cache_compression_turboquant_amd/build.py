@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libtq.so")
 
 SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_encode_prod128.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip",
            "tq_general.hip", "tq_cache128.hip", "tq_split128.hip", "tq_peaks.hip", "tq_noalloc.hip", "tq_prefill128.hip",
-           "tq_fwht128.hip", "tq_kvgen.hip"]
+           "tq_fwht128.hip", "tq_kvgen.hip", "tq_encode64.hip"]
 
 # Packed FP32 VALU instructions are disabled for all device code.  MFMA results go to ordinary
 # VGPRs rather than accumulation registers: the kernels post-process their accumulators with

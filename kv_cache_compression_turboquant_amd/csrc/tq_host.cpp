@@ -828,6 +828,10 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   }
   if (n == 0) return ok();
   const bool prod = mode == TQ_MODE_PROD;
+  if (d == 64 && !prod)
+    return check_launch(tq::launch_encode_mse_d64(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx, out->norms,
+                                                  as_stream(stream)),
+                        fn);
   if (d == 64)
     return check_launch(tq::launch_encode_d64(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args, out->idx,
                                               out->norms, prod ? out->qjl : nullptr, prod ? out->rnorms : nullptr,

@@ -139,6 +139,9 @@ hipError_t launch_decode_attn_gen(const float* q, int B, int Hq, int Hkv, int64_
 hipError_t launch_encode_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                              const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits, float* rnorms,
                              hipStream_t st);
+// TurboQuant_mse encode at d = 64 (rows layout) on the 32 x 32 x 16 matrix cores, R from rot->r32_dev.
+hipError_t launch_encode_mse_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                 const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);
 
 // TurboQuant_mse encode at d = 128 (rows layout) for the randomized Hadamard rotations, as a
 // fast Walsh-Hadamard transform in registers: full = true for H diag(sigma) / sqrt(128), false for

@@ -1,8 +1,10 @@
 """GPU parity of the KV side at head dims 64 and 256 (d = 128 has its own kernels and tests),
 through the C ABI:
 
-* the d = 64 encode (MSE b = 1..4, prod b = 2..4; bf16 and fp32) against the oracle by the band
-  rule (indices and signs), words bit for bit on the rows without a flip, norms and gamma;
+* the d = 64 encode (MSE b = 1..4, prod b = 2..4; bf16 and fp32; the MSE encode also under the
+  Hadamard rotations and at vector counts ragged against its 32-vector tiles, rows past n left
+  untouched) against the oracle by the band rule (indices and signs), words bit for bit on the
+  rows without a flip, norms and gamma;
 * scores of MSE and prod keys at d = 64 and d = 256 against the oracle's formulas on the GPU's own
   packed keys, within 1e-3 ||q|| ||k||, GQA ratios 1, 4, 8 and 12 (12: the query heads span two
   groups of the kernel's head staging), ragged T against the 256-key tiles, and a cache whose rows
@@ -78,6 +80,47 @@ def test_encode_mse_d64(dev, b, dtype):
     np.testing.assert_array_equal(words[~bad], enc.words[~bad])
     np.testing.assert_allclose(p.norms.cpu().numpy(), enc.norms, rtol=1e-6, atol=0)
     assert np.all(gidx[2] == 1 << (b - 1))
+
+
+@pytest.mark.parametrize("kind", ["wht", "block_wht"])
+@pytest.mark.parametrize("b", [2, 3])
+def test_encode_mse_d64_hadamard(dev, kind, b):
+    # the d = 64 MSE encode takes R as a matrix (two bf16 passes), whatever its kind
+    seed = 30 + b
+    rot = tq.make_rotation(64, seed, kind)
+    rmat = oracle.wht_rotation(64, seed) if kind == "wht" else oracle.block_wht_rotation(64, seed, 32)
+    x, xt = _keys(700, 64, seed=40 + b, dtype="bf16")
+    cb = tq.codebook(64, b)
+    p = tq.encode(xt.to(dev), b, "mse", cb, rot)
+    torch.cuda.synchronize()
+    cb_o = oracle.codebook(64, b)
+    enc = oracle.encode_mse(x, rmat, cb_o)
+    words = to_np_words(p.idx)
+    bad, _ = check_indices(oracle.unpack_bits(words, 64, b), enc.y, cb_o, f"d64 {kind} b={b}")
+    np.testing.assert_array_equal(words[~bad], enc.words[~bad])
+    np.testing.assert_allclose(p.norms.cpu().numpy(), enc.norms, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("n", [1, 31, 33, 64, 4097])
+def test_encode_mse_d64_ragged(dev, n):
+    # vector counts against the 32-vector tiles; rows past n keep their contents
+    b = 3
+    rot, _, rmat, _ = _handles(64)
+    x, xt = _keys(n, 64, seed=n, dtype="bf16")
+    cb = tq.codebook(64, b)
+    full = tq.alloc_packed(n + 40, 64, b, "mse", device=dev)
+    full.idx.fill_(-1)
+    full.norms.fill_(5.0)
+    p = tq.Packed(64, b, "mse", n, full.idx[:n], full.norms[:n])
+    tq.encode(xt.to(dev), b, "mse", cb, rot, out=p)
+    torch.cuda.synchronize()
+    assert torch.all(full.idx[n:] == -1) and torch.all(full.norms[n:] == 5.0)
+    cb_o = oracle.codebook(64, b)
+    enc = oracle.encode_mse(x, rmat, cb_o)
+    words = to_np_words(p.idx)
+    bad, _ = check_indices(oracle.unpack_bits(words, 64, b), enc.y, cb_o, f"d64 n={n}")
+    np.testing.assert_array_equal(words[~bad], enc.words[~bad])
+    np.testing.assert_allclose(p.norms.cpu().numpy(), enc.norms, rtol=1e-6, atol=0)
 
 
 @pytest.mark.parametrize("b", [2, 3, 4])
