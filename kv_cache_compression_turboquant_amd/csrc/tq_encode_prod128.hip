@@ -55,6 +55,17 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t lanes) {
   return r;
 }
 
+// w = (w << 1) | (sign bit of z): one v_alignbit.
+__device__ __forceinline__ uint32_t sign_in(uint32_t w, float z) {
+  return (w << 1) | (__float_as_uint(z) >> 31);
+}
+
+// Sum of v over lanes l and l ^ 32 (a register swap of the wave's halves, no LDS).
+__device__ __forceinline__ float add_halves(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Raw buffer resource over `bytes` bytes at p (loads past the end read zeros, stores past the end
 // are dropped, by the range check).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(const void* p, uint32_t bytes) {
@@ -169,12 +180,16 @@ __device__ __forceinline__ void quant_pair(const f32x16& y, const QState<BITS>& 
   rl[s][(R & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, bf16x2));
 }
 
-// Sign bits (z >= 0) of registers R and R - 1 of S' output block OB (sign index 16 OB + r of the
-// lane's 64), pushed in descending order into the lane's two sign words.
+// Sign bits of registers R and R - 1 of S' output block OB (sign index 16 OB + r of the lane's 64),
+// pushed in descending order into the lane's two sign words: w = (w << 1) | (z >> 31), one
+// v_alignbit each.  The words collect [z < 0] and are inverted once at the end, so a bit is
+// [z >= 0] for every z but -0 (which the product does not produce: its accumulator starts at +0).
 template <int OB, int R>
 __device__ __forceinline__ void push_sign_pair(const f32x16& z, uint32_t (&qw)[2]) {
-  qw[OB >> 1] = shift_in(qw[OB >> 1], __builtin_amdgcn_ballot_w64(z[R] >= 0.f));
-  qw[OB >> 1] = shift_in(qw[OB >> 1], __builtin_amdgcn_ballot_w64(z[R - 1] >= 0.f));
+  qw[OB >> 1] = sign_in(qw[OB >> 1], z[R]);
+  qw[OB >> 1] = sign_in(qw[OB >> 1], z[R - 1]);
+  // pin the pushes here: shifts are free to sink to the stores, which would keep all 64 z live
+  asm volatile("" : "+v"(qw[OB >> 1]));
 }
 
 template <int B, int E, typename F>
@@ -311,7 +326,7 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
           }
         }
         if constexpr (s == 7) {
-          ss += __shfl_xor(ss, 32);
+          ss = add_halves(ss);
           nrm = sqrtf(ss);
           const bool live = nrm > 0.f;
           const float tsc = nrm * inv_post;
@@ -367,6 +382,8 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
       __builtin_amdgcn_sched_barrier(0);
     });
     static_for<0, 8>([&](auto ic) { push_sign_pair<0, 15 - 2 * decltype(ic)::value>(zprev, qw); });
+    qw[0] = ~qw[0];
+    qw[1] = ~qw[1];
     if constexpr (TQ_PROD_PRIO) __builtin_amdgcn_s_setprio(0);
 
     // ---- stores, through buffer resources bounded by the tile's rows that exist: a row past the
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(kProdWaves * 64, 1) void k_encode_prod_d128(
     // exact count of the memory operations in flight (a store under a branch makes it wait for
     // all of them, the next tile's loads included, before the next tile starts).  Both halves of a
     // vector hold the same norm and residual norm and both store them.
-    rs += __shfl_xor(rs, 32);
+    rs = add_halves(rs);
     const int64_t row0 = tw * 32;
     const int64_t left = n - row0;
     const uint32_t live_rows = left >= 32 ? 32u : (left > 0 ? (uint32_t)left : 0u);

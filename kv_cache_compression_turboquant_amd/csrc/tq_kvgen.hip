@@ -401,31 +401,68 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
 }
 
 // out[b, h] = R_V^T (sum_s e^{m_s - M} acc_s) / (sum_s e^{m_s - M} l_s); one block of D threads per
-// query head.
+// query head.  The splits are taken D at a time: thread t forms split s0 + t's weight once, and
+// the accumulation over the chunk then reads the weights from LDS while its loads of acc_s (one
+// per split, independent) stay in flight together.
+template <int D>
+__device__ __forceinline__ float block_reduce_gen(float v, float* red, bool is_max) {
+  constexpr int NW = D / 64;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  if constexpr (NW > 1) {
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v = is_max ? fmaxf(v, red[w]) : v + red[w];
+  }
+  return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void k_attn_gen_combine(const float* __restrict__ parts, int Hq, int Hkv, int nsplit,
                                                         const float* __restrict__ r32v, float* __restrict__ out) {
   constexpr int P = attn_gen_part<D>();
   __shared__ float a[D];
+  __shared__ float wsh[D];
+  __shared__ float red[D / 64];
   const int64_t h = blockIdx.x;
   const int b = (int)(h / Hq), hq = (int)(h % Hq);
   const int ratio = Hq / Hkv;
   const int g = hq / ratio, k = hq % ratio;
-  const float* src = parts + ((int64_t)(b * Hkv + g) * nsplit) * kGenHeadGroup * P + k * P;
+  const int64_t sstride = (int64_t)kGenHeadGroup * P;
+  const float* src = parts + ((int64_t)(b * Hkv + g) * nsplit) * sstride + k * P;
   const int i = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, src[(int64_t)s * kGenHeadGroup * P]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ps = src + (int64_t)s * kGenHeadGroup * P;
-    const float w = ps[0] == -INFINITY ? 0.f : __expf(ps[0] - M);
-    L = fmaf(w, ps[1], L);
-    A = fmaf(w, ps[2 + i], A);
+  float m = -INFINITY;
+  for (int s = i; s < nsplit; s += D) m = fmaxf(m, src[s * sstride]);
+  const float M = block_reduce_gen<D>(m, red, true);
+  float lsum = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += D) {
+    const int s = s0 + i;
+    float w = 0.f;
+    if (s < nsplit) {
+      const float ms = src[s * sstride];
+      w = ms == -INFINITY ? 0.f : __expf(ms - M);
+      lsum = fmaf(w, src[s * sstride + 1], lsum);
+    }
+    wsh[i] = w;
+    __syncthreads();
+    const int cnt = nsplit - s0 < D ? nsplit - s0 : D;
+    const float* ps = src + (int64_t)s0 * sstride + 2 + i;
+#pragma unroll 8
+    for (int t = 0; t < cnt; ++t) A = fmaf(wsh[t], ps[t * sstride], A);
+    __syncthreads();
   }
+  const float L = block_reduce_gen<D>(lsum, red, false);
   a[i] = L > 0.f ? A / L : 0.f;
   __syncthreads();
   // R_V^T a: (R^T a)_i = sum_j R[j][i] a_j, R row-major: thread i reads consecutive columns
   float o = 0.f;
+#pragma unroll 8
   for (int j = 0; j < D; ++j) o = fmaf(r32v[(size_t)j * D + i], a[j], o);
   out[h * D + i] = o;
 }
