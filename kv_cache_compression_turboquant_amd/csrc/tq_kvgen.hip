@@ -4,8 +4,8 @@
 //
 // Scores ([TQ] TurboQuant_mse / TurboQuant_prod inner products; [FP] inner-product bias and the
 // QJL fix): <q, k~> = s <R q, C[idx]> (+ gamma sqrt(pi/2)/d <S q, z> for prod keys), with R q and
-// S q formed once per query head in fp32.  A thread takes one key: its packed words stay in
-// registers while the block's query heads (staged in LDS, eight at a time) are multiplied.
+// S q formed once per query head in fp32, on the matrix cores: tiles of 16 keys (centroids decoded
+// to fp16 through LDS tables) against up to 16 query heads (fp16 hi + lo).
 //
 // Decode attention ("TurboQuant 和 RotorQuant 的真相", the attention formula; "TurboQuant 详解",
 // decode with dequantization inside the kernel): softmax(scale q K^T) V over packed K and V in the
@@ -17,6 +17,7 @@
 // Encode at d = 64 ([TQ] official steps 1-5 and TurboQuant_prod): one wave per vector, lane i
 // owning coordinate i; y = R x, the residual's R^T and the sketch S are matrix-vector products
 // with the matrices in LDS (64 x 64 fp32 each).
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -66,123 +67,10 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N]) {
   return v & ((1u << BITS) - 1u);
 }
 
-// One key: its packed row (indices; signs for prod), its norm and its residual norm.
-template <int D, int BITS, bool PROD>
-struct GenKey {
-  static constexpr int W = D * BITS / 32;  // index words per key (BITS per 32-coordinate chunk)
-  static constexpr int WZ = D / 32;        // sign words per key (one per chunk)
-  const uint32_t* w;                       // the key's index words
-  const uint32_t* z;                       // the key's sign words (prod)
-  float s, g;
-};
-
-template <int D, int BITS, bool PROD>
-__device__ __forceinline__ void load_gen_key(const uint32_t* __restrict__ idx, const float* __restrict__ norms,
-                                             const uint32_t* __restrict__ qjl, const float* __restrict__ rnorms,
-                                             int64_t row, bool valid, GenKey<D, BITS, PROD>& k) {
-  using K = GenKey<D, BITS, PROD>;
-  // an invalid key reads row 0's words (in bounds) and gets norm 0, so it scores 0
-  const int64_t r = valid ? row : 0;
-  k.w = idx + r * K::W;
-  k.z = PROD ? qjl + r * K::WZ : nullptr;
-  k.s = valid ? norms[r] : 0.f;
-  k.g = (PROD && valid) ? rnorms[r] : 0.f;
-}
-
-// Raw scores of one key against NH heads whose R q (qr) and S q (qz) rows sit in LDS:
-// out[k] = s <qr_k, C[idx]> + gamma sqrt(pi/2)/D <qz_k, z>.  C: centroids in LDS.  The key's words
-// are read chunk by chunk (32 coordinates: BITS index words and one sign word).
-template <int D, int BITS, bool PROD, int NH>
-__device__ __forceinline__ void gen_key_scores(const GenKey<D, BITS, PROD>& key, const float* qr, const float* qz,
-                                               const float* cent, int nh, float (&out)[NH]) {
-  float acc[NH], accz[NH];
-#pragma unroll
-  for (int k = 0; k < NH; ++k) {
-    acc[k] = 0.f;
-    accz[k] = 0.f;
-  }
-#pragma unroll 1
-  for (int c = 0; c < D / 32; ++c) {
-    uint32_t wc[BITS];
-#pragma unroll
-    for (int b = 0; b < BITS; ++b) wc[b] = key.w[c * BITS + b];
-    const uint32_t zw = PROD ? key.z[c] : 0u;
-    float cv[32];
-    gen_for<0, 32>([&](auto ee) {
-      constexpr int e = decltype(ee)::value;
-      cv[e] = cent[field<BITS, e>(wc)];
-    });
-#pragma unroll
-    for (int k = 0; k < NH; ++k) {
-      if (k < nh) {
-        const f32x4* qr4 = reinterpret_cast<const f32x4*>(qr + k * 2 * D + 32 * c);
-#pragma unroll
-        for (int e4 = 0; e4 < 8; ++e4) {
-          const f32x4 qv = qr4[e4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[k] = fmaf(qv[e], cv[4 * e4 + e], acc[k]);
-        }
-        if constexpr (PROD) {
-          const f32x4* qz4 = reinterpret_cast<const f32x4*>(qz + k * 2 * D + 32 * c);
-#pragma unroll
-          for (int e4 = 0; e4 < 8; ++e4) {
-            const f32x4 qv = qz4[e4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int bit = 4 * e4 + e;
-              // z = +1 where the bit is set, -1 otherwise
-              accz[k] += __uint_as_float(__float_as_uint(qv[e]) ^ (((~zw >> bit) & 1u) << 31));
-            }
-          }
-        }
-      }
-    }
-  }
-  constexpr float kRootHalfPi = 1.2533141373155002512f;
-#pragma unroll
-  for (int k = 0; k < NH; ++k) out[k] = key.s * acc[k] + (PROD ? key.g * (kRootHalfPi / (float)D) * accz[k] : 0.f);
-}
-
 // Stages the R q / S q rows of heads h0 .. h0 + nh - 1 of `ws` into LDS (2 D floats per head).
 template <int D>
 __device__ __forceinline__ void stage_heads(const float* __restrict__ ws, int64_t h0, int nh, float* dst) {
   for (int i = threadIdx.x; i < nh * 2 * D; i += blockDim.x) dst[i] = ws[h0 * 2 * D + i];
-}
-
-// ---------------------------------------------------------------------------------------
-// Scores: grid (key tiles of 256, B * Hkv); keys of sequence (b, g) at rows (b Hkv + g) rows + t.
-// ---------------------------------------------------------------------------------------
-template <int D, int BITS, bool PROD>
-__global__ __launch_bounds__(kGenThreads) void k_scores_gen(const float* __restrict__ ws, int Hq, int Hkv, int64_t T,
-                                                           int64_t rows, const uint32_t* __restrict__ idx,
-                                                           const float* __restrict__ norms,
-                                                           const uint32_t* __restrict__ qjl,
-                                                           const float* __restrict__ rnorms, CodebookArgs cb,
-                                                           float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) float qh[kGenHeadGroup * 2 * D];
-  __shared__ float cent[16];
-  if (threadIdx.x < 16) cent[threadIdx.x] = cb.c[threadIdx.x];
-  const int bg = blockIdx.y;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int ratio = Hq / Hkv;
-  const int64_t t = (int64_t)blockIdx.x * kGenThreads + threadIdx.x;
-  const bool valid = t < T;
-  GenKey<D, BITS, PROD> key;
-  load_gen_key<D, BITS, PROD>(idx, norms, qjl, rnorms, (int64_t)bg * rows + t, valid, key);
-  for (int k0 = 0; k0 < ratio; k0 += kGenHeadGroup) {
-    const int nh = ratio - k0 < kGenHeadGroup ? ratio - k0 : kGenHeadGroup;
-    const int64_t h0 = (int64_t)b * Hq + (int64_t)g * ratio + k0;
-    __syncthreads();
-    stage_heads<D>(ws, h0, nh, qh);
-    __syncthreads();
-    float out[kGenHeadGroup];
-    gen_key_scores<D, BITS, PROD, kGenHeadGroup>(key, qh, qh + D, cent, nh, out);
-    if (valid) {
-#pragma unroll
-      for (int k = 0; k < kGenHeadGroup; ++k)
-        if (k < nh) scores[(h0 + k) * T + t] = out[k];
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -559,12 +447,300 @@ __global__ __launch_bounds__(kGenThreads) void k_encode_d64(const void* __restri
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Scores on the matrix cores (v_mfma_f32_16x16x32_f16).  A wave takes tiles of 16 keys of one
+// sequence against up to 16 of its query heads:
+//   A = the keys' centroids: lane (n, g) holds key n of the tile at coordinates
+//       (D/4) g + 8 s + e in instruction s (each lane a contiguous quarter of the key's row),
+//       decoded from the packed words through LDS tables that map a byte (6 bits at 3 bits per
+//       index) to the fp16 centroids of the indices it holds;
+//   B = R q of the heads in fp16 hi + lo (two instructions per slice), and for prod keys S q
+//       likewise against the +-1 sign operand (a byte of signs -> eight fp16 +-1, from a table);
+//   D row 4 g + r, column n: key 4 g + r of the tile, head n.
+// A block's four waves take gm_tiles<D>() consecutive tiles each, whose loads are all issued
+// first; grid (key ranges, sequences, groups of 16 query heads).  (Longer-lived blocks that
+// stream several such groups with the next one's loads in flight measured slower.)
+// ---------------------------------------------------------------------------------------
+// tiles of 16 keys per wave (registers); a block of four waves takes 64 gm_tiles<D>() keys
+template <int D>
+constexpr int gm_tiles() { return D == 64 ? 8 : 4; }
+
+template <int BITS>
+struct GmTab;
+template <>
+struct GmTab<1> {
+  using E = u32x4;
+  static constexpr int N = 256;
+};
+template <>
+struct GmTab<2> {
+  using E = u32x2;
+  static constexpr int N = 256;
+};
+template <>
+struct GmTab<3> {
+  using E = uint32_t;
+  static constexpr int N = 64;
+};
+template <>
+struct GmTab<4> {
+  using E = uint32_t;
+  static constexpr int N = 256;
+};
+
+__device__ __forceinline__ uint32_t f16pair(float lo, float hi) { return f16_bits(lo) | (f16_bits(hi) << 16); }
+
+// Table entry v: the fp16 centroids of the indices packed in v, first index in the low half.
+template <int BITS>
+__device__ __forceinline__ typename GmTab<BITS>::E gm_entry(uint32_t v, const float* c) {
+  constexpr uint32_t M = (1u << BITS) - 1u;
+  if constexpr (BITS == 4 || BITS == 3) {
+    return f16pair(c[v & M], c[(v >> BITS) & M]);
+  } else if constexpr (BITS == 2) {
+    return u32x2{f16pair(c[v & 3u], c[(v >> 2) & 3u]), f16pair(c[(v >> 4) & 3u], c[(v >> 6) & 3u])};
+  } else {
+    u32x4 e;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = f16pair(c[(v >> (2 * k)) & 1u], c[(v >> (2 * k + 1)) & 1u]);
+    return e;
+  }
+}
+
+// A lane's quarter of a key row: BPL bits, loaded as NW words from the word holding its first
+// bit and shifted down when that bit is not word-aligned (d = 64 at odd bit widths).
+template <int D, int BITS>
+struct GmSlice {
+  static constexpr int BPL = D / 4 * BITS;
+  static constexpr bool ALIGNED = BPL % 32 == 0;
+  static constexpr int NW = ALIGNED ? BPL / 32 : (BPL + 16 + 31) / 32;
+  static constexpr int NV = (BPL + 31) / 32;
+};
+
+// The A operand of instruction S from the lane's aligned slice words.
+template <int BITS, int S, int NV>
+__device__ __forceinline__ u32x4 gm_decode(const uint32_t (&sl)[NV], const typename GmTab<BITS>::E* tab) {
+  u32x4 a;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = tab[(sl[S] >> (8 * k)) & 0xffu];
+  } else if constexpr (BITS == 2) {
+    constexpr int w = S >> 1, b0 = 2 * (S & 1);
+    const u32x2 lo = tab[(sl[w] >> (8 * b0)) & 0xffu];
+    const u32x2 hi = tab[(sl[w] >> (8 * b0 + 8)) & 0xffu];
+    a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  } else if constexpr (BITS == 1) {
+    a = tab[(sl[S >> 2] >> (8 * (S & 3))) & 0xffu];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = 24 * S + 6 * k;   // a constant once unrolled
+      const int wi = p >> 5, sh = p & 31;
+      uint32_t v = sl[wi] >> sh;
+      if (sh > 26) v |= sl[wi + 1] << (32 - sh);
+      a[k] = tab[v & 63u];
+    }
+  }
+  return a;
+}
+
+// Eight signs (a byte of the slice's sign bits) as fp16 +-1 from the sign table.
+template <int D, int S>
+__device__ __forceinline__ u32x4 gm_signs(uint32_t z0, uint32_t z1, const u32x4* tabz) {
+  if constexpr (D == 256) {
+    return tabz[(((S < 4) ? z0 : z1) >> (8 * (S & 3))) & 0xffu];
+  } else {
+    return tabz[(z0 >> (8 * S)) & 0xffu];
+  }
+}
+
+// One tile's loads (16 keys from row t0 of the sequence; rows past T read zeros): the lane's slice words and sign words of key n, and the norms of
+// the keys 4 g .. 4 g + 3 that the lane's results belong to.
+template <int D, int BITS, bool PROD>
+struct GmTile {
+  uint32_t w[GmSlice<D, BITS>::NW];
+  uint32_t z0, z1;
+  float sn[4], gm[4];
+};
+
+template <int D, int BITS, bool PROD>
+__device__ __forceinline__ void gm_load(GmTile<D, BITS, PROD>& tl, const uint32_t* idx, const float* norms,
+                                        const uint32_t* qjl, const float* rnorms, int64_t rowb, int64_t t0,
+                                        int64_t tlim, int n, int g, uint32_t wstart) {
+  constexpr int W = D * BITS / 32, WZ = D / 32;
+  const int64_t left = tlim - t0;
+  const uint32_t nv = left >= 16 ? 16u : (left > 0 ? (uint32_t)left : 0u);
+  const int64_t r0 = rowb + (left > 0 ? t0 : 0);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(idx + r0 * W), (short)0, (int)(nv * W * 4u), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < GmSlice<D, BITS>::NW; ++i)
+    tl.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, ((uint32_t)n * W + wstart + i) * 4u, 0, 0);
+  tl.z0 = tl.z1 = 0u;
+  if constexpr (PROD) {
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qjl + r0 * WZ), (short)0,
+                                                                       (int)(nv * WZ * 4u), 0x00020000);
+    if constexpr (D == 256) {
+      tl.z0 = __builtin_amdgcn_raw_buffer_load_b32(rz, ((uint32_t)n * WZ + 2u * g) * 4u, 0, 0);
+      tl.z1 = __builtin_amdgcn_raw_buffer_load_b32(rz, ((uint32_t)n * WZ + 2u * g + 1u) * 4u, 0, 0);
+    } else {
+      tl.z0 = __builtin_amdgcn_raw_buffer_load_b32(rz, ((uint32_t)n * WZ + (g >> 1)) * 4u, 0, 0);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rn =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(norms + r0), (short)0, (int)(nv * 4u), 0x00020000);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    tl.sn[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)(4 * g + r) * 4u, 0, 0));
+  if constexpr (PROD) {
+    const __amdgpu_buffer_rsrc_t rg =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rnorms + r0), (short)0, (int)(nv * 4u), 0x00020000);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      tl.gm[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(4 * g + r) * 4u, 0, 0));
+  }
+}
+
+// Workgroup barrier that waits only for the wave's LDS operations: a __syncthreads() would also
+// wait for every global load in flight (the tile loads issued before the tables are built).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D, int BITS, bool PROD>
+__global__ __launch_bounds__(256) void k_scores_gm(const float* __restrict__ ws, int Hq, int Hkv, int64_t T,
+                                                   int64_t rows, const uint32_t* __restrict__ idx,
+                                                   const float* __restrict__ norms, const uint32_t* __restrict__ qjl,
+                                                   const float* __restrict__ rnorms, CodebookArgs cb,
+                                                   float* __restrict__ scores) {
+  using Tab = GmTab<BITS>;
+  using SL = GmSlice<D, BITS>;
+  using Tile = GmTile<D, BITS, PROD>;
+  constexpr int NS = D / 32;                 // instructions per key slice
+  constexpr int NT = gm_tiles<D>();          // tiles per wave
+  __shared__ typename Tab::E tab[Tab::N];
+  __shared__ u32x4 tabz[PROD ? 256 : 1];
+  __shared__ float cent[16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile bases in SGPRs
+  const int n = lane & 15, g = lane >> 4;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int ratio = Hq / Hkv;
+  const int k0 = blockIdx.z * 16;
+  const int nh = ratio - k0 < 16 ? ratio - k0 : 16;
+  const int64_t h0 = (int64_t)b * Hq + (int64_t)kvh * ratio + k0;
+  const int64_t rowb = (int64_t)bg * rows;
+  const int start_bit = SL::BPL * g;
+  const uint32_t wstart = (uint32_t)(start_bit >> 5), wsh = (uint32_t)(start_bit & 31);
+  constexpr float kQ = 1.2533141373155002512f / (float)D;
+  const int64_t kg = (int64_t)blockIdx.x * NT * 64 + (int64_t)wave * NT * 16;   // the wave's first key
+
+  // Head n's R q (and S q) at the lane's coordinates, loaded ahead of the tiles so that waiting
+  // for them leaves the tile loads in flight (loads complete in order).
+  const bool live = n < nh;
+  f32x4 qv[PROD ? 2 : 1][NS][2];
+  {
+    const float* qr = ws + (h0 + (live ? n : 0)) * 2 * D + (D / 4) * g;
+#pragma unroll
+    for (int part = 0; part < (PROD ? 2 : 1); ++part)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qv[part][s][0] = *reinterpret_cast<const f32x4*>(qr + part * D + 8 * s);
+        qv[part][s][1] = *reinterpret_cast<const f32x4*>(qr + part * D + 8 * s + 4);
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the tile loads
+
+  Tile ta[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) gm_load<D, BITS, PROD>(ta[tt], idx, norms, qjl, rnorms, rowb, kg + 16 * tt, T, n, g, wstart);
+
+  if (threadIdx.x == 0) {
+    // written by one lane from the (uniform) argument: an indexed read of the argument would be
+    // a global load, and waiting for it would wait for the tile loads too
+#pragma unroll
+    for (int k = 0; k < 16; ++k) cent[k] = cb.c[k];
+  }
+  lds_barrier();
+  if (threadIdx.x < Tab::N) tab[threadIdx.x] = gm_entry<BITS>(threadIdx.x, cent);
+  if constexpr (PROD) {
+    u32x4 e;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      e[k] = (((threadIdx.x >> (2 * k)) & 1u) ? 0x3C00u : 0xBC00u) |
+             ((((threadIdx.x >> (2 * k + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+    tabz[threadIdx.x] = e;
+  }
+
+  // B operands: fp16 hi + lo of the loaded R q (and S q), zero past nh
+  u32x4 qh[NS], ql[NS], zh[PROD ? NS : 1], zl[PROD ? NS : 1];
+#pragma unroll
+  for (int part = 0; part < (PROD ? 2 : 1); ++part)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 v0 = qv[part][s][0], v1 = qv[part][s][1];
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      u32x4 hi, lo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a0 = live ? v[2 * k] : 0.f, a1 = live ? v[2 * k + 1] : 0.f;
+        const _Float16 h0f = (_Float16)a0, h1f = (_Float16)a1;
+        hi[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0f) | ((uint32_t)__builtin_bit_cast(uint16_t, h1f) << 16);
+        lo[k] = f16pair(a0 - (float)h0f, a1 - (float)h1f);
+      }
+      if (part == 0) {
+        qh[s] = hi;
+        ql[s] = lo;
+      } else if constexpr (PROD) {
+        zh[s] = hi;
+        zl[s] = lo;
+      }
+    }
+  lds_barrier();   // tables ready (the tile loads stay in flight)
+
+  float* const out0 = scores + (h0 + n) * T;
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int64_t t0 = kg + 16 * tt;
+    if (t0 >= T) break;
+    const int64_t left = T - t0;
+    const uint32_t nv = left >= 16 ? 16u : (uint32_t)left;
+    uint32_t sl[SL::NV];
+#pragma unroll
+    for (int i = 0; i < SL::NV; ++i)
+      sl[i] = SL::ALIGNED ? ta[tt].w[i] : __builtin_amdgcn_alignbit(i + 1 < SL::NW ? ta[tt].w[i + 1] : 0u, ta[tt].w[i], wsh);
+    const uint32_t za = (PROD && D == 64) ? ta[tt].z0 >> (16 * (g & 1)) : ta[tt].z0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accz = {0.f, 0.f, 0.f, 0.f};
+    gen_for<0, NS>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      const u32x4 a = gm_decode<BITS, S, SL::NV>(sl, tab);
+      acc = mfma_f16(a, qh[S], acc);
+      acc = mfma_f16(a, ql[S], acc);
+      if constexpr (PROD) {
+        const u32x4 zs = gm_signs<D, S>(za, ta[tt].z1, tabz);
+        accz = mfma_f16(zs, zh[S], accz);
+        accz = mfma_f16(zs, zl[S], accz);
+      }
+    });
+    // plain stores under the lane's own condition (a buffer resource would have to be uniform,
+    // and each head's row has its own base)
+    if (live) {
+      float* dst = out0 + t0 + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = ta[tt].sn[r] * acc[r] + (PROD ? ta[tt].gm[r] * kQ * accz[r] : 0.f);
+        if ((uint32_t)(4 * g + r) < nv) dst[r] = v;
+      }
+    }
+  }
+}
+
 template <int D, int BITS, bool PROD>
 hipError_t scores_gen_launch(const float* ws, int B, int Hq, int Hkv, int64_t T, int64_t rows, const tq_packed* K,
                              const CodebookArgs& cb, float* scores, hipStream_t st) {
-  const dim3 grid((unsigned)((T + kGenThreads - 1) / kGenThreads), (unsigned)(B * Hkv));
-  hipLaunchKernelGGL((k_scores_gen<D, BITS, PROD>), grid, dim3(kGenThreads), 0, st, ws, Hq, Hkv, T, rows, K->idx,
-                     K->norms, K->qjl, K->rnorms, cb, scores);
+  const int ratio = Hq / Hkv;
+  constexpr int keys = 64 * gm_tiles<D>();
+  const dim3 grid((unsigned)((T + keys - 1) / keys), (unsigned)(B * Hkv), (unsigned)((ratio + 15) / 16));
+  hipLaunchKernelGGL((k_scores_gm<D, BITS, PROD>), grid, dim3(256), 0, st, ws, Hq, Hkv, T, rows, K->idx, K->norms,
+                     K->qjl, K->rnorms, cb, scores);
   return hipGetLastError();
 }
 

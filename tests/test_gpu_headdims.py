@@ -5,10 +5,10 @@ through the C ABI:
   Hadamard rotations and at vector counts ragged against its 32-vector tiles, rows past n left
   untouched) against the oracle by the band rule (indices and signs), words bit for bit on the
   rows without a flip, norms and gamma;
-* scores of MSE and prod keys at d = 64 and d = 256 against the oracle's formulas on the GPU's own
-  packed keys, within 1e-3 ||q|| ||k||, GQA ratios 1, 4, 8 and 12 (12: the query heads span two
-  groups of the kernel's head staging), ragged T against the 256-key tiles, and a cache whose rows
-  per sequence exceed T;
+* scores of MSE (index bits 1..4) and prod (b = 2..4) keys at d = 64 and d = 256 against the
+  oracle's formulas on the GPU's own packed keys, within 1e-3 ||q|| ||k||, GQA ratios 1, 3, 4, 8,
+  12 and 20 (20: two groups of the kernel's 16 query heads), T ragged against the 16-key tiles
+  and 256-key blocks, and a cache whose rows per sequence exceed T;
 * decode attention at d = 64 and d = 256 (rows-layout V) against the oracle within
   1e-3 max_t ||v_hat_t||, ratios 1, 3 and 8, K/V bit pairs, T from 1 to 9000 (several 4096-key
   ranges merged);
@@ -157,8 +157,9 @@ def _oracle_scores(p, q, d, b, mode):
 
 
 @pytest.mark.parametrize("d", [64, 256])
-@pytest.mark.parametrize("mode,b", [("mse", 2), ("mse", 4), ("prod", 3), ("prod", 4)])
-@pytest.mark.parametrize("B,hkv,hq,T", [(2, 2, 8, 300), (1, 1, 12, 513), (1, 3, 3, 70)])
+@pytest.mark.parametrize("mode,b", [("mse", 1), ("mse", 2), ("mse", 3), ("mse", 4), ("prod", 2), ("prod", 3),
+                                    ("prod", 4)])
+@pytest.mark.parametrize("B,hkv,hq,T", [(2, 2, 8, 300), (1, 1, 12, 513), (1, 3, 3, 70), (1, 1, 20, 33)])
 def test_scores_head_dims(dev, d, mode, b, B, hkv, hq, T):
     rot, qjl, _, _ = _handles(d)
     x, xt = _keys(B * hkv * T, d, seed=d + b + T)
