@@ -39,23 +39,48 @@ constexpr int kGenHeadGroup = 8;   // query heads staged at once
 constexpr int kGenAttnTiles = 4;   // 256-key tiles per attention range
 
 // ---------------------------------------------------------------------------------------
-// Query prologue: ws[h] = {R q_h (d floats), S q_h (d floats)}; one block of d threads per head.
+// Query prologue: ws[h] = {R q_h (d floats), S q_h (d floats)}; one block of 256 threads per head.
+// Thread (i4, jg) forms outputs 4 i4 .. 4 i4 + 3 over the rows j of its group jg (a float4 of
+// R^T per row), and the groups are summed through LDS: short dependent load chains.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(D) void k_qprep_gen(const float* __restrict__ q, const float* __restrict__ rt32,
-                                                 const float* __restrict__ st32, float* __restrict__ ws) {
+__global__ __launch_bounds__(256) void k_qprep_gen(const float* __restrict__ q, const float* __restrict__ rt32,
+                                                  const float* __restrict__ st32, float* __restrict__ ws) {
+  constexpr int NI = D / 4;            // threads per row group
+  constexpr int JG = 256 / NI;         // row groups
+  constexpr int JN = D / JG;           // rows per group
   __shared__ float qs[D];
+  __shared__ f32x4 part[2][JG][NI];
   const int64_t h = blockIdx.x;
-  const int i = threadIdx.x;
-  qs[i] = q[h * D + i];
+  const int i4 = threadIdx.x % NI, jg = threadIdx.x / NI;
+  if (threadIdx.x < D) qs[threadIdx.x] = q[h * D + threadIdx.x];
   __syncthreads();
-  float a = 0.f, c = 0.f;
-  // rt32[j][i] = R[i][j] and st32[j][i] = S[i][j]: thread i reads consecutive columns
-  for (int j = 0; j < D; ++j) a = fmaf(rt32[(size_t)j * D + i], qs[j], a);
-  if (st32)
-    for (int j = 0; j < D; ++j) c = fmaf(st32[(size_t)j * D + i], qs[j], c);
-  ws[h * 2 * D + i] = a;
-  ws[h * 2 * D + D + i] = c;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+  // rt32[j][i] = R[i][j] and st32[j][i] = S[i][j]
+#pragma unroll 8
+  for (int jj = 0; jj < JN; ++jj) {
+    const int j = jg * JN + jj;
+    const f32x4 r = *reinterpret_cast<const f32x4*>(rt32 + (size_t)j * D + 4 * i4);
+    a += r * qs[j];
+  }
+  if (st32) {
+#pragma unroll 8
+    for (int jj = 0; jj < JN; ++jj) {
+      const int j = jg * JN + jj;
+      const f32x4 r = *reinterpret_cast<const f32x4*>(st32 + (size_t)j * D + 4 * i4);
+      c += r * qs[j];
+    }
+  }
+  part[0][jg][i4] = a;
+  part[1][jg][i4] = c;
+  __syncthreads();
+  if (threadIdx.x < 2 * NI) {
+    const int which = threadIdx.x / NI, k = threadIdx.x % NI;
+    f32x4 t = part[which][0][k];
+#pragma unroll
+    for (int g2 = 1; g2 < JG; ++g2) t += part[which][g2][k];
+    *reinterpret_cast<f32x4*>(ws + h * 2 * D + which * D + 4 * k) = t;
+  }
 }
 
 // BITS-bit field of coordinate I (compile-time) of a packed row held in registers.
@@ -759,7 +784,7 @@ hipError_t scores_gen_bits(const float* ws, int B, int Hq, int Hkv, int64_t T, i
 template <int D>
 hipError_t qprep_gen_launch(const float* q, int64_t heads, const tq_rotation_s* rot, const tq_qjl_s* qjl, float* ws,
                             hipStream_t st) {
-  hipLaunchKernelGGL((k_qprep_gen<D>), dim3((unsigned)heads), dim3(D), 0, st, q, rot->rt32_dev,
+  hipLaunchKernelGGL((k_qprep_gen<D>), dim3((unsigned)heads), dim3(256), 0, st, q, rot->rt32_dev,
                      qjl ? qjl->st32_dev : nullptr, ws);
   return hipGetLastError();
 }
