@@ -45,9 +45,9 @@ HEADLINE_KERNELS = {
 # name prefixes of those kernels in a rocprofv3 database (for the counter summary)
 PMC_KERNELS = {
     "c3:prod_encode": "k_encode_prod_d128<3, true, 2>",
-    "c3:scores": "k_scores_d128<3, true, false>",
+    "c3:scores": "k_scores_d128<3, true, false, 0>",
     "c2:encode": "k_encode_mse_d128<3, true, 2,",
-    "c2:scores": "k_scores_d128<3, false, false>",
+    "c2:scores": "k_scores_d128<3, false, false, 0>",
 }
 
 
