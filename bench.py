@@ -318,6 +318,78 @@ def cpu_baseline_prod(cfg, kind, budget_s=10.0):
                       f"their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
 
 
+def cpu_baseline_headdim(d, kb, vb, ratio, budget_s=10.0):
+    """The oracle on a bounded sample of the head-dim workload: one (sequence, KV head) group of
+    4096 tokens, keys (MSE kb bits) and values (MSE vb bits) encoded, then the scores and the decode
+    attention of its query heads over them, repeated until the budget is spent.  Reports
+    attention KV positions/s (the GPU line's kv_positions_per_s) and the encode and score rates."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    threads, cpu = _cpu_info()
+    rot = oracle.dense_rotation(d, 1)
+    cbk, cbv = oracle.codebook(d, kb), oracle.codebook(d, vb)
+    T = 4096
+    kx = wl.bf16_bits_to_f32(wl.kv_tensor_bf16(1, 1, T, d, seed=1, outlier_seed=2, scale_seed=3)[0, 0]).astype(np.float64)
+    vx = wl.bf16_bits_to_f32(wl.kv_tensor_bf16(1, 1, T, d, seed=4, outlier_seed=5, scale_seed=None)[0, 0]).astype(np.float64)
+    q = wl.gaussian((1, ratio, d), 6).astype(np.float64)
+    t_enc = t_sc = t_at = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        ke, ve = oracle.encode_mse(kx, rot, cbk), oracle.encode_mse(vx, rot, cbv)
+        b = time.perf_counter()
+        oracle.scores_mse(q[0], ke.idx, ke.norms, rot, cbk)
+        c = time.perf_counter()
+        oracle.decode_attention(q, ke.idx[None, None], ke.norms[None, None], ve.idx[None, None], ve.norms[None, None],
+                                rot, rot, cbk, cbv, 1 / np.sqrt(d))
+        e = time.perf_counter()
+        t_enc += b - a
+        t_sc += c - b
+        t_at += e - c
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": reps * T / t_at, "unit": "KV positions/s (decode attention over packed K and V)",
+            "cores": threads, "kind": "oracle", "encode_vectors_per_s": 2 * reps * T / t_enc,
+            "scores_per_s": reps * T * ratio / t_sc,
+            "sample": f"{reps} rounds of one group of {T} tokens at d = {d}: keys ({kb} bits) and values ({vb} bits) "
+                      f"encoded, scored and attended by {ratio} query heads, {dt:.1f} s; numpy fp64; {cpu}"}
+
+
+def cpu_baseline_mse(cfg, kind, b, budget_s=10.0):
+    """The oracle on a bounded sample of the MSE-key workload: 4096-key chunks of one KV head slab
+    encoded (TurboQuant_mse, b bits, the given rotation as an explicit matrix) and scored by their
+    query heads; scores/s and encoded keys/s."""
+    import oracle
+    from kv_cache_compression_turboquant_amd import workloads as wl
+    threads, cpu = _cpu_info()
+    rot = {"dense": oracle.dense_rotation(cfg.d, 1), "wht": oracle.wht_rotation(cfg.d, 1),
+           "block_wht": oracle.block_wht_rotation(cfg.d, 1, 32)}[kind]
+    cb = oracle.codebook(cfg.d, b)
+    ratio = cfg.hq // cfg.hkv
+    x = wl.bf16_bits_to_f32(wl.kv_keys(cfg, T=4096, B=1)[0, 0]).astype(np.float64)
+    q = wl.kv_queries(cfg)[0, :ratio].astype(np.float64)
+    keys = scores = 0
+    t_enc = 0.0
+    t0 = time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        enc = oracle.encode_mse(x, rot, cb)
+        t_enc += time.perf_counter() - a
+        s = oracle.scores_mse(q, enc.idx, enc.norms, rot, cb)
+        keys += x.shape[0]
+        scores += s.size
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": scores / dt, "unit": "scores/s (MSE encode + score of the sampled keys)", "cores": threads,
+            "kind": "oracle", "encode_vectors_per_s": keys / t_enc,
+            "sample": f"{keys} keys (4096-key chunks of one KV head slab, {kind} rotation, b = {b}) encoded and "
+                      f"scored by their {ratio} query heads in {dt:.1f} s; numpy fp64; {cpu}"}
+
+
 def cpu_baseline_split(cfg, bo, br, budget_s=10.0):
     """The oracle on a bounded sample of the split-code workload: 4096-key chunks of one KV head
     split-encoded (outlier half b_o bits, rest b_r) and scored by their query heads; scores/s."""
@@ -420,6 +492,8 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
                     "scores_hbm_frac": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,
                     "scores_per_s": outs[0].numel() / sc_ms * 1e3})
+        if cpu_budget > 0:
+            res["cpu_baseline"] = cpu_baseline_mse(cfg, kind, b, cpu_budget)
     elif name in ("hd64", "hd256"):
         # head dims 64 and 256: scores and decode attention of 32 query heads over 4 x 8 x 32768 keys
         # and values (MSE, 4-bit keys, 2-bit values, dense R, bf16 inputs from the KV generator)
@@ -455,6 +529,8 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
                     "attention_ms": at_ms, "attention_gbs": (kbytes + vbytes) / at_ms / 1e6,
                     "attention_frac_hbm": (kbytes + vbytes) / at_ms / 1e6 / HBM_PEAK_GBS,
                     "kv_positions_per_s": n / at_ms * 1e3})
+        if cpu_budget > 0:
+            res["cpu_baseline"] = cpu_baseline_headdim(d, kb, vb, hq // hkv, cpu_budget)
     elif name in ("c4b2", "c4b4"):
         cfg = wl.CONFIGS["c4"]
         b = 2 if name == "c4b2" else 4
