@@ -13,7 +13,8 @@
 //   * the norm is the lane's sum of squares reduced over the quad the same way.
 // The Hadamard output keeps the input's index order, so each lane then owns the rotated
 // coordinates 32 u .. 32 u + 31: it quantizes them (sign-magnitude thresholds scaled by the norm,
-// as the MFMA encode) and writes its BITS words of the packed row itself.  No LDS, no MFMA.
+// bits pushed into its words from the wave's decision masks, as the MFMA encode) and writes its
+// BITS words of the packed row itself.  No LDS, no MFMA.
 #include "tq_device.h"
 
 namespace tq {
@@ -25,6 +26,14 @@ constexpr int kFwhtThreads = 256;  // 64 vectors per block
 template <int CTRL>
 __device__ __forceinline__ float quad_swap(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// w = 2 w + (this lane's bit of `lanes`): one v_addc with the lane mask as carry-in.
+__device__ __forceinline__ uint32_t shift_in_w(uint32_t w, uint64_t lanes) {
+  uint32_t r;
+  uint64_t carry;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry) : "v"(w), "s"(lanes));
+  return r;
 }
 
 template <int BITS, bool BF16IN, bool FULL>
@@ -95,8 +104,11 @@ __global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* _
   }
 
   // Sign-magnitude decisions against the thresholds t_p * ||x|| / rscale (v is sqrt(g) times the
-  // unit coordinate's scale): idx = (m ^ sign) + K/2, m = #{p : |v| >= t_p}; a zero vector gives
-  // K/2 everywhere (thresholds +inf, and its -0 coordinates counted as non-negative).
+  // unit coordinate's scale): idx = (m ^ sgn) + K/2, m = #{p : |v| >= t_p}, so the top bit is
+  // [v >= 0] and the low bits are m's bits XNOR [v >= 0]; m's bits come from a binary search over
+  // the sorted thresholds, top first.  Each bit enters its word from the bottom (one v_addc with
+  // the wave's decision mask as carry-in), coordinates in descending order.  A zero vector has
+  // every threshold at +inf and its coordinates (+-0) count as non-negative: index K/2.
   const bool live = nrm > 0.f;
   const float tsc = nrm * rscale;
   float thr[H > 1 ? H - 1 : 1];
@@ -106,28 +118,27 @@ __global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* _
 #pragma unroll
   for (int b = 0; b < BITS; ++b) w[b] = 0u;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int ii = 0; ii < 32; ++ii) {
+    const int i = 31 - ii;
+    const int P = BITS * i;
     const float y = v[i];
+    const uint64_t pos = __builtin_amdgcn_ballot_w64(y >= 0.f);
+    w[(P + BITS - 1) >> 5] = shift_in_w(w[(P + BITS - 1) >> 5], pos);
     const float a = fabsf(y);
-    uint32_t m = 0;
     if constexpr (BITS == 2) {
-      m = a >= thr[0] ? 1u : 0u;
+      w[P >> 5] = shift_in_w(w[P >> 5], ~(__builtin_amdgcn_ballot_w64(a >= thr[0]) ^ pos));
     } else if constexpr (BITS == 3) {
       const bool hi = a >= thr[1];
-      const bool lo = a >= (hi ? thr[2] : thr[0]);
-      m = (hi ? 2u : 0u) | (lo ? 1u : 0u);
+      w[(P + 1) >> 5] = shift_in_w(w[(P + 1) >> 5], ~(__builtin_amdgcn_ballot_w64(hi) ^ pos));
+      w[P >> 5] = shift_in_w(w[P >> 5], ~(__builtin_amdgcn_ballot_w64(a >= (hi ? thr[2] : thr[0])) ^ pos));
     } else if constexpr (BITS == 4) {
       const bool b2 = a >= thr[3];
+      w[(P + 2) >> 5] = shift_in_w(w[(P + 2) >> 5], ~(__builtin_amdgcn_ballot_w64(b2) ^ pos));
       const bool b1 = a >= (b2 ? thr[5] : thr[1]);
+      w[(P + 1) >> 5] = shift_in_w(w[(P + 1) >> 5], ~(__builtin_amdgcn_ballot_w64(b1) ^ pos));
       const float t0 = b2 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]);
-      const bool b0 = a >= t0;
-      m = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+      w[P >> 5] = shift_in_w(w[P >> 5], ~(__builtin_amdgcn_ballot_w64(a >= t0) ^ pos));
     }
-    const uint32_t sgn = live ? (uint32_t)(__float_as_int(y) >> 31) : 0u;
-    const uint32_t id = ((m ^ sgn) + (uint32_t)H) & ((1u << BITS) - 1u);
-    const int p = BITS * i, wi = p >> 5, sh = p & 31;
-    w[wi] |= id << sh;
-    if (sh + BITS > 32) w[wi + 1] |= id >> (32 - sh);
   }
   if (row < n) {
     uint32_t* dst = idx_out + row * (4 * BITS) + BITS * u;
