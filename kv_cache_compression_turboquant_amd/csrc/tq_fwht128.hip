@@ -36,6 +36,44 @@ __device__ __forceinline__ uint32_t shift_in_w(uint32_t w, uint64_t lanes) {
   return r;
 }
 
+// v[i .. i + 7] += s * (the same registers of the partner lane u ^ 1 (STAGE 0) or u ^ 2 (STAGE 1)):
+// one v_fmac_f32 with a DPP quad permute of its first operand each.  The s_nop gives the two wait
+// states a DPP read of a VGPR needs after the VALU instruction that wrote it (the compiler does not
+// see into the asm); inside the block each instruction reads registers written at least 8
+// instructions earlier or before the block.
+template <int STAGE>
+__device__ __forceinline__ void pair_stage8(float (&v)[32], int i, float s) {
+  if constexpr (STAGE == 0) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]), "+v"(v[i + 4]), "+v"(v[i + 5]),
+          "+v"(v[i + 6]), "+v"(v[i + 7])
+        : "v"(s));
+  } else {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]), "+v"(v[i + 4]), "+v"(v[i + 5]),
+          "+v"(v[i + 6]), "+v"(v[i + 7])
+        : "v"(s));
+  }
+}
+
 template <int BITS, bool BF16IN, bool FULL>
 __global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* __restrict__ x, int64_t n,
                                                                    uint4 sigma, float rscale, CodebookArgs cb,
@@ -94,14 +132,21 @@ __global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* _
         v[i + h] = a - b;
       }
   if constexpr (FULL) {
-    // bits 5 and 6: the partner lane holds the other half of each pair; the upper lane keeps a - b
+    // bits 5 and 6: the partner lane holds the other half of each pair.  Each lane forms
+    // own + s * partner (s = -1 in the upper lane of the pair: one fma whose DPP operand is the
+    // partner), which is the upper output negated; the stage at bit 6 pairs lanes of equal sign,
+    // so lanes u = 1 and 2 end with every coordinate negated and u = 0 and 3 with none.  Their
+    // magnitudes are exact; the sign decision below undoes the negation.
     const float s1 = (u & 1) ? -1.f : 1.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = fmaf(s1, v[i], quad_swap<0xB1>(v[i]));
+    for (int i = 0; i < 32; i += 8) pair_stage8<0>(v, i, s1);
     const float s2 = (u & 2) ? -1.f : 1.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = fmaf(s2, v[i], quad_swap<0x4E>(v[i]));
+    for (int i = 0; i < 32; i += 8) pair_stage8<1>(v, i, s2);
   }
+  // lanes whose coordinates are negated (FULL: u = 1, 2 of each quad), among the live vectors'
+  // lanes: a zero vector's +-0 coordinates must all count as non-negative
+  const uint64_t neg = FULL ? (0x6666666666666666ull & __builtin_amdgcn_ballot_w64(nrm > 0.f)) : 0ull;
 
   // Sign-magnitude decisions against the thresholds t_p * ||x|| / rscale (v is sqrt(g) times the
   // unit coordinate's scale): idx = (m ^ sgn) + K/2, m = #{p : |v| >= t_p}, so the top bit is
@@ -122,7 +167,7 @@ __global__ __launch_bounds__(kFwhtThreads) void k_encode_fwht_d128(const void* _
     const int i = 31 - ii;
     const int P = BITS * i;
     const float y = v[i];
-    const uint64_t pos = __builtin_amdgcn_ballot_w64(y >= 0.f);
+    const uint64_t pos = __builtin_amdgcn_ballot_w64(y >= 0.f) ^ neg;
     w[(P + BITS - 1) >> 5] = shift_in_w(w[(P + BITS - 1) >> 5], pos);
     const float a = fabsf(y);
     if constexpr (BITS == 2) {
