@@ -496,7 +496,8 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
             res["cpu_baseline"] = cpu_baseline_mse(cfg, kind, b, cpu_budget)
     elif name in ("hd64", "hd256"):
         # head dims 64 and 256: scores and decode attention of 32 query heads over 4 x 8 x 32768 keys
-        # and values (MSE, 4-bit keys, 2-bit values, dense R, bf16 inputs from the KV generator)
+        # and values (MSE, 4-bit keys, 2-bit values, dense R, bf16 inputs from the KV generator); the
+        # value encode and the keys' encode as TurboQuant_prod (4 bits) are timed too
         d = 64 if name == "hd64" else 256
         B, hkv, hq, T, kb, vb = 4, 8, 32, 32768, 4, 2
         n = B * hkv * T
@@ -505,7 +506,14 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         kx = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=1, outlier_seed=2, scale_seed=3)
                               .reshape(n, d).view(np.int16)).to(dev).view(torch.bfloat16)
         K = tq.encode(kx, kb, "mse", cbk, rot)
-        del kx
+        # the same keys as TurboQuant_prod (kb bits: a (kb - 1)-bit stage and the QJL sketch)
+        qjl = tq.make_qjl(d, 2, rot)
+        cbp = tq.codebook(d, kb - 1)
+        pwsb = tq.encode_workspace(n, d, kb, "prod")
+        pws = torch.empty((pwsb,), dtype=torch.uint8, device=dev) if pwsb else None
+        Kp = tq.encode(kx, kb, "prod", cbp, rot, qjl, ws=pws)
+        prod_ms = _timed(lambda i: tq.encode(kx, kb, "prod", cbp, rot, qjl, out=Kp, ws=pws), steps, warmup)
+        del Kp, pws, kx
         vx = torch.from_numpy(wl.kv_tensor_bf16(B, hkv, T, d, seed=4, outlier_seed=5, scale_seed=None)
                               .reshape(n, d).view(np.int16)).to(dev).view(torch.bfloat16)
         V = tq.encode(vx, vb, "mse", cbv, rot)
@@ -523,6 +531,9 @@ def bench_other(name, steps, warmup, cpu_budget=0.0):
         sc_bytes = kbytes + sc.numel() * 4
         res.update({"head_dim": d, "keys": [B, hkv, T], "query_heads": hq, "k_bits": kb, "v_bits": vb,
                     "value_encode_ms": enc_ms, "value_encode_frac_hbm": n * (2 * d + d * vb // 8 + 4) / enc_ms / 1e6
+                    / HBM_PEAK_GBS,
+                    "key_prod_encode_ms": prod_ms,
+                    "key_prod_encode_frac_hbm": n * (2 * d + d * (kb - 1) // 8 + d // 8 + 8) / prod_ms / 1e6
                     / HBM_PEAK_GBS,
                     "scores_ms": sc_ms, "scores_gbs": sc_bytes / sc_ms / 1e6,
                     "scores_frac_hbm": sc_bytes / sc_ms / 1e6 / HBM_PEAK_GBS,

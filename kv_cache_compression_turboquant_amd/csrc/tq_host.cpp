@@ -390,6 +390,7 @@ void free_qjl(tq_qjl_s* q) {
   if (q->frag_dev) hipFree(q->frag_dev);
   if (q->frag32_dev) hipFree(q->frag32_dev);
   if (q->gfrag_dev) hipFree(q->gfrag_dev);
+  if (q->sp32_dev) hipFree(q->sp32_dev);
   delete q;
 }
 
@@ -464,7 +465,7 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
     }
   tq_status st = upload(s32, &q->s32_dev, "upload qjl");
   if (st == TQ_OK) st = upload(st32, &q->st32_dev, "upload qjl transpose");
-  if (st == TQ_OK && (d == tq::kFragD || general_d(d))) {
+  if (st == TQ_OK && (d == tq::kFragD || general_d(d) || d == 64)) {
     // S' = S R^T in fp64
     std::vector<double> sp((size_t)d * d, 0.0);
     const double* sm = q->s.data();
@@ -489,6 +490,10 @@ tq_status make_qjl(int d, std::vector<double>&& s, tq_rotation_t rot, tq_qjl_t* 
         build_fragments_g(sp.data(), d, 1.0, frag);
         st = upload(frag, &q->gfrag_dev, "upload qjl fragments");
       }
+    } else if (d == 64) {
+      // the d = 64 prod encode splits S' into its own fragments in the kernel
+      std::vector<float> sp32(sp.begin(), sp.end());
+      st = upload(sp32, &q->sp32_dev, "upload qjl S'");
     } else {
       build_fragments_g(sp.data(), d, 1.0, frag);
       st = upload(frag, &q->gfrag_dev, "upload qjl fragments");
@@ -831,6 +836,10 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
   if (d == 64 && !prod)
     return check_launch(tq::launch_encode_mse_d64(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx, out->norms,
                                                   as_stream(stream)),
+                        fn);
+  if (d == 64 && qjl->sp32_dev && cb->args.bits <= 3)
+    return check_launch(tq::launch_encode_prod_d64(x_dev, dt == TQ_BF16, n, rot, qjl, cb->args, out->idx,
+                                                   out->norms, out->qjl, out->rnorms, as_stream(stream)),
                         fn);
   if (d == 64)
     return check_launch(tq::launch_encode_d64(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args, out->idx,

@@ -77,6 +77,7 @@ struct tq_qjl_s {
   uint16_t* frag_dev = nullptr;   // bf16 fragments of S' = S R^T [2][kFragElems] (d = 128)
   uint16_t* frag32_dev = nullptr; // S' as 32 x 32 x 16 fragments, laid out as tq_rotation_s::frag32_dev
   uint16_t* gfrag_dev = nullptr;  // general d: chunked A fragments of S', as tq_rotation_s::gfrag_dev
+  float* sp32_dev = nullptr;      // d = 64: S' = S R^T in fp32, row-major [d, d]
 };
 
 namespace tq {
@@ -142,6 +143,11 @@ hipError_t launch_encode_d64(const void* x, bool bf16, int64_t n, const tq_rotat
 // TurboQuant_mse encode at d = 64 (rows layout) on the 32 x 32 x 16 matrix cores, R from rot->r32_dev.
 hipError_t launch_encode_mse_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                                  const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);
+// TurboQuant_prod encode at d = 64 on the same matrix cores (cb: the (b-1)-bit stage), S' from
+// qjl->sp32_dev.
+hipError_t launch_encode_prod_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                  const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
+                                  uint32_t* qbits, float* rnorms, hipStream_t st);
 
 // TurboQuant_mse encode at d = 128 (rows layout) for the randomized Hadamard rotations, as a
 // fast Walsh-Hadamard transform in registers: full = true for H diag(sigma) / sqrt(128), false for
