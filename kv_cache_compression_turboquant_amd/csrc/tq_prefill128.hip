@@ -16,9 +16,10 @@
 // (query n, lane group g) over a 32-key step are keys 8 g .. 8 g + 7: exactly the B operand the
 // P V product needs, so the weights never leave the lane's registers, and each query's softmax
 // reductions are across the four lane groups only.
-// A block is four waves of one (batch, kv head); each wave takes one (query head, 16-token tile)
-// item; the block's 32-key steps of packed keys, values and norms are staged in LDS (double
-// buffered) and shared by its waves.  The output stays in V's rotated domain; k_prefill_unrotate
+// A block is four waves of one (batch, kv head); each wave takes one (pair of query heads of the
+// kv head, 16-token tile) item: the two heads see the same keys, values and causal mask, so each
+// decoded key and value operand feeds both heads' products.  The block's 32-key steps of packed
+// keys, values and norms are staged in LDS (double buffered) and shared by its waves.  The output stays in V's rotated domain; k_prefill_unrotate
 // applies R_V^T row by row.
 #include <hip/hip_runtime.h>
 
@@ -138,15 +139,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
   const int bh = blockIdx.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int ratio = Hq / Hkv;
+  const int hp = (ratio + 1) / 2;                    // head pairs per kv head
   const int64_t ntile = (n_new + kPfTok - 1) / kPfTok;
-  // this wave's item: (16-token tile tau, query head hj of the kv head), items ordered tau-major
+  // this wave's item: (16-token tile tau, heads 2 pr and 2 pr + 1 of the kv head), tau-major
   const int64_t item = (int64_t)blockIdx.x * kPfWaves + wave;
-  const int64_t tau = item / ratio;
-  const int hj = (int)(item % ratio);
+  const int64_t tau = item / hp;
+  const int pr = (int)(item % hp);
   const bool live = tau < ntile;
+  const bool live1 = live && 2 * pr + 1 < ratio;     // an odd ratio leaves the last pair one head
+  const int hjs[2] = {2 * pr, live1 ? 2 * pr + 1 : 2 * pr};
   const int64_t tok0 = tau * kPfTok;
   // the block's last live tile bounds the keys it needs: tokens 0 .. pos + (its last token)
-  int64_t tau_max = ((int64_t)blockIdx.x * kPfWaves + kPfWaves - 1) / ratio;
+  int64_t tau_max = ((int64_t)blockIdx.x * kPfWaves + kPfWaves - 1) / hp;
   if (tau_max > ntile - 1) tau_max = ntile - 1;
   const int64_t last_tok = (tau_max + 1) * kPfTok < n_new ? (tau_max + 1) * kPfTok - 1 : n_new - 1;
   const int64_t kend = pos + last_tok + 1;            // keys [0, kend)
@@ -155,24 +159,27 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
   const int64_t wave_keys = pos + tok0 + kPfTok;
   const int64_t row0 = (int64_t)bh * t_cap;
 
-  // B operand of the key product: query token tok0 + n of head h, coordinates 32 g + 8 s .. + 7
-  u32x4 bqh[4], bql[4];
-  {
+  // B operands of the key product: query token tok0 + n of each head, coordinates 32 g + 8 s .. + 7
+  u32x4 bqh[2][4], bql[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
     const int64_t tq = tok0 + nl < n_new ? tok0 + nl : n_new - 1;
-    const int64_t qrow = (((int64_t)b * Hq + kvh * ratio + hj) * n_new + (live ? tq : 0));
+    const int64_t qrow = (((int64_t)b * Hq + kvh * ratio + hjs[hh]) * n_new + (live ? tq : 0));
     const u32x4* sh = reinterpret_cast<const u32x4*>(qh + qrow * 128 + 32 * g);
     const u32x4* sl = reinterpret_cast<const u32x4*>(ql + qrow * 128 + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bqh[s] = sh[s];
-      bql[s] = sl[s];
+      bqh[hh][s] = sh[s];
+      bql[hh][s] = sl[s];
     }
   }
   const int64_t my_tok = pos + tok0 + nl;             // absolute position of the lane's query
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // cooperative staging of step st: u32x4 units 0 .. KW/4 - 1 keys, then VW/4 value words, then
   // 8 + 8 units of norms
@@ -215,87 +222,105 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
     if (st + 1 < nsteps) fetch(st + 1);
     const int64_t key0 = st * 32;
     if (live && key0 < wave_keys) {
-      // ---- scores^T for the step's 32 keys: tile t, lane (query nl, group g), register r is key
-      // 8 g + 4 t + r
-      float s[8];
+      // ---- scores^T for the step's 32 keys, both heads: tile t, lane (query nl, group g), register
+      // r is key 8 g + 4 t + r
+      float s[2][8];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int kl = 8 * (nl >> 2) + 4 * t + (nl & 3);     // this lane's A row (key) of tile t
         uint32_t kw[KB];
 #pragma unroll
         for (int j = 0; j < KB; ++j) kw[j] = kst[buf][kl * (4 * KB) + KB * g + j];
-        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const u32x4 ah = decode_keys<KB, KC>(kw, q4, kth);
           const u32x4 al = decode_keys<KB, KC>(kw, q4, ktl);
-          d = mfma_f16(ah, bqh[q4], d);
-          d = mfma_f16(al, bqh[q4], d);
-          d = mfma_f16(ah, bql[q4], d);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            d[hh] = mfma_f16(ah, bqh[hh][q4], d[hh]);
+            d[hh] = mfma_f16(al, bqh[hh][q4], d[hh]);
+            d[hh] = mfma_f16(ah, bql[hh][q4], d[hh]);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int k = 8 * g + 4 * t + r;
           const int64_t key = key0 + k;
-          s[4 * t + r] = key <= my_tok ? d[r] * knst[buf][k] * scale : -INFINITY;
+          const bool vis = key <= my_tok;
+          const float kn = knst[buf][k] * scale;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) s[hh][4 * t + r] = vis ? d[hh][r] * kn : -INFINITY;
         }
       }
-      // ---- online softmax of query nl (its 32 keys are spread over the four lane groups)
-      float mx = s[0];
+      // ---- online softmax of query nl per head (its 32 keys are spread over the four lane groups)
+      u32x4 bph[2], bpl[2];
 #pragma unroll
-      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
-      float psum = 0.f;
-      uint32_t ph[4], pl[4];
+      for (int hh = 0; hh < 2; ++hh) {
+        float mx = s[hh][0];
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const float p0 = s[k] == -INFINITY ? 0.f : __expf(s[k] - m_new);
-        const float p1 = s[k + 1] == -INFINITY ? 0.f : __expf(s[k + 1] - m_new);
-        psum += p0 + p1;
-        // masked keys give exactly 0 (rows past the written prefix may hold any bits, NaN norms too)
-        const float w0 = s[k] == -INFINITY ? 0.f : p0 * vnst[buf][8 * g + k];
-        const float w1 = s[k + 1] == -INFINITY ? 0.f : p1 * vnst[buf][8 * g + k + 1];
-        const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
-        const _Float16 r0 = (_Float16)(w0 - (float)h0), r1 = (_Float16)(w1 - (float)h1);
-        ph[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        pl[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+        for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[hh][k]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[hh], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run[hh] - m_new);
+        float psum = 0.f;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          const float p0 = s[hh][k] == -INFINITY ? 0.f : __expf(s[hh][k] - m_new);
+          const float p1 = s[hh][k + 1] == -INFINITY ? 0.f : __expf(s[hh][k + 1] - m_new);
+          psum += p0 + p1;
+          // masked keys give exactly 0 (rows past the written prefix may hold any bits, NaN norms too)
+          const float w0 = s[hh][k] == -INFINITY ? 0.f : p0 * vnst[buf][8 * g + k];
+          const float w1 = s[hh][k + 1] == -INFINITY ? 0.f : p1 * vnst[buf][8 * g + k + 1];
+          const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
+          const _Float16 r0 = (_Float16)(w0 - (float)h0), r1 = (_Float16)(w1 - (float)h1);
+          ph[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          pl[k >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+        }
+        l_run[hh] = fmaf(l_run[hh], alpha, psum);
+        m_run[hh] = m_new;
+        if (alpha < 1.f) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[hh][c] *= alpha;
+        }
+        bph[hh] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        bpl[hh] = u32x4{pl[0], pl[1], pl[2], pl[3]};
       }
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-      if (alpha < 1.f) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] *= alpha;
-      }
-      const u32x4 bph = u32x4{ph[0], ph[1], ph[2], ph[3]};
-      const u32x4 bpl = u32x4{pl[0], pl[1], pl[2], pl[3]};
       // ---- O^T += V_hat^T P^T: A row m of block c is coordinate 16 c + m; lane (m, g) holds
-      // the chunk of octet g (keys 8 g .. 8 g + 7) at that coordinate
+      // the chunk of octet g (keys 8 g .. 8 g + 7) at that coordinate; one decode, both heads
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int off = ((g * 128 + 16 * c + nl) * 8 * VB);
         const uint32_t w2[2] = {vst[buf][off >> 5], vst[buf][(off >> 5) + 1]};
         const u32x4 av = decode8<VB, VC>(w2, off & 31, vtl);
-        o[c] = mfma_f16(av, bph, o[c]);
-        o[c] = mfma_f16(av, bpl, o[c]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          o[hh][c] = mfma_f16(av, bph[hh], o[hh][c]);
+          o[hh][c] = mfma_f16(av, bpl[hh], o[hh][c]);
+        }
       }
     }
     if (st + 1 < nsteps) stash(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- the lane's query nl: its sum over the four lane groups; coordinates 16 c + 4 g + r
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (live && tok0 + nl < n_new) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* dst = out + ((((int64_t)b * Hq + kvh * ratio + hj) * n_new) + tok0 + nl) * 128;
+  // ---- the lane's query nl of each head: its sum over the four lane groups; coordinates
+  // 16 c + 4 g + r
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+  for (int hh = 0; hh < 2; ++hh) {
+    float l = l_run[hh];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (live && (hh == 0 || live1) && tok0 + nl < n_new) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* dst = out + ((((int64_t)b * Hq + kvh * ratio + hjs[hh]) * n_new) + tok0 + nl) * 128;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[16 * c + 4 * g + r] = o[c][r] * inv;
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[16 * c + 4 * g + r] = o[hh][c][r] * inv;
+    }
   }
 }
 
@@ -304,7 +329,7 @@ hipError_t prefill_launch(int B, int Hq, int Hkv, int64_t n_new, int64_t pos, in
                           const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv, float scale,
                           const uint16_t* qh, const uint16_t* ql, float* out, hipStream_t st) {
   const int ratio = Hq / Hkv;
-  const int64_t items = (n_new + kPfTok - 1) / kPfTok * ratio;
+  const int64_t items = (n_new + kPfTok - 1) / kPfTok * ((ratio + 1) / 2);
   const int64_t blocks = (items + kPfWaves - 1) / kPfWaves;
   hipLaunchKernelGGL((k_prefill_attn<KB, VB>), dim3((unsigned)blocks, (unsigned)(B * Hkv)), dim3(kPfWaves * 64), 0, st,
                      qh, ql, Hq, Hkv, n_new, pos, t_cap, K->idx, K->norms, V->idx, V->norms, cbk, cbv, scale, out);

@@ -99,7 +99,7 @@ def _run(dev, rot, B, hkv, hq, t_cap, plan, kb, vb, dtype=torch.bfloat16, seed=0
 
 
 @pytest.mark.parametrize("B,hkv,hq,kb,vb", [(1, 2, 8, 2, 2), (2, 1, 4, 4, 4), (1, 2, 4, 3, 2), (1, 1, 1, 4, 3),
-                                            (1, 1, 8, 2, 4)])
+                                            (1, 1, 8, 2, 4), (1, 2, 6, 2, 3)])
 def test_prefill_chunks_match_oracle(dev, rot, B, hkv, hq, kb, vb):
     # a 45-token prompt, a 70-token chunk, a single token, then a 33-token chunk
     _run(dev, rot, B, hkv, hq, 160, [(0, 45), (45, 70), (115, 1), (116, 33)], kb, vb, seed=kb * 10 + vb)
