@@ -36,7 +36,7 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
     const void* __restrict__ x, int64_t n, const u32x4* __restrict__ frag_r,
     const u32x4* __restrict__ frag_s, float post_scale, CodebookArgs cb,
     uint32_t* __restrict__ idx_out, float* __restrict__ norms_out, uint32_t* __restrict__ qjl_out,
-    float* __restrict__ rnorm_out, float* __restrict__ y_out) {
+    float* __restrict__ rnorm_out, float* __restrict__ y_out, int y_raw) {
   constexpr int RP = PASSES;              // rotation passes held in LDS
   constexpr int SP = PROD ? 2 : 0;        // S' passes
   constexpr int kWaves = EncShape<PROD>::kWaves;
@@ -173,10 +173,12 @@ __global__ __launch_bounds__(EncShape<PROD>::kWaves * 64, EncShape<PROD>::kBlock
       const bool valid = row < n;
       if (valid && g == 0 && norms_out) norms_out[row] = nrm;
       if constexpr (STORE_Y) {
+        // y_raw: the product itself (R x), else the unit-scale coordinates (R x / ||x||)
+        const float ys = y_raw ? post_scale : scale;
         if (valid) {
           f32x4* dst = reinterpret_cast<f32x4*>(y_out + row * 128 + 32 * g);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) dst[c] = acc[t][c] * scale;
+          for (int c = 0; c < 8; ++c) dst[c] = acc[t][c] * ys;
         }
       } else {
         // Decisions on the raw product against per-vector thresholds t_p * ||x|| / post_scale
@@ -746,7 +748,7 @@ hipError_t mse_dispatch(const void* x, bool bf16, int64_t n, const tq_rotation_s
 template <int BITS, bool PROD, bool BF16IN, bool STORE_Y, int PASSES>
 hipError_t enc_launch(const void* x, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                       const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits,
-                      float* rnorms, float* y, hipStream_t st) {
+                      float* rnorms, float* y, hipStream_t st, const uint16_t* frag = nullptr, int y_raw = 0) {
   constexpr int NT = (PROD || !BF16IN) ? 1 : 2;
   constexpr int kWaves = EncShape<PROD>::kWaves;
   const int64_t ntiles = (n + 15) / 16;
@@ -758,16 +760,16 @@ hipError_t enc_launch(const void* x, int64_t n, const tq_rotation_s* rot, const 
   if (take_armed_timer(&ev0, &ev1)) {
     hipExtLaunchKernelGGL((k_encode_d128<BITS, PROD, BF16IN, STORE_Y, PASSES, NT>), dim3((unsigned)blocks),
                           dim3(kWaves * 64), 0, st, ev0, ev1, 0, x, n,
-                          reinterpret_cast<const u32x4*>(rot->frag_dev),
+                          reinterpret_cast<const u32x4*>(frag ? frag : rot->frag_dev),
                           reinterpret_cast<const u32x4*>(qjl ? qjl->frag_dev : nullptr), rot->post_scale, cb, idx,
-                          norms, qbits, rnorms, y);
+                          norms, qbits, rnorms, y, y_raw);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((k_encode_d128<BITS, PROD, BF16IN, STORE_Y, PASSES, NT>), dim3((unsigned)blocks),
                      dim3(kWaves * 64), 0, st, x, n,
-                     reinterpret_cast<const u32x4*>(rot->frag_dev),
+                     reinterpret_cast<const u32x4*>(frag ? frag : rot->frag_dev),
                      reinterpret_cast<const u32x4*>(qjl ? qjl->frag_dev : nullptr), rot->post_scale, cb, idx,
-                     norms, qbits, rnorms, y);
+                     norms, qbits, rnorms, y, y_raw);
   return hipGetLastError();
 }
 
@@ -786,6 +788,22 @@ hipError_t enc_dispatch_in(const void* x, bool bf16, int64_t n, const tq_rotatio
 }
 
 }  // namespace
+
+hipError_t launch_rotate_raw_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, bool transpose,
+                                  float* y, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const uint16_t* frag = transpose ? rot->fragT_dev : rot->frag_dev;
+  if (!frag) return hipErrorInvalidValue;
+  CodebookArgs none{};
+  none.bits = 1;
+  if (bf16)
+    return rot->passes == 1
+               ? enc_launch<1, false, true, true, 1>(x, n, rot, nullptr, none, nullptr, nullptr, nullptr, nullptr, y, st, frag, 1)
+               : enc_launch<1, false, true, true, 2>(x, n, rot, nullptr, none, nullptr, nullptr, nullptr, nullptr, y, st, frag, 1);
+  return rot->passes == 1
+             ? enc_launch<1, false, false, true, 1>(x, n, rot, nullptr, none, nullptr, nullptr, nullptr, nullptr, y, st, frag, 1)
+             : enc_launch<1, false, false, true, 2>(x, n, rot, nullptr, none, nullptr, nullptr, nullptr, nullptr, y, st, frag, 1);
+}
 
 hipError_t launch_encode_outlier8(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const CodebookArgs& cb,
                                   const OutlierArgs& oa, uint32_t* idx, float* norms, hipStream_t st) {

@@ -378,6 +378,7 @@ void free_rotation(tq_rotation_s* r) {
   if (r->rt32_dev) hipFree(r->rt32_dev);
   if (r->frag_dev) hipFree(r->frag_dev);
   if (r->fragt_dev) hipFree(r->fragt_dev);
+  if (r->fragT_dev) hipFree(r->fragT_dev);
   if (r->frag32_dev) hipFree(r->frag32_dev);
   if (r->gfrag_dev) hipFree(r->gfrag_dev);
   delete r;
@@ -430,6 +431,19 @@ tq_status finish_rotation(tq_rotation_s* r) {
     if (st != TQ_OK) return st;
     st = upload(frag32, &r->frag32_dev, "upload rotation fragments");
     if (st != TQ_OK) return st;
+    {
+      // fragments of R^T in the same layout (for y = R^T x); a (block) Hadamard R^T has the same
+      // entries up to order, so the same scale and pass count hold
+      std::vector<double> rtr((size_t)d * d);
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) rtr[(size_t)j * d + i] = r->r[(size_t)i * d + j];
+      const bool wht_t = r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT;
+      std::vector<uint16_t> fragT;
+      build_fragments(rtr.data(), wht_t ? std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup)) : 1.0,
+                      fragT);
+      st = upload(fragT, &r->fragT_dev, "upload rotation fragments");
+      if (st != TQ_OK) return st;
+    }
     // the general-d layout too: the search's query prologue runs the general-d GEMM at any d
     const bool wht = r->kind == TQ_ROT_WHT || r->kind == TQ_ROT_BLOCK_WHT;
     build_fragments_g(r->r.data(), d, wht ? std::sqrt((double)(r->kind == TQ_ROT_WHT ? d : kBlockWhtGroup)) : 1.0,

@@ -60,6 +60,7 @@ struct tq_rotation_s {
                                   // (128 x 128) chunk per (output block ob, contraction block kc):
                                   // [ob][kc][pass 0..1][kFragElems], rows as in frag_dev, columns
                                   // 32 s + 8 g + e for instruction s of lane group g
+  uint16_t* fragT_dev = nullptr;  // d = 128: A fragments of R^T, laid out as frag_dev (y = R^T x)
   uint16_t* frag32_dev = nullptr; // d = 128: A fragments for v_mfma_f32_32x32x16_bf16 [2][kFragElems]:
                                   // [pass][ob][s][lane][e] = R[o][c], i = lane % 32, j = lane / 32,
                                   // o = 64 ((i >> 2) & 1) + 16 ob + 4 (i >> 3) + (i & 3), c = 64 j + 8 s + e
@@ -140,6 +141,11 @@ hipError_t launch_decode_attn_gen(const float* q, int B, int Hq, int Hkv, int64_
 hipError_t launch_encode_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, const tq_qjl_s* qjl,
                              const CodebookArgs& cb, uint32_t* idx, float* norms, uint32_t* qbits, float* rnorms,
                              hipStream_t st);
+// y = R x (transpose: y = R^T x) for n rows of 128 at fp32 level (bf16 hi / lo passes), the product
+// itself rather than unit coordinates; x fp32 or bf16, y fp32 [n, 128].
+hipError_t launch_rotate_raw_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot, bool transpose,
+                                  float* y, hipStream_t st);
+
 // TurboQuant_mse encode at d = 64 (rows layout) on the 32 x 32 x 16 matrix cores, R from rot->r32_dev.
 hipError_t launch_encode_mse_d64(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                                  const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);

@@ -31,72 +31,15 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfTok = 16;          // query tokens of a wave's item
-constexpr int kPfQRows = 8;         // query rows per block of the rotation kernels
-
-// q_rot = R q (fp16 hi and lo) for `rows` query rows of 128: rt = R^T row-major, so thread j's
-// reads of column j are coalesced.  Eight rows per block, staged in LDS.
-__global__ __launch_bounds__(256) void k_prefill_qrot(const float* __restrict__ q, int64_t rows,
-                                                      const float* __restrict__ rt, uint16_t* __restrict__ qh,
-                                                      uint16_t* __restrict__ ql) {
-  __shared__ float qs[kPfQRows][128];
-  const int64_t r0 = (int64_t)blockIdx.x * kPfQRows;
-  for (int i = threadIdx.x; i < kPfQRows * 128; i += 256) {
-    const int64_t rr = r0 + (i >> 7);
-    qs[i >> 7][i & 127] = rr < rows ? q[rr * 128 + (i & 127)] : 0.f;
-  }
-  __syncthreads();
-  const int j = threadIdx.x & 127, hh = threadIdx.x >> 7;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < 128; ++k) {
-    const float rv = rt[k * 128 + j];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rv, qs[4 * hh + u][k], acc[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t row = r0 + 4 * hh + u;
-    if (row < rows) {
-      const _Float16 h = (_Float16)acc[u];
-      const _Float16 l = (_Float16)(acc[u] - (float)h);
-      qh[row * 128 + j] = __builtin_bit_cast(uint16_t, h);
-      ql[row * 128 + j] = __builtin_bit_cast(uint16_t, l);
-    }
-  }
-}
-
-// out[row] = R_V^T o[row] in place for `rows` rows of 128 (r = R_V row-major, coalesced over j).
-__global__ __launch_bounds__(256) void k_prefill_unrotate(float* __restrict__ o, int64_t rows,
-                                                          const float* __restrict__ r) {
-  __shared__ float os[kPfQRows][128];
-  const int64_t r0 = (int64_t)blockIdx.x * kPfQRows;
-  for (int i = threadIdx.x; i < kPfQRows * 128; i += 256) {
-    const int64_t rr = r0 + (i >> 7);
-    os[i >> 7][i & 127] = rr < rows ? o[rr * 128 + (i & 127)] : 0.f;
-  }
-  __syncthreads();
-  const int j = threadIdx.x & 127, hh = threadIdx.x >> 7;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < 128; ++k) {
-    const float rv = r[k * 128 + j];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rv, os[4 * hh + u][k], acc[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t row = r0 + 4 * hh + u;
-    if (row < rows) o[row * 128 + j] = acc[u];
-  }
-}
-
 // LDS budgets of the three decode tables (K centroid hi, K remainder lo, V).
 constexpr int kPfTableBudget = 12288;
 
 template <int KB, int VB>
 __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
-    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql, int Hq, int Hkv, int64_t n_new, int64_t pos,
+    float* qo, int Hq, int Hkv, int64_t n_new, int64_t pos,
     int64_t t_cap, const uint32_t* __restrict__ kidx, const float* __restrict__ knorm,
     const uint32_t* __restrict__ vidx, const float* __restrict__ vnorm, CodebookArgs cbk, CodebookArgs cbv,
-    float scale, float* __restrict__ out) {
+    float scale) {
   constexpr int KC = table_copies<KB, false, kPfTableBudget>();
   constexpr int VC = table_copies<VB, false, kPfTableBudget>();
   using DK = DecodeTable<KB, false, KC>;
@@ -159,18 +102,25 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
   const int64_t wave_keys = pos + tok0 + kPfTok;
   const int64_t row0 = (int64_t)bh * t_cap;
 
-  // B operands of the key product: query token tok0 + n of each head, coordinates 32 g + 8 s .. + 7
+  // B operands of the key product: R_K q of query token tok0 + n of each head (qo, fp32), coordinates
+  // 32 g + 8 s .. + 7, as fp16 hi and lo.  Only this wave reads or writes these rows of qo.
   u32x4 bqh[2][4], bql[2][4];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int64_t tq = tok0 + nl < n_new ? tok0 + nl : n_new - 1;
     const int64_t qrow = (((int64_t)b * Hq + kvh * ratio + hjs[hh]) * n_new + (live ? tq : 0));
-    const u32x4* sh = reinterpret_cast<const u32x4*>(qh + qrow * 128 + 32 * g);
-    const u32x4* sl = reinterpret_cast<const u32x4*>(ql + qrow * 128 + 32 * g);
+    const f32x4* src = reinterpret_cast<const f32x4*>(qo + qrow * 128 + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bqh[hh][s] = sh[s];
-      bql[hh][s] = sl[s];
+      const f32x4 v0 = src[2 * s], v1 = src[2 * s + 1];
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const _Float16 h0 = (_Float16)v[2 * k], h1 = (_Float16)v[2 * k + 1];
+        const _Float16 l0 = (_Float16)(v[2 * k] - (float)h0), l1 = (_Float16)(v[2 * k + 1] - (float)h1);
+        bqh[hh][s][k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        bql[hh][s][k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
     }
   }
   const int64_t my_tok = pos + tok0 + nl;             // absolute position of the lane's query
@@ -315,7 +265,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
     l += __shfl_xor(l, 32);
     if (live && (hh == 0 || live1) && tok0 + nl < n_new) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float* dst = out + ((((int64_t)b * Hq + kvh * ratio + hjs[hh]) * n_new) + tok0 + nl) * 128;
+      float* dst = qo + ((((int64_t)b * Hq + kvh * ratio + hjs[hh]) * n_new) + tok0 + nl) * 128;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -327,20 +277,21 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void k_prefill_attn(
 template <int KB, int VB>
 hipError_t prefill_launch(int B, int Hq, int Hkv, int64_t n_new, int64_t pos, int64_t t_cap, const tq_packed* K,
                           const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv, float scale,
-                          const uint16_t* qh, const uint16_t* ql, float* out, hipStream_t st) {
+                          float* qo, hipStream_t st) {
   const int ratio = Hq / Hkv;
   const int64_t items = (n_new + kPfTok - 1) / kPfTok * ((ratio + 1) / 2);
   const int64_t blocks = (items + kPfWaves - 1) / kPfWaves;
   hipLaunchKernelGGL((k_prefill_attn<KB, VB>), dim3((unsigned)blocks, (unsigned)(B * Hkv)), dim3(kPfWaves * 64), 0, st,
-                     qh, ql, Hq, Hkv, n_new, pos, t_cap, K->idx, K->norms, V->idx, V->norms, cbk, cbv, scale, out);
+                     qo, Hq, Hkv, n_new, pos, t_cap, K->idx, K->norms, V->idx, V->norms, cbk, cbv, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t prefill_attn_workspace_bytes(int B, int Hq, int64_t n_new) {
+  // R_K q in fp32 for every query row (later the output in V's rotated domain)
   const size_t rows = (size_t)B * Hq * (size_t)n_new;
-  return ((rows * 128 * sizeof(uint16_t) + 255) & ~(size_t)255) * 2;
+  return (rows * 128 * sizeof(float) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_prefill_attn(const float* q, int B, int Hq, int Hkv, int64_t n_new, int64_t pos, int64_t t_cap,
@@ -348,22 +299,17 @@ hipError_t launch_prefill_attn(const float* q, int B, int Hq, int Hkv, int64_t n
                                const CodebookArgs& cbv, const tq_rotation_s* rot_k, const tq_rotation_s* rot_v,
                                float scale, float* out, void* ws, hipStream_t st) {
   const int64_t rows = (int64_t)B * Hq * n_new;
-  const size_t half = ((size_t)rows * 128 * sizeof(uint16_t) + 255) & ~(size_t)255;
-  uint16_t* qh = static_cast<uint16_t*>(ws);
-  uint16_t* ql = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
-  const unsigned rblocks = (unsigned)((rows + kPfQRows - 1) / kPfQRows);
-  hipLaunchKernelGGL(k_prefill_qrot, dim3(rblocks), dim3(256), 0, st, q, rows, rot_k->rt32_dev, qh, ql);
-  hipError_t e = hipGetLastError();
+  float* qo = static_cast<float*>(ws);   // R_K q, then the attention output in V's rotated domain
+  hipError_t e = launch_rotate_raw_d128(q, false, rows, rot_k, false, qo, st);
   if (e != hipSuccess) return e;
 #define TQ_PF(KB, VB) \
   if (cbk.bits == KB && cbv.bits == VB) \
-    e = prefill_launch<KB, VB>(B, Hq, Hkv, n_new, pos, t_cap, K, V, cbk, cbv, scale, qh, ql, out, st); else
+    e = prefill_launch<KB, VB>(B, Hq, Hkv, n_new, pos, t_cap, K, V, cbk, cbv, scale, qo, st); else
   TQ_PF(2, 2) TQ_PF(4, 4) TQ_PF(3, 3) TQ_PF(4, 2) TQ_PF(2, 4) TQ_PF(3, 2) TQ_PF(4, 3) TQ_PF(1, 1) TQ_PF(2, 3)
   TQ_PF(3, 4) return hipErrorInvalidValue;
 #undef TQ_PF
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_prefill_unrotate, dim3(rblocks), dim3(256), 0, st, out, rows, rot_v->r32_dev);
-  return hipGetLastError();
+  return launch_rotate_raw_d128(qo, false, rows, rot_v, true, out, st);
 }
 
 }  // namespace tq
