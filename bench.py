@@ -31,7 +31,7 @@ CACHE_DEFEAT_BYTES = 1.5e9
 
 # Sources of each timed kernel: its counters stay valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "encode": ("tq_device.h", "tq_internal.h", "tq_encode128.hip"),
+    "encode": ("tq_device.h", "tq_internal.h", "tq_encode_mse32.hip"),
     "prod_encode": ("tq_device.h", "tq_internal.h", "tq_encode_prod128.hip"),
     "scores": ("tq_device.h", "tq_internal.h", "tq_decode.h", "tq_cache.h", "tq_score128.hip"),
 }
@@ -39,14 +39,14 @@ KERNEL_SOURCES = {
 HEADLINE_KERNELS = {
     "c3": ("k_encode_prod_d128<3, true, 2> (prod b=4, dense R, bf16 keys)",
            "k_scores_d128<3, true, false, 0> (prod, GQA 4)"),
-    "c2": ("k_encode_mse_d128<3, true, 2, 2, 0> (MSE b=3, dense R, bf16 keys)",
+    "c2": ("k_encode_mse32_d128<3, true, 2> (MSE b=3, dense R, bf16 keys)",
            "k_scores_d128<3, false, false, 0> (MSE, GQA 4)"),
 }
 # name prefixes of those kernels in a rocprofv3 database (for the counter summary)
 PMC_KERNELS = {
     "c3:prod_encode": "k_encode_prod_d128<3, true, 2>",
     "c3:scores": "k_scores_d128<3, true, false, 0>",
-    "c2:encode": "k_encode_mse_d128<3, true, 2,",
+    "c2:encode": "k_encode_mse32_d128<3, true, 2>",
     "c2:scores": "k_scores_d128<3, false, false, 0>",
 }
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_encode_prod128.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip",
+SOURCES = ["tq_host.cpp", "tq_encode128.hip", "tq_encode_prod128.hip", "tq_encode_mse32.hip", "tq_misc.hip", "tq_score128.hip", "tq_attn128.hip",
            "tq_general.hip", "tq_cache128.hip", "tq_split128.hip", "tq_peaks.hip", "tq_noalloc.hip", "tq_prefill128.hip",
            "tq_fwht128.hip", "tq_kvgen.hip", "tq_encode64.hip"]
 

@@ -883,6 +883,10 @@ tq_status tq_encode(const void* x_dev, tq_dtype dt, int64_t n, int d, int b, tq_
                                                     cb->args, out->idx, out->norms, as_stream(stream)),
                         fn);
   }
+  if (!prod && rot->frag32_dev)
+    return check_launch(tq::launch_encode_mse32_d128(x_dev, dt == TQ_BF16, n, rot, cb->args, out->idx, out->norms,
+                                                     as_stream(stream)),
+                        fn);
   return check_launch(tq::launch_encode_d128(x_dev, dt == TQ_BF16, n, rot, prod ? qjl : nullptr, cb->args,
                                              out->idx, out->norms, prod ? out->qjl : nullptr,
                                              prod ? out->rnorms : nullptr, nullptr, as_stream(stream)),

@@ -121,6 +121,10 @@ hipError_t launch_encode_d128(const void* x, bool bf16, int64_t n, const tq_rota
 hipError_t launch_encode_prod_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
                                    const tq_qjl_s* qjl, const CodebookArgs& cb, uint32_t* idx, float* norms,
                                    uint32_t* qjl_bits, float* rnorms, hipStream_t st);
+// TurboQuant_mse encode at d = 128, rows layout, dense rotation, on the 32 x 32 x 16 matrix cores
+// (tq_encode_mse32.hip).
+hipError_t launch_encode_mse32_d128(const void* x, bool bf16, int64_t n, const tq_rotation_s* rot,
+                                    const CodebookArgs& cb, uint32_t* idx, float* norms, hipStream_t st);
 hipError_t launch_quantize_rotated(const float* y, int64_t n, int d, const CodebookArgs& cb,
                                    uint32_t* idx, hipStream_t st);
 hipError_t launch_decode(const tq_packed* p, const CodebookArgs& cb, const tq_rotation_s* rot,
