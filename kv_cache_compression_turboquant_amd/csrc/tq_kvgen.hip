@@ -36,7 +36,10 @@ __device__ __forceinline__ void gen_for(F&& f) {
 
 constexpr int kGenThreads = 256;
 constexpr int kGenHeadGroup = 8;   // query heads staged at once
-constexpr int kGenAttnTiles = 4;   // 256-key tiles per attention range
+#ifndef TQ_GEN_ATTN_TILES
+#define TQ_GEN_ATTN_TILES 4
+#endif
+constexpr int kGenAttnTiles = TQ_GEN_ATTN_TILES;   // 256-key tiles per attention range
 
 // ---------------------------------------------------------------------------------------
 // Query prologue: ws[h] = {R q_h (d floats), S q_h (d floats)}; one block of 256 threads per head.
@@ -92,18 +95,13 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N]) {
   return v & ((1u << BITS) - 1u);
 }
 
-// Stages the R q / S q rows of heads h0 .. h0 + nh - 1 of `ws` into LDS (2 D floats per head).
-template <int D>
-__device__ __forceinline__ void stage_heads(const float* __restrict__ ws, int64_t h0, int nh, float* dst) {
-  for (int i = threadIdx.x; i < nh * 2 * D; i += blockDim.x) dst[i] = ws[h0 * 2 * D + i];
-}
-
 // ---------------------------------------------------------------------------------------
 // Decode attention, one range of kGenAttnTiles tiles of one sequence per block; the GQA ratio
 // (<= 8) heads of the sequence's kv head at once.  Per tile of 256 keys:
-//   1. thread t stages key t's index words, its value's words and norms in LDS (one round of
-//      loads per tile);
-//   2. thread t forms key t's logits from the staged words (32 coordinates at a time);
+//   1. thread t stages key t's index words and its value's words in LDS (one round of loads per
+//      tile; the norms stay in registers);
+//   2. thread t forms key t's logits from its staged row, 32 coordinates at a time, with the
+//      queries read by scalar loads (uniform across the wave, no LDS traffic);
 //   3. online softmax per head (block reductions); p * s_v per (head, key) into LDS;
 //   4. P V: thread (g4, kp) owns coordinates 4 g4 .. 4 g4 + 3 and the keys kp, kp + KP, ... of
 //      the tile, so one value word read serves its four coordinates.
@@ -112,10 +110,12 @@ __device__ __forceinline__ void stage_heads(const float* __restrict__ ws, int64_
 template <int D>
 constexpr int attn_gen_part() { return D + 2; }
 
-// Logits of one key whose index words sit in LDS (row kw, BITS words per 32 coordinates).
+// Logits of one key whose index words sit in LDS (row kw, BITS words per 32 coordinates).  The
+// rotated queries are read from global memory at wave-uniform addresses (scalar loads), 2 D floats
+// per head.  (Rows held in registers instead measured slower at d = 64: fewer resident waves.)
 template <int D, int BITS, int NH>
-__device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, const float* qh, const float* cent,
-                                                   int nh, float (&out)[NH]) {
+__device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, const float* __restrict__ qg,
+                                                   const float* cent, int nh, float (&out)[NH]) {
   float acc[NH];
 #pragma unroll
   for (int k = 0; k < NH; ++k) acc[k] = 0.f;
@@ -132,7 +132,7 @@ __device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, 
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       if (k < nh) {
-        const f32x4* qr4 = reinterpret_cast<const f32x4*>(qh + k * 2 * D + 32 * c);
+        const f32x4* qr4 = reinterpret_cast<const f32x4*>(qg + k * 2 * D + 32 * c);
 #pragma unroll
         for (int e4 = 0; e4 < 8; ++e4) {
           const f32x4 qv = qr4[e4];
@@ -146,17 +146,17 @@ __device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, 
   for (int k = 0; k < NH; ++k) out[k] = s * acc[k];
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int NH>
 struct AttnGenLds {
   static constexpr int WK = D * KB / 32, WV = D * VB / 32;
   static constexpr int SK = WK + 1, SV = WV + 1;  // odd row strides: a thread's row reads hit distinct banks
   static constexpr int KP = kGenThreads / (D / 4);  // key phases of the P V step
   static constexpr int TILE_WORDS = kGenThreads * (SK + SV);
-  static constexpr int RED_WORDS = (KP - 1) * kGenHeadGroup * D;  // phase partials, after the last tile
+  static constexpr int RED_WORDS = (KP - 1) * NH * D;  // phase partials, after the last tile
   static constexpr int REGION = TILE_WORDS > RED_WORDS ? TILE_WORDS : RED_WORDS;
 };
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int NH, bool EXACT>
 __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restrict__ ws, int Hq, int Hkv, int64_t T,
                                                          int64_t rows, int nsplit, float scale,
                                                          const uint32_t* __restrict__ kidx,
@@ -164,14 +164,12 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
                                                          const uint32_t* __restrict__ vidx,
                                                          const float* __restrict__ vnorm, CodebookArgs cbk,
                                                          CodebookArgs cbv, float* __restrict__ parts) {
-  using L = AttnGenLds<D, KB, VB>;
+  using L = AttnGenLds<D, KB, VB, NH>;
   constexpr int P = attn_gen_part<D>();
   constexpr int KP = L::KP;
-  __shared__ __attribute__((aligned(16))) float qh[kGenHeadGroup * 2 * D];
   __shared__ float centk[16], centv[16];
-  __shared__ float pv[kGenHeadGroup][kGenThreads];   // p * s_v
-  __shared__ float ksn[kGenThreads];
-  __shared__ float red[kGenHeadGroup][kGenThreads / 64];
+  __shared__ __attribute__((aligned(16))) float pv[kGenThreads][NH];   // p * s_v, a key's heads together
+  __shared__ float red[NH][kGenThreads / 64];
   __shared__ uint32_t region[L::REGION];
   uint32_t* const kws = region;                         // [256][SK]
   uint32_t* const vws = region + kGenThreads * L::SK;   // [256][SV]
@@ -182,14 +180,14 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
   }
   const int bg = blockIdx.y, split = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int nh = Hq / Hkv;
+  const int nh = EXACT ? NH : Hq / Hkv;  // EXACT: the GQA ratio is NH
   const int64_t h0 = (int64_t)b * Hq + (int64_t)g * nh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = threadIdx.x % (D / 4), kp = threadIdx.x / (D / 4);
-  stage_heads<D>(ws, h0, nh, qh);
-  float m[kGenHeadGroup], l[kGenHeadGroup], acc[kGenHeadGroup][4];
+  const float* const qg = ws + h0 * 2 * D;
+  float m[NH], l[NH], acc[NH][4];
 #pragma unroll
-  for (int k = 0; k < kGenHeadGroup; ++k) {
+  for (int k = 0; k < NH; ++k) {
     m[k] = -INFINITY;
     l[k] = 0.f;
 #pragma unroll
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
     const int64_t t = tile * kGenThreads + threadIdx.x;
     const bool valid = t < T;
     const int64_t row = (int64_t)bg * rows + (valid ? t : 0);
-    __syncthreads();  // the previous tile's LDS reads are done (and qh is staged)
+    __syncthreads();  // the previous tile's LDS reads are done
     // 1. stage this thread's key and value words
     {
       const uint32_t* ks = kidx + row * L::WK;
@@ -211,15 +209,15 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
       for (int i = 0; i < L::WK; ++i) kws[threadIdx.x * L::SK + i] = ks[i];
 #pragma unroll
       for (int i = 0; i < L::WV; ++i) vws[threadIdx.x * L::SV + i] = vs[i];
-      ksn[threadIdx.x] = valid ? knorm[row] : 0.f;
     }
+    const float ksn = valid ? knorm[row] : 0.f;
     const float vsn = valid ? vnorm[row] : 0.f;
-    // 2. logits (a thread reads only its own staged row here)
-    float lg[kGenHeadGroup];
-    gen_key_logits_lds<D, KB, kGenHeadGroup>(kws + threadIdx.x * L::SK, ksn[threadIdx.x], qh, centk, nh, lg);
+    // 2. logits (a thread reads only its own key row)
+    float lg[NH];
+    gen_key_logits_lds<D, KB, NH>(kws + threadIdx.x * L::SK, ksn, qg, centk, nh, lg);
     // 3. online softmax per head
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k) {
+    for (int k = 0; k < NH; ++k) {
       lg[k] = valid ? lg[k] * scale : -INFINITY;
       float mx = lg[k];
 #pragma unroll
@@ -227,16 +225,16 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
       if (lane == 0) red[k][wave] = mx;
     }
     __syncthreads();
-    float pk[kGenHeadGroup];  // this thread's key's probabilities (for l)
+    float pk[NH];  // this thread's key's probabilities (for l)
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k) {
+    for (int k = 0; k < NH; ++k) {
       float mx = red[k][0];
 #pragma unroll
       for (int w = 1; w < kGenThreads / 64; ++w) mx = fmaxf(mx, red[k][w]);
       const float mn = fmaxf(m[k], mx);
       const float alpha = mn == -INFINITY ? 1.f : __expf(m[k] - mn);
       const float p = mn == -INFINITY ? 0.f : __expf(lg[k] - mn);
-      pv[k][threadIdx.x] = p * vsn;
+      pv[threadIdx.x][k] = p * vsn;
       pk[k] = p;
       m[k] = mn;
       l[k] *= alpha;
@@ -255,19 +253,21 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
         float cv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) cv[e] = centv[(f >> (VB * e)) & ((1u << VB) - 1u)];
+        // all NH heads' probabilities in NH / 4 reads (heads past the ratio carry finite values
+        // that are never stored)
 #pragma unroll
-        for (int k = 0; k < kGenHeadGroup; ++k) {
-          if (k < nh) {
-            const float p = pv[k][tt];
+        for (int k4 = 0; k4 < NH / 4; ++k4) {
+          const f32x4 p4 = reinterpret_cast<const f32x4*>(pv[tt])[k4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(p, cv[e], acc[k][e]);
-          }
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * k4 + kk][e] = fmaf(p4[kk], cv[e], acc[4 * k4 + kk][e]);
         }
       }
     }
     // l: the tile's probabilities summed over the block
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k) {
+    for (int k = 0; k < NH; ++k) {
       float sm = pk[k];
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k) {
+    for (int k = 0; k < NH; ++k) {
       float sm = 0.f;
 #pragma unroll
       for (int w = 0; w < kGenThreads / 64; ++w) sm += red[k][w];
@@ -286,21 +286,21 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
   __syncthreads();
   if (kp > 0) {
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k)
+    for (int k = 0; k < NH; ++k)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accred[((kp - 1) * kGenHeadGroup + k) * D + 4 * g4 + e] = acc[k][e];
+      for (int e = 0; e < 4; ++e) accred[((kp - 1) * NH + k) * D + 4 * g4 + e] = acc[k][e];
   }
   __syncthreads();
   if (kp == 0) {
 #pragma unroll 1
     for (int p = 0; p < KP - 1; ++p)
 #pragma unroll
-      for (int k = 0; k < kGenHeadGroup; ++k)
+      for (int k = 0; k < NH; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[k][e] += accred[(p * kGenHeadGroup + k) * D + 4 * g4 + e];
+        for (int e = 0; e < 4; ++e) acc[k][e] += accred[(p * NH + k) * D + 4 * g4 + e];
     float* dst = parts + ((int64_t)bg * nsplit + split) * kGenHeadGroup * P;
 #pragma unroll
-    for (int k = 0; k < kGenHeadGroup; ++k) {
+    for (int k = 0; k < NH; ++k) {
       if (k < nh) {
         if (g4 == 0) {
           dst[k * P] = m[k];
@@ -799,8 +799,13 @@ template <int D, int KB, int VB>
 hipError_t attn_gen_launch(const float* ws, int B, int Hq, int Hkv, int64_t T, int64_t rows, int nsplit, float scale,
                            const tq_packed* K, const tq_packed* V, const CodebookArgs& cbk, const CodebookArgs& cbv,
                            float* parts, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_gen<D, KB, VB>), dim3((unsigned)nsplit, (unsigned)(B * Hkv)), dim3(kGenThreads), 0, st,
-                     ws, Hq, Hkv, T, rows, nsplit, scale, K->idx, K->norms, V->idx, V->norms, cbk, cbv, parts);
+  if (Hq / Hkv == 4)
+    hipLaunchKernelGGL((k_attn_gen<D, KB, VB, 4, true>), dim3((unsigned)nsplit, (unsigned)(B * Hkv)), dim3(kGenThreads), 0,
+                       st, ws, Hq, Hkv, T, rows, nsplit, scale, K->idx, K->norms, V->idx, V->norms, cbk, cbv, parts);
+  else
+    hipLaunchKernelGGL((k_attn_gen<D, KB, VB, kGenHeadGroup, false>), dim3((unsigned)nsplit, (unsigned)(B * Hkv)),
+                       dim3(kGenThreads), 0, st, ws, Hq, Hkv, T, rows, nsplit, scale, K->idx, K->norms, V->idx,
+                       V->norms, cbk, cbv, parts);
   return hipGetLastError();
 }
 
