@@ -115,7 +115,7 @@ constexpr int attn_gen_part() { return D + 2; }
 // per head.  (Rows held in registers instead measured slower at d = 64: fewer resident waves.)
 template <int D, int BITS, int NH>
 __device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, const float* __restrict__ qg,
-                                                   const float* cent, int nh, float (&out)[NH]) {
+                                                   const f32x2* pair, int nh, float (&out)[NH]) {
   float acc[NH];
 #pragma unroll
   for (int k = 0; k < NH; ++k) acc[k] = 0.f;
@@ -125,9 +125,13 @@ __device__ __forceinline__ void gen_key_logits_lds(const uint32_t* kw, float s, 
 #pragma unroll
     for (int b = 0; b < BITS; ++b) wc[b] = kw[c * BITS + b];
     float cv[32];
-    gen_for<0, 32>([&](auto ee) {
-      constexpr int e = decltype(ee)::value;
-      cv[e] = cent[field<BITS, e>(wc)];
+    // two coordinates per lookup: entry f of the pair table holds the centroids of the low and
+    // the high BITS bits of the 2 BITS-bit field f
+    gen_for<0, 16>([&](auto pp) {
+      constexpr int e2 = decltype(pp)::value;
+      const f32x2 c2 = pair[field<2 * BITS, e2>(wc)];
+      cv[2 * e2] = c2[0];
+      cv[2 * e2 + 1] = c2[1];
     });
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
@@ -167,16 +171,23 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
   using L = AttnGenLds<D, KB, VB, NH>;
   constexpr int P = attn_gen_part<D>();
   constexpr int KP = L::KP;
-  __shared__ float centk[16], centv[16];
+  constexpr int VQ = VB <= 2 ? 1 << (4 * VB) : 1;   // value quad table: 4 coordinates per lookup
+  __shared__ float centv[16];
+  __shared__ __attribute__((aligned(16))) f32x2 kpair[1 << (2 * KB)];
+  __shared__ __attribute__((aligned(16))) f32x4 vquad[VQ];
   __shared__ __attribute__((aligned(16))) float pv[kGenThreads][NH];   // p * s_v, a key's heads together
   __shared__ float red[NH][kGenThreads / 64];
   __shared__ uint32_t region[L::REGION];
   uint32_t* const kws = region;                         // [256][SK]
   uint32_t* const vws = region + kGenThreads * L::SK;   // [256][SV]
   float* const accred = reinterpret_cast<float*>(region);
-  if (threadIdx.x < 16) {
-    centk[threadIdx.x] = cbk.c[threadIdx.x];
-    centv[threadIdx.x] = cbv.c[threadIdx.x];
+  if (threadIdx.x < 16) centv[threadIdx.x] = cbv.c[threadIdx.x];
+  for (int i = threadIdx.x; i < (1 << (2 * KB)); i += kGenThreads)
+    kpair[i] = f32x2{cbk.c[i & ((1 << KB) - 1)], cbk.c[i >> KB]};
+  if constexpr (VB <= 2) {
+    constexpr uint32_t vm = (1u << VB) - 1u;
+    for (int i = threadIdx.x; i < VQ; i += kGenThreads)
+      vquad[i] = f32x4{cbv.c[i & vm], cbv.c[(i >> VB) & vm], cbv.c[(i >> (2 * VB)) & vm], cbv.c[(i >> (3 * VB)) & vm]};
   }
   const int bg = blockIdx.y, split = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
     const float vsn = valid ? vnorm[row] : 0.f;
     // 2. logits (a thread reads only its own key row)
     float lg[NH];
-    gen_key_logits_lds<D, KB, NH>(kws + threadIdx.x * L::SK, ksn, qg, centk, nh, lg);
+    gen_key_logits_lds<D, KB, NH>(kws + threadIdx.x * L::SK, ksn, qg, kpair, nh, lg);
     // 3. online softmax per head
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
@@ -251,8 +262,14 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
         uint32_t f = vws[tt * L::SV + wi] >> sh;
         if (sh + 4 * VB > 32) f |= vws[tt * L::SV + wi + 1] << (32 - sh);
         float cv[4];
+        if constexpr (VB <= 2) {
+          const f32x4 c4 = vquad[f & (uint32_t)(VQ - 1)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cv[e] = centv[(f >> (VB * e)) & ((1u << VB) - 1u)];
+          for (int e = 0; e < 4; ++e) cv[e] = c4[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cv[e] = centv[(f >> (VB * e)) & ((1u << VB) - 1u)];
+        }
         // all NH heads' probabilities in NH / 4 reads (heads past the ratio carry finite values
         // that are never stored)
 #pragma unroll

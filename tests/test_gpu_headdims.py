@@ -208,7 +208,8 @@ def test_scores_cache_stride_head_dims(dev, d):
 
 @pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("B,hkv,hq,T,kb,vb", [(1, 2, 2, 1, 3, 2), (2, 1, 3, 257, 4, 4), (1, 2, 16, 9000, 2, 3),
-                                              (1, 1, 8, 4096 + 255, 3, 1)])
+                                              (1, 1, 8, 4096 + 255, 3, 1), (2, 2, 8, 3000, 4, 2),
+                                              (1, 1, 4, 70000, 4, 2)])
 def test_decode_attention_head_dims(dev, d, B, hkv, hq, T, kb, vb):
     rot, _, rmat, _ = _handles(d)
     n = B * hkv * T
@@ -255,3 +256,24 @@ def test_head_dim_errors(dev):
     with pytest.raises(tq.TQError) as e:                  # the static-scratch scores take d = 128 only
         tq.scores_noalloc(torch.zeros((1, 2, 256), device=dev), K, 1, cb, rot)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_decode_attention_head_dims_reused_workspace(dev, d):
+    # repeated calls on one workspace (and a smaller call in between) give the same result
+    rot, _, _, _ = _handles(d)
+    B, hkv, hq, T = 2, 2, 8, 5000
+    n = B * hkv * T
+    _, xkt = _keys(n, d, seed=7)
+    _, xvt = _keys(n, d, seed=8)
+    K, cbk = _encode(dev, xkt, d, 4, "mse")
+    V, cbv = _encode(dev, xvt, d, 2, "mse")
+    q = torch.from_numpy(wl.gaussian((B, hq, d), 9)).to(dev)
+    ws = torch.empty((tq.decode_attn_workspace(B, hq, hkv, T, d),), dtype=torch.uint8, device=dev)
+    first = tq.decode_attn(q, K, V, hkv, cbk, cbv, rot, rot, ws=ws).cpu()
+    Ks, cbks = _encode(dev, xkt[: hkv * 300], d, 4, "mse")
+    Vs, cbvs = _encode(dev, xvt[: hkv * 300], d, 2, "mse")
+    tq.decode_attn(q[:1], Ks, Vs, hkv, cbks, cbvs, rot, rot, ws=ws)
+    second = tq.decode_attn(q, K, V, hkv, cbk, cbv, rot, rot, ws=ws).cpu()
+    assert torch.equal(first, second)
+
