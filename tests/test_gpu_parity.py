@@ -99,6 +99,34 @@ def test_encode_mse_parity_bf16_keys(dev, rot_dense, rot_wht, b, kind):
     np.testing.assert_allclose(p.norms.cpu().numpy(), enc.norms, rtol=1e-6)
 
 
+@pytest.mark.parametrize("n", [1, 31, 33, 65, 4097])
+@pytest.mark.parametrize("dtype,b", [("bf16", 3), ("f32", 2), ("bf16", 4), ("f32", 1)])
+def test_encode_mse_dense_ragged(dev, rot_dense, n, dtype, b):
+    # vector counts against the 32-vector tiles of the dense-rotation encode, both input types; rows
+    # past n keep their contents
+    x, xt = _keys(n, hkv=1)
+    if dtype == "f32":
+        rng = np.random.default_rng(n + b)
+        x = x * rng.uniform(0.5, 2.0, size=(n, 1)) + rng.normal(0, 1e-3, size=x.shape)
+        x[:: 7] *= 1e-4
+        xt = torch.from_numpy(x.astype(np.float32))
+        x = xt.numpy().astype(np.float64)
+    cb = tq.codebook(128, b)
+    full = tq.alloc_packed(n + 40, 128, b, "mse", device=dev)
+    full.idx.fill_(-1)
+    full.norms.fill_(5.0)
+    p = tq.Packed(128, b, "mse", n, full.idx[:n], full.norms[:n])
+    tq.encode(xt.to(dev), b, "mse", cb, rot_dense, out=p)
+    torch.cuda.synchronize()
+    assert torch.all(full.idx[n:] == -1) and torch.all(full.norms[n:] == 5.0)
+    cb_o = oracle.codebook(128, b)
+    enc = oracle.encode_mse(x, R_DENSE, cb_o)
+    words = to_np_words(p.idx)
+    bad, _ = check_indices(oracle.unpack_bits(words, 128, b), enc.y, cb_o, f"dense n={n} {dtype} b={b}")
+    np.testing.assert_array_equal(words[~bad], enc.words[~bad])
+    np.testing.assert_allclose(p.norms.cpu().numpy(), enc.norms, rtol=1e-6, atol=0)
+
+
 def test_encode_mse_c1_fp32_full(dev, rot_dense):
     x32, _ = wl.c1_inputs()
     x = x32.astype(np.float64)
