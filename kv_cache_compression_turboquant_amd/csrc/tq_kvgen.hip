@@ -60,14 +60,14 @@ __global__ __launch_bounds__(256) void k_qprep_gen(const float* __restrict__ q, 
   __syncthreads();
   f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
   // rt32[j][i] = R[i][j] and st32[j][i] = S[i][j]
-#pragma unroll 8
+#pragma unroll 16
   for (int jj = 0; jj < JN; ++jj) {
     const int j = jg * JN + jj;
     const f32x4 r = *reinterpret_cast<const f32x4*>(rt32 + (size_t)j * D + 4 * i4);
     a += r * qs[j];
   }
   if (st32) {
-#pragma unroll 8
+#pragma unroll 16
     for (int jj = 0; jj < JN; ++jj) {
       const int j = jg * JN + jj;
       const f32x4 r = *reinterpret_cast<const f32x4*>(st32 + (size_t)j * D + 4 * i4);
@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_gen(const float* __restric
 // out[b, h] = R_V^T (sum_s e^{m_s - M} acc_s) / (sum_s e^{m_s - M} l_s); one block of D threads per
 // query head.  The splits are taken D at a time: thread t forms split s0 + t's weight once, and
 // the accumulation over the chunk then reads the weights from LDS while its loads of acc_s (one
-// per split, independent) stay in flight together.
+// per split, independent) stay in flight together, 32 at a time, as do the loads of R's columns
+// (the kernel is bound by these round trips to L2, not by its arithmetic).
 template <int D>
 __device__ __forceinline__ float block_reduce_gen(float v, float* red, bool is_max) {
   constexpr int NW = D / 64;
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(D) void k_attn_gen_combine(const float* __restrict_
     __syncthreads();
     const int cnt = nsplit - s0 < D ? nsplit - s0 : D;
     const float* ps = src + (int64_t)s0 * sstride + 2 + i;
-#pragma unroll 8
+#pragma unroll 32
     for (int t = 0; t < cnt; ++t) A = fmaf(wsh[t], ps[t * sstride], A);
     __syncthreads();
   }
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(D) void k_attn_gen_combine(const float* __restrict_
   __syncthreads();
   // R_V^T a: (R^T a)_i = sum_j R[j][i] a_j, R row-major: thread i reads consecutive columns
   float o = 0.f;
-#pragma unroll 8
+#pragma unroll 32
   for (int j = 0; j < D; ++j) o = fmaf(r32v[(size_t)j * D + i], a[j], o);
   out[h * D + i] = o;
 }
