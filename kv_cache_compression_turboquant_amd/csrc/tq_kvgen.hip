@@ -504,9 +504,15 @@ __global__ __launch_bounds__(kGenThreads) void k_encode_d64(const void* __restri
 // first; grid (key ranges, sequences, groups of 16 query heads).  (Longer-lived blocks that
 // stream several such groups with the next one's loads in flight measured slower.)
 // ---------------------------------------------------------------------------------------
+#ifndef TQ_GM_TILES64
+#define TQ_GM_TILES64 8
+#endif
+#ifndef TQ_GM_TILES256
+#define TQ_GM_TILES256 4
+#endif
 // tiles of 16 keys per wave (registers); a block of four waves takes 64 gm_tiles<D>() keys
 template <int D>
-constexpr int gm_tiles() { return D == 64 ? 8 : 4; }
+constexpr int gm_tiles() { return D == 64 ? TQ_GM_TILES64 : TQ_GM_TILES256; }
 
 template <int BITS>
 struct GmTab;
